@@ -1,0 +1,270 @@
+"""Gated DeltaNet token mixer core for MI355X (gfx950): Python binding of ``libgdn.so``.
+
+Argument marshalling only. Every step of the computation runs in the library's HIP kernels;
+torch provides device memory and the current HIP stream. Calls are asynchronous on
+``torch.cuda.current_stream()``. There is no CPU fallback: if ``libgdn.so`` is missing or a
+tensor is not on the GPU, the call raises.
+
+Entry points (same names as the C ABI in ``include/gdn.h``):
+  prepare(...)         conv(4) + SiLU, split, q/k L2 norm, gates
+  chunk_forward(...)   chunked prefill (chunk 64), optional initial/final states, varlen
+  chunk_intra(...), chunk_scan(...)  the two stages of chunk_forward
+  recurrent_step(...)  one decode token per sequence, state updated in place
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["prepare", "chunk_forward", "chunk_intra", "chunk_scan", "recurrent_step",
+           "workspace_size", "library_path", "GdnError", "CHUNK"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgdn.so")
+CHUNK = 64
+
+GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+_DT = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("num_qk_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise GdnError(f"{_LIB_PATH} is not built; run `python -m gated_deltanet_linear_amd.build` "
+                       "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    sp = ctypes.POINTER(GdnShape)
+    lib.gdn_prepare.restype = ctypes.c_int
+    lib.gdn_prepare.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P,
+                                _P, _P]
+    lib.gdn_chunk_forward_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_forward_workspace_size.argtypes = [sp]
+    lib.gdn_chunk_forward.restype = ctypes.c_int
+    lib.gdn_chunk_forward.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunk_intra.restype = ctypes.c_int
+    lib.gdn_chunk_intra.argtypes = [sp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunk_scan.restype = ctypes.c_int
+    lib.gdn_chunk_scan.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_recurrent_step.restype = ctypes.c_int
+    lib.gdn_recurrent_step.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_abi_version.restype = ctypes.c_int
+    lib.gdn_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise GdnError(f"{what}: {_load().gdn_status_string(rc).decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise GdnError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise GdnError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise GdnError(f"{name} must be contiguous")
+    return t
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype, name: str) -> int:
+    if dt not in _DT:
+        raise GdnError(f"{name}: dtype {dt} not supported (float32 or bfloat16)")
+    return _DT[dt]
+
+
+def _shape(num_seqs, total_tokens, hqk, hv, dk, dv, qkv_dtype, out_dtype, in_dtype=None,
+           scale=1.0) -> GdnShape:
+    return GdnShape(int(num_seqs), int(total_tokens), int(hqk), int(hv), int(dk), int(dv),
+                    _dtype_code(qkv_dtype, "q/k/v"), _dtype_code(out_dtype, "o"),
+                    _dtype_code(in_dtype or torch.bfloat16, "front-end input"), float(scale))
+
+
+def _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype):
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    _dev(g, "g", torch.float32)
+    _dev(beta, "beta", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.dim() != 3 or k.shape != q.shape:
+        raise GdnError("q and k must be [T, H_qk, d_k]")
+    T, hqk, dk = q.shape
+    if g.shape != (T, hv) or beta.shape != (T, hv):
+        raise GdnError("g and beta must be [T, H_v]")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise GdnError("cu_seqlens must be [N + 1]")
+    n = cu_seqlens.numel() - 1
+    return _shape(n, T, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale), n
+
+
+def _v_shape(v, q):
+    _dev(v, "v", q.dtype)
+    if v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise GdnError("v must be [T, H_v, d_v]")
+    return v.shape[1], v.shape[2]
+
+
+def workspace_size(total_tokens: int, num_seqs: int, num_qk_heads: int, num_v_heads: int,
+                   head_dim: int, dtype=torch.bfloat16) -> int:
+    s = _shape(num_seqs, total_tokens, num_qk_heads, num_v_heads, head_dim, head_dim, dtype, dtype)
+    return int(_load().gdn_chunk_forward_workspace_size(ctypes.byref(s)))
+
+
+def _workspace(s: GdnShape, device, workspace):
+    nbytes = int(_load().gdn_chunk_forward_workspace_size(ctypes.byref(s)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace", torch.uint8)
+    return workspace
+
+
+def chunk_forward(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_state=True,
+                  scale=1.0, out_dtype=None, workspace=None, final_state=None, o=None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill. Returns (o [T, H_v, d_v], final_state [N, H_v, d_k, d_v] or None).
+
+    ``final_state`` may be passed (and may be ``initial_state`` itself for an in-place update).
+    """
+    hv, dv = _v_shape(v, q)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype)
+    T, dk = s.total_tokens, s.head_dim_k
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", torch.float32)
+        if initial_state.shape != (n, hv, dk, dv):
+            raise GdnError("initial_state must be [N, H_v, d_k, d_v]")
+    if o is None:
+        o = torch.empty((T, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
+    _dev(o, "o", out_dtype or q.dtype)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((n, hv, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _dev(final_state, "final_state", torch.float32)
+    ws = _workspace(s, q.device, workspace)
+    rc = _load().gdn_chunk_forward(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                   _ptr(final_state), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "gdn_chunk_forward")
+    return o, final_state
+
+
+def chunk_intra(q, k, g, beta, cu_seqlens, num_v_heads, workspace, scale=1.0):
+    """Stage 1 of chunk_forward (state-independent in-chunk work) into ``workspace``."""
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, int(num_v_heads), q.shape[2], scale, None)
+    _dev(workspace, "workspace", torch.uint8)
+    rc = _load().gdn_chunk_intra(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(g),
+                                 _ptr(beta), _ptr(workspace), workspace.numel(), _stream())
+    _check(rc, "gdn_chunk_intra")
+
+
+def chunk_scan(q, k, v, g, beta, cu_seqlens, workspace, initial_state=None, o=None,
+               final_state=None, scale=1.0, out_dtype=None):
+    """Stage 2 of chunk_forward (sequential cross-chunk recurrence) from ``workspace``."""
+    hv, dv = _v_shape(v, q)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype)
+    _dev(workspace, "workspace", torch.uint8)
+    if o is None:
+        o = torch.empty((s.total_tokens, s.num_v_heads, s.head_dim_v), dtype=out_dtype or q.dtype,
+                        device=q.device)
+    rc = _load().gdn_chunk_scan(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
+                                workspace.numel(), _stream())
+    _check(rc, "gdn_chunk_scan")
+    return o, final_state
+
+
+def recurrent_step(q, k, v, g, beta, state, scale=1.0, out_dtype=None, o=None) -> torch.Tensor:
+    """One decode token per sequence: q, k [N, H_qk, d_k], v [N, H_v, d_v], g, beta [N, H_v],
+    state [N, H_v, d_k, d_v] fp32 (updated in place). Returns o [N, H_v, d_v]."""
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    _dev(g, "g", torch.float32)
+    _dev(beta, "beta", torch.float32)
+    _dev(state, "state", torch.float32)
+    N, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N or g.shape != (N, hv) or beta.shape != (N, hv) \
+            or state.shape != (N, hv, dk, dv):
+        raise GdnError("recurrent_step: inconsistent shapes")
+    s = _shape(N, N, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale)
+    if o is None:
+        o = torch.empty((N, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
+    _dev(o, "o", out_dtype or q.dtype)
+    rc = _load().gdn_recurrent_step(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(beta), _ptr(state), _ptr(o), _stream())
+    _check(rc, "gdn_recurrent_step")
+    return o
+
+
+def prepare(mixed_qkv, conv_weight, a, b, A_log, dt_bias, cu_seqlens, num_qk_heads, head_dim_k,
+            num_v_heads, head_dim_v, conv_bias=None, l2norm_eps=1e-6, qkv_dtype=None):
+    """Front end: returns q, k [T, H_qk, d_k], v [T, H_v, d_v] (qkv_dtype, default the input
+    dtype) and g, beta [T, H_v] fp32."""
+    _dev(mixed_qkv, "mixed_qkv")
+    dt = mixed_qkv.dtype
+    _dev(conv_weight, "conv_weight", dt)
+    _dev(a, "a", dt)
+    _dev(b, "b", dt)
+    _dev(A_log, "A_log", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if conv_bias is not None:
+        _dev(conv_bias, "conv_bias", dt)
+    T, conv_dim = mixed_qkv.shape
+    hqk, dk, hv, dv = int(num_qk_heads), int(head_dim_k), int(num_v_heads), int(head_dim_v)
+    if conv_dim != 2 * hqk * dk + hv * dv or conv_weight.shape != (conv_dim, 4):
+        raise GdnError("mixed_qkv must be [T, 2*H_qk*d_k + H_v*d_v] and conv_weight [conv_dim, 4]")
+    if a.shape != (T, hv) or b.shape != (T, hv) or A_log.shape != (hv,) or dt_bias.shape != (hv,):
+        raise GdnError("a, b must be [T, H_v]; A_log, dt_bias [H_v]")
+    qd = qkv_dtype or dt
+    n = cu_seqlens.numel() - 1
+    s = _shape(n, T, hqk, hv, dk, dv, qd, qd, in_dtype=dt)
+    dev = mixed_qkv.device
+    q = torch.empty((T, hqk, dk), dtype=qd, device=dev)
+    k = torch.empty((T, hqk, dk), dtype=qd, device=dev)
+    v = torch.empty((T, hv, dv), dtype=qd, device=dev)
+    g = torch.empty((T, hv), dtype=torch.float32, device=dev)
+    beta = torch.empty((T, hv), dtype=torch.float32, device=dev)
+    rc = _load().gdn_prepare(ctypes.byref(s), _ptr(cu_seqlens), _ptr(mixed_qkv), _ptr(conv_weight),
+                             _ptr(conv_bias), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                             float(l2norm_eps), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _stream())
+    _check(rc, "gdn_prepare")
+    return q, k, v, g, beta

@@ -1,0 +1,135 @@
+// gdn_abi.cpp -- the extern "C" entry points of libgdn.so: host-side validation, then the
+// kernel launchers. Validation never touches the GPU, so every error path can be exercised
+// on a machine without one. See include/gdn.h for the contract of each call.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+bool dtype_ok(int32_t d) { return d == GDN_DTYPE_F32 || d == GDN_DTYPE_BF16; }
+
+// Shape checks shared by all entry points.
+gdn_status_t check_shape(const gdn_shape_t* s) {
+  if (s == nullptr) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->num_seqs < 1 || s->total_tokens < 0 || s->num_qk_heads < 1 || s->num_v_heads < 1)
+    return GDN_ERR_INVALID_ARGUMENT;
+  if (s->num_v_heads % s->num_qk_heads != 0) return GDN_ERR_INVALID_ARGUMENT;
+  if (!dtype_ok(s->qkv_dtype) || !dtype_ok(s->out_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->head_dim_k < 1 || s->head_dim_v < 1) return GDN_ERR_INVALID_ARGUMENT;
+  if (!(s->scale == s->scale)) return GDN_ERR_INVALID_ARGUMENT;  // NaN
+  if (s->head_dim_k != s->head_dim_v) return GDN_ERR_UNSUPPORTED;
+  if (s->head_dim_k != 32 && s->head_dim_k != 64 && s->head_dim_k != 128) return GDN_ERR_UNSUPPORTED;
+  // Index arithmetic inside the kernels is 64-bit for element offsets and 32-bit for token
+  // and head counts; keep element counts of one tensor and slot counts within range.
+  const long long rows = (long long)s->total_tokens * s->num_v_heads;
+  if (rows > (1LL << 31) - 1) return GDN_ERR_UNSUPPORTED;
+  if ((long long)s->num_seqs * s->num_v_heads > (1LL << 31) - 1) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+gdn_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status_t status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT: bad shape, dtype or pointer";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: shape not compiled into this library";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: a kernel launch failed";
+  }
+  return "unknown gdn_status_t";
+}
+
+size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* s) {
+  if (check_shape(s) != GDN_OK) return 0;
+  return (size_t)gdn::chunk_slots(*s) * (size_t)s->num_v_heads *
+         (size_t)gdn::kWorkspaceRecordBytes;
+}
+
+gdn_status_t gdn_prepare(const gdn_shape_t* s, const int32_t* cu, const void* x, const void* w,
+                         const void* bias, const void* a, const void* b, const float* A_log,
+                         const float* dt_bias, float eps, void* q, void* k, void* v, float* g,
+                         float* beta, void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!cu || !A_log || !dt_bias) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens > 0 && (!x || !w || !a || !b || !q || !k || !v || !g || !beta))
+    return GDN_ERR_INVALID_ARGUMENT;
+  // 16-byte row access of mixed_qkv / q / k / v.
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return GDN_ERR_INVALID_ARGUMENT;
+  return from_hip(gdn::launch_prepare(*s, cu, x, w, bias, a, b, A_log, dt_bias, eps, q, k, v, g,
+                                      beta, static_cast<hipStream_t>(stream)));
+}
+
+static gdn_status_t check_chunk_common(const gdn_shape_t* s, const int32_t* cu, const void* q,
+                                       const void* k, const void* ws, size_t ws_bytes) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (!cu) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens > 0 && (!q || !k || !ws)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(ws, 256)) return GDN_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < gdn_chunk_forward_workspace_size(s)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+  return GDN_OK;
+}
+
+gdn_status_t gdn_chunk_intra(const gdn_shape_t* s, const int32_t* cu, const void* q,
+                             const void* k, const float* g, const float* beta, void* ws,
+                             size_t ws_bytes, void* stream) {
+  gdn_status_t st = check_chunk_common(s, cu, q, k, ws, ws_bytes);
+  if (st != GDN_OK) return st;
+  if (s->total_tokens > 0 && (!g || !beta)) return GDN_ERR_INVALID_ARGUMENT;
+  return from_hip(gdn::launch_chunk_intra(*s, cu, q, k, g, beta, ws,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_chunk_scan(const gdn_shape_t* s, const int32_t* cu, const void* q,
+                            const void* k, const void* v, const float* h0, void* o, float* ht,
+                            const void* ws, size_t ws_bytes, void* stream) {
+  gdn_status_t st = check_chunk_common(s, cu, q, k, ws, ws_bytes);
+  if (st != GDN_OK) return st;
+  if (s->total_tokens > 0 && (!v || !o)) return GDN_ERR_INVALID_ARGUMENT;
+  return from_hip(gdn::launch_chunk_scan(*s, cu, q, k, v, h0, o, ht, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_chunk_forward(const gdn_shape_t* s, const int32_t* cu, const void* q,
+                               const void* k, const void* v, const float* g, const float* beta,
+                               const float* h0, void* o, float* ht, void* ws, size_t ws_bytes,
+                               void* stream) {
+  gdn_status_t st = check_chunk_common(s, cu, q, k, ws, ws_bytes);
+  if (st != GDN_OK) return st;
+  if (s->total_tokens > 0 && (!v || !o || !g || !beta)) return GDN_ERR_INVALID_ARGUMENT;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = from_hip(gdn::launch_chunk_intra(*s, cu, q, k, g, beta, ws, hs));
+  if (st != GDN_OK) return st;
+  return from_hip(gdn::launch_chunk_scan(*s, cu, q, k, v, h0, o, ht, ws, hs));
+}
+
+gdn_status_t gdn_recurrent_step(const gdn_shape_t* s, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta, float* state,
+                                void* o, void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (s->total_tokens != s->num_seqs) return GDN_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(state, 16)) return GDN_ERR_INVALID_ARGUMENT;
+  return from_hip(gdn::launch_recurrent_step(*s, q, k, v, g, beta, state, o,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

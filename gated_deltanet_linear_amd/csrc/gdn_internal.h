@@ -1,0 +1,37 @@
+// gdn_internal.h -- launchers shared between the ABI layer and the kernel sources.
+// Host code only; every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+hipError_t launch_chunk_intra(const gdn_shape_t& s, const int32_t* cu, const void* q,
+                              const void* k, const float* g, const float* beta, void* ws,
+                              hipStream_t stream);
+
+hipError_t launch_chunk_scan(const gdn_shape_t& s, const int32_t* cu, const void* q,
+                             const void* k, const void* v, const float* h0, void* o, float* ht,
+                             const void* ws, hipStream_t stream);
+
+hipError_t launch_recurrent_step(const gdn_shape_t& s, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta, float* state,
+                                 void* o, hipStream_t stream);
+
+hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x,
+                          const void* w, const void* bias, const void* a, const void* b,
+                          const float* A_log, const float* dt_bias, float eps, void* q, void* k,
+                          void* v, float* g, float* beta, hipStream_t stream);
+
+// Bytes of one workspace record (one chunk slot x one V head); the layout is private to
+// gdn_chunk.hip, which checks this value at compile time.
+constexpr long long kWorkspaceRecordBytes = 24832;
+
+// Number of chunk slots the workspace holds: num_seqs + total_tokens / 64.
+inline long long chunk_slots(const gdn_shape_t& s) {
+  return (long long)s.num_seqs + (long long)s.total_tokens / 64;
+}
+
+}  // namespace gdn

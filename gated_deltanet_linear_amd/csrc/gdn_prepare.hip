@@ -1,0 +1,245 @@
+// gdn_prepare.hip -- front end of the Gated DeltaNet layer in one HBM-bound pass
+// ([MoE report] §3.3 stage 2 and §3.5; [xiwon notes] "Qwen3_5MoeGatedDeltaNet"; [intro]
+// "线性注意力").
+//
+//   y_t[c] = bias[c] + sum_{j=0..3} w[c][j] x_{t-3+j}[c]   (nn.Conv1d cross-correlation,
+//            left padding 3, zero history before the first token of each packed sequence)
+//   y      = SiLU(y) = y / (1 + e^-y)
+//   q | k | v = split of the channels; q, k head vectors scaled by 1 / sqrt(sum y^2 + eps)
+//   beta = sigmoid(b),  g = -exp(A_log) softplus(a + dt_bias)              (fp32)
+//
+// Grid: x = blocks of 256 tokens, y = one channel head (H_qk q heads, H_qk k heads, H_v v
+// heads) plus one extra row for the gates. A thread owns 8 channels (one 16-byte bf16 load)
+// and walks 256 * 8 / D consecutive tokens with a 3-row sliding window in registers, so each
+// input row is fetched once per thread run (plus 3 rows of history at the run start). The
+// D / 8 lanes that share a token are adjacent in the wave; the L2 norm reduces across them
+// with lane shuffles.
+#include "gdn_device.hpp"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kTokBlock = 256;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&x)[8]) {
+  const bf16x8 r = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16* p, const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[e];
+  *reinterpret_cast<bf16x8*>(p) = r;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = x[e];
+    b[e] = x[4 + e];
+  }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
+// Largest n in [0, num_seqs) with cu[n] <= t (the sequence holding token t < cu[num_seqs]).
+__device__ __forceinline__ int token_to_seq(const int32_t* cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+struct PrepParams {
+  const int32_t* cu;
+  const void* x;
+  const void* w;
+  const void* bias;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  float eps;
+  void* q;
+  void* k;
+  void* v;
+  float* g;
+  float* beta;
+  int num_seqs, T, hqk, hv;
+};
+
+template <typename InT, typename QT, int D>
+__global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
+  constexpr int CGN = D / 8;           // threads per token row of one head
+  constexpr int TL = 256 / CGN;        // token lanes per workgroup
+  constexpr int TPT = kTokBlock / TL;  // consecutive tokens per thread
+  static_assert(D % 8 == 0 && 256 % CGN == 0 && kTokBlock % TL == 0, "tile shape");
+
+  const int hb = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.x * kTokBlock;
+  const int head_blocks = 2 * p.hqk + p.hv;
+
+  if (hb == head_blocks) {  // gates
+    const InT* A = static_cast<const InT*>(p.a);
+    const InT* B = static_cast<const InT*>(p.b);
+    for (int e = tid; e < kTokBlock * p.hv; e += 256) {
+      const int t = tok0 + e / p.hv, h = e % p.hv;
+      if (t >= p.T) break;
+      const size_t i = (size_t)t * p.hv + h;
+      const float bv = to_f32(B[i]);
+      const float xa = to_f32(A[i]) + p.dt_bias[h];
+      const float sp = fmaxf(xa, 0.f) + log1pf(expf(-fabsf(xa)));
+      p.beta[i] = 1.f / (1.f + expf(-bv));
+      p.g[i] = -expf(p.A_log[h]) * sp;
+    }
+    return;
+  }
+
+  const int cg = tid % CGN, tl = tid / CGN;
+  const int conv_dim = 2 * p.hqk * D + p.hv * D;
+  int cbase;
+  QT* dst;
+  int dst_stride;
+  bool is_qk = true;
+  if (hb < p.hqk) {
+    cbase = hb * D;
+    dst = static_cast<QT*>(p.q) + hb * D;
+    dst_stride = p.hqk * D;
+  } else if (hb < 2 * p.hqk) {
+    cbase = p.hqk * D + (hb - p.hqk) * D;
+    dst = static_cast<QT*>(p.k) + (hb - p.hqk) * D;
+    dst_stride = p.hqk * D;
+  } else {
+    cbase = 2 * p.hqk * D + (hb - 2 * p.hqk) * D;
+    dst = static_cast<QT*>(p.v) + (hb - 2 * p.hqk) * D;
+    dst_stride = p.hv * D;
+    is_qk = false;
+  }
+  const int c = cbase + 8 * cg;
+  const InT* X = static_cast<const InT*>(p.x) + c;
+  dst += 8 * cg;
+
+  float w[8][4], bias[8];
+  {
+    const InT* W = static_cast<const InT*>(p.w) + (size_t)c * 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[e][j] = to_f32(W[e * 4 + j]);
+      bias[e] = p.bias ? to_f32(static_cast<const InT*>(p.bias)[c + e]) : 0.f;
+    }
+  }
+
+  const int t_first = tok0 + tl * TPT;
+  if (t_first >= p.T) return;  // whole token group idle (its CGN lanes leave together)
+  int n = token_to_seq(p.cu, p.num_seqs, t_first);
+  int seq_start = p.cu[n], seq_end = p.cu[n + 1];
+
+  float xm3[8], xm2[8], xm1[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) xm3[e] = xm2[e] = xm1[e] = 0.f;
+  if (t_first - 3 >= seq_start) load8(X + (size_t)(t_first - 3) * conv_dim, xm3);
+  if (t_first - 2 >= seq_start) load8(X + (size_t)(t_first - 2) * conv_dim, xm2);
+  if (t_first - 1 >= seq_start) load8(X + (size_t)(t_first - 1) * conv_dim, xm1);
+
+  for (int j = 0; j < TPT; ++j) {
+    const int t = t_first + j;
+    if (t >= p.T) break;
+    if (t >= seq_end) {  // a new sequence starts at t: no history
+      while (t >= p.cu[n + 1]) ++n;
+      seq_start = p.cu[n];
+      seq_end = p.cu[n + 1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xm3[e] = xm2[e] = xm1[e] = 0.f;
+    }
+    float x0[8], y[8];
+    load8(X + (size_t)t * conv_dim, x0);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = bias[e];
+      acc = fmaf(w[e][0], xm3[e], acc);
+      acc = fmaf(w[e][1], xm2[e], acc);
+      acc = fmaf(w[e][2], xm1[e], acc);
+      acc = fmaf(w[e][3], x0[e], acc);
+      y[e] = acc / (1.f + expf(-acc));
+      ss = fmaf(y[e], y[e], ss);
+    }
+    if (is_qk) {
+#pragma unroll
+      for (int d = 1; d < CGN; d <<= 1) ss += __shfl_xor(ss, d, kWave);
+      const float inv = 1.f / sqrtf(ss + p.eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= inv;
+    }
+    store8(dst + (size_t)t * dst_stride, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xm3[e] = xm2[e];
+      xm2[e] = xm1[e];
+      xm1[e] = x0[e];
+    }
+  }
+}
+
+template <typename InT, typename QT, int D>
+hipError_t launch_prepare_t(const PrepParams& p, hipStream_t stream) {
+  const unsigned gx = (unsigned)((p.T + kTokBlock - 1) / kTokBlock);
+  const unsigned gy = (unsigned)(2 * p.hqk + p.hv + 1);
+  if (gx == 0) return hipSuccess;
+  hipLaunchKernelGGL((prepare_kernel<InT, QT, D>), dim3(gx, gy), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename InT, typename QT>
+hipError_t launch_prepare_d(const PrepParams& p, int d, hipStream_t stream) {
+  switch (d) {
+    case 32: return launch_prepare_t<InT, QT, 32>(p, stream);
+    case 64: return launch_prepare_t<InT, QT, 64>(p, stream);
+    case 128: return launch_prepare_t<InT, QT, 128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x,
+                          const void* w, const void* bias, const void* a, const void* b,
+                          const float* A_log, const float* dt_bias, float eps, void* q, void* k,
+                          void* v, float* g, float* beta, hipStream_t stream) {
+  PrepParams p{cu, x, w, bias, a, b, A_log, dt_bias, eps, q, k, v, g, beta,
+               s.num_seqs, s.total_tokens, s.num_qk_heads, s.num_v_heads};
+  const bool in_bf = s.in_dtype == GDN_DTYPE_BF16, out_bf = s.qkv_dtype == GDN_DTYPE_BF16;
+  if (in_bf && out_bf) return launch_prepare_d<bf16, bf16>(p, s.head_dim_k, stream);
+  if (in_bf) return launch_prepare_d<bf16, float>(p, s.head_dim_k, stream);
+  if (out_bf) return launch_prepare_d<float, bf16>(p, s.head_dim_k, stream);
+  return launch_prepare_d<float, float>(p, s.head_dim_k, stream);
+}
+
+}  // namespace gdn

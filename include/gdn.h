@@ -1,0 +1,158 @@
+/*
+ * gdn.h -- C ABI of libgdn.so, the Gated DeltaNet token mixer core for MI355X (gfx950).
+ *
+ * The library computes the gated delta rule with a matrix state per value head,
+ *   H_t = a_t H_{t-1} + k_t u_t^T,   u_t = b_t (v_t - a_t H_{t-1}^T k_t),   o_t = scale H_t^T q_t,
+ * where a_t = exp(g_t), H is [d_k][d_v] (the spec S_t is H_t^T), and V head h reads
+ * QK head h / (H_v / H_qk). Page citations (by page title and section):
+ *   [MoE report]  "Qwen3.5-MoE-35B-A3B 模型架构深度拆解报告" (pillumina.github.io), §3.3-§3.7.
+ *   [xiwon notes] "Qwen3.5 观测记录" (xiwon.blog), sections "DeltaNet", "Gated DeltaNet",
+ *                 "Qwen3_5MoeGatedDeltaNet", "Cache".
+ *   [intro]       "Qwen3.5模型介绍" (blog.dijkstra-jhd.cn), section "线性注意力".
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major memory, owned by the
+ *     caller; the library never allocates, frees or keeps them. cu_seqlens is a device int32
+ *     array of num_seqs+1 non-decreasing offsets starting at 0, with cu_seqlens[num_seqs] ==
+ *     total_tokens (the host copy in the shape). Sequence n occupies packed rows
+ *     [cu_seqlens[n], cu_seqlens[n+1]); an empty sequence is allowed.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on it; no call
+ *     synchronises the host, so results are ready after the stream reaches that point.
+ *   - Errors: shapes, dtypes and pointers are validated on the host first. An invalid
+ *     argument returns GDN_ERR_INVALID_ARGUMENT, a valid but uncompiled shape returns
+ *     GDN_ERR_UNSUPPORTED, a short workspace GDN_ERR_WORKSPACE_TOO_SMALL; in all three
+ *     cases nothing is launched. GDN_ERR_HIP means a launch failed (hipGetLastError).
+ *     No C++ exception crosses this interface. Device contents of cu_seqlens are trusted.
+ *   - The library holds no mutable global state: concurrent calls on different streams with
+ *     disjoint outputs and workspaces are safe.
+ *   - Supported head dims: d_k == d_v in {32, 64, 128}. num_v_heads % num_qk_heads == 0.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_CHUNK 64 /* chunk length of the chunked prefill ([MoE report] §3.7 Step 2) */
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1,
+  GDN_ERR_UNSUPPORTED = 2,
+  GDN_ERR_WORKSPACE_TOO_SMALL = 3,
+  GDN_ERR_HIP = 4
+} gdn_status_t;
+
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype_t;
+
+typedef struct gdn_shape {
+  int32_t num_seqs;     /* N >= 1                                                         */
+  int32_t total_tokens; /* T = cu_seqlens[N] (for gdn_recurrent_step: == num_seqs)        */
+  int32_t num_qk_heads; /* H_qk                                                           */
+  int32_t num_v_heads;  /* H_v, a multiple of H_qk                                        */
+  int32_t head_dim_k;   /* d_k                                                            */
+  int32_t head_dim_v;   /* d_v                                                            */
+  int32_t qkv_dtype;    /* gdn_dtype_t of q, k, v (core inputs, front-end outputs). BF16   */
+                        /* runs the bf16-MFMA path, F32 the fp32-MFMA path.                */
+  int32_t out_dtype;    /* gdn_dtype_t of o. BF16 output is the round-to-nearest-even cast */
+                        /* of the same fp32 result an F32 output would hold.               */
+  int32_t in_dtype;     /* gdn_dtype_t of the front-end inputs (mixed_qkv, conv weight and */
+                        /* bias, a, b); ignored by the core entry points.                  */
+  float scale;          /* multiplies o; 1.0 for the plain rule o_t = S_t q_t              */
+} gdn_shape_t;
+
+/*
+ * gdn_prepare -- front end of the layer ([MoE report] §3.3 stage 2 and §3.5; [xiwon notes]
+ * "Qwen3_5MoeGatedDeltaNet"; [intro] "线性注意力"). Per channel c of mixed_qkv, a causal
+ * depthwise conv with 4 taps in the nn.Conv1d cross-correlation order (tap 3 multiplies the
+ * current token, tap 0 the token 3 steps back; zero history before each sequence start, so
+ * nothing leaks across cu_seqlens boundaries), plus optional bias, then SiLU(y) = y sigmoid(y).
+ * The channels split into q (H_qk*d_k) | k (H_qk*d_k) | v (H_v*d_v); each q and k head vector
+ * is divided by sqrt(sum of squares + l2norm_eps). Gates: beta = sigmoid(b),
+ * g = -exp(A_log) * softplus(a + dt_bias), computed in fp32.
+ *   mixed_qkv   [T][2*H_qk*d_k + H_v*d_v]  in_dtype
+ *   conv_weight [conv_dim][4]              in_dtype
+ *   conv_bias   [conv_dim] in_dtype, or NULL for no bias
+ *   a, b        [T][H_v]                   in_dtype
+ *   A_log, dt_bias [H_v]                   fp32
+ *   q, k (out)  [T][H_qk][d_k]             qkv_dtype
+ *   v    (out)  [T][H_v][d_v]              qkv_dtype
+ *   g, beta (out) [T][H_v]                 fp32 (g is the log-decay, <= 0)
+ */
+gdn_status_t gdn_prepare(const gdn_shape_t* shape, const int32_t* cu_seqlens,
+                         const void* mixed_qkv, const void* conv_weight, const void* conv_bias,
+                         const void* a, const void* b, const float* A_log,
+                         const float* dt_bias, float l2norm_eps, void* q, void* k, void* v,
+                         float* g, float* beta, void* stream);
+
+/* Bytes of device workspace gdn_chunk_forward needs for this shape (0 on a bad shape). The
+ * bound uses total_tokens and num_seqs only: (num_seqs + total_tokens / 64) chunk slots times
+ * H_v times 24832 bytes. */
+size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
+
+/*
+ * gdn_chunk_forward -- chunked prefill, chunk length 64 ([MoE report] §3.7 Steps 2-7, the
+ * WY/UT form of the recurrence above). Sequences are cut into chunks of 64 tokens that never
+ * straddle a sequence; a short tail chunk behaves as if padded with identity steps
+ * (q = k = v = 0, beta = 0, g = 0). The result equals the token recurrence up to rounding.
+ *   q, k          [T][H_qk][d_k] qkv_dtype     v [T][H_v][d_v] qkv_dtype
+ *   g, beta       [T][H_v] fp32
+ *   initial_state [N][H_v][d_k][d_v] fp32, or NULL for zeros
+ *   o (out)       [T][H_v][d_v] out_dtype
+ *   final_state   [N][H_v][d_k][d_v] fp32 (out), or NULL; it may equal initial_state
+ *   workspace     >= gdn_chunk_forward_workspace_size(shape) bytes, 256-byte aligned,
+ *                 caller-owned scratch; its contents on entry do not matter.
+ * It runs gdn_chunk_intra then gdn_chunk_scan on `stream`.
+ */
+gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqlens,
+                               const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* initial_state, void* o,
+                               float* final_state, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The two stages of gdn_chunk_forward, exported so that they can be timed or overlapped
+ * separately. gdn_chunk_intra computes everything that does not depend on the state
+ * ([MoE report] §3.7 Steps 3-4: the in-chunk decay cumsum, the decayed beta*K K^T, the
+ * unit-lower-triangular inverse (I + A)^-1 and the masked decayed Q K^T) into the workspace.
+ * gdn_chunk_scan then runs the sequential cross-chunk recurrence (Steps 5-7) from it. The
+ * workspace contents between the two calls are private to the library; scan must use the same
+ * shape, cu_seqlens, q, k, g and beta as the intra call that filled it.
+ */
+gdn_status_t gdn_chunk_intra(const gdn_shape_t* shape, const int32_t* cu_seqlens,
+                             const void* q, const void* k, const float* g, const float* beta,
+                             void* workspace, size_t workspace_bytes, void* stream);
+gdn_status_t gdn_chunk_scan(const gdn_shape_t* shape, const int32_t* cu_seqlens,
+                            const void* q, const void* k, const void* v,
+                            const float* initial_state, void* o, float* final_state,
+                            const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_recurrent_step -- one decode token per sequence ([MoE report] §3.3 stage 3 decode;
+ * [xiwon notes] "Qwen3_5MoeGatedDeltaNet" recurrent branch and "Cache": the state is read,
+ * updated once and written back in place). Requires total_tokens == num_seqs.
+ *   q, k  [N][H_qk][d_k] qkv_dtype     v [N][H_v][d_v] qkv_dtype
+ *   g, beta [N][H_v] fp32
+ *   state [N][H_v][d_k][d_v] fp32, read and overwritten with the new state
+ *   o (out) [N][H_v][d_v] out_dtype
+ */
+gdn_status_t gdn_recurrent_step(const gdn_shape_t* shape, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                float* state, void* o, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gdn_status_string(gdn_status_t status);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

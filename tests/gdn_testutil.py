@@ -1,0 +1,63 @@
+"""Helpers shared by the GPU parity tests: oracle runs on whole cases or on sampled
+(sequence, V head) chains, and the tolerance check max|err| <= tol * RMS(reference)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+# Tolerances: fp32 inputs 1e-4 * RMS, bf16 inputs 2e-2 * RMS, on outputs and final states.
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def f64(t):
+    return None if t is None else t.detach().double().cpu().numpy()
+
+
+def rel_err(got, ref) -> float:
+    got = f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    return err / rms if rms > 0 else err
+
+
+def assert_rms_close(got, ref, tol, what):
+    e = rel_err(got, ref)
+    print(f"  {what}: max|err| = {e:.3e} x RMS (tol {tol:g})", flush=True)
+    assert e <= tol, f"{what}: max|err| = {e:.3e} x RMS > {tol:g}"
+
+
+def oracle_case(case):
+    """float64 oracle on a whole CoreCase."""
+    return oracle.recurrent(f64(case.q), f64(case.k), f64(case.v), f64(case.g), f64(case.beta),
+                            case.cu_seqlens.numpy(), initial_state=f64(case.h0))
+
+
+def oracle_chains(case, chains):
+    """float64 oracle on chosen (sequence n, V head h) chains only.
+
+    Returns {(n, h): (o [L, d_v], final [d_k, d_v])}."""
+    cu = case.cu_seqlens.numpy().astype(np.int64)
+    hv = case.v.shape[1]
+    G = hv // case.q.shape[1]
+    out = {}
+    for n, h in chains:
+        s, e = int(cu[n]), int(cu[n + 1])
+        m = h // G
+        q = f64(case.q[s:e, m:m + 1])
+        k = f64(case.k[s:e, m:m + 1])
+        v = f64(case.v[s:e, h:h + 1])
+        g = f64(case.g[s:e, h:h + 1])
+        b = f64(case.beta[s:e, h:h + 1])
+        h0 = None if case.h0 is None else f64(case.h0[n:n + 1, h:h + 1])
+        o, ht = oracle.recurrent(q, k, v, g, b, [0, e - s], initial_state=h0)
+        out[(n, h)] = (o[:, 0], ht[0, 0])
+    return out
+
+
+def to_dev(case, dev="cuda"):
+    return {k: (None if getattr(case, k) is None else getattr(case, k).to(dev))
+            for k in ("q", "k", "v", "g", "beta", "cu_seqlens", "h0")}

@@ -1,0 +1,149 @@
+"""Host-side checks of libgdn.so that need no GPU: every symbol include/gdn.h declares is
+exported, and every validation error path returns its status code before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_linear_amd as gdn
+from gated_deltanet_linear_amd import GdnShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.library_path()):
+        pytest.fail("libgdn.so not built: run __graft_entry__.build() first")
+    return gdn._load()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert {"gdn_prepare", "gdn_chunk_forward", "gdn_recurrent_step"} <= set(names)
+    raw = ctypes.CDLL(gdn.library_path())
+    for name in names:
+        assert hasattr(raw, name), f"libgdn.so does not export {name}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    for code in range(5):
+        assert lib.gdn_status_string(code).startswith(b"GDN_")
+
+
+def _shape(**kw):
+    base = dict(num_seqs=2, total_tokens=300, num_qk_heads=16, num_v_heads=32, head_dim_k=128,
+                head_dim_v=128, qkv_dtype=1, out_dtype=1, in_dtype=1, scale=1.0)
+    base.update(kw)
+    return GdnShape(**base)
+
+
+def test_workspace_size_formula(lib):
+    s = _shape()
+    expect = (2 + 300 // 64) * 32 * 24832
+    assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(s)) == expect
+    assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(_shape(num_v_heads=33))) == 0
+    assert lib.gdn_chunk_forward_workspace_size(None) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: calls below fail validation first
+
+
+def _chunk(lib, s, ws_bytes=1 << 40, q=FAKE, ws=FAKE, cu=FAKE):
+    return lib.gdn_chunk_forward(ctypes.byref(s) if s is not None else None, cu, q, FAKE, FAKE,
+                                 FAKE, FAKE, None, FAKE, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_v_heads=33), INVALID),
+    (dict(num_seqs=0), INVALID),
+    (dict(total_tokens=-1), INVALID),
+    (dict(qkv_dtype=7), INVALID),
+    (dict(out_dtype=-1), INVALID),
+    (dict(head_dim_k=0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(head_dim_k=96, head_dim_v=96), UNSUPPORTED),
+    (dict(head_dim_k=128, head_dim_v=64), UNSUPPORTED),
+    (dict(total_tokens=1 << 30, num_v_heads=64, num_qk_heads=16), UNSUPPORTED),
+])
+def test_chunk_forward_rejects_bad_shapes(lib, kw, code):
+    assert _chunk(lib, _shape(**kw)) == code
+
+
+def test_chunk_forward_rejects_bad_pointers_and_workspace(lib):
+    s = _shape()
+    assert _chunk(lib, None) == INVALID
+    assert _chunk(lib, s, cu=None) == INVALID
+    assert _chunk(lib, s, q=None) == INVALID
+    assert _chunk(lib, s, q=ctypes.c_void_p((1 << 20) + 2)) == INVALID  # misaligned
+    assert _chunk(lib, s, ws=ctypes.c_void_p((1 << 20) + 64)) == INVALID  # ws not 256-aligned
+    need = lib.gdn_chunk_forward_workspace_size(ctypes.byref(s))
+    assert _chunk(lib, s, ws_bytes=need - 1) == WS_SMALL
+    assert lib.gdn_chunk_intra(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
+                               None) == INVALID
+    assert lib.gdn_chunk_scan(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE,
+                              1 << 40, None) == INVALID
+    assert lib.gdn_chunk_scan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                              need - 1, None) == WS_SMALL
+
+
+def test_recurrent_step_validation(lib):
+    s = _shape(total_tokens=2)
+    args = [FAKE] * 7
+    assert lib.gdn_recurrent_step(ctypes.byref(_shape(total_tokens=3)), *args, None) == INVALID
+    for i in range(7):
+        a = list(args)
+        a[i] = None
+        assert lib.gdn_recurrent_step(ctypes.byref(s), *a, None) == INVALID
+    a = list(args)
+    a[5] = ctypes.c_void_p((1 << 20) + 4)  # state must be 16-byte aligned
+    assert lib.gdn_recurrent_step(ctypes.byref(s), *a, None) == INVALID
+    assert lib.gdn_recurrent_step(ctypes.byref(_shape(total_tokens=2, head_dim_k=48,
+                                                      head_dim_v=48)), *args, None) == UNSUPPORTED
+
+
+def test_prepare_validation(lib):
+    s = _shape()
+    good = [FAKE] * 8  # cu, x, w, bias, a, b, A_log, dt_bias
+    outs = [FAKE] * 5
+
+    def call(shape, ins, eps, o):
+        return lib.gdn_prepare(ctypes.byref(shape), *ins, eps, *o, None)
+
+    assert call(_shape(in_dtype=5), good, 1e-6, outs) == INVALID
+    assert call(s, good, -1.0, outs) == INVALID
+    assert call(s, good, float("nan"), outs) == INVALID
+    for i in (0, 1, 2, 4, 5, 6, 7):  # every input except the optional bias
+        ins = list(good)
+        ins[i] = None
+        assert call(s, ins, 1e-6, outs) == INVALID
+    for i in range(5):
+        o = list(outs)
+        o[i] = None
+        assert call(s, good, 1e-6, o) == INVALID
+    ins = list(good)
+    ins[1] = ctypes.c_void_p((1 << 20) + 8)  # mixed_qkv must be 16-byte aligned
+    assert call(s, ins, 1e-6, outs) == INVALID
+    assert call(_shape(head_dim_k=16, head_dim_v=16), good, 1e-6, outs) == UNSUPPORTED
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(4, 1, 32)
+    g = torch.zeros(4, 1)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(gdn.GdnError):
+        gdn.chunk_forward(x, x, x, g, g, cu)
+    with pytest.raises(gdn.GdnError):
+        gdn.recurrent_step(x, x, x, g, g, torch.zeros(4, 1, 32, 32))

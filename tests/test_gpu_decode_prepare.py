@@ -1,0 +1,169 @@
+"""GPU parity of gdn_recurrent_step (decode) and gdn_prepare (front end) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_linear_amd as gdn
+import oracle
+import synthetic_inputs as si
+from gdn_testutil import TOL, assert_rms_close, f64, oracle_case, oracle_chains, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("d,dtype", [(32, "f32"), (64, "bf16"), (128, "bf16"), (128, "f32")])
+def test_recurrent_step_small(d, dtype):
+    case = si.make_core_case([1] * 12, 2, 6, d, d, dtype=dtype, gate="model", h0_std=0.5,
+                             seed=d + len(dtype))
+    print(f"[decode] d={d} {dtype}", flush=True)
+    dd = to_dev(case)
+    state = dd["h0"].clone()
+    o = gdn.recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state,
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_case(case)
+    assert_rms_close(o, o_ref, TOL[dtype], "decode o")
+    assert_rms_close(state, s_ref, TOL[dtype], "decode state")
+
+
+def test_recurrent_step_decode_workload_full():
+    """Workload 4 at full size: 256 sequences x 1 token, 16/32 heads, d = 128, 537 MB state."""
+    case = si.workload_case(4)
+    dd = to_dev(case)
+    state = dd["h0"].clone()
+    o16 = gdn.recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state)
+    state32 = dd["h0"].clone()
+    o32 = gdn.recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state32,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))  # bf16 output = RNE of the fp32 output
+    assert torch.equal(state, state32)
+    o_ref, s_ref = oracle_case(case)
+    assert_rms_close(o32, o_ref, TOL["bf16"], "decode workload o")
+    assert_rms_close(state32, s_ref, TOL["bf16"], "decode workload state")
+
+
+def test_decode_steps_equal_chunked_prefill():
+    """T decode steps on the GPU ~ one chunked prefill of the same T tokens (both vs oracle)."""
+    case = si.slow_decay_case([70], 1, 2, 128, 128, dtype="bf16", seed=4)
+    dd = to_dev(case)
+    state = dd["h0"].clone()
+    outs = []
+    for t in range(70):
+        sl = slice(t, t + 1)
+        outs.append(gdn.recurrent_step(dd["q"][sl], dd["k"][sl], dd["v"][sl], dd["g"][sl],
+                                       dd["beta"][sl], state, out_dtype=torch.float32))
+    oc, hc = gdn.chunk_forward(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["cu_seqlens"],
+                               initial_state=dd["h0"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle_case(case)
+    assert_rms_close(torch.cat(outs), o_ref, TOL["bf16"], "decode x70 o")
+    assert_rms_close(state, h_ref, TOL["bf16"], "decode x70 state")
+    assert_rms_close(oc, f64(torch.cat(outs)), 2 * TOL["bf16"], "chunk vs decode o")
+
+
+def _prep_case(lengths, d=32, hqk=2, hv=4, seed=0, dtype="bf16", bias=False):
+    fc = si.make_front_case(lengths, hqk, hv, d, d, dtype=dtype, seed=seed)
+    if bias:
+        rng = np.random.default_rng(seed + 1)
+        fc.meta["bias"] = si._round(rng.standard_normal(fc.conv_weight.shape[0]) * 0.1,
+                                    fc.conv_weight.dtype)
+    return fc
+
+
+def _prep_gpu(fc, qkv_dtype=None, bias=None):
+    dev = "cuda"
+    return gdn.prepare(fc.mixed_qkv.to(dev), fc.conv_weight.to(dev), fc.a.to(dev), fc.b.to(dev),
+                       fc.A_log.to(dev), fc.dt_bias.to(dev), fc.cu_seqlens.to(dev),
+                       fc.meta["hqk"], fc.meta["dk"], fc.meta["hv"], fc.meta["dv"],
+                       conv_bias=None if bias is None else bias.to(dev), qkv_dtype=qkv_dtype)
+
+
+def _prep_oracle(fc, bias=None):
+    return oracle.prepare(f64(fc.mixed_qkv), f64(fc.conv_weight), f64(fc.a), f64(fc.b),
+                          f64(fc.A_log), f64(fc.dt_bias), fc.cu_seqlens.numpy(), fc.meta["hqk"],
+                          fc.meta["dk"], fc.meta["hv"], fc.meta["dv"], conv_bias=f64(bias))
+
+
+def _check_prepare(got, ref, out_dtype):
+    # q, k, v: one rounding to the output dtype after fp32 math; g, beta in fp32.
+    rt = 2.0 ** -8 if out_dtype == torch.bfloat16 else 1e-5
+    names = ("q", "k", "v", "g", "beta")
+    for gt, rf, nm in zip(got, ref, names):
+        gt = f64(gt)
+        bound = (rt if nm in "qkv" else 1e-5) * np.abs(rf) + 1e-6
+        bad = np.abs(gt - rf) > bound
+        assert not bad.any(), f"prepare {nm}: {bad.sum()} elements off, worst " \
+            f"{np.max(np.abs(gt - rf) - bound):.3e}"
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("qkv", [torch.bfloat16, torch.float32])
+def test_prepare_small(d, qkv):
+    fc = _prep_case([5, 0, 1, 300, 3, 260], d=d, seed=d)
+    print(f"[prepare] d={d} qkv={qkv}", flush=True)
+    got = _prep_gpu(fc, qkv_dtype=qkv)
+    torch.cuda.synchronize()
+    _check_prepare(got, _prep_oracle(fc), qkv)
+
+
+def test_prepare_with_bias_fp32_inputs():
+    fc = _prep_case([40, 17], d=64, dtype="f32", seed=3, bias=True)
+    got = _prep_gpu(fc, qkv_dtype=torch.float32, bias=fc.meta["bias"])
+    torch.cuda.synchronize()
+    _check_prepare(got, _prep_oracle(fc, bias=fc.meta["bias"]), torch.float32)
+
+
+def test_front_end_workload_stagewise_and_end_to_end():
+    """Workload 5 (8 packed sequences, 16/64 heads, d = 128): the front end against the
+    oracle's front end, the core on the front end's bf16 outputs against the oracle core on
+    the same values (sampled chains), and the whole path with fp32 intermediates against the
+    float64 front end + core (sampled chains)."""
+    fc = si.workload_case(5)
+    print(f"[front] lengths={fc.meta['lengths']}", flush=True)
+    dev = "cuda"
+    q, k, v, g, beta = _prep_gpu(fc, qkv_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = _prep_oracle(fc)
+    _check_prepare((q, k, v, g, beta), ref, torch.bfloat16)
+
+    h0 = fc.h0.to(dev)
+    cu = fc.cu_seqlens.to(dev)
+    o, ht = gdn.chunk_forward(q, k, v, g, beta, cu, initial_state=h0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    core = si.CoreCase(q=q.cpu(), k=k.cpu(), v=v.cpu(), g=g.cpu(), beta=beta.cpu(),
+                       cu_seqlens=fc.cu_seqlens, h0=fc.h0, meta=fc.meta)
+    rng = np.random.default_rng(5)
+    chains = [(int(n), int(h)) for n, h in zip(rng.integers(0, 8, 6), rng.integers(0, 64, 6))]
+    cu_np = fc.cu_seqlens.numpy()
+    refs = oracle_chains(core, chains)
+    got_o = np.concatenate([f64(o[cu_np[n]:cu_np[n + 1], h]) for n, h in chains])
+    ref_o = np.concatenate([refs[c][0] for c in chains])
+    assert_rms_close(got_o, ref_o, TOL["bf16"], "front workload core o (sampled)")
+    assert_rms_close(np.stack([f64(ht[n, h]) for n, h in chains]),
+                     np.stack([refs[c][1] for c in chains]), TOL["bf16"],
+                     "front workload core final state (sampled)")
+
+    # fp32 intermediates: compare with float64 front end + float64 core.
+    q32, k32, v32, g32, b32 = _prep_gpu(fc, qkv_dtype=torch.float32)
+    o32, ht32 = gdn.chunk_forward(q32, k32, v32, g32, b32, cu, initial_state=h0,
+                                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rq, rk, rv, rg, rb = ref
+    cu64 = cu_np.astype(np.int64)
+    e2e_o, e2e_ref, e2e_h, e2e_href = [], [], [], []
+    for n, h in chains[:3]:
+        s, e = cu64[n], cu64[n + 1]
+        m = h // 4
+        oo, hh = oracle.recurrent(rq[s:e, m:m + 1], rk[s:e, m:m + 1], rv[s:e, h:h + 1],
+                                  rg[s:e, h:h + 1], rb[s:e, h:h + 1], [0, e - s],
+                                  initial_state=f64(fc.h0[n:n + 1, h:h + 1]))
+        e2e_o.append(f64(o32[s:e, h]))
+        e2e_ref.append(oo[:, 0])
+        e2e_h.append(f64(ht32[n, h]))
+        e2e_href.append(hh[0, 0])
+    assert_rms_close(np.concatenate(e2e_o), np.concatenate(e2e_ref), TOL["bf16"],
+                     "front workload end-to-end o, fp32 intermediates (sampled)")
+    assert_rms_close(np.stack(e2e_h), np.stack(e2e_href), TOL["bf16"],
+                     "front workload end-to-end final state, fp32 intermediates (sampled)")
