@@ -12,50 +12,18 @@
 // V' is the page's v_new written with T diag(beta) applied to V - gamma K H0 instead of
 // forming W = T diag(beta gamma) K: the same product, and W is never stored.
 //
-// Two kernels:
-//   chunk_intra: one workgroup per (chunk slot, QK head), fully chunk-parallel. Forms K K^T and
-//     Q K^T once per QK head on MFMA, then for each of its G V heads the cumsum, A, the
-//     inverse T (16x16 diagonal blocks by substitution, off-diagonal blocks by two levels of
-//     16x16 fp32 MFMA products) and P, and writes T diag(beta), P (as ready-made MFMA A
-//     fragments) and b to the workspace.
-//   chunk_scan: one workgroup per (sequence, V head, group of 16-column d_v tiles); each wave
-//     keeps its [d_k x 16] fp32 slice of the state in registers for the whole sequence and
-//     walks the chunks in order. d_v columns of the state evolve independently (column j
-//     depends only on column j of v), which is what lets the scan split over d_v.
+// This file holds the chunk-parallel half, chunk_intra: one workgroup per (chunk slot, V
+// head). It forms K K^T and the masked decayed Q K^T on MFMA (the decay and beta applied on
+// the fly to the result fragments), inverts the unit-lower-triangular I + A (16x16 diagonal
+// blocks by substitution, off-diagonal blocks by two levels of 16x16 fp32 MFMA products) and
+// writes T diag(beta), P (as ready-made MFMA A fragments), e^{b_t} and e^{b_C - b_t} to the
+// workspace. The sequential half, chunk_scan, is in gdn_scan.hip.
 #include "gdn_device.hpp"
 #include "gdn_internal.h"
 
 namespace gdn {
 static_assert(kWsRecordBytes == kWorkspaceRecordBytes, "workspace record size");
 namespace {
-
-// ---------------------------------------------------------------------------------------
-// Operand-fragment loads straight from q/k in global memory (row-major [T][H_qk][DK]).
-// Lane (idx, grp) of a 32-deep A fragment of rows r0.. reads K[r0 + idx][32 kb + kslot].
-// ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void load_frag_row(const bf16* row, int kb, int grp, bf16x8& f) {
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * kb + 4 * grp);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * kb + 16 + 4 * grp);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    f[s] = lo[s];
-    f[4 + s] = hi[s];
-  }
-}
-__device__ __forceinline__ void load_frag_row(const float* row, int kb, int grp, f32x8& f) {
-  const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 32 * kb + 4 * grp);
-  const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 32 * kb + 16 + 4 * grp);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    f[s] = lo[s];
-    f[4 + s] = hi[s];
-  }
-}
-template <typename F>
-__device__ __forceinline__ void zero_frag(F& f) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) f[s] = 0;
-}
 
 // 16x16x16 fp32 product on MFMA with the 16-deep version of the fragment convention:
 // A from LDS (row-major, leading dim ld), B either from LDS or from a C fragment in registers.
@@ -93,374 +61,227 @@ struct IntraParams {
   int num_seqs, hqk, hv;
 };
 
+template <typename Mode, int ROWB>
+__device__ __forceinline__ typename Mode::frag_t row_frag(const char* buf, int row, int kb, int grp);
+template <>
+__device__ __forceinline__ bf16x8 row_frag<Bf16Mode, 64>(const char* b, int r, int kb, int g) {
+  return afrag<64>(b, r, kb, g);
+}
+template <>
+__device__ __forceinline__ bf16x8 row_frag<Bf16Mode, 128>(const char* b, int r, int kb, int g) {
+  return afrag<128>(b, r, kb, g);
+}
+template <>
+__device__ __forceinline__ bf16x8 row_frag<Bf16Mode, 256>(const char* b, int r, int kb, int g) {
+  return afrag<256>(b, r, kb, g);
+}
+template <>
+__device__ __forceinline__ f32x8 row_frag<F32Mode, 128>(const char* b, int r, int kb, int g) {
+  return afrag_f32<128>(b, r, kb, g);
+}
+template <>
+__device__ __forceinline__ f32x8 row_frag<F32Mode, 256>(const char* b, int r, int kb, int g) {
+  return afrag_f32<256>(b, r, kb, g);
+}
+template <>
+__device__ __forceinline__ f32x8 row_frag<F32Mode, 512>(const char* b, int r, int kb, int g) {
+  return afrag_f32<512>(b, r, kb, g);
+}
+
+// Half fragment (slots 4*half .. +3) of a stored operand block in global memory, split like
+// Mode::make.
+__device__ __forceinline__ void store_half_global(Bf16Mode, char* blk, int lane, int half,
+                                                  const f32x4& x) {
+  bf16x4 hi, lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = (bf16)x[e];
+    lo[e] = (bf16)(x[e] - (float)hi[e]);
+  }
+  *reinterpret_cast<bf16x4*>(blk + lane * 16 + half * 8) = hi;
+  *reinterpret_cast<bf16x4*>(blk + 1024 + lane * 16 + half * 8) = lo;
+}
+__device__ __forceinline__ void store_half_global(F32Mode, char* blk, int lane, int half,
+                                                  const f32x4& x) {
+  *reinterpret_cast<f32x4*>(blk + lane * 32 + half * 16) = x;
+}
+
+// One workgroup per (chunk slot, V head). K K^T and Q K^T of the chunk's QK head are formed
+// again for every V head that shares it: ~1 MFLOP per chunk, noise next to the scan, and it
+// makes every workgroup independent.
 template <typename Mode, int DK>
 __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
   using in_t = typename Mode::in_t;
   using frag_t = typename Mode::frag_t;
   constexpr int KB = DK / 32;
+  constexpr int ROWB = DK * (int)sizeof(in_t), KBYTES = 64 * ROWB;
+  constexpr int TBYTES = 64 * kLd * 4;
+  constexpr int SBYTES = 2 * KBYTES > TBYTES ? 2 * KBYTES : TBYTES;
 
-  __shared__ float sKK[64 * kLd];
-  __shared__ float sQK[64 * kLd];
+  // Staged q/k rows; after the K K^T / Q K^T phase the same bytes hold T.
+  __shared__ __attribute__((aligned(1024))) char sKQ[SBYTES];
   __shared__ float sA[64 * kLd];
-  __shared__ float sT[64 * kLd];
   __shared__ float sb[64];
   __shared__ float sbeta[64];
+  float* sT = reinterpret_cast<float*>(sKQ);
 
-  const int slot = blockIdx.x, m = blockIdx.y;
+  const int slot = blockIdx.x, h = blockIdx.y;
   const int n = slot_to_seq(p.cu, p.num_seqs, slot);
   const int t0 = p.cu[n] + kChunk * (slot - slot_base(p.cu, n));
   const int tend = p.cu[n + 1];
   if (t0 >= tend) return;  // unused slot (uniform over the workgroup)
   const int len = min(kChunk, tend - t0);
-  const int G = p.hv / p.hqk;
+  const int m = h / (p.hv / p.hqk);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, idx = lane & 15,
             grp = lane >> 4;
-  const in_t* Q = static_cast<const in_t*>(p.q);
-  const in_t* K = static_cast<const in_t*>(p.k);
   const size_t rstride = (size_t)p.hqk * DK;
-  const in_t* Qc = Q + (size_t)t0 * rstride + (size_t)m * DK;
-  const in_t* Kc = K + (size_t)t0 * rstride + (size_t)m * DK;
+  char* rec = p.ws + ((size_t)slot * p.hv + h) * kWsRecordBytes;
 
-  // ---- K K^T and Q K^T, lower 16x16 tiles incl. the diagonal: 10 + 10 tiles, 5 per wave.
-  for (int tile = wave; tile < 20; tile += 4) {
-    const bool isq = tile >= 10;
-    const int tt = isq ? tile - 10 : tile;
-    const int tr = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
-    const int tc = tt - tr * (tr + 1) / 2;
-    const int ra = 16 * tr + idx, rb = 16 * tc + idx;
-    const in_t* rowa = (isq ? Qc : Kc) + (size_t)ra * rstride;
-    const in_t* rowb = Kc + (size_t)rb * rstride;
+  // ---- all memory reads at once: q/k rows (async into LDS) and this head's gates
+  stage_rows<in_t, DK, 4>(sKQ, static_cast<const in_t*>(p.k), static_cast<const in_t*>(p.q), t0,
+                          len, rstride, m, wave, lane);
+  float gv = 0.f, bv = 0.f;
+  if (wave == 0 && lane < len) {
+    gv = p.g[(size_t)(t0 + lane) * p.hv + h];
+    bv = p.beta[(size_t)(t0 + lane) * p.hv + h];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  if (wave == 0) {
+    const float cs = wave_inclusive_scan(gv, lane);
+    const float cl = __shfl(cs, kChunk - 1, kWave);  // b_C (identity steps keep it at b_{len-1})
+    sb[lane] = cs;
+    sbeta[lane] = bv;
+    reinterpret_cast<float*>(rec + kWsGOff)[lane] = __expf(cs);
+    reinterpret_cast<float*>(rec + kWsDOff)[lane] = __expf(cl - cs);
+  }
+  lds_barrier();
+
+  // ---- 22 tile jobs, round robin over the waves:
+  //   0..9   A tiles (tr >= tc): A_tj = beta_t e^{b_t - b_j} (k_t . k_j) for j < t, into LDS;
+  //   10..19 P^T tiles: C = K_ct Q_rt^T, whose C fragment IS half of the stored A fragment of
+  //          P = (Q K^T) o Gamma o lower-incl (block (rt, ct / 2), slots 4 (ct % 2) + r);
+  //   20, 21 the zero halves of the diagonal P blocks (ct = rt + 1 for rt = 0, 2).
+  const char* sK = sKQ;
+  const char* sQ = sKQ + KBYTES;
+  for (int job = wave; job < 22; job += 4) {
+    if (job >= 20) {
+      const int rt = job == 20 ? 0 : 2;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      store_half_global(Mode{}, rec + kWsPOff + tri_block(rt, rt / 2) * kWsBlockBytes, lane, 1, z);
+      continue;
+    }
+    const bool isp = job >= 10;
+    const int tt = isp ? job - 10 : job;
+    const int r1 = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // row tile
+    const int r2 = tt - r1 * (r1 + 1) / 2;                        // column tile (<= r1)
+    // A tiles: rows r1 of K against rows r2 of K.  P^T tiles: rows r2 of K against rows r1 of Q.
+    const int ra = isp ? 16 * r2 + idx : 16 * r1 + idx;
+    const int rb = isp ? 16 * r1 + idx : 16 * r2 + idx;
+    const char* bsrc = isp ? sQ : sK;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      frag_t a, b;
-      if (ra < len) load_frag_row(rowa, kb, grp, a); else zero_frag(a);
-      if (rb < len) load_frag_row(rowb, kb, grp, b); else zero_frag(b);
+      frag_t a = row_frag<Mode, ROWB>(sK, ra, kb, grp);
+      frag_t b = row_frag<Mode, ROWB>(bsrc, rb, kb, grp);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        a[s] = ra < len ? a[s] : (in_t)0.f;
+        b[s] = rb < len ? b[s] : (in_t)0.f;
+      }
       acc = mma32(a, b, acc);
     }
-    float* dst = isq ? sQK : sKK;
+    if (!isp) {
+      const int j = 16 * r2 + idx;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * tr + 4 * grp + r) * kLd + 16 * tc + idx] = acc[r];
-  }
-
-  for (int gg = 0; gg < G; ++gg) {
-    const int h = m * G + gg;
-    char* rec = p.ws + ((size_t)slot * p.hv + h) * kWsRecordBytes;
-    __syncthreads();  // K K^T / Q K^T ready; previous head done with sA, sT, sb
-    if (wave == 0) {
-      const float gv = lane < len ? p.g[(size_t)(t0 + lane) * p.hv + h] : 0.f;
-      const float bv = lane < len ? p.beta[(size_t)(t0 + lane) * p.hv + h] : 0.f;
-      const float cs = wave_inclusive_scan(gv, lane);
-      sb[lane] = cs;
-      sbeta[lane] = bv;
-      reinterpret_cast<float*>(rec + kWsBOff)[lane] = cs;
-    }
-    __syncthreads();
-    // A = strictly-lower(beta_t e^{b_t - b_j} KK_tj); the exponent is <= 0 wherever used.
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int t = e >> 6, j = e & 63;
-      sA[t * kLd + j] = j < t ? sbeta[t] * expf(sb[t] - sb[j]) * sKK[t * kLd + j] : 0.f;
-    }
-    __syncthreads();
-    // Diagonal 16x16 blocks of T: wave w inverts block w by forward substitution, lane c < 16
-    // carrying column c. x_i = delta_ic - sum_{j<i} A_ij x_j.
-    if (lane < 16) {
-      const float* Ab = sA + (16 * wave) * kLd + 16 * wave;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < i; ++j) acc = fmaf(Ab[i * kLd + j], x[j], acc);
-        x[i] = (i == lane) ? 1.f : -acc;
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * r1 + 4 * grp + r;
+        sA[t * kLd + j] = j < t ? sbeta[t] * __expf(sb[t] - sb[j]) * acc[r] : 0.f;
       }
+    } else {
+      const int t = 16 * r1 + idx;
+      f32x4 pv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * r2 + 4 * grp + r;
+        pv[r] = j <= t ? __expf(sb[t] - sb[j]) * acc[r] : 0.f;
+      }
+      store_half_global(Mode{}, rec + kWsPOff + tri_block(r1, r2 >> 1) * kWsBlockBytes, lane,
+                        r2 & 1, pv);
+    }
+  }
+  lds_barrier();  // sA complete; staged rows no longer needed (sT may overwrite them)
+
+  // ---- Diagonal 16x16 blocks of T: wave w inverts block w by forward substitution,
+  // x_i = delta_ic - sum_{j<i} A_ij x_j with lane c < 16 carrying column c. Lane i holds row i
+  // of the block; v_readlane broadcasts A_ij as a scalar operand (no LDS traffic in the loop).
+  {
+    const float* Ab = sA + (16 * wave) * kLd + 16 * wave;
+    float arow[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) arow[j] = Ab[(lane & 15) * kLd + j];
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j)
+        acc = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                       __builtin_bit_cast(int, arow[j]), i)),
+                   x[j], acc);
+      x[i] = (i == lane) ? 1.f : -acc;
+    }
+    if (lane < 16) {
       float* Tb = sT + (16 * wave) * kLd + 16 * wave;
 #pragma unroll
       for (int i = 0; i < 16; ++i) Tb[i * kLd + lane] = x[i];
     }
-    __syncthreads();
-    // Level 2: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22.
-    if (wave < 2) {
-      const int ib = 2 * wave + 1, jb = 2 * wave;
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 M = mm16_ll(sA + 16 * ib * kLd + 16 * jb, sT + 16 * jb * kLd + 16 * jb, z, idx, grp);
-      f32x4 R = mm16_lr(sT + 16 * ib * kLd + 16 * ib, M, z, idx, grp);
-      store_c16(sT + 16 * ib * kLd + 16 * jb, R, idx, grp, -1.f);
-    }
-    __syncthreads();
-    // Level 3, column block jb in {0, 1} (wave jb):
-    //   X_i = sum_{kb=jb..1} A_{i,kb} T_{kb,jb} (i = 2, 3)
-    //   T_{2,jb} = -T_22 X_2,  T_{3,jb} = -(T_32 X_2 + T_33 X_3)
-    if (wave < 2) {
-      const int jb = wave;
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 X2 = z, X3 = z;
-      for (int kb = jb; kb < 2; ++kb) {
-        const float* Tk = sT + 16 * kb * kLd + 16 * jb;
-        X2 = mm16_ll(sA + 32 * kLd + 16 * kb, Tk, X2, idx, grp);
-        X3 = mm16_ll(sA + 48 * kLd + 16 * kb, Tk, X3, idx, grp);
-      }
-      f32x4 T2 = mm16_lr(sT + 32 * kLd + 32, X2, z, idx, grp);
-      f32x4 T3 = mm16_lr(sT + 48 * kLd + 32, X2, z, idx, grp);
-      T3 = mm16_lr(sT + 48 * kLd + 48, X3, T3, idx, grp);
-      store_c16(sT + 32 * kLd + 16 * jb, T2, idx, grp, -1.f);
-      store_c16(sT + 48 * kLd + 16 * jb, T3, idx, grp, -1.f);
-    }
-    __syncthreads();
-    // Write T diag(beta) and P as A fragments: 2 matrices x 6 blocks x 64 lanes.
-    for (int it = tid; it < 2 * 6 * 64; it += 256) {
-      const int mat = it / 384, bi = (it / 64) % 6, ln = it & 63;
-      const int rt = bi < 2 ? bi : 2 + (bi - 2) / 2;
-      const int kb = bi < 2 ? 0 : (bi - 2) % 2;
-      const int i = ln & 15, gr = ln >> 4;
-      const int t = 16 * rt + i;
-      float x[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int j = 32 * kb + kslot(gr, s);
-        float val = 0.f;
-        if (j <= t) {
-          val = mat == 0 ? sT[t * kLd + j] * sbeta[j]
-                         : expf(sb[t] - sb[j]) * sQK[t * kLd + j];
-        }
-        x[s] = val;
-      }
-      char* blk = rec + (mat == 0 ? kWsTOff : kWsPOff) + bi * kWsBlockBytes;
-      Mode::store_block(blk, ln, Mode::make(x));
-    }
   }
-}
-
-// ---------------------------------------------------------------------------------------
-// Scan kernel.
-// ---------------------------------------------------------------------------------------
-struct ScanParams {
-  const int32_t* cu;
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* h0;
-  void* o;
-  float* ht;
-  const char* ws;
-  int num_seqs, hqk, hv;
-  float scale;
-};
-
-// Writes 4 consecutive slots of a fragment in LDS with one 8- or 16-byte store (never a
-// read-modify-write of the whole fragment, which would race with the thread that owns the
-// other 4 slots).
-__device__ __forceinline__ void put4(bf16x8* f, int s0, const float* x) {
-  bf16x4 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
-  *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(f) + s0) = v;
-}
-__device__ __forceinline__ void put4(f32x8* f, int s0, const float* x) {
-  f32x4 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = x[e];
-  *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(f) + s0) = v;
-}
-__device__ __forceinline__ void put1(bf16x8* f, int s, float x) {
-  reinterpret_cast<bf16*>(f)[s] = (bf16)x;
-}
-__device__ __forceinline__ void put1(f32x8* f, int s, float x) { reinterpret_cast<float*>(f)[s] = x; }
-
-template <typename Mode, int DK, int DV, int NW, typename OutT>
-__global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(ScanParams p) {
-  using in_t = typename Mode::in_t;
-  using frag_t = typename Mode::frag_t;
-  using Op = typename Mode::Op;
-  constexpr int KB = DK / 32;   // 32-deep blocks over d_k
-  constexpr int IT = DK / 16;   // 16-row tiles over d_k
-  constexpr int NB = DV / 16 / NW;
-  static_assert(DV % (16 * NW) == 0, "d_v tiles");
-
-  // LDS: per-chunk operand fragments shared by the NW waves.
-  __shared__ frag_t sKf[4 * KB * 64];   // A of K H   : [rt][kb][lane]
-  __shared__ frag_t sQf[4 * KB * 64];   // A of Q H   : [rt][kb][lane]
-  __shared__ frag_t sKTf[IT * 2 * 64];  // A of K^T V : [it][kb'][lane]
-  __shared__ __attribute__((aligned(16))) char sTP[12 * kWsBlockBytes];
-  __shared__ float sb[64];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, idx = lane & 15,
-            grp = lane >> 4;
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int dvb = lid % NB, nh = lid / NB;
-  const int h = nh % p.hv, n = nh / p.hv;
-  const int G = p.hv / p.hqk, m = h / G;
-  const int col = 16 * (dvb * NW + wave) + idx;  // this lane's d_v column
-
-  const in_t* Qg = static_cast<const in_t*>(p.q);
-  const in_t* Kg = static_cast<const in_t*>(p.k);
-  const in_t* Vg = static_cast<const in_t*>(p.v);
-  OutT* Og = static_cast<OutT*>(p.o);
-  const size_t qkstride = (size_t)p.hqk * DK;
-
-  // State slice: Hc[it][r] = H[16 it + 4 grp + r][col].
-  f32x4 Hc[IT];
-  {
-    const float* H0 = p.h0 ? p.h0 + (size_t)nh * DK * DV : nullptr;
-#pragma unroll
-    for (int it = 0; it < IT; ++it)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Hc[it][r] = H0 ? H0[(size_t)(16 * it + 4 * grp + r) * DV + col] : 0.f;
+  lds_barrier();
+  // ---- Level 2: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22.
+  if (wave < 2) {
+    const int ib = 2 * wave + 1, jb = 2 * wave;
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 M = mm16_ll(sA + 16 * ib * kLd + 16 * jb, sT + 16 * jb * kLd + 16 * jb, z, idx, grp);
+    f32x4 R = mm16_lr(sT + 16 * ib * kLd + 16 * ib, M, z, idx, grp);
+    store_c16(sT + 16 * ib * kLd + 16 * jb, R, idx, grp, -1.f);
   }
-
-  const int start = p.cu[n];
-  const int L = p.cu[n + 1] - start;
-  const int nchunks = (L + kChunk - 1) / kChunk;
-  const int slot0 = slot_base(p.cu, n);
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0 = start + kChunk * c;
-    const int len = min(kChunk, L - kChunk * c);
-    __syncthreads();  // previous chunk's LDS reads are done
-
-    // ---- stage q, k operand fragments (rows >= len are zero)
-    constexpr int PER_ROW = DK / 8;  // 8-element pieces per row
-    for (int pc = tid; pc < 64 * PER_ROW; pc += NW * 64) {
-      const int row = pc / PER_ROW, d0 = 8 * (pc % PER_ROW);
-      float kx[8], qx[8];
-      if (row < len) {
-        const in_t* kr = Kg + (size_t)(t0 + row) * qkstride + (size_t)m * DK + d0;
-        const in_t* qr = Qg + (size_t)(t0 + row) * qkstride + (size_t)m * DK + d0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kx[e] = to_f32(kr[e]);
-          qx[e] = to_f32(qr[e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = qx[e] = 0.f;
-      }
-      const int rt = row >> 4, i = row & 15, kb = d0 >> 5, o = d0 & 31;
-      const int g0 = (o & 15) >> 2, s0 = o >= 16 ? 4 : 0;
-      // elements 0-3 -> lane (i, g0) slots s0..s0+3; elements 4-7 -> lane (i, g0+1)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int fl = i + 16 * (g0 + half);
-        put4(&sKf[(rt * KB + kb) * 64 + fl], s0, kx + 4 * half);
-        put4(&sQf[(rt * KB + kb) * 64 + fl], s0, qx + 4 * half);
-      }
-      // K^T fragments: element d -> tile it = d / 16, lane (d % 16, grp(tok)), slot(tok)
-      const int kbp = row >> 5, tt = row & 31;
-      const int gp = (tt & 15) >> 2, sp = (tt >> 4) * 4 + (tt & 3);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = d0 + e;
-        put1(&sKTf[((d >> 4) * 2 + kbp) * 64 + (d & 15) + 16 * gp], sp, kx[e]);
-      }
+  lds_barrier();
+  // ---- Level 3, column block jb in {0, 1} (wave jb):
+  //   X_i = sum_{kb=jb..1} A_{i,kb} T_{kb,jb} (i = 2, 3)
+  //   T_{2,jb} = -T_22 X_2,  T_{3,jb} = -(T_32 X_2 + T_33 X_3)
+  if (wave < 2) {
+    const int jb = wave;
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 X2 = z, X3 = z;
+    for (int kb = jb; kb < 2; ++kb) {
+      const float* Tk = sT + 16 * kb * kLd + 16 * jb;
+      X2 = mm16_ll(sA + 32 * kLd + 16 * kb, Tk, X2, idx, grp);
+      X3 = mm16_ll(sA + 48 * kLd + 16 * kb, Tk, X3, idx, grp);
     }
-    // ---- copy T diag(beta) / P fragments and b from the workspace record
-    {
-      const char* rec = p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
-      const f32x4* src = reinterpret_cast<const f32x4*>(rec);
-      f32x4* dst = reinterpret_cast<f32x4*>(sTP);
-      for (int e = tid; e < 12 * kWsBlockBytes / 16; e += NW * 64) dst[e] = src[e];
-      if (tid < 64) sb[tid] = reinterpret_cast<const float*>(rec + kWsBOff)[tid];
-    }
-    __syncthreads();
-
-    // ---- H as split B fragments over d_k: HB[kb] from tiles 2kb, 2kb+1
-    Op HB[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      float x[8];
-      pack_c_pair(Hc[2 * kb], Hc[2 * kb + 1], x);
-      HB[kb] = Mode::make(x);
-    }
-
-    // ---- K H and Q H per 16-row tile; Y = V - gamma K H; QH scaled by gamma
-    f32x4 QH[4], Y[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        kh = Mode::mma_xs(kh, sKf[(rt * KB + kb) * 64 + lane], HB[kb]);
-        qh = Mode::mma_xs(qh, sQf[(rt * KB + kb) * 64 + lane], HB[kb]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * rt + 4 * grp + r;
-        const float gam = expf(sb[t]);
-        const float vv = t < len ? to_f32(Vg[((size_t)(t0 + t) * p.hv + h) * DV + col]) : 0.f;
-        Y[rt][r] = vv - gam * kh[r];
-        QH[rt][r] = gam * qh[r];
-      }
-    }
-    Op YB[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float x[8];
-      pack_c_pair(Y[2 * kb], Y[2 * kb + 1], x);
-      YB[kb] = Mode::make(x);
-    }
-    // ---- V' = (T diag(beta)) Y   (lower-triangular block structure)
-    f32x4 Vp[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb <= rt / 2; ++kb) {
-        const Op a = Mode::load_block(sTP + kWsTOff + tri_block(rt, kb) * kWsBlockBytes, lane);
-        acc = Mode::mma_ss(acc, a, YB[kb]);
-      }
-      Vp[rt] = acc;
-    }
-    const float bC = sb[63];
-    Op VB[2], DB[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float x[8], d[8];
-      pack_c_pair(Vp[2 * kb], Vp[2 * kb + 1], x);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int t = 32 * kb + kslot(grp, s);
-        d[s] = x[s] * expf(bC - sb[t]);
-      }
-      VB[kb] = Mode::make(x);
-      DB[kb] = Mode::make(d);
-    }
-    // ---- O = gamma Q H + P V'
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = QH[rt];
-#pragma unroll
-      for (int kb = 0; kb <= rt / 2; ++kb) {
-        const Op a = Mode::load_block(sTP + kWsPOff + tri_block(rt, kb) * kWsBlockBytes, lane);
-        acc = Mode::mma_ss(acc, a, VB[kb]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * rt + 4 * grp + r;
-        if (t < len)
-          Og[((size_t)(t0 + t) * p.hv + h) * DV + col] = from_f32<OutT>(p.scale * acc[r]);
-      }
-    }
-    // ---- H <- gamma_C H + K^T diag(e^{b_C - b}) V'
-    const float gC = expf(bC);
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      f32x4 acc = Hc[it] * gC;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) acc = Mode::mma_xs(acc, sKTf[(it * 2 + kb) * 64 + lane], DB[kb]);
-      Hc[it] = acc;
-    }
+    f32x4 T2 = mm16_lr(sT + 32 * kLd + 32, X2, z, idx, grp);
+    f32x4 T3 = mm16_lr(sT + 48 * kLd + 32, X2, z, idx, grp);
+    T3 = mm16_lr(sT + 48 * kLd + 48, X3, T3, idx, grp);
+    store_c16(sT + 32 * kLd + 16 * jb, T2, idx, grp, -1.f);
+    store_c16(sT + 48 * kLd + 16 * jb, T3, idx, grp, -1.f);
   }
-
-  if (p.ht) {
-    float* HT = p.ht + (size_t)nh * DK * DV;
+  lds_barrier();
+  // ---- T diag(beta) as stored A fragments: 6 blocks x 64 lanes.
+  for (int it = tid; it < 6 * 64; it += 256) {
+    const int bi = it >> 6, ln = it & 63;
+    const int rt = bi < 2 ? bi : 2 + (bi - 2) / 2;
+    const int kb = bi < 2 ? 0 : (bi - 2) % 2;
+    const int i = ln & 15, gr = ln >> 4;
+    const int t = 16 * rt + i;
+    float x[8];
 #pragma unroll
-    for (int it = 0; it < IT; ++it)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) HT[(size_t)(16 * it + 4 * grp + r) * DV + col] = Hc[it][r];
+    for (int s = 0; s < 8; ++s) {
+      const int j = 32 * kb + kslot(gr, s);
+      x[s] = j <= t ? sT[t * kLd + j] * sbeta[j] : 0.f;
+    }
+    Mode::store_block(rec + kWsTOff + bi * kWsBlockBytes, ln, Mode::make(x));
   }
 }
 
@@ -471,34 +292,9 @@ template <typename Mode, int D>
 hipError_t launch_intra_t(const gdn_shape_t& s, const IntraParams& p, hipStream_t stream) {
   const long long slots = chunk_slots(s);
   if (slots <= 0 || s.total_tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_intra_kernel<Mode, D>), dim3((unsigned)slots, (unsigned)s.num_qk_heads),
+  hipLaunchKernelGGL((chunk_intra_kernel<Mode, D>), dim3((unsigned)slots, (unsigned)s.num_v_heads),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
-}
-
-template <typename Mode, int D, int NW, typename OutT>
-hipError_t launch_scan_nw(const ScanParams& p, long long heads, hipStream_t stream) {
-  static_assert(D / 16 % NW == 0, "d_v tiles per workgroup");
-  const unsigned blocks = (unsigned)(heads * (D / 16 / NW));
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_scan_kernel<Mode, D, D, NW, OutT>), dim3(blocks), dim3(NW * 64), 0,
-                     stream, p);
-  return hipGetLastError();
-}
-
-template <typename Mode, int D, typename OutT>
-hipError_t launch_scan_t(const gdn_shape_t& s, const ScanParams& p, hipStream_t stream) {
-  // Waves per workgroup (each wave owns one 16-column d_v tile): the most (<= 4) that still
-  // leaves >= 512 workgroups, else 1.
-  const long long heads = (long long)s.num_seqs * s.num_v_heads;
-  constexpr int tiles = D / 16;
-  if constexpr (tiles % 4 == 0) {
-    if (heads * (tiles / 4) >= 512) return launch_scan_nw<Mode, D, 4, OutT>(p, heads, stream);
-  }
-  if constexpr (tiles % 2 == 0) {
-    if (heads * (tiles / 2) >= 512) return launch_scan_nw<Mode, D, 2, OutT>(p, heads, stream);
-  }
-  return launch_scan_nw<Mode, D, 1, OutT>(p, heads, stream);
 }
 
 template <typename Mode>
@@ -507,16 +303,6 @@ hipError_t launch_intra_d(const gdn_shape_t& s, const IntraParams& p, hipStream_
     case 32: return launch_intra_t<Mode, 32>(s, p, stream);
     case 64: return launch_intra_t<Mode, 64>(s, p, stream);
     case 128: return launch_intra_t<Mode, 128>(s, p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <typename Mode, typename OutT>
-hipError_t launch_scan_d(const gdn_shape_t& s, const ScanParams& p, hipStream_t stream) {
-  switch (s.head_dim_k) {
-    case 32: return launch_scan_t<Mode, 32, OutT>(s, p, stream);
-    case 64: return launch_scan_t<Mode, 64, OutT>(s, p, stream);
-    case 128: return launch_scan_t<Mode, 128, OutT>(s, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -530,19 +316,6 @@ hipError_t launch_chunk_intra(const gdn_shape_t& s, const int32_t* cu, const voi
                 s.num_v_heads};
   if (s.qkv_dtype == GDN_DTYPE_BF16) return launch_intra_d<Bf16Mode>(s, p, stream);
   return launch_intra_d<F32Mode>(s, p, stream);
-}
-
-hipError_t launch_chunk_scan(const gdn_shape_t& s, const int32_t* cu, const void* q,
-                             const void* k, const void* v, const float* h0, void* o, float* ht,
-                             const void* ws, hipStream_t stream) {
-  ScanParams p{cu, q, k, v, h0, o, ht, static_cast<const char*>(ws), s.num_seqs, s.num_qk_heads,
-               s.num_v_heads, s.scale};
-  const bool out_bf = s.out_dtype == GDN_DTYPE_BF16;
-  if (s.qkv_dtype == GDN_DTYPE_BF16)
-    return out_bf ? launch_scan_d<Bf16Mode, bf16>(s, p, stream)
-                  : launch_scan_d<Bf16Mode, float>(s, p, stream);
-  return out_bf ? launch_scan_d<F32Mode, bf16>(s, p, stream)
-                : launch_scan_d<F32Mode, float>(s, p, stream);
 }
 
 }  // namespace gdn

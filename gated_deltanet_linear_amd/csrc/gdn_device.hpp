@@ -160,8 +160,9 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 constexpr int kWsBlockBytes = 2048;
 constexpr int kWsTOff = 0;                      // T*diag(beta): 6 blocks
 constexpr int kWsPOff = 6 * kWsBlockBytes;      // masked decayed Q K^T: 6 blocks
-constexpr int kWsBOff = 12 * kWsBlockBytes;     // in-chunk cumsum of g: 64 fp32
-constexpr int kWsRecordBytes = kWsBOff + 256;   // 24832 bytes
+constexpr int kWsGOff = 12 * kWsBlockBytes;     // gamma_t = e^{b_t}: 64 fp32
+constexpr int kWsDOff = kWsGOff + 256;          // delta_t = e^{b_C - b_t}: 64 fp32
+constexpr int kWsRecordBytes = kWsDOff + 256;   // 25088 bytes
 
 __host__ __device__ constexpr int tri_block(int rt, int kb) {
   return rt < 2 ? rt : 2 + 2 * (rt - 2) + kb;
@@ -188,6 +189,87 @@ __device__ __forceinline__ int slot_to_seq(const int32_t* cu, int num_seqs, int 
 // over the 8 XCDs), so groups that read the same q/k tiles share an L2.
 __device__ __forceinline__ int xcd_logical_id(int b, int total) {
   return (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
+}
+
+
+// ---- LDS staging and operand fragments from staged rows -------------------------------
+
+#define GDN_AS1(p) ((const __attribute__((address_space(1))) void*)(p))
+#define GDN_AS3(p) ((__attribute__((address_space(3))) void*)(p))
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+
+// 16-byte XOR swizzle of a staged row (keeps the 8 rows that a fragment read touches on
+// different LDS banks).
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+  constexpr int NCH = ROWB / 16;
+  return (2 * row) & (NCH - 1) & ~1;
+}
+template <int ROWB, int ES>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  const int byte = col * ES;
+  return row * ROWB + (((byte >> 4) ^ swz<ROWB>(row)) << 4) + (byte & 15);
+}
+
+// A fragment of a [64 x D] row-major staged matrix (rows = tokens, depth = d_k):
+// lane (idx, grp) gets row `row`, depth 32 kb + kslot(grp, s).
+template <int ROWB>
+__device__ __forceinline__ bf16x8 afrag(const char* buf, int row, int kb, int grp) {
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(buf + swz_off<ROWB, 2>(row, 32 * kb + 4 * grp));
+  const bf16x4 hi =
+      *reinterpret_cast<const bf16x4*>(buf + swz_off<ROWB, 2>(row, 32 * kb + 16 + 4 * grp));
+  bf16x8 f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f[s] = lo[s];
+    f[4 + s] = hi[s];
+  }
+  return f;
+}
+template <int ROWB>
+__device__ __forceinline__ f32x8 afrag_f32(const char* buf, int row, int kb, int grp) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(buf + swz_off<ROWB, 4>(row, 32 * kb + 4 * grp));
+  const f32x4 hi =
+      *reinterpret_cast<const f32x4*>(buf + swz_off<ROWB, 4>(row, 32 * kb + 16 + 4 * grp));
+  f32x8 f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f[s] = lo[s];
+    f[4 + s] = hi[s];
+  }
+  return f;
+}
+
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// outstanding global loads (the next chunk's prefetch keeps flying across it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Asynchronous copy of the 64 rows [t0, t0 + 64) of head m of two [T][H][D] tensors (K, then Q)
+// into LDS at S and S + 64 * D * sizeof(T), row-major with the swizzle above, using
+// global_load_lds (16 bytes per lane; no registers; completes on vmcnt). Rows past len
+// re-read row len - 1 so that every address stays inside the tensors.
+template <typename T, int D, int NWAVES>
+__device__ __forceinline__ void stage_rows(char* S, const T* Kg, const T* Qg, int t0, int len,
+                                           size_t rstride, int m, int wave, int lane) {
+  constexpr int ROWB = D * (int)sizeof(T), NCH = ROWB / 16, KBYTES = 64 * ROWB;
+  constexpr int KINST = KBYTES / 1024;
+  for (int j = wave; j < 2 * KINST; j += NWAVES) {
+    const bool isq = j >= KINST;
+    const int jj = isq ? j - KINST : j;
+    const int P = 64 * jj + lane;
+    const int r = P / NCH, ch = (P % NCH) ^ swz<ROWB>(P / NCH);
+    const int rr = r < len ? r : len - 1;
+    const char* src = reinterpret_cast<const char*>((isq ? Qg : Kg) + (size_t)(t0 + rr) * rstride +
+                                                    (size_t)m * D) + 16 * ch;
+    __builtin_amdgcn_global_load_lds(GDN_AS1(src), GDN_AS3(S + (isq ? KBYTES : 0) + 1024 * jj),
+                                     16, 0, 0);
+  }
 }
 
 }  // namespace gdn

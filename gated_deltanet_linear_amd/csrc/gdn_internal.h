@@ -27,7 +27,7 @@ hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x
 
 // Bytes of one workspace record (one chunk slot x one V head); the layout is private to
 // gdn_chunk.hip, which checks this value at compile time.
-constexpr long long kWorkspaceRecordBytes = 24832;
+constexpr long long kWorkspaceRecordBytes = 25088;
 
 // Number of chunk slots the workspace holds: num_seqs + total_tokens / 64.
 inline long long chunk_slots(const gdn_shape_t& s) {

@@ -92,7 +92,7 @@ gdn_status_t gdn_prepare(const gdn_shape_t* shape, const int32_t* cu_seqlens,
 
 /* Bytes of device workspace gdn_chunk_forward needs for this shape (0 on a bad shape). The
  * bound uses total_tokens and num_seqs only: (num_seqs + total_tokens / 64) chunk slots times
- * H_v times 24832 bytes. */
+ * H_v times 25088 bytes. */
 size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
 
 /*

@@ -50,7 +50,7 @@ def _shape(**kw):
 
 def test_workspace_size_formula(lib):
     s = _shape()
-    expect = (2 + 300 // 64) * 32 * 24832
+    expect = (2 + 300 // 64) * 32 * 25088
     assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(s)) == expect
     assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(_shape(num_v_heads=33))) == 0
     assert lib.gdn_chunk_forward_workspace_size(None) == 0

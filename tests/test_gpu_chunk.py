@@ -182,3 +182,30 @@ def test_prefill_then_decode_equals_longer_prefill():
     o_ref, h_ref = oracle_case(case)
     assert_rms_close(torch.cat([o1, o_last]), o_ref, TOL["bf16"], "prefill+decode o")
     assert_rms_close(h1, h_ref, TOL["bf16"], "prefill+decode state")
+
+
+def test_scan_layouts_are_bit_identical():
+    """The row-split (4 waves per d_v tile) and tile-per-wave scan layouts give identical bits."""
+    import subprocess
+    import sys
+    code = (
+        "import sys, torch; sys.path.insert(0, '.'); import synthetic_inputs as si;"
+        "import gated_deltanet_linear_amd as gdn;"
+        "c = si.make_core_case([300, 64, 5], 2, 4, 128, 128, dtype='bf16', gate='model',"
+        " h0_std=0.02, seed=91);"
+        "d = {k: getattr(c, k).cuda() for k in ('q','k','v','g','beta','cu_seqlens','h0')};"
+        "o, h = gdn.chunk_forward(d['q'], d['k'], d['v'], d['g'], d['beta'], d['cu_seqlens'],"
+        " initial_state=d['h0'], out_dtype=torch.float32);"
+        "torch.save((o.cpu(), h.cpu()), sys.argv[1])")
+    import os
+    import tempfile
+    outs = []
+    with tempfile.TemporaryDirectory() as td:
+        for layout in ("rows", "tiles"):
+            path = os.path.join(td, layout + ".pt")
+            env = dict(os.environ, GDN_SCAN_LAYOUT=layout)
+            subprocess.run([sys.executable, "-c", code, path], check=True, env=env,
+                           cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           timeout=300)
+            outs.append(torch.load(path, weights_only=True))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
