@@ -133,8 +133,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
   const int len = min(kChunk, tend - t0);
   const int m = h / (p.hv / p.hqk);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, idx = lane & 15,
-            grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const size_t rstride = (size_t)p.hqk * DK;
   char* rec = p.ws + ((size_t)slot * p.hv + h) * kWsRecordBytes;
 
@@ -147,6 +147,54 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     bv = p.beta[(size_t)(t0 + lane) * p.hv + h];
   }
   __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+  if (len < kChunk) {  // tail chunk: rows past len (copies of row len-1) become zero rows
+    for (int e = tid; e < 2 * (kChunk - len) * (ROWB / 16); e += 256) {
+      const int mat = e / ((kChunk - len) * (ROWB / 16)), rem = e % ((kChunk - len) * (ROWB / 16));
+      const int row = len + rem / (ROWB / 16), c16 = rem % (ROWB / 16);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(sKQ + mat * KBYTES + row * ROWB + 16 * c16) = z;
+    }
+    lds_barrier();
+  }
+
+  // ---- 22 tile jobs, round robin over the waves (wave w: jobs w, w+4, ..., w+16 on MFMA,
+  // and job w+20 for waves 0, 1):
+  //   0..9   A tiles (tr >= tc): A_tj = beta_t e^{b_t - b_j} (k_t . k_j) for j < t, into LDS;
+  //   10..19 P^T tiles: C = K_ct Q_rt^T, whose C fragment IS half of the stored A fragment of
+  //          P = (Q K^T) o Gamma o lower-incl (block (rt, ct / 2), slots 4 (ct % 2) + r);
+  //   20, 21 the zero halves of the diagonal P blocks (ct = rt + 1 for rt = 0, 2).
+  // The products run first; wave 0 forms the gate cumsum meanwhile; the epilogues that need it
+  // follow one barrier later.
+  const char* sK = sKQ;
+  const char* sQ = sKQ + KBYTES;
+  auto job_tiles = [](int job, int& r1, int& r2) {
+    const int tt = job >= 10 ? job - 10 : job;
+    r1 = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // row tile
+    r2 = tt - r1 * (r1 + 1) / 2;                        // column tile (<= r1)
+  };
+  f32x4 acc[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int job = wave + 4 * i;
+    const bool isp = job >= 10;
+    int r1, r2;
+    job_tiles(job, r1, r2);
+    // A tiles: rows r1 of K against rows r2 of K.  P^T tiles: rows r2 of K against rows r1 of Q.
+    const int ra = isp ? 16 * r2 + idx : 16 * r1 + idx;
+    const int rb = isp ? 16 * r1 + idx : 16 * r2 + idx;
+    const char* bsrc = isp ? sQ : sK;
+    frag_t fa[KB], fb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      fa[kb] = row_frag<Mode, ROWB>(sK, ra, kb, grp);
+      fb[kb] = row_frag<Mode, ROWB>(bsrc, rb, kb, grp);
+    }
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) c = mma32(fa[kb], fb[kb], c);
+    acc[i] = c;
+  }
   if (wave == 0) {
     const float cs = wave_inclusive_scan(gv, lane);
     const float cl = __shfl(cs, kChunk - 1, kWave);  // b_C (identity steps keep it at b_{len-1})
@@ -155,56 +203,33 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     reinterpret_cast<float*>(rec + kWsGOff)[lane] = __expf(cs);
     reinterpret_cast<float*>(rec + kWsDOff)[lane] = __expf(cl - cs);
   }
-  lds_barrier();
-
-  // ---- 22 tile jobs, round robin over the waves:
-  //   0..9   A tiles (tr >= tc): A_tj = beta_t e^{b_t - b_j} (k_t . k_j) for j < t, into LDS;
-  //   10..19 P^T tiles: C = K_ct Q_rt^T, whose C fragment IS half of the stored A fragment of
-  //          P = (Q K^T) o Gamma o lower-incl (block (rt, ct / 2), slots 4 (ct % 2) + r);
-  //   20, 21 the zero halves of the diagonal P blocks (ct = rt + 1 for rt = 0, 2).
-  const char* sK = sKQ;
-  const char* sQ = sKQ + KBYTES;
-  for (int job = wave; job < 22; job += 4) {
-    if (job >= 20) {
-      const int rt = job == 20 ? 0 : 2;
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      store_half_global(Mode{}, rec + kWsPOff + tri_block(rt, rt / 2) * kWsBlockBytes, lane, 1, z);
-      continue;
-    }
-    const bool isp = job >= 10;
-    const int tt = isp ? job - 10 : job;
-    const int r1 = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // row tile
-    const int r2 = tt - r1 * (r1 + 1) / 2;                        // column tile (<= r1)
-    // A tiles: rows r1 of K against rows r2 of K.  P^T tiles: rows r2 of K against rows r1 of Q.
-    const int ra = isp ? 16 * r2 + idx : 16 * r1 + idx;
-    const int rb = isp ? 16 * r1 + idx : 16 * r2 + idx;
-    const char* bsrc = isp ? sQ : sK;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (wave < 2) {
+    const int rt = wave == 0 ? 0 : 2;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    store_half_global(Mode{}, rec + kWsPOff + tri_block(rt, rt / 2) * kWsBlockBytes, lane, 1, z);
+  }
+  lds_barrier();  // sb, sbeta ready
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      frag_t a = row_frag<Mode, ROWB>(sK, ra, kb, grp);
-      frag_t b = row_frag<Mode, ROWB>(bsrc, rb, kb, grp);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        a[s] = ra < len ? a[s] : (in_t)0.f;
-        b[s] = rb < len ? b[s] : (in_t)0.f;
-      }
-      acc = mma32(a, b, acc);
-    }
-    if (!isp) {
+  for (int i = 0; i < 5; ++i) {
+    const int job = wave + 4 * i;
+    int r1, r2;
+    job_tiles(job, r1, r2);
+    if (job < 10) {
       const int j = 16 * r2 + idx;
+      const float bj = sb[j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * r1 + 4 * grp + r;
-        sA[t * kLd + j] = j < t ? sbeta[t] * __expf(sb[t] - sb[j]) * acc[r] : 0.f;
+        sA[t * kLd + j] = j < t ? sbeta[t] * __expf(sb[t] - bj) * acc[i][r] : 0.f;
       }
     } else {
       const int t = 16 * r1 + idx;
+      const float bt = sb[t];
       f32x4 pv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * r2 + 4 * grp + r;
-        pv[r] = j <= t ? __expf(sb[t] - sb[j]) * acc[r] : 0.f;
+        pv[r] = j <= t ? __expf(bt - sb[j]) * acc[i][r] : 0.f;
       }
       store_half_global(Mode{}, rec + kWsPOff + tri_block(r1, r2 >> 1) * kWsBlockBytes, lane,
                         r2 & 1, pv);
@@ -225,13 +250,13 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
 #pragma unroll
     for (int i = 1; i < 16; ++i) {
-      float acc = 0.f;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};  // 4 independent chains
 #pragma unroll
       for (int j = 0; j < i; ++j)
-        acc = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                       __builtin_bit_cast(int, arow[j]), i)),
-                   x[j], acc);
-      x[i] = (i == lane) ? 1.f : -acc;
+        part[j & 3] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                               __builtin_bit_cast(int, arow[j]), i)),
+                           x[j], part[j & 3]);
+      x[i] = (i == lane) ? 1.f : -((part[0] + part[1]) + (part[2] + part[3]));
     }
     if (lane < 16) {
       float* Tb = sT + (16 * wave) * kLd + 16 * wave;

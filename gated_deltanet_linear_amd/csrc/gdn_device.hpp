@@ -242,12 +242,13 @@ __device__ __forceinline__ f32x8 afrag_f32(const char* buf, int row, int kb, int
   return f;
 }
 
-// Barrier for LDS traffic only: waits for this wave's LDS operations, not for its
-// outstanding global loads (the next chunk's prefetch keeps flying across it).
+// Barrier for LDS traffic only: waits for this wave's own LDS reads and writes (lgkmcnt) and
+// for the other waves, but not for outstanding global loads, including global_load_lds copies
+// into a different LDS buffer (a fence would wait for those too, serialising the prefetch of
+// the next chunk with this one). The memory clobber keeps the compiler from moving memory
+// accesses across it. Callers that need global_load_lds data wait with s_waitcnt first.
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Asynchronous copy of the 64 rows [t0, t0 + 64) of head m of two [T][H][D] tensors (K, then Q)

@@ -13,12 +13,14 @@
 //           in that wave's registers for the whole sequence (most work per wave, least LDS).
 //   RW = 4: wave r owns row tile r (16 tokens) and 32 rows of the state; Y, V' and the new
 //           state cross waves through LDS (4x the waves for shapes with few sequences x heads).
-// q/k rows and the workspace record of chunk c+1 stream into LDS with global_load_lds while
-// chunk c computes (double buffered). q/k rows are stored row-major with a 16-byte XOR
-// swizzle; K^T operand fragments are read from the same rows with ds_read_b64_tr_b16.
+// q/k rows and the workspace record of chunk c+1 are loaded into registers while chunk c
+// computes and written to LDS when chunk c+1 starts. q/k rows are stored row-major with a
+// 16-byte XOR swizzle; K^T operand fragments are read from the same rows with
+// ds_read_b64_tr_b16.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "gdn_device.hpp"
 #include "gdn_internal.h"
@@ -70,6 +72,18 @@ __device__ __forceinline__ f32x8 ktfrag_f32(const char* sK, int it, int kbp, int
   return f;
 }
 
+// Raw element loads for register prefetch. A bf16 element is fetched as the aligned 32-bit
+// word that holds it (no narrowing or masking right after the load, which would make the
+// compiler wait for it there) and its half is selected where it is used.
+__device__ __forceinline__ uint32_t load_raw(const bf16* p, int col) {
+  return *reinterpret_cast<const uint32_t*>(p + (col & ~1));
+}
+__device__ __forceinline__ float load_raw(const float* p, int col) { return p[col]; }
+__device__ __forceinline__ float raw_to_f32(uint32_t x, int col) {
+  return __uint_as_float((col & 1) ? (x & 0xffff0000u) : (x << 16));
+}
+__device__ __forceinline__ float raw_to_f32(float x, int) { return x; }
+
 template <typename Mode, int ROWB>
 struct Frags;
 template <int ROWB>
@@ -111,24 +125,53 @@ __device__ __forceinline__ void store_half(F32Mode, char* blk, int lane, int hal
 constexpr int kRecUnits = kWsRecordBytes / 16;               // 16-byte units per record
 constexpr int kRecStage = (kWsRecordBytes + 1023) / 1024 * 1024;  // staged record bytes
 
-// Issue the asynchronous copies of chunk (t0, len) into stage buffer S: K rows, Q rows
-// (rows past len repeat row len-1; they only ever meet zero coefficients), and the record.
+// One chunk's staged data (K rows, Q rows, workspace record), prefetched into registers with
+// ordinary 16-byte global loads one chunk ahead and written to LDS at the start of the chunk
+// that uses it. (global_load_lds reaches only ~38 B/clk per CU on this part; plain loads into
+// registers several times that.) Unit j of 1 KiB goes to LDS bytes [1024 j, 1024 j + 1024):
+// units [0, KI) are K rows, [KI, 2 KI) Q rows (row-major, 16-byte XOR swizzle), then the
+// record. Rows past len re-read row len - 1 (finite values that only meet zero
+// coefficients); record lanes past its end re-read its last 16 bytes into the padding.
 template <typename Mode, int D, int NWAVES>
-__device__ __forceinline__ void stage_chunk(char* S, const typename Mode::in_t* Kg,
-                                            const typename Mode::in_t* Qg, const char* rec,
-                                            int t0, int len, size_t rstride, int m, int wave,
-                                            int lane) {
-  constexpr int KBYTES = 64 * D * (int)sizeof(typename Mode::in_t);
-  stage_rows<typename Mode::in_t, D, NWAVES>(S, Kg, Qg, t0, len, rstride, m, wave, lane);
-  for (int j = wave; j < kRecStage / 1024; j += NWAVES) {
-    const int P = 64 * j + lane;
-    if (P < kRecUnits)
-      __builtin_amdgcn_global_load_lds(GDN_AS1(rec + 16 * P), GDN_AS3(S + 2 * KBYTES + 1024 * j),
-                                       16, 0, 0);
-  }
-}
+struct Stager {
+  using in_t = typename Mode::in_t;
+  static constexpr int ROWB = D * (int)sizeof(in_t), NCH = ROWB / 16, KBYTES = 64 * ROWB;
+  static constexpr int KI = KBYTES / 1024, RI = kRecStage / 1024, TOTAL = 2 * KI + RI;
+  static constexpr int PER = (TOTAL + NWAVES - 1) / NWAVES;
+  f32x4 r[PER];
 
-template <typename Mode, int D, int NT, int RW, int STAGES, typename OutT>
+  __device__ __forceinline__ void load(const in_t* Kg, const in_t* Qg, const char* rec, int t0,
+                                       int len, size_t rstride, int m, int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = wave + NWAVES * u;
+      if (j < TOTAL) {
+        const char* src;
+        if (j < 2 * KI) {
+          const bool isq = j >= KI;
+          const int P = 64 * (isq ? j - KI : j) + lane;
+          const int row = P / NCH, ch = (P % NCH) ^ swz<ROWB>(P / NCH);
+          const int rr = row < len ? row : len - 1;
+          src = reinterpret_cast<const char*>((isq ? Qg : Kg) + (size_t)(t0 + rr) * rstride +
+                                              (size_t)m * D) + 16 * ch;
+        } else {
+          const int P = min(64 * (j - 2 * KI) + lane, kRecUnits - 1);
+          src = rec + 16 * P;
+        }
+        r[u] = *reinterpret_cast<const f32x4*>(src);
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(char* S, int wave, int lane) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = wave + NWAVES * u;
+      if (j < TOTAL) *reinterpret_cast<f32x4*>(S + 1024 * j + 16 * lane) = r[u];
+    }
+  }
+};
+
+template <typename Mode, int D, int NT, int RW, typename OutT>
 __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) {
   using in_t = typename Mode::in_t;
   using Op = typename Mode::Op;
@@ -144,12 +187,12 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
   constexpr int XH = 0, XY = KB * 2048, XV = XY + 2 * 2048, XD = XV + 2 * 2048;
   constexpr int XBYTES = RW > 1 ? XD + 2 * 2048 : 0;
   static_assert(RW == 1 || RW == 2 || RW == 4, "row waves");
-  static_assert(STAGES * STAGE_BYTES + NT * XBYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGE_BYTES + NT * XBYTES <= 160 * 1024, "LDS budget");
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES + NT * XBYTES + 16];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGE_BYTES + NT * XBYTES + 16];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, idx = lane & 15,
-            grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int tile = wave / RW, rg = wave % RW;
   constexpr int NB = D / 16 / NT;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -157,7 +200,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
   const int h = nh % p.hv, n = nh / p.hv;
   const int G = p.hv / p.hqk, m = h / G;
   const int col = 16 * (dvb * NT + tile) + idx;
-  char* X = smem + STAGES * STAGE_BYTES + tile * XBYTES;
+  char* X = smem + STAGE_BYTES + tile * XBYTES;
 
   const in_t* Qg = static_cast<const in_t*>(p.q);
   const in_t* Kg = static_cast<const in_t*>(p.k);
@@ -196,23 +239,25 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
     return p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
   };
   // v rows of this wave (row tiles rg*R .. rg*R+R-1) in C-fragment order, one chunk ahead.
-  // Rows past the chunk end read the last valid row and are zeroed where used.
-  auto load_v = [&](int c, in_t (&dst)[R][4]) {
+  // Rows past the chunk end read the last valid row and are zeroed where used. The values
+  // stay raw (one element per 32-bit register) until used, so that nothing waits on the
+  // loads before the next chunk.
+  using reg_t = typename std::conditional<std::is_same<in_t, bf16>::value, uint32_t, float>::type;
+  auto load_v = [&](int c, reg_t (&dst)[R][4]) {
     const int t0c = start + kChunk * c, lenc = min(kChunk, L - kChunk * c);
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = min(16 * (rg * R + i) + 4 * grp + r, lenc - 1);
-        dst[i][r] = Vg[((size_t)(t0c + t) * p.hv + h) * D + col];
+        dst[i][r] = load_raw(Vg + ((size_t)(t0c + t) * p.hv + h) * D, col);
       }
   };
-  in_t vnext[R][4];
+  reg_t vnext[R][4];
+  Stager<Mode, D, NWAVES> st;
   if (nchunks > 0) {
     load_v(0, vnext);
-    if constexpr (STAGES == 2)
-      stage_chunk<Mode, D, NWAVES>(smem, Kg, Qg, rec_of(0), start, min(kChunk, L), rstride, m,
-                                   wave, lane);
+    st.load(Kg, Qg, rec_of(0), start, min(kChunk, L), rstride, m, wave, lane);
   }
   // Output rows of the previous chunk, stored after the next chunk's barrier so that the
   // wait for the prefetch never waits for fresh stores.
@@ -231,25 +276,21 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = start + kChunk * c;
     const int len = min(kChunk, L - kChunk * c);
-    char* S = smem + (c % STAGES) * STAGE_BYTES;
-    if constexpr (STAGES == 1) {
-      lds_barrier();  // previous chunk done with the single stage buffer
-      stage_chunk<Mode, D, NWAVES>(S, Kg, Qg, rec_of(c), t0, len, rstride, m, wave, lane);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of chunk c (and its v rows) landed
-    lds_barrier();                  // ... and every other wave's; chunk c-1 fully consumed
+    char* S = smem;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c (and its v rows) landed
+    lds_barrier();                  // every wave is done with chunk c-1's LDS
+    st.commit(S, wave, lane);
+    lds_barrier();                  // chunk c staged
     float vv[R][4];
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vv[i][r] = (16 * (rg * R + i) + 4 * grp + r < len) ? to_f32(vnext[i][r]) : 0.f;
+        vv[i][r] = (16 * (rg * R + i) + 4 * grp + r < len) ? raw_to_f32(vnext[i][r], col) : 0.f;
     if (c + 1 < nchunks) {
-      if constexpr (STAGES == 2)
-        stage_chunk<Mode, D, NWAVES>(smem + ((c + 1) % 2) * STAGE_BYTES, Kg, Qg, rec_of(c + 1),
-                                     t0 + kChunk, min(kChunk, L - kChunk * (c + 1)), rstride, m,
-                                     wave, lane);
       load_v(c + 1, vnext);
+      st.load(Kg, Qg, rec_of(c + 1), t0 + kChunk, min(kChunk, L - kChunk * (c + 1)), rstride, m,
+              wave, lane);
     }
     if (c > 0) store_prev();
     const char* sK = S;
@@ -415,15 +456,11 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
 
 template <typename Mode, int D, int NT, int RW, typename OutT>
 hipError_t launch_scan_cfg(const ScanParams& p, long long heads, hipStream_t stream) {
-  constexpr int ROWB = D * (int)sizeof(typename Mode::in_t);
-  constexpr int STAGE_BYTES = 2 * 64 * ROWB + kRecStage;
-  constexpr int XBYTES = RW > 1 ? (D / 32) * 2048 + 6 * 2048 : 0;
-  constexpr int STAGES = (2 * STAGE_BYTES + NT * XBYTES <= 160 * 1024) ? 2 : 1;
   static_assert(D / 16 % NT == 0, "d_v tiles per workgroup");
   const unsigned blocks = (unsigned)(heads * (D / 16 / NT));
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_scan_kernel<Mode, D, NT, RW, STAGES, OutT>), dim3(blocks),
-                     dim3(NT * RW * 64), 0, stream, p);
+  hipLaunchKernelGGL((chunk_scan_kernel<Mode, D, NT, RW, OutT>), dim3(blocks), dim3(NT * RW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
