@@ -72,18 +72,6 @@ __device__ __forceinline__ f32x8 ktfrag_f32(const char* sK, int it, int kbp, int
   return f;
 }
 
-// Raw element loads for register prefetch. A bf16 element is fetched as the aligned 32-bit
-// word that holds it (no narrowing or masking right after the load, which would make the
-// compiler wait for it there) and its half is selected where it is used.
-__device__ __forceinline__ uint32_t load_raw(const bf16* p, int col) {
-  return *reinterpret_cast<const uint32_t*>(p + (col & ~1));
-}
-__device__ __forceinline__ float load_raw(const float* p, int col) { return p[col]; }
-__device__ __forceinline__ float raw_to_f32(uint32_t x, int col) {
-  return __uint_as_float((col & 1) ? (x & 0xffff0000u) : (x << 16));
-}
-__device__ __forceinline__ float raw_to_f32(float x, int) { return x; }
-
 template <typename Mode, int ROWB>
 struct Frags;
 template <int ROWB>
@@ -125,38 +113,39 @@ __device__ __forceinline__ void store_half(F32Mode, char* blk, int lane, int hal
 constexpr int kRecUnits = kWsRecordBytes / 16;               // 16-byte units per record
 constexpr int kRecStage = (kWsRecordBytes + 1023) / 1024 * 1024;  // staged record bytes
 
-// One chunk's staged data (K rows, Q rows, workspace record), prefetched into registers with
-// ordinary 16-byte global loads one chunk ahead and written to LDS at the start of the chunk
-// that uses it. (global_load_lds reaches only ~38 B/clk per CU on this part; plain loads into
-// registers several times that.) Unit j of 1 KiB goes to LDS bytes [1024 j, 1024 j + 1024):
-// units [0, KI) are K rows, [KI, 2 KI) Q rows (row-major, 16-byte XOR swizzle), then the
-// record. Rows past len re-read row len - 1 (finite values that only meet zero
-// coefficients); record lanes past its end re-read its last 16 bytes into the padding.
-template <typename Mode, int D, int NWAVES>
+// Staged chunk data, prefetched into registers with ordinary 16-byte global loads one chunk
+// ahead and written to LDS at the start of the chunk that uses it (global_load_lds reaches only
+// ~38 B/clk per CU on this part; plain loads into registers several times that). Unit j of
+// 1 KiB goes to LDS bytes [1024 j, 1024 j + 1024): units [0, KI) are K rows, then (unless
+// KONLY) Q rows and the workspace record. q/k rows are row-major with a 16-byte XOR swizzle;
+// rows past len re-read row len - 1 (finite values that only meet zero coefficients); record
+// lanes past its end re-read its last 16 bytes into the padding.
+template <typename Mode, int D, int NWAVES, bool KONLY>
 struct Stager {
   using in_t = typename Mode::in_t;
   static constexpr int ROWB = D * (int)sizeof(in_t), NCH = ROWB / 16, KBYTES = 64 * ROWB;
-  static constexpr int KI = KBYTES / 1024, RI = kRecStage / 1024, TOTAL = 2 * KI + RI;
+  static constexpr int RPU = 64 / NCH;  // rows per 1 KiB unit
+  static constexpr int KI = KBYTES / 1024, QI = KONLY ? 0 : KI, RI = KONLY ? 0 : kRecStage / 1024;
+  static constexpr int TOTAL = KI + QI + RI;
   static constexpr int PER = (TOTAL + NWAVES - 1) / NWAVES;
   f32x4 r[PER];
 
-  __device__ __forceinline__ void load(const in_t* Kg, const in_t* Qg, const char* rec, int t0,
-                                       int len, size_t rstride, int m, int wave, int lane) {
+  // Kb, Qb: bytes of row t0 of head m; rs: bytes between rows.
+  __device__ __forceinline__ void load(const char* Kb, const char* Qb, const char* rec, int len,
+                                       int rs, int wave, int lane) {
+    const int lrow = lane / NCH, ch = lane % NCH;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int j = wave + NWAVES * u;
       if (j < TOTAL) {
         const char* src;
-        if (j < 2 * KI) {
-          const bool isq = j >= KI;
-          const int P = 64 * (isq ? j - KI : j) + lane;
-          const int row = P / NCH, ch = (P % NCH) ^ swz<ROWB>(P / NCH);
+        if (j < KI + QI) {
+          const int jj = j < KI ? j : j - KI;
+          const int row = jj * RPU + lrow;
           const int rr = row < len ? row : len - 1;
-          src = reinterpret_cast<const char*>((isq ? Qg : Kg) + (size_t)(t0 + rr) * rstride +
-                                              (size_t)m * D) + 16 * ch;
+          src = (j < KI ? Kb : Qb) + rr * rs + 16 * (ch ^ swz<ROWB>(row));
         } else {
-          const int P = min(64 * (j - 2 * KI) + lane, kRecUnits - 1);
-          src = rec + 16 * P;
+          src = rec + 16 * min(64 * (j - KI - QI) + lane, kRecUnits - 1);
         }
         r[u] = *reinterpret_cast<const f32x4*>(src);
       }
@@ -171,6 +160,97 @@ struct Stager {
   }
 };
 
+// C fragment (rows 4 grp + r, column idx) of a 16 x 16 tile stored row-major in LDS.
+// bf16: one ds_read_b64_tr_b16 (lane (g, a + 4e) addresses row 4g + e, columns 4a .. 4a+3;
+// lane (g, 4a + b) receives element b of those, i.e. row 4g + e, column 4a + b, for e = 0..3).
+template <typename T>
+struct VRows;
+template <>
+struct VRows<bf16> {
+  __device__ static f32x4 cfrag(const char* tile, int lane) {
+    const int g = lane >> 4, s = lane & 15, a = s & 3, e = s >> 2;
+    const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(tile + (4 * g + e) * 32 + 8 * a));
+    const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
+    f32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = (float)tb[r];
+    return out;
+  }
+};
+template <>
+struct VRows<float> {
+  __device__ static f32x4 cfrag(const char* tile, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    f32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = reinterpret_cast<const float*>(tile + (4 * g + r) * 64)[i];
+    return out;
+  }
+};
+
+// Half of a 32-deep operand fragment (4 consecutive depth indices): bf16x4 or f32x4.
+template <typename Mode>
+struct Half;
+template <>
+struct Half<Bf16Mode> {
+  using type = bf16x4;
+  __device__ static bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
+    bf16x8 f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f[s] = lo[s];
+      f[4 + s] = hi[s];
+    }
+    return f;
+  }
+};
+template <>
+struct Half<F32Mode> {
+  using type = f32x4;
+  __device__ static f32x8 join(const f32x4& lo, const f32x4& hi) {
+    f32x8 f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f[s] = lo[s];
+      f[4 + s] = hi[s];
+    }
+    return f;
+  }
+};
+
+// Per-wave register prefetch of the row-split layout (one row tile rt per wave): the Q rows
+// of the tile as A fragments, the T diag(beta) and P blocks of the tile, and gamma / delta of
+// its rows, all loaded straight from memory in the order they are consumed.
+template <typename Mode, int D>
+struct RowPrefetch {
+  using half_t = typename Half<Mode>::type;
+  using Op = typename Mode::Op;
+  static constexpr int KB = D / 32;
+  half_t qlo[KB], qhi[KB];
+  Op tb[2], pb[2];
+  f32x4 gam, del;
+  float gC;
+
+  __device__ __forceinline__ void load(const typename Mode::in_t* Qrow, const char* rec, int rt,
+                                       int grp, int lane) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qlo[kb] = *reinterpret_cast<const half_t*>(Qrow + 32 * kb + 4 * grp);
+      qhi[kb] = *reinterpret_cast<const half_t*>(Qrow + 32 * kb + 16 + 4 * grp);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= (rt >> 1)) {
+        tb[kb] = Mode::load_block(rec + kWsTOff + tri_block(rt, kb) * kWsBlockBytes, lane);
+        pb[kb] = Mode::load_block(rec + kWsPOff + tri_block(rt, kb) * kWsBlockBytes, lane);
+      }
+    gam = *reinterpret_cast<const f32x4*>(rec + kWsGOff + 4 * (16 * rt + 4 * grp));
+    del = *reinterpret_cast<const f32x4*>(rec + kWsDOff + 4 * (16 * rt + 4 * grp));
+    gC = *reinterpret_cast<const float*>(rec + kWsGOff + 4 * (kChunk - 1));
+  }
+};
+
 template <typename Mode, int D, int NT, int RW, typename OutT>
 __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) {
   using in_t = typename Mode::in_t;
@@ -181,15 +261,24 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
   constexpr int KB = D / 32;        // 32-deep blocks over d_k
   constexpr int R = 4 / RW;         // row tiles per wave
   constexpr int NWAVES = NT * RW;
-  constexpr int STAGE_BYTES = 2 * KBYTES + kRecStage;
+  // Row-split layout: each wave's Q rows and record blocks go straight to registers; only K
+  // (read transposed by every wave) is staged in LDS.
+  constexpr bool DIRECT = (R == 1);
+  using St = Stager<Mode, D, NWAVES, DIRECT>;
+  constexpr int STAGE_BYTES = St::TOTAL * 1024;
   constexpr int OWN = (KB + RW - 1) / RW;  // state blocks owned by one wave
   // Per-tile exchange area (RW > 1): H blocks, then Y, V', V'' (2 blocks each), 2 KiB blocks.
   constexpr int XH = 0, XY = KB * 2048, XV = XY + 2 * 2048, XD = XV + 2 * 2048;
   constexpr int XBYTES = RW > 1 ? XD + 2 * 2048 : 0;
+  // Per-wave row buffers that turn 16-byte row pieces of v and o into C fragments and back:
+  // 16 R rows x 16 columns of the input (v) and output (o) dtypes.
+  constexpr int VROWB = 16 * (int)sizeof(in_t), OROWB = 16 * (int)sizeof(OutT);
+  constexpr int WBYTES = 16 * R * (VROWB + OROWB);
   static_assert(RW == 1 || RW == 2 || RW == 4, "row waves");
-  static_assert(STAGE_BYTES + NT * XBYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGE_BYTES + NT * XBYTES + NWAVES * WBYTES <= 160 * 1024, "LDS budget");
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGE_BYTES + NT * XBYTES + 16];
+  __shared__ __attribute__((aligned(1024))) char
+      smem[STAGE_BYTES + NT * XBYTES + NWAVES * WBYTES + 16];
 
   const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -201,12 +290,14 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
   const int G = p.hv / p.hqk, m = h / G;
   const int col = 16 * (dvb * NT + tile) + idx;
   char* X = smem + STAGE_BYTES + tile * XBYTES;
+  char* Wv = smem + STAGE_BYTES + NT * XBYTES + wave * WBYTES;  // v rows of this wave
+  char* Wo = Wv + 16 * R * VROWB;                                 // o rows of this wave
 
   const in_t* Qg = static_cast<const in_t*>(p.q);
   const in_t* Kg = static_cast<const in_t*>(p.k);
   const in_t* Vg = static_cast<const in_t*>(p.v);
   OutT* Og = static_cast<OutT*>(p.o);
-  const size_t rstride = (size_t)p.hqk * D;
+  const int rs = p.hqk * ROWB;  // bytes between token rows of q / k
 
   // Owned state blocks: kb = rg + RW * o; Hc[o][hf][r] = H[16 (2 kb + hf) + 4 grp + r][col].
   f32x4 Hc[OWN][2];
@@ -238,39 +329,54 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
   auto rec_of = [&](int c) {
     return p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
   };
-  // v rows of this wave (row tiles rg*R .. rg*R+R-1) in C-fragment order, one chunk ahead.
-  // Rows past the chunk end read the last valid row and are zeroed where used. The values
-  // stay raw (one element per 32-bit register) until used, so that nothing waits on the
-  // loads before the next chunk.
-  using reg_t = typename std::conditional<std::is_same<in_t, bf16>::value, uint32_t, float>::type;
-  auto load_v = [&](int c, reg_t (&dst)[R][4]) {
+  auto row_bytes = [&](const in_t* base, int t) {
+    return reinterpret_cast<const char*>(base + (size_t)t * p.hqk * D + (size_t)m * D);
+  };
+  // v rows of this wave (row tiles rg*R .. rg*R+R-1, 16 columns of the tile), one chunk ahead,
+  // as 16-byte row pieces: piece q of the wave = row q / VPR, part q % VPR. Rows past the
+  // chunk end re-read the last valid row and are zeroed where used.
+  constexpr int VPR = VROWB / 16;                 // pieces per row
+  constexpr int VPIECES = 16 * R * VPR;           // pieces per wave
+  constexpr int VLD = (VPIECES + 63) / 64;        // loads per lane
+  auto load_v = [&](int c, f32x4 (&dst)[VLD]) {
     const int t0c = start + kChunk * c, lenc = min(kChunk, L - kChunk * c);
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = min(16 * (rg * R + i) + 4 * grp + r, lenc - 1);
-        dst[i][r] = load_raw(Vg + ((size_t)(t0c + t) * p.hv + h) * D, col);
-      }
+    for (int u = 0; u < VLD; ++u) {
+      const int q = min(64 * u + lane, VPIECES - 1);
+      const int t = min(16 * rg * R + q / VPR, lenc - 1);
+      dst[u] = *reinterpret_cast<const f32x4*>(
+          reinterpret_cast<const char*>(Vg + ((size_t)(t0c + t) * p.hv + h) * D + 16 * (dvb * NT + tile)) +
+          16 * (q % VPR));
+    }
   };
-  reg_t vnext[R][4];
-  Stager<Mode, D, NWAVES> st;
+  auto prefetch = [&](int c, St& st, RowPrefetch<Mode, D>& rp) {
+    const int t0c = start + kChunk * c, lenc = min(kChunk, L - kChunk * c);
+    st.load(row_bytes(Kg, t0c), row_bytes(Qg, t0c), rec_of(c), lenc, rs, wave, lane);
+    if constexpr (DIRECT)
+      rp.load(reinterpret_cast<const in_t*>(row_bytes(Qg, t0c + min(16 * rg + idx, lenc - 1))),
+              rec_of(c), rg, grp, lane);
+  };
+  f32x4 vnext[VLD];
+  St st;
+  RowPrefetch<Mode, D> rpn;
   if (nchunks > 0) {
     load_v(0, vnext);
-    st.load(Kg, Qg, rec_of(0), start, min(kChunk, L), rstride, m, wave, lane);
+    prefetch(0, st, rpn);
   }
-  // Output rows of the previous chunk, stored after the next chunk's barrier so that the
-  // wait for the prefetch never waits for fresh stores.
-  f32x4 Oprev[R];
+  // Output rows of the previous chunk (in Wo), stored as 16-byte row pieces after the next
+  // chunk's barrier so that the wait for the prefetch never waits for fresh stores.
+  constexpr int OPR = OROWB / 16, OPIECES = 16 * R * OPR, OST = (OPIECES + 63) / 64;
   int t0prev = 0, lenprev = 0;
   auto store_prev = [&]() {
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * (rg * R + i) + 4 * grp + r;
-        if (t < lenprev) Og[((size_t)(t0prev + t) * p.hv + h) * D + col] = from_f32<OutT>(Oprev[i][r]);
-      }
+    for (int u = 0; u < OST; ++u) {
+      const int q = 64 * u + lane;
+      const int t = 16 * rg * R + q / OPR;
+      if (q < OPIECES && t < lenprev)
+        *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(
+            Og + ((size_t)(t0prev + t) * p.hv + h) * D + 16 * (dvb * NT + tile)) + 16 * (q % OPR)) =
+            *reinterpret_cast<const f32x4*>(Wo + 16 * q);
+    }
   };
 
   for (int c = 0; c < nchunks; ++c) {
@@ -280,24 +386,44 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c (and its v rows) landed
     lds_barrier();                  // every wave is done with chunk c-1's LDS
     st.commit(S, wave, lane);
+    RowPrefetch<Mode, D> rp = rpn;
+#pragma unroll
+    for (int u = 0; u < VLD; ++u)
+      if (64 * u + lane < VPIECES) *reinterpret_cast<f32x4*>(Wv + 16 * (64 * u + lane)) = vnext[u];
     lds_barrier();                  // chunk c staged
-    float vv[R][4];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vv[i][r] = (16 * (rg * R + i) + 4 * grp + r < len) ? raw_to_f32(vnext[i][r], col) : 0.f;
     if (c + 1 < nchunks) {
       load_v(c + 1, vnext);
-      st.load(Kg, Qg, rec_of(c + 1), t0 + kChunk, min(kChunk, L - kChunk * (c + 1)), rstride, m,
-              wave, lane);
+      prefetch(c + 1, st, rpn);
     }
     if (c > 0) store_prev();
+    float vv[R][4];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const f32x4 v4 = VRows<in_t>::cfrag(Wv + 16 * i * VROWB, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vv[i][r] = (16 * (rg * R + i) + 4 * grp + r < len) ? v4[r] : 0.f;
+    }
     const char* sK = S;
-    const char* sQ = S + KBYTES;
-    const char* sTP = S + 2 * KBYTES;
+    const char* sQ = S + KBYTES;            // (staged layouts only)
+    const char* sTP = S + 2 * KBYTES;       // (staged layouts only)
     const float* sgam = reinterpret_cast<const float*>(sTP + kWsGOff);
     const float* sdel = reinterpret_cast<const float*>(sTP + kWsDOff);
+    auto tblock = [&](int i, int rt, int kb) -> Op {
+      if constexpr (DIRECT) return rp.tb[kb];
+      else return Mode::load_block(sTP + kWsTOff + tri_block(rt, kb) * 2048, lane);
+    };
+    auto pblock = [&](int i, int rt, int kb) -> Op {
+      if constexpr (DIRECT) return rp.pb[kb];
+      else return Mode::load_block(sTP + kWsPOff + tri_block(rt, kb) * 2048, lane);
+    };
+    auto gamma4 = [&](int rt) -> f32x4 {
+      if constexpr (DIRECT) return rp.gam;
+      else return *reinterpret_cast<const f32x4*>(sgam + 16 * rt + 4 * grp);
+    };
+    auto delta4 = [&](int rt) -> f32x4 {
+      if constexpr (DIRECT) return rp.del;
+      else return *reinterpret_cast<const f32x4*>(sdel + 16 * rt + 4 * grp);
+    };
 
     // (a) state as split B fragments over d_k
     Op HB[KB];
@@ -313,22 +439,27 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       for (int kb = 0; kb < KB; ++kb) HB[kb] = Mode::load_block(X + XH + kb * 2048, lane);
     }
 
-    // (b) K H, Q H on this wave's row tiles; Y = V - gamma K H, gamma Q H
+    // (b) K H, Q H on this wave's row tiles; Y = V - gamma K H, gamma Q H.
+    // Two accumulators per product (even / odd depth blocks) halve the dependent chains.
     f32x4 QH[R], Y[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int rt = rg * R + i;
-      f32x4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
+      f32x4 kh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      f32x4 qh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        kh = Mode::mma_xs(kh, F::a(sK, 16 * rt + idx, kb, grp), HB[kb]);
-        qh = Mode::mma_xs(qh, F::a(sQ, 16 * rt + idx, kb, grp), HB[kb]);
+        typename Mode::frag_t qa;
+        if constexpr (DIRECT) qa = Half<Mode>::join(rp.qlo[kb], rp.qhi[kb]);
+        else qa = F::a(sQ, 16 * rt + idx, kb, grp);
+        kh[kb & 1] = Mode::mma_xs(kh[kb & 1], F::a(sK, 16 * rt + idx, kb, grp), HB[kb]);
+        qh[kb & 1] = Mode::mma_xs(qh[kb & 1], qa, HB[kb]);
       }
-      const f32x4 gam = *reinterpret_cast<const f32x4*>(sgam + 16 * rt + 4 * grp);
+      const f32x4 gam = gamma4(rt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        Y[i][r] = vv[i][r] - gam[r] * kh[r];
-        QH[i][r] = gam[r] * qh[r];
+        Y[i][r] = vv[i][r] - gam[r] * (kh[0][r] + kh[1][r]);
+        QH[i][r] = gam[r] * (qh[0][r] + qh[1][r]);
       }
     }
 
@@ -361,9 +492,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1))
-          acc = Mode::mma_ss(acc, Mode::load_block(sTP + kWsTOff + tri_block(rt, kb) * 2048, lane),
-                             YB[kb]);
+        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, tblock(i, rt, kb), YB[kb]);
       Vp[i] = acc;
     }
 
@@ -374,8 +503,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       for (int kb = 0; kb < 2; ++kb) {
         float x[8], d[8];
         pack_c_pair(Vp[2 * kb], Vp[2 * kb + 1], x);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(sdel + 32 * kb + 4 * grp);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(sdel + 32 * kb + 16 + 4 * grp);
+        const f32x4 d0 = delta4(2 * kb), d1 = delta4(2 * kb + 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           d[s] = x[s] * d0[s];
@@ -388,9 +516,8 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int rt = rg * R + i;
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(sdel + 16 * rt + 4 * grp);
         store_half(Mode{}, X + XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
-        store_half(Mode{}, X + XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * dl);
+        store_half(Mode{}, X + XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
       }
       lds_barrier();
 #pragma unroll
@@ -401,7 +528,9 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
     }
 
     // (g) owned state blocks first (the next chunk waits on them): H <- gamma_C H + K^T V''
-    const float gC = sgam[kChunk - 1];
+    float gC;
+    if constexpr (DIRECT) gC = rp.gC;
+    else gC = sgam[kChunk - 1];
 #pragma unroll
     for (int o = 0; o < OWN; ++o) {
       const int kb = rg + RW * o;
@@ -429,10 +558,11 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       f32x4 acc = QH[i];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1))
-          acc = Mode::mma_ss(acc, Mode::load_block(sTP + kWsPOff + tri_block(rt, kb) * 2048, lane),
-                             VB[kb]);
-      Oprev[i] = acc * p.scale;
+        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, pblock(i, rt, kb), VB[kb]);
+      const f32x4 o4 = acc * p.scale;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        reinterpret_cast<OutT*>(Wo + (16 * i + 4 * grp + r) * OROWB)[idx] = from_f32<OutT>(o4[r]);
     }
     t0prev = t0;
     lenprev = len;
