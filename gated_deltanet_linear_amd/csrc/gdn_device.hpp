@@ -213,26 +213,19 @@ __device__ __forceinline__ int swz_off(int row, int col) {
   return row * ROWB + (((byte >> 4) ^ swz<ROWB>(row)) << 4) + (byte & 15);
 }
 
-// A fragment of a [64 x D] row-major staged matrix (rows = tokens, depth = d_k):
-// lane (idx, grp) gets row `row`, depth 32 kb + kslot(grp, s).
+// A fragment of a [64 x D] row-major staged matrix (rows = tokens, depth = d_k). Contractions
+// over d_k use a column-contiguous depth order: lane (idx, grp) gets row `row`, columns
+// 32 kb + 8 grp + s for slot s = 0..7, i.e. one 16-byte (bf16) or 32-byte (f32) piece. Both
+// operands of a d_k contraction must use this order; the scan keeps its state rows in it.
 template <int ROWB>
 __device__ __forceinline__ bf16x8 afrag(const char* buf, int row, int kb, int grp) {
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(buf + swz_off<ROWB, 2>(row, 32 * kb + 4 * grp));
-  const bf16x4 hi =
-      *reinterpret_cast<const bf16x4*>(buf + swz_off<ROWB, 2>(row, 32 * kb + 16 + 4 * grp));
-  bf16x8 f;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    f[s] = lo[s];
-    f[4 + s] = hi[s];
-  }
-  return f;
+  return *reinterpret_cast<const bf16x8*>(buf + swz_off<ROWB, 2>(row, 32 * kb + 8 * grp));
 }
 template <int ROWB>
 __device__ __forceinline__ f32x8 afrag_f32(const char* buf, int row, int kb, int grp) {
-  const f32x4 lo = *reinterpret_cast<const f32x4*>(buf + swz_off<ROWB, 4>(row, 32 * kb + 4 * grp));
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(buf + swz_off<ROWB, 4>(row, 32 * kb + 8 * grp));
   const f32x4 hi =
-      *reinterpret_cast<const f32x4*>(buf + swz_off<ROWB, 4>(row, 32 * kb + 16 + 4 * grp));
+      *reinterpret_cast<const f32x4*>(buf + swz_off<ROWB, 4>(row, 32 * kb + 8 * grp + 4));
   f32x8 f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {

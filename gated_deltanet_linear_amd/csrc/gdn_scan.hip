@@ -41,11 +41,19 @@ struct ScanParams {
   float scale;
 };
 
-// A fragment of K^T (rows = d_k tile `it`, depth = tokens of block kbp) from the row-major
+// d_k index of row m of state tile `it` (16 rows): tiles 2 kb and 2 kb + 1 interleave their
+// 4-row groups inside the 32 columns of block kb, so that the C fragments of the two tiles
+// stack into a B fragment in the column-contiguous depth order of afrag
+// (row 4 g + r of tile 2 kb + hf is column 32 kb + 8 g + 4 hf + r).
+__device__ __forceinline__ int state_row(int it, int m) {
+  return 32 * (it >> 1) + 8 * (m >> 2) + 4 * (it & 1) + (m & 3);
+}
+
+// A fragment of K^T (rows = state tile `it`, depth = tokens of block kbp) from the row-major
 // staged K. ds_read_b64_tr_b16 hands lane (g, 4a + b) element e of the 8 bytes that lane
-// (g, a + 4e) addressed; lane (g, a + 4e) addresses row 4g + e, columns 16 it + 4a .. +3, so
-// lane (g, i) receives K[tok0 + 4g + e][16 it + i] for e = 0..3 (slots 0-3, or 4-7 for the
-// second 16 tokens).
+// (g, a + 4e) addressed; lane (g, a + 4e) addresses token row 4g + e at the 4 columns
+// state_row(it, 4a .. 4a + 3), so lane (g, i) receives K[tok0 + 4g + e][state_row(it, i)] for
+// e = 0..3 (slots 0-3, or 4-7 for the second 16 tokens).
 template <int ROWB>
 __device__ __forceinline__ bf16x8 ktfrag(const char* sK, int it, int kbp, int lane) {
   const int g = lane >> 4, s = lane & 15, a = s & 3, e = s >> 2;
@@ -54,7 +62,7 @@ __device__ __forceinline__ bf16x8 ktfrag(const char* sK, int it, int kbp, int la
   for (int hf = 0; hf < 2; ++hf) {
     const int row = 32 * kbp + 16 * hf + 4 * g + e;
     const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(sK + swz_off<ROWB, 2>(row, 16 * it + 4 * a)));
+        (__attribute__((address_space(3))) s16x4*)(sK + swz_off<ROWB, 2>(row, state_row(it, 4 * a))));
     const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
 #pragma unroll
     for (int j = 0; j < 4; ++j) f[4 * hf + j] = tb[j];
@@ -68,7 +76,7 @@ __device__ __forceinline__ f32x8 ktfrag_f32(const char* sK, int it, int kbp, int
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     f[s] = *reinterpret_cast<const float*>(
-        sK + swz_off<ROWB, 4>(32 * kbp + kslot(g, s), 16 * it + idx));
+        sK + swz_off<ROWB, 4>(32 * kbp + kslot(g, s), state_row(it, idx)));
   return f;
 }
 
@@ -189,45 +197,14 @@ struct VRows<float> {
   }
 };
 
-// Half of a 32-deep operand fragment (4 consecutive depth indices): bf16x4 or f32x4.
-template <typename Mode>
-struct Half;
-template <>
-struct Half<Bf16Mode> {
-  using type = bf16x4;
-  __device__ static bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
-    bf16x8 f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      f[s] = lo[s];
-      f[4 + s] = hi[s];
-    }
-    return f;
-  }
-};
-template <>
-struct Half<F32Mode> {
-  using type = f32x4;
-  __device__ static f32x8 join(const f32x4& lo, const f32x4& hi) {
-    f32x8 f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      f[s] = lo[s];
-      f[4 + s] = hi[s];
-    }
-    return f;
-  }
-};
-
 // Per-wave register prefetch of the row-split layout (one row tile rt per wave): the Q rows
 // of the tile as A fragments, the T diag(beta) and P blocks of the tile, and gamma / delta of
 // its rows, all loaded straight from memory in the order they are consumed.
 template <typename Mode, int D>
 struct RowPrefetch {
-  using half_t = typename Half<Mode>::type;
   using Op = typename Mode::Op;
   static constexpr int KB = D / 32;
-  half_t qlo[KB], qhi[KB];
+  typename Mode::frag_t qf[KB];
   Op tb[2], pb[2];
   f32x4 gam, del;
   float gC;
@@ -235,10 +212,8 @@ struct RowPrefetch {
   __device__ __forceinline__ void load(const typename Mode::in_t* Qrow, const char* rec, int rt,
                                        int grp, int lane) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      qlo[kb] = *reinterpret_cast<const half_t*>(Qrow + 32 * kb + 4 * grp);
-      qhi[kb] = *reinterpret_cast<const half_t*>(Qrow + 32 * kb + 16 + 4 * grp);
-    }
+    for (int kb = 0; kb < KB; ++kb)
+      qf[kb] = *reinterpret_cast<const typename Mode::frag_t*>(Qrow + 32 * kb + 8 * grp);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
       if (kb <= (rt >> 1)) {
@@ -299,7 +274,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
   OutT* Og = static_cast<OutT*>(p.o);
   const int rs = p.hqk * ROWB;  // bytes between token rows of q / k
 
-  // Owned state blocks: kb = rg + RW * o; Hc[o][hf][r] = H[16 (2 kb + hf) + 4 grp + r][col].
+  // Owned state blocks: kb = rg + RW * o; Hc[o][hf][r] = H[state_row(2 kb + hf, 4 grp + r)][col].
   f32x4 Hc[OWN][2];
   {
     const float* H0 = p.h0 ? p.h0 + (size_t)nh * D * D : nullptr;
@@ -310,7 +285,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          Hc[o][hf][r] = (H0 && kb < KB) ? H0[(size_t)(16 * (2 * kb + hf) + 4 * grp + r) * D + col]
+          Hc[o][hf][r] = (H0 && kb < KB) ? H0[(size_t)state_row(2 * kb + hf, 4 * grp + r) * D + col]
                                          : 0.f;
       if constexpr (RW > 1) {
         if (kb < KB) {
@@ -450,7 +425,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         typename Mode::frag_t qa;
-        if constexpr (DIRECT) qa = Half<Mode>::join(rp.qlo[kb], rp.qhi[kb]);
+        if constexpr (DIRECT) qa = rp.qf[kb];
         else qa = F::a(sQ, 16 * rt + idx, kb, grp);
         kh[kb & 1] = Mode::mma_xs(kh[kb & 1], F::a(sK, 16 * rt + idx, kb, grp), HB[kb]);
         qh[kb & 1] = Mode::mma_xs(qh[kb & 1], qa, HB[kb]);
@@ -579,7 +554,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            HT[(size_t)(16 * (2 * kb + hf) + 4 * grp + r) * D + col] = Hc[o][hf][r];
+            HT[(size_t)state_row(2 * kb + hf, 4 * grp + r) * D + col] = Hc[o][hf][r];
     }
   }
 }
