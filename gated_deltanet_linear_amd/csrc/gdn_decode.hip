@@ -9,36 +9,47 @@
 //   o  = scale (a qh + qk u)  = scale H'^T q          (no second pass over the state)
 //
 // The step moves 2 * d_k * d_v * 4 bytes of state per head and does ~7 d_k d_v flops, so it is
-// bound by HBM. One 256-thread workgroup owns one head: thread (cg, rg) keeps a float4 column
-// group cg for rows rg, rg + RG, ... in registers between the read and the write, so every
-// state byte crosses HBM exactly once each way. A wave's load instruction covers whole
-// contiguous rows (coalesced 16-byte lanes); loads and stores are non-temporal since the state
-// is not reused by this step.
+// bound by HBM. One workgroup owns one head (columns could be split across workgroups, but
+// then every load covers 128-byte pieces of rows instead of whole rows, which streams slower):
+// thread (cg, rg) keeps a float4 column group cg for rows rg, rg + RG, ... in registers between
+// the read and the write, so every state byte crosses HBM exactly once each way. A wave's load
+// instruction covers whole contiguous rows (coalesced 16-byte lanes); loads and stores are
+// non-temporal since the state is not reused by this step. The row reductions run over lanes
+// first (xor shuffles across the row groups of a wave), then over waves through LDS.
 #include "gdn_device.hpp"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
+// Threads per workgroup: 512 for 128 x 128 heads (8 rows per thread: enough loads in flight
+// per wave without limiting occupancy), fewer for small heads (at least 2 rows per thread).
+template <int DK, int DV>
+constexpr int step_threads() {
+  return DK * DV / 8 < 512 ? DK * DV / 8 : 512;
+}
+
 template <typename InT, typename OutT, int DK, int DV>
-__global__ __launch_bounds__(256) void recurrent_step_kernel(
+__global__ __launch_bounds__((step_threads<DK, DV>())) void recurrent_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
     OutT* __restrict__ o, int hqk, int hv, float scale) {
+  constexpr int NTH = step_threads<DK, DV>();
+  constexpr int NW = NTH / 64;  // waves
   constexpr int CG = DV / 4;    // float4 column groups per row
-  constexpr int RG = 256 / CG;  // row groups
+  constexpr int RG = NTH / CG;  // row groups
   constexpr int R = DK / RG;    // rows per thread
-  static_assert(DV % 4 == 0 && 256 % CG == 0 && DK % RG == 0 && R >= 1, "tile shape");
+  static_assert(DV % 4 == 0 && NTH % 64 == 0 && 64 % CG == 0 && DK % RG == 0 && R >= 1,
+                "tile shape");
 
-  __shared__ f32x4 red_k[RG][CG];
-  __shared__ f32x4 red_q[RG][CG];
-  __shared__ float red_qk[RG];
-  __shared__ f32x4 u_sh[CG];
+  __shared__ f32x4 red_k[NW][CG];
+  __shared__ f32x4 red_q[NW][CG];
+  __shared__ float red_qk[NW];
 
   const int nh = blockIdx.x;  // n * hv + h
   const int n = nh / hv, h = nh - (nh / hv) * hv;
   const int m = h / (hv / hqk);
-  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG, lane = tid & 63, wave = tid >> 6;
 
   f32x4* S = reinterpret_cast<f32x4*>(state + (size_t)nh * DK * DV);
   const InT* qv = q + ((size_t)n * hqk + m) * DK;
@@ -65,33 +76,41 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     pq += s[r] * qi[r];
     pqk += qi[r] * ki[r];
   }
-  red_k[rg][cg] = pk;
-  red_q[rg][cg] = pq;
-  if (cg == 0) red_qk[rg] = pqk;
+  // Lanes cg, cg + CG, ... of a wave hold the same columns for different rows.
+#pragma unroll
+  for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pk[c] += __shfl_xor(pk[c], off);
+      pq[c] += __shfl_xor(pq[c], off);
+    }
+    pqk += __shfl_xor(pqk, off);
+  }
+  if (lane < CG) {
+    red_k[wave][lane] = pk;
+    red_q[wave][lane] = pq;
+    if (lane == 0) red_qk[wave] = pqk;
+  }
   __syncthreads();
 
+  f32x4 sk = red_k[0][cg], sq = red_q[0][cg];
+  float qk = red_qk[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    sk += red_k[w][cg];
+    sq += red_q[w][cg];
+    qk += red_qk[w];
+  }
+  const InT* vv = v + (size_t)nh * DV + 4 * cg;
+  f32x4 u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) u[c] = bt * (to_f32(vv[c]) - alpha * sk[c]);
   if (rg == 0) {
-    f32x4 sk = red_k[0][cg], sq = red_q[0][cg];
-#pragma unroll
-    for (int j = 1; j < RG; ++j) {
-      sk += red_k[j][cg];
-      sq += red_q[j][cg];
-    }
-    float qk = 0.f;
-#pragma unroll
-    for (int j = 0; j < RG; ++j) qk += red_qk[j];
-    const InT* vv = v + (size_t)nh * DV + 4 * cg;
-    f32x4 u;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) u[c] = bt * (to_f32(vv[c]) - alpha * sk[c]);
-    u_sh[cg] = u;
     OutT* ov = o + (size_t)nh * DV + 4 * cg;
 #pragma unroll
     for (int c = 0; c < 4; ++c) ov[c] = from_f32<OutT>(scale * (alpha * sq[c] + qk * u[c]));
   }
-  __syncthreads();
 
-  const f32x4 u = u_sh[cg];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     f32x4 nv = s[r] * alpha + u * ki[r];
@@ -105,7 +124,8 @@ hipError_t launch_step_t(const gdn_shape_t& s, const void* q, const void* k, con
                          hipStream_t stream) {
   const unsigned blocks = (unsigned)s.num_seqs * (unsigned)s.num_v_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_step_kernel<InT, OutT, D, D>), dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((recurrent_step_kernel<InT, OutT, D, D>), dim3(blocks),
+                     dim3(step_threads<D, D>()), 0, stream,
                      static_cast<const InT*>(q), static_cast<const InT*>(k),
                      static_cast<const InT*>(v), g, beta, state, static_cast<OutT*>(o),
                      s.num_qk_heads, s.num_v_heads, s.scale);
