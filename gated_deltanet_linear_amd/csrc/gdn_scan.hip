@@ -118,67 +118,22 @@ __device__ __forceinline__ void store_half(F32Mode, char* blk, int lane, int hal
   *reinterpret_cast<f32x4*>(blk + lane * 32 + half * 16) = x;
 }
 
-constexpr int kRecUnits = kWsRecordBytes / 16;               // 16-byte units per record
+constexpr int kRecUnits = kWsRecordBytes / 16;                   // 16-byte units per record
 constexpr int kRecStage = (kWsRecordBytes + 1023) / 1024 * 1024;  // staged record bytes
+constexpr int kLdsBytes = 160 * 1024;                             // LDS per workgroup
 
-// Staged chunk data, prefetched into registers with ordinary 16-byte global loads one chunk
-// ahead and written to LDS at the start of the chunk that uses it (global_load_lds reaches only
-// ~38 B/clk per CU on this part; plain loads into registers several times that). Unit j of
-// 1 KiB goes to LDS bytes [1024 j, 1024 j + 1024): units [0, KI) are K rows, then (unless
-// KONLY) Q rows and the workspace record. q/k rows are row-major with a 16-byte XOR swizzle;
-// rows past len re-read row len - 1 (finite values that only meet zero coefficients); record
-// lanes past its end re-read its last 16 bytes into the padding.
-template <typename Mode, int D, int NWAVES, bool KONLY>
-struct Stager {
-  using in_t = typename Mode::in_t;
-  static constexpr int ROWB = D * (int)sizeof(in_t), NCH = ROWB / 16, KBYTES = 64 * ROWB;
-  static constexpr int RPU = 64 / NCH;  // rows per 1 KiB unit
-  static constexpr int KI = KBYTES / 1024, QI = KONLY ? 0 : KI, RI = KONLY ? 0 : kRecStage / 1024;
-  static constexpr int TOTAL = KI + QI + RI;
-  static constexpr int PER = (TOTAL + NWAVES - 1) / NWAVES;
-  f32x4 r[PER];
-
-  // Kb, Qb: bytes of row t0 of head m; rs: bytes between rows.
-  __device__ __forceinline__ void load(const char* Kb, const char* Qb, const char* rec, int len,
-                                       int rs, int wave, int lane) {
-    const int lrow = lane / NCH, ch = lane % NCH;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int j = wave + NWAVES * u;
-      if (j < TOTAL) {
-        const char* src;
-        if (j < KI + QI) {
-          const int jj = j < KI ? j : j - KI;
-          const int row = jj * RPU + lrow;
-          const int rr = row < len ? row : len - 1;
-          src = (j < KI ? Kb : Qb) + rr * rs + 16 * (ch ^ swz<ROWB>(row));
-        } else {
-          src = rec + 16 * min(64 * (j - KI - QI) + lane, kRecUnits - 1);
-        }
-        r[u] = *reinterpret_cast<const f32x4*>(src);
-      }
-    }
-  }
-  __device__ __forceinline__ void commit(char* S, int wave, int lane) const {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int j = wave + NWAVES * u;
-      if (j < TOTAL) *reinterpret_cast<f32x4*>(S + 1024 * j + 16 * lane) = r[u];
-    }
-  }
-};
-
-// C fragment (rows 4 grp + r, column idx) of a 16 x 16 tile stored row-major in LDS.
-// bf16: one ds_read_b64_tr_b16 (lane (g, a + 4e) addresses row 4g + e, columns 4a .. 4a+3;
-// lane (g, 4a + b) receives element b of those, i.e. row 4g + e, column 4a + b, for e = 0..3).
+// C fragment (rows 4 grp + r, column idx) of a 16 x 16 tile stored row-major in LDS with row
+// stride `stride` bytes. bf16: one ds_read_b64_tr_b16 (lane (g, a + 4e) addresses row 4g + e,
+// columns 4a .. 4a+3; lane (g, 4a + b) receives element b of those, i.e. row 4g + e, column
+// 4a + b, for e = 0..3).
 template <typename T>
 struct VRows;
 template <>
 struct VRows<bf16> {
-  __device__ static f32x4 cfrag(const char* tile, int lane) {
+  __device__ static f32x4 cfrag(const char* tile, int stride, int lane) {
     const int g = lane >> 4, s = lane & 15, a = s & 3, e = s >> 2;
     const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(tile + (4 * g + e) * 32 + 8 * a));
+        (__attribute__((address_space(3))) s16x4*)(tile + (4 * g + e) * stride + 8 * a));
     const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
     f32x4 out;
 #pragma unroll
@@ -188,91 +143,197 @@ struct VRows<bf16> {
 };
 template <>
 struct VRows<float> {
-  __device__ static f32x4 cfrag(const char* tile, int lane) {
+  __device__ static f32x4 cfrag(const char* tile, int stride, int lane) {
     const int g = lane >> 4, i = lane & 15;
     f32x4 out;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) out[r] = reinterpret_cast<const float*>(tile + (4 * g + r) * 64)[i];
+    for (int r = 0; r < 4; ++r)
+      out[r] = reinterpret_cast<const float*>(tile + (4 * g + r) * stride)[i];
     return out;
   }
 };
 
-// Per-wave register prefetch of the row-split layout (one row tile rt per wave): the Q rows
-// of the tile as A fragments, the T diag(beta) and P blocks of the tile, and gamma / delta of
-// its rows, all loaded straight from memory in the order they are consumed.
-template <typename Mode, int D>
-struct RowPrefetch {
-  using Op = typename Mode::Op;
-  static constexpr int KB = D / 32;
-  typename Mode::frag_t qf[KB];
-  Op tb[2], pb[2];
-  f32x4 gam, del;
-  float gC;
-
-  __device__ __forceinline__ void load(const typename Mode::in_t* Qrow, const char* rec, int rt,
-                                       int grp, int lane) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      qf[kb] = *reinterpret_cast<const typename Mode::frag_t*>(Qrow + 32 * kb + 8 * grp);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (kb <= (rt >> 1)) {
-        tb[kb] = Mode::load_block(rec + kWsTOff + tri_block(rt, kb) * kWsBlockBytes, lane);
-        pb[kb] = Mode::load_block(rec + kWsPOff + tri_block(rt, kb) * kWsBlockBytes, lane);
-      }
-    gam = *reinterpret_cast<const f32x4*>(rec + kWsGOff + 4 * (16 * rt + 4 * grp));
-    del = *reinterpret_cast<const f32x4*>(rec + kWsDOff + 4 * (16 * rt + 4 * grp));
-    gC = *reinterpret_cast<const float*>(rec + kWsGOff + 4 * (kChunk - 1));
-  }
+// Shapes of one scan workgroup: NT tiles of 16 d_v columns x RW waves per tile compute
+// (NC waves), NP producer waves stage the chunks and store the outputs.
+//
+// A staged chunk (one LDS buffer) holds, in 1 KiB units:
+//   [0, KI)            K rows, row-major, 16-byte XOR swizzle (swz)
+//   [KI, 2 KI)         Q rows, same layout
+//   [2 KI, 2 KI + RI)  the workspace record of the chunk (T diag(beta), P, gamma, delta)
+//   [2 KI + RI, TOTAL) the v rows of the workgroup's NT * 16 columns, row stride VSTR
+// Rows past the end of a sequence re-read its last row (finite values that only ever meet zero
+// coefficients); record lanes past its end re-read its last 16 bytes into the padding.
+template <typename Mode, int D, int NT, int RW, typename OutT>
+struct ScanCfg {
+  using in_t = typename Mode::in_t;
+  static constexpr int ROWB = D * (int)sizeof(in_t), KBYTES = 64 * ROWB;
+  static constexpr int NCH = ROWB / 16, RPU = 64 / NCH;  // 16-byte chunks per row, rows per unit
+  static constexpr int KI = KBYTES / 1024, RI = kRecStage / 1024;
+  static constexpr int VROWB = 16 * (int)sizeof(in_t), VPR = VROWB / 16;  // one tile row of v
+  static constexpr int VSTR = NT * VROWB + (NT > 1 ? 16 : 0);  // padded: tile reads spread banks
+  static constexpr int VI = 64 * NT * VPR / 64;                // v units
+  static constexpr int TOTAL = 2 * KI + RI + VI;
+  static constexpr int QOFF = KBYTES, ROFF = 2 * KBYTES, VOFF = 2 * KBYTES + kRecStage;
+  static constexpr int BUFB = VOFF + 64 * VSTR;
+  static constexpr int NC = NT * RW;
+  static constexpr int NP = (TOTAL + 31) / 32;  // producers hold <= 32 units each in registers
+  static constexpr int PER = (TOTAL + NP - 1) / NP;
+  static constexpr int THREADS = 64 * (NC + NP);
+  static constexpr int KB = D / 32, R = 4 / RW, OWN = (KB + RW - 1) / RW;
+  // Per-tile exchange area (RW > 1): H blocks, then Y, V', V'' (2 blocks each), 2 KiB blocks.
+  static constexpr int XH = 0, XY = KB * 2048, XV = XY + 2 * 2048, XD = XV + 2 * 2048;
+  static constexpr int XBYTES = RW > 1 ? XD + 2 * 2048 : 0;
+  // Output rows of a chunk: 64 rows of NT * 16 columns, row stride OSTR (two buffers).
+  static constexpr int OROWB = 16 * (int)sizeof(OutT), OPR = OROWB / 16;
+  static constexpr int OSTR = NT * OROWB + (NT > 1 ? 16 : 0);
+  static constexpr int OBYTES = 64 * OSTR;
+  static constexpr int OPIECES = 64 * NT * OPR, OST = (OPIECES + 64 * NP - 1) / (64 * NP);
+  static constexpr int FIXED = NT * XBYTES + 2 * OBYTES;
+  static constexpr int NBUF = 2 * BUFB + FIXED <= kLdsBytes ? 2 : 1;
+  static constexpr int LDS = NBUF * BUFB + FIXED;
+  static_assert(LDS <= kLdsBytes, "LDS budget");
+  static_assert(RW == 1 || RW == 4, "row waves");
+  static_assert(NC + NP <= 16 && NP <= 4, "waves per workgroup");
 };
 
 template <typename Mode, int D, int NT, int RW, typename OutT>
-__global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) {
+__global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chunk_scan_kernel(
+    ScanParams p) {
+  using C = ScanCfg<Mode, D, NT, RW, OutT>;
   using in_t = typename Mode::in_t;
   using Op = typename Mode::Op;
-  using F = Frags<Mode, D * (int)sizeof(in_t)>;
-  constexpr int ROWB = D * (int)sizeof(in_t);
-  constexpr int KBYTES = 64 * ROWB;
-  constexpr int KB = D / 32;        // 32-deep blocks over d_k
-  constexpr int R = 4 / RW;         // row tiles per wave
-  constexpr int NWAVES = NT * RW;
-  // Row-split layout: each wave's Q rows and record blocks go straight to registers; only K
-  // (read transposed by every wave) is staged in LDS.
-  constexpr bool DIRECT = (R == 1);
-  using St = Stager<Mode, D, NWAVES, DIRECT>;
-  constexpr int STAGE_BYTES = St::TOTAL * 1024;
-  constexpr int OWN = (KB + RW - 1) / RW;  // state blocks owned by one wave
-  // Per-tile exchange area (RW > 1): H blocks, then Y, V', V'' (2 blocks each), 2 KiB blocks.
-  constexpr int XH = 0, XY = KB * 2048, XV = XY + 2 * 2048, XD = XV + 2 * 2048;
-  constexpr int XBYTES = RW > 1 ? XD + 2 * 2048 : 0;
-  // Per-wave row buffers that turn 16-byte row pieces of v and o into C fragments and back:
-  // 16 R rows x 16 columns of the input (v) and output (o) dtypes.
-  constexpr int VROWB = 16 * (int)sizeof(in_t), OROWB = 16 * (int)sizeof(OutT);
-  constexpr int WBYTES = 16 * R * (VROWB + OROWB);
-  static_assert(RW == 1 || RW == 2 || RW == 4, "row waves");
-  static_assert(STAGE_BYTES + NT * XBYTES + NWAVES * WBYTES <= 160 * 1024, "LDS budget");
+  using F = Frags<Mode, C::ROWB>;
+  constexpr int KB = C::KB, R = C::R, OWN = C::OWN;
 
-  __shared__ __attribute__((aligned(1024))) char
-      smem[STAGE_BYTES + NT * XBYTES + NWAVES * WBYTES + 16];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  char* const Xbase = smem + C::NBUF * C::BUFB;
+  char* const Wo = Xbase + NT * C::XBYTES;  // two output buffers of OBYTES
 
   const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int tile = wave / RW, rg = wave % RW;
   constexpr int NB = D / 16 / NT;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int dvb = lid % NB, nh = lid / NB;
   const int h = nh % p.hv, n = nh / p.hv;
   const int G = p.hv / p.hqk, m = h / G;
-  const int col = 16 * (dvb * NT + tile) + idx;
-  char* X = smem + STAGE_BYTES + tile * XBYTES;
-  char* Wv = smem + STAGE_BYTES + NT * XBYTES + wave * WBYTES;  // v rows of this wave
-  char* Wo = Wv + 16 * R * VROWB;                                 // o rows of this wave
+  const int start = p.cu[n];
+  const int L = p.cu[n + 1] - start;
+  const int nchunks = (L + kChunk - 1) / kChunk;
+  auto chunk_buf = [&](int c) -> char* { return smem + (C::NBUF == 2 ? (c & 1) * C::BUFB : 0); };
 
-  const in_t* Qg = static_cast<const in_t*>(p.q);
-  const in_t* Kg = static_cast<const in_t*>(p.k);
-  const in_t* Vg = static_cast<const in_t*>(p.v);
-  OutT* Og = static_cast<OutT*>(p.o);
-  const int rs = p.hqk * ROWB;  // bytes between token rows of q / k
+  if (wave >= C::NC) {
+    // ---------------- producer waves ----------------
+    // Each producer runs its own copy of the code with its index known at compile time, so
+    // the kind of every staged unit (K, Q, record or v rows) is fixed in the code.
+    const in_t* Qg = static_cast<const in_t*>(p.q);
+    const in_t* Kg = static_cast<const in_t*>(p.k);
+    const in_t* Vg = static_cast<const in_t*>(p.v);
+    OutT* Og = static_cast<OutT*>(p.o);
+    const int rs = p.hqk * C::ROWB;                    // bytes between token rows of q / k
+    const int vrs = p.hv * D * (int)sizeof(in_t);      // ... of v
+    const int ors = p.hv * D * (int)sizeof(OutT);      // ... of o
+    const int slot0 = slot_base(p.cu, n);
+    auto run = [&](auto pw_const) {
+      constexpr int PW = decltype(pw_const)::value;
+      f32x4 r[C::PER];
+      auto load = [&](int c) {
+        const int t0c = start + kChunk * c, lenc = min(kChunk, L - kChunk * c);
+        const char* Kb = reinterpret_cast<const char*>(Kg + (size_t)t0c * p.hqk * D + (size_t)m * D);
+        const char* Qb = reinterpret_cast<const char*>(Qg + (size_t)t0c * p.hqk * D + (size_t)m * D);
+        const char* rec = p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
+        const char* Vb = reinterpret_cast<const char*>(Vg + (size_t)t0c * p.hv * D + (size_t)h * D +
+                                                       16 * dvb * NT);
+#pragma unroll
+        for (int u = 0; u < C::PER; ++u) {
+          const int j = PW + C::NP * u;
+          if (j < C::TOTAL) {
+            // Uniform base + 32-bit lane offset (one VGPR per address in flight).
+            const char* base;
+            unsigned off;
+            if (j < 2 * C::KI) {
+              const int jj = j < C::KI ? j : j - C::KI;
+              const int row = jj * C::RPU + lane / C::NCH;
+              base = j < C::KI ? Kb : Qb;
+              off = min(row, lenc - 1) * rs + 16 * ((lane % C::NCH) ^ swz<C::ROWB>(row));
+            } else if (j < 2 * C::KI + C::RI) {
+              base = rec;
+              off = 16 * min(64 * (j - 2 * C::KI) + lane, kRecUnits - 1);
+            } else {
+              const int i = 64 * (j - 2 * C::KI - C::RI) + lane;
+              const int row = i / (NT * C::VPR), cp = i % (NT * C::VPR);
+              base = Vb;
+              off = min(row, lenc - 1) * vrs + 16 * cp;
+            }
+            r[u] = *reinterpret_cast<const f32x4*>(base + off);
+          }
+        }
+      };
+      auto commit = [&](char* buf) {
+#pragma unroll
+        for (int u = 0; u < C::PER; ++u) {
+          const int j = PW + C::NP * u;
+          if (j < C::TOTAL) {
+            int dst;
+            if (j < 2 * C::KI + C::RI) {
+              dst = 1024 * j + 16 * lane;
+            } else {
+              const int i = 64 * (j - 2 * C::KI - C::RI) + lane;
+              dst = C::VOFF + (i / (NT * C::VPR)) * C::VSTR + 16 * (i % (NT * C::VPR));
+            }
+            *reinterpret_cast<f32x4*>(buf + dst) = r[u];
+          }
+        }
+      };
+      auto store_o = [&](int c) {
+        const int t0c = start + kChunk * c, lenc = min(kChunk, L - kChunk * c);
+        const char* Ws = Wo + (c & 1) * C::OBYTES;
+        char* Ob = reinterpret_cast<char*>(Og + (size_t)t0c * p.hv * D + (size_t)h * D + 16 * dvb * NT);
+#pragma unroll
+        for (int u = 0; u < C::OST; ++u) {
+          const int i = 64 * (PW + C::NP * u) + lane;
+          const int row = i / (NT * C::OPR), cp = i % (NT * C::OPR);
+          if (i < C::OPIECES && row < lenc)
+            *reinterpret_cast<f32x4*>(Ob + (unsigned)(row * ors + 16 * cp)) =
+                *reinterpret_cast<const f32x4*>(Ws + row * C::OSTR + 16 * cp);
+        }
+      };
+
+      if (nchunks > 0) load(0);
+      if constexpr (C::NBUF == 2) {
+        if (nchunks > 0) commit(chunk_buf(0));
+        if (nchunks > 1) load(1);
+      }
+      for (int c = 0; c < nchunks; ++c) {
+        lds_barrier();  // chunk c-1 computed: its output rows are in Wo, its buffer is free
+        if constexpr (C::NBUF == 2) {
+          if (c + 1 < nchunks) commit(chunk_buf(c + 1));
+          if (c + 2 < nchunks) load(c + 2);
+        } else {
+          commit(chunk_buf(c));
+          lds_barrier();  // chunk c staged
+          if (c + 1 < nchunks) load(c + 1);
+        }
+        if (c > 0) store_o(c - 1);
+        if constexpr (RW > 1) {
+          lds_barrier();  // (the compute waves' Y exchange)
+          lds_barrier();  // (the compute waves' V' exchange)
+        }
+      }
+      lds_barrier();  // last chunk computed
+      if (nchunks > 0) store_o(nchunks - 1);
+    };
+    const int pw = wave - C::NC;
+    if (pw == 0) run(std::integral_constant<int, 0>{});
+    if constexpr (C::NP > 1) if (pw == 1) run(std::integral_constant<int, 1>{});
+    if constexpr (C::NP > 2) if (pw == 2) run(std::integral_constant<int, 2>{});
+    if constexpr (C::NP > 3) if (pw == 3) run(std::integral_constant<int, 3>{});
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const int tile = wave / RW, rg = wave % RW;
+  const int col = 16 * (dvb * NT + tile) + idx;
+  char* const X = Xbase + tile * C::XBYTES;
 
   // Owned state blocks: kb = rg + RW * o; Hc[o][hf][r] = H[state_row(2 kb + hf, 4 grp + r)][col].
   f32x4 Hc[OWN][2];
@@ -291,114 +352,32 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
         if (kb < KB) {
           float x[8];
           pack_c_pair(Hc[o][0], Hc[o][1], x);
-          Mode::store_block(X + XH + kb * 2048, lane, Mode::make(x));
+          Mode::store_block(X + C::XH + kb * 2048, lane, Mode::make(x));
         }
       }
     }
   }
 
-  const int start = p.cu[n];
-  const int L = p.cu[n + 1] - start;
-  const int nchunks = (L + kChunk - 1) / kChunk;
-  const int slot0 = slot_base(p.cu, n);
-  auto rec_of = [&](int c) {
-    return p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
-  };
-  auto row_bytes = [&](const in_t* base, int t) {
-    return reinterpret_cast<const char*>(base + (size_t)t * p.hqk * D + (size_t)m * D);
-  };
-  // v rows of this wave (row tiles rg*R .. rg*R+R-1, 16 columns of the tile), one chunk ahead,
-  // as 16-byte row pieces: piece q of the wave = row q / VPR, part q % VPR. Rows past the
-  // chunk end re-read the last valid row and are zeroed where used.
-  constexpr int VPR = VROWB / 16;                 // pieces per row
-  constexpr int VPIECES = 16 * R * VPR;           // pieces per wave
-  constexpr int VLD = (VPIECES + 63) / 64;        // loads per lane
-  auto load_v = [&](int c, f32x4 (&dst)[VLD]) {
-    const int t0c = start + kChunk * c, lenc = min(kChunk, L - kChunk * c);
-#pragma unroll
-    for (int u = 0; u < VLD; ++u) {
-      const int q = min(64 * u + lane, VPIECES - 1);
-      const int t = min(16 * rg * R + q / VPR, lenc - 1);
-      dst[u] = *reinterpret_cast<const f32x4*>(
-          reinterpret_cast<const char*>(Vg + ((size_t)(t0c + t) * p.hv + h) * D + 16 * (dvb * NT + tile)) +
-          16 * (q % VPR));
-    }
-  };
-  auto prefetch = [&](int c, St& st, RowPrefetch<Mode, D>& rp) {
-    const int t0c = start + kChunk * c, lenc = min(kChunk, L - kChunk * c);
-    st.load(row_bytes(Kg, t0c), row_bytes(Qg, t0c), rec_of(c), lenc, rs, wave, lane);
-    if constexpr (DIRECT)
-      rp.load(reinterpret_cast<const in_t*>(row_bytes(Qg, t0c + min(16 * rg + idx, lenc - 1))),
-              rec_of(c), rg, grp, lane);
-  };
-  f32x4 vnext[VLD];
-  St st;
-  RowPrefetch<Mode, D> rpn;
-  if (nchunks > 0) {
-    load_v(0, vnext);
-    prefetch(0, st, rpn);
-  }
-  // Output rows of the previous chunk (in Wo), stored as 16-byte row pieces after the next
-  // chunk's barrier so that the wait for the prefetch never waits for fresh stores.
-  constexpr int OPR = OROWB / 16, OPIECES = 16 * R * OPR, OST = (OPIECES + 63) / 64;
-  int t0prev = 0, lenprev = 0;
-  auto store_prev = [&]() {
-#pragma unroll
-    for (int u = 0; u < OST; ++u) {
-      const int q = 64 * u + lane;
-      const int t = 16 * rg * R + q / OPR;
-      if (q < OPIECES && t < lenprev)
-        *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(
-            Og + ((size_t)(t0prev + t) * p.hv + h) * D + 16 * (dvb * NT + tile)) + 16 * (q % OPR)) =
-            *reinterpret_cast<const f32x4*>(Wo + 16 * q);
-    }
-  };
-
   for (int c = 0; c < nchunks; ++c) {
-    const int t0 = start + kChunk * c;
     const int len = min(kChunk, L - kChunk * c);
-    char* S = smem;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c (and its v rows) landed
-    lds_barrier();                  // every wave is done with chunk c-1's LDS
-    st.commit(S, wave, lane);
-    RowPrefetch<Mode, D> rp = rpn;
-#pragma unroll
-    for (int u = 0; u < VLD; ++u)
-      if (64 * u + lane < VPIECES) *reinterpret_cast<f32x4*>(Wv + 16 * (64 * u + lane)) = vnext[u];
-    lds_barrier();                  // chunk c staged
-    if (c + 1 < nchunks) {
-      load_v(c + 1, vnext);
-      prefetch(c + 1, st, rpn);
-    }
-    if (c > 0) store_prev();
-    float vv[R][4];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const f32x4 v4 = VRows<in_t>::cfrag(Wv + 16 * i * VROWB, lane);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vv[i][r] = (16 * (rg * R + i) + 4 * grp + r < len) ? v4[r] : 0.f;
-    }
+    lds_barrier();  // chunk c staged (double buffer); state blocks of chunk c-1 exchanged
+    if constexpr (C::NBUF == 1) lds_barrier();  // chunk c staged
+    const char* const S = chunk_buf(c);
     const char* sK = S;
-    const char* sQ = S + KBYTES;            // (staged layouts only)
-    const char* sTP = S + 2 * KBYTES;       // (staged layouts only)
-    const float* sgam = reinterpret_cast<const float*>(sTP + kWsGOff);
-    const float* sdel = reinterpret_cast<const float*>(sTP + kWsDOff);
-    auto tblock = [&](int i, int rt, int kb) -> Op {
-      if constexpr (DIRECT) return rp.tb[kb];
-      else return Mode::load_block(sTP + kWsTOff + tri_block(rt, kb) * 2048, lane);
+    const char* sQ = S + C::QOFF;
+    const char* sR = S + C::ROFF;
+    const char* sV = S + C::VOFF + tile * C::VROWB;
+    const float* sgam = reinterpret_cast<const float*>(sR + kWsGOff);
+    const float* sdel = reinterpret_cast<const float*>(sR + kWsDOff);
+    char* const Wc = Wo + (c & 1) * C::OBYTES + tile * C::OROWB;
+    auto tblock = [&](int rt, int kb) -> Op {
+      return Mode::load_block(sR + kWsTOff + tri_block(rt, kb) * 2048, lane);
     };
-    auto pblock = [&](int i, int rt, int kb) -> Op {
-      if constexpr (DIRECT) return rp.pb[kb];
-      else return Mode::load_block(sTP + kWsPOff + tri_block(rt, kb) * 2048, lane);
+    auto pblock = [&](int rt, int kb) -> Op {
+      return Mode::load_block(sR + kWsPOff + tri_block(rt, kb) * 2048, lane);
     };
-    auto gamma4 = [&](int rt) -> f32x4 {
-      if constexpr (DIRECT) return rp.gam;
-      else return *reinterpret_cast<const f32x4*>(sgam + 16 * rt + 4 * grp);
-    };
-    auto delta4 = [&](int rt) -> f32x4 {
-      if constexpr (DIRECT) return rp.del;
-      else return *reinterpret_cast<const f32x4*>(sdel + 16 * rt + 4 * grp);
-    };
+    auto gamma4 = [&](int rt) { return *reinterpret_cast<const f32x4*>(sgam + 16 * rt + 4 * grp); };
+    auto delta4 = [&](int rt) { return *reinterpret_cast<const f32x4*>(sdel + 16 * rt + 4 * grp); };
 
     // (a) state as split B fragments over d_k
     Op HB[KB];
@@ -411,7 +390,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       }
     } else {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) HB[kb] = Mode::load_block(X + XH + kb * 2048, lane);
+      for (int kb = 0; kb < KB; ++kb) HB[kb] = Mode::load_block(X + C::XH + kb * 2048, lane);
     }
 
     // (b) K H, Q H on this wave's row tiles; Y = V - gamma K H, gamma Q H.
@@ -424,16 +403,15 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       f32x4 qh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        typename Mode::frag_t qa;
-        if constexpr (DIRECT) qa = rp.qf[kb];
-        else qa = F::a(sQ, 16 * rt + idx, kb, grp);
         kh[kb & 1] = Mode::mma_xs(kh[kb & 1], F::a(sK, 16 * rt + idx, kb, grp), HB[kb]);
-        qh[kb & 1] = Mode::mma_xs(qh[kb & 1], qa, HB[kb]);
+        qh[kb & 1] = Mode::mma_xs(qh[kb & 1], F::a(sQ, 16 * rt + idx, kb, grp), HB[kb]);
       }
+      const f32x4 v4 = VRows<in_t>::cfrag(sV + 16 * rt * C::VSTR, C::VSTR, lane);
       const f32x4 gam = gamma4(rt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        Y[i][r] = vv[i][r] - gam[r] * (kh[0][r] + kh[1][r]);
+        const float vr = 16 * rt + 4 * grp + r < len ? v4[r] : 0.f;
+        Y[i][r] = vr - gam[r] * (kh[0][r] + kh[1][r]);
         QH[i][r] = gam[r] * (qh[0][r] + qh[1][r]);
       }
     }
@@ -451,12 +429,12 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int rt = rg * R + i;
-        store_half(Mode{}, X + XY + (rt >> 1) * 2048, lane, rt & 1, Y[i]);
+        store_half(Mode{}, X + C::XY + (rt >> 1) * 2048, lane, rt & 1, Y[i]);
       }
       lds_barrier();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (2 * kb <= rg * R + R - 1) YB[kb] = Mode::load_block(X + XY + kb * 2048, lane);
+        if (2 * kb <= rg * R + R - 1) YB[kb] = Mode::load_block(X + C::XY + kb * 2048, lane);
     }
 
     // (d) V' = (T diag(beta)) Y on this wave's row tiles (block lower triangular)
@@ -467,7 +445,7 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, tblock(i, rt, kb), YB[kb]);
+        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, tblock(rt, kb), YB[kb]);
       Vp[i] = acc;
     }
 
@@ -491,21 +469,19 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int rt = rg * R + i;
-        store_half(Mode{}, X + XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
-        store_half(Mode{}, X + XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
+        store_half(Mode{}, X + C::XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
+        store_half(Mode{}, X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
       }
       lds_barrier();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        VB[kb] = Mode::load_block(X + XV + kb * 2048, lane);
-        DB[kb] = Mode::load_block(X + XD + kb * 2048, lane);
+        VB[kb] = Mode::load_block(X + C::XV + kb * 2048, lane);
+        DB[kb] = Mode::load_block(X + C::XD + kb * 2048, lane);
       }
     }
 
     // (g) owned state blocks first (the next chunk waits on them): H <- gamma_C H + K^T V''
-    float gC;
-    if constexpr (DIRECT) gC = rp.gC;
-    else gC = sgam[kChunk - 1];
+    const float gC = sgam[kChunk - 1];
 #pragma unroll
     for (int o = 0; o < OWN; ++o) {
       const int kb = rg + RW * o;
@@ -521,28 +497,26 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
         if constexpr (RW > 1) {
           float x[8];
           pack_c_pair(Hc[o][0], Hc[o][1], x);
-          Mode::store_block(X + XH + kb * 2048, lane, Mode::make(x));
+          Mode::store_block(X + C::XH + kb * 2048, lane, Mode::make(x));
         }
       }
     }
 
-    // (f) O = scale (gamma Q H + P V') on this wave's row tiles (stored next iteration)
+    // (f) O = scale (gamma Q H + P V') on this wave's row tiles, into the output rows
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int rt = rg * R + i;
       f32x4 acc = QH[i];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, pblock(i, rt, kb), VB[kb]);
+        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, pblock(rt, kb), VB[kb]);
       const f32x4 o4 = acc * p.scale;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        reinterpret_cast<OutT*>(Wo + (16 * i + 4 * grp + r) * OROWB)[idx] = from_f32<OutT>(o4[r]);
+        reinterpret_cast<OutT*>(Wc + (16 * rt + 4 * grp + r) * C::OSTR)[idx] = from_f32<OutT>(o4[r]);
     }
-    t0prev = t0;
-    lenprev = len;
   }
-  if (nchunks > 0) store_prev();
+  lds_barrier();  // last chunk computed (the producers store its output rows)
 
   if (p.ht) {
     float* HT = p.ht + (size_t)nh * D * D;
@@ -562,9 +536,10 @@ __global__ __launch_bounds__(NT * RW * 64) void chunk_scan_kernel(ScanParams p) 
 template <typename Mode, int D, int NT, int RW, typename OutT>
 hipError_t launch_scan_cfg(const ScanParams& p, long long heads, hipStream_t stream) {
   static_assert(D / 16 % NT == 0, "d_v tiles per workgroup");
+  using C = ScanCfg<Mode, D, NT, RW, OutT>;
   const unsigned blocks = (unsigned)(heads * (D / 16 / NT));
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_scan_kernel<Mode, D, NT, RW, OutT>), dim3(blocks), dim3(NT * RW * 64), 0,
+  hipLaunchKernelGGL((chunk_scan_kernel<Mode, D, NT, RW, OutT>), dim3(blocks), dim3(C::THREADS), 0,
                      stream, p);
   return hipGetLastError();
 }
