@@ -188,7 +188,8 @@ struct ScanCfg {
   static constexpr int OSTR = NT * OROWB + (NT > 1 ? 16 : 0);
   static constexpr int OBYTES = 64 * OSTR;
   static constexpr int OPIECES = 64 * NT * OPR, OST = (OPIECES + 64 * NP - 1) / (64 * NP);
-  static constexpr int FIXED = NT * XBYTES + 2 * OBYTES;
+  static constexpr int SYNCB = RW > 1 ? 16 * NT : 0;  // arrival counters of the tile groups
+  static constexpr int FIXED = NT * XBYTES + 2 * OBYTES + SYNCB;
   static constexpr int NBUF = 2 * BUFB + FIXED <= kLdsBytes ? 2 : 1;
   static constexpr int LDS = NBUF * BUFB + FIXED;
   static_assert(LDS <= kLdsBytes, "LDS budget");
@@ -208,6 +209,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const Xbase = smem + C::NBUF * C::BUFB;
   char* const Wo = Xbase + NT * C::XBYTES;  // two output buffers of OBYTES
+  int* const sync_base = reinterpret_cast<int*>(Wo + 2 * C::OBYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -314,10 +316,6 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           if (c + 1 < nchunks) load(c + 1);
         }
         if (c > 0) store_o(c - 1);
-        if constexpr (RW > 1) {
-          lds_barrier();  // (the compute waves' Y exchange)
-          lds_barrier();  // (the compute waves' V' exchange)
-        }
       }
       lds_barrier();  // last chunk computed
       if (nchunks > 0) store_o(nchunks - 1);
@@ -334,6 +332,25 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   const int tile = wave / RW, rg = wave % RW;
   const int col = 16 * (dvb * NT + tile) + idx;
   char* const X = Xbase + tile * C::XBYTES;
+  // The RW waves of a tile exchange Y and V' twice per chunk. They meet through an arrival
+  // counter in LDS rather than s_barrier, which would also wait for the producer waves.
+  int* const sync_ctr = sync_base + 4 * tile;
+  if constexpr (RW > 1)
+    if (rg == 0 && lane == 0) *sync_ctr = 0;  // ordered before first use by the first barrier
+  int sync_target = 0;
+  auto group_sync = [&]() {
+    sync_target += RW;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's exchange writes are done
+    if (lane == 0) __hip_atomic_fetch_add(sync_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // LDS serves one CU in order: once the count is reached, the other waves' writes are
+    // visible. The wait is bounded so that a broken count can never hang the device.
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(sync_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= sync_target)
+        break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+  };
 
   // Owned state blocks: kb = rg + RW * o; Hc[o][hf][r] = H[state_row(2 kb + hf, 4 grp + r)][col].
   f32x4 Hc[OWN][2];
@@ -431,7 +448,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         const int rt = rg * R + i;
         store_half(Mode{}, X + C::XY + (rt >> 1) * 2048, lane, rt & 1, Y[i]);
       }
-      lds_barrier();
+      group_sync();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         if (2 * kb <= rg * R + R - 1) YB[kb] = Mode::load_block(X + C::XY + kb * 2048, lane);
@@ -472,7 +489,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         store_half(Mode{}, X + C::XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
         store_half(Mode{}, X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
       }
-      lds_barrier();
+      group_sync();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         VB[kb] = Mode::load_block(X + C::XV + kb * 2048, lane);
