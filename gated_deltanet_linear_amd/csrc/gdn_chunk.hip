@@ -116,14 +116,15 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
   constexpr int KB = DK / 32;
   constexpr int ROWB = DK * (int)sizeof(in_t), KBYTES = 64 * ROWB;
   constexpr int TBYTES = 64 * kLd * 4;
-  constexpr int SBYTES = 2 * KBYTES > TBYTES ? 2 * KBYTES : TBYTES;
+  constexpr int SBYTES = 2 * KBYTES > 2 * TBYTES ? 2 * KBYTES : 2 * TBYTES;
 
-  // Staged q/k rows; after the K K^T / Q K^T phase the same bytes hold T.
+  // Staged q/k rows; once the K K^T / Q K^T products are in registers the same bytes hold A
+  // and T (small enough for four workgroups per CU).
   __shared__ __attribute__((aligned(1024))) char sKQ[SBYTES];
-  __shared__ float sA[64 * kLd];
   __shared__ float sb[64];
   __shared__ float sbeta[64];
-  float* sT = reinterpret_cast<float*>(sKQ);
+  float* sA = reinterpret_cast<float*>(sKQ);
+  float* sT = reinterpret_cast<float*>(sKQ + TBYTES);
 
   const int slot = blockIdx.x, h = blockIdx.y;
   const int n = slot_to_seq(p.cu, p.num_seqs, slot);
@@ -137,26 +138,43 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const size_t rstride = (size_t)p.hqk * DK;
   char* rec = p.ws + ((size_t)slot * p.hv + h) * kWsRecordBytes;
+  float gate_g, gate_b;  // g and beta of token `lane` (wave 0)
 
-  // ---- all memory reads at once: q/k rows (async into LDS) and this head's gates
-  stage_rows<in_t, DK, 4>(sKQ, static_cast<const in_t*>(p.k), static_cast<const in_t*>(p.q), t0,
-                          len, rstride, m, wave, lane);
-  float gv = 0.f, bv = 0.f;
-  if (wave == 0 && lane < len) {
-    gv = p.g[(size_t)(t0 + lane) * p.hv + h];
-    bv = p.beta[(size_t)(t0 + lane) * p.hv + h];
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
-  if (len < kChunk) {  // tail chunk: rows past len (copies of row len-1) become zero rows
-    for (int e = tid; e < 2 * (kChunk - len) * (ROWB / 16); e += 256) {
-      const int mat = e / ((kChunk - len) * (ROWB / 16)), rem = e % ((kChunk - len) * (ROWB / 16));
-      const int row = len + rem / (ROWB / 16), c16 = rem % (ROWB / 16);
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(sKQ + mat * KBYTES + row * ROWB + 16 * c16) = z;
+  // ---- all memory reads at once: q/k rows into registers (16-byte loads, 1 KiB per wave
+  // instruction) and this head's gates; then the rows go to LDS, row-major with the 16-byte
+  // XOR swizzle. Rows past len are written as zeros (identity steps).
+  {
+    constexpr int NCH = ROWB / 16, RPU = 64 / NCH, KI = KBYTES / 1024, PER = 2 * KI / 4;
+    static_assert(2 * KI % 4 == 0, "units per wave");
+    const in_t* Kg = static_cast<const in_t*>(p.k);
+    const in_t* Qg = static_cast<const in_t*>(p.q);
+    const char* Kb = reinterpret_cast<const char*>(Kg + (size_t)t0 * rstride + (size_t)m * DK);
+    const char* Qb = reinterpret_cast<const char*>(Qg + (size_t)t0 * rstride + (size_t)m * DK);
+    const unsigned rs = (unsigned)(rstride * sizeof(in_t));
+    f32x4 r[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = wave + 4 * u, jj = j < KI ? j : j - KI;
+      const int row = jj * RPU + lane / NCH;
+      const unsigned off = min(row, len - 1) * rs + 16 * ((lane % NCH) ^ swz<ROWB>(row));
+      r[u] = *reinterpret_cast<const f32x4*>((j < KI ? Kb : Qb) + off);
     }
-    lds_barrier();
+    float gv = 0.f, bv = 0.f;
+    if (wave == 0 && lane < len) {
+      gv = p.g[(size_t)(t0 + lane) * p.hv + h];
+      bv = p.beta[(size_t)(t0 + lane) * p.hv + h];
+    }
+    gate_g = gv;
+    gate_b = bv;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = wave + 4 * u, jj = j < KI ? j : j - KI;
+      const int row = jj * RPU + lane / NCH;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(sKQ + 1024 * j + 16 * lane) = row < len ? r[u] : z;
+    }
   }
+  lds_barrier();
 
   // ---- 22 tile jobs, round robin over the waves (wave w: jobs w, w+4, ..., w+16 on MFMA,
   // and job w+20 for waves 0, 1):
@@ -196,10 +214,10 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     acc[i] = c;
   }
   if (wave == 0) {
-    const float cs = wave_inclusive_scan(gv, lane);
+    const float cs = wave_inclusive_scan(gate_g, lane);
     const float cl = __shfl(cs, kChunk - 1, kWave);  // b_C (identity steps keep it at b_{len-1})
     sb[lane] = cs;
-    sbeta[lane] = bv;
+    sbeta[lane] = gate_b;
     reinterpret_cast<float*>(rec + kWsGOff)[lane] = __expf(cs);
     reinterpret_cast<float*>(rec + kWsDOff)[lane] = __expf(cl - cs);
   }
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     store_half_global(Mode{}, rec + kWsPOff + tri_block(rt, rt / 2) * kWsBlockBytes, lane, 1, z);
   }
-  lds_barrier();  // sb, sbeta ready
+  lds_barrier();  // sb, sbeta ready; every wave is done with the staged rows (sA may overwrite)
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     const int job = wave + 4 * i;
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
                         r2 & 1, pv);
     }
   }
-  lds_barrier();  // sA complete; staged rows no longer needed (sT may overwrite them)
+  lds_barrier();  // sA complete
 
   // ---- Diagonal 16x16 blocks of T: wave w inverts block w by forward substitution,
   // x_i = delta_ic - sum_{j<i} A_ij x_j with lane c < 16 carrying column c. Lane i holds row i

@@ -194,8 +194,6 @@ __device__ __forceinline__ int xcd_logical_id(int b, int total) {
 
 // ---- LDS staging and operand fragments from staged rows -------------------------------
 
-#define GDN_AS1(p) ((const __attribute__((address_space(1))) void*)(p))
-#define GDN_AS3(p) ((__attribute__((address_space(3))) void*)(p))
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -236,34 +234,11 @@ __device__ __forceinline__ f32x8 afrag_f32(const char* buf, int row, int kb, int
 }
 
 // Barrier for LDS traffic only: waits for this wave's own LDS reads and writes (lgkmcnt) and
-// for the other waves, but not for outstanding global loads, including global_load_lds copies
-// into a different LDS buffer (a fence would wait for those too, serialising the prefetch of
-// the next chunk with this one). The memory clobber keeps the compiler from moving memory
-// accesses across it. Callers that need global_load_lds data wait with s_waitcnt first.
+// for the other waves, but not for outstanding global loads (a fence would wait for those too,
+// serialising the prefetch of the next chunk with this one). The memory clobber keeps the
+// compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Asynchronous copy of the 64 rows [t0, t0 + 64) of head m of two [T][H][D] tensors (K, then Q)
-// into LDS at S and S + 64 * D * sizeof(T), row-major with the swizzle above, using
-// global_load_lds (16 bytes per lane; no registers; completes on vmcnt). Rows past len
-// re-read row len - 1 so that every address stays inside the tensors.
-template <typename T, int D, int NWAVES>
-__device__ __forceinline__ void stage_rows(char* S, const T* Kg, const T* Qg, int t0, int len,
-                                           size_t rstride, int m, int wave, int lane) {
-  constexpr int ROWB = D * (int)sizeof(T), NCH = ROWB / 16, KBYTES = 64 * ROWB;
-  constexpr int KINST = KBYTES / 1024;
-  for (int j = wave; j < 2 * KINST; j += NWAVES) {
-    const bool isq = j >= KINST;
-    const int jj = isq ? j - KINST : j;
-    const int P = 64 * jj + lane;
-    const int r = P / NCH, ch = (P % NCH) ^ swz<ROWB>(P / NCH);
-    const int rr = r < len ? r : len - 1;
-    const char* src = reinterpret_cast<const char*>((isq ? Qg : Kg) + (size_t)(t0 + rr) * rstride +
-                                                    (size_t)m * D) + 16 * ch;
-    __builtin_amdgcn_global_load_lds(GDN_AS1(src), GDN_AS3(S + (isq ? KBYTES : 0) + 1024 * jj),
-                                     16, 0, 0);
-  }
 }
 
 }  // namespace gdn

@@ -411,20 +411,39 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     }
 
     // (b) K H, Q H on this wave's row tiles; Y = V - gamma K H, gamma Q H.
-    // Two accumulators per product (even / odd depth blocks) halve the dependent chains.
+    // The K / Q fragments of a row tile are read before its products (and, for bf16, those
+    // of the next row tile while these run), so LDS latency overlaps the MFMA chains. Two
+    // accumulators per product (even / odd depth blocks) halve the dependent chains.
+    using frag_t = typename Mode::frag_t;
+    // fp32 operands over four row tiles leave no registers for reading ahead.
+    constexpr bool EARLY = !(std::is_same<Mode, F32Mode>::value && R > 1);
+    constexpr int KQB = std::is_same<Mode, Bf16Mode>::value && R > 1 ? 2 : 1;
+    frag_t ka[KQB][KB], qa[KQB][KB];
+    auto load_kq = [&](int b, int rt) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        ka[b][kb] = F::a(sK, 16 * rt + idx, kb, grp);
+        qa[b][kb] = F::a(sQ, 16 * rt + idx, kb, grp);
+      }
+    };
     f32x4 QH[R], Y[R];
+    if constexpr (EARLY) load_kq(0, rg * R);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int rt = rg * R + i;
+      const int rt = rg * R + i, b = KQB > 1 ? (i & 1) : 0;
+      if (EARLY && KQB == 1 && i > 0) load_kq(0, rt);
+      const f32x4 v4 = VRows<in_t>::cfrag(sV + 16 * rt * C::VSTR, C::VSTR, lane);
+      const f32x4 gam = gamma4(rt);
       f32x4 kh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       f32x4 qh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        kh[kb & 1] = Mode::mma_xs(kh[kb & 1], F::a(sK, 16 * rt + idx, kb, grp), HB[kb]);
-        qh[kb & 1] = Mode::mma_xs(qh[kb & 1], F::a(sQ, 16 * rt + idx, kb, grp), HB[kb]);
+        const frag_t kf = EARLY ? ka[b][kb] : F::a(sK, 16 * rt + idx, kb, grp);
+        const frag_t qf = EARLY ? qa[b][kb] : F::a(sQ, 16 * rt + idx, kb, grp);
+        kh[kb & 1] = Mode::mma_xs(kh[kb & 1], kf, HB[kb]);
+        qh[kb & 1] = Mode::mma_xs(qh[kb & 1], qf, HB[kb]);
       }
-      const f32x4 v4 = VRows<in_t>::cfrag(sV + 16 * rt * C::VSTR, C::VSTR, lane);
-      const f32x4 gam = gamma4(rt);
+      if (KQB > 1 && i + 1 < R) load_kq(b ^ 1, rt + 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float vr = 16 * rt + 4 * grp + r < len ? v4[r] : 0.f;
@@ -433,7 +452,16 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       }
     }
 
-    // (c) Y as split B fragments over tokens (blocks of 32)
+    // (c) Y as split B fragments over tokens (blocks of 32). The T diag(beta) blocks of (d)
+    // are read first; they do not depend on Y and arrive while the waves exchange it.
+    Op TB[R][2];
+#pragma unroll
+    for (int i = 0; i < (EARLY ? R : 0); ++i) {
+      const int rt = rg * R + i;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb <= (rt >> 1)) TB[i][kb] = tblock(rt, kb);
+    }
     Op YB[2];
     if constexpr (RW == 1) {
 #pragma unroll
@@ -462,11 +490,20 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, tblock(rt, kb), YB[kb]);
+        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, EARLY ? TB[i][kb] : tblock(rt, kb), YB[kb]);
       Vp[i] = acc;
     }
 
-    // (e) V' and V'' = diag(e^{b_C - b}) V' as split B fragments over tokens
+    // (e) V' and V'' = diag(e^{b_C - b}) V' as split B fragments over tokens. The P blocks of
+    // (f) are read first, for the same reason as the T blocks.
+    Op PB[R][2];
+#pragma unroll
+    for (int i = 0; i < (EARLY ? R : 0); ++i) {
+      const int rt = rg * R + i;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb <= (rt >> 1)) PB[i][kb] = pblock(rt, kb);
+    }
     Op VB[2], DB[2];
     if constexpr (RW == 1) {
 #pragma unroll
@@ -503,12 +540,18 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     for (int o = 0; o < OWN; ++o) {
       const int kb = rg + RW * o;
       if (kb < KB) {
+        frag_t kt[2][2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int kbp = 0; kbp < 2; ++kbp)
+            if constexpr (EARLY) kt[hf][kbp] = F::kt(sK, 2 * kb + hf, kbp, lane);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           f32x4 acc = Hc[o][hf] * gC;
 #pragma unroll
           for (int kbp = 0; kbp < 2; ++kbp)
-            acc = Mode::mma_xs(acc, F::kt(sK, 2 * kb + hf, kbp, lane), DB[kbp]);
+            acc = Mode::mma_xs(acc, EARLY ? kt[hf][kbp] : F::kt(sK, 2 * kb + hf, kbp, lane), DB[kbp]);
           Hc[o][hf] = acc;
         }
         if constexpr (RW > 1) {
@@ -526,7 +569,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       f32x4 acc = QH[i];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, pblock(rt, kb), VB[kb]);
+        if (kb <= (rt >> 1)) acc = Mode::mma_ss(acc, EARLY ? PB[i][kb] : pblock(rt, kb), VB[kb]);
       const f32x4 o4 = acc * p.scale;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
