@@ -8,15 +8,16 @@
 //   O   = scale ( diag(gamma) Q H + P V' )     (P = masked decayed Q K^T)
 //   H  <- gamma_C H + K^T diag(e^{b_C - b}) V'
 // Columns of H evolve independently, so a workgroup owns NT tiles of 16 d_v columns of one
-// (sequence, V head) and walks its chunks in order. Each tile is handled by RW waves:
+// (sequence, V head) and walks its chunks in order. Each tile is computed by RW waves:
 //   RW = 1: one wave owns all 64 rows of the chunk and its [d_k x 16] fp32 state slice stays
 //           in that wave's registers for the whole sequence (most work per wave, least LDS).
 //   RW = 4: wave r owns row tile r (16 tokens) and 32 rows of the state; Y, V' and the new
 //           state cross waves through LDS (4x the waves for shapes with few sequences x heads).
-// q/k rows and the workspace record of chunk c+1 are loaded into registers while chunk c
-// computes and written to LDS when chunk c+1 starts. q/k rows are stored row-major with a
-// 16-byte XOR swizzle; K^T operand fragments are read from the same rows with
-// ds_read_b64_tr_b16.
+// Separate producer waves move the data: while chunk c is computed they write chunk c+1 (held
+// in their registers) into the free one of two LDS buffers, load chunk c+2, and store the output
+// rows of chunk c-1, so the compute waves never issue a global memory instruction in the chunk
+// loop. q/k rows are staged row-major with a 16-byte XOR swizzle; K^T operand fragments are read
+// from the same rows with ds_read_b64_tr_b16.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
 #include <cstdlib>
 #include <cstring>
