@@ -184,28 +184,51 @@ def test_prefill_then_decode_equals_longer_prefill():
     assert_rms_close(h1, h_ref, TOL["bf16"], "prefill+decode state")
 
 
+_LAYOUT_CONFIGS = [(dt, d) for dt in ("bf16", "f32") for d in (32, 64, 128)]
+
+
 def test_scan_layouts_are_bit_identical():
-    """The row-split (4 waves per d_v tile) and tile-per-wave scan layouts give identical bits."""
+    """Both scan layouts (row-split: 4 waves per d_v tile; tile-per-wave) for every input dtype,
+    output dtype and head size: identical bits, the tile layout within tolerance of the oracle,
+    and bf16 outputs equal to the fp32 outputs rounded. Each layout runs in a process of its own
+    (the layout is chosen once per process)."""
+    import os
     import subprocess
     import sys
+    import tempfile
     code = (
         "import sys, torch; sys.path.insert(0, '.'); import synthetic_inputs as si;"
         "import gated_deltanet_linear_amd as gdn;"
-        "c = si.make_core_case([300, 64, 5], 2, 4, 128, 128, dtype='bf16', gate='model',"
-        " h0_std=0.02, seed=91);"
-        "d = {k: getattr(c, k).cuda() for k in ('q','k','v','g','beta','cu_seqlens','h0')};"
-        "o, h = gdn.chunk_forward(d['q'], d['k'], d['v'], d['g'], d['beta'], d['cu_seqlens'],"
-        " initial_state=d['h0'], out_dtype=torch.float32);"
-        "torch.save((o.cpu(), h.cpu()), sys.argv[1])")
-    import os
-    import tempfile
-    outs = []
+        "res = [];"
+        f"cfgs = {_LAYOUT_CONFIGS!r};\n"
+        "for dt, dd in cfgs:\n"
+        "    c = si.make_core_case([300, 64, 5], 2, 4, dd, dd, dtype=dt, gate='model',"
+        " h0_std=0.02, seed=91 + dd);\n"
+        "    d = {k: getattr(c, k).cuda() for k in ('q','k','v','g','beta','cu_seqlens','h0')};\n"
+        "    for od in (torch.float32, torch.bfloat16):\n"
+        "        print('layout case', dt, dd, od, flush=True);\n"
+        "        o, h = gdn.chunk_forward(d['q'], d['k'], d['v'], d['g'], d['beta'],"
+        " d['cu_seqlens'], initial_state=d['h0'], out_dtype=od);\n"
+        "        res.append((o.cpu(), h.cpu()))\n"
+        "torch.save(res, sys.argv[1])\n")
+    outs = {}
     with tempfile.TemporaryDirectory() as td:
         for layout in ("rows", "tiles"):
             path = os.path.join(td, layout + ".pt")
             env = dict(os.environ, GDN_SCAN_LAYOUT=layout)
+            print(f"[layout] {layout}", flush=True)
             subprocess.run([sys.executable, "-c", code, path], check=True, env=env,
                            cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            timeout=300)
-            outs.append(torch.load(path, weights_only=True))
-    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+            outs[layout] = torch.load(path, weights_only=True)
+    for i, (dt, dd) in enumerate(_LAYOUT_CONFIGS):
+        for j, od in enumerate(("f32", "bf16")):
+            (o_r, h_r), (o_t, h_t) = outs["rows"][2 * i + j], outs["tiles"][2 * i + j]
+            assert torch.equal(o_r, o_t) and torch.equal(h_r, h_t), (dt, dd, od)
+        (o32, h32), (o16, h16) = outs["tiles"][2 * i], outs["tiles"][2 * i + 1]
+        assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(h16, h32), (dt, dd)
+        case = si.make_core_case([300, 64, 5], 2, 4, dd, dd, dtype=dt, gate="model",
+                                 h0_std=0.02, seed=91 + dd)
+        o_ref, h_ref = oracle_case(case)
+        assert_rms_close(o32, o_ref, TOL[dt], f"tiles {dt} d={dd} o")
+        assert_rms_close(h32, h_ref, TOL[dt], f"tiles {dt} d={dd} final state")
