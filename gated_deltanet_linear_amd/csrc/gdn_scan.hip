@@ -334,15 +334,18 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   const int col = 16 * (dvb * NT + tile) + idx;
   char* const X = Xbase + tile * C::XBYTES;
   // The RW waves of a tile exchange Y and V' twice per chunk. They meet through an arrival
-  // counter in LDS rather than s_barrier, which would also wait for the producer waves.
+  // counter in LDS rather than s_barrier, which would also wait for the producer waves;
+  // arriving and waiting are separate so that reads can be issued in between.
   int* const sync_ctr = sync_base + 4 * tile;
   if constexpr (RW > 1)
     if (rg == 0 && lane == 0) *sync_ctr = 0;  // ordered before first use by the first barrier
   int sync_target = 0;
-  auto group_sync = [&]() {
+  auto group_arrive = [&]() {
     sync_target += RW;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's exchange writes are done
     if (lane == 0) __hip_atomic_fetch_add(sync_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  auto group_wait = [&]() {
     // LDS serves one CU in order: once the count is reached, the other waves' writes are
     // visible. The wait is bounded so that a broken count can never hang the device.
     for (int spin = 0; spin < (1 << 22); ++spin) {
@@ -454,17 +457,21 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     }
 
     // (c) Y as split B fragments over tokens (blocks of 32). The T diag(beta) blocks of (d)
-    // are read first; they do not depend on Y and arrive while the waves exchange it.
+    // do not depend on Y: they are read while the row-split waves wait for each other (after
+    // this wave has announced its Y, so that the reads do not delay the announcement).
     Op TB[R][2];
+    auto load_t = [&]() {
 #pragma unroll
-    for (int i = 0; i < (EARLY ? R : 0); ++i) {
-      const int rt = rg * R + i;
+      for (int i = 0; i < (EARLY ? R : 0); ++i) {
+        const int rt = rg * R + i;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1)) TB[i][kb] = tblock(rt, kb);
-    }
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb <= (rt >> 1)) TB[i][kb] = tblock(rt, kb);
+      }
+    };
     Op YB[2];
     if constexpr (RW == 1) {
+      load_t();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float x[8];
@@ -477,7 +484,9 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         const int rt = rg * R + i;
         store_half(Mode{}, X + C::XY + (rt >> 1) * 2048, lane, rt & 1, Y[i]);
       }
-      group_sync();
+      group_arrive();
+      load_t();
+      group_wait();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         if (2 * kb <= rg * R + R - 1) YB[kb] = Mode::load_block(X + C::XY + kb * 2048, lane);
@@ -496,17 +505,34 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     }
 
     // (e) V' and V'' = diag(e^{b_C - b}) V' as split B fragments over tokens. The P blocks of
-    // (f) are read first, for the same reason as the T blocks.
+    // (f) and, in the row-split layout, the K^T fragments of (g) are read like the T blocks.
+    constexpr bool KT_EARLY = EARLY && RW > 1;
     Op PB[R][2];
+    frag_t kt[OWN][2][2];
+    auto load_p_kt = [&]() {
 #pragma unroll
-    for (int i = 0; i < (EARLY ? R : 0); ++i) {
-      const int rt = rg * R + i;
+      for (int i = 0; i < (EARLY ? R : 0); ++i) {
+        const int rt = rg * R + i;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (kb <= (rt >> 1)) PB[i][kb] = pblock(rt, kb);
-    }
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb <= (rt >> 1)) PB[i][kb] = pblock(rt, kb);
+      }
+      if constexpr (KT_EARLY) {
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+          const int kb = rg + RW * o;
+          if (kb < KB)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+              for (int kbp = 0; kbp < 2; ++kbp)
+                kt[o][hf][kbp] = F::kt(sK, 2 * kb + hf, kbp, lane);
+        }
+      }
+    };
     Op VB[2], DB[2];
     if constexpr (RW == 1) {
+      load_p_kt();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float x[8], d[8];
@@ -527,10 +553,12 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         store_half(Mode{}, X + C::XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
         store_half(Mode{}, X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
       }
-      group_sync();
+      group_arrive();
+      load_p_kt();
+      group_wait();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        VB[kb] = Mode::load_block(X + C::XV + kb * 2048, lane);
+        if (2 * kb <= rg * R + R - 1) VB[kb] = Mode::load_block(X + C::XV + kb * 2048, lane);
         DB[kb] = Mode::load_block(X + C::XD + kb * 2048, lane);
       }
     }
@@ -541,18 +569,19 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     for (int o = 0; o < OWN; ++o) {
       const int kb = rg + RW * o;
       if (kb < KB) {
-        frag_t kt[2][2];
+        if constexpr (EARLY && !KT_EARLY) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+          for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-          for (int kbp = 0; kbp < 2; ++kbp)
-            if constexpr (EARLY) kt[hf][kbp] = F::kt(sK, 2 * kb + hf, kbp, lane);
+            for (int kbp = 0; kbp < 2; ++kbp) kt[o][hf][kbp] = F::kt(sK, 2 * kb + hf, kbp, lane);
+        }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           f32x4 acc = Hc[o][hf] * gC;
 #pragma unroll
           for (int kbp = 0; kbp < 2; ++kbp)
-            acc = Mode::mma_xs(acc, EARLY ? kt[hf][kbp] : F::kt(sK, 2 * kb + hf, kbp, lane), DB[kbp]);
+            acc = Mode::mma_xs(acc, EARLY ? kt[o][hf][kbp] : F::kt(sK, 2 * kb + hf, kbp, lane),
+                               DB[kbp]);
           Hc[o][hf] = acc;
         }
         if constexpr (RW > 1) {
