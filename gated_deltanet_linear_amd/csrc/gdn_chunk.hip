@@ -121,8 +121,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
   // Staged q/k rows; once the K K^T / Q K^T products are in registers the same bytes hold A
   // and T (small enough for four workgroups per CU).
   __shared__ __attribute__((aligned(1024))) char sKQ[SBYTES];
-  __shared__ float sb[64];
-  __shared__ float sbeta[64];
+  __shared__ __attribute__((aligned(16))) float sb[64];
+  __shared__ __attribute__((aligned(16))) float sbeta[64];
   float* sA = reinterpret_cast<float*>(sKQ);
   float* sT = reinterpret_cast<float*>(sKQ + TBYTES);
 
@@ -235,19 +235,23 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     if (job < 10) {
       const int j = 16 * r2 + idx;
       const float bj = sb[j];
+      // rows t = 16 r1 + 4 grp + r: four consecutive entries, one 16-byte read each
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(sb + 16 * r1 + 4 * grp);
+      const f32x4 bet = *reinterpret_cast<const f32x4*>(sbeta + 16 * r1 + 4 * grp);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * r1 + 4 * grp + r;
-        sA[t * kLd + j] = j < t ? sbeta[t] * __expf(sb[t] - bj) * acc[i][r] : 0.f;
+        sA[t * kLd + j] = j < t ? bet[r] * __expf(bt[r] - bj) * acc[i][r] : 0.f;
       }
     } else {
       const int t = 16 * r1 + idx;
       const float bt = sb[t];
+      const f32x4 bj = *reinterpret_cast<const f32x4*>(sb + 16 * r2 + 4 * grp);
       f32x4 pv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * r2 + 4 * grp + r;
-        pv[r] = j <= t ? __expf(bt - sb[j]) * acc[i][r] : 0.f;
+        pv[r] = j <= t ? __expf(bt - bj[r]) * acc[i][r] : 0.f;
       }
       store_half_global(Mode{}, rec + kWsPOff + tri_block(r1, r2 >> 1) * kWsBlockBytes, lane,
                         r2 & 1, pv);
@@ -318,11 +322,13 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     const int kb = bi < 2 ? 0 : (bi - 2) % 2;
     const int i = ln & 15, gr = ln >> 4;
     const int t = 16 * rt + i;
+    const f32x4 be0 = *reinterpret_cast<const f32x4*>(sbeta + 32 * kb + 4 * gr);
+    const f32x4 be1 = *reinterpret_cast<const f32x4*>(sbeta + 32 * kb + 16 + 4 * gr);
     float x[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int j = 32 * kb + kslot(gr, s);
-      x[s] = j <= t ? sT[t * kLd + j] * sbeta[j] : 0.f;
+      x[s] = j <= t ? sT[t * kLd + j] * (s < 4 ? be0[s] : be1[s - 4]) : 0.f;
     }
     Mode::store_block(rec + kWsTOff + bi * kWsBlockBytes, ln, Mode::make(x));
   }

@@ -347,12 +347,11 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   };
   auto group_wait = [&]() {
     // LDS serves one CU in order: once the count is reached, the other waves' writes are
-    // visible. The wait is bounded so that a broken count can never hang the device.
-    for (int spin = 0; spin < (1 << 22); ++spin) {
+    // visible. A tight loop (no s_sleep: the waits are short and a sleep quantum costs more
+    // than the reads); bounded so that a broken count can never hang the device.
+    for (int spin = 0; spin < (1 << 22); ++spin)
       if (__hip_atomic_load(sync_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= sync_target)
         break;
-      __builtin_amdgcn_s_sleep(1);
-    }
     asm volatile("" ::: "memory");
   };
 
