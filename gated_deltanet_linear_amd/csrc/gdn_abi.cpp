@@ -69,8 +69,9 @@ gdn_status_t gdn_prepare(const gdn_shape_t* s, const int32_t* cu, const void* x,
   if (!cu || !A_log || !dt_bias) return GDN_ERR_INVALID_ARGUMENT;
   if (s->total_tokens > 0 && (!x || !w || !a || !b || !q || !k || !v || !g || !beta))
     return GDN_ERR_INVALID_ARGUMENT;
-  // 16-byte row access of mixed_qkv / q / k / v.
-  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+  // 16-byte vector access of mixed_qkv / q / k / v rows and of the gate arrays.
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(a, 16) || !aligned(b, 16) || !aligned(g, 16) || !aligned(beta, 16))
     return GDN_ERR_INVALID_ARGUMENT;
   return from_hip(gdn::launch_prepare(*s, cu, x, w, bias, a, b, A_log, dt_bias, eps, q, k, v, g,
                                       beta, static_cast<hipStream_t>(stream)));

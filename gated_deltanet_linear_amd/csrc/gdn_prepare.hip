@@ -8,9 +8,9 @@
 //   q | k | v = split of the channels; q, k head vectors scaled by 1 / sqrt(sum y^2 + eps)
 //   beta = sigmoid(b),  g = -exp(A_log) softplus(a + dt_bias)              (fp32)
 //
-// Grid: x = blocks of 256 tokens, y = one channel head (H_qk q heads, H_qk k heads, H_v v
-// heads) plus one extra row for the gates. A thread owns 8 channels (one 16-byte bf16 load)
-// and walks 256 * 8 / D consecutive tokens with a 3-row sliding window in registers, so each
+// Grid: x = one channel head (H_qk q heads, H_qk k heads, H_v v heads) plus one extra row
+// for the gates, y = blocks of 128 tokens. A thread owns 8 channels (one 16-byte bf16 load)
+// and walks 128 * 8 / D consecutive tokens with a 3-row sliding window in registers, so each
 // input row is fetched once per thread run (plus 3 rows of history at the run start). The
 // D / 8 lanes that share a token are adjacent in the wave; the L2 norm reduces across them
 // with lane shuffles.
@@ -20,26 +20,36 @@
 namespace gdn {
 namespace {
 
-constexpr int kTokBlock = 256;
+constexpr int kTokBlock = 128;
 
+// Eight consecutive input values kept as loaded (converted where used), so that many loads
+// can be in flight before the first one is consumed.
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+struct Raw8;
 template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&x)[8]) {
-  const bf16x8 r = *reinterpret_cast<const bf16x8*>(p);
+struct Raw8<bf16> {
+  bf16x8 r;
+  __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void to(float (&x)[8]) const {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] = a[e];
-    x[4 + e] = b[e];
+    for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
   }
-}
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void to(float (&x)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+  }
+};
 
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float (&x)[8]);
@@ -100,23 +110,67 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
   constexpr int TPT = kTokBlock / TL;  // consecutive tokens per thread
   static_assert(D % 8 == 0 && 256 % CGN == 0 && kTokBlock % TL == 0, "tile shape");
 
-  const int hb = blockIdx.y;
+  // Heads vary fastest over the grid, so that workgroups running together read and write whole
+  // token rows (all heads of the same tokens) rather than one head's slice of many rows.
+  const int hb = blockIdx.x;
   const int tid = threadIdx.x;
-  const int tok0 = blockIdx.x * kTokBlock;
+  const int tok0 = blockIdx.y * kTokBlock;
   const int head_blocks = 2 * p.hqk + p.hv;
 
   if (hb == head_blocks) {  // gates
+    // The block's a / b values are one contiguous run of [128 tokens][H_v]: each thread takes
+    // 8 consecutive elements per step, all loads issued before the first use.
     const InT* A = static_cast<const InT*>(p.a);
     const InT* B = static_cast<const InT*>(p.b);
-    for (int e = tid; e < kTokBlock * p.hv; e += 256) {
-      const int t = tok0 + e / p.hv, h = e % p.hv;
-      if (t >= p.T) break;
-      const size_t i = (size_t)t * p.hv + h;
-      const float bv = to_f32(B[i]);
-      const float xa = to_f32(A[i]) + p.dt_bias[h];
-      const float sp = fmaxf(xa, 0.f) + log1pf(expf(-fabsf(xa)));
-      p.beta[i] = 1.f / (1.f + expf(-bv));
-      p.g[i] = -expf(p.A_log[h]) * sp;
+    const size_t e0 = (size_t)tok0 * p.hv;
+    const int ne = min(kTokBlock, p.T - tok0) * p.hv;  // elements of this block
+    constexpr int KMAX = 8;                           // steps per pass (H_v <= 64 in one pass)
+    for (int base = 0; base < ne; base += 8 * 256 * KMAX) {
+      Raw8<InT> ra[KMAX], rb[KMAX];
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const int e = base + 8 * (tid + 256 * k);
+        if (e + 8 <= ne) {
+          ra[k].load(A + e0 + e);
+          rb[k].load(B + e0 + e);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        const int e = base + 8 * (tid + 256 * k);
+        if (e >= ne) break;
+        float av[8], bv[8];
+        if (e + 8 <= ne) {
+          ra[k].to(av);
+          rb[k].to(bv);
+        } else {  // ragged end of the run (H_v * tokens not a multiple of 8)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            av[u] = e + u < ne ? to_f32(A[e0 + e + u]) : 0.f;
+            bv[u] = e + u < ne ? to_f32(B[e0 + e + u]) : 0.f;
+          }
+        }
+        float gv[8], betav[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int h = (int)((e0 + e + u) % p.hv);
+          const float xa = av[u] + p.dt_bias[h];
+          const float sp = fmaxf(xa, 0.f) + log1pf(expf(-fabsf(xa)));
+          betav[u] = 1.f / (1.f + expf(-bv[u]));
+          gv[u] = -expf(p.A_log[h]) * sp;
+        }
+        if (e + 8 <= ne) {
+          store8(p.beta + e0 + e, betav);
+          store8(p.g + e0 + e, gv);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (e + u < ne) {
+              p.beta[e0 + e + u] = betav[u];
+              p.g[e0 + e + u] = gv[u];
+            }
+        }
+      }
     }
     return;
   }
@@ -158,16 +212,25 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
 
   const int t_first = tok0 + tl * TPT;
   if (t_first >= p.T) return;  // whole token group idle (its CGN lanes leave together)
+
+  // Every row of this thread's run and the 3 rows of history are loaded before anything else
+  // (TPT + 3 loads in flight per thread); the sequence lookup below overlaps with them, and
+  // history rows from before the sequence start are dropped where they would be used.
+  Raw8<InT> hist[3], rows[TPT];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) hist[j].load(X + (size_t)max(t_first - 3 + j, 0) * conv_dim);
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) rows[j].load(X + (size_t)min(t_first + j, p.T - 1) * conv_dim);
   int n = token_to_seq(p.cu, p.num_seqs, t_first);
   int seq_start = p.cu[n], seq_end = p.cu[n + 1];
-
   float xm3[8], xm2[8], xm1[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) xm3[e] = xm2[e] = xm1[e] = 0.f;
-  if (t_first - 3 >= seq_start) load8(X + (size_t)(t_first - 3) * conv_dim, xm3);
-  if (t_first - 2 >= seq_start) load8(X + (size_t)(t_first - 2) * conv_dim, xm2);
-  if (t_first - 1 >= seq_start) load8(X + (size_t)(t_first - 1) * conv_dim, xm1);
+  if (t_first - 3 >= seq_start) hist[0].to(xm3);
+  if (t_first - 2 >= seq_start) hist[1].to(xm2);
+  if (t_first - 1 >= seq_start) hist[2].to(xm1);
 
+#pragma unroll
   for (int j = 0; j < TPT; ++j) {
     const int t = t_first + j;
     if (t >= p.T) break;
@@ -179,7 +242,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
       for (int e = 0; e < 8; ++e) xm3[e] = xm2[e] = xm1[e] = 0.f;
     }
     float x0[8], y[8];
-    load8(X + (size_t)t * conv_dim, x0);
+    rows[j].to(x0);
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -210,9 +273,9 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
 
 template <typename InT, typename QT, int D>
 hipError_t launch_prepare_t(const PrepParams& p, hipStream_t stream) {
-  const unsigned gx = (unsigned)((p.T + kTokBlock - 1) / kTokBlock);
-  const unsigned gy = (unsigned)(2 * p.hqk + p.hv + 1);
-  if (gx == 0) return hipSuccess;
+  const unsigned gx = (unsigned)(2 * p.hqk + p.hv + 1);
+  const unsigned gy = (unsigned)((p.T + kTokBlock - 1) / kTokBlock);
+  if (gy == 0) return hipSuccess;
   hipLaunchKernelGGL((prepare_kernel<InT, QT, D>), dim3(gx, gy), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -83,6 +83,8 @@ typedef struct gdn_shape {
  *   q, k (out)  [T][H_qk][d_k]             qkv_dtype
  *   v    (out)  [T][H_v][d_v]              qkv_dtype
  *   g, beta (out) [T][H_v]                 fp32 (g is the log-decay, <= 0)
+ * mixed_qkv, a, b, q, k, v, g and beta must be 16-byte aligned (16-byte vector accesses);
+ * GDN_ERR_INVALID_ARGUMENT otherwise.
  */
 gdn_status_t gdn_prepare(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                          const void* mixed_qkv, const void* conv_weight, const void* conv_bias,

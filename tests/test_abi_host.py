@@ -134,6 +134,14 @@ def test_prepare_validation(lib):
     ins = list(good)
     ins[1] = ctypes.c_void_p((1 << 20) + 8)  # mixed_qkv must be 16-byte aligned
     assert call(s, ins, 1e-6, outs) == INVALID
+    for i in (4, 5):  # a, b
+        ins = list(good)
+        ins[i] = ctypes.c_void_p((1 << 20) + 4)
+        assert call(s, ins, 1e-6, outs) == INVALID
+    for i in (3, 4):  # g, beta
+        o = list(outs)
+        o[i] = ctypes.c_void_p((1 << 20) + 4)
+        assert call(s, good, 1e-6, o) == INVALID
     assert call(_shape(head_dim_k=16, head_dim_v=16), good, 1e-6, outs) == UNSUPPORTED
 
 
