@@ -27,22 +27,29 @@ namespace {
 
 // 16x16x16 fp32 product on MFMA with the 16-deep version of the fragment convention:
 // A from LDS (row-major, leading dim ld), B either from LDS or from a C fragment in registers.
-constexpr int kLd = 65;  // padded row length of the 64x64 fp32 LDS matrices
+// Padded row length of the 64x64 fp32 LDS matrices: rows start 16-byte aligned (4 consecutive
+// columns are one 16-byte access) and consecutive rows start 4 banks apart.
+constexpr int kLd = 68;
+
+__device__ __forceinline__ f32x4 row4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
 
 __device__ __forceinline__ f32x4 mm16_ll(const float* A, const float* B, f32x4 c, int idx,
                                          int grp) {
   // A: 16x16 block at A (row stride kLd), B: 16x16 block at B (row stride kLd).
+  const f32x4 a = row4(A + idx * kLd + 4 * grp);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[idx * kLd + 4 * grp + r],
-                                             B[(4 * grp + r) * kLd + idx], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], B[(4 * grp + r) * kLd + idx], c, 0, 0, 0);
   return c;
 }
 __device__ __forceinline__ f32x4 mm16_lr(const float* A, const f32x4& Bc, f32x4 c, int idx,
                                          int grp) {
+  const f32x4 a = row4(A + idx * kLd + 4 * grp);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[idx * kLd + 4 * grp + r], Bc[r], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], Bc[r], c, 0, 0, 0);
   return c;
 }
 __device__ __forceinline__ void store_c16(float* C, const f32x4& c, int idx, int grp,
@@ -177,7 +184,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
   lds_barrier();
 
   // ---- 22 tile jobs, round robin over the waves (wave w: jobs w, w+4, ..., w+16 on MFMA,
-  // and job w+20 for waves 0, 1):
+  // and job w+20 for waves 0, 1). Both kinds are formed transposed (C = K_ct X_rt^T), so that a
+  // lane holds 4 consecutive columns of one row of the wanted tile:
   //   0..9   A tiles (tr >= tc): A_tj = beta_t e^{b_t - b_j} (k_t . k_j) for j < t, into LDS;
   //   10..19 P^T tiles: C = K_ct Q_rt^T, whose C fragment IS half of the stored A fragment of
   //          P = (Q K^T) o Gamma o lower-incl (block (rt, ct / 2), slots 4 (ct % 2) + r);
@@ -198,9 +206,9 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     const bool isp = job >= 10;
     int r1, r2;
     job_tiles(job, r1, r2);
-    // A tiles: rows r1 of K against rows r2 of K.  P^T tiles: rows r2 of K against rows r1 of Q.
-    const int ra = isp ? 16 * r2 + idx : 16 * r1 + idx;
-    const int rb = isp ? 16 * r1 + idx : 16 * r2 + idx;
+    // Rows r2 of K against rows r1 of K (A^T tiles) or of Q (P^T tiles).
+    const int ra = 16 * r2 + idx;
+    const int rb = 16 * r1 + idx;
     const char* bsrc = isp ? sQ : sK;
     frag_t fa[KB], fb[KB];
 #pragma unroll
@@ -233,16 +241,17 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     int r1, r2;
     job_tiles(job, r1, r2);
     if (job < 10) {
-      const int j = 16 * r2 + idx;
-      const float bj = sb[j];
-      // rows t = 16 r1 + 4 grp + r: four consecutive entries, one 16-byte read each
-      const f32x4 bt = *reinterpret_cast<const f32x4*>(sb + 16 * r1 + 4 * grp);
-      const f32x4 bet = *reinterpret_cast<const f32x4*>(sbeta + 16 * r1 + 4 * grp);
+      // lane: row t = 16 r1 + idx, columns j = 16 r2 + 4 grp + r (one 16-byte write)
+      const int t = 16 * r1 + idx;
+      const float bt = sb[t], bet = sbeta[t];
+      const f32x4 bj = *reinterpret_cast<const f32x4*>(sb + 16 * r2 + 4 * grp);
+      f32x4 av;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * r1 + 4 * grp + r;
-        sA[t * kLd + j] = j < t ? bet[r] * __expf(bt[r] - bj) * acc[i][r] : 0.f;
+        const int j = 16 * r2 + 4 * grp + r;
+        av[r] = j < t ? bet * __expf(bt - bj[r]) * acc[i][r] : 0.f;
       }
+      *reinterpret_cast<f32x4*>(sA + t * kLd + 16 * r2 + 4 * grp) = av;
     } else {
       const int t = 16 * r1 + idx;
       const float bt = sb[t];
@@ -266,7 +275,11 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     const float* Ab = sA + (16 * wave) * kLd + 16 * wave;
     float arow[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) arow[j] = Ab[(lane & 15) * kLd + j];
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const f32x4 a4 = row4(Ab + (lane & 15) * kLd + 4 * j4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) arow[4 * j4 + e] = a4[e];
+    }
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
@@ -322,13 +335,14 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     const int kb = bi < 2 ? 0 : (bi - 2) % 2;
     const int i = ln & 15, gr = ln >> 4;
     const int t = 16 * rt + i;
-    const f32x4 be0 = *reinterpret_cast<const f32x4*>(sbeta + 32 * kb + 4 * gr);
-    const f32x4 be1 = *reinterpret_cast<const f32x4*>(sbeta + 32 * kb + 16 + 4 * gr);
+    const f32x4 be0 = row4(sbeta + 32 * kb + 4 * gr), be1 = row4(sbeta + 32 * kb + 16 + 4 * gr);
+    const f32x4 t0 = row4(sT + t * kLd + 32 * kb + 4 * gr);
+    const f32x4 t1 = row4(sT + t * kLd + 32 * kb + 16 + 4 * gr);
     float x[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int j = 32 * kb + kslot(gr, s);
-      x[s] = j <= t ? sT[t * kLd + j] * (s < 4 ? be0[s] : be1[s - 4]) : 0.f;
+      x[s] = j <= t ? (s < 4 ? t0[s] * be0[s] : t1[s - 4] * be1[s - 4]) : 0.f;
     }
     Mode::store_block(rec + kWsTOff + bi * kWsBlockBytes, ln, Mode::make(x));
   }
