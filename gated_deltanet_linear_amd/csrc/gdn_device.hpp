@@ -185,11 +185,6 @@ __device__ __forceinline__ int slot_to_seq(const int32_t* cu, int num_seqs, int 
   return lo;
 }
 
-// Workgroup order that puts consecutive logical ids on one XCD (dispatch is round robin
-// over the 8 XCDs), so groups that read the same q/k tiles share an L2.
-__device__ __forceinline__ int xcd_logical_id(int b, int total) {
-  return (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
-}
 
 
 // ---- LDS staging and operand fragments from staged rows -------------------------------

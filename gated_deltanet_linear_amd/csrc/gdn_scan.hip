@@ -122,6 +122,7 @@ __device__ __forceinline__ void store_half(F32Mode, char* blk, int lane, int hal
 constexpr int kRecUnits = kWsRecordBytes / 16;                   // 16-byte units per record
 constexpr int kRecStage = (kWsRecordBytes + 1023) / 1024 * 1024;  // staged record bytes
 constexpr int kLdsBytes = 160 * 1024;                             // LDS per workgroup
+constexpr int kSortSeqs = 64;  // batches of up to this many sequences run longest first
 
 // C fragment (rows 4 grp + r, column idx) of a 16 x 16 tile stored row-major in LDS with row
 // stride `stride` bytes. bf16: one ds_read_b64_tr_b16 (lane (g, a + 4e) addresses row 4g + e,
@@ -215,9 +216,37 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   constexpr int NB = D / 16 / NT;
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int dvb = lid % NB, nh = lid / NB;
-  const int h = nh % p.hv, n = nh / p.hv;
+  // Work assignment. The hardware deals workgroups round robin over the 8 XCDs (b % 8). A unit
+  // (sequence, V head) has NB workgroups that read the same q/k rows and records: they stay on
+  // one XCD (one L2) and are dispatched back to back. Units are dealt to the XCDs round robin
+  // in order of decreasing sequence length (ties by index), so that every XCD gets an equal
+  // share of a packed batch of uneven sequences and runs its longest chains first.
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int u = 8 * (j / NB) + xcd, dvb = j % NB;
+  if (u >= p.num_seqs * p.hv) return;  // padding workgroup (whole workgroup, before any barrier)
+  const int h = u % p.hv, rank = u / p.hv;
+  int n = rank;
+  if (p.num_seqs <= kSortSeqs) {
+    // rank -> sequence: sequence t has rank #{s : L_s > L_t or (L_s = L_t and s < t)}. The
+    // scratch is the start of chunk buffer 0, which nothing else uses yet.
+    int* len_s = reinterpret_cast<int*>(smem);
+    int* pick = len_s + kSortSeqs;
+    for (int t = tid; t < p.num_seqs; t += C::THREADS) len_s[t] = p.cu[t + 1] - p.cu[t];
+    lds_barrier();
+    for (int t = tid; t < p.num_seqs; t += C::THREADS) {
+      const int lt = len_s[t];
+      int r = 0;
+      for (int s2 = 0; s2 < p.num_seqs; ++s2) {
+        const int ls = len_s[s2];
+        r += (ls > lt || (ls == lt && s2 < t)) ? 1 : 0;
+      }
+      if (r == rank) *pick = t;
+    }
+    lds_barrier();
+    n = __builtin_amdgcn_readfirstlane(*pick);
+    lds_barrier();  // every wave has read the pick before buffer 0 is staged
+  }
+  const int nh = n * p.hv + h;
   const int G = p.hv / p.hqk, m = h / G;
   const int start = p.cu[n];
   const int L = p.cu[n + 1] - start;
@@ -626,8 +655,10 @@ template <typename Mode, int D, int NT, int RW, typename OutT>
 hipError_t launch_scan_cfg(const ScanParams& p, long long heads, hipStream_t stream) {
   static_assert(D / 16 % NT == 0, "d_v tiles per workgroup");
   using C = ScanCfg<Mode, D, NT, RW, OutT>;
-  const unsigned blocks = (unsigned)(heads * (D / 16 / NT));
-  if (blocks == 0) return hipSuccess;
+  // Units (sequence, V head) are dealt to the 8 XCDs round robin; padding workgroups exit.
+  constexpr int NB = D / 16 / NT;
+  const unsigned blocks = (unsigned)(8 * NB * ((heads + 7) / 8));
+  if (heads == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_scan_kernel<Mode, D, NT, RW, OutT>), dim3(blocks), dim3(C::THREADS), 0,
                      stream, p);
   return hipGetLastError();
