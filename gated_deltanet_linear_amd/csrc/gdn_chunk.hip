@@ -65,7 +65,7 @@ struct IntraParams {
   const float* g;
   const float* beta;
   char* ws;
-  int num_seqs, hqk, hv;
+  int num_seqs, hqk, hv, num_slots;
 };
 
 template <typename Mode, int ROWB>
@@ -133,7 +133,13 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
   float* sA = reinterpret_cast<float*>(sKQ);
   float* sT = reinterpret_cast<float*>(sKQ + TBYTES);
 
-  const int slot = blockIdx.x, h = blockIdx.y;
+  // Work assignment: units (chunk slot, QK head) are dealt to the 8 XCDs round robin (the
+  // hardware deals workgroups b to XCD b % 8); the G workgroups of a unit (its V heads, which
+  // read the same q/k rows) are dispatched back to back on one XCD and share its L2.
+  const int G = p.hv / p.hqk;
+  const int j = blockIdx.x >> 3, unit = 8 * (j / G) + (blockIdx.x & 7);
+  const int slot = unit / p.hqk, h = (unit % p.hqk) * G + j % G;
+  if (slot >= p.num_slots) return;  // padding workgroup (uniform)
   const int n = slot_to_seq(p.cu, p.num_seqs, slot);
   const int t0 = p.cu[n] + kChunk * (slot - slot_base(p.cu, n));
   const int tend = p.cu[n + 1];
@@ -355,8 +361,11 @@ template <typename Mode, int D>
 hipError_t launch_intra_t(const gdn_shape_t& s, const IntraParams& p, hipStream_t stream) {
   const long long slots = chunk_slots(s);
   if (slots <= 0 || s.total_tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_intra_kernel<Mode, D>), dim3((unsigned)slots, (unsigned)s.num_v_heads),
-                     dim3(256), 0, stream, p);
+  const long long units = slots * s.num_qk_heads, G = s.num_v_heads / s.num_qk_heads;
+  IntraParams q = p;
+  q.num_slots = (int)slots;
+  hipLaunchKernelGGL((chunk_intra_kernel<Mode, D>), dim3((unsigned)(8 * G * ((units + 7) / 8))),
+                     dim3(256), 0, stream, q);
   return hipGetLastError();
 }
 
@@ -376,7 +385,7 @@ hipError_t launch_chunk_intra(const gdn_shape_t& s, const int32_t* cu, const voi
                               const void* k, const float* g, const float* beta, void* ws,
                               hipStream_t stream) {
   IntraParams p{cu, q, k, g, beta, static_cast<char*>(ws), s.num_seqs, s.num_qk_heads,
-                s.num_v_heads};
+                s.num_v_heads, 0};
   if (s.qkv_dtype == GDN_DTYPE_BF16) return launch_intra_d<Bf16Mode>(s, p, stream);
   return launch_intra_d<F32Mode>(s, p, stream);
 }
