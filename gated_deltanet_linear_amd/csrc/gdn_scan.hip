@@ -217,14 +217,15 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   constexpr int NB = D / 16 / NT;
   // Work assignment. The hardware deals workgroups round robin over the 8 XCDs (b % 8). A unit
-  // (sequence, V head) has NB workgroups that read the same q/k rows and records: they stay on
-  // one XCD (one L2) and are dispatched back to back. Units are dealt to the XCDs round robin
-  // in order of decreasing sequence length (ties by index), so that every XCD gets an equal
-  // share of a packed batch of uneven sequences and runs its longest chains first.
+  // (sequence, QK head) has G * NB workgroups (its V heads x column tiles) that read the same
+  // q/k rows: they stay on one XCD (one L2) and are dispatched back to back. Units are dealt to
+  // the XCDs round robin in order of decreasing sequence length (ties by index), so that every
+  // XCD gets an equal share of a packed batch of uneven sequences, longest chains first.
+  const int G = p.hv / p.hqk;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int u = 8 * (j / NB) + xcd, dvb = j % NB;
-  if (u >= p.num_seqs * p.hv) return;  // padding workgroup (whole workgroup, before any barrier)
-  const int h = u % p.hv, rank = u / p.hv;
+  const int u = 8 * (j / (G * NB)) + xcd, w = j % (G * NB), dvb = w % NB;
+  if (u >= p.num_seqs * p.hqk) return;  // padding workgroup (whole workgroup, before any barrier)
+  const int m = u % p.hqk, h = m * G + w / NB, rank = u / p.hqk;
   int n = rank;
   if (p.num_seqs <= kSortSeqs) {
     // rank -> sequence: sequence t has rank #{s : L_s > L_t or (L_s = L_t and s < t)}. The
@@ -247,7 +248,6 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     lds_barrier();  // every wave has read the pick before buffer 0 is staged
   }
   const int nh = n * p.hv + h;
-  const int G = p.hv / p.hqk, m = h / G;
   const int start = p.cu[n];
   const int L = p.cu[n + 1] - start;
   const int nchunks = (L + kChunk - 1) / kChunk;
@@ -652,12 +652,14 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
 }
 
 template <typename Mode, int D, int NT, int RW, typename OutT>
-hipError_t launch_scan_cfg(const ScanParams& p, long long heads, hipStream_t stream) {
+hipError_t launch_scan_cfg(const ScanParams& p, long long heads, int G, hipStream_t stream) {
   static_assert(D / 16 % NT == 0, "d_v tiles per workgroup");
   using C = ScanCfg<Mode, D, NT, RW, OutT>;
-  // Units (sequence, V head) are dealt to the 8 XCDs round robin; padding workgroups exit.
+  // Units (sequence, QK head) of G * NB workgroups are dealt to the 8 XCDs round robin;
+  // padding workgroups exit.
   constexpr int NB = D / 16 / NT;
-  const unsigned blocks = (unsigned)(8 * NB * ((heads + 7) / 8));
+  const long long units = heads / G;
+  const unsigned blocks = (unsigned)(8 * G * NB * ((units + 7) / 8));
   if (heads == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_scan_kernel<Mode, D, NT, RW, OutT>), dim3(blocks), dim3(C::THREADS), 0,
                      stream, p);
@@ -680,14 +682,15 @@ int forced_layout() {
 template <typename Mode, int D, typename OutT>
 hipError_t launch_scan_t(const gdn_shape_t& s, const ScanParams& p, hipStream_t stream) {
   const long long heads = (long long)s.num_seqs * s.num_v_heads;
+  const int G = s.num_v_heads / s.num_qk_heads;
   constexpr int tiles = D / 16;
   // Few (sequence, head) chains: 4 waves per 16-column tile so that every SIMD gets work.
   // Many chains: 1 wave per tile, 4 tiles per workgroup sharing the staged chunk.
   const int forced = forced_layout();
   if (forced == 1 || (forced == 0 && heads * tiles <= 512))
-    return launch_scan_cfg<Mode, D, 1, 4, OutT>(p, heads, stream);
-  if constexpr (tiles % 4 == 0) return launch_scan_cfg<Mode, D, 4, 1, OutT>(p, heads, stream);
-  else return launch_scan_cfg<Mode, D, 2, 1, OutT>(p, heads, stream);
+    return launch_scan_cfg<Mode, D, 1, 4, OutT>(p, heads, G, stream);
+  if constexpr (tiles % 4 == 0) return launch_scan_cfg<Mode, D, 4, 1, OutT>(p, heads, G, stream);
+  else return launch_scan_cfg<Mode, D, 2, 1, OutT>(p, heads, G, stream);
 }
 
 template <typename Mode, typename OutT>
