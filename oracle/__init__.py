@@ -51,6 +51,12 @@ def _load():
     lib.gdn_oracle_prepare.restype = ctypes.c_int
     lib.gdn_oracle_prepare.argtypes = [i64, lp, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
                                        ctypes.c_double, dp, dp, dp, dp, dp]
+    lib.gdn_oracle_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_oracle_gated_rmsnorm.argtypes = [i64, i64, dp, dp, dp, ctypes.c_double,
+                                             ctypes.c_double, dp]
+    lib.gdn_oracle_decode_prepare.restype = ctypes.c_int
+    lib.gdn_oracle_decode_prepare.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp,
+                                              dp, dp, ctypes.c_double, dp, dp, dp, dp, dp]
     lib.gdn_oracle_num_threads.restype = ctypes.c_int
     lib.gdn_oracle_num_threads.argtypes = []
     _lib = lib
@@ -129,3 +135,52 @@ def prepare(mixed_qkv, conv_weight, a, b, A_log, dt_bias, cu_seqlens, num_qk_hea
     if rc != 0:
         raise ValueError("gdn_oracle_prepare rejected its arguments")
     return q, k, v, g, beta
+
+
+def gated_rmsnorm(o, z, weight=None, weight_offset=0.0, eps=1e-6):
+    """Output gate in float64: RMSNorm(o) * SiLU(z) over the last axis.
+
+    o, z: [..., dv]; weight: [dv] or None (factor 1); factor = weight + weight_offset.
+    """
+    lib = _load()
+    o, z, w = _f64(o), _f64(z), _f64(weight)
+    assert o.shape == z.shape and o.ndim >= 1
+    dv = o.shape[-1]
+    rows = o.size // dv if dv else 0
+    if w is not None:
+        assert w.shape == (dv,)
+    out = np.zeros_like(o)
+    rc = lib.gdn_oracle_gated_rmsnorm(rows, dv, _ptr(o), _ptr(z), _ptr(w), float(weight_offset),
+                                      float(eps), _ptr(out))
+    if rc != 0:
+        raise ValueError("gdn_oracle_gated_rmsnorm rejected its arguments")
+    return out
+
+
+def decode_prepare(x, window, conv_weight, a, b, A_log, dt_bias, num_qk_heads, head_dim_k,
+                   num_v_heads, head_dim_v, conv_bias=None, l2_eps=1e-6):
+    """Decode-side front end in float64 for one token per sequence with a conv window.
+
+    x: [N, conv_dim]; window: [N, conv_dim, 3] (previous inputs, oldest first).
+    Returns q [N,Hqk,dk], k [N,Hqk,dk], v [N,Hv,dv], g [N,Hv], beta [N,Hv], new window.
+    """
+    lib = _load()
+    x, w, a, b = (_f64(t) for t in (x, conv_weight, a, b))
+    win = np.array(window, dtype=np.float64, order="C", copy=True)
+    A_log, dt_bias, bias = _f64(A_log), _f64(dt_bias), _f64(conv_bias)
+    N = x.shape[0]
+    hqk, dk, hv, dv = int(num_qk_heads), int(head_dim_k), int(num_v_heads), int(head_dim_v)
+    assert x.shape[1] == 2 * hqk * dk + hv * dv and w.shape == (x.shape[1], 4)
+    assert win.shape == (N, x.shape[1], 3) and a.shape == (N, hv) and b.shape == (N, hv)
+    q = np.zeros((N, hqk, dk))
+    k = np.zeros((N, hqk, dk))
+    v = np.zeros((N, hv, dv))
+    g = np.zeros((N, hv))
+    beta = np.zeros((N, hv))
+    rc = lib.gdn_oracle_decode_prepare(N, hqk, hv, dk, dv, _ptr(x), _ptr(win), _ptr(w),
+                                       _ptr(bias), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                       float(l2_eps), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta))
+    if rc != 0:
+        raise ValueError("gdn_oracle_decode_prepare rejected its arguments")
+    return q, k, v, g, beta, win

@@ -184,3 +184,89 @@ int gdn_oracle_prepare(int64_t num_seqs, const int64_t* cu, int64_t hqk, int64_t
   }
   return bad ? -1 : 0;
 }
+
+/* Output gate ([xiwon notes] "Qwen3_5MoeGatedDeltaNet", output stage: the core output and z are
+ * reshaped to head_v_dim rows and normed together; [MoE report] §3.3 stage 4): per row of dv
+ * values, RMSNorm then times SiLU(z). The RMSNorm divides by sqrt(mean of squares + eps) and
+ * multiplies by a per-channel weight; [MoE report] §7.5 gives the model's RMSNorm weight in
+ * the (1 + w) form, the gated norm's form is not stated, so the offset is a parameter:
+ * factor_j = w[j] + w_offset, or 1 when w is NULL. */
+int gdn_oracle_gated_rmsnorm(int64_t rows, int64_t dv, const double* o, const double* z,
+                             const double* w, double w_offset, double eps, double* out) {
+  if (rows < 0 || dv <= 0 || o == NULL || z == NULL || out == NULL || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* x = o + r * dv;
+    double ss = 0.0;
+    for (int64_t j = 0; j < dv; ++j) ss += x[j] * x[j];
+    const double inv = 1.0 / sqrt(ss / (double)dv + eps);
+    for (int64_t j = 0; j < dv; ++j) {
+      const double factor = w != NULL ? w[j] + w_offset : 1.0;
+      out[r * dv + j] = x[j] * inv * factor * silu(z[r * dv + j]);
+    }
+  }
+  return 0;
+}
+
+/* Decode-side front end: one new token per sequence with a cached convolution window
+ * ([xiwon notes] "Cache": the conv state keeps the last inputs of each channel so that a
+ * decode step convolves without the history; [MoE report] §3.3 stage 2). Per channel c of
+ * sequence n the window holds the 3 previous mixed_qkv values, oldest first (zeros before the
+ * sequence start):
+ *   y = bias[c] + w[c][0] win[0] + w[c][1] win[1] + w[c][2] win[2] + w[c][3] x[c],  SiLU(y),
+ * then the q | k | v split, q and k head vectors divided by sqrt(sum of squares + eps), and the
+ * gates beta = sigmoid(b), g = -exp(A_log) softplus(a + dt_bias), as in gdn_oracle_prepare for
+ * the same token. The window then becomes (win[1], win[2], x[c]).
+ *   x : [N][conv_dim]   window : [N][conv_dim][3] (in/out)   a, b : [N][hv]
+ *   out q, k : [N][hqk][dk]   v : [N][hv][dv]   g, beta : [N][hv] */
+int gdn_oracle_decode_prepare(int64_t num_seqs, int64_t hqk, int64_t hv, int64_t dk, int64_t dv,
+                              const double* x, double* window, const double* w,
+                              const double* bias, const double* a, const double* b,
+                              const double* A_log, const double* dt_bias, double l2_eps,
+                              double* q, double* k, double* v, double* g, double* beta) {
+  if (num_seqs < 0 || hqk <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || hv % hqk != 0) return -1;
+  const int64_t qdim = hqk * dk, vdim = hv * dv;
+  const int64_t conv_dim = 2 * qdim + vdim;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < num_seqs; ++n) {
+    double* y = (double*)malloc(sizeof(double) * (size_t)conv_dim);
+    if (y == NULL) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    for (int64_t c = 0; c < conv_dim; ++c) {
+      double* win = window + (n * conv_dim + c) * 3;
+      const double xc = x[n * conv_dim + c];
+      double acc = bias != NULL ? bias[c] : 0.0;
+      acc += w[c * 4 + 0] * win[0] + w[c * 4 + 1] * win[1] + w[c * 4 + 2] * win[2] +
+             w[c * 4 + 3] * xc;
+      y[c] = silu(acc);
+      win[0] = win[1];
+      win[1] = win[2];
+      win[2] = xc;
+    }
+    for (int64_t hh = 0; hh < hqk; ++hh) {
+      const double* yq = y + hh * dk;
+      const double* yk = y + qdim + hh * dk;
+      double sq = 0.0, sk = 0.0;
+      for (int64_t i = 0; i < dk; ++i) {
+        sq += yq[i] * yq[i];
+        sk += yk[i] * yk[i];
+      }
+      const double nq = sqrt(sq + l2_eps), nk = sqrt(sk + l2_eps);
+      for (int64_t i = 0; i < dk; ++i) {
+        q[(n * hqk + hh) * dk + i] = yq[i] / nq;
+        k[(n * hqk + hh) * dk + i] = yk[i] / nk;
+      }
+    }
+    for (int64_t i = 0; i < vdim; ++i) v[n * vdim + i] = y[2 * qdim + i];
+    for (int64_t h = 0; h < hv; ++h) {
+      beta[n * hv + h] = 1.0 / (1.0 + exp(-b[n * hv + h]));
+      g[n * hv + h] = -exp(A_log[h]) * softplus(a[n * hv + h] + dt_bias[h]);
+    }
+    free(y);
+  }
+  return bad ? -1 : 0;
+}

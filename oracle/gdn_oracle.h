@@ -50,6 +50,23 @@ int gdn_oracle_prepare(int64_t num_seqs, const int64_t* cu_seqlens,
                        const double* A_log, const double* dt_bias, double l2_eps,
                        double* q, double* k, double* v, double* g, double* beta);
 
+/* Output gate: out = RMSNorm(o) * SiLU(z) per row of dv values,
+ *   out[r][j] = o[r][j] / sqrt(mean_j o[r][.]^2 + eps) * factor_j * z[r][j] sigmoid(z[r][j]),
+ *   factor_j = w[j] + w_offset, or 1 when w is NULL.   o, z, out : [rows][dv]. */
+int gdn_oracle_gated_rmsnorm(int64_t rows, int64_t dv, const double* o, const double* z,
+                             const double* w, double w_offset, double eps, double* out);
+
+/* Decode-side front end for one token per sequence with a cached conv window.
+ *   x : [N][conv_dim]   window : [N][conv_dim][3] previous inputs, oldest first (in/out:
+ *   becomes (window[1], window[2], x))   w : [conv_dim][4]   bias : [conv_dim] or NULL
+ *   a, b : [N][hv]   A_log, dt_bias : [hv]
+ *   out q, k : [N][hqk][dk]   v : [N][hv][dv]   g, beta : [N][hv] */
+int gdn_oracle_decode_prepare(int64_t num_seqs, int64_t hqk, int64_t hv, int64_t dk, int64_t dv,
+                              const double* x, double* window, const double* w,
+                              const double* bias, const double* a, const double* b,
+                              const double* A_log, const double* dt_bias, double l2_eps,
+                              double* q, double* k, double* v, double* g, double* beta);
+
 /* Number of OpenMP threads the oracle runs on (for reporting). */
 int gdn_oracle_num_threads(void);
 
