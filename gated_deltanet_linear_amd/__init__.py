@@ -10,6 +10,8 @@ Entry points (same names as the C ABI in ``include/gdn.h``):
   chunk_forward(...)   chunked prefill (chunk 64), optional initial/final states, varlen
   chunk_intra(...), chunk_scan(...)  the two stages of chunk_forward
   recurrent_step(...)  one decode token per sequence, state updated in place
+  decode_prepare(...)  front end of one decode token per sequence with a cached conv window
+  gated_rmsnorm(...)   output gate RMSNorm(o) * SiLU(z) per V-head vector
 """
 
 from __future__ import annotations
@@ -21,7 +23,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["prepare", "chunk_forward", "chunk_intra", "chunk_scan", "recurrent_step",
-           "workspace_size", "library_path", "GdnError", "CHUNK"]
+           "decode_prepare", "gated_rmsnorm", "workspace_size", "library_path", "GdnError",
+           "CHUNK"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgdn.so")
@@ -73,6 +76,11 @@ def _load():
     lib.gdn_chunk_scan.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.gdn_decode_prepare.restype = ctypes.c_int
+    lib.gdn_decode_prepare.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                       _P, _P, _P, _P]
+    lib.gdn_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_gated_rmsnorm.argtypes = [sp, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_abi_version.restype = ctypes.c_int
@@ -268,3 +276,75 @@ def prepare(mixed_qkv, conv_weight, a, b, A_log, dt_bias, cu_seqlens, num_qk_hea
                              _stream())
     _check(rc, "gdn_prepare")
     return q, k, v, g, beta
+
+
+def decode_prepare(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, num_qk_heads,
+                   head_dim_k, num_v_heads, head_dim_v, conv_bias=None, l2norm_eps=1e-6,
+                   qkv_dtype=None):
+    """Front end of one decode token per sequence with a cached conv window.
+
+    mixed_qkv [N, conv_dim]; conv_window [N, conv_dim, 3] (previous inputs, oldest first; updated
+    in place to the last three). Returns q, k [N, H_qk, d_k], v [N, H_v, d_v] (qkv_dtype, default
+    the input dtype) and g, beta [N, H_v] fp32.
+    """
+    _dev(mixed_qkv, "mixed_qkv")
+    dt = mixed_qkv.dtype
+    _dev(conv_window, "conv_window", dt)
+    _dev(conv_weight, "conv_weight", dt)
+    _dev(a, "a", dt)
+    _dev(b, "b", dt)
+    _dev(A_log, "A_log", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    if conv_bias is not None:
+        _dev(conv_bias, "conv_bias", dt)
+    N, conv_dim = mixed_qkv.shape
+    hqk, dk, hv, dv = int(num_qk_heads), int(head_dim_k), int(num_v_heads), int(head_dim_v)
+    if conv_dim != 2 * hqk * dk + hv * dv or conv_weight.shape != (conv_dim, 4):
+        raise GdnError("mixed_qkv must be [N, 2*H_qk*d_k + H_v*d_v] and conv_weight [conv_dim, 4]")
+    if conv_window.shape != (N, conv_dim, 3):
+        raise GdnError("conv_window must be [N, conv_dim, 3]")
+    if a.shape != (N, hv) or b.shape != (N, hv) or A_log.shape != (hv,) or dt_bias.shape != (hv,):
+        raise GdnError("a, b must be [N, H_v]; A_log, dt_bias [H_v]")
+    qd = qkv_dtype or dt
+    s = _shape(N, N, hqk, hv, dk, dv, qd, qd, in_dtype=dt)
+    dev = mixed_qkv.device
+    q = torch.empty((N, hqk, dk), dtype=qd, device=dev)
+    k = torch.empty((N, hqk, dk), dtype=qd, device=dev)
+    v = torch.empty((N, hv, dv), dtype=qd, device=dev)
+    g = torch.empty((N, hv), dtype=torch.float32, device=dev)
+    beta = torch.empty((N, hv), dtype=torch.float32, device=dev)
+    rc = _load().gdn_decode_prepare(ctypes.byref(s), _ptr(mixed_qkv), _ptr(conv_window),
+                                    _ptr(conv_weight), _ptr(conv_bias), _ptr(a), _ptr(b),
+                                    _ptr(A_log), _ptr(dt_bias), float(l2norm_eps), _ptr(q),
+                                    _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _stream())
+    _check(rc, "gdn_decode_prepare")
+    return q, k, v, g, beta
+
+
+def gated_rmsnorm(o, z, weight=None, weight_offset=0.0, eps=1e-6, out=None):
+    """Output gate: RMSNorm(o) * SiLU(z) per V-head vector (last axis, d_v).
+
+    o [T, H_v, d_v] (the core output's dtype), z [T, H_v, d_v]; weight [d_v] fp32 or None
+    (factor weight + weight_offset, 1 without a weight). Returns out (a new tensor, or `out`,
+    which may be `o`).
+    """
+    _dev(o, "o")
+    _dev(z, "z")
+    if o.dim() != 3 or z.shape != o.shape:
+        raise GdnError("o and z must be [T, H_v, d_v] of the same shape")
+    if weight is not None:
+        _dev(weight, "weight", torch.float32)
+        if weight.shape != (o.shape[2],):
+            raise GdnError("weight must be [d_v]")
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _dev(out, "out", o.dtype)
+        if out.shape != o.shape:
+            raise GdnError("out must have the shape of o")
+    T, hv, dv = o.shape
+    s = _shape(1, T, 1, hv, dv, dv, o.dtype, o.dtype, in_dtype=z.dtype)
+    rc = _load().gdn_gated_rmsnorm(ctypes.byref(s), _ptr(o), _ptr(z), _ptr(weight),
+                                   float(weight_offset), float(eps), _ptr(out), _stream())
+    _check(rc, "gdn_gated_rmsnorm")
+    return out

@@ -133,4 +133,36 @@ gdn_status_t gdn_recurrent_step(const gdn_shape_t* s, const void* q, const void*
                                              static_cast<hipStream_t>(stream)));
 }
 
+gdn_status_t gdn_decode_prepare(const gdn_shape_t* s, const void* x, void* win, const void* w,
+                                const void* bias, const void* a, const void* b,
+                                const float* A_log, const float* dt_bias, float eps, void* q,
+                                void* k, void* v, float* g, float* beta, void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens != s->num_seqs) return GDN_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!x || !win || !w || !a || !b || !A_log || !dt_bias || !q || !k || !v || !g || !beta)
+    return GDN_ERR_INVALID_ARGUMENT;
+  // 16-byte vector access of the input row, the window, the taps and the q / k / v rows.
+  if (!aligned(x, 16) || !aligned(win, 16) || !aligned(w, 16) || !aligned(q, 16) ||
+      !aligned(k, 16) || !aligned(v, 16))
+    return GDN_ERR_INVALID_ARGUMENT;
+  return from_hip(gdn::launch_decode_prepare(*s, x, win, w, bias, a, b, A_log, dt_bias, eps, q, k,
+                                             v, g, beta, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_gated_rmsnorm(const gdn_shape_t* s, const void* o, const void* z,
+                               const float* weight, float weight_offset, float eps, void* out,
+                               void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f) || !(weight_offset == weight_offset)) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens > 0 && (!o || !z || !out)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(out, 16)) return GDN_ERR_INVALID_ARGUMENT;
+  return from_hip(gdn::launch_gated_rmsnorm(*s, o, z, weight, weight_offset, eps, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

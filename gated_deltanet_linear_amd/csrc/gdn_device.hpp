@@ -228,6 +228,58 @@ __device__ __forceinline__ f32x8 afrag_f32(const char* buf, int row, int kb, int
   return f;
 }
 
+// ---- 8-value vector accesses (one 16-byte bf16 / two 16-byte fp32 accesses) ------------
+
+// Eight consecutive input values kept as loaded (converted where used), so that many loads
+// can be in flight before the first one is consumed.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  bf16x8 r;
+  __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void to(float (&x)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
+  }
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void to(float (&x)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16* p, const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[e];
+  *reinterpret_cast<bf16x8*>(p) = r;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = x[e];
+    b[e] = x[4 + e];
+  }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
 // Barrier for LDS traffic only: waits for this wave's own LDS reads and writes (lgkmcnt) and
 // for the other waves, but not for outstanding global loads (a fence would wait for those too,
 // serialising the prefetch of the next chunk with this one). The memory clobber keeps the

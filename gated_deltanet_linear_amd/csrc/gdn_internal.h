@@ -25,6 +25,15 @@ hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x
                           const float* A_log, const float* dt_bias, float eps, void* q, void* k,
                           void* v, float* g, float* beta, hipStream_t stream);
 
+hipError_t launch_decode_prepare(const gdn_shape_t& s, const void* x, void* window,
+                                 const void* w, const void* bias, const void* a, const void* b,
+                                 const float* A_log, const float* dt_bias, float eps, void* q,
+                                 void* k, void* v, float* g, float* beta, hipStream_t stream);
+
+hipError_t launch_gated_rmsnorm(const gdn_shape_t& s, const void* o, const void* z,
+                                const float* w, float w_offset, float eps, void* out,
+                                hipStream_t stream);
+
 // Bytes of one workspace record (one chunk slot x one V head); the layout is private to
 // gdn_chunk.hip, which checks this value at compile time.
 constexpr long long kWorkspaceRecordBytes = 25088;

@@ -22,56 +22,6 @@ namespace {
 
 constexpr int kTokBlock = 128;
 
-// Eight consecutive input values kept as loaded (converted where used), so that many loads
-// can be in flight before the first one is consumed.
-template <typename T>
-struct Raw8;
-template <>
-struct Raw8<bf16> {
-  bf16x8 r;
-  __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const bf16x8*>(p); }
-  __device__ __forceinline__ void to(float (&x)[8]) const {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
-  }
-};
-template <>
-struct Raw8<float> {
-  f32x4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4*>(p);
-    b = *reinterpret_cast<const f32x4*>(p + 4);
-  }
-  __device__ __forceinline__ void to(float (&x)[8]) const {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = a[e];
-      x[4 + e] = b[e];
-    }
-  }
-};
-
-template <typename T>
-__device__ __forceinline__ void store8(T* p, const float (&x)[8]);
-template <>
-__device__ __forceinline__ void store8<bf16>(bf16* p, const float (&x)[8]) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[e];
-  *reinterpret_cast<bf16x8*>(p) = r;
-}
-template <>
-__device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
-  f32x4 a, b;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    a[e] = x[e];
-    b[e] = x[4 + e];
-  }
-  *reinterpret_cast<f32x4*>(p) = a;
-  *reinterpret_cast<f32x4*>(p + 4) = b;
-}
-
 // Largest n in [0, num_seqs) with cu[n] <= t (the sequence holding token t < cu[num_seqs]).
 __device__ __forceinline__ int token_to_seq(const int32_t* cu, int num_seqs, int t) {
   int lo = 0, hi = num_seqs - 1;
@@ -290,6 +240,151 @@ hipError_t launch_prepare_d(const PrepParams& p, int d, hipStream_t stream) {
   }
 }
 
+// ---- decode side: one token per sequence with a cached convolution window -----------------
+// ([xiwon notes] "Cache": the conv state keeps the last inputs of each channel so that a decode
+// step convolves without the history; [MoE report] §3.3 stage 2, decode path.) Per channel:
+//   y = bias + w[0] win[0] + w[1] win[1] + w[2] win[2] + w[3] x,  then as above,
+// and the window [3] (oldest first) becomes (win[1], win[2], x) in place.
+// Grid: x = sequence, y = groups of 256 / (D / 8) channel heads, plus one row for the gates. A
+// thread owns 8 channels: one 16-byte input access, three for its 24 window values, four for
+// its 32 taps.
+
+struct DecPrepParams {
+  const void* x;
+  void* win;
+  const void* w;
+  const void* bias;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  float eps;
+  void* q;
+  void* k;
+  void* v;
+  float* g;
+  float* beta;
+  int hqk, hv;
+};
+
+template <typename InT, typename QT, int D>
+__global__ __launch_bounds__(256) void decode_prepare_kernel(DecPrepParams p) {
+  constexpr int CGN = D / 8;      // threads per channel head
+  constexpr int HPW = 256 / CGN;  // channel heads per workgroup
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int head_blocks = 2 * p.hqk + p.hv;
+  const int groups = (head_blocks + HPW - 1) / HPW;
+
+  if ((int)blockIdx.y == groups) {  // gates of sequence n
+    const InT* A = static_cast<const InT*>(p.a);
+    const InT* B = static_cast<const InT*>(p.b);
+    for (int h = tid; h < p.hv; h += 256) {
+      const size_t i = (size_t)n * p.hv + h;
+      const float xa = to_f32(A[i]) + p.dt_bias[h];
+      const float sp = fmaxf(xa, 0.f) + log1pf(expf(-fabsf(xa)));
+      p.beta[i] = 1.f / (1.f + expf(-to_f32(B[i])));
+      p.g[i] = -expf(p.A_log[h]) * sp;
+    }
+    return;
+  }
+
+  const int hb_raw = blockIdx.y * HPW + tid / CGN, cg = tid % CGN;
+  const bool active = hb_raw < head_blocks;
+  const int hb = active ? hb_raw : 0;  // idle lanes read head 0 and store nothing
+  const int conv_dim = head_blocks * D;
+  const int c = hb * D + 8 * cg;
+
+  const InT* X = static_cast<const InT*>(p.x) + (size_t)n * conv_dim + c;
+  InT* W3 = static_cast<InT*>(p.win) + ((size_t)n * conv_dim + c) * 3;
+  const InT* Wt = static_cast<const InT*>(p.w) + (size_t)c * 4;
+  Raw8<InT> rx, rw3[3], rt[4];
+  rx.load(X);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) rw3[j].load(W3 + 8 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rt[j].load(Wt + 8 * j);
+  float x[8], wv[24], taps[32], bias[8];
+  rx.to(x);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    float t8[8];
+    rw3[j].to(t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wv[8 * j + e] = t8[e];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float t8[8];
+    rt[j].to(t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) taps[8 * j + e] = t8[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bias[e] = p.bias ? to_f32(static_cast<const InT*>(p.bias)[c + e]) : 0.f;
+
+  // channel e: window wv[3e .. 3e+2] (oldest first), taps taps[4e .. 4e+3]
+  float y[8], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float acc = bias[e];
+    acc = fmaf(taps[4 * e + 0], wv[3 * e + 0], acc);
+    acc = fmaf(taps[4 * e + 1], wv[3 * e + 1], acc);
+    acc = fmaf(taps[4 * e + 2], wv[3 * e + 2], acc);
+    acc = fmaf(taps[4 * e + 3], x[e], acc);
+    y[e] = acc / (1.f + expf(-acc));
+    ss = fmaf(y[e], y[e], ss);
+  }
+  const bool is_qk = hb < 2 * p.hqk;
+#pragma unroll
+  for (int d = 1; d < CGN; d <<= 1) ss += __shfl_xor(ss, d, kWave);  // lanes of one head
+  if (is_qk) {
+    const float inv = 1.f / sqrtf(ss + p.eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] *= inv;
+  }
+  if (!active) return;
+  QT* dst;
+  if (hb < p.hqk) dst = static_cast<QT*>(p.q) + ((size_t)n * p.hqk + hb) * D;
+  else if (hb < 2 * p.hqk) dst = static_cast<QT*>(p.k) + ((size_t)n * p.hqk + hb - p.hqk) * D;
+  else dst = static_cast<QT*>(p.v) + ((size_t)n * p.hv + hb - 2 * p.hqk) * D;
+  store8(dst + 8 * cg, y);
+  // window shift: (win[1], win[2], x) per channel
+  float nw[24];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    nw[3 * e + 0] = wv[3 * e + 1];
+    nw[3 * e + 1] = wv[3 * e + 2];
+    nw[3 * e + 2] = x[e];
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    float t8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t8[e] = nw[8 * j + e];
+    store8(W3 + 8 * j, t8);
+  }
+}
+
+template <typename InT, typename QT, int D>
+hipError_t launch_decode_prepare_t(const DecPrepParams& p, int num_seqs, hipStream_t stream) {
+  constexpr int HPW = 256 / (D / 8);
+  const int groups = (2 * p.hqk + p.hv + HPW - 1) / HPW;
+  hipLaunchKernelGGL((decode_prepare_kernel<InT, QT, D>), dim3(num_seqs, groups + 1), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <typename InT, typename QT>
+hipError_t launch_decode_prepare_d(const DecPrepParams& p, int d, int num_seqs,
+                                   hipStream_t stream) {
+  switch (d) {
+    case 32: return launch_decode_prepare_t<InT, QT, 32>(p, num_seqs, stream);
+    case 64: return launch_decode_prepare_t<InT, QT, 64>(p, num_seqs, stream);
+    case 128: return launch_decode_prepare_t<InT, QT, 128>(p, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x,
@@ -303,6 +398,20 @@ hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x
   if (in_bf) return launch_prepare_d<bf16, float>(p, s.head_dim_k, stream);
   if (out_bf) return launch_prepare_d<float, bf16>(p, s.head_dim_k, stream);
   return launch_prepare_d<float, float>(p, s.head_dim_k, stream);
+}
+
+hipError_t launch_decode_prepare(const gdn_shape_t& s, const void* x, void* window,
+                                 const void* w, const void* bias, const void* a, const void* b,
+                                 const float* A_log, const float* dt_bias, float eps, void* q,
+                                 void* k, void* v, float* g, float* beta, hipStream_t stream) {
+  DecPrepParams p{x, window, w, bias, a, b, A_log, dt_bias, eps, q, k, v, g, beta,
+                  s.num_qk_heads, s.num_v_heads};
+  const bool in_bf = s.in_dtype == GDN_DTYPE_BF16, out_bf = s.qkv_dtype == GDN_DTYPE_BF16;
+  const int d = s.head_dim_k;
+  if (in_bf && out_bf) return launch_decode_prepare_d<bf16, bf16>(p, d, s.num_seqs, stream);
+  if (in_bf) return launch_decode_prepare_d<bf16, float>(p, d, s.num_seqs, stream);
+  if (out_bf) return launch_decode_prepare_d<float, bf16>(p, d, s.num_seqs, stream);
+  return launch_decode_prepare_d<float, float>(p, d, s.num_seqs, stream);
 }
 
 }  // namespace gdn

@@ -147,6 +147,47 @@ gdn_status_t gdn_recurrent_step(const gdn_shape_t* shape, const void* q, const v
                                 const void* v, const float* g, const float* beta,
                                 float* state, void* o, void* stream);
 
+/*
+ * gdn_decode_prepare -- front end of one decode token per sequence with a cached convolution
+ * window ([xiwon notes] "Cache": the conv state keeps the last inputs of each channel;
+ * [MoE report] §3.3 stage 2, decode path). Per channel c of sequence n, with the window
+ * win = conv_window[n][c][0..2] holding the three previous mixed_qkv values, oldest first
+ * (zeros at a sequence start),
+ *   y = bias[c] + w[c][0] win[0] + w[c][1] win[1] + w[c][2] win[2] + w[c][3] x[n][c],
+ * then SiLU, the q | k | v split, the q / k L2 norm and the gates exactly as gdn_prepare does
+ * for the same token; the window then becomes (win[1], win[2], x[n][c]) in place. Requires
+ * total_tokens == num_seqs (one token each).
+ *   mixed_qkv   [N][conv_dim]              in_dtype
+ *   conv_window [N][conv_dim][3]           in_dtype, read and overwritten
+ *   conv_weight [conv_dim][4], conv_bias [conv_dim] or NULL   in_dtype
+ *   a, b        [N][H_v] in_dtype           A_log, dt_bias [H_v] fp32
+ *   q, k (out)  [N][H_qk][d_k] qkv_dtype   v (out) [N][H_v][d_v] qkv_dtype
+ *   g, beta (out) [N][H_v] fp32
+ * mixed_qkv, conv_window, conv_weight, q, k and v must be 16-byte aligned
+ * (GDN_ERR_INVALID_ARGUMENT otherwise). Followed by gdn_recurrent_step on the same stream this
+ * is a whole decode step from projected inputs.
+ */
+gdn_status_t gdn_decode_prepare(const gdn_shape_t* shape, const void* mixed_qkv,
+                                void* conv_window, const void* conv_weight,
+                                const void* conv_bias, const void* a, const void* b,
+                                const float* A_log, const float* dt_bias, float l2norm_eps,
+                                void* q, void* k, void* v, float* g, float* beta, void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- output gate of the layer ([xiwon notes] "Qwen3_5MoeGatedDeltaNet",
+ * output stage; [MoE report] §3.3 stage 4): per V-head vector of d_v values,
+ *   out_j = o_j / sqrt(mean_j o^2 + eps) * factor_j * z_j * sigmoid(z_j),
+ *   factor_j = weight[j] + weight_offset, or 1 when weight is NULL
+ * ([MoE report] §7.5 gives the model's RMSNorm weight the (1 + w) form, i.e. weight_offset 1;
+ * the gated norm's form is not stated, so it is a parameter).
+ *   o   [T][H_v][d_v] out_dtype (the core output)    z [T][H_v][d_v] in_dtype
+ *   weight [d_v] fp32 or NULL                        out [T][H_v][d_v] out_dtype (may equal o)
+ * o, z and out must be 16-byte aligned; eps >= 0.
+ */
+gdn_status_t gdn_gated_rmsnorm(const gdn_shape_t* shape, const void* o, const void* z,
+                               const float* weight, float weight_offset, float eps, void* out,
+                               void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* gdn_status_string(gdn_status_t status);
 

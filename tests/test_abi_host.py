@@ -145,6 +145,49 @@ def test_prepare_validation(lib):
     assert call(_shape(head_dim_k=16, head_dim_v=16), good, 1e-6, outs) == UNSUPPORTED
 
 
+def test_decode_prepare_validation(lib):
+    # one token per sequence
+    s = _shape(num_seqs=4, total_tokens=4)
+    ins = [FAKE] * 8  # x, window, w, bias, a, b, A_log, dt_bias
+    outs = [FAKE] * 5  # q, k, v, g, beta
+
+    def call(shape, ins, eps, outs):
+        return lib.gdn_decode_prepare(ctypes.byref(shape), *ins, eps, *outs, None)
+
+    assert call(_shape(num_seqs=4, total_tokens=5), ins, 1e-6, outs) == INVALID
+    assert call(s, ins, -1.0, outs) == INVALID
+    for i in (0, 1, 2, 4, 5, 6, 7):  # every input except the optional bias
+        bad = list(ins)
+        bad[i] = None
+        assert call(s, bad, 1e-6, outs) == INVALID
+    for i in range(5):
+        o = list(outs)
+        o[i] = None
+        assert call(s, ins, 1e-6, o) == INVALID
+    for i in (0, 1, 2):  # x, window, taps must be 16-byte aligned
+        bad = list(ins)
+        bad[i] = ctypes.c_void_p((1 << 20) + 8)
+        assert call(s, bad, 1e-6, outs) == INVALID
+    assert call(_shape(num_seqs=4, total_tokens=4, head_dim_k=16, head_dim_v=16), ins, 1e-6,
+                outs) == UNSUPPORTED
+
+
+def test_gated_rmsnorm_validation(lib):
+    s = _shape()
+
+    def call(shape, o=FAKE, z=FAKE, w=None, off=0.0, eps=1e-6, out=FAKE):
+        return lib.gdn_gated_rmsnorm(ctypes.byref(shape), o, z, w, off, eps, out, None)
+
+    assert call(s, o=None) == INVALID
+    assert call(s, z=None) == INVALID
+    assert call(s, out=None) == INVALID
+    assert call(s, eps=-1.0) == INVALID
+    assert call(s, off=float("nan")) == INVALID
+    assert call(s, z=ctypes.c_void_p((1 << 20) + 4)) == INVALID
+    assert call(_shape(in_dtype=9)) == INVALID
+    assert call(_shape(head_dim_k=48, head_dim_v=48)) == UNSUPPORTED
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
 
