@@ -69,9 +69,10 @@ gdn_status_t gdn_prepare(const gdn_shape_t* s, const int32_t* cu, const void* x,
   if (!cu || !A_log || !dt_bias) return GDN_ERR_INVALID_ARGUMENT;
   if (s->total_tokens > 0 && (!x || !w || !a || !b || !q || !k || !v || !g || !beta))
     return GDN_ERR_INVALID_ARGUMENT;
-  // 16-byte vector access of mixed_qkv / q / k / v rows and of the gate arrays.
+  // 16-byte vector access of mixed_qkv / q / k / v rows, the conv bias and the gate arrays.
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
-      !aligned(a, 16) || !aligned(b, 16) || !aligned(g, 16) || !aligned(beta, 16))
+      !aligned(a, 16) || !aligned(b, 16) || !aligned(g, 16) || !aligned(beta, 16) ||
+      !aligned(bias, 16))
     return GDN_ERR_INVALID_ARGUMENT;
   return from_hip(gdn::launch_prepare(*s, cu, x, w, bias, a, b, A_log, dt_bias, eps, q, k, v, g,
                                       beta, static_cast<hipStream_t>(stream)));
@@ -144,9 +145,10 @@ gdn_status_t gdn_decode_prepare(const gdn_shape_t* s, const void* x, void* win, 
   if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARGUMENT;
   if (!x || !win || !w || !a || !b || !A_log || !dt_bias || !q || !k || !v || !g || !beta)
     return GDN_ERR_INVALID_ARGUMENT;
-  // 16-byte vector access of the input row, the window, the taps and the q / k / v rows.
+  // 16-byte vector access of the input row, the window, the taps, the bias and the q / k / v
+  // rows.
   if (!aligned(x, 16) || !aligned(win, 16) || !aligned(w, 16) || !aligned(q, 16) ||
-      !aligned(k, 16) || !aligned(v, 16))
+      !aligned(k, 16) || !aligned(v, 16) || !aligned(bias, 16))
     return GDN_ERR_INVALID_ARGUMENT;
   return from_hip(gdn::launch_decode_prepare(*s, x, win, w, bias, a, b, A_log, dt_bias, eps, q, k,
                                              v, g, beta, static_cast<hipStream_t>(stream)));
@@ -160,7 +162,8 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_shape_t* s, const void* o, const void* 
   if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
   if (!(eps >= 0.f) || !(weight_offset == weight_offset)) return GDN_ERR_INVALID_ARGUMENT;
   if (s->total_tokens > 0 && (!o || !z || !out)) return GDN_ERR_INVALID_ARGUMENT;
-  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(out, 16)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(weight, 16))
+    return GDN_ERR_INVALID_ARGUMENT;
   return from_hip(gdn::launch_gated_rmsnorm(*s, o, z, weight, weight_offset, eps, out,
                                             static_cast<hipStream_t>(stream)));
 }

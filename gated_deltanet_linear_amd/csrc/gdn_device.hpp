@@ -238,6 +238,10 @@ template <>
 struct Raw8<bf16> {
   bf16x8 r;
   __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const bf16x8*>(p); }
+  // streaming read (data used once): nontemporal hint
+  __device__ __forceinline__ void load_nt(const bf16* p) {
+    r = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+  }
   __device__ __forceinline__ void to(float (&x)[8]) const {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
@@ -249,6 +253,10 @@ struct Raw8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = *reinterpret_cast<const f32x4*>(p);
     b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
   }
   __device__ __forceinline__ void to(float (&x)[8]) const {
 #pragma unroll
@@ -278,6 +286,28 @@ __device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
   }
   *reinterpret_cast<f32x4*>(p) = a;
   *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
+// Streaming write (not read again by this kernel): nontemporal hint.
+template <typename T>
+__device__ __forceinline__ void store8_nt(T* p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8_nt<bf16>(bf16* p, const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[e];
+  __builtin_nontemporal_store(r, reinterpret_cast<bf16x8*>(p));
+}
+template <>
+__device__ __forceinline__ void store8_nt<float>(float* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = x[e];
+    b[e] = x[4 + e];
+  }
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
 }
 
 // Barrier for LDS traffic only: waits for this wave's own LDS reads and writes (lgkmcnt) and

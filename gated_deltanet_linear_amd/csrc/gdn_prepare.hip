@@ -20,6 +20,21 @@
 namespace gdn {
 namespace {
 
+// Conv bias of channels c .. c+7, zeros without a bias. One unconditional 16-byte load (from
+// `fallback`, any readable 16-byte-aligned address, when there is no bias) and a select on the
+// values: a per-element conditional load compiles to eight dependent loads, and a branch around
+// the load makes the compiler wait for every load in flight where the branches join.
+template <typename InT>
+__device__ __forceinline__ void load_bias8(const InT* bias, const InT* fallback, int c,
+                                           float (&out)[8]) {
+  Raw8<InT> r;
+  r.load(bias ? bias + c : fallback);
+  r.to(out);
+  const bool has = bias != nullptr;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = has ? out[e] : 0.f;
+}
+
 constexpr int kTokBlock = 128;
 
 // Largest n in [0, num_seqs) with cu[n] <= t (the sequence holding token t < cu[num_seqs]).
@@ -149,17 +164,6 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
   const InT* X = static_cast<const InT*>(p.x) + c;
   dst += 8 * cg;
 
-  float w[8][4], bias[8];
-  {
-    const InT* W = static_cast<const InT*>(p.w) + (size_t)c * 4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[e][j] = to_f32(W[e * 4 + j]);
-      bias[e] = p.bias ? to_f32(static_cast<const InT*>(p.bias)[c + e]) : 0.f;
-    }
-  }
-
   const int t_first = tok0 + tl * TPT;
   if (t_first >= p.T) return;  // whole token group idle (its CGN lanes leave together)
 
@@ -171,8 +175,28 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
   for (int j = 0; j < 3; ++j) hist[j].load(X + (size_t)max(t_first - 3 + j, 0) * conv_dim);
 #pragma unroll
   for (int j = 0; j < TPT; ++j) rows[j].load(X + (size_t)min(t_first + j, p.T - 1) * conv_dim);
-  int n = token_to_seq(p.cu, p.num_seqs, t_first);
+  // Taps and bias after the rows, so that waiting for them does not hold back the row loads.
+  float w[8][4], bias[8];
+  {
+    const InT* W = static_cast<const InT*>(p.w) + (size_t)c * 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[e][j] = to_f32(W[e * 4 + j]);
+    }
+    load_bias8(static_cast<const InT*>(p.bias), W, c, bias);
+  }
+  // The lookup is done for the block's first token: a uniform search runs on scalar loads,
+  // which are counted apart from the row loads in flight (a per-lane search would wait for all
+  // of them before each step). Lanes whose run starts in a later sequence step forward; only
+  // blocks that hold a sequence start take that loop.
+  int n = token_to_seq(p.cu, p.num_seqs, tok0);
   int seq_start = p.cu[n], seq_end = p.cu[n + 1];
+  while (t_first >= seq_end) {
+    ++n;
+    seq_start = seq_end;
+    seq_end = p.cu[n + 1];
+  }
   float xm3[8], xm2[8], xm1[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) xm3[e] = xm2[e] = xm1[e] = 0.f;
@@ -267,8 +291,12 @@ struct DecPrepParams {
   int hqk, hv;
 };
 
+// At most 6 waves per SIMD: the 256-thread launch of 256 sequences fits in one round at that
+// occupancy, and the register room lets all nine loads of a thread be issued before the first
+// use (a tighter register target makes the compiler issue them one use at a time).
 template <typename InT, typename QT, int D>
-__global__ __launch_bounds__(256) void decode_prepare_kernel(DecPrepParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 6))) void
+decode_prepare_kernel(DecPrepParams p) {
   constexpr int CGN = D / 8;      // threads per channel head
   constexpr int HPW = 256 / CGN;  // channel heads per workgroup
   const int n = blockIdx.x, tid = threadIdx.x;
@@ -298,9 +326,9 @@ __global__ __launch_bounds__(256) void decode_prepare_kernel(DecPrepParams p) {
   InT* W3 = static_cast<InT*>(p.win) + ((size_t)n * conv_dim + c) * 3;
   const InT* Wt = static_cast<const InT*>(p.w) + (size_t)c * 4;
   Raw8<InT> rx, rw3[3], rt[4];
-  rx.load(X);
+  rx.load_nt(X);  // x and the window are touched once: nontemporal
 #pragma unroll
-  for (int j = 0; j < 3; ++j) rw3[j].load(W3 + 8 * j);
+  for (int j = 0; j < 3; ++j) rw3[j].load_nt(W3 + 8 * j);
 #pragma unroll
   for (int j = 0; j < 4; ++j) rt[j].load(Wt + 8 * j);
   float x[8], wv[24], taps[32], bias[8];
@@ -319,8 +347,7 @@ __global__ __launch_bounds__(256) void decode_prepare_kernel(DecPrepParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) taps[8 * j + e] = t8[e];
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) bias[e] = p.bias ? to_f32(static_cast<const InT*>(p.bias)[c + e]) : 0.f;
+  load_bias8(static_cast<const InT*>(p.bias), Wt, c, bias);
 
   // channel e: window wv[3e .. 3e+2] (oldest first), taps taps[4e .. 4e+3]
   float y[8], ss = 0.f;
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(256) void decode_prepare_kernel(DecPrepParams p) {
     float t8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) t8[e] = nw[8 * j + e];
-    store8(W3 + 8 * j, t8);
+    store8_nt(W3 + 8 * j, t8);
   }
 }
 

@@ -83,8 +83,8 @@ typedef struct gdn_shape {
  *   q, k (out)  [T][H_qk][d_k]             qkv_dtype
  *   v    (out)  [T][H_v][d_v]              qkv_dtype
  *   g, beta (out) [T][H_v]                 fp32 (g is the log-decay, <= 0)
- * mixed_qkv, a, b, q, k, v, g and beta must be 16-byte aligned (16-byte vector accesses);
- * GDN_ERR_INVALID_ARGUMENT otherwise.
+ * mixed_qkv, conv_bias (when given), a, b, q, k, v, g and beta must be 16-byte aligned
+ * (16-byte vector accesses); GDN_ERR_INVALID_ARGUMENT otherwise.
  */
 gdn_status_t gdn_prepare(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                          const void* mixed_qkv, const void* conv_weight, const void* conv_bias,
@@ -163,8 +163,8 @@ gdn_status_t gdn_recurrent_step(const gdn_shape_t* shape, const void* q, const v
  *   a, b        [N][H_v] in_dtype           A_log, dt_bias [H_v] fp32
  *   q, k (out)  [N][H_qk][d_k] qkv_dtype   v (out) [N][H_v][d_v] qkv_dtype
  *   g, beta (out) [N][H_v] fp32
- * mixed_qkv, conv_window, conv_weight, q, k and v must be 16-byte aligned
- * (GDN_ERR_INVALID_ARGUMENT otherwise). Followed by gdn_recurrent_step on the same stream this
+ * mixed_qkv, conv_window, conv_weight, conv_bias (when given), q, k and v must be 16-byte
+ * aligned (GDN_ERR_INVALID_ARGUMENT otherwise). Followed by gdn_recurrent_step on the same stream this
  * is a whole decode step from projected inputs.
  */
 gdn_status_t gdn_decode_prepare(const gdn_shape_t* shape, const void* mixed_qkv,
@@ -182,7 +182,7 @@ gdn_status_t gdn_decode_prepare(const gdn_shape_t* shape, const void* mixed_qkv,
  * the gated norm's form is not stated, so it is a parameter).
  *   o   [T][H_v][d_v] out_dtype (the core output)    z [T][H_v][d_v] in_dtype
  *   weight [d_v] fp32 or NULL                        out [T][H_v][d_v] out_dtype (may equal o)
- * o, z and out must be 16-byte aligned; eps >= 0.
+ * o, z, out and weight (when given) must be 16-byte aligned; eps >= 0.
  */
 gdn_status_t gdn_gated_rmsnorm(const gdn_shape_t* shape, const void* o, const void* z,
                                const float* weight, float weight_offset, float eps, void* out,

@@ -131,9 +131,10 @@ def test_prepare_validation(lib):
         o = list(outs)
         o[i] = None
         assert call(s, good, 1e-6, o) == INVALID
-    ins = list(good)
-    ins[1] = ctypes.c_void_p((1 << 20) + 8)  # mixed_qkv must be 16-byte aligned
-    assert call(s, ins, 1e-6, outs) == INVALID
+    for i in (1, 3):  # mixed_qkv and the conv bias must be 16-byte aligned
+        ins = list(good)
+        ins[i] = ctypes.c_void_p((1 << 20) + 8)
+        assert call(s, ins, 1e-6, outs) == INVALID
     for i in (4, 5):  # a, b
         ins = list(good)
         ins[i] = ctypes.c_void_p((1 << 20) + 4)
@@ -164,7 +165,7 @@ def test_decode_prepare_validation(lib):
         o = list(outs)
         o[i] = None
         assert call(s, ins, 1e-6, o) == INVALID
-    for i in (0, 1, 2):  # x, window, taps must be 16-byte aligned
+    for i in (0, 1, 2, 3):  # x, window, taps, bias must be 16-byte aligned
         bad = list(ins)
         bad[i] = ctypes.c_void_p((1 << 20) + 8)
         assert call(s, bad, 1e-6, outs) == INVALID
@@ -184,6 +185,8 @@ def test_gated_rmsnorm_validation(lib):
     assert call(s, eps=-1.0) == INVALID
     assert call(s, off=float("nan")) == INVALID
     assert call(s, z=ctypes.c_void_p((1 << 20) + 4)) == INVALID
+    assert call(s, w=ctypes.cast(ctypes.c_void_p((1 << 20) + 8), ctypes.POINTER(ctypes.c_float))) \
+        == INVALID
     assert call(_shape(in_dtype=9)) == INVALID
     assert call(_shape(head_dim_k=48, head_dim_v=48)) == UNSUPPORTED
 
