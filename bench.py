@@ -6,7 +6,8 @@ Prints ONE JSON line. The headline ``value`` is prefill tokens/s of the 35B-A3B-
 layer (1 x 4096 tokens, 16 QK / 32 V heads, d = 128, bf16 q/k/v): one step is one
 gdn_chunk_forward (its two kernels, gdn_chunk_intra then gdn_chunk_scan) over inputs already
 resident in HBM. The same line carries decode tokens/s (256 sequences x 1 token, 537 MB fp32
-state updated in place), the long-context and packed front-end workloads, per-kernel HIP-event
+state updated in place), the long-context and packed front-end workloads, the output gate (1 x 4096 shape), a decode
+step from projected inputs (front end + recurrent step, 256 sequences), per-kernel HIP-event
 timings, the roofline of each workload's dominant kernel and the float64 CPU oracle timed on
 a bounded sample on this host.
 
@@ -16,6 +17,9 @@ Roofline conventions (algorithmic work, not what the kernels happen to issue):
     and the masked intra-chunk product); peak = 2500 TFLOP/s dense bf16 MFMA.
   decode bytes = 2 N H_v d_k d_v 4 + N [H_qk 2 d_k e + H_v (2 d_v e + 8)];  peak 8000 GB/s.
   front-end bytes = T [2 conv_dim e + 2 H_v e + 8 H_v] (+ q/k/v written at their dtype).
+  output-gate bytes = 3 T H_v d_v e + 4 d_v   (o and z read, out written, fp32 weight).
+  decode front-end bytes = N [8 conv_dim e + H_v (2 e + 8)] + 4 conv_dim e   (x, window read
+    and rewritten, q/k/v written; a, b in, g, beta out; taps once).
 """
 
 from __future__ import annotations
@@ -42,7 +46,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="run one workload: prefill, decode, long, front")
+                    help="run one workload: prefill, decode, long, front, gate, decode_front")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the known-size kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -80,24 +84,61 @@ def _traffic(kernel_key):
     return rec.get("hbm_bytes_per_launch")
 
 
-class Timer:
-    """HIP events recorded on the stream the kernels are launched on (torch's current
-    stream; the library launches on it)."""
+def _measure(torch, kernels, steps, warmup):
+    """Time one leg. ``kernels`` lists (name, launch) in step order; a step launches each once.
 
-    def __init__(self, torch, names, steps):
-        self.torch = torch
-        self.names = names
-        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-                   for _ in range(steps)]
+    Step time: W untimed steps, then K steps between two HIP events on the launch stream
+    (torch's current stream; the library launches on it), bracketed by synchronizes.
+    Per-kernel average launch duration: for each kernel, K launches back to back between two
+    HIP events on the same stream, divided by K. A spin kernel placed before the first event
+    keeps the GPU busy until the host has queued all K launches, so that the host's own call
+    overhead (which exceeds the run time of the smaller kernels) is not timed. (An event pair
+    around every single launch would add the dispatch latency of the event markers, several
+    microseconds, to each launch.) The kernels' inputs stay valid across repeated launches;
+    in-place state is updated each time."""
+    stream = torch.cuda.current_stream()
 
-    def mark(self, step, i):
-        self.ev[step][i].record(self.torch.cuda.current_stream())
+    def step():
+        for _, fn in kernels:
+            fn()
 
-    def per_kernel_ms(self):
-        out = {}
-        for i, nm in enumerate(self.names):
-            out[nm] = sum(e[i].elapsed_time(e[i + 1]) for e in self.ev) / len(self.ev)
-        return out
+    for _ in range(warmup):
+        step()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = a.elapsed_time(b) / steps
+    # cycles of the spin kernel per millisecond
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(1_000_000)
+    b.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    kms = {}
+    for name, fn in kernels:
+        # host time to queue K launches (queuing does not wait for the GPU), then a hold just
+        # longer than that: a long idle hold lets the clocks drop before the timed launches
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        queue_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(cycles_per_ms * (1.5 * queue_ms + 0.05)))
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        kms[name] = a.elapsed_time(b) / steps
+    return step_ms, wall_ms, kms
 
 
 def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
@@ -113,34 +154,21 @@ def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
     ht = torch.empty((n, hv, dk, dv), dtype=torch.float32, device=dev)
     h0 = d["h0"] if with_h0 else None
 
-    def step(tm=None, i=0):
-        if tm:
-            tm.mark(i, 0)
-        gdn.chunk_intra(d["q"], d["k"], d["g"], d["beta"], d["cu_seqlens"], hv, ws)
-        if tm:
-            tm.mark(i, 1)
-        gdn.chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ws,
-                       initial_state=h0, o=o, final_state=ht)
-        if tm:
-            tm.mark(i, 2)
-
-    for _ in range(warmup):
-        step()
-    tm = Timer(torch, ["gdn_chunk_intra", "gdn_chunk_scan"], steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(tm, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kms = tm.per_kernel_ms()
+    kernels = [
+        ("gdn_chunk_intra",
+         lambda: gdn.chunk_intra(d["q"], d["k"], d["g"], d["beta"], d["cu_seqlens"], hv, ws)),
+        ("gdn_chunk_scan",
+         lambda: gdn.chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ws,
+                                initial_state=h0, o=o, final_state=ht)),
+    ]
+    ev_ms, ms, kms = _measure(torch, kernels, steps, warmup)
     lengths = case.meta["lengths"]
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
     B = prefill_bytes(lengths, hqk, hv, dk, dv, 2, with_h0)
-    ms = wall * 1e3 / steps
     scan_ms = kms["gdn_chunk_scan"]
-    return dict(case=case, T=T, ms_per_step=ms, tokens_per_s=T / (ms / 1e3), kernels_ms=kms,
+    return dict(case=case, T=T, ms_per_step=ms, step_ms_events=ev_ms,
+                tokens_per_s=T / (ms / 1e3), kernels_ms=kms,
                 path_tflops=F / (ms / 1e3) / 1e12, path_mfma_frac=F / (ms / 1e3) / 1e12 /
                 PEAK_BF16_TFLOPS, path_hbm_gbs=B / (ms / 1e3) / 1e9,
                 roofline=dict(kernel="gdn_chunk_scan", bound="mfma",
@@ -161,27 +189,14 @@ def run_decode(torch, gdn, si, steps, warmup):
     N, hqk, dk = case.q.shape
     hv, dv = case.v.shape[1], case.v.shape[2]
 
-    def step(tm=None, i=0):
-        if tm:
-            tm.mark(i, 0)
-        gdn.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=o)
-        if tm:
-            tm.mark(i, 1)
-
-    for _ in range(warmup):
-        step()
-    tm = Timer(torch, ["gdn_recurrent_step"], steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(tm, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kms = tm.per_kernel_ms()
+    kernels = [("gdn_recurrent_step",
+                lambda: gdn.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state,
+                                           o=o))]
+    ev_ms, ms, kms = _measure(torch, kernels, steps, warmup)
     B = 2 * N * hv * dk * dv * 4 + N * (hqk * 2 * dk * 2 + hv * (2 * dv * 2 + 8))
     kt = kms["gdn_recurrent_step"] / 1e3
-    ms = wall * 1e3 / steps
-    return dict(ms_per_step=ms, tokens_per_s=N / (ms / 1e3), kernels_ms=kms,
+    return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=N / (ms / 1e3),
+                kernels_ms=kms,
                 roofline=dict(kernel="gdn_recurrent_step", bound="hbm",
                               achieved=round(B / kt / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(B / kt / 1e9 / PEAK_HBM_GBS, 4),
@@ -202,44 +217,94 @@ def run_front(torch, gdn, si, steps, warmup):
     o = torch.empty((T, hv, dv), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((n, hv, dk, dv), dtype=torch.float32, device=dev)
 
-    def step(tm=None, i=0):
-        if tm:
-            tm.mark(i, 0)
-        q, k, v, g, beta = gdn.prepare(x, w, a, b, A_log, dt_bias, cu, hqk, dk, hv, dv)
-        if tm:
-            tm.mark(i, 1)
-        gdn.chunk_intra(q, k, g, beta, cu, hv, ws)
-        if tm:
-            tm.mark(i, 2)
-        gdn.chunk_scan(q, k, v, g, beta, cu, ws, initial_state=h0, o=o, final_state=ht)
-        if tm:
-            tm.mark(i, 3)
+    qkv = {}
 
-    for _ in range(warmup):
-        step()
-    tm = Timer(torch, ["gdn_prepare", "gdn_chunk_intra", "gdn_chunk_scan"], steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(tm, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kms = tm.per_kernel_ms()
+    def prep():
+        qkv["t"] = gdn.prepare(x, w, a, b, A_log, dt_bias, cu, hqk, dk, hv, dv)
+
+    def intra():
+        q, k, v, g, beta = qkv["t"]
+        gdn.chunk_intra(q, k, g, beta, cu, hv, ws)
+
+    def scan():
+        q, k, v, g, beta = qkv["t"]
+        gdn.chunk_scan(q, k, v, g, beta, cu, ws, initial_state=h0, o=o, final_state=ht)
+
+    ev_ms, ms, kms = _measure(
+        torch, [("gdn_prepare", prep), ("gdn_chunk_intra", intra), ("gdn_chunk_scan", scan)],
+        steps, warmup)
     conv_dim = 2 * hqk * dk + hv * dv
     Bprep = T * (2 * conv_dim * 2 + 2 * hv * 2 + 8 * hv)
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
-    ms = wall * 1e3 / steps
-    return dict(T=T, lengths=m["lengths"], ms_per_step=ms, tokens_per_s=T / (ms / 1e3),
+    return dict(T=T, lengths=m["lengths"], ms_per_step=ms, step_ms_events=ev_ms,
+                tokens_per_s=T / (ms / 1e3),
                 kernels_ms=kms, path_tflops=F / (ms / 1e3) / 1e12,
-                prepare=dict(bound="hbm", achieved=round(Bprep / (kms["gdn_prepare"] / 1e3) / 1e9, 1),
-                             peak=PEAK_HBM_GBS, unit="GB/s",
-                             frac=round(Bprep / (kms["gdn_prepare"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)),
+                prepare=_hbm("gdn_prepare", Bprep, kms["gdn_prepare"],
+                             "gdn_prepare_prefill_397b_packed_8xU512_8192"),
                 roofline=dict(kernel="gdn_chunk_scan", bound="mfma",
                               achieved=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12, 3),
                               peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                               frac=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12 /
                                          PEAK_BF16_TFLOPS, 5)))
+
+
+def _hbm(kernel, nbytes, ms, traffic_key=None):
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return dict(kernel=kernel, bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS,
+                unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                traffic=_traffic(traffic_key) if traffic_key else None,
+                algorithmic_bytes_per_launch=nbytes)
+
+
+def run_gate(torch, gdn, si, steps, warmup):
+    """Output gate over the 1 x 4096 prefill shape (4096 tokens x 32 V heads x 128, bf16)."""
+    gc = si.make_gate_case(4096, 32, 128, seed=1006, meta=dict(workload="output_gate_1x4096"))
+    o, z, w = gc.o.cuda(), gc.z.cuda(), gc.weight.cuda()
+    out = torch.empty_like(o)
+    T, hv, dv = o.shape
+
+    ev_ms, ms, kms = _measure(
+        torch, [("gdn_gated_rmsnorm", lambda: gdn.gated_rmsnorm(o, z, w, 1.0, 1e-6, out=out))],
+        steps, warmup)
+    B = T * hv * dv * 2 * 3 + dv * 4
+    return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=T / (ms / 1e3),
+                kernels_ms=kms, roofline=_hbm("gdn_gated_rmsnorm", B, kms["gdn_gated_rmsnorm"],
+                              "gdn_gated_rmsnorm_output_gate_1x4096"))
+
+
+def run_decode_front(torch, gdn, si, steps, warmup):
+    """One decode token for 256 sequences from projected inputs: gdn_decode_prepare then
+    gdn_recurrent_step (35B-A3B layer shape, bf16 inputs, fp32 state updated in place)."""
+    dc = si.make_decode_front_case(256, 16, 32, 128, 128, seed=1007,
+                                   meta=dict(workload="decode_front_256x1"))
+    dev = "cuda"
+    x, win, w, a, b = (t.to(dev) for t in (dc.mixed_qkv, dc.window, dc.conv_weight, dc.a, dc.b))
+    A_log, dt_bias, state = dc.A_log.to(dev), dc.dt_bias.to(dev), dc.h0.to(dev)
+    m = dc.meta
+    N, hqk, hv, dk, dv = m["N"], m["hqk"], m["hv"], m["dk"], m["dv"]
+    o = torch.empty((N, hv, dv), dtype=torch.bfloat16, device=dev)
+
+    qkv = {}
+
+    def prep():
+        qkv["t"] = gdn.decode_prepare(x, win, w, a, b, A_log, dt_bias, hqk, dk, hv, dv)
+
+    def rstep():
+        q, k, v, g, beta = qkv["t"]
+        gdn.recurrent_step(q, k, v, g, beta, state, o=o)
+
+    ev_ms, ms, kms = _measure(
+        torch, [("gdn_decode_prepare", prep), ("gdn_recurrent_step", rstep)], steps, warmup)
+    conv_dim = 2 * hqk * dk + hv * dv
+    Bprep = N * (conv_dim * 2 * (1 + 3 + 3 + 1) + hv * (2 * 2 + 8)) + conv_dim * 4 * 2
+    Bstep = 2 * N * hv * dk * dv * 4 + N * (hqk * 2 * dk * 2 + hv * (2 * dv * 2 + 8))
+    return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=N / (ms / 1e3),
+                kernels_ms=kms,
+                decode_prepare=_hbm("gdn_decode_prepare", Bprep, kms["gdn_decode_prepare"],
+                                    "gdn_decode_prepare_decode_front_256x1"),
+                roofline=_hbm("gdn_recurrent_step", Bstep, kms["gdn_recurrent_step"],
+                              "gdn_recurrent_step_decode_256x1"))
 
 
 def cpu_baseline(case, budget_s=20.0, min_s=3.0):
@@ -323,6 +388,10 @@ def main():
         out["long_context_4x32768"] = lg
     if only in (None, "front"):
         out["front_end_packed_8_seqs"] = run_front(torch, gdn, si, max(3, args.steps // 5), 2)
+    if only in (None, "gate"):
+        out["output_gate_1x4096"] = run_gate(torch, gdn, si, args.steps, args.warmup)
+    if only in (None, "decode_front"):
+        out["decode_front_256x1"] = run_decode_front(torch, gdn, si, args.steps, args.warmup)
 
     line = {"metric": "GDN prefill tokens/s (1 MI355X; decode tokens/s alongside)",
             "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -169,6 +169,63 @@ def make_front_case(lengths, hqk, hv, dk, dv, dtype="bf16", h0_std=0.02, conv_w_
                                lengths=lengths))
 
 
+@dataclass
+class GateCase:
+    """Inputs of the output gate (CPU tensors)."""
+
+    o: torch.Tensor        # [T, Hv, dv] dtype (stands in for the core output)
+    z: torch.Tensor        # [T, Hv, dv] dtype (gate projection)
+    weight: torch.Tensor   # [dv] float32
+    meta: dict = field(default_factory=dict)
+
+
+def make_gate_case(T, hv, dv, dtype="bf16", seed=0, meta=None) -> GateCase:
+    """Draw order: o ~ N(0, 1), z ~ N(0, 1), weight ~ N(0, 0.1) (used with offset 1)."""
+    rng = np.random.default_rng(seed)
+    td = torch_dtype(dtype)
+    o = _normal(rng, (T, hv, dv))
+    z = _normal(rng, (T, hv, dv))
+    w = _normal(rng, (dv,), std=0.1)
+    return GateCase(o=_round(o, td), z=_round(z, td), weight=_round(w, torch.float32),
+                    meta=dict(meta or {}, dtype=dtype, T=T, hv=hv, dv=dv))
+
+
+@dataclass
+class DecodeFrontCase:
+    """Inputs of one decode token per sequence from projected inputs (CPU tensors)."""
+
+    mixed_qkv: torch.Tensor    # [N, conv_dim] dtype
+    window: torch.Tensor       # [N, conv_dim, 3] dtype, oldest first
+    conv_weight: torch.Tensor  # [conv_dim, 4] dtype
+    a: torch.Tensor            # [N, Hv] dtype
+    b: torch.Tensor            # [N, Hv] dtype
+    A_log: torch.Tensor        # [Hv] float32
+    dt_bias: torch.Tensor      # [Hv] float32
+    h0: torch.Tensor           # [N, Hv, dk, dv] float32
+    meta: dict = field(default_factory=dict)
+
+
+def make_decode_front_case(N, hqk, hv, dk, dv, dtype="bf16", h0_std=0.02, conv_w_std=0.5,
+                           seed=0, meta=None) -> DecodeFrontCase:
+    """Draw order: mixed_qkv, window, conv weight, a, b, A_log, dt_bias, state."""
+    rng = np.random.default_rng(seed)
+    td = torch_dtype(dtype)
+    conv_dim = 2 * hqk * dk + hv * dv
+    x = _normal(rng, (N, conv_dim))
+    win = _normal(rng, (N, conv_dim, 3))
+    w = _normal(rng, (conv_dim, 4), std=conv_w_std)
+    a = _normal(rng, (N, hv))
+    b = _normal(rng, (N, hv))
+    A_log = rng.uniform(0.0, 2.7, size=hv)
+    dt_bias = rng.normal(0.0, 0.1, size=hv)
+    h0 = _round(_normal(rng, (N, hv, dk, dv), std=h0_std), torch.float32)
+    return DecodeFrontCase(mixed_qkv=_round(x, td), window=_round(win, td),
+                           conv_weight=_round(w, td), a=_round(a, td), b=_round(b, td),
+                           A_log=_round(A_log, torch.float32),
+                           dt_bias=_round(dt_bias, torch.float32), h0=h0,
+                           meta=dict(meta or {}, dtype=dtype, N=N, hqk=hqk, hv=hv, dk=dk, dv=dv))
+
+
 def workload_lengths(cfg_id: int, seed: Optional[int] = None):
     w = WORKLOADS[cfg_id]
     if "seqlen" in w:
