@@ -7,7 +7,7 @@ layer (1 x 4096 tokens, 16 QK / 32 V heads, d = 128, bf16 q/k/v): one step is on
 gdn_chunk_forward (its two kernels, gdn_chunk_intra then gdn_chunk_scan) over inputs already
 resident in HBM. The same line carries decode tokens/s (256 sequences x 1 token, 537 MB fp32
 state updated in place), the long-context and packed front-end workloads, the output gate (1 x 4096 shape), a decode
-step from projected inputs (front end + recurrent step, 256 sequences), per-kernel HIP-event
+step from projected inputs (fused front end + recurrent step, 256 sequences), per-kernel HIP-event
 timings, the roofline of each workload's dominant kernel and the float64 CPU oracle timed on
 a bounded sample on this host.
 
@@ -20,6 +20,8 @@ Roofline conventions (algorithmic work, not what the kernels happen to issue):
   output-gate bytes = 3 T H_v d_v e + 4 d_v   (o and z read, out written, fp32 weight).
   decode front-end bytes = N [8 conv_dim e + H_v (2 e + 8)] + 4 conv_dim e   (x, window read
     and rewritten, q/k/v written; a, b in, g, beta out; taps once).
+  fused decode-step bytes = 2 N H_v d_k d_v 4 + N [7 conv_dim e + H_v (2 e + d_v e)]
+    + 4 conv_dim e   (state read and written; x, window read and rewritten; a, b; o; taps).
 """
 
 from __future__ import annotations
@@ -274,8 +276,9 @@ def run_gate(torch, gdn, si, steps, warmup):
 
 
 def run_decode_front(torch, gdn, si, steps, warmup):
-    """One decode token for 256 sequences from projected inputs: gdn_decode_prepare then
-    gdn_recurrent_step (35B-A3B layer shape, bf16 inputs, fp32 state updated in place)."""
+    """One decode token for 256 sequences from projected inputs (35B-A3B layer shape, bf16
+    inputs, fp32 state updated in place): the fused gdn_decode_step, and for comparison the
+    two-call path gdn_decode_prepare then gdn_recurrent_step."""
     dc = si.make_decode_front_case(256, 16, 32, 128, 128, seed=1007,
                                    meta=dict(workload="decode_front_256x1"))
     dev = "cuda"
@@ -284,6 +287,11 @@ def run_decode_front(torch, gdn, si, steps, warmup):
     m = dc.meta
     N, hqk, hv, dk, dv = m["N"], m["hqk"], m["hv"], m["dk"], m["dv"]
     o = torch.empty((N, hv, dv), dtype=torch.bfloat16, device=dev)
+
+    ev_ms, ms, kms = _measure(
+        torch, [("gdn_decode_step", lambda: gdn.decode_step(x, win, w, a, b, A_log, dt_bias,
+                                                            state, hqk, dk, hv, o=o))],
+        steps, warmup)
 
     qkv = {}
 
@@ -294,17 +302,25 @@ def run_decode_front(torch, gdn, si, steps, warmup):
         q, k, v, g, beta = qkv["t"]
         gdn.recurrent_step(q, k, v, g, beta, state, o=o)
 
-    ev_ms, ms, kms = _measure(
+    ev2, ms2, kms2 = _measure(
         torch, [("gdn_decode_prepare", prep), ("gdn_recurrent_step", rstep)], steps, warmup)
     conv_dim = 2 * hqk * dk + hv * dv
-    Bprep = N * (conv_dim * 2 * (1 + 3 + 3 + 1) + hv * (2 * 2 + 8)) + conv_dim * 4 * 2
-    Bstep = 2 * N * hv * dk * dv * 4 + N * (hqk * 2 * dk * 2 + hv * (2 * dv * 2 + 8))
+    e = 2
+    Bfused = (2 * N * hv * dk * dv * 4 + N * (conv_dim * e * 7 + hv * (2 * e + dv * e))
+              + conv_dim * 4 * e)
+    Bprep = N * (conv_dim * e * 8 + hv * (2 * e + 8)) + conv_dim * 4 * e
+    Bstep = 2 * N * hv * dk * dv * 4 + N * (hqk * 2 * dk * e + hv * (2 * dv * e + 8))
     return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=N / (ms / 1e3),
                 kernels_ms=kms,
-                decode_prepare=_hbm("gdn_decode_prepare", Bprep, kms["gdn_decode_prepare"],
-                                    "gdn_decode_prepare_decode_front_256x1"),
-                roofline=_hbm("gdn_recurrent_step", Bstep, kms["gdn_recurrent_step"],
-                              "gdn_recurrent_step_decode_256x1"))
+                roofline=_hbm("gdn_decode_step", Bfused, kms["gdn_decode_step"],
+                              "gdn_decode_step_decode_front_256x1"),
+                two_call=dict(ms_per_step=ms2, tokens_per_s=N / (ms2 / 1e3), kernels_ms=kms2,
+                              decode_prepare=_hbm("gdn_decode_prepare", Bprep,
+                                                  kms2["gdn_decode_prepare"],
+                                                  "gdn_decode_prepare_decode_front_256x1"),
+                              recurrent_step=_hbm("gdn_recurrent_step", Bstep,
+                                                  kms2["gdn_recurrent_step"],
+                                                  "gdn_recurrent_step_decode_256x1")))
 
 
 def cpu_baseline(case, budget_s=20.0, min_s=3.0):

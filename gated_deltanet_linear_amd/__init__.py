@@ -79,6 +79,9 @@ def _load():
     lib.gdn_decode_prepare.restype = ctypes.c_int
     lib.gdn_decode_prepare.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                        _P, _P, _P, _P]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                    _P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [sp, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -319,6 +322,48 @@ def decode_prepare(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, nu
                                     _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _stream())
     _check(rc, "gdn_decode_prepare")
     return q, k, v, g, beta
+
+
+def decode_step(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, state, num_qk_heads,
+                head_dim, num_v_heads, conv_bias=None, l2norm_eps=1e-6, scale=1.0, out_dtype=None,
+                o=None):
+    """One decode token per sequence from projected inputs, fused (front end + gated delta step).
+
+    mixed_qkv [N, conv_dim]; conv_window [N, conv_dim, 3] (updated in place); conv_weight
+    [conv_dim, 4]; a, b [N, H_v]; A_log, dt_bias [H_v] fp32; state [N, H_v, d, d] fp32 (updated in
+    place). Returns o [N, H_v, d] (out_dtype, default the input dtype).
+    """
+    _dev(mixed_qkv, "mixed_qkv")
+    dt = mixed_qkv.dtype
+    _dev(conv_window, "conv_window", dt)
+    _dev(conv_weight, "conv_weight", dt)
+    _dev(a, "a", dt)
+    _dev(b, "b", dt)
+    _dev(A_log, "A_log", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    _dev(state, "state", torch.float32)
+    if conv_bias is not None:
+        _dev(conv_bias, "conv_bias", dt)
+    N, conv_dim = mixed_qkv.shape
+    hqk, d, hv = int(num_qk_heads), int(head_dim), int(num_v_heads)
+    if conv_dim != (2 * hqk + hv) * d or conv_weight.shape != (conv_dim, 4):
+        raise GdnError("mixed_qkv must be [N, (2*H_qk + H_v)*d] and conv_weight [conv_dim, 4]")
+    if conv_window.shape != (N, conv_dim, 3):
+        raise GdnError("conv_window must be [N, conv_dim, 3]")
+    if a.shape != (N, hv) or b.shape != (N, hv) or A_log.shape != (hv,) or dt_bias.shape != (hv,):
+        raise GdnError("a, b must be [N, H_v]; A_log, dt_bias [H_v]")
+    if state.shape != (N, hv, d, d):
+        raise GdnError("state must be [N, H_v, d, d]")
+    od = out_dtype or dt
+    s = _shape(N, N, hqk, hv, d, d, torch.float32, od, in_dtype=dt, scale=scale)
+    if o is None:
+        o = torch.empty((N, hv, d), dtype=od, device=mixed_qkv.device)
+    _dev(o, "o", od)
+    rc = _load().gdn_decode_step(ctypes.byref(s), _ptr(mixed_qkv), _ptr(conv_window),
+                                 _ptr(conv_weight), _ptr(conv_bias), _ptr(a), _ptr(b), _ptr(A_log),
+                                 _ptr(dt_bias), float(l2norm_eps), _ptr(state), _ptr(o), _stream())
+    _check(rc, "gdn_decode_step")
+    return o
 
 
 def gated_rmsnorm(o, z, weight=None, weight_offset=0.0, eps=1e-6, out=None):

@@ -154,6 +154,28 @@ gdn_status_t gdn_decode_prepare(const gdn_shape_t* s, const void* x, void* win, 
                                              v, g, beta, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status_t gdn_decode_step(const gdn_shape_t* s, const void* x, void* win, const void* w,
+                             const void* bias, const void* a, const void* b, const float* A_log,
+                             const float* dt_bias, float eps, float* state, void* o,
+                             void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens != s->num_seqs) return GDN_ERR_INVALID_ARGUMENT;
+  // q, k and the G v rows of a workgroup's QK head are held in LDS: at most 64 KiB.
+  const long long G = s->num_v_heads / s->num_qk_heads;
+  if (((2 + G) * s->head_dim_v + 2 * G) * 4 > 65536) return GDN_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!x || !win || !w || !a || !b || !A_log || !dt_bias || !state || !o)
+    return GDN_ERR_INVALID_ARGUMENT;
+  // 16-byte vector access of the input row, the window, the taps, the bias and the state.
+  if (!aligned(x, 16) || !aligned(win, 16) || !aligned(w, 16) || !aligned(bias, 16) ||
+      !aligned(state, 16))
+    return GDN_ERR_INVALID_ARGUMENT;
+  return from_hip(gdn::launch_decode_step(*s, x, win, w, bias, a, b, A_log, dt_bias, eps, state,
+                                          o, static_cast<hipStream_t>(stream)));
+}
+
 gdn_status_t gdn_gated_rmsnorm(const gdn_shape_t* s, const void* o, const void* z,
                                const float* weight, float weight_offset, float eps, void* out,
                                void* stream) {

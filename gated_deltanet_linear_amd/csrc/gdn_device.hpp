@@ -246,6 +246,8 @@ struct Raw8<bf16> {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
   }
+  __device__ __forceinline__ float at(int e) const { return (float)r[e]; }  // e compile-time
+  __device__ __forceinline__ bf16 raw(int e) const { return r[e]; }
 };
 template <>
 struct Raw8<float> {
@@ -265,6 +267,8 @@ struct Raw8<float> {
       x[4 + e] = b[e];
     }
   }
+  __device__ __forceinline__ float at(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+  __device__ __forceinline__ float raw(int e) const { return at(e); }
 };
 
 template <typename T>
@@ -286,6 +290,24 @@ __device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
   }
   *reinterpret_cast<f32x4*>(p) = a;
   *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
+// Eight stored values moved as they are (no arithmetic), nontemporal.
+__device__ __forceinline__ void store8_raw_nt(bf16* p, const bf16 (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e];
+  __builtin_nontemporal_store(r, reinterpret_cast<bf16x8*>(p));
+}
+__device__ __forceinline__ void store8_raw_nt(float* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = x[e];
+    b[e] = x[4 + e];
+  }
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
 }
 
 // Streaming write (not read again by this kernel): nontemporal hint.

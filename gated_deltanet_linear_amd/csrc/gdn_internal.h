@@ -30,6 +30,11 @@ hipError_t launch_decode_prepare(const gdn_shape_t& s, const void* x, void* wind
                                  const float* A_log, const float* dt_bias, float eps, void* q,
                                  void* k, void* v, float* g, float* beta, hipStream_t stream);
 
+hipError_t launch_decode_step(const gdn_shape_t& s, const void* x, void* window, const void* w,
+                              const void* bias, const void* a, const void* b, const float* A_log,
+                              const float* dt_bias, float eps, float* state, void* o,
+                              hipStream_t stream);
+
 hipError_t launch_gated_rmsnorm(const gdn_shape_t& s, const void* o, const void* z,
                                 const float* w, float w_offset, float eps, void* out,
                                 hipStream_t stream);

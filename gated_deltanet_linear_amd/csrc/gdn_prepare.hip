@@ -15,25 +15,11 @@
 // D / 8 lanes that share a token are adjacent in the wave; the L2 norm reduces across them
 // with lane shuffles.
 #include "gdn_device.hpp"
+#include "gdn_front.hpp"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
-
-// Conv bias of channels c .. c+7, zeros without a bias. One unconditional 16-byte load (from
-// `fallback`, any readable 16-byte-aligned address, when there is no bias) and a select on the
-// values: a per-element conditional load compiles to eight dependent loads, and a branch around
-// the load makes the compiler wait for every load in flight where the branches join.
-template <typename InT>
-__device__ __forceinline__ void load_bias8(const InT* bias, const InT* fallback, int c,
-                                           float (&out)[8]) {
-  Raw8<InT> r;
-  r.load(bias ? bias + c : fallback);
-  r.to(out);
-  const bool has = bias != nullptr;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = has ? out[e] : 0.f;
-}
 
 constexpr int kTokBlock = 128;
 
@@ -119,10 +105,8 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int h = (int)((e0 + e + u) % p.hv);
-          const float xa = av[u] + p.dt_bias[h];
-          const float sp = fmaxf(xa, 0.f) + log1pf(expf(-fabsf(xa)));
-          betav[u] = 1.f / (1.f + expf(-bv[u]));
-          gv[u] = -expf(p.A_log[h]) * sp;
+          betav[u] = sigmoid_f32(bv[u]);
+          gv[u] = -expf(p.A_log[h]) * softplus_f32(av[u] + p.dt_bias[h]);
         }
         if (e + 8 <= ne) {
           store8(p.beta + e0 + e, betav);
@@ -308,10 +292,8 @@ decode_prepare_kernel(DecPrepParams p) {
     const InT* B = static_cast<const InT*>(p.b);
     for (int h = tid; h < p.hv; h += 256) {
       const size_t i = (size_t)n * p.hv + h;
-      const float xa = to_f32(A[i]) + p.dt_bias[h];
-      const float sp = fmaxf(xa, 0.f) + log1pf(expf(-fabsf(xa)));
-      p.beta[i] = 1.f / (1.f + expf(-to_f32(B[i])));
-      p.g[i] = -expf(p.A_log[h]) * sp;
+      p.beta[i] = sigmoid_f32(to_f32(B[i]));
+      p.g[i] = -expf(p.A_log[h]) * softplus_f32(to_f32(A[i]) + p.dt_bias[h]);
     }
     return;
   }
@@ -322,45 +304,12 @@ decode_prepare_kernel(DecPrepParams p) {
   const int conv_dim = head_blocks * D;
   const int c = hb * D + 8 * cg;
 
-  const InT* X = static_cast<const InT*>(p.x) + (size_t)n * conv_dim + c;
   InT* W3 = static_cast<InT*>(p.win) + ((size_t)n * conv_dim + c) * 3;
-  const InT* Wt = static_cast<const InT*>(p.w) + (size_t)c * 4;
-  Raw8<InT> rx, rw3[3], rt[4];
-  rx.load_nt(X);  // x and the window are touched once: nontemporal
-#pragma unroll
-  for (int j = 0; j < 3; ++j) rw3[j].load_nt(W3 + 8 * j);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) rt[j].load(Wt + 8 * j);
-  float x[8], wv[24], taps[32], bias[8];
-  rx.to(x);
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    float t8[8];
-    rw3[j].to(t8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) wv[8 * j + e] = t8[e];
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float t8[8];
-    rt[j].to(t8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) taps[8 * j + e] = t8[e];
-  }
-  load_bias8(static_cast<const InT*>(p.bias), Wt, c, bias);
-
-  // channel e: window wv[3e .. 3e+2] (oldest first), taps taps[4e .. 4e+3]
-  float y[8], ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float acc = bias[e];
-    acc = fmaf(taps[4 * e + 0], wv[3 * e + 0], acc);
-    acc = fmaf(taps[4 * e + 1], wv[3 * e + 1], acc);
-    acc = fmaf(taps[4 * e + 2], wv[3 * e + 2], acc);
-    acc = fmaf(taps[4 * e + 3], x[e], acc);
-    y[e] = acc / (1.f + expf(-acc));
-    ss = fmaf(y[e], y[e], ss);
-  }
+  DecodeConv8<InT> cv;
+  cv.load(static_cast<const InT*>(p.x) + (size_t)n * conv_dim + c, W3,
+          static_cast<const InT*>(p.w) + (size_t)c * 4, static_cast<const InT*>(p.bias), c);
+  float y[8];
+  float ss = cv.conv_silu(y);
   const bool is_qk = hb < 2 * p.hqk;
 #pragma unroll
   for (int d = 1; d < CGN; d <<= 1) ss += __shfl_xor(ss, d, kWave);  // lanes of one head
@@ -375,21 +324,7 @@ decode_prepare_kernel(DecPrepParams p) {
   else if (hb < 2 * p.hqk) dst = static_cast<QT*>(p.k) + ((size_t)n * p.hqk + hb - p.hqk) * D;
   else dst = static_cast<QT*>(p.v) + ((size_t)n * p.hv + hb - 2 * p.hqk) * D;
   store8(dst + 8 * cg, y);
-  // window shift: (win[1], win[2], x) per channel
-  float nw[24];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    nw[3 * e + 0] = wv[3 * e + 1];
-    nw[3 * e + 1] = wv[3 * e + 2];
-    nw[3 * e + 2] = x[e];
-  }
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    float t8[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t8[e] = nw[8 * j + e];
-    store8_nt(W3 + 8 * j, t8);
-  }
+  cv.store_shifted_window(W3);
 }
 
 template <typename InT, typename QT, int D>

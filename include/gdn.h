@@ -164,14 +164,34 @@ gdn_status_t gdn_recurrent_step(const gdn_shape_t* shape, const void* q, const v
  *   q, k (out)  [N][H_qk][d_k] qkv_dtype   v (out) [N][H_v][d_v] qkv_dtype
  *   g, beta (out) [N][H_v] fp32
  * mixed_qkv, conv_window, conv_weight, conv_bias (when given), q, k and v must be 16-byte
- * aligned (GDN_ERR_INVALID_ARGUMENT otherwise). Followed by gdn_recurrent_step on the same stream this
- * is a whole decode step from projected inputs.
+ * aligned (GDN_ERR_INVALID_ARGUMENT otherwise). Followed by gdn_recurrent_step on the same
+ * stream this is a whole decode step from projected inputs (gdn_decode_step fuses the two).
  */
 gdn_status_t gdn_decode_prepare(const gdn_shape_t* shape, const void* mixed_qkv,
                                 void* conv_window, const void* conv_weight,
                                 const void* conv_bias, const void* a, const void* b,
                                 const float* A_log, const float* dt_bias, float l2norm_eps,
                                 void* q, void* k, void* v, float* g, float* beta, void* stream);
+
+/*
+ * gdn_decode_step -- one decode token per sequence from projected inputs, fused: the front end
+ * of gdn_decode_prepare (conv over the cached window, SiLU, split, q / k L2 norm, gates; the
+ * window shifted in place) followed by the gated delta step of gdn_recurrent_step on the state,
+ * in one kernel ([xiwon notes] "Cache"; [MoE report] §3.3 stages 2 and 3, decode path). q, k and
+ * v stay fp32 between the two (shape->qkv_dtype is ignored), so the result equals the two-call
+ * path with fp32 q/k/v up to fp32 rounding. Requires total_tokens == num_seqs; one workgroup
+ * holds the q, k and G = H_v / H_qk v rows of a QK head, so (2 + G) * d_v + 2 G floats must fit
+ * in 64 KiB (GDN_ERR_UNSUPPORTED otherwise).
+ *   mixed_qkv, conv_window, conv_weight, conv_bias, a, b, A_log, dt_bias: as gdn_decode_prepare
+ *   state [N][H_v][d_k][d_v] fp32, updated in place      o (out) [N][H_v][d_v] out_dtype
+ * mixed_qkv, conv_window, conv_weight, conv_bias (when given) and state must be 16-byte aligned
+ * (GDN_ERR_INVALID_ARGUMENT otherwise). The window and the state of a sequence must not be
+ * shared with another sequence of the same call.
+ */
+gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* mixed_qkv, void* conv_window,
+                             const void* conv_weight, const void* conv_bias, const void* a,
+                             const void* b, const float* A_log, const float* dt_bias,
+                             float l2norm_eps, float* state, void* o, void* stream);
 
 /*
  * gdn_gated_rmsnorm -- output gate of the layer ([xiwon notes] "Qwen3_5MoeGatedDeltaNet",

@@ -173,6 +173,35 @@ def test_decode_prepare_validation(lib):
                 outs) == UNSUPPORTED
 
 
+def test_decode_step_validation(lib):
+    s = _shape(num_seqs=4, total_tokens=4)
+    ins = [FAKE] * 8  # x, window, w, bias, a, b, A_log, dt_bias
+
+    def call(shape, ins, eps=1e-6, state=FAKE, o=FAKE):
+        return lib.gdn_decode_step(ctypes.byref(shape), *ins, eps, state, o, None)
+
+    assert call(_shape(num_seqs=4, total_tokens=5), ins) == INVALID
+    assert call(s, ins, eps=-1.0) == INVALID
+    for i in (0, 1, 2, 4, 5, 6, 7):  # every input except the optional bias
+        bad = list(ins)
+        bad[i] = None
+        assert call(s, bad) == INVALID
+    assert call(s, ins, state=None) == INVALID
+    assert call(s, ins, o=None) == INVALID
+    for i in (0, 1, 2, 3):  # x, window, taps, bias must be 16-byte aligned
+        bad = list(ins)
+        bad[i] = ctypes.c_void_p((1 << 20) + 8)
+        assert call(s, bad) == INVALID
+    assert call(s, ins, state=ctypes.c_void_p((1 << 20) + 4)) == INVALID
+    assert call(_shape(num_seqs=4, total_tokens=4, head_dim_k=64, head_dim_v=128), ins) \
+        == UNSUPPORTED
+    assert call(_shape(num_seqs=4, total_tokens=4, head_dim_k=16, head_dim_v=16), ins) \
+        == UNSUPPORTED
+    # G = 128 V heads per QK head: q, k and 128 v rows of 128 floats exceed the 64 KiB of LDS
+    assert call(_shape(num_seqs=4, total_tokens=4, num_qk_heads=1, num_v_heads=128), ins) \
+        == UNSUPPORTED
+
+
 def test_gated_rmsnorm_validation(lib):
     s = _shape()
 

@@ -136,3 +136,115 @@ def test_decode_steps_from_projected_inputs_match_whole_sequence():
     ro, rh = oracle.recurrent(rq, rk, rv, rg, rb, [0, L])
     assert_rms_close(got, ro[L0:], TOL["f32"], "decode outputs from projected inputs")
     assert_rms_close(state.cpu(), rh, TOL["f32"], "state after decode")
+
+
+def _decode_oracle(x, win, w, bc, a, b, A_log, dt_bias, h0, hqk, hv, d, scale=1.0):
+    """Float64 decode step from projected inputs: the oracle's front end, then one token of the
+    oracle's recurrence per sequence from the given state."""
+    N = x.shape[0]
+    rq, rk, rv, rg, rb, rwin = oracle.decode_prepare(
+        f64(x), f64(win), f64(w), f64(a), f64(b), f64(A_log), f64(dt_bias), hqk, d, hv, d,
+        conv_bias=f64(bc))
+    ro, rh = oracle.recurrent(rq, rk, rv, rg, rb, np.arange(N + 1), initial_state=f64(h0),
+                              scale=scale)
+    return ro, rh, rwin
+
+
+@pytest.mark.parametrize("d,dt,G", [(32, "f32", 1), (64, "bf16", 2), (128, "bf16", 2),
+                                    (128, "f32", 4), (64, "bf16", 3)])
+def test_decode_step_fused_against_oracle(d, dt, G):
+    rng = np.random.default_rng(500 + d + G)
+    N, hqk = 19, 2
+    hv = hqk * G
+    x, win, w, bc, a, b, A_log, dt_bias = _front(rng, N, hqk, hv, d, _DT[dt], bias=(G != 3))
+    h0 = torch.from_numpy(rng.standard_normal((N, hv, d, d)) * 0.05).float()
+    for odt in ("f32", dt):
+        print(f"[decode_step] d={d} {dt} G={G} out={odt}", flush=True)
+        wd, hd = win.cuda(), h0.cuda()
+        o = gdn.decode_step(x.cuda(), wd, w.cuda(), a.cuda(), b.cuda(), A_log.cuda(),
+                            dt_bias.cuda(), hd, hqk, d, hv,
+                            conv_bias=None if bc is None else bc.cuda(), scale=0.7,
+                            out_dtype=_DT[odt])
+        torch.cuda.synchronize()
+        ro, rh, rwin = _decode_oracle(x, win, w, bc, a, b, A_log, dt_bias, h0, hqk, hv, d,
+                                      scale=0.7)
+        # every value the oracle does not see is an fp32 intermediate: the fp32 bar
+        check = assert_rms_close_rounded_out if odt == "bf16" else assert_rms_close
+        check(o, ro, TOL["f32"], "fused decode o")
+        assert_rms_close(hd.cpu(), rh, TOL["f32"], "fused decode state")
+        assert np.array_equal(f64(wd), rwin)
+
+
+def test_decode_step_fused_matches_two_call_path():
+    rng = np.random.default_rng(77)
+    N, hqk, hv, d = 33, 4, 8, 128
+    x, win, w, bc, a, b, A_log, dt_bias = _front(rng, N, hqk, hv, d, torch.bfloat16)
+    h0 = torch.from_numpy(rng.standard_normal((N, hv, d, d)) * 0.02).float().cuda()
+    w1, w2 = win.cuda(), win.cuda()
+    s1, s2 = h0.clone(), h0.clone()
+    o1 = gdn.decode_step(x.cuda(), w1, w.cuda(), a.cuda(), b.cuda(), A_log.cuda(),
+                         dt_bias.cuda(), s1, hqk, d, hv, conv_bias=bc.cuda(),
+                         out_dtype=torch.float32)
+    q, k, v, g, beta = gdn.decode_prepare(x.cuda(), w2, w.cuda(), a.cuda(), b.cuda(),
+                                          A_log.cuda(), dt_bias.cuda(), hqk, d, hv, d,
+                                          conv_bias=bc.cuda(), qkv_dtype=torch.float32)
+    o2 = gdn.recurrent_step(q, k, v, g, beta, s2, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(w1, w2)
+    assert_rms_close(o1.cpu(), f64(o2), 1e-5, "fused vs two-call o")
+    assert_rms_close(s1.cpu(), f64(s2), 1e-5, "fused vs two-call state")
+
+
+def test_decode_step_fused_after_prefill_matches_whole_sequence():
+    """Prefill 70 tokens, then 5 fused decode steps: the decode outputs and the final state must
+    match the oracle over the whole 75-token sequence (front end + recurrence)."""
+    rng = np.random.default_rng(12)
+    hqk, hv, d, dtype = 2, 4, 64, torch.bfloat16
+    L0, steps = 70, 5
+    L = L0 + steps
+    conv_dim = (2 * hqk + hv) * d
+    x = _rand(rng, (L, conv_dim), dtype)
+    w = _rand(rng, (conv_dim, 4), dtype, 0.5)
+    a = _rand(rng, (L, hv), dtype)
+    b = _rand(rng, (L, hv), dtype)
+    A_log = torch.tensor(rng.uniform(-1.0, 1.0, hv), dtype=torch.float32)
+    dt_bias = torch.tensor(rng.standard_normal(hv) * 0.2, dtype=torch.float32)
+    cu = torch.tensor([0, L0], dtype=torch.int32)
+    q, k, v, g, beta = gdn.prepare(x[:L0].cuda(), w.cuda(), a[:L0].cuda(), b[:L0].cuda(),
+                                   A_log.cuda(), dt_bias.cuda(), cu.cuda(), hqk, d, hv, d,
+                                   qkv_dtype=torch.float32)
+    _, state = gdn.chunk_forward(q, k, v, g, beta, cu.cuda(), out_dtype=torch.float32)
+    window = x[L0 - 3:L0].T.contiguous().unsqueeze(0).cuda()
+    outs = [gdn.decode_step(x[t:t + 1].cuda(), window, w.cuda(), a[t:t + 1].cuda(),
+                            b[t:t + 1].cuda(), A_log.cuda(), dt_bias.cuda(), state, hqk, d, hv,
+                            out_dtype=torch.float32)
+            for t in range(L0, L)]
+    torch.cuda.synchronize()
+    got = torch.cat(outs).cpu()
+    rq, rk, rv, rg, rb = oracle.prepare(f64(x), f64(w), f64(a), f64(b), f64(A_log),
+                                        f64(dt_bias), [0, L], hqk, d, hv, d)
+    ro, rh = oracle.recurrent(rq, rk, rv, rg, rb, [0, L])
+    assert_rms_close(got, ro[L0:], TOL["f32"], "fused decode outputs after prefill")
+    assert_rms_close(state.cpu(), rh, TOL["f32"], "state after fused decode")
+    assert np.array_equal(f64(window[0]), f64(x[L - 3:L]).T)
+
+
+def test_decode_step_fused_full_size_sampled():
+    """256 sequences of the 35B-A3B shape (16 QK / 32 V heads, d = 128, 537 MB state): outputs,
+    states and windows of 6 sampled sequences against the oracle."""
+    import synthetic_inputs as si
+
+    dc = si.make_decode_front_case(256, 16, 32, 128, 128, seed=1007)
+    dev = "cuda"
+    x, win, w, a, b = (t.to(dev) for t in (dc.mixed_qkv, dc.window, dc.conv_weight, dc.a, dc.b))
+    A_log, dt_bias, state = dc.A_log.to(dev), dc.dt_bias.to(dev), dc.h0.to(dev)
+    o = gdn.decode_step(x, win, w, a, b, A_log, dt_bias, state, 16, 128, 32)
+    torch.cuda.synchronize()
+    rows = [0, 1, 77, 128, 200, 255]
+    sel = torch.tensor(rows)
+    ro, rh, rwin = _decode_oracle(dc.mixed_qkv[sel], dc.window[sel], dc.conv_weight, None,
+                                  dc.a[sel], dc.b[sel], dc.A_log, dc.dt_bias, dc.h0[sel], 16, 32,
+                                  128)
+    assert_rms_close_rounded_out(o[sel.cuda()].cpu(), ro, TOL["f32"], "fused decode 256x1 o")
+    assert_rms_close(state[sel.cuda()].cpu(), rh, TOL["f32"], "fused decode 256x1 state")
+    assert np.array_equal(f64(win[sel.cuda()].cpu()), rwin)
