@@ -15,7 +15,8 @@ Roofline conventions (algorithmic work, not what the kernels happen to issue):
   prefill FLOPs per token per V head = (4/G) C d_k + 2 C d_k + 4 C d_v + 6 d_k d_v   (C = 64)
     of which the scan kernel's share is 4 C d_v + 6 d_k d_v (state products, T diag(beta) Y
     and the masked intra-chunk product); peak = 2500 TFLOP/s dense bf16 MFMA.
-  decode bytes = 2 N H_v d_k d_v 4 + N [H_qk 2 d_k e + H_v (2 d_v e + 8)];  peak 8000 GB/s.
+  decode bytes = 2 N H_v d_k d_v s + N [H_qk 2 d_k e + H_v (2 d_v e + 8)];  peak 8000 GB/s
+    (s = 4 for the fp32 state, 2 for the bf16 state).
   front-end bytes = T [2 conv_dim e + 2 H_v e + 8 H_v] (+ q/k/v written at their dtype).
   output-gate bytes = 3 T H_v d_v e + 4 d_v   (o and z read, out written, fp32 weight).
   decode front-end bytes = N [8 conv_dim e + H_v (2 e + 8)] + 4 conv_dim e   (x, window read
@@ -197,8 +198,20 @@ def run_decode(torch, gdn, si, steps, warmup):
     ev_ms, ms, kms = _measure(torch, kernels, steps, warmup)
     B = 2 * N * hv * dk * dv * 4 + N * (hqk * 2 * dk * 2 + hv * (2 * dv * 2 + 8))
     kt = kms["gdn_recurrent_step"] / 1e3
+    # the same step on a bf16 state (half the state bytes)
+    state16 = state.to(torch.bfloat16)
+    del state
+    ev16, ms16, kms16 = _measure(
+        torch, [("gdn_recurrent_step",
+                 lambda: gdn.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state16,
+                                            o=o))], steps, warmup)
+    B16 = 2 * N * hv * dk * dv * 2 + N * (hqk * 2 * dk * 2 + hv * (2 * dv * 2 + 8))
+    bf16_state = dict(ms_per_step=ms16, tokens_per_s=N / (ms16 / 1e3), kernels_ms=kms16,
+                      roofline=_hbm("gdn_recurrent_step", B16, kms16["gdn_recurrent_step"],
+                                    "gdn_recurrent_step_decode_256x1_bf16_state"))
+    del state16
     return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=N / (ms / 1e3),
-                kernels_ms=kms,
+                kernels_ms=kms, bf16_state=bf16_state,
                 roofline=dict(kernel="gdn_recurrent_step", bound="hbm",
                               achieved=round(B / kt / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(B / kt / 1e9 / PEAK_HBM_GBS, 4),
@@ -304,16 +317,27 @@ def run_decode_front(torch, gdn, si, steps, warmup):
 
     ev2, ms2, kms2 = _measure(
         torch, [("gdn_decode_prepare", prep), ("gdn_recurrent_step", rstep)], steps, warmup)
+    state16 = state.to(torch.bfloat16)
+    del state
+    ev3, ms3, kms3 = _measure(
+        torch, [("gdn_decode_step", lambda: gdn.decode_step(x, win, w, a, b, A_log, dt_bias,
+                                                            state16, hqk, dk, hv, o=o))],
+        steps, warmup)
+    del state16
     conv_dim = 2 * hqk * dk + hv * dv
     e = 2
     Bfused = (2 * N * hv * dk * dv * 4 + N * (conv_dim * e * 7 + hv * (2 * e + dv * e))
               + conv_dim * 4 * e)
+    Bfused16 = Bfused - N * hv * dk * dv * 4
     Bprep = N * (conv_dim * e * 8 + hv * (2 * e + 8)) + conv_dim * 4 * e
     Bstep = 2 * N * hv * dk * dv * 4 + N * (hqk * 2 * dk * e + hv * (2 * dv * e + 8))
     return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=N / (ms / 1e3),
                 kernels_ms=kms,
                 roofline=_hbm("gdn_decode_step", Bfused, kms["gdn_decode_step"],
                               "gdn_decode_step_decode_front_256x1"),
+                bf16_state=dict(ms_per_step=ms3, tokens_per_s=N / (ms3 / 1e3), kernels_ms=kms3,
+                                roofline=_hbm("gdn_decode_step", Bfused16, kms3["gdn_decode_step"],
+                                              "gdn_decode_step_decode_front_256x1_bf16_state")),
                 two_call=dict(ms_per_step=ms2, tokens_per_s=N / (ms2 / 1e3), kernels_ms=kms2,
                               decode_prepare=_hbm("gdn_decode_prepare", Bprep,
                                                   kms2["gdn_decode_prepare"],

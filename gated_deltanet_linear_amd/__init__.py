@@ -30,6 +30,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgdn.so")
 CHUNK = 64
 
+ABI_VERSION = 2  # GDN_ABI_VERSION of include/gdn.h that GdnShape and the signatures follow
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 _DT = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
 
@@ -43,7 +44,8 @@ class GdnShape(ctypes.Structure):
                 ("num_qk_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("in_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("in_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("state_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -88,6 +90,9 @@ def _load():
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_abi_version.restype = ctypes.c_int
     lib.gdn_abi_version.argtypes = []
+    if lib.gdn_abi_version() != ABI_VERSION:
+        raise GdnError(f"{_LIB_PATH} has ABI version {lib.gdn_abi_version()}, this binding "
+                       f"expects {ABI_VERSION}; rebuild the library")
     _lib = lib
     return lib
 
@@ -122,13 +127,22 @@ def _dtype_code(dt: torch.dtype, name: str) -> int:
 
 
 def _shape(num_seqs, total_tokens, hqk, hv, dk, dv, qkv_dtype, out_dtype, in_dtype=None,
-           scale=1.0) -> GdnShape:
+           scale=1.0, state_dtype=None) -> GdnShape:
     return GdnShape(int(num_seqs), int(total_tokens), int(hqk), int(hv), int(dk), int(dv),
                     _dtype_code(qkv_dtype, "q/k/v"), _dtype_code(out_dtype, "o"),
-                    _dtype_code(in_dtype or torch.bfloat16, "front-end input"), float(scale))
+                    _dtype_code(in_dtype or torch.bfloat16, "front-end input"), float(scale),
+                    _dtype_code(state_dtype or torch.float32, "state"))
 
 
-def _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype):
+def _state_dtype(*states, default=None):
+    """The one dtype of the given state tensors (None entries skipped)."""
+    dts = {t.dtype for t in states if t is not None}
+    if len(dts) > 1:
+        raise GdnError("initial and final states must have the same dtype")
+    return dts.pop() if dts else (default or torch.float32)
+
+
+def _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, state_dtype=None):
     _dev(q, "q")
     _dev(k, "k", q.dtype)
     _dev(g, "g", torch.float32)
@@ -142,7 +156,8 @@ def _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype):
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise GdnError("cu_seqlens must be [N + 1]")
     n = cu_seqlens.numel() - 1
-    return _shape(n, T, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale), n
+    return _shape(n, T, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale,
+                  state_dtype=state_dtype), n
 
 
 def _v_shape(v, q):
@@ -167,26 +182,29 @@ def _workspace(s: GdnShape, device, workspace):
 
 
 def chunk_forward(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_state=True,
-                  scale=1.0, out_dtype=None, workspace=None, final_state=None, o=None
-                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  scale=1.0, out_dtype=None, workspace=None, final_state=None, o=None,
+                  state_dtype=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill. Returns (o [T, H_v, d_v], final_state [N, H_v, d_k, d_v] or None).
 
     ``final_state`` may be passed (and may be ``initial_state`` itself for an in-place update).
+    States are fp32 or bf16 (one dtype for both: ``state_dtype``, else the given states' dtype,
+    else fp32).
     """
     hv, dv = _v_shape(v, q)
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype)
+    sd = _state_dtype(initial_state, final_state, default=state_dtype)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, sd)
     T, dk = s.total_tokens, s.head_dim_k
     if initial_state is not None:
-        _dev(initial_state, "initial_state", torch.float32)
+        _dev(initial_state, "initial_state", sd)
         if initial_state.shape != (n, hv, dk, dv):
             raise GdnError("initial_state must be [N, H_v, d_k, d_v]")
     if o is None:
         o = torch.empty((T, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
     _dev(o, "o", out_dtype or q.dtype)
     if output_final_state and final_state is None:
-        final_state = torch.empty((n, hv, dk, dv), dtype=torch.float32, device=q.device)
+        final_state = torch.empty((n, hv, dk, dv), dtype=sd, device=q.device)
     if final_state is not None:
-        _dev(final_state, "final_state", torch.float32)
+        _dev(final_state, "final_state", sd)
     ws = _workspace(s, q.device, workspace)
     rc = _load().gdn_chunk_forward(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
@@ -208,7 +226,13 @@ def chunk_scan(q, k, v, g, beta, cu_seqlens, workspace, initial_state=None, o=No
                final_state=None, scale=1.0, out_dtype=None):
     """Stage 2 of chunk_forward (sequential cross-chunk recurrence) from ``workspace``."""
     hv, dv = _v_shape(v, q)
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype)
+    sd = _state_dtype(initial_state, final_state)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, sd)
+    for t, name in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _dev(t, name, sd)
+            if t.shape != (n, hv, s.head_dim_k, dv):
+                raise GdnError(f"{name} must be [N, H_v, d_k, d_v]")
     _dev(workspace, "workspace", torch.uint8)
     if o is None:
         o = torch.empty((s.total_tokens, s.num_v_heads, s.head_dim_v), dtype=out_dtype or q.dtype,
@@ -222,19 +246,20 @@ def chunk_scan(q, k, v, g, beta, cu_seqlens, workspace, initial_state=None, o=No
 
 def recurrent_step(q, k, v, g, beta, state, scale=1.0, out_dtype=None, o=None) -> torch.Tensor:
     """One decode token per sequence: q, k [N, H_qk, d_k], v [N, H_v, d_v], g, beta [N, H_v],
-    state [N, H_v, d_k, d_v] fp32 (updated in place). Returns o [N, H_v, d_v]."""
+    state [N, H_v, d_k, d_v] fp32 or bf16 (updated in place). Returns o [N, H_v, d_v]."""
     _dev(q, "q")
     _dev(k, "k", q.dtype)
     _dev(v, "v", q.dtype)
     _dev(g, "g", torch.float32)
     _dev(beta, "beta", torch.float32)
-    _dev(state, "state", torch.float32)
+    _dev(state, "state")
     N, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     if k.shape != q.shape or v.shape[0] != N or g.shape != (N, hv) or beta.shape != (N, hv) \
             or state.shape != (N, hv, dk, dv):
         raise GdnError("recurrent_step: inconsistent shapes")
-    s = _shape(N, N, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale)
+    s = _shape(N, N, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale,
+               state_dtype=state.dtype)
     if o is None:
         o = torch.empty((N, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
     _dev(o, "o", out_dtype or q.dtype)
@@ -330,8 +355,8 @@ def decode_step(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, state
     """One decode token per sequence from projected inputs, fused (front end + gated delta step).
 
     mixed_qkv [N, conv_dim]; conv_window [N, conv_dim, 3] (updated in place); conv_weight
-    [conv_dim, 4]; a, b [N, H_v]; A_log, dt_bias [H_v] fp32; state [N, H_v, d, d] fp32 (updated in
-    place). Returns o [N, H_v, d] (out_dtype, default the input dtype).
+    [conv_dim, 4]; a, b [N, H_v]; A_log, dt_bias [H_v] fp32; state [N, H_v, d, d] fp32 or bf16
+    (updated in place). Returns o [N, H_v, d] (out_dtype, default the input dtype).
     """
     _dev(mixed_qkv, "mixed_qkv")
     dt = mixed_qkv.dtype
@@ -341,7 +366,7 @@ def decode_step(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, state
     _dev(b, "b", dt)
     _dev(A_log, "A_log", torch.float32)
     _dev(dt_bias, "dt_bias", torch.float32)
-    _dev(state, "state", torch.float32)
+    _dev(state, "state")
     if conv_bias is not None:
         _dev(conv_bias, "conv_bias", dt)
     N, conv_dim = mixed_qkv.shape
@@ -355,7 +380,8 @@ def decode_step(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, state
     if state.shape != (N, hv, d, d):
         raise GdnError("state must be [N, H_v, d, d]")
     od = out_dtype or dt
-    s = _shape(N, N, hqk, hv, d, d, torch.float32, od, in_dtype=dt, scale=scale)
+    s = _shape(N, N, hqk, hv, d, d, torch.float32, od, in_dtype=dt, scale=scale,
+               state_dtype=state.dtype)
     if o is None:
         o = torch.empty((N, hv, d), dtype=od, device=mixed_qkv.device)
     _dev(o, "o", od)

@@ -18,7 +18,8 @@ gdn_status_t check_shape(const gdn_shape_t* s) {
   if (s->num_seqs < 1 || s->total_tokens < 0 || s->num_qk_heads < 1 || s->num_v_heads < 1)
     return GDN_ERR_INVALID_ARGUMENT;
   if (s->num_v_heads % s->num_qk_heads != 0) return GDN_ERR_INVALID_ARGUMENT;
-  if (!dtype_ok(s->qkv_dtype) || !dtype_ok(s->out_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!dtype_ok(s->qkv_dtype) || !dtype_ok(s->out_dtype) || !dtype_ok(s->state_dtype))
+    return GDN_ERR_INVALID_ARGUMENT;
   if (s->head_dim_k < 1 || s->head_dim_v < 1) return GDN_ERR_INVALID_ARGUMENT;
   if (!(s->scale == s->scale)) return GDN_ERR_INVALID_ARGUMENT;  // NaN
   if (s->head_dim_k != s->head_dim_v) return GDN_ERR_UNSUPPORTED;
@@ -100,7 +101,7 @@ gdn_status_t gdn_chunk_intra(const gdn_shape_t* s, const int32_t* cu, const void
 }
 
 gdn_status_t gdn_chunk_scan(const gdn_shape_t* s, const int32_t* cu, const void* q,
-                            const void* k, const void* v, const float* h0, void* o, float* ht,
+                            const void* k, const void* v, const void* h0, void* o, void* ht,
                             const void* ws, size_t ws_bytes, void* stream) {
   gdn_status_t st = check_chunk_common(s, cu, q, k, ws, ws_bytes);
   if (st != GDN_OK) return st;
@@ -111,7 +112,7 @@ gdn_status_t gdn_chunk_scan(const gdn_shape_t* s, const int32_t* cu, const void*
 
 gdn_status_t gdn_chunk_forward(const gdn_shape_t* s, const int32_t* cu, const void* q,
                                const void* k, const void* v, const float* g, const float* beta,
-                               const float* h0, void* o, float* ht, void* ws, size_t ws_bytes,
+                               const void* h0, void* o, void* ht, void* ws, size_t ws_bytes,
                                void* stream) {
   gdn_status_t st = check_chunk_common(s, cu, q, k, ws, ws_bytes);
   if (st != GDN_OK) return st;
@@ -123,7 +124,7 @@ gdn_status_t gdn_chunk_forward(const gdn_shape_t* s, const int32_t* cu, const vo
 }
 
 gdn_status_t gdn_recurrent_step(const gdn_shape_t* s, const void* q, const void* k,
-                                const void* v, const float* g, const float* beta, float* state,
+                                const void* v, const float* g, const float* beta, void* state,
                                 void* o, void* stream) {
   gdn_status_t st = check_shape(s);
   if (st != GDN_OK) return st;
@@ -156,7 +157,7 @@ gdn_status_t gdn_decode_prepare(const gdn_shape_t* s, const void* x, void* win, 
 
 gdn_status_t gdn_decode_step(const gdn_shape_t* s, const void* x, void* win, const void* w,
                              const void* bias, const void* a, const void* b, const float* A_log,
-                             const float* dt_bias, float eps, float* state, void* o,
+                             const float* dt_bias, float eps, void* state, void* o,
                              void* stream) {
   gdn_status_t st = check_shape(s);
   if (st != GDN_OK) return st;

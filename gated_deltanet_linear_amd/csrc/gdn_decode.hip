@@ -1,4 +1,4 @@
-// gdn_decode.hip -- one decode token per sequence: gated delta rule step on the fp32 state,
+// gdn_decode.hip -- one decode token per sequence: gated delta rule step on the stored state,
 // updated in place ([MoE report] §3.3 stage 3, decode path; [xiwon notes]
 // "Qwen3_5MoeGatedDeltaNet" recurrent branch and "Cache").
 //
@@ -8,14 +8,16 @@
 //   H' = a H + k u^T                                 (written back in place)
 //   o  = scale (a qh + qk u)  = scale H'^T q          (no second pass over the state)
 //
-// The step moves 2 * d_k * d_v * 4 bytes of state per head and does ~7 d_k d_v flops, so it is
-// bound by HBM. One workgroup owns one head (columns could be split across workgroups, but
-// then every load covers 128-byte pieces of rows instead of whole rows, which streams slower):
-// thread (cg, rg) keeps a float4 column group cg for rows rg, rg + RG, ... in registers between
-// the read and the write, so every state byte crosses HBM exactly once each way. A wave's load
-// instruction covers whole contiguous rows (coalesced 16-byte lanes); loads and stores are
-// non-temporal since the state is not reused by this step. The row reductions run over lanes
-// first (xor shuffles across the row groups of a wave), then over waves through LDS.
+// The step moves 2 * d_k * d_v * sizeof(state) bytes of state per head and does ~7 d_k d_v
+// flops, so it is bound by HBM. One workgroup owns one head (columns could be split across
+// workgroups, but then every load covers 128-byte pieces of rows instead of whole rows, which
+// streams slower): thread (cg, rg) keeps one 16-byte column group cg (4 fp32 or 8 bf16 values)
+// for rows rg, rg + RG, ... in registers between the read and the write, so every state byte
+// crosses HBM exactly once each way. A wave's load instruction covers whole contiguous rows
+// (coalesced 16-byte lanes); loads and stores are non-temporal since the state is not reused by
+// this step. The row reductions run over lanes first (xor shuffles across the row groups of a
+// wave), then over waves through LDS. A bf16 state is read exactly, carried in fp32 through the
+// step and stored as the round-to-nearest-even cast of the new fp32 state.
 // decode_step_kernel below is the same step fused with the decode-side front end.
 #include "gdn_device.hpp"
 #include "gdn_front.hpp"
@@ -24,100 +26,169 @@
 namespace gdn {
 namespace {
 
-// Threads per workgroup: 512 for 128 x 128 heads (8 rows per thread: enough loads in flight
-// per wave without limiting occupancy), fewer for small heads (at least 2 rows per thread).
-template <int DK, int DV>
+// Threads per workgroup. fp32 state: 512 for 128 x 128 heads (8 rows of 16 bytes per thread:
+// enough loads in flight per wave without limiting occupancy), fewer for small heads. bf16
+// state: also 8 rows of 16 bytes per thread (256 threads for 128 x 128), at least one wave; with
+// 512 threads each thread would hold half the bytes and the CU too few loads in flight.
+template <typename ST, int D>
 constexpr int step_threads() {
-  return DK * DV / 8 < 512 ? DK * DV / 8 : 512;
+  if constexpr (sizeof(ST) == 4) return D * D / 8 < 512 ? D * D / 8 : 512;
+  return D * D / 64 > 64 ? D * D / 64 : 64;
 }
 
-template <typename InT, typename OutT, int DK, int DV>
-__global__ __launch_bounds__((step_threads<DK, DV>())) void recurrent_step_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    OutT* __restrict__ o, int hqk, int hv, float scale) {
-  constexpr int NTH = step_threads<DK, DV>();
-  constexpr int NW = NTH / 64;  // waves
-  constexpr int CG = DV / 4;    // float4 column groups per row
-  constexpr int RG = NTH / CG;  // row groups
-  constexpr int R = DK / RG;    // rows per thread
-  static_assert(DV % 4 == 0 && NTH % 64 == 0 && 64 % CG == 0 && DK % RG == 0 && R >= 1,
-                "tile shape");
-
-  __shared__ f32x4 red_k[NW][CG];
-  __shared__ f32x4 red_q[NW][CG];
-  __shared__ float red_qk[NW];
-
-  const int nh = blockIdx.x;  // n * hv + h
-  const int n = nh / hv, h = nh - (nh / hv) * hv;
-  const int m = h / (hv / hqk);
-  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG, lane = tid & 63, wave = tid >> 6;
-
-  f32x4* S = reinterpret_cast<f32x4*>(state + (size_t)nh * DK * DV);
-  const InT* qv = q + ((size_t)n * hqk + m) * DK;
-  const InT* kv = k + ((size_t)n * hqk + m) * DK;
-
-  f32x4 s[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) s[r] = __builtin_nontemporal_load(S + (rg + RG * r) * CG + cg);
-
-  float qi[R], ki[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    qi[r] = to_f32(qv[rg + RG * r]);
-    ki[r] = to_f32(kv[rg + RG * r]);
+// 16 bytes of one state row: 4 fp32 or 8 bf16 values.
+template <typename ST>
+struct StateVec;
+template <>
+struct StateVec<float> {
+  static constexpr int VEC = 4;
+  f32x4 r;
+  __device__ __forceinline__ void load(const float* p) {
+    r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   }
-  const float alpha = expf(g[nh]);
-  const float bt = beta[nh];
+  __device__ __forceinline__ float at(int c) const { return r[c]; }
+  __device__ __forceinline__ static void store(float* p, const float (&x)[VEC]) {
+    f32x4 v = {x[0], x[1], x[2], x[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+  }
+};
+template <>
+struct StateVec<bf16> {
+  static constexpr int VEC = 8;
+  bf16x8 r;
+  __device__ __forceinline__ void load(const bf16* p) {
+    r = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+  }
+  __device__ __forceinline__ float at(int c) const { return (float)r[c]; }
+  __device__ __forceinline__ static void store(bf16* p, const float (&x)[VEC]) {
+    bf16x8 v;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) v[c] = (bf16)x[c];  // round to nearest even
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
+  }
+};
 
-  f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-  float pqk = 0.f;
+// Thread layout of one D x D head over NTH threads.
+template <typename ST, int D>
+struct StepLayout {
+  static constexpr int NTH = step_threads<ST, D>();
+  static constexpr int NW = NTH / 64;
+  static constexpr int VEC = StateVec<ST>::VEC;
+  static constexpr int CG = D / VEC;    // 16-byte column groups per row
+  static constexpr int RG = NTH / CG;   // row groups
+  static constexpr int R = D / RG;      // rows per thread
+  static_assert(D % VEC == 0 && NTH % 64 == 0 && 64 % CG == 0 && D % RG == 0 && R >= 1,
+                "tile shape");
+};
+
+// LDS for the cross-wave reductions of one head.
+template <typename ST, int D>
+struct StepRed {
+  using L = StepLayout<ST, D>;
+  float k[L::NW][L::CG][L::VEC];
+  float q[L::NW][L::CG][L::VEC];
+  float qk[L::NW];
+};
+
+// The step of one head whose rows the thread holds in s[0 .. R) (registers of the caller, which
+// loaded them; the call is inlined). qrow / krow give q and k at the thread's rows (index r),
+// vcol the v value of column c of its group. Writes o (threads of row group 0) and the new
+// state; the barrier inside is workgroup-wide.
+template <typename ST, typename OutT, int D, typename QF, typename KF, typename VF>
+__device__ __forceinline__ void head_step(const StateVec<ST>* s, StepRed<ST, D>& red, QF qrow,
+                                          KF krow, VF vcol,
+                                          float alpha, float bt, float scale, ST* S, OutT* ov,
+                                          int tid) {
+  using L = StepLayout<ST, D>;
+  constexpr int VEC = L::VEC, CG = L::CG, RG = L::RG, R = L::R, NW = L::NW;
+  const int cg = tid % CG, rg = tid / CG, lane = tid & 63, wave = tid >> 6;
+  float pk[VEC], pq[VEC], pqk = 0.f;
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) pk[c] = pq[c] = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    pk += s[r] * ki[r];
-    pq += s[r] * qi[r];
-    pqk += qi[r] * ki[r];
+    const float qr = qrow(r), kr = krow(r);
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      pk[c] = fmaf(s[r].at(c), kr, pk[c]);
+      pq[c] = fmaf(s[r].at(c), qr, pq[c]);
+    }
+    pqk = fmaf(qr, kr, pqk);
   }
   // Lanes cg, cg + CG, ... of a wave hold the same columns for different rows.
 #pragma unroll
   for (int off = CG; off < 64; off <<= 1) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < VEC; ++c) {
       pk[c] += __shfl_xor(pk[c], off);
       pq[c] += __shfl_xor(pq[c], off);
     }
     pqk += __shfl_xor(pqk, off);
   }
   if (lane < CG) {
-    red_k[wave][lane] = pk;
-    red_q[wave][lane] = pq;
-    if (lane == 0) red_qk[wave] = pqk;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      red.k[wave][lane][c] = pk[c];
+      red.q[wave][lane][c] = pq[c];
+    }
+    if (lane == 0) red.qk[wave] = pqk;
   }
   __syncthreads();
-
-  f32x4 sk = red_k[0][cg], sq = red_q[0][cg];
-  float qk = red_qk[0];
+  float qk = red.qk[0], u[VEC];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    sk += red_k[w][cg];
-    sq += red_q[w][cg];
-    qk += red_qk[w];
+  for (int w = 1; w < NW; ++w) qk += red.qk[w];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) {
+    float skc = red.k[0][cg][c], sqc = red.q[0][cg][c];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      skc += red.k[w][cg][c];
+      sqc += red.q[w][cg][c];
+    }
+    u[c] = bt * (vcol(c) - alpha * skc);
+    if (rg == 0) ov[VEC * cg + c] = from_f32<OutT>(scale * (alpha * sqc + qk * u[c]));
   }
-  const InT* vv = v + (size_t)nh * DV + 4 * cg;
-  f32x4 u;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) u[c] = bt * (to_f32(vv[c]) - alpha * sk[c]);
-  if (rg == 0) {
-    OutT* ov = o + (size_t)nh * DV + 4 * cg;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ov[c] = from_f32<OutT>(scale * (alpha * sq[c] + qk * u[c]));
-  }
-
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    f32x4 nv = s[r] * alpha + u * ki[r];
-    __builtin_nontemporal_store(nv, S + (rg + RG * r) * CG + cg);
+    const float kr = krow(r);
+    float nv[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) nv[c] = fmaf(s[r].at(c), alpha, u[c] * kr);
+    StateVec<ST>::store(S + (size_t)(rg + RG * r) * D + VEC * cg, nv);
   }
+}
+
+template <typename InT, typename OutT, typename ST, int D>
+__global__ __launch_bounds__((step_threads<ST, D>())) void recurrent_step_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, ST* __restrict__ state,
+    OutT* __restrict__ o, int hqk, int hv, float scale) {
+  using L = StepLayout<ST, D>;
+  __shared__ StepRed<ST, D> red;
+
+  const int nh = blockIdx.x;  // n * hv + h
+  const int n = nh / hv, h = nh - (nh / hv) * hv;
+  const int m = h / (hv / hqk);
+  const int tid = threadIdx.x, cg = tid % L::CG, rg = tid / L::CG;
+
+  ST* S = state + (size_t)nh * D * D;
+  StateVec<ST> s[L::R];
+#pragma unroll
+  for (int r = 0; r < L::R; ++r) s[r].load(S + (size_t)(rg + L::RG * r) * D + L::VEC * cg);
+
+  const InT* qv = q + ((size_t)n * hqk + m) * D;
+  const InT* kv = k + ((size_t)n * hqk + m) * D;
+  float qi[L::R], ki[L::R];
+#pragma unroll
+  for (int r = 0; r < L::R; ++r) {
+    qi[r] = to_f32(qv[rg + L::RG * r]);
+    ki[r] = to_f32(kv[rg + L::RG * r]);
+  }
+  const InT* vv = v + (size_t)nh * D + L::VEC * cg;
+  head_step<ST, OutT, D>(
+      s, red, [&](int r) { return qi[r]; }, [&](int r) { return ki[r]; },
+      [&](int c) { return to_f32(vv[c]); }, expf(g[nh]), beta[nh], scale, S, o + (size_t)nh * D,
+      tid);
 }
 
 // ---- fused decode step from projected inputs --------------------------------------------
@@ -139,50 +210,44 @@ struct DecStepParams {
   const float* A_log;
   const float* dt_bias;
   float eps;
-  float* state;
+  void* state;
   void* o;
   int hqk, hv;
   float scale;
 };
 
-// At least 4 waves per SIMD (<= 128 VGPRs): two 512-thread workgroups per CU, as for the plain
-// step.
-template <typename InT, typename OutT, int D>
-__global__ __launch_bounds__((step_threads<D, D>())) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void decode_step_kernel(DecStepParams p) {
-  constexpr int NTH = step_threads<D, D>();
-  constexpr int NW = NTH / 64;
-  constexpr int CG = D / 4;    // float4 column groups per state row
-  constexpr int RG = NTH / CG;  // row groups
-  constexpr int R = D / RG;     // state rows per thread
-  constexpr int CGN = D / 8;    // front-end threads per channel head (8 channels each)
-  static_assert(NTH % 64 == 0 && 64 % CG == 0 && D % RG == 0 && R >= 1 && NTH % CGN == 0,
-                "tile shape");
+// fp32 state: at least 4 waves per SIMD (<= 128 VGPRs), two 512-thread workgroups per CU as for
+// the plain step. bf16 state (256-thread workgroups): at least 3 (<= 168 VGPRs, no spills).
+template <typename InT, typename OutT, typename ST, int D>
+__global__ __launch_bounds__((step_threads<ST, D>()))
+__attribute__((amdgpu_waves_per_eu(sizeof(ST) == 4 ? 4 : 3, 8))) void decode_step_kernel(
+    DecStepParams p) {
+  using L = StepLayout<ST, D>;
+  constexpr int NTH = L::NTH;
+  constexpr int CGN = D / 8;  // front-end threads per channel head (8 channels each)
+  static_assert(NTH % CGN == 0, "front-end lane groups");
 
   extern __shared__ float lds[];  // q[D] | k[D] | v[G][D] | alpha[G] | beta[G]
-  __shared__ f32x4 red_k[2][NW][CG];
-  __shared__ f32x4 red_q[2][NW][CG];
-  __shared__ float red_qk[2][NW];
+  __shared__ StepRed<ST, D> red[2];
 
   const int G = p.hv / p.hqk;
   const int nm = blockIdx.x;  // n * hqk + m
   const int n = nm / p.hqk, m = nm - n * p.hqk;
   const int h0 = m * G;
-  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, cg = tid % L::CG, rg = tid / L::CG;
   float* sq = lds;
   float* sk = lds + D;
   float* sv = lds + 2 * D;
   float* s_alpha = lds + (2 + G) * D;
   float* s_beta = s_alpha + G;
 
-  auto state_of = [&](int j) {
-    return reinterpret_cast<f32x4*>(p.state + ((size_t)n * p.hv + h0 + j) * D * D);
-  };
-  f32x4 s[R];
+  ST* const state = static_cast<ST*>(p.state);
+  auto state_of = [&](int j) { return state + ((size_t)n * p.hv + h0 + j) * D * D; };
+  StateVec<ST> s[L::R];
   {
-    const f32x4* S = state_of(0);
+    const ST* S = state_of(0);
 #pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = __builtin_nontemporal_load(S + (rg + RG * r) * CG + cg);
+    for (int r = 0; r < L::R; ++r) s[r].load(S + (size_t)(rg + L::RG * r) * D + L::VEC * cg);
   }
 
   // Front end. Channel head hb: 0 = q of head m, 1 = k of head m, 2 + j = v of V head h0 + j.
@@ -219,135 +284,110 @@ void decode_step_kernel(DecStepParams p) {
   __syncthreads();
 
   // q and k of the thread's rows are read from LDS where used (registers go to the state).
+  // The reduction buffers alternate between heads: one barrier per head.
   for (int j = 0; j < G; ++j) {
-    const int buf = j & 1;  // reductions double-buffered: one barrier per head
-    f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-    float pqk = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float qr = sq[rg + RG * r], kr = sk[rg + RG * r];
-      pk += s[r] * kr;
-      pq += s[r] * qr;
-      pqk += qr * kr;
-    }
-#pragma unroll
-    for (int off = CG; off < 64; off <<= 1) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        pk[c] += __shfl_xor(pk[c], off);
-        pq[c] += __shfl_xor(pq[c], off);
-      }
-      pqk += __shfl_xor(pqk, off);
-    }
-    if (lane < CG) {
-      red_k[buf][wave][lane] = pk;
-      red_q[buf][wave][lane] = pq;
-      if (lane == 0) red_qk[buf][wave] = pqk;
-    }
-    __syncthreads();
-    f32x4 skv = red_k[buf][0][cg], sqv = red_q[buf][0][cg];
-    float qk = red_qk[buf][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      skv += red_k[buf][w][cg];
-      sqv += red_q[buf][w][cg];
-      qk += red_qk[buf][w];
-    }
-    const float alpha = s_alpha[j], bt = s_beta[j];
-    f32x4 u;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) u[c] = bt * (sv[j * D + 4 * cg + c] - alpha * skv[c]);
-    if (rg == 0) {
-      OutT* ov = static_cast<OutT*>(p.o) + ((size_t)n * p.hv + h0 + j) * D + 4 * cg;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ov[c] = from_f32<OutT>(p.scale * (alpha * sqv[c] + qk * u[c]));
-    }
-    f32x4* S = state_of(j);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      f32x4 nv = s[r] * alpha + u * sk[rg + RG * r];
-      __builtin_nontemporal_store(nv, S + (rg + RG * r) * CG + cg);
-    }
+    ST* S = state_of(j);
+    const float* vj = sv + j * D + L::VEC * cg;
+    head_step<ST, OutT, D>(
+        s, red[j & 1], [&](int r) { return sq[rg + L::RG * r]; },
+        [&](int r) { return sk[rg + L::RG * r]; }, [&](int c) { return vj[c]; }, s_alpha[j],
+        s_beta[j], p.scale, S, static_cast<OutT*>(p.o) + ((size_t)n * p.hv + h0 + j) * D, tid);
     if (j + 1 < G) {  // the next head's rows into the same registers
-      const f32x4* Sn = state_of(j + 1);
+      const ST* Sn = state_of(j + 1);
 #pragma unroll
-      for (int r = 0; r < R; ++r) s[r] = __builtin_nontemporal_load(Sn + (rg + RG * r) * CG + cg);
+      for (int r = 0; r < L::R; ++r) s[r].load(Sn + (size_t)(rg + L::RG * r) * D + L::VEC * cg);
     }
   }
 }
 
-template <typename InT, typename OutT, int D>
+template <typename InT, typename OutT, typename ST, int D>
 hipError_t launch_decode_step_t(const gdn_shape_t& s, const DecStepParams& p,
                                 hipStream_t stream) {
   const unsigned blocks = (unsigned)s.num_seqs * (unsigned)s.num_qk_heads;
   if (blocks == 0) return hipSuccess;
   const int G = s.num_v_heads / s.num_qk_heads;
   const size_t lds = (size_t)((2 + G) * D + 2 * G) * sizeof(float);
-  hipLaunchKernelGGL((decode_step_kernel<InT, OutT, D>), dim3(blocks), dim3(step_threads<D, D>()),
-                     lds, stream, p);
+  hipLaunchKernelGGL((decode_step_kernel<InT, OutT, ST, D>), dim3(blocks),
+                     dim3(step_threads<ST, D>()), lds, stream, p);
   return hipGetLastError();
 }
 
-template <typename InT, typename OutT>
+template <typename InT, typename OutT, typename ST>
 hipError_t launch_decode_step_d(const gdn_shape_t& s, const DecStepParams& p,
                                 hipStream_t stream) {
   switch (s.head_dim_k) {
-    case 32: return launch_decode_step_t<InT, OutT, 32>(s, p, stream);
-    case 64: return launch_decode_step_t<InT, OutT, 64>(s, p, stream);
-    case 128: return launch_decode_step_t<InT, OutT, 128>(s, p, stream);
+    case 32: return launch_decode_step_t<InT, OutT, ST, 32>(s, p, stream);
+    case 64: return launch_decode_step_t<InT, OutT, ST, 64>(s, p, stream);
+    case 128: return launch_decode_step_t<InT, OutT, ST, 128>(s, p, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-template <typename InT, typename OutT, int D>
-hipError_t launch_step_t(const gdn_shape_t& s, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, float* state, void* o,
-                         hipStream_t stream) {
-  const unsigned blocks = (unsigned)s.num_seqs * (unsigned)s.num_v_heads;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_step_kernel<InT, OutT, D, D>), dim3(blocks),
-                     dim3(step_threads<D, D>()), 0, stream,
-                     static_cast<const InT*>(q), static_cast<const InT*>(k),
-                     static_cast<const InT*>(v), g, beta, state, static_cast<OutT*>(o),
-                     s.num_qk_heads, s.num_v_heads, s.scale);
-  return hipGetLastError();
 }
 
 template <typename InT, typename OutT>
+hipError_t launch_decode_step_s(const gdn_shape_t& s, const DecStepParams& p,
+                                hipStream_t stream) {
+  return s.state_dtype == GDN_DTYPE_BF16 ? launch_decode_step_d<InT, OutT, bf16>(s, p, stream)
+                                         : launch_decode_step_d<InT, OutT, float>(s, p, stream);
+}
+
+template <typename InT, typename OutT, typename ST, int D>
+hipError_t launch_step_t(const gdn_shape_t& s, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, void* state, void* o,
+                         hipStream_t stream) {
+  const unsigned blocks = (unsigned)s.num_seqs * (unsigned)s.num_v_heads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((recurrent_step_kernel<InT, OutT, ST, D>), dim3(blocks),
+                     dim3(step_threads<ST, D>()), 0, stream,
+                     static_cast<const InT*>(q), static_cast<const InT*>(k),
+                     static_cast<const InT*>(v), g, beta, static_cast<ST*>(state),
+                     static_cast<OutT*>(o), s.num_qk_heads, s.num_v_heads, s.scale);
+  return hipGetLastError();
+}
+
+template <typename InT, typename OutT, typename ST>
 hipError_t launch_step_d(const gdn_shape_t& s, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, float* state, void* o,
+                         const float* g, const float* beta, void* state, void* o,
                          hipStream_t stream) {
   switch (s.head_dim_k) {
-    case 32: return launch_step_t<InT, OutT, 32>(s, q, k, v, g, beta, state, o, stream);
-    case 64: return launch_step_t<InT, OutT, 64>(s, q, k, v, g, beta, state, o, stream);
-    case 128: return launch_step_t<InT, OutT, 128>(s, q, k, v, g, beta, state, o, stream);
+    case 32: return launch_step_t<InT, OutT, ST, 32>(s, q, k, v, g, beta, state, o, stream);
+    case 64: return launch_step_t<InT, OutT, ST, 64>(s, q, k, v, g, beta, state, o, stream);
+    case 128: return launch_step_t<InT, OutT, ST, 128>(s, q, k, v, g, beta, state, o, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename InT, typename OutT>
+hipError_t launch_step_s(const gdn_shape_t& s, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, void* state, void* o,
+                         hipStream_t stream) {
+  return s.state_dtype == GDN_DTYPE_BF16
+             ? launch_step_d<InT, OutT, bf16>(s, q, k, v, g, beta, state, o, stream)
+             : launch_step_d<InT, OutT, float>(s, q, k, v, g, beta, state, o, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_step(const gdn_shape_t& s, const void* x, void* window, const void* w,
                               const void* bias, const void* a, const void* b, const float* A_log,
-                              const float* dt_bias, float eps, float* state, void* o,
+                              const float* dt_bias, float eps, void* state, void* o,
                               hipStream_t stream) {
   DecStepParams p{x, window, w, bias, a, b, A_log, dt_bias, eps, state, o,
                   s.num_qk_heads, s.num_v_heads, s.scale};
   const bool in_bf16 = s.in_dtype == GDN_DTYPE_BF16, out_bf16 = s.out_dtype == GDN_DTYPE_BF16;
-  if (in_bf16 && out_bf16) return launch_decode_step_d<bf16, bf16>(s, p, stream);
-  if (in_bf16) return launch_decode_step_d<bf16, float>(s, p, stream);
-  if (out_bf16) return launch_decode_step_d<float, bf16>(s, p, stream);
-  return launch_decode_step_d<float, float>(s, p, stream);
+  if (in_bf16 && out_bf16) return launch_decode_step_s<bf16, bf16>(s, p, stream);
+  if (in_bf16) return launch_decode_step_s<bf16, float>(s, p, stream);
+  if (out_bf16) return launch_decode_step_s<float, bf16>(s, p, stream);
+  return launch_decode_step_s<float, float>(s, p, stream);
 }
 
 hipError_t launch_recurrent_step(const gdn_shape_t& s, const void* q, const void* k,
-                                 const void* v, const float* g, const float* beta, float* state,
+                                 const void* v, const float* g, const float* beta, void* state,
                                  void* o, hipStream_t stream) {
   const bool in_bf16 = s.qkv_dtype == GDN_DTYPE_BF16, out_bf16 = s.out_dtype == GDN_DTYPE_BF16;
-  if (in_bf16 && out_bf16) return launch_step_d<bf16, bf16>(s, q, k, v, g, beta, state, o, stream);
-  if (in_bf16) return launch_step_d<bf16, float>(s, q, k, v, g, beta, state, o, stream);
-  if (out_bf16) return launch_step_d<float, bf16>(s, q, k, v, g, beta, state, o, stream);
-  return launch_step_d<float, float>(s, q, k, v, g, beta, state, o, stream);
+  if (in_bf16 && out_bf16) return launch_step_s<bf16, bf16>(s, q, k, v, g, beta, state, o, stream);
+  if (in_bf16) return launch_step_s<bf16, float>(s, q, k, v, g, beta, state, o, stream);
+  if (out_bf16) return launch_step_s<float, bf16>(s, q, k, v, g, beta, state, o, stream);
+  return launch_step_s<float, float>(s, q, k, v, g, beta, state, o, stream);
 }
 
 }  // namespace gdn

@@ -13,11 +13,11 @@ hipError_t launch_chunk_intra(const gdn_shape_t& s, const int32_t* cu, const voi
                               hipStream_t stream);
 
 hipError_t launch_chunk_scan(const gdn_shape_t& s, const int32_t* cu, const void* q,
-                             const void* k, const void* v, const float* h0, void* o, float* ht,
+                             const void* k, const void* v, const void* h0, void* o, void* ht,
                              const void* ws, hipStream_t stream);
 
 hipError_t launch_recurrent_step(const gdn_shape_t& s, const void* q, const void* k,
-                                 const void* v, const float* g, const float* beta, float* state,
+                                 const void* v, const float* g, const float* beta, void* state,
                                  void* o, hipStream_t stream);
 
 hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x,
@@ -32,7 +32,7 @@ hipError_t launch_decode_prepare(const gdn_shape_t& s, const void* x, void* wind
 
 hipError_t launch_decode_step(const gdn_shape_t& s, const void* x, void* window, const void* w,
                               const void* bias, const void* a, const void* b, const float* A_log,
-                              const float* dt_bias, float eps, float* state, void* o,
+                              const float* dt_bias, float eps, void* state, void* o,
                               hipStream_t stream);
 
 hipError_t launch_gated_rmsnorm(const gdn_shape_t& s, const void* o, const void* z,

@@ -34,13 +34,26 @@ struct ScanParams {
   const void* q;
   const void* k;
   const void* v;
-  const float* h0;
+  const void* h0;  // initial states, fp32 or bf16 (state_bf16), or null
   void* o;
-  float* ht;
+  void* ht;  // final states, same dtype, or null
   const char* ws;
   int num_seqs, hqk, hv;
   float scale;
+  int state_bf16;
 };
+
+// Element i of a stored state (fp32, or bf16 read exactly) and the store of an fp32 value (bf16:
+// round to nearest even). The state dtype is uniform over the launch.
+__device__ __forceinline__ float state_load(const void* base, size_t i, int bf) {
+  return bf ? to_f32(static_cast<const bf16*>(base)[i]) : static_cast<const float*>(base)[i];
+}
+__device__ __forceinline__ void state_store(void* base, size_t i, float x, int bf) {
+  if (bf)
+    static_cast<bf16*>(base)[i] = from_f32<bf16>(x);
+  else
+    static_cast<float*>(base)[i] = x;
+}
 
 // d_k index of row m of state tile `it` (16 rows): tiles 2 kb and 2 kb + 1 interleave their
 // 4-row groups inside the 32 columns of block kb, so that the C fragments of the two tiles
@@ -387,7 +400,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   // Owned state blocks: kb = rg + RW * o; Hc[o][hf][r] = H[state_row(2 kb + hf, 4 grp + r)][col].
   f32x4 Hc[OWN][2];
   {
-    const float* H0 = p.h0 ? p.h0 + (size_t)nh * D * D : nullptr;
+    const size_t h0_base = (size_t)nh * D * D;
 #pragma unroll
     for (int o = 0; o < OWN; ++o) {
       const int kb = rg + RW * o;
@@ -395,8 +408,11 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          Hc[o][hf][r] = (H0 && kb < KB) ? H0[(size_t)state_row(2 * kb + hf, 4 * grp + r) * D + col]
-                                         : 0.f;
+          Hc[o][hf][r] =
+              (p.h0 && kb < KB)
+                  ? state_load(p.h0, h0_base + (size_t)state_row(2 * kb + hf, 4 * grp + r) * D + col,
+                               p.state_bf16)
+                  : 0.f;
       if constexpr (RW > 1) {
         if (kb < KB) {
           float x[8];
@@ -637,7 +653,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   lds_barrier();  // last chunk computed (the producers store its output rows)
 
   if (p.ht) {
-    float* HT = p.ht + (size_t)nh * D * D;
+    const size_t ht_base = (size_t)nh * D * D;
 #pragma unroll
     for (int o = 0; o < OWN; ++o) {
       const int kb = rg + RW * o;
@@ -646,7 +662,8 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            HT[(size_t)state_row(2 * kb + hf, 4 * grp + r) * D + col] = Hc[o][hf][r];
+            state_store(p.ht, ht_base + (size_t)state_row(2 * kb + hf, 4 * grp + r) * D + col,
+                        Hc[o][hf][r], p.state_bf16);
     }
   }
 }
@@ -706,10 +723,10 @@ hipError_t launch_scan_d(const gdn_shape_t& s, const ScanParams& p, hipStream_t 
 }  // namespace
 
 hipError_t launch_chunk_scan(const gdn_shape_t& s, const int32_t* cu, const void* q,
-                             const void* k, const void* v, const float* h0, void* o, float* ht,
+                             const void* k, const void* v, const void* h0, void* o, void* ht,
                              const void* ws, hipStream_t stream) {
   ScanParams p{cu, q, k, v, h0, o, ht, static_cast<const char*>(ws), s.num_seqs, s.num_qk_heads,
-               s.num_v_heads, s.scale};
+               s.num_v_heads, s.scale, s.state_dtype == GDN_DTYPE_BF16 ? 1 : 0};
   const bool out_bf = s.out_dtype == GDN_DTYPE_BF16;
   if (s.qkv_dtype == GDN_DTYPE_BF16)
     return out_bf ? launch_scan_d<Bf16Mode, bf16>(s, p, stream)

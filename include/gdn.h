@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 #define GDN_CHUNK 64 /* chunk length of the chunked prefill ([MoE report] §3.7 Step 2) */
 
 typedef enum {
@@ -64,6 +64,10 @@ typedef struct gdn_shape {
   int32_t in_dtype;     /* gdn_dtype_t of the front-end inputs (mixed_qkv, conv weight and */
                         /* bias, a, b); ignored by the core entry points.                  */
   float scale;          /* multiplies o; 1.0 for the plain rule o_t = S_t q_t              */
+  int32_t state_dtype;  /* gdn_dtype_t of every stored recurrent state (initial, final and */
+                        /* decode state). Inside a call the state is carried in fp32; a    */
+                        /* BF16 state is read exactly and stored as the round-to-nearest-  */
+                        /* even cast of the fp32 state, halving its bytes.                 */
 } gdn_shape_t;
 
 /*
@@ -104,17 +108,17 @@ size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
  * (q = k = v = 0, beta = 0, g = 0). The result equals the token recurrence up to rounding.
  *   q, k          [T][H_qk][d_k] qkv_dtype     v [T][H_v][d_v] qkv_dtype
  *   g, beta       [T][H_v] fp32
- *   initial_state [N][H_v][d_k][d_v] fp32, or NULL for zeros
+ *   initial_state [N][H_v][d_k][d_v] state_dtype, or NULL for zeros
  *   o (out)       [T][H_v][d_v] out_dtype
- *   final_state   [N][H_v][d_k][d_v] fp32 (out), or NULL; it may equal initial_state
+ *   final_state   [N][H_v][d_k][d_v] state_dtype (out), or NULL; it may equal initial_state
  *   workspace     >= gdn_chunk_forward_workspace_size(shape) bytes, 256-byte aligned,
  *                 caller-owned scratch; its contents on entry do not matter.
  * It runs gdn_chunk_intra then gdn_chunk_scan on `stream`.
  */
 gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                                const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, const float* initial_state, void* o,
-                               float* final_state, void* workspace, size_t workspace_bytes,
+                               const float* beta, const void* initial_state, void* o,
+                               void* final_state, void* workspace, size_t workspace_bytes,
                                void* stream);
 
 /*
@@ -131,7 +135,7 @@ gdn_status_t gdn_chunk_intra(const gdn_shape_t* shape, const int32_t* cu_seqlens
                              void* workspace, size_t workspace_bytes, void* stream);
 gdn_status_t gdn_chunk_scan(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                             const void* q, const void* k, const void* v,
-                            const float* initial_state, void* o, float* final_state,
+                            const void* initial_state, void* o, void* final_state,
                             const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -140,12 +144,13 @@ gdn_status_t gdn_chunk_scan(const gdn_shape_t* shape, const int32_t* cu_seqlens,
  * updated once and written back in place). Requires total_tokens == num_seqs.
  *   q, k  [N][H_qk][d_k] qkv_dtype     v [N][H_v][d_v] qkv_dtype
  *   g, beta [N][H_v] fp32
- *   state [N][H_v][d_k][d_v] fp32, read and overwritten with the new state
+ *   state [N][H_v][d_k][d_v] state_dtype, read and overwritten with the new state (16-byte
+ *         aligned)
  *   o (out) [N][H_v][d_v] out_dtype
  */
 gdn_status_t gdn_recurrent_step(const gdn_shape_t* shape, const void* q, const void* k,
                                 const void* v, const float* g, const float* beta,
-                                float* state, void* o, void* stream);
+                                void* state, void* o, void* stream);
 
 /*
  * gdn_decode_prepare -- front end of one decode token per sequence with a cached convolution
@@ -183,7 +188,7 @@ gdn_status_t gdn_decode_prepare(const gdn_shape_t* shape, const void* mixed_qkv,
  * holds the q, k and G = H_v / H_qk v rows of a QK head, so (2 + G) * d_v + 2 G floats must fit
  * in 64 KiB (GDN_ERR_UNSUPPORTED otherwise).
  *   mixed_qkv, conv_window, conv_weight, conv_bias, a, b, A_log, dt_bias: as gdn_decode_prepare
- *   state [N][H_v][d_k][d_v] fp32, updated in place      o (out) [N][H_v][d_v] out_dtype
+ *   state [N][H_v][d_k][d_v] state_dtype, updated in place    o (out) [N][H_v][d_v] out_dtype
  * mixed_qkv, conv_window, conv_weight, conv_bias (when given) and state must be 16-byte aligned
  * (GDN_ERR_INVALID_ARGUMENT otherwise). The window and the state of a sequence must not be
  * shared with another sequence of the same call.
@@ -191,7 +196,7 @@ gdn_status_t gdn_decode_prepare(const gdn_shape_t* shape, const void* mixed_qkv,
 gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* mixed_qkv, void* conv_window,
                              const void* conv_weight, const void* conv_bias, const void* a,
                              const void* b, const float* A_log, const float* dt_bias,
-                             float l2norm_eps, float* state, void* o, void* stream);
+                             float l2norm_eps, void* state, void* o, void* stream);
 
 /*
  * gdn_gated_rmsnorm -- output gate of the layer ([xiwon notes] "Qwen3_5MoeGatedDeltaNet",

@@ -36,7 +36,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    declared = int(re.search(r"#define GDN_ABI_VERSION (\d+)", hdr).group(1))
+    assert lib.gdn_abi_version() == declared == gdn.ABI_VERSION
     for code in range(5):
         assert lib.gdn_status_string(code).startswith(b"GDN_")
 
@@ -108,6 +110,8 @@ def test_recurrent_step_validation(lib):
     a = list(args)
     a[5] = ctypes.c_void_p((1 << 20) + 4)  # state must be 16-byte aligned
     assert lib.gdn_recurrent_step(ctypes.byref(s), *a, None) == INVALID
+    assert lib.gdn_recurrent_step(ctypes.byref(_shape(total_tokens=2, state_dtype=7)), *args,
+                                  None) == INVALID
     assert lib.gdn_recurrent_step(ctypes.byref(_shape(total_tokens=2, head_dim_k=48,
                                                       head_dim_v=48)), *args, None) == UNSUPPORTED
 
