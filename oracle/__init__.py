@@ -57,6 +57,10 @@ def _load():
     lib.gdn_oracle_decode_prepare.restype = ctypes.c_int
     lib.gdn_oracle_decode_prepare.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp,
                                               dp, dp, ctypes.c_double, dp, dp, dp, dp, dp]
+    lib.gdn_oracle_recurrent_backward.restype = ctypes.c_int
+    lib.gdn_oracle_recurrent_backward.argtypes = [i64, lp, i64, i64, i64, i64, dp, dp, dp, dp,
+                                                  dp, dp, ctypes.c_double, dp, dp, dp, dp, dp,
+                                                  dp, dp, dp]
     lib.gdn_oracle_num_threads.restype = ctypes.c_int
     lib.gdn_oracle_num_threads.argtypes = []
     _lib = lib
@@ -107,6 +111,38 @@ def recurrent(q, k, v, g, beta, cu_seqlens, initial_state=None, scale=1.0,
     if rc != 0:
         raise ValueError("gdn_oracle_recurrent rejected its arguments")
     return o, ht
+
+
+def recurrent_backward(q, k, v, g, beta, cu_seqlens, dout, initial_state=None, dht=None,
+                       scale=1.0):
+    """Gradients of sum(o * dout) + sum(ht * dht) through the token recurrence, float64.
+
+    Returns (dq, dk [T, Hqk, dk], dv [T, Hv, dv], dg, dbeta [T, Hv], dh0 [N, Hv, dk, dv]).
+    """
+    lib = _load()
+    q, k, v, g, beta, dout = (_f64(a) for a in (q, k, v, g, beta, dout))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    n = cu.shape[0] - 1
+    assert dout.shape == (T, hv, dv) and int(cu[-1]) == T
+    h0, dh = _f64(initial_state), _f64(dht)
+    for st in (h0, dh):
+        if st is not None:
+            assert st.shape == (n, hv, dk, dv)
+    dq = np.zeros((T, hqk, dk))
+    dkk = np.zeros((T, hqk, dk))
+    dvv = np.zeros((T, hv, dv))
+    dg = np.zeros((T, hv))
+    dbeta = np.zeros((T, hv))
+    dh0 = np.zeros((n, hv, dk, dv))
+    rc = lib.gdn_oracle_recurrent_backward(
+        n, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), hqk, hv, dk, dv, _ptr(q), _ptr(k),
+        _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), float(scale), _ptr(dout), _ptr(dh), _ptr(dq),
+        _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(dbeta), _ptr(dh0))
+    if rc != 0:
+        raise ValueError("gdn_oracle_recurrent_backward rejected its arguments")
+    return dq, dkk, dvv, dg, dbeta, dh0
 
 
 def prepare(mixed_qkv, conv_weight, a, b, A_log, dt_bias, cu_seqlens, num_qk_heads,

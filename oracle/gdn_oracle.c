@@ -11,7 +11,8 @@
  * WY form at several chunk sizes, the spec matrix form, beta = 0 decay,
  * exact retrieval with orthonormal keys, exact rational arithmetic in the
  * scalar case, numpy.convolve for the conv, and library sigmoid / softplus
- * for the gates. Nothing here is "parity unpinned".
+ * for the gates; the reverse mode against central finite differences of the
+ * forward recurrence. Nothing here is "parity unpinned".
  *
  * Page citations are listed in gdn_oracle.h.
  */
@@ -267,6 +268,155 @@ int gdn_oracle_decode_prepare(int64_t num_seqs, int64_t hqk, int64_t hv, int64_t
       g[n * hv + h] = -exp(A_log[h]) * softplus(a[n * hv + h] + dt_bias[h]);
     }
     free(y);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ---- reverse mode of the token recurrence --------------------------------------------
+ * Gradients of L = sum(o * dout) + sum(ht * dht) with respect to every input of
+ * gdn_oracle_recurrent, by backpropagation through the tokens in reverse order (the
+ * recurrence itself is the definition: [MoE report] §3.3 stage 3; the chunked training form
+ * of [MoE report] §3.7 and the chunk-wise training the pages mention compute the same
+ * gradients). Per token, with Ht~ = alpha H_{t-1}, w = Ht~^T k, u = beta (v - w),
+ * H_t = Ht~ + k u^T and o = scale H_t^T q, given dH = dL/dH_t:
+ *   dH += scale q do^T;  dq += scale H_t do;
+ *   du = dH^T k;  dk += dH u;  dbeta = du . (v - w);  dv = beta du;
+ *   dw = -beta du;  dHt~ = dH + k dw^T;  dk += Ht~ dw;
+ *   dg = alpha <dHt~, H_{t-1}>;  dL/dH_{t-1} = alpha dHt~.
+ * States are recomputed from checkpoints every kSeg tokens (memory stays small). */
+enum { kSeg = 64 };
+
+static void step_forward(int64_t dk, int64_t dv, const double* Hp, double* Hn,
+                         const double* kt, const double* vt, double alpha, double bt) {
+  for (int64_t j = 0; j < dv; ++j) {
+    double w = 0.0;
+    for (int64_t i = 0; i < dk; ++i) w += alpha * Hp[i * dv + j] * kt[i];
+    const double u = bt * (vt[j] - w);
+    for (int64_t i = 0; i < dk; ++i) Hn[i * dv + j] = alpha * Hp[i * dv + j] + kt[i] * u;
+  }
+}
+
+int gdn_oracle_recurrent_backward(int64_t num_seqs, const int64_t* cu, int64_t hqk, int64_t hv,
+                                  int64_t dk, int64_t dv, const double* q, const double* k,
+                                  const double* v, const double* g, const double* beta,
+                                  const double* h0, double scale, const double* dout,
+                                  const double* dht, double* dq, double* dkk, double* dvv,
+                                  double* dg, double* dbeta, double* dh0) {
+  if (check_cu(num_seqs, cu) != 0) return -1;
+  if (hqk <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || hv % hqk != 0) return -1;
+  const int64_t group = hv / hqk;
+  const int64_t T = cu[num_seqs];
+  const int64_t S = dk * dv;
+  memset(dq, 0, sizeof(double) * (size_t)(T * hqk * dk));
+  memset(dkk, 0, sizeof(double) * (size_t)(T * hqk * dk));
+  int bad = 0;
+
+  /* One unit = (sequence, QK head): its V heads add into the same dq / dk rows. */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t unit = 0; unit < num_seqs * hqk; ++unit) {
+    const int64_t n = unit / hqk, m = unit % hqk;
+    const int64_t t0 = cu[n], L = cu[n + 1] - cu[n];
+    const int64_t nseg = (L + kSeg - 1) / kSeg;
+    double* ckpt = (double*)malloc(sizeof(double) * (size_t)((nseg > 0 ? nseg : 1) * S));
+    double* Hs = (double*)malloc(sizeof(double) * (size_t)((kSeg + 1) * S));
+    double* dH = (double*)malloc(sizeof(double) * (size_t)S);
+    double* dHt = (double*)malloc(sizeof(double) * (size_t)S);
+    double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* w = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* du = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!ckpt || !Hs || !dH || !dHt || !u || !w || !du) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+      for (int64_t h = m * group; h < (m + 1) * group; ++h) {
+        const int64_t nh = n * hv + h;
+        /* forward: checkpoint the state at the start of every segment */
+        double* H = Hs;
+        if (h0 != NULL)
+          memcpy(H, h0 + nh * S, sizeof(double) * (size_t)S);
+        else
+          memset(H, 0, sizeof(double) * (size_t)S);
+        for (int64_t i = 0; i < L; ++i) {
+          const int64_t t = t0 + i;
+          if (i % kSeg == 0) memcpy(ckpt + (i / kSeg) * S, H, sizeof(double) * (size_t)S);
+          step_forward(dk, dv, H, Hs + S, k + (t * hqk + m) * dk, v + (t * hv + h) * dv,
+                       exp(g[t * hv + h]), beta[t * hv + h]);
+          memcpy(H, Hs + S, sizeof(double) * (size_t)S);
+        }
+        if (dht != NULL)
+          memcpy(dH, dht + nh * S, sizeof(double) * (size_t)S);
+        else
+          memset(dH, 0, sizeof(double) * (size_t)S);
+        for (int64_t sg = nseg - 1; sg >= 0; --sg) {
+          const int64_t i0 = sg * kSeg, len = (L - i0 < kSeg) ? L - i0 : kSeg;
+          memcpy(Hs, ckpt + sg * S, sizeof(double) * (size_t)S);
+          for (int64_t i = 0; i < len; ++i) {
+            const int64_t t = t0 + i0 + i;
+            step_forward(dk, dv, Hs + i * S, Hs + (i + 1) * S, k + (t * hqk + m) * dk,
+                         v + (t * hv + h) * dv, exp(g[t * hv + h]), beta[t * hv + h]);
+          }
+          for (int64_t i = len - 1; i >= 0; --i) {
+            const int64_t t = t0 + i0 + i;
+            const double* Hp = Hs + i * S;       /* H_{t-1} */
+            const double* Hn = Hs + (i + 1) * S; /* H_t */
+            const double* qt = q + (t * hqk + m) * dk;
+            const double* kt = k + (t * hqk + m) * dk;
+            const double* vt = v + (t * hv + h) * dv;
+            const double* dot = dout + (t * hv + h) * dv;
+            double* dqt = dq + (t * hqk + m) * dk;
+            double* dkt = dkk + (t * hqk + m) * dk;
+            const double alpha = exp(g[t * hv + h]), bt = beta[t * hv + h];
+            /* output: o = scale H_t^T q */
+            for (int64_t a = 0; a < dk; ++a) {
+              double acc = 0.0;
+              for (int64_t j = 0; j < dv; ++j) {
+                dH[a * dv + j] += scale * qt[a] * dot[j];
+                acc += Hn[a * dv + j] * dot[j];
+              }
+              dqt[a] += scale * acc;
+            }
+            /* write: H_t = alpha H_{t-1} + k u^T, u = beta (v - w), w = alpha H_{t-1}^T k */
+            double dbt = 0.0;
+            for (int64_t j = 0; j < dv; ++j) {
+              double wj = 0.0, duj = 0.0;
+              for (int64_t a = 0; a < dk; ++a) {
+                wj += alpha * Hp[a * dv + j] * kt[a];
+                duj += dH[a * dv + j] * kt[a];
+              }
+              w[j] = wj;
+              u[j] = bt * (vt[j] - wj);
+              du[j] = duj;
+              dbt += duj * (vt[j] - wj);
+              dvv[(t * hv + h) * dv + j] = bt * duj;
+            }
+            dbeta[t * hv + h] = dbt;
+            double dalpha = 0.0;
+            for (int64_t a = 0; a < dk; ++a) {
+              double acc_u = 0.0, acc_w = 0.0;
+              for (int64_t j = 0; j < dv; ++j) {
+                const double dwj = -bt * du[j];
+                acc_u += dH[a * dv + j] * u[j];
+                acc_w += alpha * Hp[a * dv + j] * dwj;
+                const double dtil = dH[a * dv + j] + kt[a] * dwj; /* dL/dHt~ */
+                dHt[a * dv + j] = dtil;
+                dalpha += dtil * Hp[a * dv + j];
+              }
+              dkt[a] += acc_u + acc_w;
+            }
+            dg[t * hv + h] = alpha * dalpha;
+            for (int64_t e = 0; e < S; ++e) dH[e] = alpha * dHt[e];
+          }
+        }
+        if (dh0 != NULL) memcpy(dh0 + nh * S, dH, sizeof(double) * (size_t)S);
+      }
+    }
+    free(ckpt);
+    free(Hs);
+    free(dH);
+    free(dHt);
+    free(u);
+    free(w);
+    free(du);
   }
   return bad ? -1 : 0;
 }

@@ -67,6 +67,21 @@ int gdn_oracle_decode_prepare(int64_t num_seqs, int64_t hqk, int64_t hv, int64_t
                               const double* A_log, const double* dt_bias, double l2_eps,
                               double* q, double* k, double* v, double* g, double* beta);
 
+/* Reverse mode of gdn_oracle_recurrent: gradients of L = sum(o * dout) + sum(ht * dht)
+ * (dht may be NULL: no final-state term) by backpropagation through the tokens.
+ *   dout : [T][hv][dv]      dht : [N][hv][dk][dv] or NULL
+ *   out dq, dk : [T][hqk][dk] (summed over the V heads that read each QK head)
+ *       dv : [T][hv][dv]    dg, dbeta : [T][hv]    dh0 : [N][hv][dk][dv] or NULL
+ * The other arguments are those of gdn_oracle_recurrent. */
+int gdn_oracle_recurrent_backward(int64_t num_seqs, const int64_t* cu_seqlens,
+                                  int64_t hqk, int64_t hv, int64_t dk, int64_t dv,
+                                  const double* q, const double* k, const double* v,
+                                  const double* g, const double* beta,
+                                  const double* h0, double scale,
+                                  const double* dout, const double* dht,
+                                  double* dq, double* dkk, double* dvv,
+                                  double* dg, double* dbeta, double* dh0);
+
 /* Number of OpenMP threads the oracle runs on (for reporting). */
 int gdn_oracle_num_threads(void);
 
