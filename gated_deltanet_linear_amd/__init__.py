@@ -76,6 +76,11 @@ def _load():
     lib.gdn_chunk_intra.argtypes = [sp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.gdn_chunk_scan.restype = ctypes.c_int
     lib.gdn_chunk_scan.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunk_backward_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_backward_workspace_size.argtypes = [sp]
+    lib.gdn_chunk_backward.restype = ctypes.c_int
+    lib.gdn_chunk_backward.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, ctypes.c_size_t, _P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.gdn_decode_prepare.restype = ctypes.c_int
@@ -242,6 +247,43 @@ def chunk_scan(q, k, v, g, beta, cu_seqlens, workspace, initial_state=None, o=No
                                 workspace.numel(), _stream())
     _check(rc, "gdn_chunk_scan")
     return o, final_state
+
+
+def chunk_backward(q, k, v, g, beta, cu_seqlens, dout, initial_state=None, dht=None, scale=1.0,
+                   workspace=None, state_dtype=None):
+    """Gradients of sum(o * dout) + sum(final_state * dht) for the chunked prefill with these
+    inputs. Returns (dq, dk [T, H_qk, d_k], dv [T, H_v, d_v] in the q/k/v dtype, dg, dbeta
+    [T, H_v] fp32, dh0 [N, H_v, d_k, d_v] in the state dtype)."""
+    hv, dv_ = _v_shape(v, q)
+    _dev(dout, "dout")
+    sd = _state_dtype(initial_state, dht, default=state_dtype)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv_, scale, dout.dtype, sd)
+    T, hqk, dk_ = s.total_tokens, s.num_qk_heads, s.head_dim_k
+    if dout.shape != (T, hv, dv_):
+        raise GdnError("dout must be [T, H_v, d_v]")
+    for t, name in ((initial_state, "initial_state"), (dht, "dht")):
+        if t is not None:
+            _dev(t, name, sd)
+            if t.shape != (n, hv, dk_, dv_):
+                raise GdnError(f"{name} must be [N, H_v, d_k, d_v]")
+    lib = _load()
+    nbytes = int(lib.gdn_chunk_backward_workspace_size(ctypes.byref(s)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    dev = q.device
+    dq = torch.empty((T, hqk, dk_), dtype=q.dtype, device=dev)
+    dk = torch.empty((T, hqk, dk_), dtype=q.dtype, device=dev)
+    dv = torch.empty((T, hv, dv_), dtype=q.dtype, device=dev)
+    dg = torch.empty((T, hv), dtype=torch.float32, device=dev)
+    dbeta = torch.empty((T, hv), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((n, hv, dk_, dv_), dtype=sd, device=dev)
+    rc = lib.gdn_chunk_backward(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout), _ptr(dht),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                _ptr(workspace), workspace.numel(), _stream())
+    _check(rc, "gdn_chunk_backward")
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def recurrent_step(q, k, v, g, beta, state, scale=1.0, out_dtype=None, o=None) -> torch.Tensor:

@@ -123,6 +123,29 @@ gdn_status_t gdn_chunk_forward(const gdn_shape_t* s, const int32_t* cu, const vo
   return from_hip(gdn::launch_chunk_scan(*s, cu, q, k, v, h0, o, ht, ws, hs));
 }
 
+size_t gdn_chunk_backward_workspace_size(const gdn_shape_t* s) {
+  if (check_shape(s) != GDN_OK) return 0;
+  return (size_t)gdn::chunk_backward_workspace_floats(*s) * sizeof(float);
+}
+
+gdn_status_t gdn_chunk_backward(const gdn_shape_t* s, const int32_t* cu, const void* q,
+                                const void* k, const void* v, const float* g, const float* beta,
+                                const void* h0, const void* dout, const void* dht, void* dq,
+                                void* dk, void* dv, float* dg, float* dbeta, void* dh0,
+                                void* ws, size_t ws_bytes, void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (!cu || !ws) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens > 0 &&
+      (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+    return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(ws, 256)) return GDN_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < gdn_chunk_backward_workspace_size(s)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(gdn::launch_chunk_backward(*s, cu, q, k, v, g, beta, h0, dout, dht, dq, dk, dv,
+                                             dg, dbeta, dh0, ws,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 gdn_status_t gdn_recurrent_step(const gdn_shape_t* s, const void* q, const void* k,
                                 const void* v, const float* g, const float* beta, void* state,
                                 void* o, void* stream) {

@@ -1,0 +1,616 @@
+// gdn_backward.hip -- gradients of the chunked gated delta rule (training backward pass):
+// dq, dk, dv, dg, dbeta and the initial-state gradient from the output gradient and, optionally,
+// the final-state gradient ([MoE report] §3.7, the chunked form trained chunk by chunk; the token
+// recurrence of §3.3 stage 3 is the definition it differentiates).
+//
+// Chunk form (C = 64 rows, b = in-chunk cumsum of g, gamma = e^b, B = b of the chunk's last
+// token, gamma_C = e^B, delta = e^{B - b}, Gamma_tj = e^{b_t - b_j}):
+//   Y  = V - diag(gamma) K H              V' = T diag(beta) Y,   T = (I + diag(beta) At)^-1
+//   O  = scale (diag(gamma) Q H + P V')   P = lower-incl(Q K^T o Gamma), At = lower(K K^T o Gamma)
+//   H' = gamma_C H + K^T diag(delta) V'
+// Reverse mode per chunk, with dO^ = scale dO and dH' the gradient of the chunk's end state:
+//   dV' = P^T dO^ + diag(delta) K dH'      Z = T^T dV'      dY = dV = diag(beta) Z
+//   dH  = gamma_C dH' + Q^T diag(gamma) dO^ - K^T diag(gamma) dY        (the previous chunk's dH')
+//   dQ  = diag(gamma) dO^ H^T + (dP o Gamma) K,                         dP = lower-incl(dO^ V'^T)
+//   dK  = diag(delta) V' dH'^T - diag(gamma) dY H^T + (dP o Gamma)^T Q + (dS + dS^T) K,
+//         dA = -Z V'^T (strictly lower),  dS = dA o diag(beta) Gamma
+//   dbeta_t = <Y_t, Z_t> + sum_j dA_tj At_tj
+//   dg_s (the reverse in-chunk cumsum of db, written without cancelling terms):
+//        sum_{t >= s} gamma_t (<Q_t, (dO^ H^T)_t> - <K_t, (dY H^T)_t>)
+//      + sum_{t < s} delta_t <K_t, (V' dH'^T)_t> + gamma_C <H, dH'>
+//      + sum_{t >= s, j < s} E_tj,          E = dP o P + dA o diag(beta) At
+//   (db_t itself has E's row sum minus its column sum and a -delta_t term balanced by the last
+//   token's dB; summed in this form, the parts that cancel are never formed: plain fp32 suffix
+//   sums of db lost ~1e-4 of dg's RMS).
+//
+// Four launches, all fp32 (fp32 MFMA 16x16x4; bf16 inputs widened exactly):
+//   bwd_intra  one workgroup per (chunk slot, V head): b, T (forward substitution), P, At.
+//   bwd_scan<false>  per (sequence, V head, 16-column tile): the states H at every chunk start
+//              (from the initial state), and Y, V' of every token.
+//   bwd_scan<true>   same layout, chunks in reverse: dH' of every chunk, Z, dv, dh0.
+//   bwd_grads  one workgroup per (chunk slot, QK head), its G V heads in turn: dq, dk (summed
+//              over the G heads), dg, dbeta.
+// Every product is formed by tile_mma, one 16 x 16 output tile per call, its operands read
+// through accessors from LDS or global memory (the state matrices stay in global memory, read
+// along their contiguous axis).
+#include "gdn_device.hpp"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kC = kChunk;  // 64
+constexpr int kRecFloats = 3 * kC * kC + 2 * kC;  // T | P | At (fp32) | b (64 fp64)
+
+// In-chunk cumsum b of the log-decays, in fp64: a fp32 b of a chunk with strong decay (|g| up to
+// ~40 per token, |b| up to ~2500) loses ~1e-4 of Gamma_tj = e^{b_t - b_j} where b_t - b_j is
+// small, and the gate gradient lost as much; from fp64 values the differences are exact enough.
+__device__ __forceinline__ const double* rec_b(const float* rec) {
+  return reinterpret_cast<const double*>(rec + 3 * kC * kC);
+}
+
+__device__ __forceinline__ double wave_inclusive_scan_f64(double x, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+struct BwdParams {
+  const int32_t* cu;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const void* h0;    // initial states (state dtype) or null
+  const void* dout;  // [T][hv][d] out dtype
+  const void* dht;   // final-state gradient (state dtype) or null
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  void* dh0;         // initial-state gradient (state dtype) or null
+  float* rec;        // [slots][hv] records of kRecFloats
+  float* hs;         // [slots][hv][d][d] state at every chunk start
+  float* dhs;        // [slots][hv][d][d] gradient of every chunk's end state
+  float* ys;         // [T][hv][d] Y
+  float* vp;         // [T][hv][d] V'
+  float* zs;         // [T][hv][d] Z
+  int num_seqs, T, hqk, hv, num_slots;
+  float scale;
+  int state_bf16;
+};
+
+__device__ __forceinline__ float ld_state(const void* base, size_t i, int bf) {
+  return bf ? to_f32(static_cast<const bf16*>(base)[i]) : static_cast<const float*>(base)[i];
+}
+__device__ __forceinline__ void st_state(void* base, size_t i, float x, int bf) {
+  if (bf)
+    static_cast<bf16*>(base)[i] = from_f32<bf16>(x);
+  else
+    static_cast<float*>(base)[i] = x;
+}
+
+// acc += A[0..16)[0..K) * B[0..K)[0..16) for the calling wave; a(i, kk) and b(kk, j) return the
+// elements (i, j in 0..15, kk the depth index). Result: lane (idx, grp) holds rows 4 grp + r,
+// column idx. K is a multiple of 32.
+template <typename FA, typename FB>
+__device__ __forceinline__ f32x4 tile_mma(FA a, FB b, int K, f32x4 acc) {
+  const int lane = threadIdx.x & 63, idx = lane & 15, grp = lane >> 4;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f32x8 av, bv;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int kk = k0 + kslot(grp, s);
+      av[s] = a(idx, kk);
+      bv[s] = b(kk, idx);
+    }
+    acc = mma32(av, bv, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// (sequence, first token, valid rows) of chunk slot `slot`; false for an unused slot.
+__device__ __forceinline__ bool slot_chunk(const BwdParams& p, int slot, int& n, int& t0, int& L) {
+  n = slot_to_seq(p.cu, p.num_seqs, slot);
+  t0 = p.cu[n] + kC * (slot - slot_base(p.cu, n));
+  const int tend = p.cu[n + 1];
+  L = min(kC, tend - t0);
+  return t0 < tend;
+}
+
+// ---- bwd_intra ------------------------------------------------------------------------------
+template <typename InT, int D>
+__global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
+  constexpr int KP = D + 4;  // padded row of the staged q / k rows
+  __shared__ float sK[kC][KP];
+  __shared__ float sQ[kC][KP];
+  __shared__ float sA[kC][kC + 1];
+  __shared__ float sT[kC][kC + 1];
+  __shared__ double sb[kC];
+  __shared__ float sbeta[kC];
+
+  const int slot = blockIdx.x / p.hv, h = blockIdx.x % p.hv;
+  const int G = p.hv / p.hqk, m = h / G;
+  int n, t0, L;
+  if (slot >= p.num_slots || !slot_chunk(p, slot, n, t0, L)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int idx = lane & 15, grp = lane >> 4;
+  float* rec = p.rec + ((size_t)slot * p.hv + h) * kRecFloats;
+
+  const InT* Q = static_cast<const InT*>(p.q);
+  const InT* K = static_cast<const InT*>(p.k);
+  for (int e = tid; e < kC * D; e += 256) {
+    const int i = e / D, c = e % D;
+    const bool ok = i < L;
+    sK[i][c] = ok ? to_f32(K[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
+    sQ[i][c] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
+  }
+  if (wave == 0) {  // b = inclusive cumsum of g (0 past the end: identity steps)
+    const double gi = lane < L ? (double)p.g[(size_t)(t0 + lane) * p.hv + h] : 0.0;
+    const double bi = wave_inclusive_scan_f64(gi, lane);
+    sb[lane] = bi;
+    reinterpret_cast<double*>(rec + 3 * kC * kC)[lane] = bi;
+    sbeta[lane] = lane < L ? p.beta[(size_t)(t0 + lane) * p.hv + h] : 0.f;
+  }
+  __syncthreads();
+
+  // wave w: rows 16 w .. 16 w + 15 of S = K K^T and Q K^T
+  for (int ct = 0; ct < 4; ++ct) {
+    const f32x4 s = tile_mma([&](int i, int kk) { return sK[16 * wave + i][kk]; },
+                             [&](int kk, int j) { return sK[16 * ct + j][kk]; }, D, zero4());
+    const f32x4 qk = tile_mma([&](int i, int kk) { return sQ[16 * wave + i][kk]; },
+                              [&](int kk, int j) { return sK[16 * ct + j][kk]; }, D, zero4());
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * grp + r, j = 16 * ct + idx;
+      const float gam = t >= j ? expf((float)(sb[t] - sb[j])) : 0.f;
+      const float pv = t >= j ? qk[r] * gam : 0.f;
+      const float at = t > j ? s[r] * gam : 0.f;
+      rec[kC * kC + t * kC + j] = pv;
+      rec[2 * kC * kC + t * kC + j] = at;
+      sA[t][j] = sbeta[t] * at;  // A = diag(beta) At
+    }
+  }
+  __syncthreads();
+
+  // T = (I + A)^-1 by forward substitution, one row per step: T_tj = [t == j] - sum_{j<=m<t}
+  // A_tm T_mj (thread j of wave 0 owns column j; the other waves wait at the barriers).
+  for (int t = 0; t < kC; ++t) {
+    if (tid < kC) {
+      const int j = tid;
+      float x = t == j ? 1.f : 0.f;
+      if (j < t)
+        for (int mm = j; mm < t; ++mm) x -= sA[t][mm] * sT[mm][j];
+      sT[t][j] = j <= t ? x : 0.f;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < kC * kC; e += 256) rec[e] = sT[e / kC][e % kC];
+}
+
+// ---- bwd_scan: states forward, state gradients in reverse ---------------------------------
+template <typename InT, typename OT, int D, bool REV>
+__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
+  constexpr int KP = D + 4;
+  constexpr int NB = D / 16;  // column tiles per head
+  __shared__ float sK[kC][KP];
+  __shared__ float sQ[REV ? kC : 1][KP];
+  __shared__ float sT[kC][kC + 1];
+  __shared__ float sP[REV ? kC : 1][kC + 1];
+  __shared__ float sX[D][17];      // the carried d_k x 16 tile (state or state gradient)
+  __shared__ float sIn[kC][17];    // V (forward) or dO^ (reverse) columns of the tile
+  __shared__ float sW[kC][17];     // Y (forward) or dV' (reverse)
+  __shared__ float sZ[kC][17];     // V' (forward) or Z (reverse)
+  __shared__ float sgam[kC], sdel[kC], sbeta[kC];
+  __shared__ float sgc;
+
+  const int jt = blockIdx.x % NB, nh = blockIdx.x / NB;
+  const int n = nh / p.hv, h = nh % p.hv;
+  const int G = p.hv / p.hqk, m = h / G;
+  const int j0 = 16 * jt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int idx = lane & 15, grp = lane >> 4;
+  const int seq0 = p.cu[n], len = p.cu[n + 1] - seq0;
+  const int nch = (len + kC - 1) / kC;
+  const int sb0 = slot_base(p.cu, n);
+  const size_t st_base = (size_t)nh * D * D;
+
+  // carried tile: the initial state (forward) or the final-state gradient (reverse)
+  const void* init = REV ? p.dht : p.h0;
+  for (int e = tid; e < D * 16; e += 256) {
+    const int r = e / 16, c = e % 16;
+    sX[r][c] = init ? ld_state(init, st_base + (size_t)r * D + j0 + c, p.state_bf16) : 0.f;
+  }
+  const InT* Q = static_cast<const InT*>(p.q);
+  const InT* K = static_cast<const InT*>(p.k);
+  const InT* V = static_cast<const InT*>(p.v);
+  const OT* dO = static_cast<const OT*>(p.dout);
+  __syncthreads();
+
+  for (int ci = 0; ci < nch; ++ci) {
+    const int c = REV ? nch - 1 - ci : ci;
+    const int slot = sb0 + c, t0 = seq0 + kC * c, L = min(kC, len - kC * c);
+    const float* rec = p.rec + ((size_t)slot * p.hv + h) * kRecFloats;
+    float* xs = (REV ? p.dhs : p.hs) + ((size_t)slot * p.hv + h) * D * D;
+    for (int e = tid; e < D * 16; e += 256) {  // the tile at the chunk boundary
+      const int r = e / 16, cc = e % 16;
+      xs[(size_t)r * D + j0 + cc] = sX[r][cc];
+    }
+    for (int e = tid; e < kC * D; e += 256) {
+      const int i = e / D, cc = e % D;
+      const bool ok = i < L;
+      sK[i][cc] = ok ? to_f32(K[((size_t)(t0 + i) * p.hqk + m) * D + cc]) : 0.f;
+      if constexpr (REV) sQ[i][cc] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + cc]) : 0.f;
+    }
+    for (int e = tid; e < kC * kC; e += 256) {
+      sT[e / kC][e % kC] = rec[e];
+      if constexpr (REV) sP[e / kC][e % kC] = rec[kC * kC + e];
+    }
+    for (int e = tid; e < kC * 16; e += 256) {
+      const int i = e / 16, cc = e % 16;
+      const size_t off = ((size_t)(t0 + i) * p.hv + h) * D + j0 + cc;
+      if constexpr (REV)
+        sIn[i][cc] = i < L ? p.scale * to_f32(dO[off]) : 0.f;
+      else
+        sIn[i][cc] = i < L ? to_f32(V[off]) : 0.f;
+    }
+    if (tid < kC) {
+      const double* bb = rec_b(rec);
+      sgam[tid] = expf((float)bb[tid]);
+      sdel[tid] = expf((float)(bb[kC - 1] - bb[tid]));
+      sbeta[tid] = tid < L ? p.beta[(size_t)(t0 + tid) * p.hv + h] : 0.f;
+      if (tid == 0) sgc = expf((float)bb[kC - 1]);
+    }
+    __syncthreads();
+
+    // rows 16 w .. 16 w + 15 of U = K X
+    const int rw = 16 * wave;
+    const f32x4 u = tile_mma([&](int i, int kk) { return sK[rw + i][kk]; },
+                             [&](int kk, int j) { return sX[kk][j]; }, D, zero4());
+    if constexpr (!REV) {  // Y = V - diag(gamma) U
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r;
+        const float y = sIn[t][idx] - sgam[t] * u[r];
+        sW[t][idx] = y;
+        if (t < L) p.ys[((size_t)(t0 + t) * p.hv + h) * D + j0 + idx] = y;
+      }
+    } else {  // dV' = P^T dO^ + diag(delta) U
+      const f32x4 pd = tile_mma([&](int i, int kk) { return sP[kk][rw + i]; },
+                                [&](int kk, int j) { return sIn[kk][j]; }, kC, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r;
+        sW[t][idx] = pd[r] + sdel[t] * u[r];
+      }
+    }
+    __syncthreads();
+    if constexpr (!REV) {  // V' = T diag(beta) Y
+      const f32x4 vpr = tile_mma([&](int i, int kk) { return sT[rw + i][kk] * sbeta[kk]; },
+                                 [&](int kk, int j) { return sW[kk][j]; }, kC, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r;
+        sZ[t][idx] = vpr[r];
+        if (t < L) p.vp[((size_t)(t0 + t) * p.hv + h) * D + j0 + idx] = vpr[r];
+      }
+    } else {  // Z = T^T dV';  dv = dY = diag(beta) Z
+      const f32x4 z = tile_mma([&](int i, int kk) { return sT[kk][rw + i]; },
+                               [&](int kk, int j) { return sW[kk][j]; }, kC, zero4());
+      InT* dV = static_cast<InT*>(p.dv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r;
+        sZ[t][idx] = z[r];
+        if (t < L) {
+          const size_t off = ((size_t)(t0 + t) * p.hv + h) * D + j0 + idx;
+          p.zs[off] = z[r];
+          dV[off] = from_f32<InT>(sbeta[t] * z[r]);
+        }
+      }
+    }
+    __syncthreads();
+    // carried tile update, its 16-row tiles dealt to the waves
+    for (int rt = wave; rt < D / 16; rt += 4) {
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = sgc * sX[16 * rt + 4 * grp + r][idx];
+      if constexpr (!REV) {  // + K^T diag(delta) V'
+        acc = tile_mma([&](int i, int kk) { return sK[kk][16 * rt + i]; },
+                       [&](int kk, int j) { return sdel[kk] * sZ[kk][j]; }, kC, acc);
+      } else {  // + Q^T diag(gamma) dO^ - K^T diag(gamma) diag(beta) Z
+        acc = tile_mma([&](int i, int kk) { return sQ[kk][16 * rt + i]; },
+                       [&](int kk, int j) { return sgam[kk] * sIn[kk][j]; }, kC, acc);
+        acc = tile_mma([&](int i, int kk) { return sK[kk][16 * rt + i]; },
+                       [&](int kk, int j) { return -sgam[kk] * sbeta[kk] * sZ[kk][j]; }, kC,
+                       acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sX[16 * rt + 4 * grp + r][idx] = acc[r];
+    }
+    __syncthreads();
+  }
+  if (REV && p.dh0) {
+    for (int e = tid; e < D * 16; e += 256) {
+      const int r = e / 16, c = e % 16;
+      st_state(p.dh0, st_base + (size_t)r * D + j0 + c, sX[r][c], p.state_bf16);
+    }
+  }
+}
+
+// ---- bwd_grads --------------------------------------------------------------------------------
+template <typename InT, typename OT, int D>
+__global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
+  constexpr int KP = D + 4;
+  constexpr int NB = D / 16;
+  __shared__ float sK[kC][KP];
+  __shared__ float sQ[kC][KP];
+  __shared__ float sPG[kC][kC + 1];  // dP o Gamma
+  __shared__ float sDS[kC][kC + 1];  // dS
+  __shared__ double sb[kC];
+  __shared__ float sbeta[kC], sgam[kC], sdel[kC];
+  __shared__ float sE[kC][kC + 1];   // E, then its row-wise exclusive prefix sums
+  __shared__ float sga[kC];          // gamma_t (<Q_t, R1_t> - <K_t, R2_t>)
+  __shared__ float sdc[kC];          // delta_t <K_t, R3_t>
+  __shared__ float sred[4];
+
+  const int slot = blockIdx.x / p.hqk, m = blockIdx.x % p.hqk;
+  const int G = p.hv / p.hqk;
+  int n, t0, L;
+  if (slot >= p.num_slots || !slot_chunk(p, slot, n, t0, L)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int idx = lane & 15, grp = lane >> 4;
+  const int rw = 16 * wave;  // this wave's rows
+
+  const InT* Q = static_cast<const InT*>(p.q);
+  const InT* K = static_cast<const InT*>(p.k);
+  const OT* dO = static_cast<const OT*>(p.dout);
+  for (int e = tid; e < kC * D; e += 256) {
+    const int i = e / D, c = e % D;
+    const bool ok = i < L;
+    sK[i][c] = ok ? to_f32(K[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
+    sQ[i][c] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
+  }
+
+  f32x4 dq[NB], dk[NB];
+#pragma unroll
+  for (int ct = 0; ct < NB; ++ct) dq[ct] = dk[ct] = zero4();
+
+  for (int jh = 0; jh < G; ++jh) {
+    const int h = m * G + jh;
+    const float* rec = p.rec + ((size_t)slot * p.hv + h) * kRecFloats;
+    const float* Pm = rec + kC * kC;
+    const float* At = rec + 2 * kC * kC;
+    const float* H = p.hs + ((size_t)slot * p.hv + h) * D * D;
+    const float* dH = p.dhs + ((size_t)slot * p.hv + h) * D * D;
+    if (tid < kC) {
+      const double* bb = rec_b(rec);
+      sb[tid] = bb[tid];
+      sgam[tid] = expf((float)bb[tid]);
+      sdel[tid] = expf((float)(bb[kC - 1] - bb[tid]));
+      sbeta[tid] = tid < L ? p.beta[(size_t)(t0 + tid) * p.hv + h] : 0.f;
+    }
+    __syncthreads();
+
+    // token-row accessors (zero past the chunk end)
+    auto row_off = [&](int t) { return ((size_t)(t0 + t) * p.hv + h) * D; };
+    auto dOh = [&](int t, int c) { return t < L ? p.scale * to_f32(dO[row_off(t) + c]) : 0.f; };
+    auto Zv = [&](int t, int c) { return t < L ? p.zs[row_off(t) + c] : 0.f; };
+    auto Vpv = [&](int t, int c) { return t < L ? p.vp[row_off(t) + c] : 0.f; };
+
+    // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (rows rw.., all d_k columns) into dq, dk and the
+    // row sums of db.
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // gamma (<Q, R1> - <K, R2>)
+    float rdB[4] = {0.f, 0.f, 0.f, 0.f};    // delta <K, R3>
+    for (int ct = 0; ct < NB; ++ct) {
+      const int c0 = 16 * ct;
+      const f32x4 r1 = tile_mma([&](int i, int kk) { return dOh(rw + i, kk); },
+                                [&](int kk, int j) { return H[(size_t)(c0 + j) * D + kk]; }, D,
+                                zero4());
+      const f32x4 r2 = tile_mma([&](int i, int kk) { return sbeta[rw + i] * Zv(rw + i, kk); },
+                                [&](int kk, int j) { return H[(size_t)(c0 + j) * D + kk]; }, D,
+                                zero4());
+      const f32x4 r3 = tile_mma([&](int i, int kk) { return Vpv(rw + i, kk); },
+                                [&](int kk, int j) { return dH[(size_t)(c0 + j) * D + kk]; }, D,
+                                zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r, cc = c0 + idx;
+        dq[ct][r] += sgam[t] * r1[r];
+        dk[ct][r] += sdel[t] * r3[r] - sgam[t] * r2[r];
+        rsum[r] += sgam[t] * (sQ[t][cc] * r1[r] - sK[t][cc] * r2[r]);
+        rdB[r] += sdel[t] * sK[t][cc] * r3[r];
+      }
+    }
+    // dP = dO^ V'^T (lower-incl), dA = -Z V'^T (strictly lower); dP o Gamma, dS, E
+    float rbeta[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < 4; ++ct) {
+      const int c0 = 16 * ct;
+      const f32x4 dp = tile_mma([&](int i, int kk) { return dOh(rw + i, kk); },
+                                [&](int kk, int j) { return Vpv(c0 + j, kk); }, D, zero4());
+      const f32x4 za = tile_mma([&](int i, int kk) { return Zv(rw + i, kk); },
+                                [&](int kk, int j) { return Vpv(c0 + j, kk); }, D, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r, j = c0 + idx;
+        const float gam = t >= j ? expf((float)(sb[t] - sb[j])) : 0.f;
+        const float dPm = t >= j ? dp[r] : 0.f;
+        const float dAm = t > j ? -za[r] : 0.f;
+        const float at = At[t * kC + j];
+        sPG[t][j] = dPm * gam;
+        sDS[t][j] = dAm * sbeta[t] * gam;
+        sE[t][j] = dPm * Pm[t * kC + j] + dAm * sbeta[t] * at;
+        rbeta[r] += dAm * at;
+      }
+    }
+    // row sums over the 16 lanes of each row group
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        rsum[r] += __shfl_xor(rsum[r], off);
+        rdB[r] += __shfl_xor(rdB[r], off);
+        rbeta[r] += __shfl_xor(rbeta[r], off);
+      }
+    }
+    if (idx == 0) {  // per-row pieces (rows past the chunk end hold zeros)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r;
+        sga[t] = rsum[r];
+        sdc[t] = rdB[r];
+      }
+    }
+    // <H, dH'> over the whole head
+    float hdh = 0.f;
+    for (int e = tid; e < D * D; e += 256) hdh += H[e] * dH[e];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) hdh += __shfl_xor(hdh, off);
+    if (lane == 0) sred[wave] = hdh;
+    // dbeta_t = <Y_t, Z_t> + sum_j dA_tj At_tj (rows of this wave)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = rw + 4 * grp + r;
+      float yz = 0.f;
+      if (t < L)
+        for (int c = idx; c < D; c += 16) yz += p.ys[row_off(t) + c] * p.zs[row_off(t) + c];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) yz += __shfl_xor(yz, off);
+      if (idx == 0 && t < L) p.dbeta[(size_t)(t0 + t) * p.hv + h] = yz + rbeta[r];
+    }
+    __syncthreads();  // sPG, sDS, sE, sga, sdc, sred complete
+    if (tid < kC) {  // row t of E -> exclusive prefix sums along j
+      float acc = 0.f;
+      for (int j = 0; j < kC; ++j) {
+        const float e = sE[tid][j];
+        sE[tid][j] = acc;
+        acc += e;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int sidx = lane;
+      // sum_{t >= s} sum_{j < s} E_tj = sum_{t >= s} prefix_t(s)
+      float fe = 0.f;
+      for (int t = sidx; t < kC; ++t) fe += sE[t][sidx];
+      // suffix sum of sga (reverse inclusive scan), prefix sum of sdc (exclusive)
+      const float ga_rev = sga[kC - 1 - lane];  // lane l: row 63 - l
+      const float suf = __shfl(wave_inclusive_scan(ga_rev, lane), kC - 1 - lane);
+      const float dcv = sdc[lane];
+      const float pre = wave_inclusive_scan(dcv, lane) - dcv;
+      const float hdhs = sgam[kC - 1] * (sred[0] + sred[1] + sred[2] + sred[3]);
+      if (lane < L) p.dg[(size_t)(t0 + lane) * p.hv + h] = suf + pre + hdhs + fe;
+    }
+    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dS + dS^T) K
+    for (int ct = 0; ct < NB; ++ct) {
+      const int c0 = 16 * ct;
+      dq[ct] = tile_mma([&](int i, int kk) { return sPG[rw + i][kk]; },
+                        [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[ct]);
+      dk[ct] = tile_mma([&](int i, int kk) { return sPG[kk][rw + i]; },
+                        [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[ct]);
+      dk[ct] = tile_mma([&](int i, int kk) { return sDS[rw + i][kk] + sDS[kk][rw + i]; },
+                        [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[ct]);
+    }
+    __syncthreads();  // LDS reused by the next V head
+  }
+
+  InT* dQo = static_cast<InT*>(p.dq);
+  InT* dKo = static_cast<InT*>(p.dk);
+#pragma unroll
+  for (int ct = 0; ct < NB; ++ct) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = rw + 4 * grp + r;
+      if (t < L) {
+        const size_t off = ((size_t)(t0 + t) * p.hqk + m) * D + 16 * ct + idx;
+        dQo[off] = from_f32<InT>(dq[ct][r]);
+        dKo[off] = from_f32<InT>(dk[ct][r]);
+      }
+    }
+  }
+}
+
+// Workspace sections, each rounded to 256 bytes.
+struct BwdLayout {
+  size_t rec, hs, dhs, ys, vp, zs, total;  // float offsets, total in floats
+};
+inline size_t round64(size_t x) { return (x + 63) / 64 * 64; }
+inline BwdLayout bwd_layout(const gdn_shape_t& s) {
+  const size_t slots = (size_t)chunk_slots(s), hv = (size_t)s.num_v_heads, d = (size_t)s.head_dim_k;
+  const size_t rows = (size_t)s.total_tokens * hv * d;
+  BwdLayout L{};
+  L.rec = 0;
+  L.hs = L.rec + round64(slots * hv * kRecFloats);
+  L.dhs = L.hs + round64(slots * hv * d * d);
+  L.ys = L.dhs + round64(slots * hv * d * d);
+  L.vp = L.ys + round64(rows);
+  L.zs = L.vp + round64(rows);
+  L.total = L.zs + round64(rows);
+  return L;
+}
+
+template <typename InT, typename OT, int D>
+hipError_t launch_bwd_t(const gdn_shape_t& s, BwdParams p, hipStream_t stream) {
+  const unsigned slot_blocks_v = (unsigned)(p.num_slots * p.hv);
+  const unsigned slot_blocks_qk = (unsigned)(p.num_slots * p.hqk);
+  const unsigned scan_blocks = (unsigned)(s.num_seqs * s.num_v_heads * (D / 16));
+  if (s.total_tokens > 0) {
+    hipLaunchKernelGGL((bwd_intra_kernel<InT, D>), dim3(slot_blocks_v), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_scan_kernel<InT, OT, D, false>), dim3(scan_blocks), dim3(256), 0,
+                       stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // the reverse scan also runs for empty sequences: dh0 = dht there
+  hipLaunchKernelGGL((bwd_scan_kernel<InT, OT, D, true>), dim3(scan_blocks), dim3(256), 0, stream,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s.total_tokens == 0) return e;
+  hipLaunchKernelGGL((bwd_grads_kernel<InT, OT, D>), dim3(slot_blocks_qk), dim3(256), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+template <typename InT, typename OT>
+hipError_t launch_bwd_d(const gdn_shape_t& s, const BwdParams& p, hipStream_t stream) {
+  switch (s.head_dim_k) {
+    case 32: return launch_bwd_t<InT, OT, 32>(s, p, stream);
+    case 64: return launch_bwd_t<InT, OT, 64>(s, p, stream);
+    case 128: return launch_bwd_t<InT, OT, 128>(s, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+long long chunk_backward_workspace_floats(const gdn_shape_t& s) {
+  return (long long)bwd_layout(s).total;
+}
+
+hipError_t launch_chunk_backward(const gdn_shape_t& s, const int32_t* cu, const void* q,
+                                 const void* k, const void* v, const float* g, const float* beta,
+                                 const void* h0, const void* dout, const void* dht, void* dq,
+                                 void* dk, void* dv, float* dg, float* dbeta, void* dh0, void* ws,
+                                 hipStream_t stream) {
+  const BwdLayout L = bwd_layout(s);
+  float* w = static_cast<float*>(ws);
+  BwdParams p{cu, q, k, v, g, beta, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0,
+              w + L.rec, w + L.hs, w + L.dhs, w + L.ys, w + L.vp, w + L.zs,
+              s.num_seqs, s.total_tokens, s.num_qk_heads, s.num_v_heads,
+              (int)chunk_slots(s), s.scale, s.state_dtype == GDN_DTYPE_BF16 ? 1 : 0};
+  const bool in_bf = s.qkv_dtype == GDN_DTYPE_BF16, out_bf = s.out_dtype == GDN_DTYPE_BF16;
+  if (in_bf && out_bf) return launch_bwd_d<bf16, bf16>(s, p, stream);
+  if (in_bf) return launch_bwd_d<bf16, float>(s, p, stream);
+  if (out_bf) return launch_bwd_d<float, bf16>(s, p, stream);
+  return launch_bwd_d<float, float>(s, p, stream);
+}
+
+}  // namespace gdn

@@ -39,6 +39,14 @@ hipError_t launch_gated_rmsnorm(const gdn_shape_t& s, const void* o, const void*
                                 const float* w, float w_offset, float eps, void* out,
                                 hipStream_t stream);
 
+// Backward pass of the chunked form (gdn_backward.hip): workspace size in floats, and launch.
+long long chunk_backward_workspace_floats(const gdn_shape_t& s);
+hipError_t launch_chunk_backward(const gdn_shape_t& s, const int32_t* cu, const void* q,
+                                 const void* k, const void* v, const float* g, const float* beta,
+                                 const void* h0, const void* dout, const void* dht, void* dq,
+                                 void* dk, void* dv, float* dg, float* dbeta, void* dh0, void* ws,
+                                 hipStream_t stream);
+
 // Bytes of one workspace record (one chunk slot x one V head); the layout is private to
 // gdn_chunk.hip, which checks this value at compile time.
 constexpr long long kWorkspaceRecordBytes = 25088;

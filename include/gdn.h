@@ -139,6 +139,27 @@ gdn_status_t gdn_chunk_scan(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                             const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_chunk_backward -- gradients of the chunked prefill for training ([MoE report] §3.7: the
+ * chunked form trained chunk by chunk; the token recurrence above is the definition it
+ * differentiates). For the loss L = sum(o * dout) + sum(final_state * dht), with o and
+ * final_state those gdn_chunk_forward returns for the same inputs, it writes
+ *   dq, dk [T][H_qk][d_k] qkv_dtype (summed over the V heads that read each QK head),
+ *   dv [T][H_v][d_v] qkv_dtype, dg, dbeta [T][H_v] fp32, dh0 [N][H_v][d_k][d_v] state_dtype.
+ *   dout [T][H_v][d_v] out_dtype; dht [N][H_v][d_k][d_v] state_dtype, or NULL for no
+ *   final-state term; initial_state as in gdn_chunk_forward (NULL for zeros); dh0 may be NULL.
+ * All arithmetic is fp32. The forward states are recomputed from initial_state (nothing from a
+ * forward call is reused). workspace >= gdn_chunk_backward_workspace_size(shape) bytes,
+ * 256-byte aligned, caller-owned scratch.
+ */
+size_t gdn_chunk_backward_workspace_size(const gdn_shape_t* shape);
+gdn_status_t gdn_chunk_backward(const gdn_shape_t* shape, const int32_t* cu_seqlens,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const void* initial_state, const void* dout,
+                                const void* dht, void* dq, void* dk, void* dv, float* dg,
+                                float* dbeta, void* dh0, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * gdn_recurrent_step -- one decode token per sequence ([MoE report] §3.3 stage 3 decode;
  * [xiwon notes] "Qwen3_5MoeGatedDeltaNet" recurrent branch and "Cache": the state is read,
  * updated once and written back in place). Requires total_tokens == num_seqs.

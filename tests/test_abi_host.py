@@ -206,6 +206,30 @@ def test_decode_step_validation(lib):
         == UNSUPPORTED
 
 
+def test_chunk_backward_validation(lib):
+    s = _shape()
+    ins = [FAKE] * 10  # cu, q, k, v, g, beta, h0, dout, dht  (+ placeholder)
+    outs = [FAKE] * 6  # dq, dk, dv, dg, dbeta, dh0
+    need = lib.gdn_chunk_backward_workspace_size(ctypes.byref(s))
+    assert need > 0
+
+    def call(shape, ins=ins[:9], outs=outs, ws=FAKE, nbytes=need):
+        return lib.gdn_chunk_backward(ctypes.byref(shape), *ins, *outs, ws, nbytes, None)
+
+    assert call(s, nbytes=need - 1) == WS_SMALL
+    assert call(s, ws=ctypes.c_void_p((1 << 20) + 64)) == INVALID
+    for i in (0, 1, 2, 3, 4, 5, 7):  # all but the optional initial state and dht
+        bad = list(ins[:9])
+        bad[i] = None
+        assert call(s, ins=bad) == INVALID
+    for i in range(5):  # all but the optional dh0
+        o = list(outs)
+        o[i] = None
+        assert call(s, outs=o) == INVALID
+    assert call(_shape(state_dtype=3)) == INVALID
+    assert call(_shape(head_dim_k=48, head_dim_v=48)) == UNSUPPORTED
+
+
 def test_gated_rmsnorm_validation(lib):
     s = _shape()
 
