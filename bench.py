@@ -7,7 +7,8 @@ layer (1 x 4096 tokens, 16 QK / 32 V heads, d = 128, bf16 q/k/v): one step is on
 gdn_chunk_forward (its two kernels, gdn_chunk_intra then gdn_chunk_scan) over inputs already
 resident in HBM. The same line carries decode tokens/s (256 sequences x 1 token, 537 MB fp32
 state updated in place), the long-context and packed front-end workloads, the output gate (1 x 4096 shape), a decode
-step from projected inputs (fused front end + recurrent step, 256 sequences), per-kernel HIP-event
+step from projected inputs (fused front end + recurrent step, 256 sequences), the backward of
+the 1 x 4096 prefill, per-kernel HIP-event
 timings, the roofline of each workload's dominant kernel and the float64 CPU oracle timed on
 a bounded sample on this host.
 
@@ -38,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3  # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 C = 64
 
@@ -49,7 +51,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="run one workload: prefill, decode, long, front, gate, decode_front")
+                    help="run one workload: prefill, decode, long, front, gate, decode_front, backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the known-size kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -347,6 +349,44 @@ def run_decode_front(torch, gdn, si, steps, warmup):
                                                   "gdn_recurrent_step_decode_256x1")))
 
 
+def backward_flops_per_token_head(dk, dv):
+    """Algorithmic MACs x 2 of the backward per token per V head (d = d_k = d_v, C = 64): the
+    intra products (K K^T, Q K^T: 2 C d), the state recomputation (K H, T Y, K^T V': 2 d^2 + C d),
+    the reverse scan (K dH', P^T dO, T^T dV', Q^T dO, K^T dY: 3 d^2 + 2 C d) and the gradient
+    products (dO H^T, dY H^T, V' dH'^T: 3 d^2; dO V'^T, Z V'^T, (dP o G) K, (dP o G)^T Q,
+    (dS + dS^T) K: 5 C d)."""
+    d = dk
+    return 2 * (8 * d * d + 10 * C * d)
+
+
+def run_backward(torch, gdn, si, steps, warmup):
+    """Backward of the 1 x 4096 prefill (gdn_chunk_backward: dq, dk, dv, dg, dbeta and dh0 from a
+    bf16 output gradient), inputs resident in HBM, workspace preallocated."""
+    case = si.workload_case(2)
+    dev = "cuda"
+    d = {k: getattr(case, k).to(dev) for k in ("q", "k", "v", "g", "beta", "cu_seqlens")}
+    T, hqk, dk = case.q.shape
+    hv, dv = case.v.shape[1], case.v.shape[2]
+    gen = torch.Generator(device="cpu").manual_seed(1008)
+    dout = torch.randn((T, hv, dv), generator=gen).to(torch.bfloat16).to(dev)
+    nbytes = gdn.backward_workspace_size(T, 1, hqk, hv, dk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.chunk_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], dout,
+                           workspace=ws)
+
+    ev_ms, ms, kms = _measure(torch, [("gdn_chunk_backward", step)], steps, warmup)
+    F = backward_flops_per_token_head(dk, dv) * T * hv
+    tf = F / (kms["gdn_chunk_backward"] / 1e3) / 1e12
+    return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=T / (ms / 1e3),
+                kernels_ms=kms, workspace_bytes=nbytes,
+                roofline=dict(kernel="gdn_chunk_backward (4 launches)", bound="mfma",
+                              achieved=round(tf, 3), peak=PEAK_F32_TFLOPS, unit="TFLOP/s",
+                              frac=round(tf / PEAK_F32_TFLOPS, 5), traffic=None,
+                              algorithmic_flops_per_launch=F))
+
+
 def cpu_baseline(case, budget_s=20.0, min_s=3.0):
     """The float64 oracle as it stands on this host, on whole (sequence, V head) chains of the
     prefill workload: whole passes over all V heads are repeated until ~min_s of work (a
@@ -430,6 +470,8 @@ def main():
         out["front_end_packed_8_seqs"] = run_front(torch, gdn, si, max(3, args.steps // 5), 2)
     if only in (None, "gate"):
         out["output_gate_1x4096"] = run_gate(torch, gdn, si, args.steps, args.warmup)
+    if only in (None, "backward"):
+        out["backward_1x4096"] = run_backward(torch, gdn, si, max(3, args.steps // 5), 2)
     if only in (None, "decode_front"):
         out["decode_front_256x1"] = run_decode_front(torch, gdn, si, args.steps, args.warmup)
 

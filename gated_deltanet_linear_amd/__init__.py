@@ -178,6 +178,13 @@ def workspace_size(total_tokens: int, num_seqs: int, num_qk_heads: int, num_v_he
     return int(_load().gdn_chunk_forward_workspace_size(ctypes.byref(s)))
 
 
+def backward_workspace_size(total_tokens: int, num_seqs: int, num_qk_heads: int,
+                            num_v_heads: int, head_dim: int) -> int:
+    s = _shape(num_seqs, total_tokens, num_qk_heads, num_v_heads, head_dim, head_dim,
+               torch.bfloat16, torch.bfloat16)
+    return int(_load().gdn_chunk_backward_workspace_size(ctypes.byref(s)))
+
+
 def _workspace(s: GdnShape, device, workspace):
     nbytes = int(_load().gdn_chunk_forward_workspace_size(ctypes.byref(s)))
     if workspace is None:

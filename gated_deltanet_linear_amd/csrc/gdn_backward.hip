@@ -33,6 +33,8 @@
 // Every product is formed by tile_mma, one 16 x 16 output tile per call, its operands read
 // through accessors from LDS or global memory (the state matrices stay in global memory, read
 // along their contiguous axis).
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_internal.h"
 
@@ -116,6 +118,48 @@ __device__ __forceinline__ f32x4 tile_mma(FA a, FB b, int K, f32x4 acc) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// 8 fragment values of a row contiguous along the depth: slots 0-3 are depth k0 + 4 grp .. + 3,
+// slots 4-7 depth k0 + 16 + 4 grp .. + 3 (kslot), so two 16-byte (fp32) or 8-byte (bf16) loads.
+__device__ __forceinline__ void row_frag(const float* row, int k0, int grp, float scale, f32x8& o) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(row + k0 + 4 * grp);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(row + k0 + 16 + 4 * grp);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    o[s] = scale * lo[s];
+    o[4 + s] = scale * hi[s];
+  }
+}
+__device__ __forceinline__ void row_frag(const bf16* row, int k0, int grp, float scale, f32x8& o) {
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + k0 + 4 * grp);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + k0 + 16 + 4 * grp);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    o[s] = scale * (float)lo[s];
+    o[4 + s] = scale * (float)hi[s];
+  }
+}
+
+// acc += A B^T over depth K where this lane's A row (row idx of the tile) and B row (column idx)
+// are both contiguous along the depth: the common case of the gradient products, read with
+// vector loads. A null A row stands for zeros (rows past the chunk end).
+template <typename TA, typename TB>
+__device__ __forceinline__ f32x4 tile_mma_rows(const TA* a_row, float a_scale, const TB* b_row,
+                                               int K, f32x4 acc) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f32x8 av, bv;
+    if (a_row) {
+      row_frag(a_row, k0, grp, a_scale, av);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) av[s] = 0.f;
+    }
+    row_frag(b_row, k0, grp, 1.f, bv);
+    acc = mma32(av, bv, acc);
+  }
+  return acc;
+}
+
 // (sequence, first token, valid rows) of chunk slot `slot`; false for an unused slot.
 __device__ __forceinline__ bool slot_chunk(const BwdParams& p, int slot, int& n, int& t0, int& L) {
   n = slot_to_seq(p.cu, p.num_seqs, slot);
@@ -163,10 +207,9 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
 
   // wave w: rows 16 w .. 16 w + 15 of S = K K^T and Q K^T
   for (int ct = 0; ct < 4; ++ct) {
-    const f32x4 s = tile_mma([&](int i, int kk) { return sK[16 * wave + i][kk]; },
-                             [&](int kk, int j) { return sK[16 * ct + j][kk]; }, D, zero4());
-    const f32x4 qk = tile_mma([&](int i, int kk) { return sQ[16 * wave + i][kk]; },
-                              [&](int kk, int j) { return sK[16 * ct + j][kk]; }, D, zero4());
+    const f32x4 s = tile_mma_rows(&sK[16 * wave + idx][0], 1.f, &sK[16 * ct + idx][0], D, zero4());
+    const f32x4 qk = tile_mma_rows(&sQ[16 * wave + idx][0], 1.f, &sK[16 * ct + idx][0], D,
+                                   zero4());
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * wave + 4 * grp + r, j = 16 * ct + idx;
@@ -180,17 +223,52 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // T = (I + A)^-1 by forward substitution, one row per step: T_tj = [t == j] - sum_{j<=m<t}
-  // A_tm T_mj (thread j of wave 0 owns column j; the other waves wait at the barriers).
-  for (int t = 0; t < kC; ++t) {
-    if (tid < kC) {
-      const int j = tid;
-      float x = t == j ? 1.f : 0.f;
-      if (j < t)
-        for (int mm = j; mm < t; ++mm) x -= sA[t][mm] * sT[mm][j];
-      sT[t][j] = j <= t ? x : 0.f;
+  // T = (I + A)^-1, A strictly lower, by 16 x 16 blocks. Diagonal blocks: wave w inverts block
+  // w by forward substitution, lane c owning column c (each column is an independent triangular
+  // solve; a lane reads back only its own column). Off-diagonal blocks, one block row after the
+  // other: T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, the i products of a block row on i waves.
+  {
+    const int b0 = 16 * wave;
+    for (int e = tid; e < kC * kC; e += 256) sT[e / kC][e % kC] = 0.f;
+    __syncthreads();
+    if (lane < 16) {
+      const int c = lane;
+      for (int r = 0; r < 16; ++r) {
+        float x = r == c ? 1.f : 0.f;
+        for (int mm = c; mm < r; ++mm) x -= sA[b0 + r][b0 + mm] * sT[b0 + mm][b0 + c];
+        if (r >= c) sT[b0 + r][b0 + c] = x;
+      }
     }
     __syncthreads();
+    for (int bi = 1; bi < 4; ++bi) {
+      const int bj = wave;  // block column of this wave
+      f32x4 w = zero4();
+      if (bj < bi) {  // W = sum_{bj <= k < bi} A_(bi,k) T_(k,bj): depth 16 (bi - bj), padded to 32s
+        const int depth = 16 * (bi - bj);
+        w = tile_mma(
+            [&](int r, int kk) { return kk < depth ? sA[16 * bi + r][16 * bj + kk] : 0.f; },
+            [&](int kk, int cc) { return kk < depth ? sT[16 * bj + kk][16 * bj + cc] : 0.f; },
+            (depth + 31) / 32 * 32, zero4());
+      }
+      // stage W in the (still zero) target block, then T_ij = -T_ii W in place of it
+      if (bj < bi) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sT[16 * bi + 4 * grp + r][16 * bj + idx] = w[r];
+      }
+      __syncthreads();
+      f32x4 t = zero4();
+      if (bj < bi) {
+        t = tile_mma([&](int r, int kk) { return kk < 16 ? sT[16 * bi + r][16 * bi + kk] : 0.f; },
+                     [&](int kk, int cc) { return kk < 16 ? sT[16 * bi + kk][16 * bj + cc] : 0.f; },
+                     32, zero4());
+      }
+      __syncthreads();
+      if (bj < bi) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sT[16 * bi + 4 * grp + r][16 * bj + idx] = -t[r];
+      }
+      __syncthreads();
+    }
   }
   for (int e = tid; e < kC * kC; e += 256) rec[e] = sT[e / kC][e % kC];
 }
@@ -234,6 +312,73 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   const OT* dO = static_cast<const OT*>(p.dout);
   __syncthreads();
 
+  // A chunk's global operands are loaded into registers (16-byte pieces) one chunk ahead: the
+  // next chunk's loads are in flight while this one is computed. Rows past the chunk end load
+  // row 0 of the chunk and are zeroed when staged.
+  constexpr int KV = kC * D / 8 / 256;  // 8-value pieces of the k (q) rows per thread
+  static_assert(kC * D % (8 * 256) == 0, "k row pieces");
+  using InT2 = std::conditional_t<REV, OT, InT>;  // dO^ (reverse) or v (forward) columns
+  Raw8<InT> rk[KV], rq[REV ? KV : 1];
+  f32x4 rt[4], rp[REV ? 4 : 1];
+  Raw8<InT2> rin;
+  auto load_chunk = [&](int c) {
+    const int t0 = seq0 + kC * c, L = min(kC, len - kC * c);
+    const float* rec = p.rec + ((size_t)(sb0 + c) * p.hv + h) * kRecFloats;
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int e = tid + 256 * i, row = e / (D / 8), c8 = e % (D / 8);
+      const size_t off = ((size_t)(t0 + (row < L ? row : 0)) * p.hqk + m) * D + 8 * c8;
+      rk[i].load(K + off);
+      if constexpr (REV) rq[i].load(Q + off);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rt[i] = reinterpret_cast<const f32x4*>(rec)[tid + 256 * i];
+      if constexpr (REV) rp[i] = reinterpret_cast<const f32x4*>(rec + kC * kC)[tid + 256 * i];
+    }
+    if (tid < 2 * kC) {
+      const int row = tid / 2, half = tid % 2;
+      const size_t off = ((size_t)(t0 + (row < L ? row : 0)) * p.hv + h) * D + j0 + 8 * half;
+      if constexpr (REV)
+        rin.load(dO + off);
+      else
+        rin.load(V + off);
+    }
+  };
+  auto stage_chunk = [&](int L) {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int e = tid + 256 * i, row = e / (D / 8), c8 = e % (D / 8);
+      float x[8];
+      rk[i].to(x);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sK[row][8 * c8 + u] = row < L ? x[u] : 0.f;
+      if constexpr (REV) {
+        rq[i].to(x);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sQ[row][8 * c8 + u] = row < L ? x[u] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * (tid + 256 * i), r = e / kC, cc = e % kC;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sT[r][cc + u] = rt[i][u];
+        if constexpr (REV) sP[r][cc + u] = rp[i][u];
+      }
+    }
+    if (tid < 2 * kC) {
+      const int row = tid / 2, half = tid % 2;
+      float x[8];
+      rin.to(x);
+      const float sc = REV ? p.scale : 1.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sIn[row][8 * half + u] = row < L ? sc * x[u] : 0.f;
+    }
+  };
+  if (nch > 0) load_chunk(REV ? nch - 1 : 0);
+
   for (int ci = 0; ci < nch; ++ci) {
     const int c = REV ? nch - 1 - ci : ci;
     const int slot = sb0 + c, t0 = seq0 + kC * c, L = min(kC, len - kC * c);
@@ -243,24 +388,8 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
       const int r = e / 16, cc = e % 16;
       xs[(size_t)r * D + j0 + cc] = sX[r][cc];
     }
-    for (int e = tid; e < kC * D; e += 256) {
-      const int i = e / D, cc = e % D;
-      const bool ok = i < L;
-      sK[i][cc] = ok ? to_f32(K[((size_t)(t0 + i) * p.hqk + m) * D + cc]) : 0.f;
-      if constexpr (REV) sQ[i][cc] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + cc]) : 0.f;
-    }
-    for (int e = tid; e < kC * kC; e += 256) {
-      sT[e / kC][e % kC] = rec[e];
-      if constexpr (REV) sP[e / kC][e % kC] = rec[kC * kC + e];
-    }
-    for (int e = tid; e < kC * 16; e += 256) {
-      const int i = e / 16, cc = e % 16;
-      const size_t off = ((size_t)(t0 + i) * p.hv + h) * D + j0 + cc;
-      if constexpr (REV)
-        sIn[i][cc] = i < L ? p.scale * to_f32(dO[off]) : 0.f;
-      else
-        sIn[i][cc] = i < L ? to_f32(V[off]) : 0.f;
-    }
+    stage_chunk(L);
+    if (ci + 1 < nch) load_chunk(REV ? c - 1 : c + 1);
     if (tid < kC) {
       const double* bb = rec_b(rec);
       sgam[tid] = expf((float)bb[tid]);
@@ -401,25 +530,24 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
 
     // token-row accessors (zero past the chunk end)
     auto row_off = [&](int t) { return ((size_t)(t0 + t) * p.hv + h) * D; };
-    auto dOh = [&](int t, int c) { return t < L ? p.scale * to_f32(dO[row_off(t) + c]) : 0.f; };
-    auto Zv = [&](int t, int c) { return t < L ? p.zs[row_off(t) + c] : 0.f; };
-    auto Vpv = [&](int t, int c) { return t < L ? p.vp[row_off(t) + c] : 0.f; };
 
+    // this lane's A rows (row rw + idx of the chunk; null past its end)
+    const bool my_ok = rw + idx < L;
+    const OT* my_dO = my_ok ? dO + row_off(rw + idx) : nullptr;
+    const float* my_Z = my_ok ? p.zs + row_off(rw + idx) : nullptr;
+    const float* my_Vp = my_ok ? p.vp + row_off(rw + idx) : nullptr;
+    const float my_beta = sbeta[rw + idx];
     // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (rows rw.., all d_k columns) into dq, dk and the
     // row sums of db.
     float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // gamma (<Q, R1> - <K, R2>)
     float rdB[4] = {0.f, 0.f, 0.f, 0.f};    // delta <K, R3>
     for (int ct = 0; ct < NB; ++ct) {
       const int c0 = 16 * ct;
-      const f32x4 r1 = tile_mma([&](int i, int kk) { return dOh(rw + i, kk); },
-                                [&](int kk, int j) { return H[(size_t)(c0 + j) * D + kk]; }, D,
-                                zero4());
-      const f32x4 r2 = tile_mma([&](int i, int kk) { return sbeta[rw + i] * Zv(rw + i, kk); },
-                                [&](int kk, int j) { return H[(size_t)(c0 + j) * D + kk]; }, D,
-                                zero4());
-      const f32x4 r3 = tile_mma([&](int i, int kk) { return Vpv(rw + i, kk); },
-                                [&](int kk, int j) { return dH[(size_t)(c0 + j) * D + kk]; }, D,
-                                zero4());
+      const float* hrow = H + (size_t)(c0 + idx) * D;
+      const float* dhrow = dH + (size_t)(c0 + idx) * D;
+      const f32x4 r1 = tile_mma_rows(my_dO, p.scale, hrow, D, zero4());
+      const f32x4 r2 = tile_mma_rows(my_Z, my_beta, hrow, D, zero4());
+      const f32x4 r3 = tile_mma_rows(my_Vp, 1.f, dhrow, D, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r, cc = c0 + idx;
@@ -433,10 +561,10 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
     float rbeta[4] = {0.f, 0.f, 0.f, 0.f};
     for (int ct = 0; ct < 4; ++ct) {
       const int c0 = 16 * ct;
-      const f32x4 dp = tile_mma([&](int i, int kk) { return dOh(rw + i, kk); },
-                                [&](int kk, int j) { return Vpv(c0 + j, kk); }, D, zero4());
-      const f32x4 za = tile_mma([&](int i, int kk) { return Zv(rw + i, kk); },
-                                [&](int kk, int j) { return Vpv(c0 + j, kk); }, D, zero4());
+      // V' rows past the chunk end are read as row 0 of the chunk and masked by Gamma below
+      const float* vprow = p.vp + row_off(c0 + idx < L ? c0 + idx : 0);
+      const f32x4 dp = tile_mma_rows(my_dO, p.scale, vprow, D, zero4());
+      const f32x4 za = tile_mma_rows(my_Z, 1.f, vprow, D, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r, j = c0 + idx;
