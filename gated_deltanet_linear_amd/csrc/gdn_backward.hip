@@ -28,8 +28,8 @@
 //   bwd_scan<false>  per (sequence, V head, 16-column tile): the states H at every chunk start
 //              (from the initial state), and Y, V' of every token.
 //   bwd_scan<true>   same layout, chunks in reverse: dH' of every chunk, Z, dv, dh0.
-//   bwd_grads  one workgroup per (chunk slot, QK head), its G V heads in turn: dq, dk (summed
-//              over the G heads), dg, dbeta.
+//   bwd_grads  one 512-thread workgroup per (chunk slot, QK head), its G V heads in turn: dq, dk
+//              (summed over the G heads), dg, dbeta.
 // Every product is formed by tile_mma, one 16 x 16 output tile per call, its operands read
 // through accessors from LDS or global memory (the state matrices stay in global memory, read
 // along their contiguous axis).
@@ -146,6 +146,7 @@ template <typename TA, typename TB>
 __device__ __forceinline__ f32x4 tile_mma_rows(const TA* a_row, float a_scale, const TB* b_row,
                                                int K, f32x4 acc) {
   const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll 2
   for (int k0 = 0; k0 < K; k0 += 32) {
     f32x8 av, bv;
     if (a_row) {
@@ -475,10 +476,15 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
 }
 
 // ---- bwd_grads --------------------------------------------------------------------------------
+// 512 threads: wave w owns the 16 rows of row tile w % 4 and half of the columns of every
+// product (d_k half w / 4 of the R and dq / dk tiles, chunk-column half of the C x C tiles), so
+// two waves share each SIMD; row sums that span the two halves meet in LDS.
 template <typename InT, typename OT, int D>
-__global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   constexpr int KP = D + 4;
   constexpr int NB = D / 16;
+  constexpr int NBH = NB / 2;  // d_k column tiles per wave
+  static_assert(NB % 2 == 0, "column halves");
   __shared__ float sK[kC][KP];
   __shared__ float sQ[kC][KP];
   __shared__ float sPG[kC][kC + 1];  // dP o Gamma
@@ -488,7 +494,8 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
   __shared__ float sE[kC][kC + 1];   // E, then its row-wise exclusive prefix sums
   __shared__ float sga[kC];          // gamma_t (<Q_t, R1_t> - <K_t, R2_t>)
   __shared__ float sdc[kC];          // delta_t <K_t, R3_t>
-  __shared__ float sred[4];
+  __shared__ float sbt[kC];          // sum_j dA_tj At_tj
+  __shared__ float sred[8];
 
   const int slot = blockIdx.x / p.hqk, m = blockIdx.x % p.hqk;
   const int G = p.hv / p.hqk;
@@ -496,21 +503,22 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
   if (slot >= p.num_slots || !slot_chunk(p, slot, n, t0, L)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int idx = lane & 15, grp = lane >> 4;
-  const int rw = 16 * wave;  // this wave's rows
+  const int rw = 16 * (wave & 3);  // this wave's rows
+  const int ch = wave >> 2;        // this wave's column half
 
   const InT* Q = static_cast<const InT*>(p.q);
   const InT* K = static_cast<const InT*>(p.k);
   const OT* dO = static_cast<const OT*>(p.dout);
-  for (int e = tid; e < kC * D; e += 256) {
+  for (int e = tid; e < kC * D; e += 512) {
     const int i = e / D, c = e % D;
     const bool ok = i < L;
     sK[i][c] = ok ? to_f32(K[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
     sQ[i][c] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
   }
 
-  f32x4 dq[NB], dk[NB];
+  f32x4 dq[NBH], dk[NBH];
 #pragma unroll
-  for (int ct = 0; ct < NB; ++ct) dq[ct] = dk[ct] = zero4();
+  for (int u = 0; u < NBH; ++u) dq[u] = dk[u] = zero4();
 
   for (int jh = 0; jh < G; ++jh) {
     const int h = m * G + jh;
@@ -525,24 +533,24 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
       sgam[tid] = expf((float)bb[tid]);
       sdel[tid] = expf((float)(bb[kC - 1] - bb[tid]));
       sbeta[tid] = tid < L ? p.beta[(size_t)(t0 + tid) * p.hv + h] : 0.f;
+      sga[tid] = sdc[tid] = sbt[tid] = 0.f;
     }
     __syncthreads();
 
-    // token-row accessors (zero past the chunk end)
     auto row_off = [&](int t) { return ((size_t)(t0 + t) * p.hv + h) * D; };
-
     // this lane's A rows (row rw + idx of the chunk; null past its end)
     const bool my_ok = rw + idx < L;
     const OT* my_dO = my_ok ? dO + row_off(rw + idx) : nullptr;
     const float* my_Z = my_ok ? p.zs + row_off(rw + idx) : nullptr;
     const float* my_Vp = my_ok ? p.vp + row_off(rw + idx) : nullptr;
     const float my_beta = sbeta[rw + idx];
-    // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (rows rw.., all d_k columns) into dq, dk and the
-    // row sums of db.
+    // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (this wave's rows and d_k half) into dq, dk and
+    // the row sums of db.
     float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // gamma (<Q, R1> - <K, R2>)
     float rdB[4] = {0.f, 0.f, 0.f, 0.f};    // delta <K, R3>
-    for (int ct = 0; ct < NB; ++ct) {
-      const int c0 = 16 * ct;
+#pragma unroll
+    for (int u = 0; u < NBH; ++u) {
+      const int c0 = 16 * (ch * NBH + u);
       const float* hrow = H + (size_t)(c0 + idx) * D;
       const float* dhrow = dH + (size_t)(c0 + idx) * D;
       const f32x4 r1 = tile_mma_rows(my_dO, p.scale, hrow, D, zero4());
@@ -551,17 +559,17 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r, cc = c0 + idx;
-        dq[ct][r] += sgam[t] * r1[r];
-        dk[ct][r] += sdel[t] * r3[r] - sgam[t] * r2[r];
+        dq[u][r] += sgam[t] * r1[r];
+        dk[u][r] += sdel[t] * r3[r] - sgam[t] * r2[r];
         rsum[r] += sgam[t] * (sQ[t][cc] * r1[r] - sK[t][cc] * r2[r]);
         rdB[r] += sdel[t] * sK[t][cc] * r3[r];
       }
     }
-    // dP = dO^ V'^T (lower-incl), dA = -Z V'^T (strictly lower); dP o Gamma, dS, E
+    // dP = dO^ V'^T (lower-incl), dA = -Z V'^T (strictly lower): this wave's two column tiles
     float rbeta[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ct = 0; ct < 4; ++ct) {
-      const int c0 = 16 * ct;
-      // V' rows past the chunk end are read as row 0 of the chunk and masked by Gamma below
+    for (int u = 0; u < 2; ++u) {
+      const int c0 = 16 * (2 * ch + u);
+      // V' rows past the chunk end are read as row 0 of the chunk and masked below
       const float* vprow = p.vp + row_off(c0 + idx < L ? c0 + idx : 0);
       const f32x4 dp = tile_mma_rows(my_dO, p.scale, vprow, D, zero4());
       const f32x4 za = tile_mma_rows(my_Z, 1.f, vprow, D, zero4());
@@ -578,7 +586,7 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
         rbeta[r] += dAm * at;
       }
     }
-    // row sums over the 16 lanes of each row group
+    // row sums over the 16 lanes of each row group, then the two column halves through LDS
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -588,32 +596,44 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
         rbeta[r] += __shfl_xor(rbeta[r], off);
       }
     }
-    if (idx == 0) {  // per-row pieces (rows past the chunk end hold zeros)
+    if (idx == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r;
-        sga[t] = rsum[r];
-        sdc[t] = rdB[r];
+        atomicAdd(&sga[t], rsum[r]);
+        atomicAdd(&sdc[t], rdB[r]);
+        atomicAdd(&sbt[t], rbeta[r]);
       }
     }
     // <H, dH'> over the whole head
     float hdh = 0.f;
-    for (int e = tid; e < D * D; e += 256) hdh += H[e] * dH[e];
+#pragma unroll 4
+    for (int e = tid; e < D * D; e += 512) hdh += H[e] * dH[e];
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) hdh += __shfl_xor(hdh, off);
     if (lane == 0) sred[wave] = hdh;
-    // dbeta_t = <Y_t, Z_t> + sum_j dA_tj At_tj (rows of this wave)
+    // <Y_t, Z_t> of this wave's rows (column half 0 only)
+    float yz[4] = {0.f, 0.f, 0.f, 0.f};
+    if (ch == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = rw + 4 * grp + r;
-      float yz = 0.f;
-      if (t < L)
-        for (int c = idx; c < D; c += 16) yz += p.ys[row_off(t) + c] * p.zs[row_off(t) + c];
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r;
+        if (t < L) {
+#pragma unroll 2
+          for (int c = idx; c < D; c += 16) yz[r] += p.ys[row_off(t) + c] * p.zs[row_off(t) + c];
+        }
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) yz += __shfl_xor(yz, off);
-      if (idx == 0 && t < L) p.dbeta[(size_t)(t0 + t) * p.hv + h] = yz + rbeta[r];
+        for (int off = 1; off < 16; off <<= 1) yz[r] += __shfl_xor(yz[r], off);
+      }
     }
-    __syncthreads();  // sPG, sDS, sE, sga, sdc, sred complete
+    __syncthreads();  // sPG, sDS, sE, sga, sdc, sbt, sred complete
+    if (ch == 0 && idx == 0) {  // dbeta_t = <Y_t, Z_t> + sum_j dA_tj At_tj
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r;
+        if (t < L) p.dbeta[(size_t)(t0 + t) * p.hv + h] = yz[r] + sbt[t];
+      }
+    }
     if (tid < kC) {  // row t of E -> exclusive prefix sums along j
       float acc = 0.f;
       for (int j = 0; j < kC; ++j) {
@@ -633,18 +653,22 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
       const float suf = __shfl(wave_inclusive_scan(ga_rev, lane), kC - 1 - lane);
       const float dcv = sdc[lane];
       const float pre = wave_inclusive_scan(dcv, lane) - dcv;
-      const float hdhs = sgam[kC - 1] * (sred[0] + sred[1] + sred[2] + sred[3]);
+      float hs8 = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) hs8 += sred[w];
+      const float hdhs = sgam[kC - 1] * hs8;
       if (lane < L) p.dg[(size_t)(t0 + lane) * p.hv + h] = suf + pre + hdhs + fe;
     }
-    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dS + dS^T) K
-    for (int ct = 0; ct < NB; ++ct) {
-      const int c0 = 16 * ct;
-      dq[ct] = tile_mma([&](int i, int kk) { return sPG[rw + i][kk]; },
-                        [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[ct]);
-      dk[ct] = tile_mma([&](int i, int kk) { return sPG[kk][rw + i]; },
-                        [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[ct]);
-      dk[ct] = tile_mma([&](int i, int kk) { return sDS[rw + i][kk] + sDS[kk][rw + i]; },
-                        [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[ct]);
+    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dS + dS^T) K  (this wave's tiles)
+#pragma unroll
+    for (int u = 0; u < NBH; ++u) {
+      const int c0 = 16 * (ch * NBH + u);
+      dq[u] = tile_mma([&](int i, int kk) { return sPG[rw + i][kk]; },
+                       [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
+      dk[u] = tile_mma([&](int i, int kk) { return sPG[kk][rw + i]; },
+                       [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
+      dk[u] = tile_mma([&](int i, int kk) { return sDS[rw + i][kk] + sDS[kk][rw + i]; },
+                       [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
     }
     __syncthreads();  // LDS reused by the next V head
   }
@@ -652,14 +676,14 @@ __global__ __launch_bounds__(256) void bwd_grads_kernel(BwdParams p) {
   InT* dQo = static_cast<InT*>(p.dq);
   InT* dKo = static_cast<InT*>(p.dk);
 #pragma unroll
-  for (int ct = 0; ct < NB; ++ct) {
+  for (int u = 0; u < NBH; ++u) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = rw + 4 * grp + r;
       if (t < L) {
-        const size_t off = ((size_t)(t0 + t) * p.hqk + m) * D + 16 * ct + idx;
-        dQo[off] = from_f32<InT>(dq[ct][r]);
-        dKo[off] = from_f32<InT>(dk[ct][r]);
+        const size_t off = ((size_t)(t0 + t) * p.hqk + m) * D + 16 * (ch * NBH + u) + idx;
+        dQo[off] = from_f32<InT>(dq[u][r]);
+        dKo[off] = from_f32<InT>(dk[u][r]);
       }
     }
   }
@@ -702,7 +726,7 @@ hipError_t launch_bwd_t(const gdn_shape_t& s, BwdParams p, hipStream_t stream) {
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s.total_tokens == 0) return e;
-  hipLaunchKernelGGL((bwd_grads_kernel<InT, OT, D>), dim3(slot_blocks_qk), dim3(256), 0, stream,
+  hipLaunchKernelGGL((bwd_grads_kernel<InT, OT, D>), dim3(slot_blocks_qk), dim3(512), 0, stream,
                      p);
   return hipGetLastError();
 }
