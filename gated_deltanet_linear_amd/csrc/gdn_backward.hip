@@ -116,6 +116,25 @@ __device__ __forceinline__ f32x4 tile_mma(FA a, FB b, int K, f32x4 acc) {
   return acc;
 }
 
+// tile_mma with the depth loop kept rolled (fewer operands in flight; for register-bound
+// callers).
+template <typename FA, typename FB>
+__device__ __forceinline__ f32x4 tile_mma_rolled(FA a, FB b, int K, f32x4 acc) {
+  const int lane = threadIdx.x & 63, idx = lane & 15, grp = lane >> 4;
+#pragma unroll 1
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f32x8 av, bv;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int kk = k0 + kslot(grp, s);
+      av[s] = a(idx, kk);
+      bv[s] = b(kk, idx);
+    }
+    acc = mma32(av, bv, acc);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // 8 fragment values of a row contiguous along the depth: slots 0-3 are depth k0 + 4 grp .. + 3,
@@ -290,7 +309,11 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   __shared__ float sgam[kC], sdel[kC], sbeta[kC];
   __shared__ float sgc;
 
-  const int jt = blockIdx.x % NB, nh = blockIdx.x / NB;
+  // The NB column tiles of one (sequence, V head) read the same chunk operands: keep them on one
+  // XCD (workgroups are dealt to the 8 XCDs round robin, so blockIdx % 8 picks the XCD).
+  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
+  const int jt = jj % NB, nh = 8 * (jj / NB) + xcd;
+  if (nh >= p.num_seqs * p.hv) return;  // padding workgroup
   const int n = nh / p.hv, h = nh % p.hv;
   const int G = p.hv / p.hqk, m = h / G;
   const int j0 = 16 * jt;
@@ -476,15 +499,16 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
 }
 
 // ---- bwd_grads --------------------------------------------------------------------------------
-// 512 threads: wave w owns the 16 rows of row tile w % 4 and half of the columns of every
-// product (d_k half w / 4 of the R and dq / dk tiles, chunk-column half of the C x C tiles), so
-// two waves share each SIMD; row sums that span the two halves meet in LDS.
+// 512 threads, two waves per SIMD. For the products with the states (R1..R3) and the dq / dk
+// tiles, wave w owns one d_k column tile (w % NB) and NB / 2 of the 4 row tiles: a state-row
+// fragment is loaded once and used for all of them. For the C x C tiles (dP, dA) it owns row tile
+// w % 4 and half of the columns. Row sums spanning several waves meet in LDS.
 template <typename InT, typename OT, int D>
 __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   constexpr int KP = D + 4;
   constexpr int NB = D / 16;
-  constexpr int NBH = NB / 2;  // d_k column tiles per wave
-  static_assert(NB % 2 == 0, "column halves");
+  constexpr int RPW = NB / 2;  // row tiles per wave in the R / dq / dk products
+  static_assert(NB % 2 == 0 && 4 * NB == 8 * RPW, "tile split");
   __shared__ float sK[kC][KP];
   __shared__ float sQ[kC][KP];
   __shared__ float sPG[kC][kC + 1];  // dP o Gamma
@@ -503,8 +527,10 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   if (slot >= p.num_slots || !slot_chunk(p, slot, n, t0, L)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int idx = lane & 15, grp = lane >> 4;
-  const int rw = 16 * (wave & 3);  // this wave's rows
-  const int ch = wave >> 2;        // this wave's column half
+  const int rw = 16 * (wave & 3);  // this wave's rows in the C x C products
+  const int ch = wave >> 2;        // this wave's column half of the C x C products
+  const int ctw = wave % NB;       // this wave's d_k column tile in the R / dq / dk products
+  const int rt0 = (wave / NB) * RPW;  // and its first row tile there
 
   const InT* Q = static_cast<const InT*>(p.q);
   const InT* K = static_cast<const InT*>(p.k);
@@ -516,9 +542,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
     sQ[i][c] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
   }
 
-  f32x4 dq[NBH], dk[NBH];
+  f32x4 dq[RPW], dk[RPW];
 #pragma unroll
-  for (int u = 0; u < NBH; ++u) dq[u] = dk[u] = zero4();
+  for (int u = 0; u < RPW; ++u) dq[u] = dk[u] = zero4();
 
   for (int jh = 0; jh < G; ++jh) {
     const int h = m * G + jh;
@@ -542,27 +568,58 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
     const bool my_ok = rw + idx < L;
     const OT* my_dO = my_ok ? dO + row_off(rw + idx) : nullptr;
     const float* my_Z = my_ok ? p.zs + row_off(rw + idx) : nullptr;
-    const float* my_Vp = my_ok ? p.vp + row_off(rw + idx) : nullptr;
-    const float my_beta = sbeta[rw + idx];
-    // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (this wave's rows and d_k half) into dq, dk and
-    // the row sums of db.
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // gamma (<Q, R1> - <K, R2>)
-    float rdB[4] = {0.f, 0.f, 0.f, 0.f};    // delta <K, R3>
-#pragma unroll
-    for (int u = 0; u < NBH; ++u) {
-      const int c0 = 16 * (ch * NBH + u);
+    // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (this wave's d_k column tile, RPW row tiles) into
+    // dq, dk and the row sums of db. The state rows of the column tile are loaded once per depth
+    // step and shared by the row tiles.
+    {
+      const int c0 = 16 * ctw;
       const float* hrow = H + (size_t)(c0 + idx) * D;
       const float* dhrow = dH + (size_t)(c0 + idx) * D;
-      const f32x4 r1 = tile_mma_rows(my_dO, p.scale, hrow, D, zero4());
-      const f32x4 r2 = tile_mma_rows(my_Z, my_beta, hrow, D, zero4());
-      const f32x4 r3 = tile_mma_rows(my_Vp, 1.f, dhrow, D, zero4());
+      f32x4 r1[RPW], r2[RPW], r3[RPW];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rw + 4 * grp + r, cc = c0 + idx;
-        dq[u][r] += sgam[t] * r1[r];
-        dk[u][r] += sdel[t] * r3[r] - sgam[t] * r2[r];
-        rsum[r] += sgam[t] * (sQ[t][cc] * r1[r] - sK[t][cc] * r2[r]);
-        rdB[r] += sdel[t] * sK[t][cc] * r3[r];
+      for (int u = 0; u < RPW; ++u) r1[u] = r2[u] = r3[u] = zero4();
+#pragma unroll 1
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        f32x8 hb, dhb;
+        row_frag(hrow, k0, grp, 1.f, hb);
+        row_frag(dhrow, k0, grp, 1.f, dhb);
+#pragma unroll
+        for (int u = 0; u < RPW; ++u) {
+          const int row = 16 * (rt0 + u) + idx;
+          f32x8 ao, az, av;
+          if (row < L) {
+            row_frag(dO + row_off(row), k0, grp, p.scale, ao);
+            row_frag(p.zs + row_off(row), k0, grp, sbeta[row], az);
+            row_frag(p.vp + row_off(row), k0, grp, 1.f, av);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ao[e] = az[e] = av[e] = 0.f;
+          }
+          r1[u] = mma32(ao, hb, r1[u]);
+          r2[u] = mma32(az, hb, r2[u]);
+          r3[u] = mma32(av, dhb, r3[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < RPW; ++u) {
+        float rs[4], rd[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * (rt0 + u) + 4 * grp + r, cc = c0 + idx;
+          dq[u][r] += sgam[t] * r1[u][r];
+          dk[u][r] += sdel[t] * r3[u][r] - sgam[t] * r2[u][r];
+          rs[r] = sgam[t] * (sQ[t][cc] * r1[u][r] - sK[t][cc] * r2[u][r]);
+          rd[r] = sdel[t] * sK[t][cc] * r3[u][r];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            rs[r] += __shfl_xor(rs[r], off);
+            rd[r] += __shfl_xor(rd[r], off);
+          }
+          if (idx == 0) {
+            atomicAdd(&sga[t], rs[r]);
+            atomicAdd(&sdc[t], rd[r]);
+          }
+        }
       }
     }
     // dP = dO^ V'^T (lower-incl), dA = -Z V'^T (strictly lower): this wave's two column tiles
@@ -586,24 +643,15 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         rbeta[r] += dAm * at;
       }
     }
-    // row sums over the 16 lanes of each row group, then the two column halves through LDS
+    // row sums of rbeta over the 16 lanes of each row group, then across the waves through LDS
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        rsum[r] += __shfl_xor(rsum[r], off);
-        rdB[r] += __shfl_xor(rdB[r], off);
-        rbeta[r] += __shfl_xor(rbeta[r], off);
-      }
+      for (int off = 1; off < 16; off <<= 1) rbeta[r] += __shfl_xor(rbeta[r], off);
     }
     if (idx == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rw + 4 * grp + r;
-        atomicAdd(&sga[t], rsum[r]);
-        atomicAdd(&sdc[t], rdB[r]);
-        atomicAdd(&sbt[t], rbeta[r]);
-      }
+      for (int r = 0; r < 4; ++r) atomicAdd(&sbt[rw + 4 * grp + r], rbeta[r]);
     }
     // <H, dH'> over the whole head
     float hdh = 0.f;
@@ -661,14 +709,14 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
     }
     // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dS + dS^T) K  (this wave's tiles)
 #pragma unroll
-    for (int u = 0; u < NBH; ++u) {
-      const int c0 = 16 * (ch * NBH + u);
-      dq[u] = tile_mma([&](int i, int kk) { return sPG[rw + i][kk]; },
-                       [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
-      dk[u] = tile_mma([&](int i, int kk) { return sPG[kk][rw + i]; },
-                       [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
-      dk[u] = tile_mma([&](int i, int kk) { return sDS[rw + i][kk] + sDS[kk][rw + i]; },
-                       [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
+    for (int u = 0; u < RPW; ++u) {
+      const int c0 = 16 * ctw, r0 = 16 * (rt0 + u);
+      dq[u] = tile_mma_rolled([&](int i, int kk) { return sPG[r0 + i][kk]; },
+                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
+      dk[u] = tile_mma_rolled([&](int i, int kk) { return sPG[kk][r0 + i]; },
+                              [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
+      dk[u] = tile_mma_rolled([&](int i, int kk) { return sDS[r0 + i][kk] + sDS[kk][r0 + i]; },
+                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
     }
     __syncthreads();  // LDS reused by the next V head
   }
@@ -676,12 +724,12 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   InT* dQo = static_cast<InT*>(p.dq);
   InT* dKo = static_cast<InT*>(p.dk);
 #pragma unroll
-  for (int u = 0; u < NBH; ++u) {
+  for (int u = 0; u < RPW; ++u) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = rw + 4 * grp + r;
+      const int t = 16 * (rt0 + u) + 4 * grp + r;
       if (t < L) {
-        const size_t off = ((size_t)(t0 + t) * p.hqk + m) * D + 16 * (ch * NBH + u) + idx;
+        const size_t off = ((size_t)(t0 + t) * p.hqk + m) * D + 16 * ctw + idx;
         dQo[off] = from_f32<InT>(dq[u][r]);
         dKo[off] = from_f32<InT>(dk[u][r]);
       }
@@ -712,7 +760,7 @@ template <typename InT, typename OT, int D>
 hipError_t launch_bwd_t(const gdn_shape_t& s, BwdParams p, hipStream_t stream) {
   const unsigned slot_blocks_v = (unsigned)(p.num_slots * p.hv);
   const unsigned slot_blocks_qk = (unsigned)(p.num_slots * p.hqk);
-  const unsigned scan_blocks = (unsigned)(s.num_seqs * s.num_v_heads * (D / 16));
+  const unsigned scan_blocks = (unsigned)(8 * (D / 16) * ((s.num_seqs * s.num_v_heads + 7) / 8));
   if (s.total_tokens > 0) {
     hipLaunchKernelGGL((bwd_intra_kernel<InT, D>), dim3(slot_blocks_v), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();

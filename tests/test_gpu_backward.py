@@ -120,3 +120,15 @@ def test_backward_full_size_sampled_heads():
         check(gs, rv, TOL["f32"], f"1x4096 {name}")
     # no initial state given: dh0 is still the gradient of the (zero) initial state
     assert_rms_close(got[5][:, v_heads].cpu(), ref[5], TOL["f32"], "1x4096 dh0")
+
+
+def test_backward_all_sequences_empty():
+    # no tokens: every gradient is empty and dh0 is the final-state gradient passed through
+    hqk, hv, d = 1, 2, 32
+    case = si.make_core_case([0, 0], hqk, hv, d, d, dtype="f32", seed=1)
+    dout = torch.zeros((0, hv, d))
+    dht = torch.from_numpy(np.random.default_rng(2).standard_normal((2, hv, d, d))).float()
+    got = _run(case, dout, dht, None, 1.0)
+    torch.cuda.synchronize()
+    assert all(t.shape[0] == 0 for t in got[:5])
+    assert torch.equal(got[5].cpu(), dht)
