@@ -192,9 +192,6 @@ __device__ __forceinline__ bool slot_chunk(const BwdParams& p, int slot, int& n,
 // ---- bwd_intra ------------------------------------------------------------------------------
 template <typename InT, int D>
 __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
-  constexpr int KP = D + 4;  // padded row of the staged q / k rows
-  __shared__ float sK[kC][KP];
-  __shared__ float sQ[kC][KP];
   __shared__ float sA[kC][kC + 1];
   __shared__ float sT[kC][kC + 1];
   __shared__ double sb[kC];
@@ -210,12 +207,6 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
 
   const InT* Q = static_cast<const InT*>(p.q);
   const InT* K = static_cast<const InT*>(p.k);
-  for (int e = tid; e < kC * D; e += 256) {
-    const int i = e / D, c = e % D;
-    const bool ok = i < L;
-    sK[i][c] = ok ? to_f32(K[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
-    sQ[i][c] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
-  }
   if (wave == 0) {  // b = inclusive cumsum of g (0 past the end: identity steps)
     const double gi = lane < L ? (double)p.g[(size_t)(t0 + lane) * p.hv + h] : 0.0;
     const double bi = wave_inclusive_scan_f64(gi, lane);
@@ -225,11 +216,16 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // wave w: rows 16 w .. 16 w + 15 of S = K K^T and Q K^T
+  // wave w: rows 16 w .. 16 w + 15 of S = K K^T and Q K^T, the q / k rows read from global
+  // memory as 16-byte fragments (rows past the chunk end: zeros as A rows; as B rows they read
+  // row 0 and land only in masked entries, j > t).
+  auto krow = [&](int i) { return K + ((size_t)(t0 + (i < L ? i : 0)) * p.hqk + m) * D; };
+  const int ra = 16 * wave + idx;
+  const InT* a_k = ra < L ? K + ((size_t)(t0 + ra) * p.hqk + m) * D : nullptr;
+  const InT* a_q = ra < L ? Q + ((size_t)(t0 + ra) * p.hqk + m) * D : nullptr;
   for (int ct = 0; ct < 4; ++ct) {
-    const f32x4 s = tile_mma_rows(&sK[16 * wave + idx][0], 1.f, &sK[16 * ct + idx][0], D, zero4());
-    const f32x4 qk = tile_mma_rows(&sQ[16 * wave + idx][0], 1.f, &sK[16 * ct + idx][0], D,
-                                   zero4());
+    const f32x4 s = tile_mma_rows(a_k, 1.f, krow(16 * ct + idx), D, zero4());
+    const f32x4 qk = tile_mma_rows(a_q, 1.f, krow(16 * ct + idx), D, zero4());
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * wave + 4 * grp + r, j = 16 * ct + idx;
