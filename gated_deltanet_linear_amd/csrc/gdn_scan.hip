@@ -172,23 +172,29 @@ struct VRows<float> {
 // (NC waves), NP producer waves stage the chunks and store the outputs.
 //
 // A staged chunk (one LDS buffer) holds, in 1 KiB units:
-//   [0, KI)            K rows, row-major, 16-byte XOR swizzle (swz)
-//   [KI, 2 KI)         Q rows, same layout
-//   [2 KI, 2 KI + RI)  the workspace record of the chunk (T diag(beta), P, gamma, delta)
-//   [2 KI + RI, TOTAL) the v rows of the workgroup's NT * 16 columns, row stride VSTR
+//   [0, KI)              K rows, row-major, 16-byte XOR swizzle (swz)
+//   [KI, KQ)             Q rows, same layout
+//   [KQ, KQ + RI)        the workspace record of the chunk (T diag(beta), P, gamma, delta)
+//   [KQ + RI, TOTAL)     the v rows of the workgroup's NT * 16 columns, row stride VSTR
+// RREC (row-split bf16 layout): a compute wave uses only its own row tile's blocks of the
+// record, so it loads them from global memory itself, one chunk ahead, into registers, and
+// the chunk buffer holds no record (RI = 0). (Loading the wave's own K / Q row fragments the
+// same way, instead of staging Q, measured slower.)
 // Rows past the end of a sequence re-read its last row (finite values that only ever meet zero
 // coefficients); record lanes past its end re-read its last 16 bytes into the padding.
 template <typename Mode, int D, int NT, int RW, typename OutT>
 struct ScanCfg {
   using in_t = typename Mode::in_t;
+  static constexpr bool RREC = RW > 1 && std::is_same<Mode, Bf16Mode>::value;
   static constexpr int ROWB = D * (int)sizeof(in_t), KBYTES = 64 * ROWB;
   static constexpr int NCH = ROWB / 16, RPU = 64 / NCH;  // 16-byte chunks per row, rows per unit
-  static constexpr int KI = KBYTES / 1024, RI = kRecStage / 1024;
+  static constexpr int KI = KBYTES / 1024, RI = RREC ? 0 : kRecStage / 1024;
+  static constexpr int KQ = 2 * KI;  // K and Q units
   static constexpr int VROWB = 16 * (int)sizeof(in_t), VPR = VROWB / 16;  // one tile row of v
   static constexpr int VSTR = NT * VROWB + (NT > 1 ? 16 : 0);  // padded: tile reads spread banks
   static constexpr int VI = 64 * NT * VPR / 64;                // v units
-  static constexpr int TOTAL = 2 * KI + RI + VI;
-  static constexpr int QOFF = KBYTES, ROFF = 2 * KBYTES, VOFF = 2 * KBYTES + kRecStage;
+  static constexpr int TOTAL = KQ + RI + VI;
+  static constexpr int QOFF = KBYTES, ROFF = 1024 * KQ, VOFF = 1024 * (KQ + RI);
   static constexpr int BUFB = VOFF + 64 * VSTR;
   static constexpr int NC = NT * RW;
   static constexpr int NP = (TOTAL + 31) / 32;  // producers hold <= 32 units each in registers
@@ -295,16 +301,16 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
             // Uniform base + 32-bit lane offset (one VGPR per address in flight).
             const char* base;
             unsigned off;
-            if (j < 2 * C::KI) {
+            if (j < C::KQ) {
               const int jj = j < C::KI ? j : j - C::KI;
               const int row = jj * C::RPU + lane / C::NCH;
               base = j < C::KI ? Kb : Qb;
               off = min(row, lenc - 1) * rs + 16 * ((lane % C::NCH) ^ swz<C::ROWB>(row));
-            } else if (j < 2 * C::KI + C::RI) {
+            } else if (j < C::KQ + C::RI) {
               base = rec;
-              off = 16 * min(64 * (j - 2 * C::KI) + lane, kRecUnits - 1);
+              off = 16 * min(64 * (j - C::KQ) + lane, kRecUnits - 1);
             } else {
-              const int i = 64 * (j - 2 * C::KI - C::RI) + lane;
+              const int i = 64 * (j - C::KQ - C::RI) + lane;
               const int row = i / (NT * C::VPR), cp = i % (NT * C::VPR);
               base = Vb;
               off = min(row, lenc - 1) * vrs + 16 * cp;
@@ -319,10 +325,10 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           const int j = PW + C::NP * u;
           if (j < C::TOTAL) {
             int dst;
-            if (j < 2 * C::KI + C::RI) {
+            if (j < C::KQ + C::RI) {
               dst = 1024 * j + 16 * lane;
             } else {
-              const int i = 64 * (j - 2 * C::KI - C::RI) + lane;
+              const int i = 64 * (j - C::KQ - C::RI) + lane;
               dst = C::VOFF + (i / (NT * C::VPR)) * C::VSTR + 16 * (i % (NT * C::VPR));
             }
             *reinterpret_cast<f32x4*>(buf + dst) = r[u];
@@ -423,10 +429,37 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     }
   }
 
-  for (int c = 0; c < nchunks; ++c) {
+  // RREC: this wave's blocks of the chunk's workspace record (row tile rt = rg): T diag(beta)
+  // and P, gamma, delta and gamma_C, loaded one chunk ahead. Every fetch issues the same loads
+  // with no branch (row tiles 0 and 1 also load a second, unused block; the last chunk
+  // re-loads itself), so that the compiler's wait counts stay exact: after a path with fewer
+  // loads in flight it would wait for all of them, the next chunk's included.
+  struct Rec {
+    Op TB[2], PB[2];
+    f32x4 gam, del;
+    float gC;
+  };
+  const int slot0 = slot_base(p.cu, n);
+  auto fetch = [&](int c, Rec& f) __attribute__((always_inline)) {
+    if constexpr (C::RREC) {
+      const int rt = rg;
+      const char* rec = p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f.TB[kb] = Mode::load_block(rec + kWsTOff + tri_block(rt, kb) * kWsBlockBytes, lane);
+        f.PB[kb] = Mode::load_block(rec + kWsPOff + tri_block(rt, kb) * kWsBlockBytes, lane);
+      }
+      f.gam = *reinterpret_cast<const f32x4*>(rec + kWsGOff + 4 * (16 * rt + 4 * grp));
+      f.del = *reinterpret_cast<const f32x4*>(rec + kWsDOff + 4 * (16 * rt + 4 * grp));
+      f.gC = reinterpret_cast<const float*>(rec + kWsGOff)[kChunk - 1];
+    }
+  };
+
+  auto body = [&](int c, const Rec& cur, Rec& nxt) __attribute__((always_inline)) {
     const int len = min(kChunk, L - kChunk * c);
     lds_barrier();  // chunk c staged (double buffer); state blocks of chunk c-1 exchanged
     if constexpr (C::NBUF == 1) lds_barrier();  // chunk c staged
+    if constexpr (C::RREC) fetch(min(c + 1, nchunks - 1), nxt);
     const char* const S = chunk_buf(c);
     const char* sK = S;
     const char* sQ = S + C::QOFF;
@@ -435,14 +468,23 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     const float* sgam = reinterpret_cast<const float*>(sR + kWsGOff);
     const float* sdel = reinterpret_cast<const float*>(sR + kWsDOff);
     char* const Wc = Wo + (c & 1) * C::OBYTES + tile * C::OROWB;
+    // Operand accessors: RREC waves use the fetched registers (rt is always their own).
     auto tblock = [&](int rt, int kb) -> Op {
+      if constexpr (C::RREC) return cur.TB[kb];
       return Mode::load_block(sR + kWsTOff + tri_block(rt, kb) * 2048, lane);
     };
     auto pblock = [&](int rt, int kb) -> Op {
+      if constexpr (C::RREC) return cur.PB[kb];
       return Mode::load_block(sR + kWsPOff + tri_block(rt, kb) * 2048, lane);
     };
-    auto gamma4 = [&](int rt) { return *reinterpret_cast<const f32x4*>(sgam + 16 * rt + 4 * grp); };
-    auto delta4 = [&](int rt) { return *reinterpret_cast<const f32x4*>(sdel + 16 * rt + 4 * grp); };
+    auto gamma4 = [&](int rt) -> f32x4 {
+      if constexpr (C::RREC) return cur.gam;
+      return *reinterpret_cast<const f32x4*>(sgam + 16 * rt + 4 * grp);
+    };
+    auto delta4 = [&](int rt) -> f32x4 {
+      if constexpr (C::RREC) return cur.del;
+      return *reinterpret_cast<const f32x4*>(sdel + 16 * rt + 4 * grp);
+    };
 
     // (a) state as split B fragments over d_k
     Op HB[KB];
@@ -608,7 +650,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     }
 
     // (g) owned state blocks first (the next chunk waits on them): H <- gamma_C H + K^T V''
-    const float gC = sgam[kChunk - 1];
+    const float gC = C::RREC ? cur.gC : sgam[kChunk - 1];
 #pragma unroll
     for (int o = 0; o < OWN; ++o) {
       const int kb = rg + RW * o;
@@ -649,6 +691,19 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       for (int r = 0; r < 4; ++r)
         reinterpret_cast<OutT*>(Wc + (16 * rt + 4 * grp + r) * C::OSTR)[idx] = from_f32<OutT>(o4[r]);
     }
+  };
+
+  Rec pa, pb;
+  if constexpr (C::RREC) {
+    // Two register sets, alternating by chunk: the loop is unrolled by two so that no copy
+    // of the fetched operands is needed.
+    if (nchunks > 0) fetch(0, pa);
+    for (int c = 0; c < nchunks; c += 2) {
+      body(c, pa, pb);
+      if (c + 1 < nchunks) body(c + 1, pb, pa);
+    }
+  } else {
+    for (int c = 0; c < nchunks; ++c) body(c, pa, pb);
   }
   lds_barrier();  // last chunk computed (the producers store its output rows)
 
