@@ -209,8 +209,7 @@ struct ScanCfg {
   static constexpr int OSTR = NT * OROWB + (NT > 1 ? 16 : 0);
   static constexpr int OBYTES = 64 * OSTR;
   static constexpr int OPIECES = 64 * NT * OPR, OST = (OPIECES + 64 * NP - 1) / (64 * NP);
-  static constexpr int SYNCB = RW > 1 ? 16 * NT : 0;  // arrival counters of the tile groups
-  static constexpr int FIXED = NT * XBYTES + 2 * OBYTES + SYNCB;
+  static constexpr int FIXED = NT * XBYTES + 2 * OBYTES;
   static constexpr int NBUF = 2 * BUFB + FIXED <= kLdsBytes ? 2 : 1;
   static constexpr int LDS = NBUF * BUFB + FIXED;
   static_assert(LDS <= kLdsBytes, "LDS budget");
@@ -230,7 +229,6 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   char* const Xbase = smem + C::NBUF * C::BUFB;
   char* const Wo = Xbase + NT * C::XBYTES;  // two output buffers of OBYTES
-  int* const sync_base = reinterpret_cast<int*>(Wo + 2 * C::OBYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -364,6 +362,12 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           lds_barrier();  // chunk c staged
           if (c + 1 < nchunks) load(c + 1);
         }
+        if constexpr (RW > 1) {
+          // the compute waves' Y and V' exchanges of chunk c (the producers' LDS writes are
+          // waited for at the next chunk's barrier)
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_s_barrier();
+        }
         if (c > 0) store_o(c - 1);
       }
       lds_barrier();  // last chunk computed
@@ -381,27 +385,12 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   const int tile = wave / RW, rg = wave % RW;
   const int col = 16 * (dvb * NT + tile) + idx;
   char* const X = Xbase + tile * C::XBYTES;
-  // The RW waves of a tile exchange Y and V' twice per chunk. They meet through an arrival
-  // counter in LDS rather than s_barrier, which would also wait for the producer waves;
-  // arriving and waiting are separate so that reads can be issued in between.
-  int* const sync_ctr = sync_base + 4 * tile;
-  if constexpr (RW > 1)
-    if (rg == 0 && lane == 0) *sync_ctr = 0;  // ordered before first use by the first barrier
-  int sync_target = 0;
-  auto group_arrive = [&]() {
-    sync_target += RW;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's exchange writes are done
-    if (lane == 0) __hip_atomic_fetch_add(sync_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  };
-  auto group_wait = [&]() {
-    // LDS serves one CU in order: once the count is reached, the other waves' writes are
-    // visible. A tight loop (no s_sleep: the waits are short and a sleep quantum costs more
-    // than the reads); bounded so that a broken count can never hang the device.
-    for (int spin = 0; spin < (1 << 22); ++spin)
-      if (__hip_atomic_load(sync_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= sync_target)
-        break;
-    asm volatile("" ::: "memory");
-  };
+  // The RW waves of a tile exchange Y and V' twice per chunk, at two s_barriers that the
+  // producer waves also pass once their own work of the chunk allows it (an LDS arrival
+  // counter among the compute waves alone, with reads issued between arriving and waiting,
+  // measured 3% slower).
+  auto exchange = [&]() { lds_barrier(); };
+
 
   // Owned state blocks: kb = rg + RW * o; Hc[o][hf][r] = H[state_row(2 kb + hf, 4 grp + r)][col].
   f32x4 Hc[OWN][2];
@@ -542,9 +531,23 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       }
     }
 
-    // (c) Y as split B fragments over tokens (blocks of 32). The T diag(beta) blocks of (d)
-    // do not depend on Y: they are read while the row-split waves wait for each other (after
-    // this wave has announced its Y, so that the reads do not delay the announcement).
+    // K^T fragments of the state update (g) for this wave's state rows, over all 64 tokens.
+    constexpr bool KT_EARLY = EARLY && RW > 1;
+    frag_t kt[OWN][2][2];
+    auto load_kt = [&]() {
+#pragma unroll
+      for (int o = 0; o < OWN; ++o) {
+        const int kb = rg + RW * o;
+        if (kb < KB)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int kbp = 0; kbp < 2; ++kbp) kt[o][hf][kbp] = F::kt(sK, 2 * kb + hf, kbp, lane);
+      }
+    };
+    // (c) Y as split B fragments over tokens (blocks of 32). Row-split layout: the waves
+    // exchange their Y rows; the T diag(beta) blocks of (d) are then in registers (bf16) or
+    // read from the staged record, and the K^T fragments of (g) are read while (d) runs.
     Op TB[R][2];
     auto load_t = [&]() {
 #pragma unroll
@@ -570,12 +573,12 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         const int rt = rg * R + i;
         store_half(Mode{}, X + C::XY + (rt >> 1) * 2048, lane, rt & 1, Y[i]);
       }
-      group_arrive();
+      exchange();
       load_t();
-      group_wait();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         if (2 * kb <= rg * R + R - 1) YB[kb] = Mode::load_block(X + C::XY + kb * 2048, lane);
+      load_kt();
     }
 
     // (d) V' = (T diag(beta)) Y on this wave's row tiles (block lower triangular)
@@ -590,12 +593,10 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       Vp[i] = acc;
     }
 
-    // (e) V' and V'' = diag(e^{b_C - b}) V' as split B fragments over tokens. The P blocks of
-    // (f) and, in the row-split layout, the K^T fragments of (g) are read like the T blocks.
-    constexpr bool KT_EARLY = EARLY && RW > 1;
+    // (e) V' and V'' = diag(e^{b_C - b}) V' as split B fragments over tokens (row-split
+    // layout: exchanged). The P blocks of (f) are taken like the T blocks.
     Op PB[R][2];
-    frag_t kt[OWN][2][2];
-    auto load_p_kt = [&]() {
+    auto load_p = [&]() {
 #pragma unroll
       for (int i = 0; i < (EARLY ? R : 0); ++i) {
         const int rt = rg * R + i;
@@ -603,22 +604,10 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         for (int kb = 0; kb < 2; ++kb)
           if (kb <= (rt >> 1)) PB[i][kb] = pblock(rt, kb);
       }
-      if constexpr (KT_EARLY) {
-#pragma unroll
-        for (int o = 0; o < OWN; ++o) {
-          const int kb = rg + RW * o;
-          if (kb < KB)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-              for (int kbp = 0; kbp < 2; ++kbp)
-                kt[o][hf][kbp] = F::kt(sK, 2 * kb + hf, kbp, lane);
-        }
-      }
     };
     Op VB[2], DB[2];
     if constexpr (RW == 1) {
-      load_p_kt();
+      load_p();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float x[8], d[8];
@@ -639,9 +628,8 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         store_half(Mode{}, X + C::XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
         store_half(Mode{}, X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
       }
-      group_arrive();
-      load_p_kt();
-      group_wait();
+      exchange();
+      load_p();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb <= rg * R + R - 1) VB[kb] = Mode::load_block(X + C::XV + kb * 2048, lane);
