@@ -158,7 +158,14 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
 #pragma unroll
   for (int j = 0; j < 3; ++j) hist[j].load(X + (size_t)max(t_first - 3 + j, 0) * conv_dim);
 #pragma unroll
-  for (int j = 0; j < TPT; ++j) rows[j].load(X + (size_t)min(t_first + j, p.T - 1) * conv_dim);
+  for (int j = 0; j < TPT; ++j) {
+    // nontemporal, except the last 3 rows: the next token lane's run reads them as history
+    const InT* row = X + (size_t)min(t_first + j, p.T - 1) * conv_dim;
+    if (j < TPT - 3)
+      rows[j].load_nt(row);
+    else
+      rows[j].load(row);
+  }
   // Taps and bias after the rows, so that waiting for them does not hold back the row loads.
   float w[8][4], bias[8];
   {
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] *= inv;
     }
-    store8(dst + (size_t)t * dst_stride, y);
+    store8_nt(dst + (size_t)t * dst_stride, y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       xm3[e] = xm2[e];
