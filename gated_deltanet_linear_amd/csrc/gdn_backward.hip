@@ -290,19 +290,41 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
 }
 
 // ---- bwd_scan: states forward, state gradients in reverse ---------------------------------
+// One 4-wave workgroup per (sequence, V head, 16-column tile); wave w owns token rows
+// 16 w .. 16 w + 15 of the chunk products and d_k row tiles w, w + 4 of the carried tile.
+// Operands are laid out in LDS so that an MFMA fragment (8 values along the depth) is two 16-byte
+// reads: the carried tile and the 16-column operands (v or dO^, Y or dV', V' or Z) are stored
+// transposed (a row per column, contiguous along the depth), T and P row-major in the forward
+// pass and transposed in the reverse pass (whose products take T^T and P^T). K^T and Q^T are
+// read element-wise from the row-major k / q rows.
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+// fragment of a row contiguous along the depth, each value scaled by sv[depth]
+__device__ __forceinline__ void row_frag_sv(const float* row, const float* sv, int k0, int grp,
+                                            f32x8& o) {
+  const f32x4 lo = ld4(row + k0 + 4 * grp), hi = ld4(row + k0 + 16 + 4 * grp);
+  const f32x4 slo = ld4(sv + k0 + 4 * grp), shi = ld4(sv + k0 + 16 + 4 * grp);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    o[s] = lo[s] * slo[s];
+    o[4 + s] = hi[s] * shi[s];
+  }
+}
+
 template <typename InT, typename OT, int D, bool REV>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
-  constexpr int KP = D + 4;
-  constexpr int NB = D / 16;  // column tiles per head
-  __shared__ float sK[kC][KP];
-  __shared__ float sQ[REV ? kC : 1][KP];
-  __shared__ float sT[kC][kC + 1];
-  __shared__ float sP[REV ? kC : 1][kC + 1];
-  __shared__ float sX[D][17];      // the carried d_k x 16 tile (state or state gradient)
-  __shared__ float sIn[kC][17];    // V (forward) or dO^ (reverse) columns of the tile
-  __shared__ float sW[kC][17];     // Y (forward) or dV' (reverse)
-  __shared__ float sZ[kC][17];     // V' (forward) or Z (reverse)
-  __shared__ float sgam[kC], sdel[kC], sbeta[kC];
+  constexpr int KP = D + 4;    // k / q rows and the transposed carried tile
+  constexpr int CP = kC + 4;   // rows along the tokens
+  constexpr int NB = D / 16;   // column tiles per head
+  __shared__ __attribute__((aligned(16))) float sK[kC][KP];
+  __shared__ __attribute__((aligned(16))) float sQ[REV ? kC : 1][KP];
+  __shared__ __attribute__((aligned(16))) float sT[kC][CP];            // T (forward), T^T (reverse)
+  __shared__ __attribute__((aligned(16))) float sP[REV ? kC : 1][CP];  // P^T (reverse)
+  __shared__ __attribute__((aligned(16))) float sXt[16][KP];  // carried tile (state / gradient)^T
+  __shared__ __attribute__((aligned(16))) float sInT[16][CP];  // (V or dO^ columns)^T
+  __shared__ __attribute__((aligned(16))) float sWt[16][CP];   // (Y or dV')^T
+  __shared__ __attribute__((aligned(16))) float sZt[16][CP];   // (V' or Z)^T
+  __shared__ __attribute__((aligned(16))) float sgam[kC], sdel[kC], sbeta[kC], sgb[kC];
   __shared__ float sgc;
 
   // The NB column tiles of one (sequence, V head) read the same chunk operands: keep them on one
@@ -315,6 +337,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   const int j0 = 16 * jt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int idx = lane & 15, grp = lane >> 4;
+  const int rw = 16 * wave;
   const int seq0 = p.cu[n], len = p.cu[n + 1] - seq0;
   const int nch = (len + kC - 1) / kC;
   const int sb0 = slot_base(p.cu, n);
@@ -324,7 +347,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   const void* init = REV ? p.dht : p.h0;
   for (int e = tid; e < D * 16; e += 256) {
     const int r = e / 16, c = e % 16;
-    sX[r][c] = init ? ld_state(init, st_base + (size_t)r * D + j0 + c, p.state_bf16) : 0.f;
+    sXt[c][r] = init ? ld_state(init, st_base + (size_t)r * D + j0 + c, p.state_bf16) : 0.f;
   }
   const InT* Q = static_cast<const InT*>(p.q);
   const InT* K = static_cast<const InT*>(p.k);
@@ -372,20 +395,28 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
       float x[8];
       rk[i].to(x);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sK[row][8 * c8 + u] = row < L ? x[u] : 0.f;
+      for (int u = 0; u < 8; ++u) x[u] = row < L ? x[u] : 0.f;
+      st4(&sK[row][8 * c8], f32x4{x[0], x[1], x[2], x[3]});
+      st4(&sK[row][8 * c8 + 4], f32x4{x[4], x[5], x[6], x[7]});
       if constexpr (REV) {
         rq[i].to(x);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sQ[row][8 * c8 + u] = row < L ? x[u] : 0.f;
+        for (int u = 0; u < 8; ++u) x[u] = row < L ? x[u] : 0.f;
+        st4(&sQ[row][8 * c8], f32x4{x[0], x[1], x[2], x[3]});
+        st4(&sQ[row][8 * c8 + 4], f32x4{x[4], x[5], x[6], x[7]});
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * (tid + 256 * i), r = e / kC, cc = e % kC;
+      if constexpr (REV) {  // transposed: the reverse products take T^T and P^T
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sT[r][cc + u] = rt[i][u];
-        if constexpr (REV) sP[r][cc + u] = rp[i][u];
+        for (int u = 0; u < 4; ++u) {
+          sT[cc + u][r] = rt[i][u];
+          sP[cc + u][r] = rp[i][u];
+        }
+      } else {
+        st4(&sT[r][cc], rt[i]);
       }
     }
     if (tid < 2 * kC) {
@@ -394,7 +425,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
       rin.to(x);
       const float sc = REV ? p.scale : 1.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sIn[row][8 * half + u] = row < L ? sc * x[u] : 0.f;
+      for (int u = 0; u < 8; ++u) sInT[8 * half + u][row] = row < L ? sc * x[u] : 0.f;
     }
   };
   if (nch > 0) load_chunk(REV ? nch - 1 : 0);
@@ -406,90 +437,118 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
     float* xs = (REV ? p.dhs : p.hs) + ((size_t)slot * p.hv + h) * D * D;
     for (int e = tid; e < D * 16; e += 256) {  // the tile at the chunk boundary
       const int r = e / 16, cc = e % 16;
-      xs[(size_t)r * D + j0 + cc] = sX[r][cc];
+      xs[(size_t)r * D + j0 + cc] = sXt[cc][r];
     }
     stage_chunk(L);
     if (ci + 1 < nch) load_chunk(REV ? c - 1 : c + 1);
     if (tid < kC) {
       const double* bb = rec_b(rec);
-      sgam[tid] = expf((float)bb[tid]);
+      const float gm = expf((float)bb[tid]);
+      const float bt = tid < L ? p.beta[(size_t)(t0 + tid) * p.hv + h] : 0.f;
+      sgam[tid] = gm;
       sdel[tid] = expf((float)(bb[kC - 1] - bb[tid]));
-      sbeta[tid] = tid < L ? p.beta[(size_t)(t0 + tid) * p.hv + h] : 0.f;
+      sbeta[tid] = bt;
+      sgb[tid] = -gm * bt;
       if (tid == 0) sgc = expf((float)bb[kC - 1]);
     }
     __syncthreads();
 
-    // rows 16 w .. 16 w + 15 of U = K X
-    const int rw = 16 * wave;
-    const f32x4 u = tile_mma([&](int i, int kk) { return sK[rw + i][kk]; },
-                             [&](int kk, int j) { return sX[kk][j]; }, D, zero4());
+    // rows rw .. rw + 15 of U = K X
+    f32x4 u = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 32) {
+      f32x8 av, bv;
+      row_frag(&sK[rw + idx][0], k0, grp, 1.f, av);
+      row_frag(&sXt[idx][0], k0, grp, 1.f, bv);
+      u = mma32(av, bv, u);
+    }
     if constexpr (!REV) {  // Y = V - diag(gamma) U
+      const f32x4 vv = ld4(&sInT[idx][rw + 4 * grp]), gm = ld4(&sgam[rw + 4 * grp]);
+      f32x4 y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r;
-        const float y = sIn[t][idx] - sgam[t] * u[r];
-        sW[t][idx] = y;
-        if (t < L) p.ys[((size_t)(t0 + t) * p.hv + h) * D + j0 + idx] = y;
+        y[r] = vv[r] - gm[r] * u[r];
+        if (t < L) p.ys[((size_t)(t0 + t) * p.hv + h) * D + j0 + idx] = y[r];
       }
+      st4(&sWt[idx][rw + 4 * grp], y);
     } else {  // dV' = P^T dO^ + diag(delta) U
-      const f32x4 pd = tile_mma([&](int i, int kk) { return sP[kk][rw + i]; },
-                                [&](int kk, int j) { return sIn[kk][j]; }, kC, zero4());
+      f32x4 pd = zero4();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rw + 4 * grp + r;
-        sW[t][idx] = pd[r] + sdel[t] * u[r];
+      for (int k0 = 0; k0 < kC; k0 += 32) {
+        f32x8 av, bv;
+        row_frag(&sP[rw + idx][0], k0, grp, 1.f, av);
+        row_frag(&sInT[idx][0], k0, grp, 1.f, bv);
+        pd = mma32(av, bv, pd);
       }
+      const f32x4 dl = ld4(&sdel[rw + 4 * grp]);
+      f32x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = pd[r] + dl[r] * u[r];
+      st4(&sWt[idx][rw + 4 * grp], w);
     }
     __syncthreads();
     if constexpr (!REV) {  // V' = T diag(beta) Y
-      const f32x4 vpr = tile_mma([&](int i, int kk) { return sT[rw + i][kk] * sbeta[kk]; },
-                                 [&](int kk, int j) { return sW[kk][j]; }, kC, zero4());
+      f32x4 vpr = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < kC; k0 += 32) {
+        f32x8 av, bv;
+        row_frag(&sT[rw + idx][0], k0, grp, 1.f, av);
+        row_frag_sv(&sWt[idx][0], sbeta, k0, grp, bv);
+        vpr = mma32(av, bv, vpr);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r;
-        sZ[t][idx] = vpr[r];
         if (t < L) p.vp[((size_t)(t0 + t) * p.hv + h) * D + j0 + idx] = vpr[r];
       }
+      st4(&sZt[idx][rw + 4 * grp], vpr);
     } else {  // Z = T^T dV';  dv = dY = diag(beta) Z
-      const f32x4 z = tile_mma([&](int i, int kk) { return sT[kk][rw + i]; },
-                               [&](int kk, int j) { return sW[kk][j]; }, kC, zero4());
+      f32x4 z = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < kC; k0 += 32) {
+        f32x8 av, bv;
+        row_frag(&sT[rw + idx][0], k0, grp, 1.f, av);
+        row_frag(&sWt[idx][0], k0, grp, 1.f, bv);
+        z = mma32(av, bv, z);
+      }
       InT* dV = static_cast<InT*>(p.dv);
+      const f32x4 bt = ld4(&sbeta[rw + 4 * grp]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r;
-        sZ[t][idx] = z[r];
         if (t < L) {
           const size_t off = ((size_t)(t0 + t) * p.hv + h) * D + j0 + idx;
           p.zs[off] = z[r];
-          dV[off] = from_f32<InT>(sbeta[t] * z[r]);
+          dV[off] = from_f32<InT>(bt[r] * z[r]);
         }
       }
+      st4(&sZt[idx][rw + 4 * grp], z);
     }
     __syncthreads();
-    // carried tile update, its 16-row tiles dealt to the waves
-    for (int rt = wave; rt < D / 16; rt += 4) {
+    // carried tile update, its 16-row tiles dealt to the waves (K^T, Q^T read element-wise)
+    for (int rt = wave; rt < NB; rt += 4) {
+      const f32x4 x0 = ld4(&sXt[idx][16 * rt + 4 * grp]);
       f32x4 acc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = sgc * sX[16 * rt + 4 * grp + r][idx];
+      for (int r = 0; r < 4; ++r) acc[r] = sgc * x0[r];
       if constexpr (!REV) {  // + K^T diag(delta) V'
         acc = tile_mma([&](int i, int kk) { return sK[kk][16 * rt + i]; },
-                       [&](int kk, int j) { return sdel[kk] * sZ[kk][j]; }, kC, acc);
+                       [&](int kk, int j) { return sdel[kk] * sZt[j][kk]; }, kC, acc);
       } else {  // + Q^T diag(gamma) dO^ - K^T diag(gamma) diag(beta) Z
         acc = tile_mma([&](int i, int kk) { return sQ[kk][16 * rt + i]; },
-                       [&](int kk, int j) { return sgam[kk] * sIn[kk][j]; }, kC, acc);
+                       [&](int kk, int j) { return sgam[kk] * sInT[j][kk]; }, kC, acc);
         acc = tile_mma([&](int i, int kk) { return sK[kk][16 * rt + i]; },
-                       [&](int kk, int j) { return -sgam[kk] * sbeta[kk] * sZ[kk][j]; }, kC,
-                       acc);
+                       [&](int kk, int j) { return sgb[kk] * sZt[j][kk]; }, kC, acc);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sX[16 * rt + 4 * grp + r][idx] = acc[r];
+      st4(&sXt[idx][16 * rt + 4 * grp], acc);
     }
     __syncthreads();
   }
   if (REV && p.dh0) {
     for (int e = tid; e < D * 16; e += 256) {
       const int r = e / 16, c = e % 16;
-      st_state(p.dh0, st_base + (size_t)r * D + j0 + c, sX[r][c], p.state_bf16);
+      st_state(p.dh0, st_base + (size_t)r * D + j0 + c, sXt[c][r], p.state_bf16);
     }
   }
 }
