@@ -146,6 +146,43 @@ def _measure(torch, kernels, steps, warmup):
     return step_ms, wall_ms, kms
 
 
+def _cold_step_ms(torch, kernels, steps):
+    """Step time with the Infinity Cache (MALL, 256 MB) and the L2s emptied of the step's data
+    before every step: each step follows a read of a 1 GiB buffer. K (read, step) pairs and K
+    reads alone are timed back to back between events; the difference divided by K is the cold
+    step. (A read, not a write: a write would leave 1 GiB of dirty lines to be written back
+    during the step.)"""
+    stream = torch.cuda.current_stream()
+    buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        torch.sum(buf, dim=0, out=out)
+
+    def timed(with_step):
+        for _ in range(2):
+            flush()
+            if with_step:
+                for _, fn in kernels:
+                    fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            flush()
+            if with_step:
+                for _, fn in kernels:
+                    fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    both = timed(True)
+    alone = timed(False)
+    del buf
+    return both - alone, alone
+
+
 def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
     case = si.workload_case(cfg_id)
     dev = "cuda"
@@ -167,6 +204,7 @@ def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
                                 initial_state=h0, o=o, final_state=ht)),
     ]
     ev_ms, ms, kms = _measure(torch, kernels, steps, warmup)
+    cold_ms, flush_ms = _cold_step_ms(torch, kernels, steps)
     lengths = case.meta["lengths"]
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
@@ -182,7 +220,11 @@ def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
                               frac=round(Fscan / (scan_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 5),
                               traffic=_traffic(f"gdn_chunk_scan_{case.meta['workload']}"),
                               algorithmic_flops_per_launch=Fscan),
-                algorithmic=dict(flops=F, bytes=B))
+                algorithmic=dict(flops=F, bytes=B),
+                cold_cache=dict(ms_per_step=round(cold_ms, 5), tokens_per_s=round(T / (cold_ms / 1e3), 1),
+                                flush_read_ms=round(flush_ms, 5),
+                                method="each step after a 1 GiB read (caches hold none of its "
+                                       "data); (read + step) minus read, K each, HIP events"))
 
 
 def run_decode(torch, gdn, si, steps, warmup):
@@ -487,6 +529,7 @@ def main():
                             "qkv_dtype": "bf16", "out_dtype": "bf16", "state_dtype": "f32",
                             "initial_state": False, "final_state": True},
                     roofline=pre["roofline"], kernels_ms=pre["kernels_ms"],
+                    cold_cache=pre["cold_cache"],
                     path=dict(tflops=round(pre["path_tflops"], 3),
                               mfma_frac=round(pre["path_mfma_frac"], 5),
                               hbm_gbs=round(pre["path_hbm_gbs"], 1), **pre["algorithmic"]))
