@@ -15,9 +15,11 @@
 //           state cross waves through LDS (4x the waves for shapes with few sequences x heads).
 // Separate producer waves move the data: while chunk c is computed they write chunk c+1 (held
 // in their registers) into the free one of two LDS buffers, load chunk c+2, and store the output
-// rows of chunk c-1, so the compute waves never issue a global memory instruction in the chunk
-// loop. q/k rows are staged row-major with a 16-byte XOR swizzle; K^T operand fragments are read
-// from the same rows with ds_read_b64_tr_b16.
+// rows of chunk c-1; the compute waves' only global memory instructions in the chunk loop are
+// the row-split layout's loads of their own workspace-record blocks, one chunk ahead. q/k rows
+// are staged row-major with a 16-byte XOR swizzle; K^T operand fragments are read from the same
+// rows with ds_read_b64_tr_b16. In the row-split layout the waves of a tile exchange Y and V'
+// at two s_barriers per chunk that the producers also pass.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
 #include <cstdlib>
 #include <cstring>
