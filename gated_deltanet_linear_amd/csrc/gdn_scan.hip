@@ -728,17 +728,31 @@ hipError_t launch_scan_cfg(const ScanParams& p, long long heads, int G, hipStrea
   return hipGetLastError();
 }
 
-// GDN_SCAN_LAYOUT=rows|tiles overrides the choice below (both layouts compute bit-identical
-// results; the tests use it to check that).
+// GDN_SCAN_LAYOUT=rows|tiles|tiles8 overrides the choice below (all layouts compute
+// bit-identical results; the tests use it to check that). tiles8 applies where the 8-tile
+// workgroup exists (bf16 operands and output, d = 128) and means tiles elsewhere.
 int forced_layout() {
   static const int v = [] {
     const char* e = getenv("GDN_SCAN_LAYOUT");
     if (!e) return 0;
     if (!strcmp(e, "rows")) return 1;
     if (!strcmp(e, "tiles")) return 2;
+    if (!strcmp(e, "tiles8")) return 3;
     return 0;
   }();
   return v;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    cus[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+  }
+  return cus[dev];
 }
 
 template <typename Mode, int D, typename OutT>
@@ -747,10 +761,18 @@ hipError_t launch_scan_t(const gdn_shape_t& s, const ScanParams& p, hipStream_t 
   const int G = s.num_v_heads / s.num_qk_heads;
   constexpr int tiles = D / 16;
   // Few (sequence, head) chains: 4 waves per 16-column tile so that every SIMD gets work.
-  // Many chains: 1 wave per tile, 4 tiles per workgroup sharing the staged chunk.
+  // Many chains: 1 wave per tile, 4 tiles per workgroup sharing the staged chunk; with at least
+  // one chain per CU (bf16 operands and output, d = 128), all 8 tiles of a chain in one
+  // workgroup: two compute waves per SIMD and half the staging per tile, at one workgroup per
+  // CU (fewer chains would leave CUs idle).
   const int forced = forced_layout();
   if (forced == 1 || (forced == 0 && heads * tiles <= 512))
     return launch_scan_cfg<Mode, D, 1, 4, OutT>(p, heads, G, stream);
+  if constexpr (tiles % 8 == 0 && std::is_same<Mode, Bf16Mode>::value &&
+                std::is_same<OutT, bf16>::value) {
+    if (forced == 3 || (forced == 0 && heads >= device_cus()))
+      return launch_scan_cfg<Mode, D, 8, 1, OutT>(p, heads, G, stream);
+  }
   if constexpr (tiles % 4 == 0) return launch_scan_cfg<Mode, D, 4, 1, OutT>(p, heads, G, stream);
   else return launch_scan_cfg<Mode, D, 2, 1, OutT>(p, heads, G, stream);
 }

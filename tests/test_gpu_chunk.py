@@ -188,10 +188,11 @@ _LAYOUT_CONFIGS = [(dt, d) for dt in ("bf16", "f32") for d in (32, 64, 128)]
 
 
 def test_scan_layouts_are_bit_identical():
-    """Both scan layouts (row-split: 4 waves per d_v tile; tile-per-wave) for every input dtype,
-    output dtype and head size: identical bits, the tile layout within tolerance of the oracle,
-    and bf16 outputs equal to the fp32 outputs rounded. Each layout runs in a process of its own
-    (the layout is chosen once per process)."""
+    """The scan layouts (row-split: 4 waves per d_v tile; tile-per-wave with 4 tiles per
+    workgroup; tile-per-wave with all 8 tiles of a d = 128 chain per workgroup, bf16 in and out)
+    for every input dtype, output dtype and head size: identical bits, the tile layout within
+    tolerance of the oracle, and bf16 outputs equal to the fp32 outputs rounded. Each layout runs
+    in a process of its own (the layout is chosen once per process)."""
     import os
     import subprocess
     import sys
@@ -213,7 +214,7 @@ def test_scan_layouts_are_bit_identical():
         "torch.save(res, sys.argv[1])\n")
     outs = {}
     with tempfile.TemporaryDirectory() as td:
-        for layout in ("rows", "tiles"):
+        for layout in ("rows", "tiles", "tiles8"):
             path = os.path.join(td, layout + ".pt")
             env = dict(os.environ, GDN_SCAN_LAYOUT=layout)
             print(f"[layout] {layout}", flush=True)
@@ -225,6 +226,8 @@ def test_scan_layouts_are_bit_identical():
         for j, od in enumerate(("f32", "bf16")):
             (o_r, h_r), (o_t, h_t) = outs["rows"][2 * i + j], outs["tiles"][2 * i + j]
             assert torch.equal(o_r, o_t) and torch.equal(h_r, h_t), (dt, dd, od)
+            o_8, h_8 = outs["tiles8"][2 * i + j]
+            assert torch.equal(o_r, o_8) and torch.equal(h_r, h_8), (dt, dd, od, "tiles8")
         (o32, h32), (o16, h16) = outs["tiles"][2 * i], outs["tiles"][2 * i + 1]
         assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(h16, h32), (dt, dd)
         case = si.make_core_case([300, 64, 5], 2, 4, dd, dd, dtype=dt, gate="model",
