@@ -21,6 +21,7 @@
 // rows with ds_read_b64_tr_b16. In the row-split layout the waves of a tile exchange Y and V'
 // at two s_barriers per chunk that the producers also pass.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -743,16 +744,19 @@ int forced_layout() {
   return v;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (a write-once cache per device; concurrent first calls
+// store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int v = 0;
-    cus[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+    c = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return c;
 }
 
 template <typename Mode, int D, typename OutT>
