@@ -570,7 +570,8 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   __shared__ float sDS[kC][kC + 1];  // dS
   __shared__ double sb[kC];
   __shared__ float sbeta[kC], sgam[kC], sdel[kC];
-  __shared__ float sE[kC][kC + 1];   // E, then its row-wise exclusive prefix sums
+  __shared__ float sE[kC][kC + 1];   // E
+  __shared__ float sfe[8][kC];       // per wave: sum over its rows t >= s of sum_{j<s} E_tj
   __shared__ float sga[kC];          // gamma_t (<Q_t, R1_t> - <K_t, R2_t>)
   __shared__ float sdc[kC];          // delta_t <K_t, R3_t>
   __shared__ float sbt[kC];          // sum_j dA_tj At_tj
@@ -625,7 +626,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
     const float* my_Z = my_ok ? p.zs + row_off(rw + idx) : nullptr;
     // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (this wave's d_k column tile, RPW row tiles) into
     // dq, dk and the row sums of db. The state rows of the column tile are loaded once per depth
-    // step and shared by the row tiles.
+    // step and shared by the row tiles; the waves of the first row-tile group also sum
+    // H o dH' over them (each state element once).
+    float hdh = 0.f;
     {
       const int c0 = 16 * ctw;
       const float* hrow = H + (size_t)(c0 + idx) * D;
@@ -638,6 +641,10 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         f32x8 hb, dhb;
         row_frag(hrow, k0, grp, 1.f, hb);
         row_frag(dhrow, k0, grp, 1.f, dhb);
+        if (rt0 == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hdh = fmaf(hb[e], dhb[e], hdh);
+        }
 #pragma unroll
         for (int u = 0; u < RPW; ++u) {
           const int row = 16 * (rt0 + u) + idx;
@@ -708,22 +715,26 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) atomicAdd(&sbt[rw + 4 * grp + r], rbeta[r]);
     }
-    // <H, dH'> over the whole head
-    float hdh = 0.f;
-#pragma unroll 4
-    for (int e = tid; e < D * D; e += 512) hdh += H[e] * dH[e];
+    // <H, dH'> over the whole head: accumulated from the state fragments of the R products
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) hdh += __shfl_xor(hdh, off);
     if (lane == 0) sred[wave] = hdh;
-    // <Y_t, Z_t> of this wave's rows (column half 0 only)
+    // <Y_t, Z_t> of this wave's rows (column half 0 only; D / 16 consecutive values per lane)
     float yz[4] = {0.f, 0.f, 0.f, 0.f};
     if (ch == 0) {
+      constexpr int CPL = D / 16;  // values per lane
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r;
         if (t < L) {
-#pragma unroll 2
-          for (int c = idx; c < D; c += 16) yz[r] += p.ys[row_off(t) + c] * p.zs[row_off(t) + c];
+          const float* yr = p.ys + row_off(t) + CPL * idx;
+          const float* zr = p.zs + row_off(t) + CPL * idx;
+#pragma unroll
+          for (int c = 0; c < CPL; c += 2) {
+            const float2 y2 = *reinterpret_cast<const float2*>(yr + c);
+            const float2 z2 = *reinterpret_cast<const float2*>(zr + c);
+            yz[r] = fmaf(y2.x, z2.x, fmaf(y2.y, z2.y, yz[r]));
+          }
         }
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) yz[r] += __shfl_xor(yz[r], off);
@@ -737,20 +748,23 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         if (t < L) p.dbeta[(size_t)(t0 + t) * p.hv + h] = yz[r] + sbt[t];
       }
     }
-    if (tid < kC) {  // row t of E -> exclusive prefix sums along j
-      float acc = 0.f;
-      for (int j = 0; j < kC; ++j) {
-        const float e = sE[tid][j];
-        sE[tid][j] = acc;
-        acc += e;
+    {  // sum_{t >= s} sum_{j < s} E_tj: wave w takes rows 8 w .. 8 w + 7, lane = s; each row's
+       // exclusive prefix along j by a wave scan
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = 8 * wave + i;
+        const float e = sE[t][lane];
+        const float pre = wave_inclusive_scan(e, lane) - e;
+        if (t >= lane) part += pre;
       }
+      sfe[wave][lane] = part;
     }
     __syncthreads();
     if (wave == 0) {
-      const int sidx = lane;
-      // sum_{t >= s} sum_{j < s} E_tj = sum_{t >= s} prefix_t(s)
       float fe = 0.f;
-      for (int t = sidx; t < kC; ++t) fe += sE[t][sidx];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) fe += sfe[w][lane];
       // suffix sum of sga (reverse inclusive scan), prefix sum of sdc (exclusive)
       const float ga_rev = sga[kC - 1 - lane];  // lane l: row 63 - l
       const float suf = __shfl(wave_inclusive_scan(ga_rev, lane), kC - 1 - lane);
