@@ -564,8 +564,8 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   constexpr int NB = D / 16;
   constexpr int RPW = NB / 2;  // row tiles per wave in the R / dq / dk products
   static_assert(NB % 2 == 0 && 4 * NB == 8 * RPW, "tile split");
-  __shared__ float sK[kC][KP];
-  __shared__ float sQ[kC][KP];
+  __shared__ __attribute__((aligned(16))) float sK[kC][KP];
+  __shared__ __attribute__((aligned(16))) float sQ[kC][KP];
   __shared__ float sPG[kC][kC + 1];  // dP o Gamma
   __shared__ float sDS[kC][kC + 1];  // dS
   __shared__ double sb[kC];
@@ -591,11 +591,32 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   const InT* Q = static_cast<const InT*>(p.q);
   const InT* K = static_cast<const InT*>(p.k);
   const OT* dO = static_cast<const OT*>(p.dout);
-  for (int e = tid; e < kC * D; e += 512) {
-    const int i = e / D, c = e % D;
-    const bool ok = i < L;
-    sK[i][c] = ok ? to_f32(K[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
-    sQ[i][c] = ok ? to_f32(Q[((size_t)(t0 + i) * p.hqk + m) * D + c]) : 0.f;
+  {  // k / q rows of the chunk as 8-value pieces, every load of a thread issued at once
+    constexpr int NPc = kC * D / 8, PPT = (NPc + 511) / 512;
+    Raw8<InT> rk[PPT], rq[PPT];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + 512 * u, i = e / (D / 8), c8 = e % (D / 8);
+      if (e < NPc) {
+        const size_t off = ((size_t)(t0 + (i < L ? i : 0)) * p.hqk + m) * D + 8 * c8;
+        rk[u].load(K + off);
+        rq[u].load(Q + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = tid + 512 * u, i = e / (D / 8), c8 = e % (D / 8);
+      if (e < NPc) {
+        float xk[8], xq[8];
+        rk[u].to(xk);
+        rq[u].to(xq);
+        const bool ok = i < L;
+        *reinterpret_cast<f32x4*>(&sK[i][8 * c8]) = ok ? f32x4{xk[0], xk[1], xk[2], xk[3]} : zero4();
+        *reinterpret_cast<f32x4*>(&sK[i][8 * c8 + 4]) = ok ? f32x4{xk[4], xk[5], xk[6], xk[7]} : zero4();
+        *reinterpret_cast<f32x4*>(&sQ[i][8 * c8]) = ok ? f32x4{xq[0], xq[1], xq[2], xq[3]} : zero4();
+        *reinterpret_cast<f32x4*>(&sQ[i][8 * c8 + 4]) = ok ? f32x4{xq[4], xq[5], xq[6], xq[7]} : zero4();
+      }
+    }
   }
 
   f32x4 dq[RPW], dk[RPW];
@@ -686,6 +707,16 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
     }
     // dP = dO^ V'^T (lower-incl), dA = -Z V'^T (strictly lower): this wave's two column tiles
     float rbeta[4] = {0.f, 0.f, 0.f, 0.f};
+    float at_v[2][4], pm_v[2][4];  // this lane's At and P entries, loaded ahead of the products
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rw + 4 * grp + r, j = 16 * (2 * ch + u) + idx;
+        at_v[u][r] = At[t * kC + j];
+        pm_v[u][r] = Pm[t * kC + j];
+      }
+#pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int c0 = 16 * (2 * ch + u);
       // V' rows past the chunk end are read as row 0 of the chunk and masked below
@@ -698,10 +729,10 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         const float gam = t >= j ? expf((float)(sb[t] - sb[j])) : 0.f;
         const float dPm = t >= j ? dp[r] : 0.f;
         const float dAm = t > j ? -za[r] : 0.f;
-        const float at = At[t * kC + j];
+        const float at = at_v[u][r];
         sPG[t][j] = dPm * gam;
         sDS[t][j] = dAm * sbeta[t] * gam;
-        sE[t][j] = dPm * Pm[t * kC + j] + dAm * sbeta[t] * at;
+        sE[t][j] = dPm * pm_v[u][r] + dAm * sbeta[t] * at;
         rbeta[r] += dAm * at;
       }
     }
