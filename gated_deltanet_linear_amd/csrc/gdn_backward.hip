@@ -180,6 +180,22 @@ __device__ __forceinline__ f32x4 tile_mma_rows(const TA* a_row, float a_scale, c
   return acc;
 }
 
+// tile_mma_rows with a valid A row always (rows past the chunk end pass row 0 with scale 0):
+// no branch, so that the loads of all depth steps can be in flight together.
+template <typename TA, typename TB>
+__device__ __forceinline__ f32x4 tile_mma_rows_s(const TA* a_row, float a_scale, const TB* b_row,
+                                                 int K, f32x4 acc) {
+  const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f32x8 av, bv;
+    row_frag(a_row, k0, grp, a_scale, av);
+    row_frag(b_row, k0, grp, 1.f, bv);
+    acc = mma32(av, bv, acc);
+  }
+  return acc;
+}
+
 // (sequence, first token, valid rows) of chunk slot `slot`; false for an unused slot.
 __device__ __forceinline__ bool slot_chunk(const BwdParams& p, int slot, int& n, int& t0, int& L) {
   n = slot_to_seq(p.cu, p.num_seqs, slot);
@@ -641,66 +657,78 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
     __syncthreads();
 
     auto row_off = [&](int t) { return ((size_t)(t0 + t) * p.hv + h) * D; };
-    // this lane's A rows (row rw + idx of the chunk; null past its end)
+    // this lane's A rows (row rw + idx of the chunk)
     const bool my_ok = rw + idx < L;
-    const OT* my_dO = my_ok ? dO + row_off(rw + idx) : nullptr;
-    const float* my_Z = my_ok ? p.zs + row_off(rw + idx) : nullptr;
+    const OT* my_dO = dO + row_off(my_ok ? rw + idx : 0);  // zero scale past the chunk end
+    const float* my_Z = p.zs + row_off(my_ok ? rw + idx : 0);
     // R1 = dO^ H^T, R2 = dY H^T, R3 = V' dH'^T (this wave's d_k column tile, RPW row tiles) into
     // dq, dk and the row sums of db. The state rows of the column tile are loaded once per depth
     // step and shared by the row tiles; the waves of the first row-tile group also sum
     // H o dH' over them (each state element once).
     float hdh = 0.f;
     {
+      // row tiles in passes of UB (the state fragments are read again per pass, from the cache):
+      // the accumulators and the operands of one depth step stay within the register budget
+      constexpr int UB = RPW < 2 ? RPW : 2;
       const int c0 = 16 * ctw;
       const float* hrow = H + (size_t)(c0 + idx) * D;
       const float* dhrow = dH + (size_t)(c0 + idx) * D;
-      f32x4 r1[RPW], r2[RPW], r3[RPW];
-#pragma unroll
-      for (int u = 0; u < RPW; ++u) r1[u] = r2[u] = r3[u] = zero4();
 #pragma unroll 1
-      for (int k0 = 0; k0 < D; k0 += 32) {
-        f32x8 hb, dhb;
-        row_frag(hrow, k0, grp, 1.f, hb);
-        row_frag(dhrow, k0, grp, 1.f, dhb);
-        if (rt0 == 0) {
+      for (int ub = 0; ub < RPW; ub += UB) {
+        f32x4 r1[UB], r2[UB], r3[UB];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) hdh = fmaf(hb[e], dhb[e], hdh);
+        for (int u = 0; u < UB; ++u) r1[u] = r2[u] = r3[u] = zero4();
+#pragma unroll 1
+        for (int k0 = 0; k0 < D; k0 += 32) {
+          f32x8 hb, dhb;
+          row_frag(hrow, k0, grp, 1.f, hb);
+          row_frag(dhrow, k0, grp, 1.f, dhb);
+          if (rt0 == 0 && ub == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hdh = fmaf(hb[e], dhb[e], hdh);
+          }
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            // rows past the chunk end read row 0 with a zero scale (no branch: the loads of the
+            // pass's row tiles are in flight together)
+            const int row = 16 * (rt0 + ub + u) + idx;
+            const bool ok = row < L;
+            const int rr = ok ? row : 0;
+            f32x8 ao, az, av;
+            row_frag(dO + row_off(rr), k0, grp, ok ? p.scale : 0.f, ao);
+            row_frag(p.zs + row_off(rr), k0, grp, ok ? sbeta[row] : 0.f, az);
+            row_frag(p.vp + row_off(rr), k0, grp, ok ? 1.f : 0.f, av);
+            r1[u] = mma32(ao, hb, r1[u]);
+            r2[u] = mma32(az, hb, r2[u]);
+            r3[u] = mma32(av, dhb, r3[u]);
+          }
         }
 #pragma unroll
-        for (int u = 0; u < RPW; ++u) {
-          const int row = 16 * (rt0 + u) + idx;
-          f32x8 ao, az, av;
-          if (row < L) {
-            row_frag(dO + row_off(row), k0, grp, p.scale, ao);
-            row_frag(p.zs + row_off(row), k0, grp, sbeta[row], az);
-            row_frag(p.vp + row_off(row), k0, grp, 1.f, av);
-          } else {
+        for (int u = 0; u < UB; ++u) {
+          float rs[4], rd[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ao[e] = az[e] = av[e] = 0.f;
-          }
-          r1[u] = mma32(ao, hb, r1[u]);
-          r2[u] = mma32(az, hb, r2[u]);
-          r3[u] = mma32(av, dhb, r3[u]);
-        }
-      }
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * (rt0 + ub + u) + 4 * grp + r, cc = c0 + idx;
+            const float dqv = sgam[t] * r1[u][r];
+            const float dkv = sdel[t] * r3[u][r] - sgam[t] * r2[u][r];
+            // dq / dk of row tile ub + u (a runtime index: selected per tile, kept in registers)
 #pragma unroll
-      for (int u = 0; u < RPW; ++u) {
-        float rs[4], rd[4];
+            for (int w = 0; w < RPW; ++w)
+              if (w == ub + u) {
+                dq[w][r] += dqv;
+                dk[w][r] += dkv;
+              }
+            rs[r] = sgam[t] * (sQ[t][cc] * r1[u][r] - sK[t][cc] * r2[u][r]);
+            rd[r] = sdel[t] * sK[t][cc] * r3[u][r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * (rt0 + u) + 4 * grp + r, cc = c0 + idx;
-          dq[u][r] += sgam[t] * r1[u][r];
-          dk[u][r] += sdel[t] * r3[u][r] - sgam[t] * r2[u][r];
-          rs[r] = sgam[t] * (sQ[t][cc] * r1[u][r] - sK[t][cc] * r2[u][r]);
-          rd[r] = sdel[t] * sK[t][cc] * r3[u][r];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            rs[r] += __shfl_xor(rs[r], off);
-            rd[r] += __shfl_xor(rd[r], off);
-          }
-          if (idx == 0) {
-            atomicAdd(&sga[t], rs[r]);
-            atomicAdd(&sdc[t], rd[r]);
+            for (int off = 1; off < 16; off <<= 1) {
+              rs[r] += __shfl_xor(rs[r], off);
+              rd[r] += __shfl_xor(rd[r], off);
+            }
+            if (idx == 0) {
+              atomicAdd(&sga[t], rs[r]);
+              atomicAdd(&sdc[t], rd[r]);
+            }
           }
         }
       }
@@ -721,8 +749,8 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
       const int c0 = 16 * (2 * ch + u);
       // V' rows past the chunk end are read as row 0 of the chunk and masked below
       const float* vprow = p.vp + row_off(c0 + idx < L ? c0 + idx : 0);
-      const f32x4 dp = tile_mma_rows(my_dO, p.scale, vprow, D, zero4());
-      const f32x4 za = tile_mma_rows(my_Z, 1.f, vprow, D, zero4());
+      const f32x4 dp = tile_mma_rows_s(my_dO, my_ok ? p.scale : 0.f, vprow, D, zero4());
+      const f32x4 za = tile_mma_rows_s(my_Z, my_ok ? 1.f : 0.f, vprow, D, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r, j = c0 + idx;
