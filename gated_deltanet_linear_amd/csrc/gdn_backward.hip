@@ -582,11 +582,17 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   static_assert(NB % 2 == 0 && 4 * NB == 8 * RPW, "tile split");
   __shared__ __attribute__((aligned(16))) float sK[kC][KP];
   __shared__ __attribute__((aligned(16))) float sQ[kC][KP];
-  __shared__ float sPG[kC][kC + 1];  // dP o Gamma
-  __shared__ float sDS[kC][kC + 1];  // dS
+  // One region serves two phases: the R products' operand slab (dO^, Z diag(beta) and V' of
+  // SR rows of the chunk over the whole depth, rows padded to SLD floats), then dP o Gamma, dS
+  // and E.
+  constexpr int SR = 32, SLD = D + 4;
+  constexpr int SLAB = 3 * SR * SLD, PGE = 3 * kC * (kC + 1);
+  __shared__ __attribute__((aligned(16))) float sU[SLAB > PGE ? SLAB : PGE];
+  float (*const sPG)[kC + 1] = reinterpret_cast<float (*)[kC + 1]>(sU);                // dP o Gamma
+  float (*const sDS)[kC + 1] = reinterpret_cast<float (*)[kC + 1]>(sU + kC * (kC + 1));  // dS
+  float (*const sE)[kC + 1] = reinterpret_cast<float (*)[kC + 1]>(sU + 2 * kC * (kC + 1));  // E
   __shared__ double sb[kC];
   __shared__ float sbeta[kC], sgam[kC], sdel[kC];
-  __shared__ float sE[kC][kC + 1];   // E
   __shared__ float sfe[8][kC];       // per wave: sum over its rows t >= s of sum_{j<s} E_tj
   __shared__ float sga[kC];          // gamma_t (<Q_t, R1_t> - <K_t, R2_t>)
   __shared__ float sdc[kC];          // delta_t <K_t, R3_t>
@@ -667,59 +673,80 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
     // H o dH' over them (each state element once).
     float hdh = 0.f;
     {
-      // row tiles in passes of UB (the state fragments are read again per pass, from the cache):
-      // the accumulators and the operands of one depth step stay within the register budget
-      constexpr int UB = RPW < 2 ? RPW : 2;
+      // The A operands are staged in LDS SR = 32 rows (two row tiles) at a time over the whole
+      // depth, with one coalesced load of each 16-byte piece (rows past the chunk end: zeros);
+      // each wave reads its state fragments from global memory once, for both row groups.
       const int c0 = 16 * ctw;
       const float* hrow = H + (size_t)(c0 + idx) * D;
       const float* dhrow = dH + (size_t)(c0 + idx) * D;
-#pragma unroll 1
-      for (int ub = 0; ub < RPW; ub += UB) {
-        f32x4 r1[UB], r2[UB], r3[UB];
+      constexpr int KS = D / 32, PR = D / 4, NPS = 3 * SR * PR, PPS = (NPS + 511) / 512;
+      constexpr int UPG = SR / 16;  // row tiles per group
+      f32x8 hb[KS], dhb[KS];
 #pragma unroll
-        for (int u = 0; u < UB; ++u) r1[u] = r2[u] = r3[u] = zero4();
-#pragma unroll 1
-        for (int k0 = 0; k0 < D; k0 += 32) {
-          f32x8 hb, dhb;
-          row_frag(hrow, k0, grp, 1.f, hb);
-          row_frag(dhrow, k0, grp, 1.f, dhb);
-          if (rt0 == 0 && ub == 0) {
+      for (int ks = 0; ks < KS; ++ks) {
+        row_frag(hrow, 32 * ks, grp, 1.f, hb[ks]);
+        row_frag(dhrow, 32 * ks, grp, 1.f, dhb[ks]);
+      }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) hdh = fmaf(hb[e], dhb[e], hdh);
-          }
+      for (int g0 = 0; g0 < kC; g0 += SR) {
+        f32x4 pc[PPS];
 #pragma unroll
-          for (int u = 0; u < UB; ++u) {
-            // rows past the chunk end read row 0 with a zero scale (no branch: the loads of the
-            // pass's row tiles are in flight together)
-            const int row = 16 * (rt0 + ub + u) + idx;
-            const bool ok = row < L;
-            const int rr = ok ? row : 0;
-            f32x8 ao, az, av;
-            row_frag(dO + row_off(rr), k0, grp, ok ? p.scale : 0.f, ao);
-            row_frag(p.zs + row_off(rr), k0, grp, ok ? sbeta[row] : 0.f, az);
-            row_frag(p.vp + row_off(rr), k0, grp, ok ? 1.f : 0.f, av);
-            r1[u] = mma32(ao, hb, r1[u]);
-            r2[u] = mma32(az, hb, r2[u]);
-            r3[u] = mma32(av, dhb, r3[u]);
+        for (int i = 0; i < PPS; ++i) {
+          const int pi = tid + 512 * i, op = pi / (SR * PR), row = g0 + (pi / PR) % SR;
+          const size_t off = row_off(row < L ? row : 0) + 4 * (pi % PR);
+          if (pi < NPS) {
+            if (op == 0) {
+              if constexpr (std::is_same<OT, bf16>::value) {
+                const bf16x4 b = *reinterpret_cast<const bf16x4*>(dO + off);
+                pc[i] = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+              } else {
+                pc[i] = *reinterpret_cast<const f32x4*>(dO + off);
+              }
+            } else {
+              pc[i] = *reinterpret_cast<const f32x4*>((op == 1 ? p.zs : p.vp) + off);
+            }
           }
         }
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
+        for (int i = 0; i < PPS; ++i) {
+          const int pi = tid + 512 * i, op = pi / (SR * PR), rl = (pi / PR) % SR, row = g0 + rl;
+          if (pi < NPS) {
+            const float sc = row >= L ? 0.f : op == 0 ? p.scale : op == 1 ? sbeta[row] : 1.f;
+            *reinterpret_cast<f32x4*>(sU + (op * SR + rl) * SLD + 4 * (pi % PR)) = pc[i] * sc;
+          }
+        }
+        __syncthreads();  // rows g0 .. g0 + SR - 1 staged
+        // this wave's row tiles of the group (rt0 .. rt0 + RPW - 1 intersected with the group)
+#pragma unroll
+        for (int uu = 0; uu < UPG; ++uu) {
+          const int rtile = g0 / 16 + uu, u = rtile - rt0;
+          if (u < 0 || u >= RPW) continue;  // uniform over the wave
+          const int rl = 16 * uu + idx;
+          f32x4 r1 = zero4(), r2 = zero4(), r3 = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            f32x8 ao, az, av;
+            row_frag(sU + rl * SLD, 32 * ks, grp, 1.f, ao);
+            row_frag(sU + (SR + rl) * SLD, 32 * ks, grp, 1.f, az);
+            row_frag(sU + (2 * SR + rl) * SLD, 32 * ks, grp, 1.f, av);
+            r1 = mma32(ao, hb[ks], r1);
+            r2 = mma32(az, hb[ks], r2);
+            r3 = mma32(av, dhb[ks], r3);
+          }
           float rs[4], rd[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int t = 16 * (rt0 + ub + u) + 4 * grp + r, cc = c0 + idx;
-            const float dqv = sgam[t] * r1[u][r];
-            const float dkv = sdel[t] * r3[u][r] - sgam[t] * r2[u][r];
-            // dq / dk of row tile ub + u (a runtime index: selected per tile, kept in registers)
+            const int t = 16 * rtile + 4 * grp + r, cc = c0 + idx;
+            const float dqv = sgam[t] * r1[r];
+            const float dkv = sdel[t] * r3[r] - sgam[t] * r2[r];
 #pragma unroll
             for (int w = 0; w < RPW; ++w)
-              if (w == ub + u) {
+              if (w == u) {
                 dq[w][r] += dqv;
                 dk[w][r] += dkv;
               }
-            rs[r] = sgam[t] * (sQ[t][cc] * r1[u][r] - sK[t][cc] * r2[u][r]);
-            rd[r] = sdel[t] * sK[t][cc] * r3[u][r];
+            rs[r] = sgam[t] * (sQ[t][cc] * r1[r] - sK[t][cc] * r2[r]);
+            rd[r] = sdel[t] * sK[t][cc] * r3[r];
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) {
               rs[r] += __shfl_xor(rs[r], off);
@@ -731,6 +758,13 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
             }
           }
         }
+        __syncthreads();  // group consumed
+      }
+      if (rt0 == 0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hdh = fmaf(hb[ks][e], dhb[ks][e], hdh);
       }
     }
     // dP = dO^ V'^T (lower-incl), dA = -Z V'^T (strictly lower): this wave's two column tiles
