@@ -327,21 +327,45 @@ __device__ __forceinline__ void row_frag_sv(const float* row, const float* sv, i
   }
 }
 
+// LDS of one scan pass. k / q rows are kept in the input dtype (bf16 exactly), rows padded to
+// 16 bytes; the fp32 operands rows padded by 4 floats.
+template <typename KT, int D, bool REV>
+struct BwdScanLds {
+  static constexpr int KP = D + 16 / (int)sizeof(KT);  // k / q rows
+  static constexpr int XP = D + 4;                     // the transposed carried tile
+  static constexpr int CP = kC + 4;                    // rows along the tokens
+  float sT[kC][CP];            // T (forward), T^T (reverse)
+  float sP[REV ? kC : 1][CP];  // P^T (reverse)
+  float sXt[16][XP];           // carried tile (state / gradient)^T
+  float sInT[16][CP];          // (V or dO^ columns)^T
+  float sWt[16][CP];           // (Y or dV')^T
+  float sZt[16][CP];           // (V' or Z)^T
+  float sgam[kC], sdel[kC], sbeta[kC], sgb[kC];
+  KT sK[kC][KP];
+  KT sQ[REV ? kC : 1][KP];
+  float sgc;
+};
+
+// One pass (forward states or reverse state gradients) on 4 waves; `tid` is the thread's index
+// among them. Every barrier of a pass is a workgroup barrier: a workgroup that runs both passes
+// side by side executes the same number in each.
 template <typename InT, typename OT, int D, bool REV>
-__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
-  constexpr int KP = D + 4;    // k / q rows and the transposed carried tile
-  constexpr int CP = kC + 4;   // rows along the tokens
+__device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
+                                              BwdScanLds<InT, D, REV>& S, int tid) {
   constexpr int NB = D / 16;   // column tiles per head
-  __shared__ __attribute__((aligned(16))) float sK[kC][KP];
-  __shared__ __attribute__((aligned(16))) float sQ[REV ? kC : 1][KP];
-  __shared__ __attribute__((aligned(16))) float sT[kC][CP];            // T (forward), T^T (reverse)
-  __shared__ __attribute__((aligned(16))) float sP[REV ? kC : 1][CP];  // P^T (reverse)
-  __shared__ __attribute__((aligned(16))) float sXt[16][KP];  // carried tile (state / gradient)^T
-  __shared__ __attribute__((aligned(16))) float sInT[16][CP];  // (V or dO^ columns)^T
-  __shared__ __attribute__((aligned(16))) float sWt[16][CP];   // (Y or dV')^T
-  __shared__ __attribute__((aligned(16))) float sZt[16][CP];   // (V' or Z)^T
-  __shared__ __attribute__((aligned(16))) float sgam[kC], sdel[kC], sbeta[kC], sgb[kC];
-  __shared__ float sgc;
+  auto& sK = S.sK;
+  auto& sQ = S.sQ;
+  auto& sT = S.sT;
+  auto& sP = S.sP;
+  auto& sXt = S.sXt;
+  auto& sInT = S.sInT;
+  auto& sWt = S.sWt;
+  auto& sZt = S.sZt;
+  auto& sgam = S.sgam;
+  auto& sdel = S.sdel;
+  auto& sbeta = S.sbeta;
+  auto& sgb = S.sgb;
+  float& sgc = S.sgc;
 
   // The NB column tiles of one (sequence, V head) read the same chunk operands: keep them on one
   // XCD (workgroups are dealt to the 8 XCDs round robin, so blockIdx % 8 picks the XCD).
@@ -351,7 +375,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   const int n = nh / p.hv, h = nh % p.hv;
   const int G = p.hv / p.hqk, m = h / G;
   const int j0 = 16 * jt;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int idx = lane & 15, grp = lane >> 4;
   const int rw = 16 * wave;
   const int seq0 = p.cu[n], len = p.cu[n + 1] - seq0;
@@ -408,18 +432,23 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
       const int e = tid + 256 * i, row = e / (D / 8), c8 = e % (D / 8);
-      float x[8];
-      rk[i].to(x);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = row < L ? x[u] : 0.f;
-      st4(&sK[row][8 * c8], f32x4{x[0], x[1], x[2], x[3]});
-      st4(&sK[row][8 * c8 + 4], f32x4{x[4], x[5], x[6], x[7]});
-      if constexpr (REV) {
-        rq[i].to(x);
+      if constexpr (std::is_same<InT, bf16>::value) {  // kept in bf16 (exact), raw 16-byte rows
+        *reinterpret_cast<bf16x8*>(&sK[row][8 * c8]) = row < L ? rk[i].r : bf16x8{};
+        if constexpr (REV) *reinterpret_cast<bf16x8*>(&sQ[row][8 * c8]) = row < L ? rq[i].r : bf16x8{};
+      } else {
+        float x[8];
+        rk[i].to(x);
 #pragma unroll
         for (int u = 0; u < 8; ++u) x[u] = row < L ? x[u] : 0.f;
-        st4(&sQ[row][8 * c8], f32x4{x[0], x[1], x[2], x[3]});
-        st4(&sQ[row][8 * c8 + 4], f32x4{x[4], x[5], x[6], x[7]});
+        st4(&sK[row][8 * c8], f32x4{x[0], x[1], x[2], x[3]});
+        st4(&sK[row][8 * c8 + 4], f32x4{x[4], x[5], x[6], x[7]});
+        if constexpr (REV) {
+          rq[i].to(x);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) x[u] = row < L ? x[u] : 0.f;
+          st4(&sQ[row][8 * c8], f32x4{x[0], x[1], x[2], x[3]});
+          st4(&sQ[row][8 * c8 + 4], f32x4{x[4], x[5], x[6], x[7]});
+        }
       }
     }
 #pragma unroll
@@ -549,12 +578,12 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = sgc * x0[r];
       if constexpr (!REV) {  // + K^T diag(delta) V'
-        acc = tile_mma([&](int i, int kk) { return sK[kk][16 * rt + i]; },
+        acc = tile_mma([&](int i, int kk) { return to_f32(sK[kk][16 * rt + i]); },
                        [&](int kk, int j) { return sdel[kk] * sZt[j][kk]; }, kC, acc);
       } else {  // + Q^T diag(gamma) dO^ - K^T diag(gamma) diag(beta) Z
-        acc = tile_mma([&](int i, int kk) { return sQ[kk][16 * rt + i]; },
+        acc = tile_mma([&](int i, int kk) { return to_f32(sQ[kk][16 * rt + i]); },
                        [&](int kk, int j) { return sgam[kk] * sInT[j][kk]; }, kC, acc);
-        acc = tile_mma([&](int i, int kk) { return sK[kk][16 * rt + i]; },
+        acc = tile_mma([&](int i, int kk) { return to_f32(sK[kk][16 * rt + i]); },
                        [&](int kk, int j) { return sgb[kk] * sZt[j][kk]; }, kC, acc);
       }
       st4(&sXt[idx][16 * rt + 4 * grp], acc);
@@ -567,6 +596,25 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
       st_state(p.dh0, st_base + (size_t)r * D + j0 + c, sXt[c][r], p.state_bf16);
     }
   }
+}
+
+template <typename InT, typename OT, int D, bool REV>
+__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) BwdScanLds<InT, D, REV> S;
+  bwd_scan_pass<InT, OT, D, REV>(p, S, threadIdx.x);
+}
+
+// Both passes side by side (they read the same records and neither needs the other's output):
+// waves 0-3 run the forward pass, waves 4-7 the reverse one, so that each hides the other's
+// latencies. Used where both LDS sets fit one CU (bf16 k / q rows).
+template <typename InT, typename OT, int D>
+__global__ __launch_bounds__(512) void bwd_scan2_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) BwdScanLds<InT, D, false> Sf;
+  __shared__ __attribute__((aligned(16))) BwdScanLds<InT, D, true> Sr;
+  if (threadIdx.x < 256)
+    bwd_scan_pass<InT, OT, D, false>(p, Sf, threadIdx.x);
+  else
+    bwd_scan_pass<InT, OT, D, true>(p, Sr, threadIdx.x - 256);
 }
 
 // ---- bwd_grads --------------------------------------------------------------------------------
@@ -927,13 +975,21 @@ hipError_t launch_bwd_t(const gdn_shape_t& s, BwdParams p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_intra_kernel<InT, D>), dim3(slot_blocks_v), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_scan_kernel<InT, OT, D, false>), dim3(scan_blocks), dim3(256), 0,
-                       stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // the reverse scan also runs for empty sequences: dh0 = dht there
-  hipLaunchKernelGGL((bwd_scan_kernel<InT, OT, D, true>), dim3(scan_blocks), dim3(256), 0, stream,
-                     p);
+  // The reverse pass also runs for empty sequences (dh0 = dht there); the forward pass of an
+  // empty sequence writes nothing.
+  if constexpr (std::is_same<InT, bf16>::value) {  // both passes in one workgroup
+    hipLaunchKernelGGL((bwd_scan2_kernel<InT, OT, D>), dim3(scan_blocks), dim3(512), 0, stream, p);
+  } else {
+    if (s.total_tokens > 0) {
+      hipLaunchKernelGGL((bwd_scan_kernel<InT, OT, D, false>), dim3(scan_blocks), dim3(256), 0,
+                         stream, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_scan_kernel<InT, OT, D, true>), dim3(scan_blocks), dim3(256), 0,
+                       stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s.total_tokens == 0) return e;
   hipLaunchKernelGGL((bwd_grads_kernel<InT, OT, D>), dim3(slot_blocks_qk), dim3(512), 0, stream,
