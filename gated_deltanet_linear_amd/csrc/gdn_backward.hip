@@ -395,15 +395,18 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
   const OT* dO = static_cast<const OT*>(p.dout);
   __syncthreads();
 
-  // A chunk's global operands are loaded into registers (16-byte pieces) one chunk ahead: the
-  // next chunk's loads are in flight while this one is computed. Rows past the chunk end load
-  // row 0 of the chunk and are zeroed when staged.
+  // A chunk's global operands (its gates and beta included) are loaded into registers one chunk
+  // ahead (16-byte pieces): the next chunk's loads are in flight while this one is computed, and
+  // no wait inside a chunk covers them. Rows past the chunk end load row 0 of the chunk and are
+  // zeroed when staged.
   constexpr int KV = kC * D / 8 / 256;  // 8-value pieces of the k (q) rows per thread
   static_assert(kC * D % (8 * 256) == 0, "k row pieces");
   using InT2 = std::conditional_t<REV, OT, InT>;  // dO^ (reverse) or v (forward) columns
   Raw8<InT> rk[KV], rq[REV ? KV : 1];
   f32x4 rt[4], rp[REV ? 4 : 1];
   Raw8<InT2> rin;
+  double rbb = 0.0, rbl = 0.0;  // b at this lane's row and at the chunk's last row
+  float rbt = 0.f;              // beta at this lane's row
   auto load_chunk = [&](int c) {
     const int t0 = seq0 + kC * c, L = min(kC, len - kC * c);
     const float* rec = p.rec + ((size_t)(sb0 + c) * p.hv + h) * kRecFloats;
@@ -426,6 +429,12 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
         rin.load(dO + off);
       else
         rin.load(V + off);
+    }
+    if (tid < kC) {
+      const double* bb = rec_b(rec);
+      rbb = bb[tid];
+      rbl = bb[kC - 1];
+      rbt = p.beta[(size_t)(t0 + (tid < L ? tid : 0)) * p.hv + h];
     }
   };
   auto stage_chunk = [&](int L) {
@@ -472,13 +481,20 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
 #pragma unroll
       for (int u = 0; u < 8; ++u) sInT[8 * half + u][row] = row < L ? sc * x[u] : 0.f;
     }
+    if (tid < kC) {
+      const float gm = expf((float)rbb), bt = tid < L ? rbt : 0.f;
+      sgam[tid] = gm;
+      sdel[tid] = expf((float)(rbl - rbb));
+      sbeta[tid] = bt;
+      sgb[tid] = -gm * bt;
+      if (tid == 0) sgc = expf((float)rbl);
+    }
   };
   if (nch > 0) load_chunk(REV ? nch - 1 : 0);
 
   for (int ci = 0; ci < nch; ++ci) {
     const int c = REV ? nch - 1 - ci : ci;
     const int slot = sb0 + c, t0 = seq0 + kC * c, L = min(kC, len - kC * c);
-    const float* rec = p.rec + ((size_t)slot * p.hv + h) * kRecFloats;
     float* xs = (REV ? p.dhs : p.hs) + ((size_t)slot * p.hv + h) * D * D;
     for (int e = tid; e < D * 16; e += 256) {  // the tile at the chunk boundary
       const int r = e / 16, cc = e % 16;
@@ -486,16 +502,6 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     }
     stage_chunk(L);
     if (ci + 1 < nch) load_chunk(REV ? c - 1 : c + 1);
-    if (tid < kC) {
-      const double* bb = rec_b(rec);
-      const float gm = expf((float)bb[tid]);
-      const float bt = tid < L ? p.beta[(size_t)(t0 + tid) * p.hv + h] : 0.f;
-      sgam[tid] = gm;
-      sdel[tid] = expf((float)(bb[kC - 1] - bb[tid]));
-      sbeta[tid] = bt;
-      sgb[tid] = -gm * bt;
-      if (tid == 0) sgc = expf((float)bb[kC - 1]);
-    }
     __syncthreads();
 
     // rows rw .. rw + 15 of U = K X
