@@ -577,20 +577,29 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
       st4(&sZt[idx][rw + 4 * grp], z);
     }
     __syncthreads();
-    // carried tile update, its 16-row tiles dealt to the waves (K^T, Q^T read element-wise)
+    // carried tile update, its 16-row tiles dealt to the waves (K^T, Q^T read element-wise; the
+    // right operands are rows of the transposed 16-column tiles, read as fragments)
     for (int rt = wave; rt < NB; rt += 4) {
       const f32x4 x0 = ld4(&sXt[idx][16 * rt + 4 * grp]);
       f32x4 acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = sgc * x0[r];
-      if constexpr (!REV) {  // + K^T diag(delta) V'
-        acc = tile_mma([&](int i, int kk) { return to_f32(sK[kk][16 * rt + i]); },
-                       [&](int kk, int j) { return sdel[kk] * sZt[j][kk]; }, kC, acc);
-      } else {  // + Q^T diag(gamma) dO^ - K^T diag(gamma) diag(beta) Z
-        acc = tile_mma([&](int i, int kk) { return to_f32(sQ[kk][16 * rt + i]); },
-                       [&](int kk, int j) { return sgam[kk] * sInT[j][kk]; }, kC, acc);
-        acc = tile_mma([&](int i, int kk) { return to_f32(sK[kk][16 * rt + i]); },
-                       [&](int kk, int j) { return sgb[kk] * sZt[j][kk]; }, kC, acc);
+#pragma unroll
+      for (int k0 = 0; k0 < kC; k0 += 32) {
+        f32x8 av, bv;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) av[s] = to_f32(sK[k0 + kslot(grp, s)][16 * rt + idx]);
+        if constexpr (!REV) {  // + K^T diag(delta) V'
+          row_frag_sv(&sZt[idx][0], sdel, k0, grp, bv);
+          acc = mma32(av, bv, acc);
+        } else {  // + Q^T diag(gamma) dO^ - K^T diag(gamma) diag(beta) Z
+          row_frag_sv(&sZt[idx][0], sgb, k0, grp, bv);
+          acc = mma32(av, bv, acc);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) av[s] = to_f32(sQ[k0 + kslot(grp, s)][16 * rt + idx]);
+          row_frag_sv(&sInT[idx][0], sgam, k0, grp, bv);
+          acc = mma32(av, bv, acc);
+        }
       }
       st4(&sXt[idx][16 * rt + 4 * grp], acc);
     }
