@@ -496,9 +496,11 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     const int c = REV ? nch - 1 - ci : ci;
     const int slot = sb0 + c, t0 = seq0 + kC * c, L = min(kC, len - kC * c);
     float* xs = (REV ? p.dhs : p.hs) + ((size_t)slot * p.hv + h) * D * D;
-    for (int e = tid; e < D * 16; e += 256) {  // the tile at the chunk boundary
-      const int r = e / 16, cc = e % 16;
-      xs[(size_t)r * D + j0 + cc] = sXt[cc][r];
+#pragma unroll
+    for (int e = tid; e < D * 4; e += 256) {  // the tile at the chunk boundary, 16-byte stores
+      const int r = e / 4, c4 = 4 * (e % 4);
+      *reinterpret_cast<f32x4*>(xs + (size_t)r * D + j0 + c4) =
+          f32x4{sXt[c4][r], sXt[c4 + 1][r], sXt[c4 + 2][r], sXt[c4 + 3][r]};
     }
     stage_chunk(L);
     if (ci + 1 < nch) load_chunk(REV ? c - 1 : c + 1);
