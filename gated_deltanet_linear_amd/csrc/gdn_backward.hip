@@ -327,6 +327,49 @@ __device__ __forceinline__ void row_frag_sv(const float* row, const float* sv, i
   }
 }
 
+// Operand fragments of the scan products in precision mode M (bf16 k / q rows: Bf16Mode, the
+// computed fp32 operands carried as hi + lo bf16 pairs; fp32 inputs: F32Mode).
+template <typename M>
+__device__ __forceinline__ typename M::Op op_frag(const float* row, int k0, int grp) {
+  const f32x4 lo = ld4(row + k0 + 4 * grp), hi = ld4(row + k0 + 16 + 4 * grp);
+  const float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return M::make(x);
+}
+template <typename M>
+__device__ __forceinline__ typename M::Op op_frag_sv(const float* row, const float* sv, int k0,
+                                                     int grp) {
+  f32x8 v;
+  row_frag_sv(row, sv, k0, grp, v);
+  const float x[8] = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+  return M::make(x);
+}
+// exact fragment of a k / q row (contiguous along the depth)
+__device__ __forceinline__ bf16x8 in_frag(const bf16* row, int k0, int grp) {
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + k0 + 4 * grp);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + k0 + 16 + 4 * grp);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ f32x8 in_frag(const float* row, int k0, int grp) {
+  f32x8 o;
+  row_frag(row, k0, grp, 1.f, o);
+  return o;
+}
+// exact fragment of a k / q column: element (kk, col) of rows kk = k0 + kslot(grp, s)
+template <int KP>
+__device__ __forceinline__ bf16x8 in_col_frag(const bf16 (*rows)[KP], int k0, int grp, int col) {
+  bf16x8 o;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) o[s] = rows[k0 + kslot(grp, s)][col];
+  return o;
+}
+template <int KP>
+__device__ __forceinline__ f32x8 in_col_frag(const float (*rows)[KP], int k0, int grp, int col) {
+  f32x8 o;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) o[s] = rows[k0 + kslot(grp, s)][col];
+  return o;
+}
+
 // LDS of one scan pass. k / q rows are kept in the input dtype (bf16 exactly), rows padded to
 // 16 bytes; the fp32 operands rows padded by 4 floats.
 template <typename KT, int D, bool REV>
@@ -353,6 +396,7 @@ template <typename InT, typename OT, int D, bool REV>
 __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
                                               BwdScanLds<InT, D, REV>& S, int tid) {
   constexpr int NB = D / 16;   // column tiles per head
+  using M = std::conditional_t<std::is_same<InT, bf16>::value, Bf16Mode, F32Mode>;
   auto& sK = S.sK;
   auto& sQ = S.sQ;
   auto& sT = S.sT;
@@ -509,12 +553,8 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     // rows rw .. rw + 15 of U = K X
     f32x4 u = zero4();
 #pragma unroll
-    for (int k0 = 0; k0 < D; k0 += 32) {
-      f32x8 av, bv;
-      row_frag(&sK[rw + idx][0], k0, grp, 1.f, av);
-      row_frag(&sXt[idx][0], k0, grp, 1.f, bv);
-      u = mma32(av, bv, u);
-    }
+    for (int k0 = 0; k0 < D; k0 += 32)
+      u = M::mma_xs(u, in_frag(&sK[rw + idx][0], k0, grp), op_frag<M>(&sXt[idx][0], k0, grp));
     if constexpr (!REV) {  // Y = V - diag(gamma) U
       const f32x4 vv = ld4(&sInT[idx][rw + 4 * grp]), gm = ld4(&sgam[rw + 4 * grp]);
       f32x4 y;
@@ -528,12 +568,9 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     } else {  // dV' = P^T dO^ + diag(delta) U
       f32x4 pd = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < kC; k0 += 32) {
-        f32x8 av, bv;
-        row_frag(&sP[rw + idx][0], k0, grp, 1.f, av);
-        row_frag(&sInT[idx][0], k0, grp, 1.f, bv);
-        pd = mma32(av, bv, pd);
-      }
+      for (int k0 = 0; k0 < kC; k0 += 32)
+        pd = M::mma_ss(pd, op_frag<M>(&sP[rw + idx][0], k0, grp),
+                       op_frag<M>(&sInT[idx][0], k0, grp));
       const f32x4 dl = ld4(&sdel[rw + 4 * grp]);
       f32x4 w;
 #pragma unroll
@@ -544,12 +581,9 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     if constexpr (!REV) {  // V' = T diag(beta) Y
       f32x4 vpr = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < kC; k0 += 32) {
-        f32x8 av, bv;
-        row_frag(&sT[rw + idx][0], k0, grp, 1.f, av);
-        row_frag_sv(&sWt[idx][0], sbeta, k0, grp, bv);
-        vpr = mma32(av, bv, vpr);
-      }
+      for (int k0 = 0; k0 < kC; k0 += 32)
+        vpr = M::mma_ss(vpr, op_frag<M>(&sT[rw + idx][0], k0, grp),
+                        op_frag_sv<M>(&sWt[idx][0], sbeta, k0, grp));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r;
@@ -559,12 +593,8 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     } else {  // Z = T^T dV';  dv = dY = diag(beta) Z
       f32x4 z = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < kC; k0 += 32) {
-        f32x8 av, bv;
-        row_frag(&sT[rw + idx][0], k0, grp, 1.f, av);
-        row_frag(&sWt[idx][0], k0, grp, 1.f, bv);
-        z = mma32(av, bv, z);
-      }
+      for (int k0 = 0; k0 < kC; k0 += 32)
+        z = M::mma_ss(z, op_frag<M>(&sT[rw + idx][0], k0, grp), op_frag<M>(&sWt[idx][0], k0, grp));
       InT* dV = static_cast<InT*>(p.dv);
       const f32x4 bt = ld4(&sbeta[rw + 4 * grp]);
 #pragma unroll
@@ -588,19 +618,14 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
       for (int r = 0; r < 4; ++r) acc[r] = sgc * x0[r];
 #pragma unroll
       for (int k0 = 0; k0 < kC; k0 += 32) {
-        f32x8 av, bv;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) av[s] = to_f32(sK[k0 + kslot(grp, s)][16 * rt + idx]);
         if constexpr (!REV) {  // + K^T diag(delta) V'
-          row_frag_sv(&sZt[idx][0], sdel, k0, grp, bv);
-          acc = mma32(av, bv, acc);
+          acc = M::mma_xs(acc, in_col_frag(sK, k0, grp, 16 * rt + idx),
+                          op_frag_sv<M>(&sZt[idx][0], sdel, k0, grp));
         } else {  // + Q^T diag(gamma) dO^ - K^T diag(gamma) diag(beta) Z
-          row_frag_sv(&sZt[idx][0], sgb, k0, grp, bv);
-          acc = mma32(av, bv, acc);
-#pragma unroll
-          for (int s = 0; s < 8; ++s) av[s] = to_f32(sQ[k0 + kslot(grp, s)][16 * rt + idx]);
-          row_frag_sv(&sInT[idx][0], sgam, k0, grp, bv);
-          acc = mma32(av, bv, acc);
+          acc = M::mma_xs(acc, in_col_frag(sK, k0, grp, 16 * rt + idx),
+                          op_frag_sv<M>(&sZt[idx][0], sgb, k0, grp));
+          acc = M::mma_xs(acc, in_col_frag(sQ, k0, grp, 16 * rt + idx),
+                          op_frag_sv<M>(&sInT[idx][0], sgam, k0, grp));
         }
       }
       st4(&sXt[idx][16 * rt + 4 * grp], acc);
