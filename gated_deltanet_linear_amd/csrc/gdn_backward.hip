@@ -116,25 +116,6 @@ __device__ __forceinline__ f32x4 tile_mma(FA a, FB b, int K, f32x4 acc) {
   return acc;
 }
 
-// tile_mma with the depth loop kept rolled (fewer operands in flight; for register-bound
-// callers).
-template <typename FA, typename FB>
-__device__ __forceinline__ f32x4 tile_mma_rolled(FA a, FB b, int K, f32x4 acc) {
-  const int lane = threadIdx.x & 63, idx = lane & 15, grp = lane >> 4;
-#pragma unroll 1
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    f32x8 av, bv;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int kk = k0 + kslot(grp, s);
-      av[s] = a(idx, kk);
-      bv[s] = b(kk, idx);
-    }
-    acc = mma32(av, bv, acc);
-  }
-  return acc;
-}
-
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // 8 fragment values of a row contiguous along the depth: slots 0-3 are depth k0 + 4 grp .. + 3,
@@ -174,22 +155,6 @@ __device__ __forceinline__ f32x4 tile_mma_rows(const TA* a_row, float a_scale, c
 #pragma unroll
       for (int s = 0; s < 8; ++s) av[s] = 0.f;
     }
-    row_frag(b_row, k0, grp, 1.f, bv);
-    acc = mma32(av, bv, acc);
-  }
-  return acc;
-}
-
-// tile_mma_rows with a valid A row always (rows past the chunk end pass row 0 with scale 0):
-// no branch, so that the loads of all depth steps can be in flight together.
-template <typename TA, typename TB>
-__device__ __forceinline__ f32x4 tile_mma_rows_s(const TA* a_row, float a_scale, const TB* b_row,
-                                                 int K, f32x4 acc) {
-  const int grp = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    f32x8 av, bv;
-    row_frag(a_row, k0, grp, a_scale, av);
     row_frag(b_row, k0, grp, 1.f, bv);
     acc = mma32(av, bv, acc);
   }
@@ -659,6 +624,49 @@ __global__ __launch_bounds__(512) void bwd_scan2_kernel(BwdParams p) {
     bwd_scan_pass<InT, OT, D, true>(p, Sr, threadIdx.x - 256);
 }
 
+// Fragment of an operand whose values are representable in the fragment type of mode M.
+template <typename M>
+__device__ __forceinline__ typename M::frag_t exact_frag(const float (&x)[8]) {
+  typename M::frag_t o;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) o[s] = x[s];
+  return o;
+}
+// acc += A B over depth K on fp32 MFMA, A and B from element accessors, the depth loop kept
+// rolled (fewer operands in flight, for the register-bound gradient kernel).
+template <typename FA, typename FB>
+__device__ __forceinline__ f32x4 tile_mma_f32(FA a, FB b, int K, f32x4 acc) {
+  const int lane = threadIdx.x & 63, idx = lane & 15, grp = lane >> 4;
+#pragma unroll 1
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    float xa[8], xb[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int kk = k0 + kslot(grp, s);
+      xa[s] = a(idx, kk);
+      xb[s] = b(kk, idx);
+    }
+    acc = F32Mode::mma_ss(acc, F32Mode::make(xa), F32Mode::make(xb));
+  }
+  return acc;
+}
+// acc += A B^T over depth K on fp32 MFMA, this lane's A row and B row contiguous along the depth
+template <typename TA>
+__device__ __forceinline__ f32x4 tile_mma_rows_f32(const TA* a_row, float a_scale,
+                                                   const float* b_row, int K, f32x4 acc) {
+  const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f32x8 av, bv;
+    row_frag(a_row, k0, grp, a_scale, av);
+    row_frag(b_row, k0, grp, 1.f, bv);
+    const float xa[8] = {av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+    const float xb[8] = {bv[0], bv[1], bv[2], bv[3], bv[4], bv[5], bv[6], bv[7]};
+    acc = F32Mode::mma_ss(acc, F32Mode::make(xa), F32Mode::make(xb));
+  }
+  return acc;
+}
+
 // ---- bwd_grads --------------------------------------------------------------------------------
 // 512 threads, two waves per SIMD. For the products with the states (R1..R3) and the dq / dk
 // tiles, wave w owns one d_k column tile (w % NB) and NB / 2 of the 4 row tiles: a state-row
@@ -699,6 +707,11 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   const int ch = wave >> 2;        // this wave's column half of the C x C products
   const int ctw = wave % NB;       // this wave's d_k column tile in the R / dq / dk products
   const int rt0 = (wave / NB) * RPW;  // and its first row tile there
+  // bf16 inputs: the products with the states (R1..R3) on bf16 MFMA, a bf16 dO exact and the
+  // other operands split hi + lo. The C x C products and dq / dk stay on fp32 MFMA: dg sums
+  // their entries with cancellation, and split operands there double its error.
+  using MR = std::conditional_t<std::is_same<InT, bf16>::value, Bf16Mode, F32Mode>;
+  constexpr bool kDoXR = MR::kSplit && std::is_same<OT, bf16>::value;  // dO values exact
 
   const InT* Q = static_cast<const InT*>(p.q);
   const InT* K = static_cast<const InT*>(p.k);
@@ -777,6 +790,22 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         row_frag(hrow, 32 * ks, grp, 1.f, hb[ks]);
         row_frag(dhrow, 32 * ks, grp, 1.f, dhb[ks]);
       }
+      if (rt0 == 0) {  // <H, dH'>: each state element once over the waves of row-tile group 0
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hdh = fmaf(hb[ks][e], dhb[ks][e], hdh);
+      }
+      typename MR::Op ho[KS], dho[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float xh[8] = {hb[ks][0], hb[ks][1], hb[ks][2], hb[ks][3],
+                             hb[ks][4], hb[ks][5], hb[ks][6], hb[ks][7]};
+        const float xd[8] = {dhb[ks][0], dhb[ks][1], dhb[ks][2], dhb[ks][3],
+                             dhb[ks][4], dhb[ks][5], dhb[ks][6], dhb[ks][7]};
+        ho[ks] = MR::make(xh);
+        dho[ks] = MR::make(xd);
+      }
 #pragma unroll
       for (int g0 = 0; g0 < kC; g0 += SR) {
         f32x4 pc[PPS];
@@ -801,7 +830,7 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         for (int i = 0; i < PPS; ++i) {
           const int pi = tid + 512 * i, op = pi / (SR * PR), rl = (pi / PR) % SR, row = g0 + rl;
           if (pi < NPS) {
-            const float sc = row >= L ? 0.f : op == 0 ? p.scale : op == 1 ? sbeta[row] : 1.f;
+            const float sc = row >= L ? 0.f : op == 1 ? sbeta[row] : 1.f;  // dO^ = scale dO: later
             *reinterpret_cast<f32x4*>(sU + (op * SR + rl) * SLD + 4 * (pi % PR)) = pc[i] * sc;
           }
         }
@@ -815,14 +844,27 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
           f32x4 r1 = zero4(), r2 = zero4(), r3 = zero4();
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            f32x8 ao, az, av;
-            row_frag(sU + rl * SLD, 32 * ks, grp, 1.f, ao);
-            row_frag(sU + (SR + rl) * SLD, 32 * ks, grp, 1.f, az);
-            row_frag(sU + (2 * SR + rl) * SLD, 32 * ks, grp, 1.f, av);
-            r1 = mma32(ao, hb[ks], r1);
-            r2 = mma32(az, hb[ks], r2);
-            r3 = mma32(av, dhb[ks], r3);
+            float ao[8], az[8], av[8];
+            {
+              f32x8 f;
+              row_frag(sU + rl * SLD, 32 * ks, grp, 1.f, f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) ao[e] = f[e];
+              row_frag(sU + (SR + rl) * SLD, 32 * ks, grp, 1.f, f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) az[e] = f[e];
+              row_frag(sU + (2 * SR + rl) * SLD, 32 * ks, grp, 1.f, f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) av[e] = f[e];
+            }
+            if constexpr (kDoXR)
+              r1 = MR::mma_xs(r1, exact_frag<MR>(ao), ho[ks]);
+            else
+              r1 = MR::mma_ss(r1, MR::make(ao), ho[ks]);
+            r2 = MR::mma_ss(r2, MR::make(az), ho[ks]);
+            r3 = MR::mma_ss(r3, MR::make(av), dho[ks]);
           }
+          r1 *= p.scale;
           float rs[4], rd[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -850,12 +892,6 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         }
         __syncthreads();  // group consumed
       }
-      if (rt0 == 0) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) hdh = fmaf(hb[ks][e], dhb[ks][e], hdh);
-      }
     }
     // dP = dO^ V'^T (lower-incl), dA = -Z V'^T (strictly lower): this wave's two column tiles
     float rbeta[4] = {0.f, 0.f, 0.f, 0.f};
@@ -873,8 +909,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
       const int c0 = 16 * (2 * ch + u);
       // V' rows past the chunk end are read as row 0 of the chunk and masked below
       const float* vprow = p.vp + row_off(c0 + idx < L ? c0 + idx : 0);
-      const f32x4 dp = tile_mma_rows_s(my_dO, my_ok ? p.scale : 0.f, vprow, D, zero4());
-      const f32x4 za = tile_mma_rows_s(my_Z, my_ok ? 1.f : 0.f, vprow, D, zero4());
+      const f32x4 dp =
+          p.scale * tile_mma_rows_f32(my_dO, my_ok ? 1.f : 0.f, vprow, D, zero4());
+      const f32x4 za = tile_mma_rows_f32(my_Z, my_ok ? 1.f : 0.f, vprow, D, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r, j = c0 + idx;
@@ -963,12 +1000,12 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
       const int c0 = 16 * ctw, r0 = 16 * (rt0 + u);
-      dq[u] = tile_mma_rolled([&](int i, int kk) { return sPG[r0 + i][kk]; },
-                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
-      dk[u] = tile_mma_rolled([&](int i, int kk) { return sPG[kk][r0 + i]; },
-                              [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
-      dk[u] = tile_mma_rolled([&](int i, int kk) { return sDS[r0 + i][kk] + sDS[kk][r0 + i]; },
-                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
+      dq[u] = tile_mma_f32([&](int i, int kk) { return sPG[r0 + i][kk]; },
+                           [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
+      dk[u] = tile_mma_f32([&](int i, int kk) { return sPG[kk][r0 + i]; },
+                           [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
+      dk[u] = tile_mma_f32([&](int i, int kk) { return sDS[r0 + i][kk] + sDS[kk][r0 + i]; },
+                           [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
     }
     __syncthreads();  // LDS reused by the next V head
   }
