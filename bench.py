@@ -423,7 +423,7 @@ def run_backward(torch, gdn, si, steps, warmup):
     tf = F / (kms["gdn_chunk_backward"] / 1e3) / 1e12
     return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=T / (ms / 1e3),
                 kernels_ms=kms, workspace_bytes=nbytes,
-                roofline=dict(kernel="gdn_chunk_backward (4 launches)", bound="mfma",
+                roofline=dict(kernel="gdn_chunk_backward (3 launches)", bound="mfma",
                               achieved=round(tf, 3), peak=PEAK_F32_TFLOPS, unit="TFLOP/s",
                               frac=round(tf / PEAK_F32_TFLOPS, 5), traffic=None,
                               algorithmic_flops_per_launch=F))
