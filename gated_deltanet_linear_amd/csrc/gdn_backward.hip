@@ -575,23 +575,25 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     }
     __syncthreads();
     // carried tile update, its 16-row tiles dealt to the waves (K^T, Q^T read element-wise; the
-    // right operands are rows of the transposed 16-column tiles, read as fragments)
+    // right operands, rows of the transposed 16-column tiles, read as fragments once for all of
+    // a wave's tiles)
+    typename M::Op bz[kC / 32], bi[REV ? kC / 32 : 1];
+#pragma unroll
+    for (int ks = 0; ks < kC / 32; ++ks) {
+      bz[ks] = op_frag_sv<M>(&sZt[idx][0], REV ? sgb : sdel, 32 * ks, grp);
+      if constexpr (REV) bi[ks] = op_frag_sv<M>(&sInT[idx][0], sgam, 32 * ks, grp);
+    }
     for (int rt = wave; rt < NB; rt += 4) {
       const f32x4 x0 = ld4(&sXt[idx][16 * rt + 4 * grp]);
       f32x4 acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = sgc * x0[r];
 #pragma unroll
-      for (int k0 = 0; k0 < kC; k0 += 32) {
-        if constexpr (!REV) {  // + K^T diag(delta) V'
-          acc = M::mma_xs(acc, in_col_frag(sK, k0, grp, 16 * rt + idx),
-                          op_frag_sv<M>(&sZt[idx][0], sdel, k0, grp));
-        } else {  // + Q^T diag(gamma) dO^ - K^T diag(gamma) diag(beta) Z
-          acc = M::mma_xs(acc, in_col_frag(sK, k0, grp, 16 * rt + idx),
-                          op_frag_sv<M>(&sZt[idx][0], sgb, k0, grp));
-          acc = M::mma_xs(acc, in_col_frag(sQ, k0, grp, 16 * rt + idx),
-                          op_frag_sv<M>(&sInT[idx][0], sgam, k0, grp));
-        }
+      for (int ks = 0; ks < kC / 32; ++ks) {
+        // + K^T diag(delta) V' (forward);  - K^T diag(gamma) diag(beta) Z + Q^T diag(gamma) dO^
+        acc = M::mma_xs(acc, in_col_frag(sK, 32 * ks, grp, 16 * rt + idx), bz[ks]);
+        if constexpr (REV)
+          acc = M::mma_xs(acc, in_col_frag(sQ, 32 * ks, grp, 16 * rt + idx), bi[ks]);
       }
       st4(&sXt[idx][16 * rt + 4 * grp], acc);
     }
