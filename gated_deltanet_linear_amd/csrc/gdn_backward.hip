@@ -339,12 +339,16 @@ __device__ __forceinline__ f32x8 in_col_frag(const float (*rows)[KP], int k0, in
 // 16 bytes; the fp32 operands rows padded by 4 floats.
 template <typename KT, int D, bool REV>
 struct BwdScanLds {
+  static constexpr bool kSplit = std::is_same<KT, bf16>::value;  // split-bf16 products
+  using XT = std::conditional_t<kSplit, bf16, float>;
   static constexpr int KP = D + 16 / (int)sizeof(KT);  // k / q rows
-  static constexpr int XP = D + 4;                     // the transposed carried tile
+  static constexpr int XP = D + 16 / (int)sizeof(XT);  // the transposed carried tile
   static constexpr int CP = kC + 4;                    // rows along the tokens
   float sT[kC][CP];            // T (forward), T^T (reverse)
   float sP[REV ? kC : 1][CP];  // P^T (reverse)
-  float sXt[16][XP];           // carried tile (state / gradient)^T
+  // carried tile (state / gradient)^T as the products read it: hi + lo bf16 pair (split) or fp32
+  XT sXh[16][XP];
+  XT sXl[kSplit ? 16 : 1][XP];
   float sInT[16][CP];          // (V or dO^ columns)^T
   float sWt[16][CP];           // (Y or dV')^T
   float sZt[16][CP];           // (V' or Z)^T
@@ -353,6 +357,35 @@ struct BwdScanLds {
   KT sQ[REV ? kC : 1][KP];
   float sgc;
 };
+
+// Carried-tile copy in LDS: 4 consecutive depth values of column `row` from a C fragment, and
+// the B fragment of a product over the depth.
+template <typename M, typename L>
+__device__ __forceinline__ void store_x(L& S, int row, int col, const f32x4& v) {
+  if constexpr (M::kSplit) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h[s] = (bf16)v[s];
+      l[s] = (bf16)(v[s] - (float)h[s]);
+    }
+    *reinterpret_cast<bf16x4*>(&S.sXh[row][col]) = h;
+    *reinterpret_cast<bf16x4*>(&S.sXl[row][col]) = l;
+  } else {
+    st4(&S.sXh[row][col], v);
+  }
+}
+template <typename M, typename L>
+__device__ __forceinline__ typename M::Op x_frag(const L& S, int row, int k0, int grp) {
+  typename M::Op o;
+  if constexpr (M::kSplit) {
+    o.hi = in_frag(&S.sXh[row][0], k0, grp);
+    o.lo = in_frag(&S.sXl[row][0], k0, grp);
+  } else {
+    row_frag(&S.sXh[row][0], k0, grp, 1.f, o.v);
+  }
+  return o;
+}
 
 // One pass (forward states or reverse state gradients) on 4 waves; `tid` is the thread's index
 // among them. Every barrier of a pass is a workgroup barrier: a workgroup that runs both passes
@@ -366,7 +399,6 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
   auto& sQ = S.sQ;
   auto& sT = S.sT;
   auto& sP = S.sP;
-  auto& sXt = S.sXt;
   auto& sInT = S.sInT;
   auto& sWt = S.sWt;
   auto& sZt = S.sZt;
@@ -392,11 +424,23 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
   const int sb0 = slot_base(p.cu, n);
   const size_t st_base = (size_t)nh * D * D;
 
-  // carried tile: the initial state (forward) or the final-state gradient (reverse)
+  // carried tile: the initial state (forward) or the final-state gradient (reverse). Wave w
+  // holds row tiles w, w + 4, .. of it in registers (lane: rows 4 grp + r, column idx) and keeps
+  // the LDS copy the products read.
+  constexpr int TPW = (NB + 3) / 4;
+  f32x4 xr[TPW];
   const void* init = REV ? p.dht : p.h0;
-  for (int e = tid; e < D * 16; e += 256) {
-    const int r = e / 16, c = e % 16;
-    sXt[c][r] = init ? ld_state(init, st_base + (size_t)r * D + j0 + c, p.state_bf16) : 0.f;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int rt = wave + 4 * u;
+    if (rt < NB) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t e = st_base + (size_t)(16 * rt + 4 * grp + r) * D + j0 + idx;
+        xr[u][r] = init ? ld_state(init, e, p.state_bf16) : 0.f;
+      }
+      store_x<M>(S, idx, 16 * rt + 4 * grp, xr[u]);
+    }
   }
   const InT* Q = static_cast<const InT*>(p.q);
   const InT* K = static_cast<const InT*>(p.k);
@@ -506,10 +550,12 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     const int slot = sb0 + c, t0 = seq0 + kC * c, L = min(kC, len - kC * c);
     float* xs = (REV ? p.dhs : p.hs) + ((size_t)slot * p.hv + h) * D * D;
 #pragma unroll
-    for (int e = tid; e < D * 4; e += 256) {  // the tile at the chunk boundary, 16-byte stores
-      const int r = e / 4, c4 = 4 * (e % 4);
-      *reinterpret_cast<f32x4*>(xs + (size_t)r * D + j0 + c4) =
-          f32x4{sXt[c4][r], sXt[c4 + 1][r], sXt[c4 + 2][r], sXt[c4 + 3][r]};
+    for (int u = 0; u < TPW; ++u) {  // the tile at the chunk boundary
+      const int rt = wave + 4 * u;
+      if (rt < NB) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xs[(size_t)(16 * rt + 4 * grp + r) * D + j0 + idx] = xr[u][r];
+      }
     }
     stage_chunk(L);
     if (ci + 1 < nch) load_chunk(REV ? c - 1 : c + 1);
@@ -519,7 +565,7 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
     f32x4 u = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 32)
-      u = M::mma_xs(u, in_frag(&sK[rw + idx][0], k0, grp), op_frag<M>(&sXt[idx][0], k0, grp));
+      u = M::mma_xs(u, in_frag(&sK[rw + idx][0], k0, grp), x_frag<M>(S, idx, k0, grp));
     if constexpr (!REV) {  // Y = V - diag(gamma) U
       const f32x4 vv = ld4(&sInT[idx][rw + 4 * grp]), gm = ld4(&sgam[rw + 4 * grp]);
       f32x4 y;
@@ -583,11 +629,13 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
       bz[ks] = op_frag_sv<M>(&sZt[idx][0], REV ? sgb : sdel, 32 * ks, grp);
       if constexpr (REV) bi[ks] = op_frag_sv<M>(&sInT[idx][0], sgam, 32 * ks, grp);
     }
-    for (int rt = wave; rt < NB; rt += 4) {
-      const f32x4 x0 = ld4(&sXt[idx][16 * rt + 4 * grp]);
+#pragma unroll
+    for (int uu = 0; uu < TPW; ++uu) {
+      const int rt = wave + 4 * uu;
+      if (rt >= NB) break;
       f32x4 acc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = sgc * x0[r];
+      for (int r = 0; r < 4; ++r) acc[r] = sgc * xr[uu][r];
 #pragma unroll
       for (int ks = 0; ks < kC / 32; ++ks) {
         // + K^T diag(delta) V' (forward);  - K^T diag(gamma) diag(beta) Z + Q^T diag(gamma) dO^
@@ -595,14 +643,21 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
         if constexpr (REV)
           acc = M::mma_xs(acc, in_col_frag(sQ, 32 * ks, grp, 16 * rt + idx), bi[ks]);
       }
-      st4(&sXt[idx][16 * rt + 4 * grp], acc);
+      xr[uu] = acc;
+      store_x<M>(S, idx, 16 * rt + 4 * grp, acc);
     }
     __syncthreads();
   }
   if (REV && p.dh0) {
-    for (int e = tid; e < D * 16; e += 256) {
-      const int r = e / 16, c = e % 16;
-      st_state(p.dh0, st_base + (size_t)r * D + j0 + c, sXt[c][r], p.state_bf16);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int rt = wave + 4 * u;
+      if (rt < NB) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          st_state(p.dh0, st_base + (size_t)(16 * rt + 4 * grp + r) * D + j0 + idx, xr[u][r],
+                   p.state_bf16);
+      }
     }
   }
 }
