@@ -39,7 +39,8 @@ def _check(case, dout, dht, h0, scale, what):
         check(gv, rv, TOL["f32"], f"{what} {name}")
 
 
-@pytest.mark.parametrize("d,dtype", [(32, "f32"), (64, "bf16"), (128, "bf16"), (128, "f32")])
+@pytest.mark.parametrize("d,dtype", [(32, "f32"), (32, "bf16"), (64, "bf16"), (64, "f32"),
+                                     (128, "bf16"), (128, "f32")])
 @pytest.mark.parametrize("lengths", [[1], [63], [64, 65], [130, 7]])
 def test_backward_small(d, dtype, lengths):
     rng = np.random.default_rng(d * 1000 + sum(lengths))
