@@ -319,19 +319,31 @@ __device__ __forceinline__ f32x8 in_frag(const float* row, int k0, int grp) {
   row_frag(row, k0, grp, 1.f, o);
   return o;
 }
-// exact fragment of a k / q column: element (kk, col) of rows kk = k0 + kslot(grp, s)
+// exact fragment of a k / q column: lane (idx, grp) gets element (kk, col0 + idx) of rows
+// kk = k0 + kslot(grp, s). bf16: two ds_read_b64_tr_b16 over the 16 x 16 blocks of rows k0 and
+// k0 + 16 (lane (g, a + 4e) addresses row 4 g + e, columns col0 + 4 a .. + 3 of the block; lane
+// (g, i) receives element i of row 4 g + e, for e = 0..3).
 template <int KP>
-__device__ __forceinline__ bf16x8 in_col_frag(const bf16 (*rows)[KP], int k0, int grp, int col) {
+__device__ __forceinline__ bf16x8 in_col_frag(const bf16 (*rows)[KP], int k0, int grp, int col0) {
+  const int s = threadIdx.x & 15, a = s & 3, e = s >> 2;
   bf16x8 o;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) o[s] = rows[k0 + kslot(grp, s)][col];
+  for (int hf = 0; hf < 2; ++hf) {
+    const bf16* pa = &rows[k0 + 16 * hf + 4 * grp + e][col0 + 4 * a];
+    const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(pa));
+    const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[4 * hf + j] = tb[j];
+  }
   return o;
 }
 template <int KP>
-__device__ __forceinline__ f32x8 in_col_frag(const float (*rows)[KP], int k0, int grp, int col) {
+__device__ __forceinline__ f32x8 in_col_frag(const float (*rows)[KP], int k0, int grp, int col0) {
+  const int idx = threadIdx.x & 15;
   f32x8 o;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) o[s] = rows[k0 + kslot(grp, s)][col];
+  for (int s = 0; s < 8; ++s) o[s] = rows[k0 + kslot(grp, s)][col0 + idx];
   return o;
 }
 
@@ -620,9 +632,9 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
       st4(&sZt[idx][rw + 4 * grp], z);
     }
     __syncthreads();
-    // carried tile update, its 16-row tiles dealt to the waves (K^T, Q^T read element-wise; the
-    // right operands, rows of the transposed 16-column tiles, read as fragments once for all of
-    // a wave's tiles)
+    // carried tile update, its 16-row tiles dealt to the waves (K^T, Q^T fragments by transposing
+    // reads of the row-major k / q rows; the right operands, rows of the transposed 16-column
+    // tiles, read as fragments once for all of a wave's tiles)
     typename M::Op bz[kC / 32], bi[REV ? kC / 32 : 1];
 #pragma unroll
     for (int ks = 0; ks < kC / 32; ++ks) {
@@ -639,9 +651,8 @@ __device__ __forceinline__ void bwd_scan_pass(const BwdParams& p,
 #pragma unroll
       for (int ks = 0; ks < kC / 32; ++ks) {
         // + K^T diag(delta) V' (forward);  - K^T diag(gamma) diag(beta) Z + Q^T diag(gamma) dO^
-        acc = M::mma_xs(acc, in_col_frag(sK, 32 * ks, grp, 16 * rt + idx), bz[ks]);
-        if constexpr (REV)
-          acc = M::mma_xs(acc, in_col_frag(sQ, 32 * ks, grp, 16 * rt + idx), bi[ks]);
+        acc = M::mma_xs(acc, in_col_frag(sK, 32 * ks, grp, 16 * rt), bz[ks]);
+        if constexpr (REV) acc = M::mma_xs(acc, in_col_frag(sQ, 32 * ks, grp, 16 * rt), bi[ks]);
       }
       xr[uu] = acc;
       store_x<M>(S, idx, 16 * rt + 4 * grp, acc);
