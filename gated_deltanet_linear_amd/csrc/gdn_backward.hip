@@ -700,10 +700,10 @@ __device__ __forceinline__ typename M::frag_t exact_frag(const float (&x)[8]) {
   for (int s = 0; s < 8; ++s) o[s] = x[s];
   return o;
 }
-// acc += A B over depth K on fp32 MFMA, A and B from element accessors, the depth loop kept
-// rolled (fewer operands in flight, for the register-bound gradient kernel).
-template <typename FA, typename FB>
-__device__ __forceinline__ f32x4 tile_mma_f32(FA a, FB b, int K, f32x4 acc) {
+// acc += A B over depth K, A and B from element accessors, B exact in mode M and A split (fp32
+// MFMA in F32Mode), the depth loop kept rolled.
+template <typename M, typename FA, typename FB>
+__device__ __forceinline__ f32x4 tile_mma_sx(FA a, FB b, int K, f32x4 acc) {
   const int lane = threadIdx.x & 63, idx = lane & 15, grp = lane >> 4;
 #pragma unroll 1
   for (int k0 = 0; k0 < K; k0 += 32) {
@@ -714,7 +714,14 @@ __device__ __forceinline__ f32x4 tile_mma_f32(FA a, FB b, int K, f32x4 acc) {
       xa[s] = a(idx, kk);
       xb[s] = b(kk, idx);
     }
-    acc = F32Mode::mma_ss(acc, F32Mode::make(xa), F32Mode::make(xb));
+    const typename M::Op oa = M::make(xa);
+    if constexpr (M::kSplit) {
+      const bf16x8 fb = exact_frag<M>(xb);
+      acc = mma32(oa.hi, fb, acc);
+      acc = mma32(oa.lo, fb, acc);
+    } else {
+      acc = mma32(oa.v, exact_frag<M>(xb), acc);
+    }
   }
   return acc;
 }
@@ -775,9 +782,10 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
   const int ch = wave >> 2;        // this wave's column half of the C x C products
   const int ctw = wave % NB;       // this wave's d_k column tile in the R / dq / dk products
   const int rt0 = (wave / NB) * RPW;  // and its first row tile there
-  // bf16 inputs: the products with the states (R1..R3) on bf16 MFMA, a bf16 dO exact and the
-  // other operands split hi + lo. The C x C products and dq / dk stay on fp32 MFMA: dg sums
-  // their entries with cancellation, and split operands there double its error.
+  // bf16 inputs: the products with the states (R1..R3) and the dq / dk products on bf16 MFMA,
+  // k / q and a bf16 dO exact, the other operands split hi + lo. The C x C products (dP, dA) stay
+  // on fp32 MFMA: dg sums their entries with cancellation, and split operands there double its
+  // error.
   using MR = std::conditional_t<std::is_same<InT, bf16>::value, Bf16Mode, F32Mode>;
   constexpr bool kDoXR = MR::kSplit && std::is_same<OT, bf16>::value;  // dO values exact
 
@@ -1068,12 +1076,12 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
       const int c0 = 16 * ctw, r0 = 16 * (rt0 + u);
-      dq[u] = tile_mma_f32([&](int i, int kk) { return sPG[r0 + i][kk]; },
-                           [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
-      dk[u] = tile_mma_f32([&](int i, int kk) { return sPG[kk][r0 + i]; },
-                           [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
-      dk[u] = tile_mma_f32([&](int i, int kk) { return sDS[r0 + i][kk] + sDS[kk][r0 + i]; },
-                           [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
+      dq[u] = tile_mma_sx<MR>([&](int i, int kk) { return sPG[r0 + i][kk]; },
+                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
+      dk[u] = tile_mma_sx<MR>([&](int i, int kk) { return sPG[kk][r0 + i]; },
+                              [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
+      dk[u] = tile_mma_sx<MR>([&](int i, int kk) { return sDS[r0 + i][kk] + sDS[kk][r0 + i]; },
+                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
     }
     __syncthreads();  // LDS reused by the next V head
   }
