@@ -161,6 +161,25 @@ __device__ __forceinline__ f32x4 tile_mma_rows(const TA* a_row, float a_scale, c
   return acc;
 }
 
+// acc += A B^T over depth K for bf16 rows (exact operands: one bf16 MFMA per 32-deep step, the
+// products exact, fp32 accumulation); an A row with ok == false counts as zeros.
+__device__ __forceinline__ f32x4 tile_mma_rows_bf16(const bf16* a_row, bool ok, const bf16* b_row,
+                                                    int K, f32x4 acc) {
+  const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const bf16x4 alo = *reinterpret_cast<const bf16x4*>(a_row + k0 + 4 * grp);
+    const bf16x4 ahi = *reinterpret_cast<const bf16x4*>(a_row + k0 + 16 + 4 * grp);
+    const bf16x4 blo = *reinterpret_cast<const bf16x4*>(b_row + k0 + 4 * grp);
+    const bf16x4 bhi = *reinterpret_cast<const bf16x4*>(b_row + k0 + 16 + 4 * grp);
+    const bf16x8 av = ok ? bf16x8{alo[0], alo[1], alo[2], alo[3], ahi[0], ahi[1], ahi[2], ahi[3]}
+                         : bf16x8{};
+    const bf16x8 bv{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+    acc = mma32(av, bv, acc);
+  }
+  return acc;
+}
+
 // (sequence, first token, valid rows) of chunk slot `slot`; false for an unused slot.
 __device__ __forceinline__ bool slot_chunk(const BwdParams& p, int slot, int& n, int& t0, int& L) {
   n = slot_to_seq(p.cu, p.num_seqs, slot);
@@ -205,8 +224,16 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
   const InT* a_k = ra < L ? K + ((size_t)(t0 + ra) * p.hqk + m) * D : nullptr;
   const InT* a_q = ra < L ? Q + ((size_t)(t0 + ra) * p.hqk + m) * D : nullptr;
   for (int ct = 0; ct < 4; ++ct) {
-    const f32x4 s = tile_mma_rows(a_k, 1.f, krow(16 * ct + idx), D, zero4());
-    const f32x4 qk = tile_mma_rows(a_q, 1.f, krow(16 * ct + idx), D, zero4());
+    f32x4 s, qk;
+    if constexpr (std::is_same<InT, bf16>::value) {  // exact operands on bf16 MFMA
+      const bf16* a0 = krow(ra);
+      const bf16* q0 = Q + ((size_t)(t0 + (ra < L ? ra : 0)) * p.hqk + m) * D;
+      s = tile_mma_rows_bf16(a0, ra < L, krow(16 * ct + idx), D, zero4());
+      qk = tile_mma_rows_bf16(q0, ra < L, krow(16 * ct + idx), D, zero4());
+    } else {
+      s = tile_mma_rows(a_k, 1.f, krow(16 * ct + idx), D, zero4());
+      qk = tile_mma_rows(a_q, 1.f, krow(16 * ct + idx), D, zero4());
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * wave + 4 * grp + r, j = 16 * ct + idx;
