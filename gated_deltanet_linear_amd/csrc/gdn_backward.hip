@@ -248,20 +248,33 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
   __syncthreads();
 
   // T = (I + A)^-1, A strictly lower, by 16 x 16 blocks. Diagonal blocks: wave w inverts block
-  // w by forward substitution, lane c owning column c (each column is an independent triangular
-  // solve; a lane reads back only its own column). Off-diagonal blocks, one block row after the
-  // other: T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, the i products of a block row on i waves.
+  // w by forward substitution in registers, x_i = delta_ic - sum_{j<i} A_ij x_j with lane c < 16
+  // carrying column c; lane i holds row i of the block and readlane broadcasts A_ij. Off-diagonal
+  // blocks, one block row after the other: T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, the i products of
+  // a block row on i waves.
   {
     const int b0 = 16 * wave;
     for (int e = tid; e < kC * kC; e += 256) sT[e / kC][e % kC] = 0.f;
-    __syncthreads();
+    float arow[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) arow[j] = sA[b0 + (lane & 15)][b0 + j];
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = i == lane ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float part[4] = {0.f, 0.f, 0.f, 0.f};  // independent chains
+#pragma unroll
+      for (int j = 0; j < i; ++j)
+        part[j & 3] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                               __builtin_bit_cast(int, arow[j]), i)),
+                           x[j], part[j & 3]);
+      x[i] = i == lane ? 1.f : -((part[0] + part[1]) + (part[2] + part[3]));
+    }
+    __syncthreads();  // sT zeroed
     if (lane < 16) {
-      const int c = lane;
-      for (int r = 0; r < 16; ++r) {
-        float x = r == c ? 1.f : 0.f;
-        for (int mm = c; mm < r; ++mm) x -= sA[b0 + r][b0 + mm] * sT[b0 + mm][b0 + c];
-        if (r >= c) sT[b0 + r][b0 + c] = x;
-      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sT[b0 + i][b0 + lane] = x[i];
     }
     __syncthreads();
     for (int bi = 1; bi < 4; ++bi) {
