@@ -311,13 +311,15 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
 }
 
 // ---- bwd_scan: states forward, state gradients in reverse ---------------------------------
-// One 4-wave workgroup per (sequence, V head, 16-column tile); wave w owns token rows
-// 16 w .. 16 w + 15 of the chunk products and d_k row tiles w, w + 4 of the carried tile.
-// Operands are laid out in LDS so that an MFMA fragment (8 values along the depth) is two 16-byte
-// reads: the carried tile and the 16-column operands (v or dO^, Y or dV', V' or Z) are stored
-// transposed (a row per column, contiguous along the depth), T and P row-major in the forward
-// pass and transposed in the reverse pass (whose products take T^T and P^T). K^T and Q^T are
-// read element-wise from the row-major k / q rows.
+// One pass per (sequence, V head, 16-column tile) on 4 waves; wave w owns token rows
+// 16 w .. 16 w + 15 of the chunk products and d_k row tiles w, w + 4 of the carried tile, which
+// it holds in registers. Operands are laid out in LDS so that an MFMA fragment (8 values along
+// the depth) is two wide reads: the carried tile's copy (hi + lo bf16 pairs for bf16 inputs) and
+// the 16-column operands (v or dO^, Y or dV', V' or Z) are stored transposed (a row per column,
+// contiguous along the depth), T and P row-major in the forward pass and transposed in the
+// reverse pass (whose products take T^T and P^T). K^T and Q^T fragments come from the row-major
+// k / q rows: transposing LDS reads for bf16, element reads for fp32. With bf16 inputs both
+// passes run side by side in one 8-wave workgroup.
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 // fragment of a row contiguous along the depth, each value scaled by sv[depth]
