@@ -1057,32 +1057,41 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) hdh += __shfl_xor(hdh, off);
     if (lane == 0) sred[wave] = hdh;
-    // <Y_t, Z_t> of this wave's rows (column half 0 only; D / 16 consecutive values per lane)
-    float yz[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ch == 0) {
+    // <Y_t, Z_t>: wave w takes rows 8 w + 2 grp + r (r = 0, 1), D / 16 consecutive values per
+    // lane; rows past the chunk end read row 0 and are dropped at the store
+    float yz[2];
+    {
       constexpr int CPL = D / 16;  // values per lane
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rw + 4 * grp + r;
-        if (t < L) {
-          const float* yr = p.ys + row_off(t) + CPL * idx;
-          const float* zr = p.zs + row_off(t) + CPL * idx;
+      for (int r = 0; r < 2; ++r) {
+        const int t = 8 * wave + 2 * grp + r;
+        const float* yr = p.ys + row_off(t < L ? t : 0) + CPL * idx;
+        const float* zr = p.zs + row_off(t < L ? t : 0) + CPL * idx;
+        float acc = 0.f;
+        if constexpr (CPL % 4 == 0) {
+#pragma unroll
+          for (int c = 0; c < CPL; c += 4) {
+            const f32x4 y4 = ld4(yr + c), z4 = ld4(zr + c);
+            acc = fmaf(y4[0], z4[0], fmaf(y4[1], z4[1], fmaf(y4[2], z4[2], fmaf(y4[3], z4[3], acc))));
+          }
+        } else {
 #pragma unroll
           for (int c = 0; c < CPL; c += 2) {
             const float2 y2 = *reinterpret_cast<const float2*>(yr + c);
             const float2 z2 = *reinterpret_cast<const float2*>(zr + c);
-            yz[r] = fmaf(y2.x, z2.x, fmaf(y2.y, z2.y, yz[r]));
+            acc = fmaf(y2.x, z2.x, fmaf(y2.y, z2.y, acc));
           }
         }
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) yz[r] += __shfl_xor(yz[r], off);
+        for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+        yz[r] = acc;
       }
     }
     __syncthreads();  // sPG, sDS, sE, sga, sdc, sbt, sred complete
-    if (ch == 0 && idx == 0) {  // dbeta_t = <Y_t, Z_t> + sum_j dA_tj At_tj
+    if (idx == 0) {  // dbeta_t = <Y_t, Z_t> + sum_j dA_tj At_tj
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rw + 4 * grp + r;
+      for (int r = 0; r < 2; ++r) {
+        const int t = 8 * wave + 2 * grp + r;
         if (t < L) p.dbeta[(size_t)(t0 + t) * p.hv + h] = yz[r] + sbt[t];
       }
     }
