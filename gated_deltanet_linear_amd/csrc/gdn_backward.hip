@@ -23,16 +23,18 @@
 //   token's dB; summed in this form, the parts that cancel are never formed: plain fp32 suffix
 //   sums of db lost ~1e-4 of dg's RMS).
 //
-// Four launches, all fp32 (fp32 MFMA 16x16x4; bf16 inputs widened exactly):
+// Launches (fp32 accumulation throughout; with bf16 inputs the products whose operands allow it
+// run on bf16 MFMA, exact operands as they are and computed ones as hi + lo bf16 pairs, the C x C
+// products of the gradient kernel on fp32 MFMA; with fp32 inputs every product on fp32 MFMA):
 //   bwd_intra  one workgroup per (chunk slot, V head): b, T (forward substitution), P, At.
-//   bwd_scan<false>  per (sequence, V head, 16-column tile): the states H at every chunk start
-//              (from the initial state), and Y, V' of every token.
-//   bwd_scan<true>   same layout, chunks in reverse: dH' of every chunk, Z, dv, dh0.
+//   bwd_scan forward pass, per (sequence, V head, 16-column tile): the states H at every chunk
+//              start (from the initial state), and Y, V' of every token.
+//   bwd_scan reverse pass, same layout, chunks in reverse: dH' of every chunk, Z, dv, dh0. The
+//              two passes share no outputs: with bf16 inputs one 8-wave workgroup runs both side
+//              by side (bwd_scan2), with fp32 inputs they are two launches.
 //   bwd_grads  one 512-thread workgroup per (chunk slot, QK head), its G V heads in turn: dq, dk
 //              (summed over the G heads), dg, dbeta.
-// Every product is formed by tile_mma, one 16 x 16 output tile per call, its operands read
-// through accessors from LDS or global memory (the state matrices stay in global memory, read
-// along their contiguous axis).
+// The state matrices stay in global memory, read along their contiguous axis.
 #include <type_traits>
 
 #include "gdn_device.hpp"
