@@ -147,8 +147,10 @@ gdn_status_t gdn_chunk_scan(const gdn_shape_t* shape, const int32_t* cu_seqlens,
  *   dv [T][H_v][d_v] qkv_dtype, dg, dbeta [T][H_v] fp32, dh0 [N][H_v][d_k][d_v] state_dtype.
  *   dout [T][H_v][d_v] out_dtype; dht [N][H_v][d_k][d_v] state_dtype, or NULL for no
  *   final-state term; initial_state as in gdn_chunk_forward (NULL for zeros); dh0 may be NULL.
- * All arithmetic is fp32. The forward states are recomputed from initial_state (nothing from a
- * forward call is reused). workspace >= gdn_chunk_backward_workspace_size(shape) bytes,
+ * Accumulation is fp32; with bf16 q/k/v most products run on bf16 MFMA with the computed
+ * operands carried as hi + lo bf16 pairs (about 16 significant bits), the rest on fp32 MFMA; with
+ * fp32 inputs every product is fp32. The forward states are recomputed from initial_state
+ * (nothing from a forward call is reused). workspace >= gdn_chunk_backward_workspace_size(shape) bytes,
  * 256-byte aligned, caller-owned scratch.
  */
 size_t gdn_chunk_backward_workspace_size(const gdn_shape_t* shape);
