@@ -769,23 +769,6 @@ __device__ __forceinline__ f32x4 tile_mma_sx(FA a, FB b, int K, f32x4 acc) {
   }
   return acc;
 }
-// acc += A B^T over depth K on fp32 MFMA, this lane's A row and B row contiguous along the depth
-template <typename TA>
-__device__ __forceinline__ f32x4 tile_mma_rows_f32(const TA* a_row, float a_scale,
-                                                   const float* b_row, int K, f32x4 acc) {
-  const int grp = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    f32x8 av, bv;
-    row_frag(a_row, k0, grp, a_scale, av);
-    row_frag(b_row, k0, grp, 1.f, bv);
-    const float xa[8] = {av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
-    const float xb[8] = {bv[0], bv[1], bv[2], bv[3], bv[4], bv[5], bv[6], bv[7]};
-    acc = F32Mode::mma_ss(acc, F32Mode::make(xa), F32Mode::make(xb));
-  }
-  return acc;
-}
-
 // ---- bwd_grads --------------------------------------------------------------------------------
 // 512 threads, two waves per SIMD. For the products with the states (R1..R3) and the dq / dk
 // tiles, wave w owns one d_k column tile (w % NB) and NB / 2 of the 4 row tiles: a state-row
@@ -1024,14 +1007,33 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
         at_v[u][r] = At[t * kC + j];
         pm_v[u][r] = Pm[t * kC + j];
       }
+    // both column tiles in one pass over the depth: this lane's dO and Z fragments are loaded
+    // once for the four products (V' rows past the chunk end are read as row 0 of the chunk and
+    // masked below)
+    f32x4 dpv[2] = {zero4(), zero4()}, zav[2] = {zero4(), zero4()};
+    {
+      const int j0 = 32 * ch + idx, j1 = 32 * ch + 16 + idx;
+      const float* vp0 = p.vp + row_off(j0 < L ? j0 : 0);
+      const float* vp1 = p.vp + row_off(j1 < L ? j1 : 0);
+      const float am = my_ok ? 1.f : 0.f;
+#pragma unroll 2
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        f32x8 ao, az, b0, b1;
+        row_frag(my_dO, k0, grp, am, ao);
+        row_frag(my_Z, k0, grp, am, az);
+        row_frag(vp0, k0, grp, 1.f, b0);
+        row_frag(vp1, k0, grp, 1.f, b1);
+        dpv[0] = mma32(ao, b0, dpv[0]);
+        zav[0] = mma32(az, b0, zav[0]);
+        dpv[1] = mma32(ao, b1, dpv[1]);
+        zav[1] = mma32(az, b1, zav[1]);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int c0 = 16 * (2 * ch + u);
-      // V' rows past the chunk end are read as row 0 of the chunk and masked below
-      const float* vprow = p.vp + row_off(c0 + idx < L ? c0 + idx : 0);
-      const f32x4 dp =
-          p.scale * tile_mma_rows_f32(my_dO, my_ok ? 1.f : 0.f, vprow, D, zero4());
-      const f32x4 za = tile_mma_rows_f32(my_Z, my_ok ? 1.f : 0.f, vprow, D, zero4());
+      const f32x4 dp = p.scale * dpv[u];
+      const f32x4 za = zav[u];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rw + 4 * grp + r, j = c0 + idx;
