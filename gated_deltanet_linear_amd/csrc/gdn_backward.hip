@@ -744,31 +744,6 @@ __device__ __forceinline__ typename M::frag_t exact_frag(const float (&x)[8]) {
   for (int s = 0; s < 8; ++s) o[s] = x[s];
   return o;
 }
-// acc += A B over depth K, A and B from element accessors, B exact in mode M and A split (fp32
-// MFMA in F32Mode), the depth loop kept rolled.
-template <typename M, typename FA, typename FB>
-__device__ __forceinline__ f32x4 tile_mma_sx(FA a, FB b, int K, f32x4 acc) {
-  const int lane = threadIdx.x & 63, idx = lane & 15, grp = lane >> 4;
-#pragma unroll 1
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    float xa[8], xb[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int kk = k0 + kslot(grp, s);
-      xa[s] = a(idx, kk);
-      xb[s] = b(kk, idx);
-    }
-    const typename M::Op oa = M::make(xa);
-    if constexpr (M::kSplit) {
-      const bf16x8 fb = exact_frag<M>(xb);
-      acc = mma32(oa.hi, fb, acc);
-      acc = mma32(oa.lo, fb, acc);
-    } else {
-      acc = mma32(oa.v, exact_frag<M>(xb), acc);
-    }
-  }
-  return acc;
-}
 // ---- bwd_grads --------------------------------------------------------------------------------
 // 512 threads, two waves per SIMD. For the products with the states (R1..R3) and the dq / dk
 // tiles, wave w owns one d_k column tile (w % NB) and NB / 2 of the 4 row tiles: a state-row
@@ -1128,15 +1103,43 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(BwdParams p) {
       if (lane < L) p.dg[(size_t)(t0 + lane) * p.hv + h] = suf + pre + hdhs + fe;
     }
     // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dS + dS^T) K  (this wave's tiles)
+    // (the k / q column fragments of a depth step are read once for all of this wave's row tiles;
+    // on bf16 MFMA they are exact and the left operands split)
+    auto mma_sx = [](f32x4 acc, const float (&xa)[8], const typename MR::frag_t& fb) {
+      const typename MR::Op oa = MR::make(xa);
+      if constexpr (MR::kSplit) {
+        acc = mma32(oa.hi, fb, acc);
+        return mma32(oa.lo, fb, acc);
+      } else {
+        return mma32(oa.v, fb, acc);
+      }
+    };
+#pragma unroll 1
+    for (int k0 = 0; k0 < kC; k0 += 32) {
+      const int c0 = 16 * ctw;
+      float xk[8], xq[8];
 #pragma unroll
-    for (int u = 0; u < RPW; ++u) {
-      const int c0 = 16 * ctw, r0 = 16 * (rt0 + u);
-      dq[u] = tile_mma_sx<MR>([&](int i, int kk) { return sPG[r0 + i][kk]; },
-                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dq[u]);
-      dk[u] = tile_mma_sx<MR>([&](int i, int kk) { return sPG[kk][r0 + i]; },
-                              [&](int kk, int j) { return sQ[kk][c0 + j]; }, kC, dk[u]);
-      dk[u] = tile_mma_sx<MR>([&](int i, int kk) { return sDS[r0 + i][kk] + sDS[kk][r0 + i]; },
-                              [&](int kk, int j) { return sK[kk][c0 + j]; }, kC, dk[u]);
+      for (int s = 0; s < 8; ++s) {
+        const int kk = k0 + kslot(grp, s);
+        xk[s] = sK[kk][c0 + idx];
+        xq[s] = sQ[kk][c0 + idx];
+      }
+      const typename MR::frag_t fk = exact_frag<MR>(xk), fq = exact_frag<MR>(xq);
+#pragma unroll
+      for (int u = 0; u < RPW; ++u) {
+        const int ri = 16 * (rt0 + u) + idx;
+        float a1[8], a2[8], a3[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int kk = k0 + kslot(grp, s);
+          a1[s] = sPG[ri][kk];
+          a2[s] = sPG[kk][ri];
+          a3[s] = sDS[ri][kk] + sDS[kk][ri];
+        }
+        dq[u] = mma_sx(dq[u], a1, fk);
+        dk[u] = mma_sx(dk[u], a2, fq);
+        dk[u] = mma_sx(dk[u], a3, fk);
+      }
     }
     __syncthreads();  // LDS reused by the next V head
   }
