@@ -3,7 +3,7 @@
  *
  * The library computes the gated delta rule with a matrix state per value head,
  *   H_t = a_t H_{t-1} + k_t u_t^T,   u_t = b_t (v_t - a_t H_{t-1}^T k_t),   o_t = scale H_t^T q_t,
- * where a_t = exp(g_t), H is [d_k][d_v] (the spec S_t is H_t^T), and V head h reads
+ * where a_t = exp(g_t), H is [d_k][d_v] (the matrix-form state S_t is H_t^T), and V head h reads
  * QK head h / (H_v / H_qk). Page citations (by page title and section):
  *   [MoE report]  "Qwen3.5-MoE-35B-A3B 模型架构深度拆解报告" (pillumina.github.io), §3.3-§3.7.
  *   [xiwon notes] "Qwen3.5 观测记录" (xiwon.blog), sections "DeltaNet", "Gated DeltaNet",

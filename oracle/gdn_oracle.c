@@ -8,7 +8,7 @@
  *
  * Pins (tests/test_oracle_*.py check this file against values that it does
  * not compute itself): a dense closed form solved with LAPACK, the chunked
- * WY form at several chunk sizes, the spec matrix form, beta = 0 decay,
+ * WY form at several chunk sizes, the matrix form of the gated delta rule, beta = 0 decay,
  * exact retrieval with orthonormal keys, exact rational arithmetic in the
  * scalar case, numpy.convolve for the conv, and library sigmoid / softplus
  * for the gates; the reverse mode against central finite differences of the
@@ -44,7 +44,7 @@ static int check_cu(int64_t num_seqs, const int64_t* cu) {
  * One recurrent step per token, per (sequence, V head) chain.
  *
  * The state H is [dk][dv] ("key_dim x value_dim", [MoE report] §3.3 stage 3;
- * the spec S is its transpose). Per token t, following the order of the
+ * the matrix-form state S is its transpose). Per token t, following the order of the
  * read / error / write steps in [xiwon notes] "DeltaNet" and "Gated DeltaNet"
  * and the decode code there (state multiplied by exp(g) first, then
  * delta = (v - kv_mem) * beta):

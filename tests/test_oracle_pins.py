@@ -2,8 +2,8 @@
 
 Each test compares ``oracle.recurrent`` (token-by-token, in C) with a different
 route to the same numbers: a dense closed form solved by LAPACK, the chunked
-WY/UT form of the MoE report's §3.7 at several chunk sizes, the north-star
-matrix form S_t = a S (I - b k k^T) + b v k^T, closed forms of special cases,
+WY/UT form of the MoE report's §3.7 at several chunk sizes, the matrix form
+of the gated delta rule S_t = a S (I - b k k^T) + b v k^T, closed forms of special cases,
 and exact rational arithmetic. A dropped decay, a wrong sign, a transposed state
 or a wrong GQA index fails at least one of them.
 """
@@ -95,7 +95,7 @@ def test_chunked_wy_form_equals_recurrence(C, T):
     assert _rel(ht[0, 0], H) < 1e-10
 
 
-def test_north_star_matrix_form():
+def test_delta_rule_matrix_form():
     """S_t = a_t S_{t-1} (I - b_t k k^T) + b_t v k^T,  o_t = S_t q_t  with S = H^T."""
     rng = np.random.default_rng(5)
     T, dk, dv = 50, 7, 9
