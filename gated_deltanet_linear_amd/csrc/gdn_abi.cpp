@@ -106,6 +106,8 @@ gdn_status_t gdn_chunk_scan(const gdn_shape_t* s, const int32_t* cu, const void*
   gdn_status_t st = check_chunk_common(s, cu, q, k, ws, ws_bytes);
   if (st != GDN_OK) return st;
   if (s->total_tokens > 0 && (!v || !o)) return GDN_ERR_INVALID_ARGUMENT;
+  // v rows are loaded and o rows stored with 16-byte accesses.
+  if (!aligned(v, 16) || !aligned(o, 16)) return GDN_ERR_INVALID_ARGUMENT;
   return from_hip(gdn::launch_chunk_scan(*s, cu, q, k, v, h0, o, ht, ws,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -117,6 +119,7 @@ gdn_status_t gdn_chunk_forward(const gdn_shape_t* s, const int32_t* cu, const vo
   gdn_status_t st = check_chunk_common(s, cu, q, k, ws, ws_bytes);
   if (st != GDN_OK) return st;
   if (s->total_tokens > 0 && (!v || !o || !g || !beta)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(v, 16) || !aligned(o, 16)) return GDN_ERR_INVALID_ARGUMENT;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   st = from_hip(gdn::launch_chunk_intra(*s, cu, q, k, g, beta, ws, hs));
   if (st != GDN_OK) return st;
@@ -140,6 +143,11 @@ gdn_status_t gdn_chunk_backward(const gdn_shape_t* s, const int32_t* cu, const v
       (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
     return GDN_ERR_INVALID_ARGUMENT;
   if (!aligned(ws, 256)) return GDN_ERR_INVALID_ARGUMENT;
+  // Rows of q, k, v, dout and of the gradients are read and written with 8- and 16-byte
+  // vector accesses.
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return GDN_ERR_INVALID_ARGUMENT;
   if (ws_bytes < gdn_chunk_backward_workspace_size(s)) return GDN_ERR_WORKSPACE_TOO_SMALL;
   return from_hip(gdn::launch_chunk_backward(*s, cu, q, k, v, g, beta, h0, dout, dht, dq, dk, dv,
                                              dg, dbeta, dh0, ws,

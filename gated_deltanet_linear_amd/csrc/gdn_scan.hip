@@ -22,8 +22,6 @@
 // at two s_barriers per chunk that the producers also pass.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
 #include <atomic>
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -729,21 +727,6 @@ hipError_t launch_scan_cfg(const ScanParams& p, long long heads, int G, hipStrea
   return hipGetLastError();
 }
 
-// GDN_SCAN_LAYOUT=rows|tiles|tiles8 overrides the choice below (all layouts compute
-// bit-identical results; the tests use it to check that). tiles8 applies where the 8-tile
-// workgroup exists (bf16 operands and output, d = 128) and means tiles elsewhere.
-int forced_layout() {
-  static const int v = [] {
-    const char* e = getenv("GDN_SCAN_LAYOUT");
-    if (!e) return 0;
-    if (!strcmp(e, "rows")) return 1;
-    if (!strcmp(e, "tiles")) return 2;
-    if (!strcmp(e, "tiles8")) return 3;
-    return 0;
-  }();
-  return v;
-}
-
 // Compute units of the current device (a write-once cache per device; concurrent first calls
 // store the same value).
 int device_cus() {
@@ -769,13 +752,10 @@ hipError_t launch_scan_t(const gdn_shape_t& s, const ScanParams& p, hipStream_t 
   // one chain per CU (bf16 operands and output, d = 128), all 8 tiles of a chain in one
   // workgroup: two compute waves per SIMD and half the staging per tile, at one workgroup per
   // CU (fewer chains would leave CUs idle).
-  const int forced = forced_layout();
-  if (forced == 1 || (forced == 0 && heads * tiles <= 512))
-    return launch_scan_cfg<Mode, D, 1, 4, OutT>(p, heads, G, stream);
+  if (heads * tiles <= 512) return launch_scan_cfg<Mode, D, 1, 4, OutT>(p, heads, G, stream);
   if constexpr (tiles % 8 == 0 && std::is_same<Mode, Bf16Mode>::value &&
                 std::is_same<OutT, bf16>::value) {
-    if (forced == 3 || (forced == 0 && heads >= device_cus()))
-      return launch_scan_cfg<Mode, D, 8, 1, OutT>(p, heads, G, stream);
+    if (heads >= device_cus()) return launch_scan_cfg<Mode, D, 8, 1, OutT>(p, heads, G, stream);
   }
   if constexpr (tiles % 4 == 0) return launch_scan_cfg<Mode, D, 4, 1, OutT>(p, heads, G, stream);
   else return launch_scan_cfg<Mode, D, 2, 1, OutT>(p, heads, G, stream);

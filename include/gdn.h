@@ -113,7 +113,8 @@ size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
  *   final_state   [N][H_v][d_k][d_v] state_dtype (out), or NULL; it may equal initial_state
  *   workspace     >= gdn_chunk_forward_workspace_size(shape) bytes, 256-byte aligned,
  *                 caller-owned scratch; its contents on entry do not matter.
- * It runs gdn_chunk_intra then gdn_chunk_scan on `stream`.
+ * q, k, v and o must be 16-byte aligned (16-byte row accesses); GDN_ERR_INVALID_ARGUMENT
+ * otherwise. It runs gdn_chunk_intra then gdn_chunk_scan on `stream`.
  */
 gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                                const void* q, const void* k, const void* v, const float* g,
@@ -128,7 +129,8 @@ gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqle
  * unit-lower-triangular inverse (I + A)^-1 and the masked decayed Q K^T) into the workspace.
  * gdn_chunk_scan then runs the sequential cross-chunk recurrence (Steps 5-7) from it. The
  * workspace contents between the two calls are private to the library; scan must use the same
- * shape, cu_seqlens, q, k, g and beta as the intra call that filled it.
+ * shape, cu_seqlens, q, k, g and beta as the intra call that filled it. Alignment as for
+ * gdn_chunk_forward (q, k, v, o 16 bytes; workspace 256 bytes).
  */
 gdn_status_t gdn_chunk_intra(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                              const void* q, const void* k, const float* g, const float* beta,
@@ -151,7 +153,8 @@ gdn_status_t gdn_chunk_scan(const gdn_shape_t* shape, const int32_t* cu_seqlens,
  * operands carried as hi + lo bf16 pairs (about 16 significant bits), the rest on fp32 MFMA; with
  * fp32 inputs every product is fp32. The forward states are recomputed from initial_state
  * (nothing from a forward call is reused). workspace >= gdn_chunk_backward_workspace_size(shape) bytes,
- * 256-byte aligned, caller-owned scratch.
+ * 256-byte aligned, caller-owned scratch. q, k, v, dout, dq, dk and dv must be 16-byte aligned
+ * (vector row accesses); GDN_ERR_INVALID_ARGUMENT otherwise.
  */
 size_t gdn_chunk_backward_workspace_size(const gdn_shape_t* shape);
 gdn_status_t gdn_chunk_backward(const gdn_shape_t* shape, const int32_t* cu_seqlens,

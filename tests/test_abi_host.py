@@ -61,9 +61,9 @@ def test_workspace_size_formula(lib):
 FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: calls below fail validation first
 
 
-def _chunk(lib, s, ws_bytes=1 << 40, q=FAKE, ws=FAKE, cu=FAKE):
-    return lib.gdn_chunk_forward(ctypes.byref(s) if s is not None else None, cu, q, FAKE, FAKE,
-                                 FAKE, FAKE, None, FAKE, None, ws, ws_bytes, None)
+def _chunk(lib, s, ws_bytes=1 << 40, q=FAKE, ws=FAKE, cu=FAKE, v=FAKE, o=FAKE, k=FAKE):
+    return lib.gdn_chunk_forward(ctypes.byref(s) if s is not None else None, cu, q, k, v,
+                                 FAKE, FAKE, None, o, None, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -87,7 +87,9 @@ def test_chunk_forward_rejects_bad_pointers_and_workspace(lib):
     assert _chunk(lib, None) == INVALID
     assert _chunk(lib, s, cu=None) == INVALID
     assert _chunk(lib, s, q=None) == INVALID
-    assert _chunk(lib, s, q=ctypes.c_void_p((1 << 20) + 2)) == INVALID  # misaligned
+    for name in ("q", "k", "v", "o"):  # 16-byte row accesses
+        for off in (2, 8):
+            assert _chunk(lib, s, **{name: ctypes.c_void_p((1 << 20) + off)}) == INVALID, name
     assert _chunk(lib, s, ws=ctypes.c_void_p((1 << 20) + 64)) == INVALID  # ws not 256-aligned
     need = lib.gdn_chunk_forward_workspace_size(ctypes.byref(s))
     assert _chunk(lib, s, ws_bytes=need - 1) == WS_SMALL
@@ -97,6 +99,11 @@ def test_chunk_forward_rejects_bad_pointers_and_workspace(lib):
                               1 << 40, None) == INVALID
     assert lib.gdn_chunk_scan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
                               need - 1, None) == WS_SMALL
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.gdn_chunk_scan(ctypes.byref(s), FAKE, FAKE, FAKE, mis, None, FAKE, None, FAKE,
+                              1 << 40, None) == INVALID  # v
+    assert lib.gdn_chunk_scan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, mis, None, FAKE,
+                              1 << 40, None) == INVALID  # o
 
 
 def test_recurrent_step_validation(lib):
@@ -226,6 +233,15 @@ def test_chunk_backward_validation(lib):
         o = list(outs)
         o[i] = None
         assert call(s, outs=o) == INVALID
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    for i in (1, 2, 3, 7):  # q, k, v, dout: 16-byte row accesses
+        bad = list(ins[:9])
+        bad[i] = mis
+        assert call(s, ins=bad) == INVALID, i
+    for i in (0, 1, 2):  # dq, dk, dv
+        o = list(outs)
+        o[i] = mis
+        assert call(s, outs=o) == INVALID, i
     assert call(_shape(state_dtype=3)) == INVALID
     assert call(_shape(head_dim_k=48, head_dim_v=48)) == UNSUPPORTED
 

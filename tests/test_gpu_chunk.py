@@ -187,51 +187,45 @@ def test_prefill_then_decode_equals_longer_prefill():
 _LAYOUT_CONFIGS = [(dt, d) for dt in ("bf16", "f32") for d in (32, 64, 128)]
 
 
-def test_scan_layouts_are_bit_identical():
-    """The scan layouts (row-split: 4 waves per d_v tile; tile-per-wave with 4 tiles per
-    workgroup; tile-per-wave with all 8 tiles of a d = 128 chain per workgroup, bf16 in and out)
-    for every input dtype, output dtype and head size: identical bits, the tile layout within
-    tolerance of the oracle, and bf16 outputs equal to the fp32 outputs rounded. Each layout runs
-    in a process of its own (the layout is chosen once per process)."""
-    import os
-    import subprocess
-    import sys
-    import tempfile
-    code = (
-        "import sys, torch; sys.path.insert(0, '.'); import synthetic_inputs as si;"
-        "import gated_deltanet_linear_amd as gdn;"
-        "res = [];"
-        f"cfgs = {_LAYOUT_CONFIGS!r};\n"
-        "for dt, dd in cfgs:\n"
-        "    c = si.make_core_case([300, 64, 5], 2, 4, dd, dd, dtype=dt, gate='model',"
-        " h0_std=0.02, seed=91 + dd);\n"
-        "    d = {k: getattr(c, k).cuda() for k in ('q','k','v','g','beta','cu_seqlens','h0')};\n"
-        "    for od in (torch.float32, torch.bfloat16):\n"
-        "        print('layout case', dt, dd, od, flush=True);\n"
-        "        o, h = gdn.chunk_forward(d['q'], d['k'], d['v'], d['g'], d['beta'],"
-        " d['cu_seqlens'], initial_state=d['h0'], out_dtype=od);\n"
-        "        res.append((o.cpu(), h.cpu()))\n"
-        "torch.save(res, sys.argv[1])\n")
-    outs = {}
-    with tempfile.TemporaryDirectory() as td:
-        for layout in ("rows", "tiles", "tiles8"):
-            path = os.path.join(td, layout + ".pt")
-            env = dict(os.environ, GDN_SCAN_LAYOUT=layout)
-            print(f"[layout] {layout}", flush=True)
-            subprocess.run([sys.executable, "-c", code, path], check=True, env=env,
-                           cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                           timeout=300)
-            outs[layout] = torch.load(path, weights_only=True)
-    for i, (dt, dd) in enumerate(_LAYOUT_CONFIGS):
-        for j, od in enumerate(("f32", "bf16")):
-            (o_r, h_r), (o_t, h_t) = outs["rows"][2 * i + j], outs["tiles"][2 * i + j]
-            assert torch.equal(o_r, o_t) and torch.equal(h_r, h_t), (dt, dd, od)
-            o_8, h_8 = outs["tiles8"][2 * i + j]
-            assert torch.equal(o_r, o_8) and torch.equal(h_r, h_8), (dt, dd, od, "tiles8")
-        (o32, h32), (o16, h16) = outs["tiles"][2 * i], outs["tiles"][2 * i + 1]
-        assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(h16, h32), (dt, dd)
-        case = si.make_core_case([300, 64, 5], 2, 4, dd, dd, dtype=dt, gate="model",
-                                 h0_std=0.02, seed=91 + dd)
-        o_ref, h_ref = oracle_case(case)
-        assert_rms_close(o32, o_ref, TOL[dt], f"tiles {dt} d={dd} o")
-        assert_rms_close(h32, h_ref, TOL[dt], f"tiles {dt} d={dd} final state")
+def _concat_cases(a, b):
+    """Case a followed by the sequences of case b (same heads and dtypes)."""
+    cu = torch.cat([a.cu_seqlens, a.cu_seqlens[-1] + b.cu_seqlens[1:]])
+    h0 = None if a.h0 is None else torch.cat([a.h0, b.h0])
+    return si.CoreCase(q=torch.cat([a.q, b.q]), k=torch.cat([a.k, b.k]), v=torch.cat([a.v, b.v]),
+                       g=torch.cat([a.g, b.g]), beta=torch.cat([a.beta, b.beta]), cu_seqlens=cu,
+                       h0=h0, meta=dict(a.meta))
+
+
+@pytest.mark.parametrize("dt,dd", _LAYOUT_CONFIGS)
+def test_scan_batch_invariance_across_layouts(dt, dd):
+    """A sequence's outputs and final state do not depend on what else is in the batch. The scan
+    picks its workgroup layout from the number of (sequence, V head) chains: three sequences alone
+    (12 chains) run the row-split layout; the same three followed by 70 filler sequences (292
+    chains) run a tile layout at every head size, and followed by 20 (92 chains) at d = 128 as
+    well (for d = 128 with bf16 in and out, 292 chains take the 8-tile workgroup). All three must agree bit for bit, for fp32 and bf16 outputs, the
+    bf16 output must be the fp32 output rounded, and the small run must meet the oracle."""
+    base = si.make_core_case([300, 64, 5], 2, 4, dd, dd, dtype=dt, gate="model", h0_std=0.02,
+                             seed=91 + dd)
+    T0 = int(base.cu_seqlens[-1])
+    runs = {}
+    for fill in (0, 20, 70):
+        case = base if fill == 0 else _concat_cases(
+            base, si.make_core_case([64] * fill, 2, 4, dd, dd, dtype=dt, gate="model",
+                                    h0_std=0.02, seed=500 + fill + dd))
+        d = to_dev(case)
+        for od in (torch.float32, torch.bfloat16):
+            print(f"layout case {dt} d={dd} fillers={fill} out={od}", flush=True)
+            o, h = gdn.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                     initial_state=d["h0"], out_dtype=od)
+            torch.cuda.synchronize()
+            runs[(fill, od)] = (o[:T0].cpu(), h[:3].cpu())
+    for od in (torch.float32, torch.bfloat16):
+        o_a, h_a = runs[(0, od)]
+        for fill in (20, 70):
+            o_b, h_b = runs[(fill, od)]
+            assert torch.equal(o_a, o_b) and torch.equal(h_a, h_b), (dt, dd, fill, od)
+    (o32, h32), (o16, h16) = runs[(0, torch.float32)], runs[(0, torch.bfloat16)]
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(h16, h32), (dt, dd)
+    o_ref, h_ref = oracle_case(base)
+    assert_rms_close(o32, o_ref, TOL[dt], f"{dt} d={dd} o")
+    assert_rms_close(h32, h_ref, TOL[dt], f"{dt} d={dd} final state")
