@@ -2,15 +2,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
 
-Prints ONE JSON line. The headline ``value`` is prefill tokens/s of the 35B-A3B-shaped GDN
-layer (1 x 4096 tokens, 16 QK / 32 V heads, d = 128, bf16 q/k/v): one step is one
-gdn_chunk_forward (its two kernels, gdn_chunk_intra then gdn_chunk_scan) over inputs already
-resident in HBM. The same line carries decode tokens/s (256 sequences x 1 token, 537 MB fp32
-state updated in place), the long-context and packed front-end workloads, the output gate (1 x 4096 shape), a decode
-step from projected inputs (fused front end + recurrent step, 256 sequences), the backward of
-the 1 x 4096 prefill, per-kernel HIP-event
-timings, the roofline of each workload's dominant kernel and the float64 CPU oracle timed on
-a bounded sample on this host.
+Prints ONE JSON line. The headline ``value`` is prefill tokens/s of the long-context workload,
+the largest single-GPU configuration: 4 sequences x 32768 tokens of the 35B-A3B-shaped GDN layer
+(16 QK / 32 V heads, d = 128, bf16 q/k/v, fp32 initial states given and final states returned).
+One step is one gdn_chunk_forward (its two kernels, gdn_chunk_intra then gdn_chunk_scan) over
+inputs already resident in HBM; W untimed steps, then exactly K timed steps. The same line
+carries, as extra keys: the 1 x 4096 prefill, decode tokens/s (256 sequences x 1 token, 537 MB
+fp32 state updated in place), the packed front-end workload, the output gate (1 x 4096 shape), a
+decode step from projected inputs (fused front end + recurrent step, 256 sequences), the
+backward of the 1 x 4096 prefill, per-kernel HIP-event timings, the roofline of each workload's
+dominant kernel and the float64 CPU oracle timed on a bounded sample of the headline workload
+on this host.
 
 Roofline conventions (algorithmic work, not what the kernels happen to issue):
   prefill FLOPs per token per V head = (4/G) C d_k + 2 C d_k + 4 C d_v + 6 d_k d_v   (C = 64)
@@ -18,7 +20,8 @@ Roofline conventions (algorithmic work, not what the kernels happen to issue):
     and the masked intra-chunk product); peak = 2500 TFLOP/s dense bf16 MFMA.
   decode bytes = 2 N H_v d_k d_v s + N [H_qk 2 d_k e + H_v (2 d_v e + 8)];  peak 8000 GB/s
     (s = 4 for the fp32 state, 2 for the bf16 state).
-  front-end bytes = T [2 conv_dim e + 2 H_v e + 8 H_v] (+ q/k/v written at their dtype).
+  front-end bytes = T [conv_dim e + 2 H_v e + 8 H_v + conv_dim e_qkv]  (mixed_qkv and a, b
+    read, g and beta written, q / k / v written at their dtype e_qkv).
   output-gate bytes = 3 T H_v d_v e + 4 d_v   (o and z read, out written, fp32 weight).
   decode front-end bytes = N [8 conv_dim e + H_v (2 e + 8)] + 4 conv_dim e   (x, window read
     and rewritten, q/k/v written; a, b in, g, beta out; taps once).
@@ -146,43 +149,6 @@ def _measure(torch, kernels, steps, warmup):
     return step_ms, wall_ms, kms
 
 
-def _cold_step_ms(torch, kernels, steps):
-    """Step time with the Infinity Cache (MALL, 256 MB) and the L2s emptied of the step's data
-    before every step: each step follows a read of a 1 GiB buffer. K (read, step) pairs and K
-    reads alone are timed back to back between events; the difference divided by K is the cold
-    step. (A read, not a write: a write would leave 1 GiB of dirty lines to be written back
-    during the step.)"""
-    stream = torch.cuda.current_stream()
-    buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    out = torch.empty((), dtype=torch.float32, device="cuda")
-
-    def flush():
-        torch.sum(buf, dim=0, out=out)
-
-    def timed(with_step):
-        for _ in range(2):
-            flush()
-            if with_step:
-                for _, fn in kernels:
-                    fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(steps):
-            flush()
-            if with_step:
-                for _, fn in kernels:
-                    fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
-
-    both = timed(True)
-    alone = timed(False)
-    del buf
-    return both - alone, alone
-
-
 def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
     case = si.workload_case(cfg_id)
     dev = "cuda"
@@ -204,7 +170,6 @@ def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
                                 initial_state=h0, o=o, final_state=ht)),
     ]
     ev_ms, ms, kms = _measure(torch, kernels, steps, warmup)
-    cold_ms, flush_ms = _cold_step_ms(torch, kernels, steps)
     lengths = case.meta["lengths"]
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
@@ -220,11 +185,7 @@ def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
                               frac=round(Fscan / (scan_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 5),
                               traffic=_traffic(f"gdn_chunk_scan_{case.meta['workload']}"),
                               algorithmic_flops_per_launch=Fscan),
-                algorithmic=dict(flops=F, bytes=B),
-                cold_cache=dict(ms_per_step=round(cold_ms, 5), tokens_per_s=round(T / (cold_ms / 1e3), 1),
-                                flush_read_ms=round(flush_ms, 5),
-                                method="each step after a 1 GiB read (caches hold none of its "
-                                       "data); (read + step) minus read, K each, HIP events"))
+                algorithmic=dict(flops=F, bytes=B))
 
 
 def run_decode(torch, gdn, si, steps, warmup):
@@ -264,6 +225,12 @@ def run_decode(torch, gdn, si, steps, warmup):
 
 
 def run_front(torch, gdn, si, steps, warmup):
+    """Workload 5 (8 packed sequences, 16 QK / 64 V heads, d = 128, bf16 projected inputs,
+    initial states): gdn_prepare then the chunked core, exactly the call sequence the end-to-end
+    parity test checks. q, k and v cross from the front end to the core in fp32: rounding them
+    to bf16 there moves the result ~15% x RMS away from the float64 front end + core on this
+    workload (its conv makes neighbouring keys nearly collinear), so the bf16 intermediates do
+    not meet the bf16 bar."""
     fc = si.workload_case(5)
     dev = "cuda"
     x, w, a, b = (t.to(dev) for t in (fc.mixed_qkv, fc.conv_weight, fc.a, fc.b))
@@ -275,11 +242,13 @@ def run_front(torch, gdn, si, steps, warmup):
     ws = torch.empty(gdn.workspace_size(T, n, hqk, hv, dk), dtype=torch.uint8, device=dev)
     o = torch.empty((T, hv, dv), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((n, hv, dk, dv), dtype=torch.float32, device=dev)
+    qkv_dtype = torch.float32
 
     qkv = {}
 
     def prep():
-        qkv["t"] = gdn.prepare(x, w, a, b, A_log, dt_bias, cu, hqk, dk, hv, dv)
+        qkv["t"] = gdn.prepare(x, w, a, b, A_log, dt_bias, cu, hqk, dk, hv, dv,
+                               qkv_dtype=qkv_dtype)
 
     def intra():
         q, k, v, g, beta = qkv["t"]
@@ -293,19 +262,21 @@ def run_front(torch, gdn, si, steps, warmup):
         torch, [("gdn_prepare", prep), ("gdn_chunk_intra", intra), ("gdn_chunk_scan", scan)],
         steps, warmup)
     conv_dim = 2 * hqk * dk + hv * dv
-    Bprep = T * (2 * conv_dim * 2 + 2 * hv * 2 + 8 * hv)
+    eq = 4 if qkv_dtype == torch.float32 else 2
+    # mixed_qkv read, a and b read, g and beta written, q / k / v written at their dtype
+    Bprep = T * (conv_dim * 2 + 2 * hv * 2 + 8 * hv + conv_dim * eq)
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
+    peak = PEAK_F32_TFLOPS if qkv_dtype == torch.float32 else PEAK_BF16_TFLOPS
     return dict(T=T, lengths=m["lengths"], ms_per_step=ms, step_ms_events=ev_ms,
-                tokens_per_s=T / (ms / 1e3),
+                tokens_per_s=T / (ms / 1e3), qkv_dtype=str(qkv_dtype).replace("torch.", ""),
                 kernels_ms=kms, path_tflops=F / (ms / 1e3) / 1e12,
                 prepare=_hbm("gdn_prepare", Bprep, kms["gdn_prepare"],
-                             "gdn_prepare_prefill_397b_packed_8xU512_8192"),
+                             "gdn_prepare_prefill_397b_packed_8xU512_8192_f32qkv"),
                 roofline=dict(kernel="gdn_chunk_scan", bound="mfma",
                               achieved=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12, 3),
-                              peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                              frac=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12 /
-                                         PEAK_BF16_TFLOPS, 5)))
+                              peak=peak, unit="TFLOP/s",
+                              frac=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12 / peak, 5)))
 
 
 def _hbm(kernel, nbytes, ms, traffic_key=None):
@@ -424,16 +395,21 @@ def run_backward(torch, gdn, si, steps, warmup):
     return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=T / (ms / 1e3),
                 kernels_ms=kms, workspace_bytes=nbytes,
                 roofline=dict(kernel="gdn_chunk_backward (3 launches)", bound="mfma",
-                              achieved=round(tf, 3), peak=PEAK_F32_TFLOPS, unit="TFLOP/s",
-                              frac=round(tf / PEAK_F32_TFLOPS, 5), traffic=None,
-                              algorithmic_flops_per_launch=F))
+                              achieved=round(tf, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=round(tf / PEAK_BF16_TFLOPS, 5),
+                              traffic=_traffic("gdn_chunk_backward_backward_1x4096"),
+                              algorithmic_flops_per_launch=F,
+                              note="bf16 inputs: most products on bf16 MFMA (computed operands "
+                                   "as hi + lo pairs), the C x C dP and dA products on fp32 "
+                                   "MFMA; priced against the bf16 dense peak"))
 
 
 def cpu_baseline(case, budget_s=20.0, min_s=3.0):
-    """The float64 oracle as it stands on this host, on whole (sequence, V head) chains of the
-    prefill workload: whole passes over all V heads are repeated until ~min_s of work (a
-    partial pass is scaled if the budget runs out first); tokens/s for the whole layer."""
-    import numpy as np  # noqa: F401
+    """The float64 oracle as it stands on this host, on whole (sequence, V head) chains of a
+    prefill workload: chains are taken in order (sequence-major, all V heads of a sequence with
+    their QK heads) in groups of one per thread until about min_s of work (or the budget) is
+    spent; tokens/s for the whole layer is scaled from the chain-tokens done."""
+    import numpy as np
 
     import oracle
 
@@ -441,32 +417,36 @@ def cpu_baseline(case, budget_s=20.0, min_s=3.0):
     T, hqk, dk = case.q.shape
     hv = case.v.shape[1]
     G = hv // hqk
+    cu = case.cu_seqlens.numpy().astype(np.int64)
+    n_seqs = len(cu) - 1
     threads = oracle.num_threads()
-    heads_total, t_spent, passes = 0, 0.0, 0
-    while t_spent < min_s and t_spent < budget_s:
-        # One oracle call over a group of V heads (threads chains at once).
-        heads_done = 0
-        while heads_done < hv and t_spent < budget_s:
-            hs = list(range(heads_done, min(hv, heads_done + max(1, threads))))
-            ms = sorted({h // G for h in hs})
-            # keep the h -> h // G mapping by taking whole QK groups
-            q = f64(case.q[:, ms[0]:ms[-1] + 1])
-            k = f64(case.k[:, ms[0]:ms[-1] + 1])
-            h_lo, h_hi = ms[0] * G, (ms[-1] + 1) * G
-            v = f64(case.v[:, h_lo:h_hi])
-            g = f64(case.g[:, h_lo:h_hi])
-            b = f64(case.beta[:, h_lo:h_hi])
-            t0 = time.perf_counter()
-            oracle.recurrent(q, k, v, g, b, case.cu_seqlens.numpy(), output_final_state=True)
-            t_spent += time.perf_counter() - t0
-            heads_done = h_hi
-        heads_total += heads_done
-        passes += 1
-    per_layer_s = t_spent * hv / heads_total
+    chain_tokens_total = int(sum((cu[n + 1] - cu[n]) * hv for n in range(n_seqs)))
+    done_tokens, chains, t_spent = 0, 0, 0.0
+    n, h0 = 0, 0
+    while t_spent < min_s and t_spent < budget_s and n < n_seqs:
+        # one oracle call over up to `threads` V heads of sequence n (whole QK groups)
+        h1 = min(hv, h0 + max(G, (threads // G) * G))
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        q = f64(case.q[s0:s1, h0 // G:h1 // G])
+        k = f64(case.k[s0:s1, h0 // G:h1 // G])
+        v = f64(case.v[s0:s1, h0:h1])
+        g = f64(case.g[s0:s1, h0:h1])
+        b = f64(case.beta[s0:s1, h0:h1])
+        init = None if case.h0 is None else f64(case.h0[n:n + 1, h0:h1])
+        t0 = time.perf_counter()
+        oracle.recurrent(q, k, v, g, b, [0, s1 - s0], initial_state=init,
+                         output_final_state=True)
+        t_spent += time.perf_counter() - t0
+        done_tokens += (s1 - s0) * (h1 - h0)
+        chains += h1 - h0
+        h0 = h1
+        if h0 >= hv:
+            n, h0 = n + 1, 0
+    per_layer_s = t_spent * chain_tokens_total / done_tokens
     return dict(value=round(T / per_layer_s, 2), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"workload prefill_35b_a3b_1x4096: {heads_total} V-head chains of {T} "
-                       f"tokens ({passes} pass(es) over the {hv} heads) in {t_spent:.1f} s on "
-                       f"{threads} threads, scaled to one layer of {hv} heads",
+                sample=f"workload {case.meta['workload']}: {chains} (sequence, V head) chains, "
+                       f"{done_tokens} chain-tokens of the layer's {chain_tokens_total}, in "
+                       f"{t_spent:.1f} s on {threads} threads, scaled to the whole layer",
                 wall_s=round(t_spent, 2),
                 host_cpu_count=os.cpu_count(),
                 affinity=len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None)
@@ -499,15 +479,15 @@ def main():
         return
     out = {}
     only = args.only
-    pre = None
+    lg = None
+    if only in (None, "long"):
+        lg = run_prefill(torch, gdn, si, 3, args.steps, args.warmup, with_h0=True)
     if only in (None, "prefill"):
         pre = run_prefill(torch, gdn, si, 2, args.steps, args.warmup, with_h0=False)
+        pre.pop("case")
+        out["prefill_35b_a3b_1x4096"] = pre
     if only in (None, "decode"):
         out["decode"] = run_decode(torch, gdn, si, args.steps, args.warmup)
-    if only in (None, "long"):
-        lg = run_prefill(torch, gdn, si, 3, max(3, args.steps // 10), 2, with_h0=True)
-        lg.pop("case")
-        out["long_context_4x32768"] = lg
     if only in (None, "front"):
         out["front_end_packed_8_seqs"] = run_front(torch, gdn, si, max(3, args.steps // 5), 2)
     if only in (None, "gate"):
@@ -518,21 +498,20 @@ def main():
         out["decode_front_256x1"] = run_decode_front(torch, gdn, si, args.steps, args.warmup)
 
     line = {"metric": "GDN prefill tokens/s (1 MI355X; decode tokens/s alongside)",
-            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic"}
-    if pre is not None:
-        case = pre.pop("case")
-        line.update(value=round(pre["tokens_per_s"], 1), ms_per_step=round(pre["ms_per_step"], 5),
-                    config={"workload": "prefill_35b_a3b_1x4096", "num_seqs": 1, "seq_len": 4096,
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic"}
+    if lg is not None:
+        case = lg.pop("case")
+        line.update(value=round(lg["tokens_per_s"], 1), ms_per_step=round(lg["ms_per_step"], 5),
+                    config={"workload": "prefill_long_4x32768", "num_seqs": 4, "seq_len": 32768,
                             "num_qk_heads": 16, "num_v_heads": 32, "head_dim": 128, "chunk": 64,
                             "qkv_dtype": "bf16", "out_dtype": "bf16", "state_dtype": "f32",
-                            "initial_state": False, "final_state": True},
-                    roofline=pre["roofline"], kernels_ms=pre["kernels_ms"],
-                    cold_cache=pre["cold_cache"],
-                    path=dict(tflops=round(pre["path_tflops"], 3),
-                              mfma_frac=round(pre["path_mfma_frac"], 5),
-                              hbm_gbs=round(pre["path_hbm_gbs"], 1), **pre["algorithmic"]))
+                            "initial_state": True, "final_state": True},
+                    roofline=lg["roofline"], kernels_ms=lg["kernels_ms"],
+                    path=dict(tflops=round(lg["path_tflops"], 3),
+                              mfma_frac=round(lg["path_mfma_frac"], 5),
+                              hbm_gbs=round(lg["path_hbm_gbs"], 1), **lg["algorithmic"]))
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(case)
     else:

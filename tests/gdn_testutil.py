@@ -74,3 +74,38 @@ def oracle_chains(case, chains):
 def to_dev(case, dev="cuda"):
     return {k: (None if getattr(case, k) is None else getattr(case, k).to(dev))
             for k in ("q", "k", "v", "g", "beta", "cu_seqlens", "h0")}
+
+
+def bf16_store(x, rounding):
+    """Store float64 values as bf16 and read them back: round to nearest even ("rne", torch's
+    cast of the fp32 value) or truncate toward zero ("trunc", the top 16 bits of the fp32 value),
+    or keep them ("none")."""
+    if rounding == "none":
+        return x
+    x32 = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if rounding == "rne":
+        return x32.to(torch.bfloat16).double().numpy()
+    if rounding == "trunc":
+        return (x32.view(torch.int32) & ~0xFFFF).view(torch.float32).double().numpy()
+    raise ValueError(rounding)
+
+
+def decode_state_storage_model(case, h0, N, T, rounding):
+    """Error model of a stored bf16 decode state: T decode steps of N sequences (token t of
+    sequence n at row t * N + n) in float64 arithmetic, with the state written back through
+    bf16_store(rounding) after every step and each output formed before that store, as the decode
+    kernel does. Returns (o [N, T, H_v, d_v], final state [N, H_v, d_k, d_v]). With rounding
+    "none" it is the plain token recurrence (pinned against the oracle)."""
+    q, k, v, g, b = (f64(getattr(case, a)) for a in ("q", "k", "v", "g", "beta"))
+    G = v.shape[1] // q.shape[1]
+    H = f64(h0).copy()
+    outs = []
+    for t in range(T):
+        sl = slice(t * N, (t + 1) * N)
+        qt, kt = np.repeat(q[sl], G, axis=1), np.repeat(k[sl], G, axis=1)
+        H = np.exp(g[sl])[:, :, None, None] * H
+        u = b[sl][:, :, None] * (v[sl] - np.einsum("nhij,nhi->nhj", H, kt))
+        H = H + kt[:, :, :, None] * u[:, :, None, :]
+        outs.append(np.einsum("nhij,nhi->nhj", H, qt))
+        H = bf16_store(H, rounding)
+    return np.stack(outs, 1), H

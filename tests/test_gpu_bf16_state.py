@@ -6,9 +6,10 @@ even cast of the fp32 state. Bars:
   an fp32 intermediate except the stored state itself, so outputs meet the fp32 bar (1e-4 * RMS,
   fp32 outputs; bf16 inputs of the chunked path: the bf16 bar) and the stored state meets the
   same bar on top of its own rounding (one bf16 ulp of the reference);
-* many steps: the rounding of the stored state accumulates. Measured over 256 decode steps on the
-  model-gate distribution and on slow decay; the bars below are the documented tolerance of the
-  bf16 state (errors printed for the record), the same run with an fp32 state meets the fp32 bar.
+* many steps: the rounding of the stored state accumulates. The bar of each checked step is an
+  error model of the storage format (float64 arithmetic, state stored through RNE bf16 after each
+  step, same inputs) times 1.25 plus the fp32 bar; the same run with an fp32 state meets the fp32
+  bar.
 """
 
 import numpy as np
@@ -18,7 +19,8 @@ import torch
 import gated_deltanet_linear_amd as gdn
 import oracle
 import synthetic_inputs as si
-from gdn_testutil import TOL, assert_rms_close, assert_rms_close_rounded_out, f64, rel_err
+from gdn_testutil import (TOL, assert_rms_close, assert_rms_close_rounded_out,
+                          decode_state_storage_model, f64, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,12 +109,13 @@ def _multi_step_errors(case, h0, steps_checked):
     return res
 
 
-# Measured (256 steps, 16 sequences x 4 heads, d = 128): model gates o 1.4e-2, state 2.3e-2
-# beyond one ulp; slow decay (g ~ U(-0.01, 0)) o 5.1e-2, state 1.5e-1. The error grows like the
-# square root of the steps a rounding survives (unbiased rounding; a truncating cast would grow
-# linearly and fail these bars). The bars are about twice the measurement.
-@pytest.mark.parametrize("gate,bar,state_bar", [("model", 2e-2, 5e-2), ("slow", 1e-1, 3e-1)])
-def test_bf16_state_many_decode_steps(gate, bar, state_bar):
+@pytest.mark.parametrize("gate", ["model", "slow"])
+def test_bf16_state_many_decode_steps(gate):
+    """256 decode steps of 16 sequences x 4 heads (d = 128) from and to a bf16 state. The bar at
+    every checked step is the storage-error model of the bf16 state (float64 arithmetic with the
+    state stored through round-to-nearest-even bf16 after every step, on the same inputs) times
+    1.25, plus the fp32 bar for the kernel's own arithmetic; a truncating cast exceeds it (shown
+    on the CPU in test_bf16_state_model). The same run with an fp32 state meets the fp32 bar."""
     N, hqk, hv, d, T = 16, 2, 4, 128, 256
     lengths = [N] * T  # T groups of N tokens; token t of sequence n is row t * N + n
     if gate == "model":
@@ -124,16 +127,27 @@ def test_bf16_state_many_decode_steps(gate, bar, state_bar):
     h0 = _bf16_state(rng, (N, hv, d, d), 0.02)
     steps = [1, 16, 64, 256]
     res = _multi_step_errors(case, h0, steps)
+    # the storage-error model on the same inputs (CPU)
+    perm = np.arange(T * N).reshape(T, N).T.reshape(-1)
+    ro, rh = oracle.recurrent(f64(case.q)[perm], f64(case.k)[perm], f64(case.v)[perm],
+                              f64(case.g)[perm], f64(case.beta)[perm], np.arange(0, T * N + 1, T),
+                              initial_state=f64(h0))
+    ro = ro.reshape(N, T, *ro.shape[1:])
+    mo, mh = decode_state_storage_model(case, h0, N, T, "rne")
+    rms = float(np.sqrt(np.mean(rh * rh)))
+    model = {s: rel_err(mo[:, s - 1], ro[:, s - 1]) for s in steps}
+    model["state"] = float(np.max(np.abs(mh - rh) - 2.0 ** -8 * np.abs(rh))) / rms
+    bar = {key: 1.25 * e + TOL["f32"] for key, e in model.items()}
     for s in steps:
-        print(f"  {gate} gates, step {s}: o max|err| bf16 state {res[s][0]:.3e} x RMS, "
-              f"fp32 state {res[s][1]:.3e} x RMS", flush=True)
-    print(f"  {gate} gates, final state: bf16 {res['state'][0]:.3e} "
-          f"({res['state_beyond_ulp']:.3e} beyond one ulp), fp32 {res['state'][1]:.3e}",
+        print(f"  {gate} gates, step {s}: o max|err| bf16 state {res[s][0]:.3e} x RMS "
+              f"(model {model[s]:.3e}, bar {bar[s]:.3e}), fp32 state {res[s][1]:.3e}", flush=True)
+    print(f"  {gate} gates, final state beyond one ulp: bf16 {res['state_beyond_ulp']:.3e} "
+          f"(model {model['state']:.3e}, bar {bar['state']:.3e}), fp32 {res['state'][1]:.3e}",
           flush=True)
     for s in steps:
-        assert res[s][0] <= bar, f"{gate} step {s}: {res[s][0]:.3e} > {bar}"
+        assert res[s][0] <= bar[s], f"{gate} step {s}: {res[s][0]:.3e} > {bar[s]:.3e}"
         assert res[s][1] <= TOL["f32"]
-    assert res["state_beyond_ulp"] <= state_bar
+    assert res["state_beyond_ulp"] <= bar["state"]
     assert res["state"][1] <= TOL["f32"]
 
 

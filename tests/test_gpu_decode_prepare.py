@@ -7,7 +7,7 @@ import torch
 import gated_deltanet_linear_amd as gdn
 import oracle
 import synthetic_inputs as si
-from gdn_testutil import TOL, assert_rms_close, f64, oracle_case, oracle_chains, to_dev
+from gdn_testutil import TOL, rel_err, assert_rms_close, f64, oracle_case, oracle_chains, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -116,10 +116,17 @@ def test_prepare_with_bias_fp32_inputs():
 
 
 def test_front_end_workload_stagewise_and_end_to_end():
-    """Workload 5 (8 packed sequences, 16/64 heads, d = 128): the front end against the
-    oracle's front end, the core on the front end's bf16 outputs against the oracle core on
-    the same values (sampled chains), and the whole path with fp32 intermediates against the
-    float64 front end + core (sampled chains)."""
+    """Workload 5 (8 packed sequences, 16/64 heads, d = 128).
+
+    Stage by stage: the front end against the oracle's front end, and the core on the front
+    end's bf16 outputs against the oracle core on the same values (sampled chains).
+
+    End to end, exactly the benchmark's call sequence: gdn_prepare with fp32 q / k / v, then
+    gdn_chunk_intra and gdn_chunk_scan with a bf16 output, against the float64 front end + float64
+    core (sampled chains): the fp32 output twin meets the bf16 bar and the bf16 output is its
+    round-to-nearest-even cast. The path with bf16 q / k / v between the two stages is measured
+    and printed but not held to the bar: that rounding alone moves the float64 result by ~15% x
+    RMS on this workload."""
     fc = si.workload_case(5)
     print(f"[front] lengths={fc.meta['lengths']}", flush=True)
     dev = "cuda"
@@ -135,7 +142,7 @@ def test_front_end_workload_stagewise_and_end_to_end():
     core = si.CoreCase(q=q.cpu(), k=k.cpu(), v=v.cpu(), g=g.cpu(), beta=beta.cpu(),
                        cu_seqlens=fc.cu_seqlens, h0=fc.h0, meta=fc.meta)
     rng = np.random.default_rng(5)
-    chains = [(int(n), int(h)) for n, h in zip(rng.integers(0, 8, 6), rng.integers(0, 64, 6))]
+    chains = [(int(n), int(h)) for n, h in zip(rng.integers(0, 8, 8), rng.integers(0, 64, 8))]
     cu_np = fc.cu_seqlens.numpy()
     refs = oracle_chains(core, chains)
     got_o = np.concatenate([f64(o[cu_np[n]:cu_np[n + 1], h]) for n, h in chains])
@@ -145,25 +152,42 @@ def test_front_end_workload_stagewise_and_end_to_end():
                      np.stack([refs[c][1] for c in chains]), TOL["bf16"],
                      "front workload core final state (sampled)")
 
-    # fp32 intermediates: compare with float64 front end + float64 core.
-    q32, k32, v32, g32, b32 = _prep_gpu(fc, qkv_dtype=torch.float32)
-    o32, ht32 = gdn.chunk_forward(q32, k32, v32, g32, b32, cu, initial_state=h0,
-                                  out_dtype=torch.float32)
-    torch.cuda.synchronize()
+    # float64 front end + float64 core on the sampled chains
     rq, rk, rv, rg, rb = ref
     cu64 = cu_np.astype(np.int64)
-    e2e_o, e2e_ref, e2e_h, e2e_href = [], [], [], []
-    for n, h in chains[:3]:
-        s, e = cu64[n], cu64[n + 1]
+    e2e_ref, e2e_href = [], []
+    for n, h in chains:
+        s0, e0 = cu64[n], cu64[n + 1]
         m = h // 4
-        oo, hh = oracle.recurrent(rq[s:e, m:m + 1], rk[s:e, m:m + 1], rv[s:e, h:h + 1],
-                                  rg[s:e, h:h + 1], rb[s:e, h:h + 1], [0, e - s],
+        oo, hh = oracle.recurrent(rq[s0:e0, m:m + 1], rk[s0:e0, m:m + 1], rv[s0:e0, h:h + 1],
+                                  rg[s0:e0, h:h + 1], rb[s0:e0, h:h + 1], [0, e0 - s0],
                                   initial_state=f64(fc.h0[n:n + 1, h:h + 1]))
-        e2e_o.append(f64(o32[s:e, h]))
         e2e_ref.append(oo[:, 0])
-        e2e_h.append(f64(ht32[n, h]))
         e2e_href.append(hh[0, 0])
-    assert_rms_close(np.concatenate(e2e_o), np.concatenate(e2e_ref), TOL["bf16"],
-                     "front workload end-to-end o, fp32 intermediates (sampled)")
-    assert_rms_close(np.stack(e2e_h), np.stack(e2e_href), TOL["bf16"],
-                     "front workload end-to-end final state, fp32 intermediates (sampled)")
+    e2e_ref, e2e_href = np.concatenate(e2e_ref), np.stack(e2e_href)
+
+    def sampled(o_, ht_):
+        return (np.concatenate([f64(o_[cu64[n]:cu64[n + 1], h]) for n, h in chains]),
+                np.stack([f64(ht_[n, h]) for n, h in chains]))
+
+    # the old bf16-intermediate path, for the record
+    bo, bh = sampled(o, ht)
+    print(f"  bf16 q/k/v between the stages: end-to-end o {rel_err(bo, e2e_ref):.3e} x RMS, "
+          f"final state {rel_err(bh, e2e_href):.3e} x RMS (not held to the bar)", flush=True)
+
+    # the benchmark's sequence: fp32 q/k/v, intra, scan; bf16 output and its fp32 twin
+    q32, k32, v32, g32, b32 = _prep_gpu(fc, qkv_dtype=torch.float32)
+    T, n_seqs = q32.shape[0], len(fc.meta["lengths"])
+    ws = torch.empty(gdn.workspace_size(T, n_seqs, 16, 64, 128), dtype=torch.uint8, device=dev)
+    outs = {}
+    for od in (torch.float32, torch.bfloat16):
+        gdn.chunk_intra(q32, k32, g32, b32, cu, 64, ws)
+        o_e, h_e = gdn.chunk_scan(q32, k32, v32, g32, b32, cu, ws, initial_state=h0,
+                                  final_state=torch.empty_like(h0), out_dtype=od)
+        torch.cuda.synchronize()
+        outs[od] = (o_e.cpu(), h_e.cpu())
+    eo, eh = sampled(*outs[torch.float32])
+    assert_rms_close(eo, e2e_ref, TOL["bf16"], "front workload end-to-end o (sampled)")
+    assert_rms_close(eh, e2e_href, TOL["bf16"], "front workload end-to-end final state (sampled)")
+    assert torch.equal(outs[torch.bfloat16][0], outs[torch.float32][0].to(torch.bfloat16))
+    assert torch.equal(outs[torch.bfloat16][1], outs[torch.float32][1])
