@@ -121,6 +121,24 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
     return t
 
 
+def _out(t, shape, dtype, device, name):
+    """An output buffer: a new tensor, or the caller's, which must be a contiguous GPU tensor of
+    exactly this shape and dtype (the kernels write shape x dtype bytes through its pointer)."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise GdnError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _out_dtype(out_dtype, o, default):
+    """Output dtype: the one asked for, else that of a given output buffer, else the default."""
+    if out_dtype is not None:
+        return out_dtype
+    return o.dtype if isinstance(o, torch.Tensor) else default
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -204,19 +222,16 @@ def chunk_forward(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final
     """
     hv, dv = _v_shape(v, q)
     sd = _state_dtype(initial_state, final_state, default=state_dtype)
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, sd)
+    od = _out_dtype(out_dtype, o, q.dtype)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd)
     T, dk = s.total_tokens, s.head_dim_k
     if initial_state is not None:
         _dev(initial_state, "initial_state", sd)
         if initial_state.shape != (n, hv, dk, dv):
             raise GdnError("initial_state must be [N, H_v, d_k, d_v]")
-    if o is None:
-        o = torch.empty((T, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
-    _dev(o, "o", out_dtype or q.dtype)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((n, hv, dk, dv), dtype=sd, device=q.device)
-    if final_state is not None:
-        _dev(final_state, "final_state", sd)
+    o = _out(o, (T, hv, dv), od, q.device, "o")
+    if output_final_state or final_state is not None:
+        final_state = _out(final_state, (n, hv, dk, dv), sd, q.device, "final_state")
     ws = _workspace(s, q.device, workspace)
     rc = _load().gdn_chunk_forward(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
@@ -239,16 +254,15 @@ def chunk_scan(q, k, v, g, beta, cu_seqlens, workspace, initial_state=None, o=No
     """Stage 2 of chunk_forward (sequential cross-chunk recurrence) from ``workspace``."""
     hv, dv = _v_shape(v, q)
     sd = _state_dtype(initial_state, final_state)
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, sd)
+    od = _out_dtype(out_dtype, o, q.dtype)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd)
     for t, name in ((initial_state, "initial_state"), (final_state, "final_state")):
         if t is not None:
             _dev(t, name, sd)
             if t.shape != (n, hv, s.head_dim_k, dv):
                 raise GdnError(f"{name} must be [N, H_v, d_k, d_v]")
     _dev(workspace, "workspace", torch.uint8)
-    if o is None:
-        o = torch.empty((s.total_tokens, s.num_v_heads, s.head_dim_v), dtype=out_dtype or q.dtype,
-                        device=q.device)
+    o = _out(o, (s.total_tokens, s.num_v_heads, s.head_dim_v), od, q.device, "o")
     rc = _load().gdn_chunk_scan(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
                                 workspace.numel(), _stream())
@@ -307,11 +321,9 @@ def recurrent_step(q, k, v, g, beta, state, scale=1.0, out_dtype=None, o=None) -
     if k.shape != q.shape or v.shape[0] != N or g.shape != (N, hv) or beta.shape != (N, hv) \
             or state.shape != (N, hv, dk, dv):
         raise GdnError("recurrent_step: inconsistent shapes")
-    s = _shape(N, N, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale,
-               state_dtype=state.dtype)
-    if o is None:
-        o = torch.empty((N, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
-    _dev(o, "o", out_dtype or q.dtype)
+    od = _out_dtype(out_dtype, o, q.dtype)
+    s = _shape(N, N, hqk, hv, dk, dv, q.dtype, od, scale=scale, state_dtype=state.dtype)
+    o = _out(o, (N, hv, dv), od, q.device, "o")
     rc = _load().gdn_recurrent_step(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                     _ptr(beta), _ptr(state), _ptr(o), _stream())
     _check(rc, "gdn_recurrent_step")
@@ -428,12 +440,10 @@ def decode_step(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, state
         raise GdnError("a, b must be [N, H_v]; A_log, dt_bias [H_v]")
     if state.shape != (N, hv, d, d):
         raise GdnError("state must be [N, H_v, d, d]")
-    od = out_dtype or dt
+    od = _out_dtype(out_dtype, o, dt)
     s = _shape(N, N, hqk, hv, d, d, torch.float32, od, in_dtype=dt, scale=scale,
                state_dtype=state.dtype)
-    if o is None:
-        o = torch.empty((N, hv, d), dtype=od, device=mixed_qkv.device)
-    _dev(o, "o", od)
+    o = _out(o, (N, hv, d), od, mixed_qkv.device, "o")
     rc = _load().gdn_decode_step(ctypes.byref(s), _ptr(mixed_qkv), _ptr(conv_window),
                                  _ptr(conv_weight), _ptr(conv_bias), _ptr(a), _ptr(b), _ptr(A_log),
                                  _ptr(dt_bias), float(l2norm_eps), _ptr(state), _ptr(o), _stream())

@@ -229,3 +229,44 @@ def test_scan_batch_invariance_across_layouts(dt, dd):
     o_ref, h_ref = oracle_case(base)
     assert_rms_close(o32, o_ref, TOL[dt], f"{dt} d={dd} o")
     assert_rms_close(h32, h_ref, TOL[dt], f"{dt} d={dd} final state")
+
+
+def test_binding_output_buffers_follow_the_given_tensor():
+    """A caller-provided o decides the output dtype when out_dtype is not given (fp32 q/k/v with
+    a bf16 o writes bf16, the rounded fp32 result); an o, final state or workspace that does not
+    match the call is refused on the host before any launch."""
+    case = si.make_core_case([70, 5], 2, 4, 64, 64, dtype="f32", gate="model", h0_std=0.02,
+                             seed=71)
+    d = to_dev(case)
+    T = case.q.shape[0]
+    o32, h32 = gdn.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                 initial_state=d["h0"])
+    o16 = torch.empty((T, 4, 64), dtype=torch.bfloat16, device="cuda")
+    o_ret, _ = gdn.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                 initial_state=d["h0"], o=o16)
+    ws = torch.empty(gdn.workspace_size(T, 2, 2, 4, 64), dtype=torch.uint8, device="cuda")
+    gdn.chunk_intra(d["q"], d["k"], d["g"], d["beta"], d["cu_seqlens"], 4, ws)
+    o16s = torch.empty_like(o16)
+    gdn.chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ws,
+                   initial_state=d["h0"], o=o16s)
+    torch.cuda.synchronize()
+    assert o_ret.data_ptr() == o16.data_ptr()
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(o16s, o16)
+    bad = [
+        dict(o=torch.empty((T, 4, 64), dtype=torch.bfloat16, device="cuda"),
+             out_dtype=torch.float32),                                     # dtype mismatch
+        dict(o=torch.empty((T - 1, 4, 64), dtype=torch.float32, device="cuda")),  # short
+        dict(o=torch.empty((T, 4, 64), dtype=torch.float32, device="cuda")[:, :, ::1].transpose(0, 1)),
+        dict(final_state=torch.empty((1, 4, 64, 64), dtype=torch.float32, device="cuda")),
+    ]
+    for kw in bad:
+        with pytest.raises(gdn.GdnError):
+            gdn.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                              initial_state=d["h0"], **kw)
+        if "o" in kw:
+            with pytest.raises(gdn.GdnError):
+                gdn.chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ws,
+                               initial_state=d["h0"], **kw)
+    with pytest.raises(gdn.GdnError):
+        gdn.recurrent_step(d["q"][:2], d["k"][:2], d["v"][:2], d["g"][:2], d["beta"][:2],
+                           d["h0"].clone(), o=torch.empty((2, 4, 32), device="cuda"))
