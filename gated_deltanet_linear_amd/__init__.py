@@ -72,6 +72,8 @@ def _load():
     lib.gdn_chunk_forward_workspace_size.argtypes = [sp]
     lib.gdn_chunk_forward.restype = ctypes.c_int
     lib.gdn_chunk_forward.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunk_forward_noalloc.restype = ctypes.c_int
+    lib.gdn_chunk_forward_noalloc.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.gdn_chunk_intra.restype = ctypes.c_int
     lib.gdn_chunk_intra.argtypes = [sp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.gdn_chunk_scan.restype = ctypes.c_int
@@ -237,6 +239,31 @@ def chunk_forward(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final
                                    _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
                                    _ptr(final_state), _ptr(ws), ws.numel(), _stream())
     _check(rc, "gdn_chunk_forward")
+    return o, final_state
+
+
+def chunk_forward_noalloc(q, k, v, g, beta, cu_seqlens, initial_state=None,
+                          output_final_state=True, scale=1.0, out_dtype=None, final_state=None,
+                          o=None, state_dtype=None):
+    """chunk_forward through gdn_chunk_forward_noalloc: the same result, with the workspace in the
+    library's own device array (no device allocation by the library; this wrapper still creates
+    o and final_state unless they are given)."""
+    hv, dv = _v_shape(v, q)
+    sd = _state_dtype(initial_state, final_state, default=state_dtype)
+    od = _out_dtype(out_dtype, o, q.dtype)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd)
+    T, dk = s.total_tokens, s.head_dim_k
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", sd)
+        if initial_state.shape != (n, hv, dk, dv):
+            raise GdnError("initial_state must be [N, H_v, d_k, d_v]")
+    o = _out(o, (T, hv, dv), od, q.device, "o")
+    if output_final_state or final_state is not None:
+        final_state = _out(final_state, (n, hv, dk, dv), sd, q.device, "final_state")
+    rc = _load().gdn_chunk_forward_noalloc(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                           _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                           _ptr(o), _ptr(final_state), _stream())
+    _check(rc, "gdn_chunk_forward_noalloc")
     return o, final_state
 
 

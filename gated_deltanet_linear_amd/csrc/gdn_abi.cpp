@@ -49,6 +49,9 @@ const char* gdn_status_string(gdn_status_t status) {
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: shape not compiled into this library";
     case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: a kernel launch failed";
+    case GDN_ERR_SCRATCH_LIMIT:
+      return "GDN_ERR_SCRATCH_LIMIT: the shape needs more workspace than the no-allocation "
+             "entry point's device array holds";
   }
   return "unknown gdn_status_t";
 }
@@ -124,6 +127,27 @@ gdn_status_t gdn_chunk_forward(const gdn_shape_t* s, const int32_t* cu, const vo
   st = from_hip(gdn::launch_chunk_intra(*s, cu, q, k, g, beta, ws, hs));
   if (st != GDN_OK) return st;
   return from_hip(gdn::launch_chunk_scan(*s, cu, q, k, v, h0, o, ht, ws, hs));
+}
+
+gdn_status_t gdn_chunk_forward_noalloc(const gdn_shape_t* s, const int32_t* cu, const void* q,
+                                       const void* k, const void* v, const float* g,
+                                       const float* beta, const void* h0, void* o, void* ht,
+                                       void* stream) {
+  // The same checks as gdn_chunk_forward (with the library's array standing in for the
+  // workspace), and the size limit, before any HIP call.
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (gdn_chunk_forward_workspace_size(s) > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+    return GDN_ERR_SCRATCH_LIMIT;
+  if (!cu) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens > 0 && (!q || !k || !v || !o || !g || !beta))
+    return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return GDN_ERR_INVALID_ARGUMENT;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (gdn::noalloc_scratch(&ws, &ws_bytes) != hipSuccess) return GDN_ERR_HIP;
+  return gdn_chunk_forward(s, cu, q, k, v, g, beta, h0, o, ht, ws, ws_bytes, stream);
 }
 
 size_t gdn_chunk_backward_workspace_size(const gdn_shape_t* s) {

@@ -47,6 +47,10 @@ hipError_t launch_chunk_backward(const gdn_shape_t& s, const int32_t* cu, const 
                                  void* dk, void* dv, float* dg, float* dbeta, void* dh0, void* ws,
                                  hipStream_t stream);
 
+// Device address and size of the calling thread's current device's copy of the workspace array
+// of gdn_chunk_forward_noalloc (gdn_noalloc.hip); the address is looked up once per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // Bytes of one workspace record (one chunk slot x one V head); the layout is private to
 // gdn_chunk.hip, which checks this value at compile time.
 constexpr long long kWorkspaceRecordBytes = 25088;

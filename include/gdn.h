@@ -23,8 +23,9 @@
  *     GDN_ERR_UNSUPPORTED, a short workspace GDN_ERR_WORKSPACE_TOO_SMALL; in all three
  *     cases nothing is launched. GDN_ERR_HIP means a launch failed (hipGetLastError).
  *     No C++ exception crosses this interface. Device contents of cu_seqlens are trusted.
- *   - The library holds no mutable global state: concurrent calls on different streams with
- *     disjoint outputs and workspaces are safe.
+ *   - The library holds no mutable global state apart from the device array of
+ *     gdn_chunk_forward_noalloc: concurrent calls on different streams with disjoint outputs and
+ *     workspaces are safe (gdn_chunk_forward_noalloc calls on one GPU share that array).
  *   - Supported head dims: d_k == d_v in {32, 64, 128}. num_v_heads % num_qk_heads == 0.
  */
 #ifndef GDN_H
@@ -45,7 +46,9 @@ typedef enum {
   GDN_ERR_INVALID_ARGUMENT = 1,
   GDN_ERR_UNSUPPORTED = 2,
   GDN_ERR_WORKSPACE_TOO_SMALL = 3,
-  GDN_ERR_HIP = 4
+  GDN_ERR_HIP = 4,
+  GDN_ERR_SCRATCH_LIMIT = 5 /* the shape needs more workspace than gdn_chunk_forward_noalloc's
+                               library-owned array holds (GDN_NOALLOC_SCRATCH_BYTES) */
 } gdn_status_t;
 
 typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype_t;
@@ -121,6 +124,25 @@ gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqle
                                const float* beta, const void* initial_state, void* o,
                                void* final_state, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * gdn_chunk_forward_noalloc -- gdn_chunk_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It takes
+ * the same arguments minus the workspace and computes the same result (the same kernels); the
+ * workspace is a library-owned device array of GDN_NOALLOC_SCRATCH_BYTES bytes per GPU, held from
+ * the library's first use on that GPU until the process ends. It calls no hipMalloc, hipFree or
+ * other allocating routine. A shape whose workspace (gdn_chunk_forward_workspace_size) exceeds the
+ * array returns GDN_ERR_SCRATCH_LIMIT without launching anything: 64 MiB holds, for example, one
+ * 4096-token sequence at 32 V heads ((1 + 64) x 32 records of 25088 bytes). All calls on one GPU
+ * share the array, so calls that overlap on one GPU (different streams or host threads) race and
+ * must be serialised by the caller. Other errors as gdn_chunk_forward.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdn_status_t gdn_chunk_forward_noalloc(const gdn_shape_t* shape, const int32_t* cu_seqlens,
+                                       const void* q, const void* k, const void* v,
+                                       const float* g, const float* beta,
+                                       const void* initial_state, void* o, void* final_state,
+                                       void* stream);
 
 /*
  * The two stages of gdn_chunk_forward, exported so that they can be timed or overlapped

@@ -39,7 +39,7 @@ def test_version_and_status_strings(lib):
     hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
     declared = int(re.search(r"#define GDN_ABI_VERSION (\d+)", hdr).group(1))
     assert lib.gdn_abi_version() == declared == gdn.ABI_VERSION
-    for code in range(5):
+    for code in range(6):
         assert lib.gdn_status_string(code).startswith(b"GDN_")
 
 
@@ -274,3 +274,27 @@ def test_python_binding_refuses_cpu_tensors():
         gdn.chunk_forward(x, x, x, g, g, cu)
     with pytest.raises(gdn.GdnError):
         gdn.recurrent_step(x, x, x, g, g, torch.zeros(4, 1, 32, 32))
+
+
+def test_chunk_forward_noalloc_validation(lib):
+    """The no-allocation entry point validates like gdn_chunk_forward and refuses a shape whose
+    workspace exceeds its device array before any HIP call."""
+    def call(shape, q=FAKE, v=FAKE, o=FAKE, cu=FAKE):
+        return lib.gdn_chunk_forward_noalloc(ctypes.byref(shape) if shape is not None else None,
+                                             cu, q, FAKE, v, FAKE, FAKE, None, o, None, None)
+
+    assert call(None) == INVALID
+    assert call(_shape(num_v_heads=33)) == INVALID
+    assert call(_shape(head_dim_k=96, head_dim_v=96)) == UNSUPPORTED
+    # 64 MiB holds 2674 records of 25088 bytes: 1 x 4096 tokens at 32 V heads is 65 x 32 = 2080
+    limit = 64 << 20
+    big = _shape(num_seqs=1, total_tokens=8192)  # 129 slots x 32 heads x 25088 > 64 MiB
+    assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(big)) > limit
+    assert call(big) == 5  # GDN_ERR_SCRATCH_LIMIT
+    assert b"SCRATCH_LIMIT" in lib.gdn_status_string(5)
+    ok = _shape(num_seqs=1, total_tokens=4096)
+    assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(ok)) <= limit
+    assert call(ok, cu=None) == INVALID
+    assert call(ok, q=None) == INVALID
+    assert call(ok, v=ctypes.c_void_p((1 << 20) + 8)) == INVALID
+    assert call(ok, o=ctypes.c_void_p((1 << 20) + 8)) == INVALID
