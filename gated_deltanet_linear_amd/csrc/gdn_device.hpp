@@ -24,8 +24,10 @@
 namespace gdn {
 
 typedef __bf16 bf16;
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -68,13 +70,21 @@ struct Bf16Mode {
   struct Op {
     bf16x8 hi, lo;
   };
+  // hi = RNE(x), lo = RNE(x - hi), two slots per packed conversion; the float value of a hi
+  // half is its bits moved to the top of a word, so no slot is converted twice.
   __device__ __forceinline__ static Op make(const float (&x)[8]) {
     Op o;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      bf16 h = (bf16)x[s];
-      o.hi[s] = h;
-      o.lo[s] = (bf16)(x[s] - (float)h);
+    for (int s = 0; s < 8; s += 2) {
+      const bf16x2 h = __builtin_convertvector((f32x2){x[s], x[s + 1]}, bf16x2);
+      const uint32_t u = __builtin_bit_cast(uint32_t, h);
+      const float h0 = __builtin_bit_cast(float, u << 16);
+      const float h1 = __builtin_bit_cast(float, u & 0xffff0000u);
+      const bf16x2 l = __builtin_convertvector((f32x2){x[s] - h0, x[s + 1] - h1}, bf16x2);
+      o.hi[s] = h[0];
+      o.hi[s + 1] = h[1];
+      o.lo[s] = l[0];
+      o.lo[s + 1] = l[1];
     }
     return o;
   }
@@ -83,11 +93,24 @@ struct Bf16Mode {
     c = mma32(a, b.hi, c);
     return mma32(a, b.lo, c);
   }
+  // split x exact (the split operand as A)
+  __device__ __forceinline__ static f32x4 mma_sx(f32x4 c, const Op& a, const frag_t& b) {
+    c = mma32(a.hi, b, c);
+    return mma32(a.lo, b, c);
+  }
   // split x split (lo*lo dropped: below fp32 rounding of the sum)
   __device__ __forceinline__ static f32x4 mma_ss(f32x4 c, const Op& a, const Op& b) {
     c = mma32(a.hi, b.hi, c);
     c = mma32(a.hi, b.lo, c);
     return mma32(a.lo, b.hi, c);
+  }
+  // split x split with the roles of the operands exchanged: the same three products accumulated
+  // in the order mma_ss(c, b, a) accumulates them, so that a product computed transposed
+  // (C^T = B^T A^T) rounds exactly like the untransposed one
+  __device__ __forceinline__ static f32x4 mma_ss_t(f32x4 c, const Op& a, const Op& b) {
+    c = mma32(a.hi, b.hi, c);
+    c = mma32(a.lo, b.hi, c);
+    return mma32(a.hi, b.lo, c);
   }
   // Op stored as [hi fragments of 64 lanes][lo fragments of 64 lanes] = 2 KiB per block.
   __device__ __forceinline__ static Op load_block(const char* blk, int lane) {

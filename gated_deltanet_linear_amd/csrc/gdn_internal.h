@@ -16,6 +16,11 @@ hipError_t launch_chunk_scan(const gdn_shape_t& s, const int32_t* cu, const void
                              const void* k, const void* v, const void* h0, void* o, void* ht,
                              const void* ws, hipStream_t stream);
 
+// The many-chain layout of the scan for bf16 q/k/v (gdn_scan_tiles.hip).
+hipError_t launch_chunk_scan_tiles(const gdn_shape_t& s, const int32_t* cu, const void* q,
+                                   const void* k, const void* v, const void* h0, void* o,
+                                   void* ht, const void* ws, hipStream_t stream);
+
 hipError_t launch_recurrent_step(const gdn_shape_t& s, const void* q, const void* k,
                                  const void* v, const float* g, const float* beta, void* state,
                                  void* o, hipStream_t stream);

@@ -10,7 +10,8 @@
 // Columns of H evolve independently, so a workgroup owns NT tiles of 16 d_v columns of one
 // (sequence, V head) and walks its chunks in order. Each tile is computed by RW waves:
 //   RW = 1: one wave owns all 64 rows of the chunk and its [d_k x 16] fp32 state slice stays
-//           in that wave's registers for the whole sequence (most work per wave, least LDS).
+//           in that wave's registers for the whole sequence (fp32 operands with many chains;
+//           bf16 operands with many chains run gdn_scan_tiles.hip).
 //   RW = 4: wave r owns row tile r (16 tokens) and 32 rows of the state; Y, V' and the new
 //           state cross waves through LDS (4x the waves for shapes with few sequences x heads).
 // Separate producer waves move the data: while chunk c is computed they write chunk c+1 (held
@@ -21,7 +22,6 @@
 // rows with ds_read_b64_tr_b16. In the row-split layout the waves of a tile exchange Y and V'
 // at two s_barriers per chunk that the producers also pass.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
-#include <atomic>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -727,38 +727,20 @@ hipError_t launch_scan_cfg(const ScanParams& p, long long heads, int G, hipStrea
   return hipGetLastError();
 }
 
-// Compute units of the current device (a write-once cache per device; concurrent first calls
-// store the same value).
-int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int c = cus[dev].load(std::memory_order_relaxed);
-  if (c == 0) {
-    int v = 0;
-    c = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
-    cus[dev].store(c, std::memory_order_relaxed);
-  }
-  return c;
-}
-
 template <typename Mode, int D, typename OutT>
 hipError_t launch_scan_t(const gdn_shape_t& s, const ScanParams& p, hipStream_t stream) {
   const long long heads = (long long)s.num_seqs * s.num_v_heads;
   const int G = s.num_v_heads / s.num_qk_heads;
   constexpr int tiles = D / 16;
   // Few (sequence, head) chains: 4 waves per 16-column tile so that every SIMD gets work.
-  // Many chains: 1 wave per tile, 4 tiles per workgroup sharing the staged chunk; with at least
-  // one chain per CU (bf16 operands and output, d = 128), all 8 tiles of a chain in one
-  // workgroup: two compute waves per SIMD and half the staging per tile, at one workgroup per
-  // CU (fewer chains would leave CUs idle).
+  // Many chains, fp32 operands: 1 wave per tile, 4 (or 2) tiles per workgroup sharing the staged
+  // chunk. (Many chains with bf16 operands run chunk_scan_tiles_kernel, gdn_scan_tiles.hip.)
   if (heads * tiles <= 512) return launch_scan_cfg<Mode, D, 1, 4, OutT>(p, heads, G, stream);
-  if constexpr (tiles % 8 == 0 && std::is_same<Mode, Bf16Mode>::value &&
-                std::is_same<OutT, bf16>::value) {
-    if (heads >= device_cus()) return launch_scan_cfg<Mode, D, 8, 1, OutT>(p, heads, G, stream);
+  if constexpr (std::is_same<Mode, F32Mode>::value) {
+    if constexpr (tiles % 4 == 0) return launch_scan_cfg<Mode, D, 4, 1, OutT>(p, heads, G, stream);
+    else return launch_scan_cfg<Mode, D, 2, 1, OutT>(p, heads, G, stream);
   }
-  if constexpr (tiles % 4 == 0) return launch_scan_cfg<Mode, D, 4, 1, OutT>(p, heads, G, stream);
-  else return launch_scan_cfg<Mode, D, 2, 1, OutT>(p, heads, G, stream);
+  return hipErrorInvalidValue;  // not reached: the caller dispatches bf16 many-chain shapes
 }
 
 template <typename Mode, typename OutT>
@@ -779,6 +761,9 @@ hipError_t launch_chunk_scan(const gdn_shape_t& s, const int32_t* cu, const void
   ScanParams p{cu, q, k, v, h0, o, ht, static_cast<const char*>(ws), s.num_seqs, s.num_qk_heads,
                s.num_v_heads, s.scale, s.state_dtype == GDN_DTYPE_BF16 ? 1 : 0};
   const bool out_bf = s.out_dtype == GDN_DTYPE_BF16;
+  if (s.qkv_dtype == GDN_DTYPE_BF16 &&
+      (long long)s.num_seqs * s.num_v_heads * (s.head_dim_v / 16) > 512)
+    return launch_chunk_scan_tiles(s, cu, q, k, v, h0, o, ht, ws, stream);
   if (s.qkv_dtype == GDN_DTYPE_BF16)
     return out_bf ? launch_scan_d<Bf16Mode, bf16>(s, p, stream)
                   : launch_scan_d<Bf16Mode, float>(s, p, stream);

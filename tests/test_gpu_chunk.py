@@ -199,11 +199,13 @@ def _concat_cases(a, b):
 @pytest.mark.parametrize("dt,dd", _LAYOUT_CONFIGS)
 def test_scan_batch_invariance_across_layouts(dt, dd):
     """A sequence's outputs and final state do not depend on what else is in the batch. The scan
-    picks its workgroup layout from the number of (sequence, V head) chains: three sequences alone
-    (12 chains) run the row-split layout; the same three followed by 70 filler sequences (292
-    chains) run a tile layout at every head size, and followed by 20 (92 chains) at d = 128 as
-    well (for d = 128 with bf16 in and out, 292 chains take the 8-tile workgroup). All three must agree bit for bit, for fp32 and bf16 outputs, the
-    bf16 output must be the fp32 output rounded, and the small run must meet the oracle."""
+    picks its workgroup layout from the number of (chain, 16-column tile) pairs, a chain being a
+    (sequence, V head): three sequences alone (12 chains) run the row-split layout; the same three
+    followed by 70 filler sequences (292 chains) run a one-wave-per-tile layout at every head size
+    (for bf16 q/k/v the many-chain kernel with separate chain and output waves), and followed by
+    20 (92 chains) at d = 128 as well. All three must agree bit for bit, for fp32 and bf16
+    outputs, the bf16 output must be the fp32 output rounded, and the small run must meet the
+    oracle."""
     base = si.make_core_case([300, 64, 5], 2, 4, dd, dd, dtype=dt, gate="model", h0_std=0.02,
                              seed=91 + dd)
     T0 = int(base.cu_seqlens[-1])
