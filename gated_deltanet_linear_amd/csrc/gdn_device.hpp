@@ -27,6 +27,9 @@ typedef __bf16 bf16;
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -122,6 +125,49 @@ struct Bf16Mode {
   __device__ __forceinline__ static void store_block(char* blk, int lane, const Op& o) {
     *reinterpret_cast<bf16x8*>(blk + lane * 16) = o.hi;
     *reinterpret_cast<bf16x8*>(blk + 1024 + lane * 16) = o.lo;
+  }
+};
+
+// fp16 operands of the scan's three state products when q / k / v are bf16: K H, Q H and
+// K^T (diag(delta) V'). K and Q are staged as fp16 (a bf16 value converts exactly unless it lies
+// below 2^-14 in magnitude, where the fp16 spacing is 2^-24, or beyond 65504); the state slice
+// and diag(delta) V' are rounded once to fp16 (RNE) for these products, while the state itself
+// stays fp32. Each such product is one v_mfma_f32_16x16x32_f16 per 32-deep block instead of
+// the two of an exact x hi/lo pair; T diag(beta) Y and P V' keep the bf16 hi/lo pairs.
+struct Half {
+  // 8 slots rounded to fp16 (RNE), two per packed conversion
+  __device__ __forceinline__ static f16x8 make(const float (&x)[8]) {
+    f16x8 o;
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      const f16x2 h = __builtin_convertvector((f32x2){x[s], x[s + 1]}, f16x2);
+      o[s] = h[0];
+      o[s + 1] = h[1];
+    }
+    return o;
+  }
+  __device__ __forceinline__ static f32x4 mma(const f16x8& a, const f16x8& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // 16 bytes of 8 bf16 values rewritten as 8 fp16 values (the staging of K and Q rows)
+  __device__ __forceinline__ static f32x4 from_bf16(const f32x4& raw) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&raw);
+    f32x4 out;
+    uint32_t* ow = reinterpret_cast<uint32_t*>(&out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __builtin_bit_cast(float, w[i] << 16);
+      const float hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+      ow[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+    }
+    return out;
+  }
+  // 1 KiB block: the 16-byte fragments of 64 lanes
+  __device__ __forceinline__ static f16x8 load_block(const char* blk, int lane) {
+    return *reinterpret_cast<const f16x8*>(blk + lane * 16);
+  }
+  __device__ __forceinline__ static void store_block(char* blk, int lane, const f16x8& o) {
+    *reinterpret_cast<f16x8*>(blk + lane * 16) = o;
   }
 };
 

@@ -133,6 +133,45 @@ __device__ __forceinline__ void store_half(F32Mode, char* blk, int lane, int hal
   *reinterpret_cast<f32x4*>(blk + lane * 32 + half * 16) = x;
 }
 
+// Operand of the three state products (K H, Q H and K^T V''): fp16 for bf16 q / k / v (K and Q
+// rows then staged as fp16, see Half), the mode's own operand for fp32.
+template <typename Mode>
+struct StateOp;
+template <>
+struct StateOp<Bf16Mode> {
+  using op = f16x8;
+  static constexpr bool kHalfRows = true;
+  __device__ static op make(const float (&x)[8]) { return Half::make(x); }
+  __device__ static op load(const char* blk, int lane) { return Half::load_block(blk, lane); }
+  __device__ static void store(char* blk, int lane, const op& o) { Half::store_block(blk, lane, o); }
+  __device__ static f32x4 mma(f32x4 c, const bf16x8& a, const op& b) {
+    return Half::mma(__builtin_bit_cast(f16x8, a), b, c);
+  }
+  // slots 4*half .. 4*half+3 of every lane
+  __device__ static void store_half(char* blk, int lane, int half, const f32x4& x) {
+    f16 v[4];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const f16x2 h = __builtin_convertvector((f32x2){x[e], x[e + 1]}, f16x2);
+      v[e] = h[0];
+      v[e + 1] = h[1];
+    }
+    *reinterpret_cast<uint2*>(blk + lane * 16 + half * 8) = *reinterpret_cast<const uint2*>(v);
+  }
+};
+template <>
+struct StateOp<F32Mode> {
+  using op = F32Mode::Op;
+  static constexpr bool kHalfRows = false;
+  __device__ static op make(const float (&x)[8]) { return F32Mode::make(x); }
+  __device__ static op load(const char* blk, int lane) { return F32Mode::load_block(blk, lane); }
+  __device__ static void store(char* blk, int lane, const op& o) { F32Mode::store_block(blk, lane, o); }
+  __device__ static f32x4 mma(f32x4 c, const f32x8& a, const op& b) { return F32Mode::mma_xs(c, a, b); }
+  __device__ static void store_half(char* blk, int lane, int half, const f32x4& x) {
+    ::gdn::store_half(F32Mode{}, blk, lane, half, x);
+  }
+};
+
 constexpr int kRecUnits = kWsRecordBytes / 16;                   // 16-byte units per record
 constexpr int kRecStage = (kWsRecordBytes + 1023) / 1024 * 1024;  // staged record bytes
 constexpr int kLdsBytes = 160 * 1024;                             // LDS per workgroup
@@ -198,7 +237,9 @@ struct ScanCfg {
   static constexpr int QOFF = KBYTES, ROFF = 1024 * KQ, VOFF = 1024 * (KQ + RI);
   static constexpr int BUFB = VOFF + 64 * VSTR;
   static constexpr int NC = NT * RW;
-  static constexpr int NP = (TOTAL + 31) / 32;  // producers hold <= 32 units each in registers
+  // producers hold <= 32 units each in registers; with bf16 q / k / v they also convert the K and
+  // Q rows to fp16 on the way, and four of them share that work
+  static constexpr int NP = std::is_same<Mode, Bf16Mode>::value ? 4 : (TOTAL + 31) / 32;
   static constexpr int PER = (TOTAL + NP - 1) / NP;
   static constexpr int THREADS = 64 * (NC + NP);
   static constexpr int KB = D / 32, R = 4 / RW, OWN = (KB + RW - 1) / RW;
@@ -225,6 +266,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
   using in_t = typename Mode::in_t;
   using Op = typename Mode::Op;
   using F = Frags<Mode, C::ROWB>;
+  using SO = StateOp<Mode>;
   constexpr int KB = C::KB, R = C::R, OWN = C::OWN;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -330,7 +372,8 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
               const int i = 64 * (j - C::KQ - C::RI) + lane;
               dst = C::VOFF + (i / (NT * C::VPR)) * C::VSTR + 16 * (i % (NT * C::VPR));
             }
-            *reinterpret_cast<f32x4*>(buf + dst) = r[u];
+            *reinterpret_cast<f32x4*>(buf + dst) =
+                (SO::kHalfRows && j < C::KQ) ? Half::from_bf16(r[u]) : r[u];
           }
         }
       };
@@ -413,7 +456,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
         if (kb < KB) {
           float x[8];
           pack_c_pair(Hc[o][0], Hc[o][1], x);
-          Mode::store_block(X + C::XH + kb * 2048, lane, Mode::make(x));
+          SO::store(X + C::XH + kb * 2048, lane, SO::make(x));
         }
       }
     }
@@ -476,18 +519,18 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       return *reinterpret_cast<const f32x4*>(sdel + 16 * rt + 4 * grp);
     };
 
-    // (a) state as split B fragments over d_k
-    Op HB[KB];
+    // (a) state as B fragments over d_k (the operand of the state products)
+    typename SO::op HB[KB];
     if constexpr (RW == 1) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float x[8];
         pack_c_pair(Hc[kb][0], Hc[kb][1], x);
-        HB[kb] = Mode::make(x);
+        HB[kb] = SO::make(x);
       }
     } else {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) HB[kb] = Mode::load_block(X + C::XH + kb * 2048, lane);
+      for (int kb = 0; kb < KB; ++kb) HB[kb] = SO::load(X + C::XH + kb * 2048, lane);
     }
 
     // (b) K H, Q H on this wave's row tiles; Y = V - gamma K H, gamma Q H.
@@ -520,8 +563,8 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       for (int kb = 0; kb < KB; ++kb) {
         const frag_t kf = EARLY ? ka[b][kb] : F::a(sK, 16 * rt + idx, kb, grp);
         const frag_t qf = EARLY ? qa[b][kb] : F::a(sQ, 16 * rt + idx, kb, grp);
-        kh[kb & 1] = Mode::mma_xs(kh[kb & 1], kf, HB[kb]);
-        qh[kb & 1] = Mode::mma_xs(qh[kb & 1], qf, HB[kb]);
+        kh[kb & 1] = SO::mma(kh[kb & 1], kf, HB[kb]);
+        qh[kb & 1] = SO::mma(qh[kb & 1], qf, HB[kb]);
       }
       if (KQB > 1 && i + 1 < R) load_kq(b ^ 1, rt + 1);
 #pragma unroll
@@ -606,7 +649,8 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           if (kb <= (rt >> 1)) PB[i][kb] = pblock(rt, kb);
       }
     };
-    Op VB[2], DB[2];
+    Op VB[2];
+    typename SO::op DB[2];
     if constexpr (RW == 1) {
       load_p();
 #pragma unroll
@@ -620,21 +664,21 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           d[4 + s] = x[4 + s] * d1[s];
         }
         VB[kb] = Mode::make(x);
-        DB[kb] = Mode::make(d);
+        DB[kb] = SO::make(d);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int rt = rg * R + i;
         store_half(Mode{}, X + C::XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
-        store_half(Mode{}, X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
+        SO::store_half(X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
       }
       exchange();
       load_p();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb <= rg * R + R - 1) VB[kb] = Mode::load_block(X + C::XV + kb * 2048, lane);
-        DB[kb] = Mode::load_block(X + C::XD + kb * 2048, lane);
+        DB[kb] = SO::load(X + C::XD + kb * 2048, lane);
       }
     }
 
@@ -655,14 +699,14 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           f32x4 acc = Hc[o][hf] * gC;
 #pragma unroll
           for (int kbp = 0; kbp < 2; ++kbp)
-            acc = Mode::mma_xs(acc, EARLY ? kt[o][hf][kbp] : F::kt(sK, 2 * kb + hf, kbp, lane),
-                               DB[kbp]);
+            acc = SO::mma(acc, EARLY ? kt[o][hf][kbp] : F::kt(sK, 2 * kb + hf, kbp, lane),
+                          DB[kbp]);
           Hc[o][hf] = acc;
         }
         if constexpr (RW > 1) {
           float x[8];
           pack_c_pair(Hc[o][0], Hc[o][1], x);
-          Mode::store_block(X + C::XH + kb * 2048, lane, Mode::make(x));
+          SO::store(X + C::XH + kb * 2048, lane, SO::make(x));
         }
       }
     }

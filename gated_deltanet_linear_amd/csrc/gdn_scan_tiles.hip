@@ -12,8 +12,8 @@
 // (sequence, V head) chain and has three kinds of waves:
 //   * chain wave t (one per tile) runs the recurrence of tile t: its [d_k x 16] fp32 state slice
 //     stays in its registers for the whole sequence. Per chunk it forms Y, V' and the new state,
-//     and hands the split state and V' to the output wave through LDS.
-//   * output wave t forms the output rows of tile t from Q, the split state and V'. The output
+//     and hands the state (as fp16 operand fragments) and V' to the output wave through LDS.
+//   * output wave t forms the output rows of tile t from Q, the state and V'. The output
 //     is computed transposed, so a lane holds 4 consecutive columns of one token and stores them
 //     straight to global memory.
 //   * four producer waves stage chunk c+1 (K, Q and v rows, T diag(beta), P, gamma, delta)
@@ -24,8 +24,9 @@
 // one another, while those of different waves on a SIMD do; the chain wave is the serial path,
 // so it issues only the recurrence itself, and everything else is done by the other waves.
 // Three s_barriers per chunk order the hand-overs (see the schedule below the work assignment).
-// Every product runs on bf16 MFMA in the fragment convention of gdn_device.hpp, computed
-// operands as hi + lo pairs.
+// Products run on MFMA in the fragment convention of gdn_device.hpp: the three with the state or
+// V'' (K H, Q H, K^T diag(delta) V') on fp16 operands (Half), T diag(beta) Y and P V' on bf16
+// hi + lo pairs.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -86,7 +87,7 @@ struct TilesCfg {
   static constexpr int VSTR = NT * VROWB + 16;         // padded stride: tile reads spread banks
   static constexpr int VPR = NT * VROWB / 16;          // 16-byte pieces per staged v row
   static constexpr int VU = 64 * VPR / 64;             // v units
-  static constexpr int HXB = KB * kWsBlockBytes;       // exchanged split state of one tile
+  static constexpr int HXB = KB * 1024;                // exchanged fp16 state of one tile
   static constexpr int VXB = 4 * 1024;                 // exchanged V' of one tile (4 C fragments)
   // LDS: each piece is staged once per chunk, at a point of the chunk where its previous
   // contents are no longer read; only the K^T fragments (built while the previous ones are in
@@ -166,9 +167,14 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
   //   chain wave t:  [B] Y = V - diag(gamma) K H            [M] V' = T Y, V' -> LDS
   //                  [X] H <- gamma_C H + K^T diag(delta) V', split state -> LDS
   //   output wave t: [B] Q H^T from the split state in LDS  [M] -  [X] V' P^T, output rows
-  //   producers:     [B] P(c)  [M] K, Q, v rows and K^T of chunk c + 1  [X] T, gamma, delta of c + 1
+  //   producers:     [B] P(c)  [M] K, Q, v rows of chunk c + 1
+  //                  [X] K^T, T, gamma, delta of chunk c + 1
+  // Wave priorities (s_setprio) order the SIMD's instruction arbitration among its waves:
+  // producers first (the staging of a window is on every other wave's path), then the chain,
+  // then the output waves, whose work has the most slack.
   if (wave >= 2 * NT) {
     // ---------------- producer waves ----------------
+    __builtin_amdgcn_s_setprio(3);  // highest: see the schedule above
     // Each producer runs its own copy of this code with its index known at compile time, so the
     // units it moves are fixed in the code: no branch around a load, and the compiler's waits for
     // the loads in flight stay exact.
@@ -219,11 +225,13 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
           rp[i] = *reinterpret_cast<const f32x4*>(rec + kWsPOff + 1024 * (PW * C::TPER + i) +
                                                   16 * lane);
       };
-      auto commit_rows = [&]() {
+      auto commit_rows = [&]() {  // K and Q rows staged as fp16 (operands of the state products)
 #pragma unroll
         for (int i = 0; i < C::KPER; ++i) {
-          *reinterpret_cast<f32x4*>(smem + C::KOFF + 1024 * (PW * C::KPER + i) + 16 * lane) = rk[i];
-          *reinterpret_cast<f32x4*>(smem + C::QOFF + 1024 * (PW * C::KPER + i) + 16 * lane) = rq[i];
+          *reinterpret_cast<f32x4*>(smem + C::KOFF + 1024 * (PW * C::KPER + i) + 16 * lane) =
+              Half::from_bf16(rk[i]);
+          *reinterpret_cast<f32x4*>(smem + C::QOFF + 1024 * (PW * C::KPER + i) + 16 * lane) =
+              Half::from_bf16(rq[i]);
         }
 #pragma unroll
         for (int i = 0; i < C::VPER; ++i) {
@@ -289,11 +297,11 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
         lds_barrier();  // M(c): the K, Q and v rows of chunk c are read
         if (c + 1 < nchunks) {
           commit_rows();
-          transpose(ktbuf(c + 1));  // the K^T buffer of chunk c - 1
           if (c + 2 < nchunks) load_rows(c + 2);
         }
         lds_barrier();  // X(c): T, gamma and delta of chunk c are read
         if (c + 1 < nchunks) {
+          transpose(ktbuf(c + 1));  // the K^T buffer of chunk c - 1, from this wave's own rows
           commit_t();
           if (c + 2 < nchunks) load_t(c + 2);
           lds_barrier();  // B(c + 1)
@@ -322,9 +330,14 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
   const char* sP = smem + C::POFF;
   const float* sgam = reinterpret_cast<const float*>(smem + C::GOFF);
   const float* sdel = sgam + kChunk;
+  // A fragment of fp16 K (or Q) rows of the staged chunk
+  auto hfrag = [&](const char* rows, int row, int kb) {
+    return __builtin_bit_cast(f16x8, afrag<C::ROWB>(rows, row, kb, grp));
+  };
 
   if (chain) {
     // ---------------- chain waves ----------------
+    __builtin_amdgcn_s_setprio(2);
     // Hc[it][r] = H[st_row(it, 4 grp + r)][col] (the dtype branch outside the element loops, so
     // that all loads are issued before the first wait)
     f32x4 Hc[NST];
@@ -344,15 +357,15 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
     } else {
       load_state(0.f);
     }
-    // the state as split B fragments over d_k, kept here and written for the output wave
-    Op HB[KB];
+    // the state as fp16 B fragments over d_k, kept here and written for the output wave
+    f16x8 HB[KB];
     auto split_state = [&]() {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float x[8];
         pack_c_pair(Hc[2 * kb], Hc[2 * kb + 1], x);
-        HB[kb] = M::make(x);
-        M::store_block(HX + kb * kWsBlockBytes, lane, HB[kb]);
+        HB[kb] = Half::make(x);
+        Half::store_block(HX + kb * 1024, lane, HB[kb]);
       }
     };
     split_state();
@@ -364,12 +377,12 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
       f32x4 Y[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        bf16x8 kf[KB];
+        f16x8 kf[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[kb] = afrag<C::ROWB>(sK, 16 * rt + idx, kb, grp);
+        for (int kb = 0; kb < KB; ++kb) kf[kb] = hfrag(sK, 16 * rt + idx, kb);
         f32x4 kh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kh[kb & 1] = M::mma_xs(kh[kb & 1], kf[kb], HB[kb]);
+        for (int kb = 0; kb < KB; ++kb) kh[kb & 1] = Half::mma(kf[kb], HB[kb], kh[kb & 1]);
         const int vg = lane >> 4, vs = lane & 15, va = vs & 3, ve = vs >> 2;
         const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(sV + (16 * rt + 4 * vg + ve) * C::VSTR + 8 * va));
@@ -406,9 +419,9 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
         Vp[rt] = acc;
         *reinterpret_cast<f32x4*>(VX + 1024 * rt + 16 * lane) = acc;
       }
-      // V'' = diag(delta) V' as split B fragments over tokens; gamma_C (read before X(c), after
+      // V'' = diag(delta) V' as fp16 B fragments over tokens; gamma_C (read before X(c), after
       // which the producers restage gamma and delta)
-      Op DB[2];
+      f16x8 DB[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float x[8], dx[8];
@@ -420,15 +433,15 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
           dx[s4] = x[s4] * d0[s4];
           dx[4 + s4] = x[4 + s4] * d1[s4];
         }
-        DB[kb] = M::make(dx);
+        DB[kb] = Half::make(dx);
       }
       const float gC = sgam[kChunk - 1];
-      bf16x8 KT[NST][2];
+      f16x8 KT[NST][2];
 #pragma unroll
       for (int it = 0; it < NST; ++it)
 #pragma unroll
         for (int kbp = 0; kbp < 2; ++kbp)
-          KT[it][kbp] = *reinterpret_cast<const bf16x8*>(sKT + ((it * 2 + kbp) * 64 + lane) * 16);
+          KT[it][kbp] = *reinterpret_cast<const f16x8*>(sKT + ((it * 2 + kbp) * 64 + lane) * 16);
       lds_barrier();  // X(c)
 
       // H <- gamma_C H + K^T V''
@@ -436,7 +449,7 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
       for (int it = 0; it < NST; ++it) {
         f32x4 acc = Hc[it] * gC;
 #pragma unroll
-        for (int kbp = 0; kbp < 2; ++kbp) acc = M::mma_xs(acc, KT[it][kbp], DB[kbp]);
+        for (int kbp = 0; kbp < 2; ++kbp) acc = Half::mma(KT[it][kbp], DB[kbp], acc);
         Hc[it] = acc;
       }
       split_state();  // the output wave read the previous one before M(c)
@@ -462,24 +475,25 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
   }
 
   // ---------------- output waves ----------------
+  __builtin_amdgcn_s_setprio(1);
   // O^T = scale (H^T Q^T diag(gamma) + V'^T P^T), computed transposed so that lane (idx = token,
   // grp) holds 4 consecutive columns of its token's output row and stores them directly.
   OutT* Oh = static_cast<OutT*>(p.o) + (size_t)h * D + col0 + 4 * grp;
   if (nchunks > 0) lds_barrier();  // B(0)
   for (int c = 0; c < nchunks; ++c) {
     const int t0c = start + kChunk * c, len = min(kChunk, L - kChunk * c);
-    Op HB[KB];
+    f16x8 HB[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) HB[kb] = M::load_block(HX + kb * kWsBlockBytes, lane);
+    for (int kb = 0; kb < KB; ++kb) HB[kb] = Half::load_block(HX + kb * 1024, lane);
     f32x4 QH[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      bf16x8 qf[KB];
+      f16x8 qf[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qf[kb] = afrag<C::ROWB>(sQ, 16 * rt + idx, kb, grp);
+      for (int kb = 0; kb < KB; ++kb) qf[kb] = hfrag(sQ, 16 * rt + idx, kb);
       f32x4 qh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qh[kb & 1] = M::mma_sx(qh[kb & 1], HB[kb], qf[kb]);
+      for (int kb = 0; kb < KB; ++kb) qh[kb & 1] = Half::mma(HB[kb], qf[kb], qh[kb & 1]);
       QH[rt] = (qh[0] + qh[1]) * sgam[16 * rt + idx];
     }
     lds_barrier();  // M(c)
