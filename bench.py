@@ -78,16 +78,34 @@ def prefill_bytes(lengths, hqk, hv, dk, dv, e, h0_given, state_out=True):
     return b
 
 
+def scan_bytes(lengths, hqk, hv, dk, dv, e, h0_given, state_out=True):
+    """Algorithmic HBM bytes of one scan launch: q and k (each unique byte once), v, the
+    workspace records the intra kernel wrote (25088 bytes per chunk and V head), the initial
+    states, o and the final states."""
+    T = sum(lengths)
+    n = len(lengths)
+    chunks = sum((L + C - 1) // C for L in lengths)
+    b = T * (hqk * 2 * dk * e + hv * 2 * dv * e) + chunks * hv * 25088
+    b += n * hv * dk * dv * 4 * ((1 if state_out else 0) + (1 if h0_given else 0))
+    return b
+
+
+def _sha(rel):
+    path = os.path.join(ROOT, rel)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest() if os.path.exists(path) else None
+
+
 def _traffic(kernel_key):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken on the
-    current source of that kernel; else None."""
+    current sources of that kernel (every file the record lists, by SHA-256); else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, rec["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest() if os.path.exists(src) else None
-    if sha != rec.get("source_sha256"):
+    if "sources" in rec:
+        if any(_sha(f) != h for f, h in rec["sources"].items()):
+            return None
+    elif _sha(rec["source"]) != rec.get("source_sha256"):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -174,6 +192,7 @@ def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
     B = prefill_bytes(lengths, hqk, hv, dk, dv, 2, with_h0)
+    Bscan = scan_bytes(lengths, hqk, hv, dk, dv, 2, with_h0)
     scan_ms = kms["gdn_chunk_scan"]
     return dict(case=case, T=T, ms_per_step=ms, step_ms_events=ev_ms,
                 tokens_per_s=T / (ms / 1e3), kernels_ms=kms,
@@ -184,7 +203,10 @@ def run_prefill(torch, gdn, si, cfg_id, steps, warmup, with_h0):
                               peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                               frac=round(Fscan / (scan_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 5),
                               traffic=_traffic(f"gdn_chunk_scan_{case.meta['workload']}"),
-                              algorithmic_flops_per_launch=Fscan),
+                              algorithmic_flops_per_launch=Fscan,
+                              algorithmic_bytes_per_launch=Bscan,
+                              hbm_gbs=round(Bscan / (scan_ms / 1e3) / 1e9, 1),
+                              hbm_frac=round(Bscan / (scan_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)),
                 algorithmic=dict(flops=F, bytes=B))
 
 
