@@ -33,6 +33,7 @@ typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 64;  // chunk length (tokens); one token per lane of a wave
 constexpr int kWave = 64;
@@ -128,12 +129,13 @@ struct Bf16Mode {
   }
 };
 
-// fp16 operands of the scan's three state products when q / k / v are bf16: K H, Q H and
-// K^T (diag(delta) V'). K and Q are staged as fp16 (a bf16 value converts exactly unless it lies
-// below 2^-14 in magnitude, where the fp16 spacing is 2^-24, or beyond 65504); the state slice
-// and diag(delta) V' are rounded once to fp16 (RNE) for these products, while the state itself
-// stays fp32. Each such product is one v_mfma_f32_16x16x32_f16 per 32-deep block instead of
-// the two of an exact x hi/lo pair; T diag(beta) Y and P V' keep the bf16 hi/lo pairs.
+// fp16 operands of the scan's two products with the state when q / k / v are bf16: K H and Q H.
+// K and Q are staged as fp16 (a bf16 value converts exactly unless it lies below 2^-14 in
+// magnitude, where the fp16 spacing is 2^-24, or beyond 65504); the state slice is rounded once
+// per chunk to fp16 (RNE) for these products, while the state itself stays fp32. Each such
+// product is one v_mfma_f32_16x16x32_f16 per 32-deep block instead of the two of an exact x
+// hi/lo pair. The update K^T diag(delta) V', T diag(beta) Y and P V' keep bf16 hi/lo pairs (K^T
+// converted back from the staged fp16 rows, exactly).
 struct Half {
   // 8 slots rounded to fp16 (RNE), two per packed conversion
   __device__ __forceinline__ static f16x8 make(const float (&x)[8]) {
@@ -161,6 +163,29 @@ struct Half {
       ow[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
     }
     return out;
+  }
+  // 4 fp16 values (as read by ds_read_b64_tr_b16) to bf16 (RNE; exact for values that were bf16)
+  __device__ __forceinline__ static bf16x4 to_bf16(const s16x4& raw) {
+    typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 h = __builtin_bit_cast(f16x4, raw);
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const bf16x2 b = __builtin_convertvector((f32x2){(float)h[e], (float)h[e + 1]}, bf16x2);
+      o[e] = b[0];
+      o[e + 1] = b[1];
+    }
+    return o;
+  }
+  __device__ __forceinline__ static bf16x8 to_bf16(const f16x8& h) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 b = __builtin_convertvector((f32x2){(float)h[e], (float)h[e + 1]}, bf16x2);
+      o[e] = b[0];
+      o[e + 1] = b[1];
+    }
+    return o;
   }
   // 1 KiB block: the 16-byte fragments of 64 lanes
   __device__ __forceinline__ static f16x8 load_block(const char* blk, int lane) {
@@ -259,7 +284,6 @@ __device__ __forceinline__ int slot_to_seq(const int32_t* cu, int num_seqs, int 
 // ---- LDS staging and operand fragments from staged rows -------------------------------
 
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 
 // 16-byte XOR swizzle of a staged row (keeps the 8 rows that a fragment read touches on

@@ -133,8 +133,9 @@ __device__ __forceinline__ void store_half(F32Mode, char* blk, int lane, int hal
   *reinterpret_cast<f32x4*>(blk + lane * 32 + half * 16) = x;
 }
 
-// Operand of the three state products (K H, Q H and K^T V''): fp16 for bf16 q / k / v (K and Q
-// rows then staged as fp16, see Half), the mode's own operand for fp32.
+// Operand of the two products with the state (K H, Q H): fp16 for bf16 q / k / v (K and Q rows
+// then staged as fp16, see Half), the mode's own operand for fp32. kt() turns a K^T fragment read
+// from those rows into the operand of the state update (back to bf16 for bf16 q / k / v).
 template <typename Mode>
 struct StateOp;
 template <>
@@ -147,16 +148,8 @@ struct StateOp<Bf16Mode> {
   __device__ static f32x4 mma(f32x4 c, const bf16x8& a, const op& b) {
     return Half::mma(__builtin_bit_cast(f16x8, a), b, c);
   }
-  // slots 4*half .. 4*half+3 of every lane
-  __device__ static void store_half(char* blk, int lane, int half, const f32x4& x) {
-    f16 v[4];
-#pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      const f16x2 h = __builtin_convertvector((f32x2){x[e], x[e + 1]}, f16x2);
-      v[e] = h[0];
-      v[e + 1] = h[1];
-    }
-    *reinterpret_cast<uint2*>(blk + lane * 16 + half * 8) = *reinterpret_cast<const uint2*>(v);
+  __device__ static bf16x8 kt(const bf16x8& raw) {
+    return Half::to_bf16(__builtin_bit_cast(f16x8, raw));
   }
 };
 template <>
@@ -167,9 +160,7 @@ struct StateOp<F32Mode> {
   __device__ static op load(const char* blk, int lane) { return F32Mode::load_block(blk, lane); }
   __device__ static void store(char* blk, int lane, const op& o) { F32Mode::store_block(blk, lane, o); }
   __device__ static f32x4 mma(f32x4 c, const f32x8& a, const op& b) { return F32Mode::mma_xs(c, a, b); }
-  __device__ static void store_half(char* blk, int lane, int half, const f32x4& x) {
-    ::gdn::store_half(F32Mode{}, blk, lane, half, x);
-  }
+  __device__ static f32x8 kt(const f32x8& f) { return f; }
 };
 
 constexpr int kRecUnits = kWsRecordBytes / 16;                   // 16-byte units per record
@@ -649,8 +640,7 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           if (kb <= (rt >> 1)) PB[i][kb] = pblock(rt, kb);
       }
     };
-    Op VB[2];
-    typename SO::op DB[2];
+    Op VB[2], DB[2];
     if constexpr (RW == 1) {
       load_p();
 #pragma unroll
@@ -664,21 +654,21 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           d[4 + s] = x[4 + s] * d1[s];
         }
         VB[kb] = Mode::make(x);
-        DB[kb] = SO::make(d);
+        DB[kb] = Mode::make(d);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int rt = rg * R + i;
         store_half(Mode{}, X + C::XV + (rt >> 1) * 2048, lane, rt & 1, Vp[i]);
-        SO::store_half(X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
+        store_half(Mode{}, X + C::XD + (rt >> 1) * 2048, lane, rt & 1, Vp[i] * delta4(rt));
       }
       exchange();
       load_p();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb <= rg * R + R - 1) VB[kb] = Mode::load_block(X + C::XV + kb * 2048, lane);
-        DB[kb] = SO::load(X + C::XD + kb * 2048, lane);
+        DB[kb] = Mode::load_block(X + C::XD + kb * 2048, lane);
       }
     }
 
@@ -699,8 +689,8 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
           f32x4 acc = Hc[o][hf] * gC;
 #pragma unroll
           for (int kbp = 0; kbp < 2; ++kbp)
-            acc = SO::mma(acc, EARLY ? kt[o][hf][kbp] : F::kt(sK, 2 * kb + hf, kbp, lane),
-                          DB[kbp]);
+            acc = Mode::mma_xs(
+                acc, SO::kt(EARLY ? kt[o][hf][kbp] : F::kt(sK, 2 * kb + hf, kbp, lane)), DB[kbp]);
           Hc[o][hf] = acc;
         }
         if constexpr (RW > 1) {

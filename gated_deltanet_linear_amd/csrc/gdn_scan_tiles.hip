@@ -24,9 +24,9 @@
 // one another, while those of different waves on a SIMD do; the chain wave is the serial path,
 // so it issues only the recurrence itself, and everything else is done by the other waves.
 // Three s_barriers per chunk order the hand-overs (see the schedule below the work assignment).
-// Products run on MFMA in the fragment convention of gdn_device.hpp: the three with the state or
-// V'' (K H, Q H, K^T diag(delta) V') on fp16 operands (Half), T diag(beta) Y and P V' on bf16
-// hi + lo pairs.
+// Products run on MFMA in the fragment convention of gdn_device.hpp: the two with the state
+// (K H, Q H) on fp16 operands (Half); T diag(beta) Y, P V' and the update K^T diag(delta) V' on
+// bf16, computed operands as hi + lo pairs.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -271,8 +271,9 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
               (__attribute__((address_space(3))) s16x4*)(smem + C::KOFF +
                                                          swz_off<C::ROWB, 2>(row, st_row(it, 4 * a))));
 #pragma unroll
-        for (int it = 0; it < NST; ++it)
-          *reinterpret_cast<s16x4*>(kt + ((it * 2 + kbp) * 64 + lane) * 16 + 8 * hf) = t[it];
+        for (int it = 0; it < NST; ++it)  // fp16 back to bf16: exact, the values came from bf16
+          *reinterpret_cast<bf16x4*>(kt + ((it * 2 + kbp) * 64 + lane) * 16 + 8 * hf) =
+              Half::to_bf16(t[it]);
       };
 
       // Chunk 0 staged before the first barrier; the next pieces held in registers.
@@ -419,9 +420,9 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
         Vp[rt] = acc;
         *reinterpret_cast<f32x4*>(VX + 1024 * rt + 16 * lane) = acc;
       }
-      // V'' = diag(delta) V' as fp16 B fragments over tokens; gamma_C (read before X(c), after
+      // V'' = diag(delta) V' as split B fragments over tokens; gamma_C (read before X(c), after
       // which the producers restage gamma and delta)
-      f16x8 DB[2];
+      Op DB[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float x[8], dx[8];
@@ -433,15 +434,15 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
           dx[s4] = x[s4] * d0[s4];
           dx[4 + s4] = x[4 + s4] * d1[s4];
         }
-        DB[kb] = Half::make(dx);
+        DB[kb] = M::make(dx);
       }
       const float gC = sgam[kChunk - 1];
-      f16x8 KT[NST][2];
+      bf16x8 KT[NST][2];
 #pragma unroll
       for (int it = 0; it < NST; ++it)
 #pragma unroll
         for (int kbp = 0; kbp < 2; ++kbp)
-          KT[it][kbp] = *reinterpret_cast<const f16x8*>(sKT + ((it * 2 + kbp) * 64 + lane) * 16);
+          KT[it][kbp] = *reinterpret_cast<const bf16x8*>(sKT + ((it * 2 + kbp) * 64 + lane) * 16);
       lds_barrier();  // X(c)
 
       // H <- gamma_C H + K^T V''
@@ -449,7 +450,7 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
       for (int it = 0; it < NST; ++it) {
         f32x4 acc = Hc[it] * gC;
 #pragma unroll
-        for (int kbp = 0; kbp < 2; ++kbp) acc = Half::mma(KT[it][kbp], DB[kbp], acc);
+        for (int kbp = 0; kbp < 2; ++kbp) acc = M::mma_xs(acc, KT[it][kbp], DB[kbp]);
         Hc[it] = acc;
       }
       split_state();  // the output wave read the previous one before M(c)

@@ -119,12 +119,11 @@ size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
  * q, k, v and o must be 16-byte aligned (16-byte row accesses); GDN_ERR_INVALID_ARGUMENT
  * otherwise. It runs gdn_chunk_intra then gdn_chunk_scan on `stream`.
  * Precision: the state is carried in fp32 and every product accumulates in fp32. With fp32
- * q/k/v every product is fp32. With bf16 q/k/v the products with the state or with
- * diag(delta) V' (K H, Q H and the state update) take fp16 operands: q and k converted (exact for
- * magnitudes in [2^-14, 65504], within 2^-25 below that; L2-normalised vectors are in range),
- * the state and V' rounded to fp16 once per chunk for these products (so their magnitudes must
- * stay below 65504). T diag(beta) Y and P V' take the computed operands as hi + lo bf16 pairs
- * (about 16 significant bits).
+ * q/k/v every product is fp32. With bf16 q/k/v the two products with the state (K H and Q H)
+ * take fp16 operands: q and k converted (exact for magnitudes in [2^-14, 65504], within 2^-25
+ * below that; L2-normalised vectors are in range) and the state rounded to fp16 once per chunk
+ * for these products (so its magnitude must stay below 65504). The state update, T diag(beta) Y
+ * and P V' take the computed operands as hi + lo bf16 pairs (about 16 significant bits).
  */
 gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                                const void* q, const void* k, const void* v, const float* g,
