@@ -14,8 +14,8 @@ import torch
 
 import gated_deltanet_linear_amd as gdn
 import synthetic_inputs as si
-from gdn_testutil import (TOL, assert_rms_close, assert_rms_close_rounded_out, f64,
-                          oracle_case, to_dev)
+from gdn_testutil import (TOL, assert_rms_close, assert_rms_close_rounded_out, oracle_case,
+                          to_dev)
 
 pytestmark = pytest.mark.gpu
 
