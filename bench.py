@@ -78,14 +78,15 @@ def prefill_bytes(lengths, hqk, hv, dk, dv, e, h0_given, state_out=True):
     return b
 
 
-def scan_bytes(lengths, hqk, hv, dk, dv, e, h0_given, state_out=True):
-    """Algorithmic HBM bytes of one scan launch: q and k (each unique byte once), v, the
-    workspace records the intra kernel wrote (25088 bytes per chunk and V head), the initial
-    states, o and the final states."""
+def scan_bytes(lengths, hqk, hv, dk, dv, e, h0_given, state_out=True, eo=None):
+    """Algorithmic HBM bytes of one scan launch: q and k (each unique byte once), v (e bytes an
+    element), the workspace records the intra kernel wrote (25088 bytes per chunk and V head),
+    the initial states, o (eo bytes an element, e unless given) and the final states."""
     T = sum(lengths)
     n = len(lengths)
     chunks = sum((L + C - 1) // C for L in lengths)
-    b = T * (hqk * 2 * dk * e + hv * 2 * dv * e) + chunks * hv * 25088
+    eo = e if eo is None else eo
+    b = T * (hqk * 2 * dk * e + hv * dv * (e + eo)) + chunks * hv * 25088
     b += n * hv * dk * dv * 4 * ((1 if state_out else 0) + (1 if h0_given else 0))
     return b
 
@@ -290,6 +291,7 @@ def run_front(torch, gdn, si, steps, warmup):
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
     peak = PEAK_F32_TFLOPS if qkv_dtype == torch.float32 else PEAK_BF16_TFLOPS
+    Bscan = scan_bytes(m["lengths"], hqk, hv, dk, dv, eq, True, eo=2)
     return dict(T=T, lengths=m["lengths"], ms_per_step=ms, step_ms_events=ev_ms,
                 tokens_per_s=T / (ms / 1e3), qkv_dtype=str(qkv_dtype).replace("torch.", ""),
                 kernels_ms=kms, path_tflops=F / (ms / 1e3) / 1e12,
@@ -298,7 +300,12 @@ def run_front(torch, gdn, si, steps, warmup):
                 roofline=dict(kernel="gdn_chunk_scan", bound="mfma",
                               achieved=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12, 3),
                               peak=peak, unit="TFLOP/s",
-                              frac=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12 / peak, 5)))
+                              frac=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12 / peak, 5),
+                              traffic=_traffic("gdn_chunk_scan_prefill_397b_packed_8xU512_8192"
+                                               + ("_f32qkv" if eq == 4 else "")),
+                              algorithmic_flops_per_launch=Fscan,
+                              algorithmic_bytes_per_launch=Bscan,
+                              hbm_gbs=round(Bscan / (kms["gdn_chunk_scan"] / 1e3) / 1e9, 1)))
 
 
 def _hbm(kernel, nbytes, ms, traffic_key=None):
@@ -394,6 +401,13 @@ def backward_flops_per_token_head(dk, dv):
     return 2 * (8 * d * d + 10 * C * d)
 
 
+def backward_bytes(T, hqk, hv, dk, dv, e):
+    """Algorithmic HBM bytes of one backward call without initial or final states: q, k, v and
+    dout read and dq, dk, dv written once (e bytes an element), g and beta read and dg, dbeta
+    written in fp32."""
+    return T * (2 * (hqk * 2 * dk * e + hv * 2 * dv * e) + 16 * hv)
+
+
 def run_backward(torch, gdn, si, steps, warmup):
     """Backward of the 1 x 4096 prefill (gdn_chunk_backward: dq, dk, dv, dg, dbeta and dh0 from a
     bf16 output gradient), inputs resident in HBM, workspace preallocated."""
@@ -413,6 +427,7 @@ def run_backward(torch, gdn, si, steps, warmup):
 
     ev_ms, ms, kms = _measure(torch, [("gdn_chunk_backward", step)], steps, warmup)
     F = backward_flops_per_token_head(dk, dv) * T * hv
+    Bb = backward_bytes(T, hqk, hv, dk, dv, 2)
     tf = F / (kms["gdn_chunk_backward"] / 1e3) / 1e12
     return dict(ms_per_step=ms, step_ms_events=ev_ms, tokens_per_s=T / (ms / 1e3),
                 kernels_ms=kms, workspace_bytes=nbytes,
@@ -421,6 +436,7 @@ def run_backward(torch, gdn, si, steps, warmup):
                               frac=round(tf / PEAK_BF16_TFLOPS, 5),
                               traffic=_traffic("gdn_chunk_backward_backward_1x4096"),
                               algorithmic_flops_per_launch=F,
+                              algorithmic_bytes_per_launch=Bb,
                               note="bf16 inputs: most products on bf16 MFMA (computed operands "
                                    "as hi + lo pairs), the C x C dP and dA products on fp32 "
                                    "MFMA; priced against the bf16 dense peak"))
