@@ -113,52 +113,53 @@ __device__ __forceinline__ void store_half_global(F32Mode, char* blk, int lane, 
   *reinterpret_cast<f32x4*>(blk + lane * 32 + half * 16) = x;
 }
 
-// One workgroup per (chunk slot, V head). K K^T and Q K^T of the chunk's QK head are formed
-// again for every V head that shares it: ~1 MFLOP per chunk, noise next to the scan, and it
-// makes every workgroup independent.
-template <typename Mode, int DK>
-__global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
+// One workgroup per (chunk slot, group of NV V heads of one QK head): NV = 2 when the heads per
+// QK head come in pairs, else 1. K K^T and Q K^T of the chunk's QK head are formed once and
+// serve the NV heads, whose gates, decay masks, inverses and records are worked on side by side
+// by 4 waves each. T = (I + A)^-1 overwrites A in place, so that NV heads need the LDS of the
+// staged q/k rows, or of one 64x64 fp32 matrix per head, whichever is larger.
+template <typename Mode, int DK, int NV>
+__global__ __launch_bounds__(256 * NV) void chunk_intra_kernel(IntraParams p) {
   using in_t = typename Mode::in_t;
   using frag_t = typename Mode::frag_t;
+  constexpr int NWV = 4 * NV;  // waves
   constexpr int KB = DK / 32;
   constexpr int ROWB = DK * (int)sizeof(in_t), KBYTES = 64 * ROWB;
-  constexpr int TBYTES = 64 * kLd * 4;
-  constexpr int SBYTES = 2 * KBYTES > 2 * TBYTES ? 2 * KBYTES : 2 * TBYTES;
+  constexpr int TBYTES = 64 * kLd * 4;  // one head's A, then T in place
+  constexpr int SBYTES = 2 * KBYTES > NV * TBYTES ? 2 * KBYTES : NV * TBYTES;
 
-  // Staged q/k rows; once the K K^T / Q K^T products are in registers the same bytes hold A
-  // and T (small enough for four workgroups per CU).
+  // Staged q/k rows; once the K K^T / Q K^T products are in registers the same bytes hold the
+  // heads' A (then T) matrices.
   __shared__ __attribute__((aligned(1024))) char sKQ[SBYTES];
-  __shared__ __attribute__((aligned(16))) float sb[64];
-  __shared__ __attribute__((aligned(16))) float sbeta[64];
-  float* sA = reinterpret_cast<float*>(sKQ);
-  float* sT = reinterpret_cast<float*>(sKQ + TBYTES);
+  __shared__ __attribute__((aligned(16))) float sb[NV][64];
+  __shared__ __attribute__((aligned(16))) float sbeta[NV][64];
+  auto sA = [&](int v) { return reinterpret_cast<float*>(sKQ + v * TBYTES); };
 
   // Work assignment: units (chunk slot, QK head) are dealt to the 8 XCDs round robin (the
-  // hardware deals workgroups b to XCD b % 8); the G workgroups of a unit (its V heads, which
-  // read the same q/k rows) are dispatched back to back on one XCD and share its L2.
-  const int G = p.hv / p.hqk;
-  const int j = blockIdx.x >> 3, unit = 8 * (j / G) + (blockIdx.x & 7);
-  const int slot = unit / p.hqk, h = (unit % p.hqk) * G + j % G;
+  // hardware deals workgroups b to XCD b % 8); the G / NV workgroups of a unit (its V-head
+  // groups, which read the same q/k rows) are dispatched back to back on one XCD and share its L2.
+  const int G = p.hv / p.hqk, NG = G / NV;
+  const int j = blockIdx.x >> 3, unit = 8 * (j / NG) + (blockIdx.x & 7);
+  const int slot = unit / p.hqk, m = unit % p.hqk, hb = m * G + (j % NG) * NV;
   if (slot >= p.num_slots) return;  // padding workgroup (uniform)
   const int n = slot_to_seq(p.cu, p.num_seqs, slot);
   const int t0 = p.cu[n] + kChunk * (slot - slot_base(p.cu, n));
   const int tend = p.cu[n + 1];
   if (t0 >= tend) return;  // unused slot (uniform over the workgroup)
   const int len = min(kChunk, tend - t0);
-  const int m = h / (p.hv / p.hqk);
 
   const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const size_t rstride = (size_t)p.hqk * DK;
-  char* rec = p.ws + ((size_t)slot * p.hv + h) * kWsRecordBytes;
-  float gate_g, gate_b;  // g and beta of token `lane` (wave 0)
+  auto rec = [&](int v) { return p.ws + ((size_t)slot * p.hv + hb + v) * kWsRecordBytes; };
+  float gate_g = 0.f, gate_b = 0.f;  // g and beta of token `lane` of head hb + wave (wave < NV)
 
   // ---- all memory reads at once: q/k rows into registers (16-byte loads, 1 KiB per wave
-  // instruction) and this head's gates; then the rows go to LDS, row-major with the 16-byte
-  // XOR swizzle. Rows past len are written as zeros (identity steps).
+  // instruction) and the gates; then the rows go to LDS, row-major with the 16-byte XOR
+  // swizzle. Rows past len are written as zeros (identity steps).
   {
-    constexpr int NCH = ROWB / 16, RPU = 64 / NCH, KI = KBYTES / 1024, PER = 2 * KI / 4;
-    static_assert(2 * KI % 4 == 0, "units per wave");
+    constexpr int NCH = ROWB / 16, RPU = 64 / NCH, KI = KBYTES / 1024;
+    constexpr int PER = (2 * KI + NWV - 1) / NWV;  // units per wave (the last ones may idle)
     const in_t* Kg = static_cast<const in_t*>(p.k);
     const in_t* Qg = static_cast<const in_t*>(p.q);
     const char* Kb = reinterpret_cast<const char*>(Kg + (size_t)t0 * rstride + (size_t)m * DK);
@@ -167,190 +168,205 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(IntraParams p) {
     f32x4 r[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int j = wave + 4 * u, jj = j < KI ? j : j - KI;
+      const int j2 = wave + NWV * u, jj = j2 < KI ? j2 : j2 - KI;
       const int row = jj * RPU + lane / NCH;
       const unsigned off = min(row, len - 1) * rs + 16 * ((lane % NCH) ^ swz<ROWB>(row));
-      r[u] = *reinterpret_cast<const f32x4*>((j < KI ? Kb : Qb) + off);
+      if (j2 < 2 * KI) r[u] = *reinterpret_cast<const f32x4*>((j2 < KI ? Kb : Qb) + off);
     }
-    float gv = 0.f, bv = 0.f;
-    if (wave == 0 && lane < len) {
-      gv = p.g[(size_t)(t0 + lane) * p.hv + h];
-      bv = p.beta[(size_t)(t0 + lane) * p.hv + h];
+    if (wave < NV && lane < len) {
+      gate_g = p.g[(size_t)(t0 + lane) * p.hv + hb + wave];
+      gate_b = p.beta[(size_t)(t0 + lane) * p.hv + hb + wave];
     }
-    gate_g = gv;
-    gate_b = bv;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int j = wave + 4 * u, jj = j < KI ? j : j - KI;
+      const int j2 = wave + NWV * u, jj = j2 < KI ? j2 : j2 - KI;
       const int row = jj * RPU + lane / NCH;
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(sKQ + 1024 * j + 16 * lane) = row < len ? r[u] : z;
+      if (j2 < 2 * KI)
+        *reinterpret_cast<f32x4*>(sKQ + 1024 * j2 + 16 * lane) = row < len ? r[u] : z;
     }
   }
   lds_barrier();
 
-  // ---- 22 tile jobs, round robin over the waves (wave w: jobs w, w+4, ..., w+16 on MFMA,
-  // and job w+20 for waves 0, 1). Both kinds are formed transposed (C = K_ct X_rt^T), so that a
-  // lane holds 4 consecutive columns of one row of the wanted tile:
+  // ---- 20 tile products: the A tiles on the first half of the waves, the P tiles on the
+  // second half (wave w of a half: its jobs w, w + NWV / 2, ...). Both kinds are formed
+  // transposed (C = K_ct X_rt^T), so that a lane holds 4 consecutive columns of one row of the
+  // wanted tile:
   //   0..9   A tiles (tr >= tc): A_tj = beta_t e^{b_t - b_j} (k_t . k_j) for j < t, into LDS;
   //   10..19 P^T tiles: C = K_ct Q_rt^T, whose C fragment IS half of the stored A fragment of
-  //          P = (Q K^T) o Gamma o lower-incl (block (rt, ct / 2), slots 4 (ct % 2) + r);
-  //   20, 21 the zero halves of the diagonal P blocks (ct = rt + 1 for rt = 0, 2).
-  // The products run first; wave 0 forms the gate cumsum meanwhile; the epilogues that need it
-  // follow one barrier later.
+  //          P = (Q K^T) o Gamma o lower-incl (block (rt, ct / 2), slots 4 (ct % 2) + r).
+  // The zero halves of the diagonal P blocks (ct = rt + 1 for rt = 0, 2) are stored directly.
+  // The products run first; waves 0 .. NV - 1 form their head's gate cumsum meanwhile. After
+  // one barrier the first half writes the A tiles of all NV heads to LDS while the second half
+  // writes the P blocks to the workspace.
+  constexpr int HW = NWV / 2;                 // waves per half
+  constexpr int NJ = (10 + HW - 1) / HW;      // jobs per wave
+  const bool pw = wave >= HW;                 // P-tile wave
+  const int wj = pw ? wave - HW : wave;       // index inside the half
   const char* sK = sKQ;
   const char* sQ = sKQ + KBYTES;
-  auto job_tiles = [](int job, int& r1, int& r2) {
-    const int tt = job >= 10 ? job - 10 : job;
+  auto job_tiles = [](int tt, int& r1, int& r2) {
     r1 = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // row tile
     r2 = tt - r1 * (r1 + 1) / 2;                        // column tile (<= r1)
   };
-  f32x4 acc[5];
+  f32x4 acc[NJ];
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int job = wave + 4 * i;
-    const bool isp = job >= 10;
-    int r1, r2;
-    job_tiles(job, r1, r2);
-    // Rows r2 of K against rows r1 of K (A^T tiles) or of Q (P^T tiles).
-    const int ra = 16 * r2 + idx;
-    const int rb = 16 * r1 + idx;
-    const char* bsrc = isp ? sQ : sK;
-    frag_t fa[KB], fb[KB];
+  for (int i = 0; i < NJ; ++i) {
+    const int tt = wj + HW * i;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tt < 10) {
+      int r1, r2;
+      job_tiles(tt, r1, r2);
+      // Rows r2 of K against rows r1 of K (A^T tiles) or of Q (P^T tiles).
+      const int ra = 16 * r2 + idx;
+      const int rb = 16 * r1 + idx;
+      const char* bsrc = pw ? sQ : sK;
+      frag_t fa[KB], fb[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      fa[kb] = row_frag<Mode, ROWB>(sK, ra, kb, grp);
-      fb[kb] = row_frag<Mode, ROWB>(bsrc, rb, kb, grp);
+      for (int kb = 0; kb < KB; ++kb) {
+        fa[kb] = row_frag<Mode, ROWB>(sK, ra, kb, grp);
+        fb[kb] = row_frag<Mode, ROWB>(bsrc, rb, kb, grp);
+      }
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) c = mma32(fa[kb], fb[kb], c);
+      acc[i] = c;
     }
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) c = mma32(fa[kb], fb[kb], c);
-    acc[i] = c;
   }
-  if (wave == 0) {
+  if (wave < NV) {
     const float cs = wave_inclusive_scan(gate_g, lane);
     const float cl = __shfl(cs, kChunk - 1, kWave);  // b_C (identity steps keep it at b_{len-1})
-    sb[lane] = cs;
-    sbeta[lane] = gate_b;
-    reinterpret_cast<float*>(rec + kWsGOff)[lane] = __expf(cs);
-    reinterpret_cast<float*>(rec + kWsDOff)[lane] = __expf(cl - cs);
-  }
-  if (wave < 2) {
-    const int rt = wave == 0 ? 0 : 2;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    store_half_global(Mode{}, rec + kWsPOff + tri_block(rt, rt / 2) * kWsBlockBytes, lane, 1, z);
+    sb[wave][lane] = cs;
+    sbeta[wave][lane] = gate_b;
+    reinterpret_cast<float*>(rec(wave) + kWsGOff)[lane] = __expf(cs);
+    reinterpret_cast<float*>(rec(wave) + kWsDOff)[lane] = __expf(cl - cs);
   }
   lds_barrier();  // sb, sbeta ready; every wave is done with the staged rows (sA may overwrite)
+  if (pw && wj < 2 * NV) {
+    const int v = wj >> 1, rt = (wj & 1) ? 2 : 0;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    store_half_global(Mode{}, rec(v) + kWsPOff + tri_block(rt, rt / 2) * kWsBlockBytes, lane, 1, z);
+  }
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int job = wave + 4 * i;
+  for (int i = 0; i < NJ; ++i) {
+    const int tt = wj + HW * i;
+    if (tt >= 10) continue;
     int r1, r2;
-    job_tiles(job, r1, r2);
-    if (job < 10) {
-      // lane: row t = 16 r1 + idx, columns j = 16 r2 + 4 grp + r (one 16-byte write)
-      const int t = 16 * r1 + idx;
-      const float bt = sb[t], bet = sbeta[t];
-      const f32x4 bj = *reinterpret_cast<const f32x4*>(sb + 16 * r2 + 4 * grp);
-      f32x4 av;
+    job_tiles(tt, r1, r2);
+    // lane: row t = 16 r1 + idx, columns j = 16 r2 + 4 grp + r (one 16-byte access)
+    const int t = 16 * r1 + idx;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * r2 + 4 * grp + r;
-        av[r] = j < t ? bet * __expf(bt - bj[r]) * acc[i][r] : 0.f;
-      }
-      *reinterpret_cast<f32x4*>(sA + t * kLd + 16 * r2 + 4 * grp) = av;
-    } else {
-      const int t = 16 * r1 + idx;
-      const float bt = sb[t];
-      const f32x4 bj = *reinterpret_cast<const f32x4*>(sb + 16 * r2 + 4 * grp);
-      f32x4 pv;
+    for (int v = 0; v < NV; ++v) {
+      const float bt = sb[v][t];
+      const f32x4 bj = *reinterpret_cast<const f32x4*>(&sb[v][16 * r2 + 4 * grp]);
+      if (!pw) {
+        const float bet = sbeta[v][t];
+        f32x4 av;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * r2 + 4 * grp + r;
-        pv[r] = j <= t ? __expf(bt - bj[r]) * acc[i][r] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int jc = 16 * r2 + 4 * grp + r;
+          av[r] = jc < t ? bet * __expf(bt - bj[r]) * acc[i][r] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(sA(v) + t * kLd + 16 * r2 + 4 * grp) = av;
+      } else {
+        f32x4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jc = 16 * r2 + 4 * grp + r;
+          pv[r] = jc <= t ? __expf(bt - bj[r]) * acc[i][r] : 0.f;
+        }
+        store_half_global(Mode{}, rec(v) + kWsPOff + tri_block(r1, r2 >> 1) * kWsBlockBytes,
+                          lane, r2 & 1, pv);
       }
-      store_half_global(Mode{}, rec + kWsPOff + tri_block(r1, r2 >> 1) * kWsBlockBytes, lane,
-                        r2 & 1, pv);
     }
   }
-  lds_barrier();  // sA complete
+  lds_barrier();  // A complete
 
-  // ---- Diagonal 16x16 blocks of T: wave w inverts block w by forward substitution,
-  // x_i = delta_ic - sum_{j<i} A_ij x_j with lane c < 16 carrying column c. Lane i holds row i
-  // of the block; v_readlane broadcasts A_ij as a scalar operand (no LDS traffic in the loop).
-  {
-    const float* Ab = sA + (16 * wave) * kLd + 16 * wave;
-    float arow[16];
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const f32x4 a4 = row4(Ab + (lane & 15) * kLd + 4 * j4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) arow[4 * j4 + e] = a4[e];
-    }
+  // ---- Diagonal 16x16 blocks of T, in place of A's: wave v < NV inverts the four blocks of
+  // head v at once by forward substitution, lane (blk, c) = (lane / 16, lane % 16) solving for
+  // column c of block blk: x_i = delta_ic - sum_{j<i} A_ij x_j. Row i of a block is read as
+  // 16-byte pieces that the block's 16 lanes share (one address per lane group).
+  if (wave < NV) {
+    const int blk = lane >> 4, c = lane & 15;
+    float* Ab = sA(wave) + (16 * blk) * kLd + 16 * blk;
     float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+    x[0] = c == 0 ? 1.f : 0.f;
 #pragma unroll
     for (int i = 1; i < 16; ++i) {
+      float a[16];
+#pragma unroll
+      for (int q = 0; q < (i + 3) / 4; ++q) {
+        const f32x4 a4 = row4(Ab + i * kLd + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * q + e] = a4[e];
+      }
       float part[4] = {0.f, 0.f, 0.f, 0.f};  // 4 independent chains
 #pragma unroll
-      for (int j = 0; j < i; ++j)
-        part[j & 3] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                               __builtin_bit_cast(int, arow[j]), i)),
-                           x[j], part[j & 3]);
-      x[i] = (i == lane) ? 1.f : -((part[0] + part[1]) + (part[2] + part[3]));
+      for (int jj = 0; jj < i; ++jj) part[jj & 3] = fmaf(a[jj], x[jj], part[jj & 3]);
+      x[i] = (i == c) ? 1.f : -((part[0] + part[1]) + (part[2] + part[3]));
     }
-    if (lane < 16) {
-      float* Tb = sT + (16 * wave) * kLd + 16 * wave;
+    // row i is written after its own read (x_i depends on it); other rows are disjoint
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Tb[i * kLd + lane] = x[i];
-    }
+    for (int i = 0; i < 16; ++i) Ab[i * kLd + c] = x[i];
   }
   lds_barrier();
-  // ---- Level 2: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22.
-  if (wave < 2) {
-    const int ib = 2 * wave + 1, jb = 2 * wave;
+  // Waves 2 v and 2 v + 1 finish head v's inverse; wl is the wave's index in that pair.
+  const int hv_ = wave >> 1, wl = wave & 1;
+  const bool lw = wave < 2 * NV;
+  float* const Mx = sA(lw ? hv_ : 0);
+  // ---- Level 2: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22 (over A_10, A_32: each wave
+  // reads its block into M before writing it).
+  if (lw) {
+    const int ib = 2 * wl + 1, jb = 2 * wl;
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 M = mm16_ll(sA + 16 * ib * kLd + 16 * jb, sT + 16 * jb * kLd + 16 * jb, z, idx, grp);
-    f32x4 R = mm16_lr(sT + 16 * ib * kLd + 16 * ib, M, z, idx, grp);
-    store_c16(sT + 16 * ib * kLd + 16 * jb, R, idx, grp, -1.f);
+    f32x4 M = mm16_ll(Mx + 16 * ib * kLd + 16 * jb, Mx + 16 * jb * kLd + 16 * jb, z, idx, grp);
+    f32x4 R = mm16_lr(Mx + 16 * ib * kLd + 16 * ib, M, z, idx, grp);
+    store_c16(Mx + 16 * ib * kLd + 16 * jb, R, idx, grp, -1.f);
   }
   lds_barrier();
-  // ---- Level 3, column block jb in {0, 1} (wave jb):
+  // ---- Level 3, column block jb in {0, 1} (wave jb of the pair):
   //   X_i = sum_{kb=jb..1} A_{i,kb} T_{kb,jb} (i = 2, 3)
   //   T_{2,jb} = -T_22 X_2,  T_{3,jb} = -(T_32 X_2 + T_33 X_3)
-  if (wave < 2) {
-    const int jb = wave;
+  // Wave 0 of the pair reads A_21 and A_31, which wave 1 overwrites: the stores wait for a
+  // barrier.
+  f32x4 T2 = {0.f, 0.f, 0.f, 0.f}, T3 = {0.f, 0.f, 0.f, 0.f};
+  if (lw) {
+    const int jb = wl;
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     f32x4 X2 = z, X3 = z;
     for (int kb = jb; kb < 2; ++kb) {
-      const float* Tk = sT + 16 * kb * kLd + 16 * jb;
-      X2 = mm16_ll(sA + 32 * kLd + 16 * kb, Tk, X2, idx, grp);
-      X3 = mm16_ll(sA + 48 * kLd + 16 * kb, Tk, X3, idx, grp);
+      const float* Tk = Mx + 16 * kb * kLd + 16 * jb;
+      X2 = mm16_ll(Mx + 32 * kLd + 16 * kb, Tk, X2, idx, grp);
+      X3 = mm16_ll(Mx + 48 * kLd + 16 * kb, Tk, X3, idx, grp);
     }
-    f32x4 T2 = mm16_lr(sT + 32 * kLd + 32, X2, z, idx, grp);
-    f32x4 T3 = mm16_lr(sT + 48 * kLd + 32, X2, z, idx, grp);
-    T3 = mm16_lr(sT + 48 * kLd + 48, X3, T3, idx, grp);
-    store_c16(sT + 32 * kLd + 16 * jb, T2, idx, grp, -1.f);
-    store_c16(sT + 48 * kLd + 16 * jb, T3, idx, grp, -1.f);
+    T2 = mm16_lr(Mx + 32 * kLd + 32, X2, z, idx, grp);
+    T3 = mm16_lr(Mx + 48 * kLd + 32, X2, z, idx, grp);
+    T3 = mm16_lr(Mx + 48 * kLd + 48, X3, T3, idx, grp);
   }
   lds_barrier();
-  // ---- T diag(beta) as stored A fragments: 6 blocks x 64 lanes.
-  for (int it = tid; it < 6 * 64; it += 256) {
-    const int bi = it >> 6, ln = it & 63;
+  if (lw) {
+    store_c16(Mx + 32 * kLd + 16 * wl, T2, idx, grp, -1.f);
+    store_c16(Mx + 48 * kLd + 16 * wl, T3, idx, grp, -1.f);
+  }
+  lds_barrier();
+  // ---- T diag(beta) of every head as stored A fragments: NV x 6 blocks x 64 lanes.
+  for (int it = tid; it < NV * 6 * 64; it += 256 * NV) {
+    const int v = it / 384, bi = (it >> 6) % 6, ln = it & 63;
     const int rt = bi < 2 ? bi : 2 + (bi - 2) / 2;
     const int kb = bi < 2 ? 0 : (bi - 2) % 2;
     const int i = ln & 15, gr = ln >> 4;
     const int t = 16 * rt + i;
-    const f32x4 be0 = row4(sbeta + 32 * kb + 4 * gr), be1 = row4(sbeta + 32 * kb + 16 + 4 * gr);
-    const f32x4 t0 = row4(sT + t * kLd + 32 * kb + 4 * gr);
-    const f32x4 t1 = row4(sT + t * kLd + 32 * kb + 16 + 4 * gr);
+    const float* Tv = sA(v);
+    const f32x4 be0 = row4(&sbeta[v][32 * kb + 4 * gr]), be1 = row4(&sbeta[v][32 * kb + 16 + 4 * gr]);
+    const f32x4 ta = row4(Tv + t * kLd + 32 * kb + 4 * gr);
+    const f32x4 tb = row4(Tv + t * kLd + 32 * kb + 16 + 4 * gr);
     float x[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int j = 32 * kb + kslot(gr, s);
-      x[s] = j <= t ? (s < 4 ? t0[s] * be0[s] : t1[s - 4] * be1[s - 4]) : 0.f;
+      const int jc = 32 * kb + kslot(gr, s);
+      x[s] = jc <= t ? (s < 4 ? ta[s] * be0[s] : tb[s - 4] * be1[s - 4]) : 0.f;
     }
-    Mode::store_block(rec + kWsTOff + bi * kWsBlockBytes, ln, Mode::make(x));
+    Mode::store_block(rec(v) + kWsTOff + bi * kWsBlockBytes, ln, Mode::make(x));
   }
 }
 
@@ -364,8 +380,12 @@ hipError_t launch_intra_t(const gdn_shape_t& s, const IntraParams& p, hipStream_
   const long long units = slots * s.num_qk_heads, G = s.num_v_heads / s.num_qk_heads;
   IntraParams q = p;
   q.num_slots = (int)slots;
-  hipLaunchKernelGGL((chunk_intra_kernel<Mode, D>), dim3((unsigned)(8 * G * ((units + 7) / 8))),
-                     dim3(256), 0, stream, q);
+  // one workgroup per (unit, pair of V heads) when G is even, else per (unit, V head)
+  const unsigned blocks = (unsigned)(8 * ((G % 2 == 0) ? G / 2 : G) * ((units + 7) / 8));
+  if (G % 2 == 0)
+    hipLaunchKernelGGL((chunk_intra_kernel<Mode, D, 2>), dim3(blocks), dim3(512), 0, stream, q);
+  else
+    hipLaunchKernelGGL((chunk_intra_kernel<Mode, D, 1>), dim3(blocks), dim3(256), 0, stream, q);
   return hipGetLastError();
 }
 
