@@ -192,124 +192,141 @@ __device__ __forceinline__ bool slot_chunk(const BwdParams& p, int slot, int& n,
 }
 
 // ---- bwd_intra ------------------------------------------------------------------------------
+// One workgroup of 4 waves per (chunk slot, V head); the G workgroups of a (chunk slot, QK head)
+// run back to back on one XCD (their q/k rows come from its L2). The chunk's q/k rows are staged
+// in LDS (rows past the end as zeros); the 20 lower 16x16 tiles of K K^T and Q K^T are formed
+// transposed (C = K_ct X_rt^T, so a lane holds 4 consecutive columns of one row and writes
+// them with one 16-byte store); then T = (I + diag(beta) At)^-1 in place of the staged rows.
 template <typename InT, int D>
 __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
-  __shared__ float sA[kC][kC + 1];
-  __shared__ float sT[kC][kC + 1];
+  constexpr int ROWB = D * (int)sizeof(InT), KBYTES = 64 * ROWB, KB = D / 32;
+  constexpr int MBYTES = 64 * kLd * 4;
+  constexpr int SBYTES = 2 * KBYTES > MBYTES ? 2 * KBYTES : MBYTES;
+  __shared__ __attribute__((aligned(1024))) char sKQ[SBYTES];  // q/k rows, then A / T
   __shared__ double sb[kC];
   __shared__ float sbeta[kC];
+  float* const sM = reinterpret_cast<float*>(sKQ);
 
-  const int slot = blockIdx.x / p.hv, h = blockIdx.x % p.hv;
-  const int G = p.hv / p.hqk, m = h / G;
+  const int G = p.hv / p.hqk;
+  const int j = blockIdx.x >> 3, unit = 8 * (j / G) + (blockIdx.x & 7);
+  const int slot = unit / p.hqk, m = unit % p.hqk, h = m * G + j % G;
   int n, t0, L;
   if (slot >= p.num_slots || !slot_chunk(p, slot, n, t0, L)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int idx = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   float* rec = p.rec + ((size_t)slot * p.hv + h) * kRecFloats;
 
-  const InT* Q = static_cast<const InT*>(p.q);
-  const InT* K = static_cast<const InT*>(p.k);
-  if (wave == 0) {  // b = inclusive cumsum of g (0 past the end: identity steps)
-    const double gi = lane < L ? (double)p.g[(size_t)(t0 + lane) * p.hv + h] : 0.0;
-    const double bi = wave_inclusive_scan_f64(gi, lane);
-    sb[lane] = bi;
-    reinterpret_cast<double*>(rec + 3 * kC * kC)[lane] = bi;
-    sbeta[lane] = lane < L ? p.beta[(size_t)(t0 + lane) * p.hv + h] : 0.f;
-  }
-  __syncthreads();
-
-  // wave w: rows 16 w .. 16 w + 15 of S = K K^T and Q K^T, the q / k rows read from global
-  // memory as 16-byte fragments (rows past the chunk end: zeros as A rows; as B rows they read
-  // row 0 and land only in masked entries, j > t).
-  auto krow = [&](int i) { return K + ((size_t)(t0 + (i < L ? i : 0)) * p.hqk + m) * D; };
-  const int ra = 16 * wave + idx;
-  const InT* a_k = ra < L ? K + ((size_t)(t0 + ra) * p.hqk + m) * D : nullptr;
-  const InT* a_q = ra < L ? Q + ((size_t)(t0 + ra) * p.hqk + m) * D : nullptr;
-  for (int ct = 0; ct < 4; ++ct) {
-    f32x4 s, qk;
-    if constexpr (std::is_same<InT, bf16>::value) {  // exact operands on bf16 MFMA
-      const bf16* a0 = krow(ra);
-      const bf16* q0 = Q + ((size_t)(t0 + (ra < L ? ra : 0)) * p.hqk + m) * D;
-      s = tile_mma_rows_bf16(a0, ra < L, krow(16 * ct + idx), D, zero4());
-      qk = tile_mma_rows_bf16(q0, ra < L, krow(16 * ct + idx), D, zero4());
-    } else {
-      s = tile_mma_rows(a_k, 1.f, krow(16 * ct + idx), D, zero4());
-      qk = tile_mma_rows(a_q, 1.f, krow(16 * ct + idx), D, zero4());
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * grp + r, j = 16 * ct + idx;
-      const float gam = t >= j ? expf((float)(sb[t] - sb[j])) : 0.f;
-      const float pv = t >= j ? qk[r] * gam : 0.f;
-      const float at = t > j ? s[r] * gam : 0.f;
-      rec[kC * kC + t * kC + j] = pv;
-      rec[2 * kC * kC + t * kC + j] = at;
-      sA[t][j] = sbeta[t] * at;  // A = diag(beta) At
-    }
-  }
-  __syncthreads();
-
-  // T = (I + A)^-1, A strictly lower, by 16 x 16 blocks. Diagonal blocks: wave w inverts block
-  // w by forward substitution in registers, x_i = delta_ic - sum_{j<i} A_ij x_j with lane c < 16
-  // carrying column c; lane i holds row i of the block and readlane broadcasts A_ij. Off-diagonal
-  // blocks, one block row after the other: T_ij = -T_ii sum_{j<=k<i} A_ik T_kj, the i products of
-  // a block row on i waves.
+  // ---- q/k rows into registers (16-byte loads; rows past L re-read the last row), then to LDS
+  // row-major with the 16-byte XOR swizzle (rows past L as zeros: identity steps)
   {
-    const int b0 = 16 * wave;
-    for (int e = tid; e < kC * kC; e += 256) sT[e / kC][e % kC] = 0.f;
-    float arow[16];
+    constexpr int NCH = ROWB / 16, RPU = 64 / NCH, KI = KBYTES / 1024, PER = 2 * KI / 4;
+    static_assert(2 * KI % 4 == 0, "units per wave");
+    const size_t rstride = (size_t)p.hqk * D;
+    const char* Kb = reinterpret_cast<const char*>(static_cast<const InT*>(p.k) +
+                                                   (size_t)t0 * rstride + (size_t)m * D);
+    const char* Qb = reinterpret_cast<const char*>(static_cast<const InT*>(p.q) +
+                                                   (size_t)t0 * rstride + (size_t)m * D);
+    const unsigned rs = (unsigned)(rstride * sizeof(InT));
+    f32x4 r[PER];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) arow[j] = sA[b0 + (lane & 15)][b0 + j];
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = i == lane ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float part[4] = {0.f, 0.f, 0.f, 0.f};  // independent chains
-#pragma unroll
-      for (int j = 0; j < i; ++j)
-        part[j & 3] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                               __builtin_bit_cast(int, arow[j]), i)),
-                           x[j], part[j & 3]);
-      x[i] = i == lane ? 1.f : -((part[0] + part[1]) + (part[2] + part[3]));
+    for (int u = 0; u < PER; ++u) {
+      const int j2 = wave + 4 * u, jj = j2 < KI ? j2 : j2 - KI;
+      const int row = jj * RPU + lane / NCH;
+      const unsigned off = min(row, L - 1) * rs + 16 * ((lane % NCH) ^ swz<ROWB>(row));
+      r[u] = *reinterpret_cast<const f32x4*>((j2 < KI ? Kb : Qb) + off);
     }
-    __syncthreads();  // sT zeroed
-    if (lane < 16) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sT[b0 + i][b0 + lane] = x[i];
+    if (wave == 0) {  // b = inclusive cumsum of g (0 past the end: identity steps)
+      const double gi = lane < L ? (double)p.g[(size_t)(t0 + lane) * p.hv + h] : 0.0;
+      const double bi = wave_inclusive_scan_f64(gi, lane);
+      sb[lane] = bi;
+      reinterpret_cast<double*>(rec + 3 * kC * kC)[lane] = bi;
+      sbeta[lane] = lane < L ? p.beta[(size_t)(t0 + lane) * p.hv + h] : 0.f;
     }
-    __syncthreads();
-    for (int bi = 1; bi < 4; ++bi) {
-      const int bj = wave;  // block column of this wave
-      f32x4 w = zero4();
-      if (bj < bi) {  // W = sum_{bj <= k < bi} A_(bi,k) T_(k,bj): depth 16 (bi - bj), padded to 32s
-        const int depth = 16 * (bi - bj);
-        w = tile_mma(
-            [&](int r, int kk) { return kk < depth ? sA[16 * bi + r][16 * bj + kk] : 0.f; },
-            [&](int kk, int cc) { return kk < depth ? sT[16 * bj + kk][16 * bj + cc] : 0.f; },
-            (depth + 31) / 32 * 32, zero4());
-      }
-      // stage W in the (still zero) target block, then T_ij = -T_ii W in place of it
-      if (bj < bi) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sT[16 * bi + 4 * grp + r][16 * bj + idx] = w[r];
-      }
-      __syncthreads();
-      f32x4 t = zero4();
-      if (bj < bi) {
-        t = tile_mma([&](int r, int kk) { return kk < 16 ? sT[16 * bi + r][16 * bi + kk] : 0.f; },
-                     [&](int kk, int cc) { return kk < 16 ? sT[16 * bi + kk][16 * bj + cc] : 0.f; },
-                     32, zero4());
-      }
-      __syncthreads();
-      if (bj < bi) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sT[16 * bi + 4 * grp + r][16 * bj + idx] = -t[r];
-      }
-      __syncthreads();
+    for (int u = 0; u < PER; ++u) {
+      const int j2 = wave + 4 * u, jj = j2 < KI ? j2 : j2 - KI;
+      const int row = jj * RPU + lane / NCH;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(sKQ + 1024 * j2 + 16 * lane) = row < L ? r[u] : z;
     }
   }
-  for (int e = tid; e < kC * kC; e += 256) rec[e] = sT[e / kC][e % kC];
+  lds_barrier();
+
+  // ---- 20 tile products, round robin over the waves (wave w: jobs w, w + 4, ...):
+  //   0..9   S tiles (rt >= ct) of K K^T,  10..19 the same tiles of Q K^T,
+  // each as C = K_ct X_rt^T: lane (idx, grp) gets row t = 16 rt + idx, columns 16 ct + 4 grp + r.
+  // Depth order of both operands: column-contiguous over d_k (one 16-byte piece per fragment).
+  const char* sK = sKQ;
+  const char* sQ = sKQ + KBYTES;
+  auto job_tiles = [](int tt, int& r1, int& r2) {
+    r1 = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // row tile
+    r2 = tt - r1 * (r1 + 1) / 2;                        // column tile (<= r1)
+  };
+  f32x4 acc[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int job = wave + 4 * i, tt = job >= 10 ? job - 10 : job;
+    int r1, r2;
+    job_tiles(tt, r1, r2);
+    const char* bsrc = job >= 10 ? sQ : sK;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (std::is_same<InT, bf16>::value) {
+        c = mma32(afrag<ROWB>(sK, 16 * r2 + idx, kb, grp), afrag<ROWB>(bsrc, 16 * r1 + idx, kb, grp), c);
+      } else {
+        c = mma32(afrag_f32<ROWB>(sK, 16 * r2 + idx, kb, grp),
+                  afrag_f32<ROWB>(bsrc, 16 * r1 + idx, kb, grp), c);
+      }
+    }
+    acc[i] = c;
+  }
+  lds_barrier();  // the staged rows are read: the matrix may overwrite them
+
+  // ---- records At = lower(S o Gamma), P = lower-incl(Q K^T o Gamma) (row-major, 16-byte
+  // stores; the 6 tiles above the diagonal of each as zeros) and A = diag(beta) At into LDS
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int job = wave + 4 * i, tt = job >= 10 ? job - 10 : job;
+    int r1, r2;
+    job_tiles(tt, r1, r2);
+    const int t = 16 * r1 + idx, j0 = 16 * r2 + 4 * grp;
+    f32x4 gm;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gm[r] = j0 + r <= t ? expf((float)(sb[t] - sb[j0 + r])) : 0.f;
+    if (job < 10) {
+      f32x4 at;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) at[r] = j0 + r < t ? acc[i][r] * gm[r] : 0.f;
+      *reinterpret_cast<f32x4*>(rec + 2 * kC * kC + t * kC + j0) = at;
+      *reinterpret_cast<f32x4*>(sM + t * kLd + j0) = at * sbeta[t];
+    } else {
+      *reinterpret_cast<f32x4*>(rec + kC * kC + t * kC + j0) = acc[i] * gm;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {  // tiles above the diagonal: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+    const int zt = wave + 4 * i;   // 0..11: 6 tiles of At, then 6 of P
+    const int u = zt % 6, r1 = u < 3 ? 0 : u < 5 ? 1 : 2, r2 = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(rec + (zt < 6 ? 2 : 1) * kC * kC + (16 * r1 + idx) * kC + 16 * r2 +
+                              4 * grp) = z;
+  }
+  lds_barrier();  // A complete
+
+  // ---- T = (I + A)^-1 in place: diagonal blocks on wave 0, the others on waves 0 and 1
+  invert_unit_lower64(wave == 0 ? sM : nullptr, wave < 2 ? sM : nullptr, wave & 1, lane);
+
+  // ---- T to the record, row-major, zeros above the diagonal
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, t = e >> 4, j0 = 4 * (e & 15);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(sM + t * kLd + j0);
+    f32x4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = j0 + r <= t ? v[r] : 0.f;
+    *reinterpret_cast<f32x4*>(rec + t * kC + j0) = o;
+  }
 }
 
 // ---- bwd_scan: states forward, state gradients in reverse ---------------------------------
@@ -1181,11 +1198,14 @@ inline BwdLayout bwd_layout(const gdn_shape_t& s) {
 
 template <typename InT, typename OT, int D>
 hipError_t launch_bwd_t(const gdn_shape_t& s, BwdParams p, hipStream_t stream) {
-  const unsigned slot_blocks_v = (unsigned)(p.num_slots * p.hv);
+  // (chunk slot, QK head) units dealt to the 8 XCDs round robin, the G V heads of a unit back to
+  // back on one XCD
+  const unsigned intra_blocks =
+      (unsigned)(8 * (p.hv / p.hqk) * (((long long)p.num_slots * p.hqk + 7) / 8));
   const unsigned slot_blocks_qk = (unsigned)(p.num_slots * p.hqk);
   const unsigned scan_blocks = (unsigned)(8 * (D / 16) * ((s.num_seqs * s.num_v_heads + 7) / 8));
   if (s.total_tokens > 0) {
-    hipLaunchKernelGGL((bwd_intra_kernel<InT, D>), dim3(slot_blocks_v), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_intra_kernel<InT, D>), dim3(intra_blocks), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

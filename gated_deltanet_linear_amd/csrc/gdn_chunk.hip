@@ -25,39 +25,6 @@ namespace gdn {
 static_assert(kWsRecordBytes == kWorkspaceRecordBytes, "workspace record size");
 namespace {
 
-// 16x16x16 fp32 product on MFMA with the 16-deep version of the fragment convention:
-// A from LDS (row-major, leading dim ld), B either from LDS or from a C fragment in registers.
-// Padded row length of the 64x64 fp32 LDS matrices: rows start 16-byte aligned (4 consecutive
-// columns are one 16-byte access) and consecutive rows start 4 banks apart.
-constexpr int kLd = 68;
-
-__device__ __forceinline__ f32x4 row4(const float* p) {
-  return *reinterpret_cast<const f32x4*>(p);
-}
-
-__device__ __forceinline__ f32x4 mm16_ll(const float* A, const float* B, f32x4 c, int idx,
-                                         int grp) {
-  // A: 16x16 block at A (row stride kLd), B: 16x16 block at B (row stride kLd).
-  const f32x4 a = row4(A + idx * kLd + 4 * grp);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], B[(4 * grp + r) * kLd + idx], c, 0, 0, 0);
-  return c;
-}
-__device__ __forceinline__ f32x4 mm16_lr(const float* A, const f32x4& Bc, f32x4 c, int idx,
-                                         int grp) {
-  const f32x4 a = row4(A + idx * kLd + 4 * grp);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], Bc[r], c, 0, 0, 0);
-  return c;
-}
-__device__ __forceinline__ void store_c16(float* C, const f32x4& c, int idx, int grp,
-                                          float sign) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) C[(4 * grp + r) * kLd + idx] = sign * c[r];
-}
-
 struct IntraParams {
   const int32_t* cu;
   const void* q;
@@ -282,73 +249,10 @@ __global__ __launch_bounds__(256 * NV) void chunk_intra_kernel(IntraParams p) {
   }
   lds_barrier();  // A complete
 
-  // ---- Diagonal 16x16 blocks of T, in place of A's: wave v < NV inverts the four blocks of
-  // head v at once by forward substitution, lane (blk, c) = (lane / 16, lane % 16) solving for
-  // column c of block blk: x_i = delta_ic - sum_{j<i} A_ij x_j. Row i of a block is read as
-  // 16-byte pieces that the block's 16 lanes share (one address per lane group).
-  if (wave < NV) {
-    const int blk = lane >> 4, c = lane & 15;
-    float* Ab = sA(wave) + (16 * blk) * kLd + 16 * blk;
-    float x[16];
-    x[0] = c == 0 ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float a[16];
-#pragma unroll
-      for (int q = 0; q < (i + 3) / 4; ++q) {
-        const f32x4 a4 = row4(Ab + i * kLd + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[4 * q + e] = a4[e];
-      }
-      float part[4] = {0.f, 0.f, 0.f, 0.f};  // 4 independent chains
-#pragma unroll
-      for (int jj = 0; jj < i; ++jj) part[jj & 3] = fmaf(a[jj], x[jj], part[jj & 3]);
-      x[i] = (i == c) ? 1.f : -((part[0] + part[1]) + (part[2] + part[3]));
-    }
-    // row i is written after its own read (x_i depends on it); other rows are disjoint
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Ab[i * kLd + c] = x[i];
-  }
-  lds_barrier();
-  // Waves 2 v and 2 v + 1 finish head v's inverse; wl is the wave's index in that pair.
-  const int hv_ = wave >> 1, wl = wave & 1;
-  const bool lw = wave < 2 * NV;
-  float* const Mx = sA(lw ? hv_ : 0);
-  // ---- Level 2: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22 (over A_10, A_32: each wave
-  // reads its block into M before writing it).
-  if (lw) {
-    const int ib = 2 * wl + 1, jb = 2 * wl;
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 M = mm16_ll(Mx + 16 * ib * kLd + 16 * jb, Mx + 16 * jb * kLd + 16 * jb, z, idx, grp);
-    f32x4 R = mm16_lr(Mx + 16 * ib * kLd + 16 * ib, M, z, idx, grp);
-    store_c16(Mx + 16 * ib * kLd + 16 * jb, R, idx, grp, -1.f);
-  }
-  lds_barrier();
-  // ---- Level 3, column block jb in {0, 1} (wave jb of the pair):
-  //   X_i = sum_{kb=jb..1} A_{i,kb} T_{kb,jb} (i = 2, 3)
-  //   T_{2,jb} = -T_22 X_2,  T_{3,jb} = -(T_32 X_2 + T_33 X_3)
-  // Wave 0 of the pair reads A_21 and A_31, which wave 1 overwrites: the stores wait for a
-  // barrier.
-  f32x4 T2 = {0.f, 0.f, 0.f, 0.f}, T3 = {0.f, 0.f, 0.f, 0.f};
-  if (lw) {
-    const int jb = wl;
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 X2 = z, X3 = z;
-    for (int kb = jb; kb < 2; ++kb) {
-      const float* Tk = Mx + 16 * kb * kLd + 16 * jb;
-      X2 = mm16_ll(Mx + 32 * kLd + 16 * kb, Tk, X2, idx, grp);
-      X3 = mm16_ll(Mx + 48 * kLd + 16 * kb, Tk, X3, idx, grp);
-    }
-    T2 = mm16_lr(Mx + 32 * kLd + 32, X2, z, idx, grp);
-    T3 = mm16_lr(Mx + 48 * kLd + 32, X2, z, idx, grp);
-    T3 = mm16_lr(Mx + 48 * kLd + 48, X3, T3, idx, grp);
-  }
-  lds_barrier();
-  if (lw) {
-    store_c16(Mx + 32 * kLd + 16 * wl, T2, idx, grp, -1.f);
-    store_c16(Mx + 48 * kLd + 16 * wl, T3, idx, grp, -1.f);
-  }
-  lds_barrier();
+  // ---- T = (I + A)^-1 in place: head v's diagonal blocks on wave v, its off-diagonal blocks on
+  // waves 2 v and 2 v + 1.
+  invert_unit_lower64(wave < NV ? sA(wave) : nullptr, wave < 2 * NV ? sA(wave >> 1) : nullptr,
+                      wave & 1, lane);
   // ---- T diag(beta) of every head as stored A fragments: NV x 6 blocks x 64 lanes.
   for (int it = tid; it < NV * 6 * 64; it += 256 * NV) {
     const int v = it / 384, bi = (it >> 6) % 6, ln = it & 63;

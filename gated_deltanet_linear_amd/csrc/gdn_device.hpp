@@ -433,4 +433,114 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// ---- 64x64 fp32 matrices in LDS (the chunk's triangular systems) ------------------------
+
+// 16x16x16 fp32 product on MFMA with the 16-deep version of the fragment convention:
+// A from LDS (row-major, leading dim ld), B either from LDS or from a C fragment in registers.
+// Padded row length of the 64x64 fp32 LDS matrices: rows start 16-byte aligned (4 consecutive
+// columns are one 16-byte access) and consecutive rows start 4 banks apart.
+constexpr int kLd = 68;
+
+__device__ __forceinline__ f32x4 row4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+
+__device__ __forceinline__ f32x4 mm16_ll(const float* A, const float* B, f32x4 c, int idx,
+                                         int grp) {
+  // A: 16x16 block at A (row stride kLd), B: 16x16 block at B (row stride kLd).
+  const f32x4 a = row4(A + idx * kLd + 4 * grp);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], B[(4 * grp + r) * kLd + idx], c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ f32x4 mm16_lr(const float* A, const f32x4& Bc, f32x4 c, int idx,
+                                         int grp) {
+  const f32x4 a = row4(A + idx * kLd + 4 * grp);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], Bc[r], c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ void store_c16(float* C, const f32x4& c, int idx, int grp,
+                                          float sign) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) C[(4 * grp + r) * kLd + idx] = sign * c[r];
+}
+
+// T = (I + A)^-1 of a unit-lower-triangular 64x64 matrix, in place: on entry the fp32 matrix at
+// M (row stride kLd, in LDS) holds A in its lower triangle (diagonal blocks: strictly lower part
+// and zeros above; blocks above the diagonal are never read), on exit T on and below the
+// diagonal (its diagonal blocks hold zeros above their diagonal; blocks above the diagonal keep
+// whatever they held). Every wave of the workgroup calls this (it has three workgroup
+// barriers and ends with a fourth); a wave may serve two matrices at once:
+//   msub  (or null): this wave inverts the four 16x16 diagonal blocks of msub by forward
+//         substitution, lane (blk, c) = (lane / 16, lane % 16) solving for column c of block
+//         blk: x_i = delta_ic - sum_{j<i} A_ij x_j; row i of a block is read as 16-byte pieces
+//         that the block's 16 lanes share (one address per lane group);
+//   mpair (or null), wl in {0, 1}: this wave is wave wl of the pair that forms the blocks below
+//         the diagonal of mpair (after the diagonal blocks) by 16x16 fp32 MFMA products:
+//         level 2: T_10 = -T_11 A_10 T_00 (wl = 0), T_32 = -T_33 A_32 T_22 (wl = 1);
+//         level 3, column block jb = wl: X_i = sum_{kb=jb..1} A_{i,kb} T_{kb,jb} (i = 2, 3),
+//         T_{2,jb} = -T_22 X_2, T_{3,jb} = -(T_32 X_2 + T_33 X_3).
+__device__ __forceinline__ void invert_unit_lower64(float* msub, float* mpair, int wl, int lane) {
+  const int idx = lane & 15, grp = lane >> 4;
+  if (msub) {
+    const int blk = lane >> 4, c = lane & 15;
+    float* Ab = msub + (16 * blk) * kLd + 16 * blk;
+    float x[16];
+    x[0] = c == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float a[16];
+#pragma unroll
+      for (int q = 0; q < (i + 3) / 4; ++q) {
+        const f32x4 a4 = row4(Ab + i * kLd + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * q + e] = a4[e];
+      }
+      float part[4] = {0.f, 0.f, 0.f, 0.f};  // 4 independent chains
+#pragma unroll
+      for (int jj = 0; jj < i; ++jj) part[jj & 3] = fmaf(a[jj], x[jj], part[jj & 3]);
+      x[i] = (i == c) ? 1.f : -((part[0] + part[1]) + (part[2] + part[3]));
+    }
+    // row i is written after its own read (x_i depends on it); other rows are disjoint
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ab[i * kLd + c] = x[i];
+  }
+  lds_barrier();
+  // level 2 (over A_10, A_32: each wave reads its block into M before writing it)
+  if (mpair) {
+    const int ib = 2 * wl + 1, jb = 2 * wl;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 M = mm16_ll(mpair + 16 * ib * kLd + 16 * jb, mpair + 16 * jb * kLd + 16 * jb, z,
+                            idx, grp);
+    const f32x4 R = mm16_lr(mpair + 16 * ib * kLd + 16 * ib, M, z, idx, grp);
+    store_c16(mpair + 16 * ib * kLd + 16 * jb, R, idx, grp, -1.f);
+  }
+  lds_barrier();
+  // level 3: wave 0 of the pair reads A_21 and A_31, which wave 1 overwrites, so the stores
+  // wait for a barrier
+  f32x4 T2 = {0.f, 0.f, 0.f, 0.f}, T3 = {0.f, 0.f, 0.f, 0.f};
+  if (mpair) {
+    const int jb = wl;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 X2 = z, X3 = z;
+    for (int kb = jb; kb < 2; ++kb) {
+      const float* Tk = mpair + 16 * kb * kLd + 16 * jb;
+      X2 = mm16_ll(mpair + 32 * kLd + 16 * kb, Tk, X2, idx, grp);
+      X3 = mm16_ll(mpair + 48 * kLd + 16 * kb, Tk, X3, idx, grp);
+    }
+    T2 = mm16_lr(mpair + 32 * kLd + 32, X2, z, idx, grp);
+    T3 = mm16_lr(mpair + 48 * kLd + 32, X2, z, idx, grp);
+    T3 = mm16_lr(mpair + 48 * kLd + 48, X3, T3, idx, grp);
+  }
+  lds_barrier();
+  if (mpair) {
+    store_c16(mpair + 32 * kLd + 16 * wl, T2, idx, grp, -1.f);
+    store_c16(mpair + 48 * kLd + 16 * wl, T3, idx, grp, -1.f);
+  }
+  lds_barrier();
+}
+
 }  // namespace gdn
