@@ -335,7 +335,8 @@ def run_gate(torch, gdn, si, steps, warmup):
 def run_decode_front(torch, gdn, si, steps, warmup):
     """One decode token for 256 sequences from projected inputs (35B-A3B layer shape, bf16
     inputs, fp32 state updated in place): the fused gdn_decode_step, and for comparison the
-    two-call path gdn_decode_prepare then gdn_recurrent_step."""
+    two-call path gdn_decode_prepare then gdn_recurrent_step; with the layer's output gate,
+    gdn_decode_step_gated (one kernel) against gdn_decode_step then gdn_gated_rmsnorm."""
     dc = si.make_decode_front_case(256, 16, 32, 128, 128, seed=1007,
                                    meta=dict(workload="decode_front_256x1"))
     dev = "cuda"
@@ -361,6 +362,22 @@ def run_decode_front(torch, gdn, si, steps, warmup):
 
     ev2, ms2, kms2 = _measure(
         torch, [("gdn_decode_prepare", prep), ("gdn_recurrent_step", rstep)], steps, warmup)
+    # the layer's output gate: fused into the step (one kernel) and as the step + gate kernel
+    gen = torch.Generator().manual_seed(1008)
+    z = torch.randn((N, hv, dv), generator=gen).to(torch.bfloat16).to(dev)
+    gw = (0.1 * torch.randn((dv,), generator=gen)).to(dev)
+    out = torch.empty_like(o)
+    ev4, ms4, kms4 = _measure(
+        torch, [("gdn_decode_step_gated",
+                 lambda: gdn.decode_step_gated(x, win, w, a, b, A_log, dt_bias, state, z, hqk, dk,
+                                               hv, weight=gw, weight_offset=1.0, out=out))],
+        steps, warmup)
+    ev5, ms5, kms5 = _measure(
+        torch, [("gdn_decode_step", lambda: gdn.decode_step(x, win, w, a, b, A_log, dt_bias,
+                                                            state, hqk, dk, hv, o=o)),
+                ("gdn_gated_rmsnorm", lambda: gdn.gated_rmsnorm(o, z, gw, 1.0, 1e-6, out=out))],
+        steps, warmup)
+    del z, gw, out
     state16 = state.to(torch.bfloat16)
     del state
     ev3, ms3, kms3 = _measure(
@@ -382,6 +399,11 @@ def run_decode_front(torch, gdn, si, steps, warmup):
                 bf16_state=dict(ms_per_step=ms3, tokens_per_s=N / (ms3 / 1e3), kernels_ms=kms3,
                                 roofline=_hbm("gdn_decode_step", Bfused16, kms3["gdn_decode_step"],
                                               "gdn_decode_step_decode_front_256x1_bf16_state")),
+                gated=dict(ms_per_step=ms4, tokens_per_s=N / (ms4 / 1e3), kernels_ms=kms4,
+                           roofline=_hbm("gdn_decode_step_gated", Bfused + N * hv * dv * e + dv * 4,
+                                         kms4["gdn_decode_step_gated"]),
+                           unfused=dict(ms_per_step=ms5, tokens_per_s=N / (ms5 / 1e3),
+                                        kernels_ms=kms5)),
                 two_call=dict(ms_per_step=ms2, tokens_per_s=N / (ms2 / 1e3), kernels_ms=kms2,
                               decode_prepare=_hbm("gdn_decode_prepare", Bprep,
                                                   kms2["gdn_decode_prepare"],

@@ -23,6 +23,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["prepare", "chunk_forward", "chunk_intra", "chunk_scan", "recurrent_step",
+           "recurrent_step_gated", "decode_step", "decode_step_gated",
            "decode_prepare", "gated_rmsnorm", "workspace_size", "library_path", "GdnError",
            "CHUNK"]
 
@@ -91,6 +92,12 @@ def _load():
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                     _P]
+    lib.gdn_recurrent_step_gated.restype = ctypes.c_int
+    lib.gdn_recurrent_step_gated.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                             ctypes.c_float, _P, _P]
+    lib.gdn_decode_step_gated.restype = ctypes.c_int
+    lib.gdn_decode_step_gated.argtypes = [sp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                          _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [sp, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -357,6 +364,45 @@ def recurrent_step(q, k, v, g, beta, state, scale=1.0, out_dtype=None, o=None) -
     return o
 
 
+def _gate_args(z, weight, n, hv, dv, name):
+    _dev(z, "z")
+    if z.shape != (n, hv, dv):
+        raise GdnError(f"{name}: z must be [N, H_v, d_v]")
+    if weight is not None:
+        _dev(weight, "weight", torch.float32)
+        if weight.shape != (dv,):
+            raise GdnError(f"{name}: weight must be [d_v]")
+
+
+def recurrent_step_gated(q, k, v, g, beta, state, z, weight=None, weight_offset=0.0, eps=1e-6,
+                         scale=1.0, out_dtype=None, out=None) -> torch.Tensor:
+    """recurrent_step with the output gate fused into the same kernel: returns
+    RMSNorm(o) * (weight + weight_offset) * SiLU(z) per V-head row, [N, H_v, d_v] (out_dtype,
+    default q's dtype); z [N, H_v, d_v] (its dtype is the shape's in_dtype), weight [d_v] fp32
+    or None (factor 1). The state is updated in place as by recurrent_step."""
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    _dev(g, "g", torch.float32)
+    _dev(beta, "beta", torch.float32)
+    _dev(state, "state")
+    N, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N or g.shape != (N, hv) or beta.shape != (N, hv) \
+            or state.shape != (N, hv, dk, dv):
+        raise GdnError("recurrent_step_gated: inconsistent shapes")
+    _gate_args(z, weight, N, hv, dv, "recurrent_step_gated")
+    od = _out_dtype(out_dtype, out, q.dtype)
+    s = _shape(N, N, hqk, hv, dk, dv, q.dtype, od, in_dtype=z.dtype, scale=scale,
+               state_dtype=state.dtype)
+    out = _out(out, (N, hv, dv), od, q.device, "out")
+    rc = _load().gdn_recurrent_step_gated(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                          _ptr(beta), _ptr(state), _ptr(z), _ptr(weight),
+                                          float(weight_offset), float(eps), _ptr(out), _stream())
+    _check(rc, "gdn_recurrent_step_gated")
+    return out
+
+
 def prepare(mixed_qkv, conv_weight, a, b, A_log, dt_bias, cu_seqlens, num_qk_heads, head_dim_k,
             num_v_heads, head_dim_v, conv_bias=None, l2norm_eps=1e-6, qkv_dtype=None):
     """Front end: returns q, k [T, H_qk, d_k], v [T, H_v, d_v] (qkv_dtype, default the input
@@ -476,6 +522,51 @@ def decode_step(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, state
                                  _ptr(dt_bias), float(l2norm_eps), _ptr(state), _ptr(o), _stream())
     _check(rc, "gdn_decode_step")
     return o
+
+
+def decode_step_gated(mixed_qkv, conv_window, conv_weight, a, b, A_log, dt_bias, state, z,
+                      num_qk_heads, head_dim, num_v_heads, weight=None, weight_offset=0.0,
+                      norm_eps=1e-6, conv_bias=None, l2norm_eps=1e-6, scale=1.0, out_dtype=None,
+                      out=None):
+    """decode_step with the output gate fused into the same kernel: one decode token per
+    sequence from projected inputs to RMSNorm(o) * (weight + weight_offset) * SiLU(z), [N, H_v, d]
+    (out_dtype, default the input dtype). z [N, H_v, d] in the input dtype; the window and the
+    state are updated in place as by decode_step."""
+    _dev(mixed_qkv, "mixed_qkv")
+    dt = mixed_qkv.dtype
+    _dev(conv_window, "conv_window", dt)
+    _dev(conv_weight, "conv_weight", dt)
+    _dev(a, "a", dt)
+    _dev(b, "b", dt)
+    _dev(A_log, "A_log", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    _dev(state, "state")
+    if conv_bias is not None:
+        _dev(conv_bias, "conv_bias", dt)
+    N, conv_dim = mixed_qkv.shape
+    hqk, d, hv = int(num_qk_heads), int(head_dim), int(num_v_heads)
+    if conv_dim != (2 * hqk + hv) * d or conv_weight.shape != (conv_dim, 4):
+        raise GdnError("mixed_qkv must be [N, (2*H_qk + H_v)*d] and conv_weight [conv_dim, 4]")
+    if conv_window.shape != (N, conv_dim, 3):
+        raise GdnError("conv_window must be [N, conv_dim, 3]")
+    if a.shape != (N, hv) or b.shape != (N, hv) or A_log.shape != (hv,) or dt_bias.shape != (hv,):
+        raise GdnError("a, b must be [N, H_v]; A_log, dt_bias [H_v]")
+    if state.shape != (N, hv, d, d):
+        raise GdnError("state must be [N, H_v, d, d]")
+    _gate_args(z, weight, N, hv, d, "decode_step_gated")
+    if z.dtype != dt:
+        raise GdnError("decode_step_gated: z must have the input dtype")
+    od = _out_dtype(out_dtype, out, dt)
+    s = _shape(N, N, hqk, hv, d, d, torch.float32, od, in_dtype=dt, scale=scale,
+               state_dtype=state.dtype)
+    out = _out(out, (N, hv, d), od, mixed_qkv.device, "out")
+    rc = _load().gdn_decode_step_gated(ctypes.byref(s), _ptr(mixed_qkv), _ptr(conv_window),
+                                       _ptr(conv_weight), _ptr(conv_bias), _ptr(a), _ptr(b),
+                                       _ptr(A_log), _ptr(dt_bias), float(l2norm_eps), _ptr(state),
+                                       _ptr(z), _ptr(weight), float(weight_offset),
+                                       float(norm_eps), _ptr(out), _stream())
+    _check(rc, "gdn_decode_step_gated")
+    return out
 
 
 def gated_rmsnorm(o, z, weight=None, weight_offset=0.0, eps=1e-6, out=None):

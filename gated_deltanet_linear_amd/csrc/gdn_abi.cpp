@@ -36,6 +36,15 @@ gdn_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Output-gate arguments shared by the gated decode entry points.
+gdn_status_t check_gate(const gdn_shape_t* s, const void* z, const float* weight,
+                        float weight_offset, float eps) {
+  if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!z || !(eps >= 0.f) || !(weight_offset == weight_offset)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(z, 16) || !aligned(weight, 16)) return GDN_ERR_INVALID_ARGUMENT;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,6 +199,23 @@ gdn_status_t gdn_recurrent_step(const gdn_shape_t* s, const void* q, const void*
                                              static_cast<hipStream_t>(stream)));
 }
 
+gdn_status_t gdn_recurrent_step_gated(const gdn_shape_t* s, const void* q, const void* k,
+                                      const void* v, const float* g, const float* beta,
+                                      void* state, const void* z, const float* norm_weight,
+                                      float weight_offset, float norm_eps, void* out,
+                                      void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (s->total_tokens != s->num_seqs) return GDN_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(state, 16)) return GDN_ERR_INVALID_ARGUMENT;
+  st = check_gate(s, z, norm_weight, weight_offset, norm_eps);
+  if (st != GDN_OK) return st;
+  return from_hip(gdn::launch_recurrent_step(*s, q, k, v, g, beta, state, out,
+                                             static_cast<hipStream_t>(stream), z, norm_weight,
+                                             weight_offset, norm_eps));
+}
+
 gdn_status_t gdn_decode_prepare(const gdn_shape_t* s, const void* x, void* win, const void* w,
                                 const void* bias, const void* a, const void* b,
                                 const float* A_log, const float* dt_bias, float eps, void* q,
@@ -230,6 +256,31 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* s, const void* x, void* win, con
     return GDN_ERR_INVALID_ARGUMENT;
   return from_hip(gdn::launch_decode_step(*s, x, win, w, bias, a, b, A_log, dt_bias, eps, state,
                                           o, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_decode_step_gated(const gdn_shape_t* s, const void* x, void* win, const void* w,
+                                   const void* bias, const void* a, const void* b,
+                                   const float* A_log, const float* dt_bias, float eps,
+                                   void* state, const void* z, const float* norm_weight,
+                                   float weight_offset, float norm_eps, void* out, void* stream) {
+  gdn_status_t st = check_shape(s);
+  if (st != GDN_OK) return st;
+  if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens != s->num_seqs) return GDN_ERR_INVALID_ARGUMENT;
+  // q, k, the G v rows and z rows of a workgroup's QK head and the factors are held in LDS
+  const long long G = s->num_v_heads / s->num_qk_heads;
+  if (((3 + 2 * G) * s->head_dim_v + 2 * G) * 4 > 65536) return GDN_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARGUMENT;
+  if (!x || !win || !w || !a || !b || !A_log || !dt_bias || !state || !out)
+    return GDN_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(win, 16) || !aligned(w, 16) || !aligned(bias, 16) ||
+      !aligned(state, 16))
+    return GDN_ERR_INVALID_ARGUMENT;
+  st = check_gate(s, z, norm_weight, weight_offset, norm_eps);
+  if (st != GDN_OK) return st;
+  return from_hip(gdn::launch_decode_step(*s, x, win, w, bias, a, b, A_log, dt_bias, eps, state,
+                                          out, static_cast<hipStream_t>(stream), z, norm_weight,
+                                          weight_offset, norm_eps));
 }
 
 gdn_status_t gdn_gated_rmsnorm(const gdn_shape_t* s, const void* o, const void* z,

@@ -94,11 +94,35 @@ struct StepRed {
 // loaded them; the call is inlined). qrow / krow give q and k at the thread's rows (index r),
 // vcol the v value of column c of its group. Writes o (threads of row group 0) and the new
 // state; the barrier inside is workgroup-wide.
-template <typename ST, typename OutT, int D, typename QF, typename KF, typename VF>
+// Output gate fused into the step: out_j = o_j / sqrt(mean_j o^2 + eps) * fac_j * SiLU(z_j) over
+// the d_v columns of the head ([xiwon notes] "Qwen3_5MoeGatedDeltaNet", output stage). The
+// workgroup holds the whole row, so the mean square is a shuffle reduction over the lanes of
+// one row group. z is read as in_dtype (bf16 when z_bf16), the weight (or null: factor 1) as
+// fp32.
+struct OutGate {
+  const void* z;  // [N][H_v][d_v], null: no gate (o is written)
+  const float* w;
+  float woff, eps;
+  int z_bf16;
+};
+
+// z of one row and the factors into LDS (D values each; threads 0 .. D - 1 of the caller).
+template <int D>
+__device__ __forceinline__ void gate_to_lds(const OutGate& ga, size_t row, float* zs, float* fs,
+                                            int tid) {
+  if (tid < D) {
+    zs[tid] = ga.z_bf16 ? (float)static_cast<const bf16*>(ga.z)[row + tid]
+                        : static_cast<const float*>(ga.z)[row + tid];
+    if (fs) fs[tid] = ga.w ? ga.w[tid] + ga.woff : 1.f;
+  }
+}
+
+template <typename ST, typename OutT, int D, bool GATE, typename QF, typename KF, typename VF>
 __device__ __forceinline__ void head_step(const StateVec<ST>* s, StepRed<ST, D>& red, QF qrow,
                                           KF krow, VF vcol,
                                           float alpha, float bt, float scale, ST* S, OutT* ov,
-                                          int tid) {
+                                          int tid, const float* zs = nullptr,
+                                          const float* fs = nullptr, float geps = 0.f) {
   using L = StepLayout<ST, D>;
   constexpr int VEC = L::VEC, CG = L::CG, RG = L::RG, R = L::R, NW = L::NW;
   const int cg = tid % CG, rg = tid / CG, lane = tid & 63, wave = tid >> 6;
@@ -134,7 +158,7 @@ __device__ __forceinline__ void head_step(const StateVec<ST>* s, StepRed<ST, D>&
     if (lane == 0) red.qk[wave] = pqk;
   }
   __syncthreads();
-  float qk = red.qk[0], u[VEC];
+  float qk = red.qk[0], u[VEC], oc[VEC];
 #pragma unroll
   for (int w = 1; w < NW; ++w) qk += red.qk[w];
 #pragma unroll
@@ -146,7 +170,27 @@ __device__ __forceinline__ void head_step(const StateVec<ST>* s, StepRed<ST, D>&
       sqc += red.q[w][cg][c];
     }
     u[c] = bt * (vcol(c) - alpha * skc);
-    if (rg == 0) ov[VEC * cg + c] = from_f32<OutT>(scale * (alpha * sqc + qk * u[c]));
+    oc[c] = scale * (alpha * sqc + qk * u[c]);
+    if constexpr (!GATE) {
+      if (rg == 0) ov[VEC * cg + c] = from_f32<OutT>(oc[c]);
+    }
+  }
+  if constexpr (GATE) {
+    // every row group holds the whole row: the CG lanes of one group reduce it (z and the
+    // factors were put in LDS before the barrier above)
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) ss = fmaf(oc[c], oc[c], ss);
+#pragma unroll
+    for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.f / sqrtf(ss * (1.f / D) + geps);
+    if (rg == 0) {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        const float zc = zs[VEC * cg + c];
+        ov[VEC * cg + c] = from_f32<OutT>(oc[c] * inv * fs[VEC * cg + c] * (zc / (1.f + expf(-zc))));
+      }
+    }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -158,11 +202,11 @@ __device__ __forceinline__ void head_step(const StateVec<ST>* s, StepRed<ST, D>&
   }
 }
 
-template <typename InT, typename OutT, typename ST, int D>
+template <typename InT, typename OutT, typename ST, int D, bool GATE>
 __global__ __launch_bounds__((step_threads<ST, D>())) void recurrent_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ST* __restrict__ state,
-    OutT* __restrict__ o, int hqk, int hv, float scale) {
+    OutT* __restrict__ o, int hqk, int hv, float scale, OutGate ga) {
   using L = StepLayout<ST, D>;
   __shared__ StepRed<ST, D> red;
 
@@ -185,10 +229,12 @@ __global__ __launch_bounds__((step_threads<ST, D>())) void recurrent_step_kernel
     ki[r] = to_f32(kv[rg + L::RG * r]);
   }
   const InT* vv = v + (size_t)nh * D + L::VEC * cg;
-  head_step<ST, OutT, D>(
+  __shared__ float gzs[GATE ? D : 1], gfs[GATE ? D : 1];
+  if constexpr (GATE) gate_to_lds<D>(ga, (size_t)nh * D, gzs, gfs, tid);
+  head_step<ST, OutT, D, GATE>(
       s, red, [&](int r) { return qi[r]; }, [&](int r) { return ki[r]; },
       [&](int c) { return to_f32(vv[c]); }, expf(g[nh]), beta[nh], scale, S, o + (size_t)nh * D,
-      tid);
+      tid, gzs, gfs, ga.eps);
 }
 
 // ---- fused decode step from projected inputs --------------------------------------------
@@ -201,6 +247,7 @@ __global__ __launch_bounds__((step_threads<ST, D>())) void recurrent_step_kernel
 // (a second register set would halve the workgroups per CU). q, k and v stay fp32 (in LDS)
 // between the front end and the step.
 struct DecStepParams {
+  OutGate gate;  // z null: no output gate
   const void* x;
   void* win;
   const void* w;
@@ -218,7 +265,7 @@ struct DecStepParams {
 
 // fp32 state: at least 4 waves per SIMD (<= 128 VGPRs), two 512-thread workgroups per CU as for
 // the plain step. bf16 state (256-thread workgroups): at least 3 (<= 168 VGPRs, no spills).
-template <typename InT, typename OutT, typename ST, int D>
+template <typename InT, typename OutT, typename ST, int D, bool GATE>
 __global__ __launch_bounds__((step_threads<ST, D>()))
 __attribute__((amdgpu_waves_per_eu(sizeof(ST) == 4 ? 4 : 3, 8))) void decode_step_kernel(
     DecStepParams p) {
@@ -227,7 +274,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(ST) == 4 ? 4 : 3, 8))) void decode_ste
   constexpr int CGN = D / 8;  // front-end threads per channel head (8 channels each)
   static_assert(NTH % CGN == 0, "front-end lane groups");
 
-  extern __shared__ float lds[];  // q[D] | k[D] | v[G][D] | alpha[G] | beta[G]
+  // q[D] | k[D] | v[G][D] | alpha[G] | beta[G], then with the output gate z[G][D] | factors[D]
+  extern __shared__ float lds[];
   __shared__ StepRed<ST, D> red[2];
 
   const int G = p.hv / p.hqk;
@@ -240,6 +288,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(ST) == 4 ? 4 : 3, 8))) void decode_ste
   float* sv = lds + 2 * D;
   float* s_alpha = lds + (2 + G) * D;
   float* s_beta = s_alpha + G;
+  float* s_z = s_beta + G;
+  float* s_f = s_z + G * D;
 
   ST* const state = static_cast<ST*>(p.state);
   auto state_of = [&](int j) { return state + ((size_t)n * p.hv + h0 + j) * D * D; };
@@ -274,6 +324,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(ST) == 4 ? 4 : 3, 8))) void decode_ste
     for (int e = 0; e < 8; ++e) dst[e] = y[e];
     cv.store_shifted_window(W3);
   }
+  if constexpr (GATE) {
+    for (int j = 0; j < G; ++j)
+      gate_to_lds<D>(p.gate, ((size_t)n * p.hv + h0 + j) * D, s_z + j * D, j == 0 ? s_f : nullptr,
+                     tid);
+  }
   for (int j = tid; j < G; j += NTH) {
     const size_t i = (size_t)n * p.hv + h0 + j;
     const float ga = -expf(p.A_log[h0 + j]) *
@@ -288,10 +343,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(ST) == 4 ? 4 : 3, 8))) void decode_ste
   for (int j = 0; j < G; ++j) {
     ST* S = state_of(j);
     const float* vj = sv + j * D + L::VEC * cg;
-    head_step<ST, OutT, D>(
+    head_step<ST, OutT, D, GATE>(
         s, red[j & 1], [&](int r) { return sq[rg + L::RG * r]; },
         [&](int r) { return sk[rg + L::RG * r]; }, [&](int c) { return vj[c]; }, s_alpha[j],
-        s_beta[j], p.scale, S, static_cast<OutT*>(p.o) + ((size_t)n * p.hv + h0 + j) * D, tid);
+        s_beta[j], p.scale, S, static_cast<OutT*>(p.o) + ((size_t)n * p.hv + h0 + j) * D, tid,
+        s_z + j * D, s_f, p.gate.eps);
     if (j + 1 < G) {  // the next head's rows into the same registers
       const ST* Sn = state_of(j + 1);
 #pragma unroll
@@ -306,9 +362,14 @@ hipError_t launch_decode_step_t(const gdn_shape_t& s, const DecStepParams& p,
   const unsigned blocks = (unsigned)s.num_seqs * (unsigned)s.num_qk_heads;
   if (blocks == 0) return hipSuccess;
   const int G = s.num_v_heads / s.num_qk_heads;
-  const size_t lds = (size_t)((2 + G) * D + 2 * G) * sizeof(float);
-  hipLaunchKernelGGL((decode_step_kernel<InT, OutT, ST, D>), dim3(blocks),
-                     dim3(step_threads<ST, D>()), lds, stream, p);
+  const size_t lds =
+      (size_t)((2 + G) * D + 2 * G + (p.gate.z ? (G + 1) * D : 0)) * sizeof(float);
+  if (p.gate.z)
+    hipLaunchKernelGGL((decode_step_kernel<InT, OutT, ST, D, true>), dim3(blocks),
+                       dim3(step_threads<ST, D>()), lds, stream, p);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<InT, OutT, ST, D, false>), dim3(blocks),
+                       dim3(step_threads<ST, D>()), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -333,25 +394,32 @@ hipError_t launch_decode_step_s(const gdn_shape_t& s, const DecStepParams& p,
 template <typename InT, typename OutT, typename ST, int D>
 hipError_t launch_step_t(const gdn_shape_t& s, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, void* state, void* o,
-                         hipStream_t stream) {
+                         const OutGate& ga, hipStream_t stream) {
   const unsigned blocks = (unsigned)s.num_seqs * (unsigned)s.num_v_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((recurrent_step_kernel<InT, OutT, ST, D>), dim3(blocks),
-                     dim3(step_threads<ST, D>()), 0, stream,
-                     static_cast<const InT*>(q), static_cast<const InT*>(k),
-                     static_cast<const InT*>(v), g, beta, static_cast<ST*>(state),
-                     static_cast<OutT*>(o), s.num_qk_heads, s.num_v_heads, s.scale);
+  if (ga.z)
+    hipLaunchKernelGGL((recurrent_step_kernel<InT, OutT, ST, D, true>), dim3(blocks),
+                       dim3(step_threads<ST, D>()), 0, stream,
+                       static_cast<const InT*>(q), static_cast<const InT*>(k),
+                       static_cast<const InT*>(v), g, beta, static_cast<ST*>(state),
+                       static_cast<OutT*>(o), s.num_qk_heads, s.num_v_heads, s.scale, ga);
+  else
+    hipLaunchKernelGGL((recurrent_step_kernel<InT, OutT, ST, D, false>), dim3(blocks),
+                       dim3(step_threads<ST, D>()), 0, stream,
+                       static_cast<const InT*>(q), static_cast<const InT*>(k),
+                       static_cast<const InT*>(v), g, beta, static_cast<ST*>(state),
+                       static_cast<OutT*>(o), s.num_qk_heads, s.num_v_heads, s.scale, ga);
   return hipGetLastError();
 }
 
 template <typename InT, typename OutT, typename ST>
 hipError_t launch_step_d(const gdn_shape_t& s, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, void* state, void* o,
-                         hipStream_t stream) {
+                         const OutGate& ga, hipStream_t stream) {
   switch (s.head_dim_k) {
-    case 32: return launch_step_t<InT, OutT, ST, 32>(s, q, k, v, g, beta, state, o, stream);
-    case 64: return launch_step_t<InT, OutT, ST, 64>(s, q, k, v, g, beta, state, o, stream);
-    case 128: return launch_step_t<InT, OutT, ST, 128>(s, q, k, v, g, beta, state, o, stream);
+    case 32: return launch_step_t<InT, OutT, ST, 32>(s, q, k, v, g, beta, state, o, ga, stream);
+    case 64: return launch_step_t<InT, OutT, ST, 64>(s, q, k, v, g, beta, state, o, ga, stream);
+    case 128: return launch_step_t<InT, OutT, ST, 128>(s, q, k, v, g, beta, state, o, ga, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -359,10 +427,10 @@ hipError_t launch_step_d(const gdn_shape_t& s, const void* q, const void* k, con
 template <typename InT, typename OutT>
 hipError_t launch_step_s(const gdn_shape_t& s, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, void* state, void* o,
-                         hipStream_t stream) {
+                         const OutGate& ga, hipStream_t stream) {
   return s.state_dtype == GDN_DTYPE_BF16
-             ? launch_step_d<InT, OutT, bf16>(s, q, k, v, g, beta, state, o, stream)
-             : launch_step_d<InT, OutT, float>(s, q, k, v, g, beta, state, o, stream);
+             ? launch_step_d<InT, OutT, bf16>(s, q, k, v, g, beta, state, o, ga, stream)
+             : launch_step_d<InT, OutT, float>(s, q, k, v, g, beta, state, o, ga, stream);
 }
 
 }  // namespace
@@ -370,8 +438,10 @@ hipError_t launch_step_s(const gdn_shape_t& s, const void* q, const void* k, con
 hipError_t launch_decode_step(const gdn_shape_t& s, const void* x, void* window, const void* w,
                               const void* bias, const void* a, const void* b, const float* A_log,
                               const float* dt_bias, float eps, void* state, void* o,
-                              hipStream_t stream) {
-  DecStepParams p{x, window, w, bias, a, b, A_log, dt_bias, eps, state, o,
+                              hipStream_t stream, const void* gate_z, const float* gate_w,
+                              float gate_woff, float gate_eps) {
+  const OutGate ga{gate_z, gate_w, gate_woff, gate_eps, s.in_dtype == GDN_DTYPE_BF16 ? 1 : 0};
+  DecStepParams p{ga, x, window, w, bias, a, b, A_log, dt_bias, eps, state, o,
                   s.num_qk_heads, s.num_v_heads, s.scale};
   const bool in_bf16 = s.in_dtype == GDN_DTYPE_BF16, out_bf16 = s.out_dtype == GDN_DTYPE_BF16;
   if (in_bf16 && out_bf16) return launch_decode_step_s<bf16, bf16>(s, p, stream);
@@ -382,12 +452,14 @@ hipError_t launch_decode_step(const gdn_shape_t& s, const void* x, void* window,
 
 hipError_t launch_recurrent_step(const gdn_shape_t& s, const void* q, const void* k,
                                  const void* v, const float* g, const float* beta, void* state,
-                                 void* o, hipStream_t stream) {
+                                 void* o, hipStream_t stream, const void* gate_z,
+                                 const float* gate_w, float gate_woff, float gate_eps) {
+  const OutGate ga{gate_z, gate_w, gate_woff, gate_eps, s.in_dtype == GDN_DTYPE_BF16 ? 1 : 0};
   const bool in_bf16 = s.qkv_dtype == GDN_DTYPE_BF16, out_bf16 = s.out_dtype == GDN_DTYPE_BF16;
-  if (in_bf16 && out_bf16) return launch_step_s<bf16, bf16>(s, q, k, v, g, beta, state, o, stream);
-  if (in_bf16) return launch_step_s<bf16, float>(s, q, k, v, g, beta, state, o, stream);
-  if (out_bf16) return launch_step_s<float, bf16>(s, q, k, v, g, beta, state, o, stream);
-  return launch_step_s<float, float>(s, q, k, v, g, beta, state, o, stream);
+  if (in_bf16 && out_bf16) return launch_step_s<bf16, bf16>(s, q, k, v, g, beta, state, o, ga, stream);
+  if (in_bf16) return launch_step_s<bf16, float>(s, q, k, v, g, beta, state, o, ga, stream);
+  if (out_bf16) return launch_step_s<float, bf16>(s, q, k, v, g, beta, state, o, ga, stream);
+  return launch_step_s<float, float>(s, q, k, v, g, beta, state, o, ga, stream);
 }
 
 }  // namespace gdn

@@ -21,9 +21,13 @@ hipError_t launch_chunk_scan_tiles(const gdn_shape_t& s, const int32_t* cu, cons
                                    const void* k, const void* v, const void* h0, void* o,
                                    void* ht, const void* ws, hipStream_t stream);
 
+// gate_z non-null: the output gate out = RMSNorm(o) (gate_w + gate_woff) SiLU(gate_z) is applied
+// in the step's epilogue and written to o (z in shape in_dtype, gate_w fp32 or null).
 hipError_t launch_recurrent_step(const gdn_shape_t& s, const void* q, const void* k,
                                  const void* v, const float* g, const float* beta, void* state,
-                                 void* o, hipStream_t stream);
+                                 void* o, hipStream_t stream, const void* gate_z = nullptr,
+                                 const float* gate_w = nullptr, float gate_woff = 0.f,
+                                 float gate_eps = 0.f);
 
 hipError_t launch_prepare(const gdn_shape_t& s, const int32_t* cu, const void* x,
                           const void* w, const void* bias, const void* a, const void* b,
@@ -38,7 +42,9 @@ hipError_t launch_decode_prepare(const gdn_shape_t& s, const void* x, void* wind
 hipError_t launch_decode_step(const gdn_shape_t& s, const void* x, void* window, const void* w,
                               const void* bias, const void* a, const void* b, const float* A_log,
                               const float* dt_bias, float eps, void* state, void* o,
-                              hipStream_t stream);
+                              hipStream_t stream, const void* gate_z = nullptr,
+                              const float* gate_w = nullptr, float gate_woff = 0.f,
+                              float gate_eps = 0.f);
 
 hipError_t launch_gated_rmsnorm(const gdn_shape_t& s, const void* o, const void* z,
                                 const float* w, float w_offset, float eps, void* out,

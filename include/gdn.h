@@ -267,6 +267,43 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_shape_t* shape, const void* o, const vo
                                const float* weight, float weight_offset, float eps, void* out,
                                void* stream);
 
+/*
+ * gdn_recurrent_step_gated -- gdn_recurrent_step with the layer's output gate applied in the
+ * same kernel ([xiwon notes] "Qwen3_5MoeGatedDeltaNet", output stage; [MoE report] §3.3 stages
+ * 3 and 4): the step's fp32 output row o of each (sequence, V head) is never stored; instead
+ *   out_j = o_j / sqrt(mean_j o^2 + norm_eps) * factor_j * z_j * sigmoid(z_j),
+ *   factor_j = norm_weight[j] + weight_offset, or 1 when norm_weight is NULL,
+ * as gdn_gated_rmsnorm computes it from a stored o (here without o's rounding to out_dtype).
+ * One workgroup holds a head's whole row, so the mean square needs no second pass.
+ *   q, k, v, g, beta, state: as gdn_recurrent_step
+ *   z     [N][H_v][d_v] in_dtype (the gate projection), 16-byte aligned
+ *   norm_weight [d_v] fp32 or NULL, 16-byte aligned     norm_eps >= 0, weight_offset finite
+ *   out   [N][H_v][d_v] out_dtype
+ * GDN_ERR_INVALID_ARGUMENT for a NULL z, a bad in_dtype, a misaligned z / weight / state, a
+ * negative or NaN norm_eps or a NaN weight_offset, and everything gdn_recurrent_step rejects.
+ */
+gdn_status_t gdn_recurrent_step_gated(const gdn_shape_t* shape, const void* q, const void* k,
+                                      const void* v, const float* g, const float* beta,
+                                      void* state, const void* z, const float* norm_weight,
+                                      float weight_offset, float norm_eps, void* out,
+                                      void* stream);
+
+/*
+ * gdn_decode_step_gated -- gdn_decode_step (front end + gated delta step, one kernel) with the
+ * output gate of gdn_recurrent_step_gated applied to each V head's row before it is written:
+ * one decode token per sequence from projected inputs to the gated mixer output. Arguments as
+ * gdn_decode_step, plus z [N][H_v][d_v] in_dtype, norm_weight [d_v] fp32 or NULL,
+ * weight_offset and norm_eps as above, and out [N][H_v][d_v] out_dtype. The workgroup of a QK
+ * head also holds its G z rows and the d_v factors in LDS: (3 + 2 G) * d_v + 2 G floats must
+ * fit in 64 KiB (GDN_ERR_UNSUPPORTED otherwise).
+ */
+gdn_status_t gdn_decode_step_gated(const gdn_shape_t* shape, const void* mixed_qkv,
+                                   void* conv_window, const void* conv_weight,
+                                   const void* conv_bias, const void* a, const void* b,
+                                   const float* A_log, const float* dt_bias, float l2norm_eps,
+                                   void* state, const void* z, const float* norm_weight,
+                                   float weight_offset, float norm_eps, void* out, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* gdn_status_string(gdn_status_t status);
 

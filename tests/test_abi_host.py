@@ -298,3 +298,35 @@ def test_chunk_forward_noalloc_validation(lib):
     assert call(ok, q=None) == INVALID
     assert call(ok, v=ctypes.c_void_p((1 << 20) + 8)) == INVALID
     assert call(ok, o=ctypes.c_void_p((1 << 20) + 8)) == INVALID
+
+
+def test_gated_decode_validation(lib):
+    """gdn_recurrent_step_gated and gdn_decode_step_gated: the step's checks plus the gate's (z
+    given, 16-byte aligned z and weight, eps >= 0, a finite offset, a valid in_dtype)."""
+    s = _shape(num_seqs=4, total_tokens=4)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+
+    def rstep(shape, z=FAKE, w=None, off=1.0, eps=1e-6, out=FAKE, state=FAKE):
+        return lib.gdn_recurrent_step_gated(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            state, z, w, off, eps, out, None)
+
+    def dstep(shape, z=FAKE, w=None, off=1.0, eps=1e-6, out=FAKE):
+        return lib.gdn_decode_step_gated(ctypes.byref(shape), *([FAKE] * 8), 1e-6, FAKE, z, w,
+                                         off, eps, out, None)
+
+    for call in (rstep, dstep):
+        assert call(_shape(num_seqs=4, total_tokens=5)) == INVALID
+        assert call(s, z=None) == INVALID
+        assert call(s, out=None) == INVALID
+        assert call(s, z=mis) == INVALID
+        assert call(s, w=mis) == INVALID
+        assert call(s, eps=-1.0) == INVALID
+        assert call(s, eps=float("nan")) == INVALID
+        assert call(s, off=float("nan")) == INVALID
+        assert call(_shape(num_seqs=4, total_tokens=4, in_dtype=9)) == INVALID
+        assert call(_shape(num_seqs=4, total_tokens=4, head_dim_k=48, head_dim_v=48)) \
+            == UNSUPPORTED
+    assert rstep(s, state=ctypes.c_void_p((1 << 20) + 4)) == INVALID
+    # G = 64 V heads per QK head: q, k, 64 v and 64 z rows and the factors exceed 64 KiB of LDS
+    assert dstep(_shape(num_seqs=4, total_tokens=4, num_qk_heads=1, num_v_heads=64)) \
+        == UNSUPPORTED

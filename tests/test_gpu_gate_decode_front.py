@@ -248,3 +248,131 @@ def test_decode_step_fused_full_size_sampled():
     assert_rms_close_rounded_out(o[sel.cuda()].cpu(), ro, TOL["f32"], "fused decode 256x1 o")
     assert_rms_close(state[sel.cuda()].cpu(), rh, TOL["f32"], "fused decode 256x1 state")
     assert np.array_equal(f64(win[sel.cuda()].cpu()), rwin)
+
+
+# ---- output gate fused into the decode step ---------------------------------------------------
+
+def _gate_inputs(rng, N, hv, d, zdt, form):
+    z = _rand(rng, (N, hv, d), _DT[zdt], 1.5)
+    if form == "none":
+        return z, None, 0.0
+    if form == "plus1":
+        return z, torch.tensor(rng.standard_normal(d) * 0.1, dtype=torch.float32), 1.0
+    return z, torch.tensor(rng.uniform(0.5, 1.5, d), dtype=torch.float32), 0.0
+
+
+@pytest.mark.parametrize("d,dt,G,sdt", [(32, "f32", 1, "f32"), (64, "bf16", 2, "f32"),
+                                        (128, "bf16", 2, "f32"), (128, "f32", 3, "bf16"),
+                                        (128, "bf16", 4, "bf16")])
+def test_recurrent_step_gated_against_oracle(d, dt, G, sdt):
+    """The fused step + output gate against the float64 oracle's recurrence followed by its
+    output gate. Every value the oracle does not see is an fp32 intermediate: the fp32 bar (a
+    bf16 state is stored as the RNE cast of the fp32 state: its own rounding is allowed)."""
+    rng = np.random.default_rng(900 + d + G)
+    N, hqk = 13, 2
+    hv = hqk * G
+    q = torch.nn.functional.normalize(torch.from_numpy(rng.standard_normal((N, hqk, d))), dim=-1)
+    k = torch.nn.functional.normalize(torch.from_numpy(rng.standard_normal((N, hqk, d))), dim=-1)
+    q, k = q.to(_DT[dt]), k.to(_DT[dt])
+    v = _rand(rng, (N, hv, d), _DT[dt])
+    g = torch.from_numpy(-rng.uniform(0.0, 2.0, (N, hv))).float()
+    beta = torch.from_numpy(rng.uniform(0.0, 1.0, (N, hv))).float()
+    h0 = _rand(rng, (N, hv, d, d), _DT[sdt], 0.05)
+    for zdt, form, odt in (("f32", "none", "f32"), ("bf16", "plus1", "f32"),
+                           (dt, "plain", "bf16")):
+        z, w, off = _gate_inputs(rng, N, hv, d, zdt, form)
+        print(f"[step_gated] d={d} qkv={dt} G={G} state={sdt} z={zdt} weight={form} "
+              f"out={odt}", flush=True)
+        hd = h0.cuda()
+        out = gdn.recurrent_step_gated(q.cuda(), k.cuda(), v.cuda(), g.cuda(), beta.cuda(), hd,
+                                       z.cuda(), None if w is None else w.cuda(), off, 1e-6,
+                                       scale=0.8, out_dtype=_DT[odt])
+        torch.cuda.synchronize()
+        ro, rh = oracle.recurrent(f64(q), f64(k), f64(v), f64(g), f64(beta), np.arange(N + 1),
+                                  initial_state=f64(h0), scale=0.8)
+        ref = oracle.gated_rmsnorm(ro, f64(z), f64(w), off, 1e-6)
+        check = assert_rms_close_rounded_out if odt == "bf16" else assert_rms_close
+        check(out, ref, TOL["f32"], "gated step out")
+        scheck = assert_rms_close_rounded_out if sdt == "bf16" else assert_rms_close
+        scheck(hd.cpu(), rh, TOL["f32"], "gated step state")
+
+
+def test_recurrent_step_gated_matches_step_then_gate():
+    """Fused gate = recurrent_step (fp32 o) followed by gdn_gated_rmsnorm, to fp32 rounding;
+    the state update is the plain step's, bit for bit."""
+    rng = np.random.default_rng(91)
+    N, hqk, hv, d = 40, 4, 8, 128
+    q = torch.nn.functional.normalize(torch.randn(N, hqk, d, dtype=torch.float64), dim=-1)
+    k = torch.nn.functional.normalize(torch.randn(N, hqk, d, dtype=torch.float64), dim=-1)
+    q, k = q.bfloat16().cuda(), k.bfloat16().cuda()
+    v = _rand(rng, (N, hv, d), torch.bfloat16).cuda()
+    g = torch.from_numpy(-rng.uniform(0.0, 2.0, (N, hv))).float().cuda()
+    beta = torch.from_numpy(rng.uniform(0.0, 1.0, (N, hv))).float().cuda()
+    h0 = _rand(rng, (N, hv, d, d), torch.float32, 0.02).cuda()
+    z, w, off = _gate_inputs(rng, N, hv, d, "bf16", "plus1")
+    z, w = z.cuda(), w.cuda()
+    s1, s2 = h0.clone(), h0.clone()
+    out1 = gdn.recurrent_step_gated(q, k, v, g, beta, s1, z, w, off, 1e-6,
+                                    out_dtype=torch.float32)
+    o2 = gdn.recurrent_step(q, k, v, g, beta, s2, out_dtype=torch.float32)
+    out2 = gdn.gated_rmsnorm(o2, z, w, off, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert_rms_close(out1.cpu(), f64(out2), 1e-5, "fused vs two-call gated out")
+
+
+@pytest.mark.parametrize("d,dt,G,sdt", [(32, "f32", 1, "f32"), (128, "bf16", 2, "f32"),
+                                        (64, "bf16", 3, "bf16"), (128, "f32", 4, "f32")])
+def test_decode_step_gated_against_oracle(d, dt, G, sdt):
+    """Projected inputs to the gated mixer output in one kernel, against the oracle's front
+    end, one recurrence step and its output gate (fp32 bar)."""
+    rng = np.random.default_rng(950 + d + G)
+    N, hqk = 17, 2
+    hv = hqk * G
+    x, win, wc, bc, a, b, A_log, dt_bias = _front(rng, N, hqk, hv, d, _DT[dt], bias=(G != 3))
+    h0 = _rand(rng, (N, hv, d, d), _DT[sdt], 0.05)
+    z, w, off = _gate_inputs(rng, N, hv, d, dt, "plus1" if G % 2 == 0 else "none")
+    for odt in ("f32", dt):
+        print(f"[decode_step_gated] d={d} {dt} G={G} state={sdt} out={odt}", flush=True)
+        wd, hd = win.cuda(), h0.cuda()
+        out = gdn.decode_step_gated(x.cuda(), wd, wc.cuda(), a.cuda(), b.cuda(), A_log.cuda(),
+                                    dt_bias.cuda(), hd, z.cuda(), hqk, d, hv,
+                                    weight=None if w is None else w.cuda(), weight_offset=off,
+                                    conv_bias=None if bc is None else bc.cuda(), scale=0.7,
+                                    out_dtype=_DT[odt])
+        torch.cuda.synchronize()
+        ro, rh, rwin = _decode_oracle(x, win, wc, bc, a, b, A_log, dt_bias, h0, hqk, hv, d,
+                                      scale=0.7)
+        ref = oracle.gated_rmsnorm(ro, f64(z), f64(w), off, 1e-6)
+        check = assert_rms_close_rounded_out if odt == "bf16" else assert_rms_close
+        check(out, ref, TOL["f32"], "gated decode out")
+        scheck = assert_rms_close_rounded_out if sdt == "bf16" else assert_rms_close
+        scheck(hd.cpu(), rh, TOL["f32"], "gated decode state")
+        assert np.array_equal(f64(wd), rwin)
+
+
+def test_decode_step_gated_full_size_sampled():
+    """The benchmark's shape (256 sequences, 16 QK / 32 V heads, d = 128, bf16, fp32 state):
+    the fused gated step equals the fused step followed by the gate kernel to fp32 rounding on
+    every row, and the oracle on 6 sampled sequences."""
+    rng = np.random.default_rng(1234)
+    N, hqk, hv, d = 256, 16, 32, 128
+    x, win, wc, bc, a, b, A_log, dt_bias = _front(rng, N, hqk, hv, d, torch.bfloat16, bias=False)
+    h0 = _rand(rng, (N, hv, d, d), torch.float32, 0.02)
+    z, w, off = _gate_inputs(rng, N, hv, d, "bf16", "plus1")
+    dev = [t.cuda() for t in (x, win, wc, a, b, A_log, dt_bias, h0, z, w)]
+    xd, w1, wcd, ad, bd, Ad, dtd, s1, zd, wd = dev
+    w2, s2 = w1.clone(), s1.clone()
+    out1 = gdn.decode_step_gated(xd, w1, wcd, ad, bd, Ad, dtd, s1, zd, hqk, d, hv, weight=wd,
+                                 weight_offset=off, out_dtype=torch.float32)
+    o2 = gdn.decode_step(xd, w2, wcd, ad, bd, Ad, dtd, s2, hqk, d, hv, out_dtype=torch.float32)
+    out2 = gdn.gated_rmsnorm(o2, zd, wd, off, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(w1, w2)
+    assert_rms_close(out1.cpu(), f64(out2), 1e-5, "fused gated vs step + gate (all rows)")
+    seqs = rng.choice(N, size=6, replace=False)
+    ro, rh, _ = _decode_oracle(x[seqs], win[seqs], wc, None, a[seqs], b[seqs], A_log, dt_bias,
+                               h0[seqs], hqk, hv, d)
+    ref = oracle.gated_rmsnorm(ro, f64(z[seqs]), f64(w), off, 1e-6)
+    assert_rms_close(out1.cpu()[torch.from_numpy(seqs)], ref, TOL["f32"],
+                     "gated decode out, sampled sequences")
