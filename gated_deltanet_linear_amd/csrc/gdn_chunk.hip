@@ -62,31 +62,15 @@ __device__ __forceinline__ f32x8 row_frag<F32Mode, 512>(const char* b, int r, in
   return afrag_f32<512>(b, r, kb, g);
 }
 
-// Half fragment (slots 4*half .. +3) of a stored operand block in global memory, split like
-// Mode::make.
-__device__ __forceinline__ void store_half_global(Bf16Mode, char* blk, int lane, int half,
-                                                  const f32x4& x) {
-  bf16x4 hi, lo;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    hi[e] = (bf16)x[e];
-    lo[e] = (bf16)(x[e] - (float)hi[e]);
-  }
-  *reinterpret_cast<bf16x4*>(blk + lane * 16 + half * 8) = hi;
-  *reinterpret_cast<bf16x4*>(blk + 1024 + lane * 16 + half * 8) = lo;
-}
-__device__ __forceinline__ void store_half_global(F32Mode, char* blk, int lane, int half,
-                                                  const f32x4& x) {
-  *reinterpret_cast<f32x4*>(blk + lane * 32 + half * 16) = x;
-}
-
 // One workgroup per (chunk slot, group of NV V heads of one QK head): NV = 2 when the heads per
 // QK head come in pairs, else 1. K K^T and Q K^T of the chunk's QK head are formed once and
 // serve the NV heads, whose gates, decay masks, inverses and records are worked on side by side
 // by 4 waves each. T = (I + A)^-1 overwrites A in place, so that NV heads need the LDS of the
 // staged q/k rows, or of one 64x64 fp32 matrix per head, whichever is larger.
 template <typename Mode, int DK, int NV>
-__global__ __launch_bounds__(256 * NV) void chunk_intra_kernel(IntraParams p) {
+__global__ __launch_bounds__(256 * NV)
+__attribute__((amdgpu_waves_per_eu(sizeof(typename Mode::in_t) == 4 && DK == 128 && NV == 1 ? 2 : 4)))
+void chunk_intra_kernel(IntraParams p) {
   using in_t = typename Mode::in_t;
   using frag_t = typename Mode::frag_t;
   constexpr int NWV = 4 * NV;  // waves
@@ -155,19 +139,20 @@ __global__ __launch_bounds__(256 * NV) void chunk_intra_kernel(IntraParams p) {
   }
   lds_barrier();
 
-  // ---- 20 tile products: the A tiles on the first half of the waves, the P tiles on the
-  // second half (wave w of a half: its jobs w, w + NWV / 2, ...). Both kinds are formed
-  // transposed (C = K_ct X_rt^T), so that a lane holds 4 consecutive columns of one row of the
-  // wanted tile:
-  //   0..9   A tiles (tr >= tc): A_tj = beta_t e^{b_t - b_j} (k_t . k_j) for j < t, into LDS;
-  //   10..19 P^T tiles: C = K_ct Q_rt^T, whose C fragment IS half of the stored A fragment of
-  //          P = (Q K^T) o Gamma o lower-incl (block (rt, ct / 2), slots 4 (ct % 2) + r).
-  // The zero halves of the diagonal P blocks (ct = rt + 1 for rt = 0, 2) are stored directly.
+  // ---- 20 tile products: the 10 A tiles on the first half of the waves (wave w of the half:
+  // tiles w, w + NWV / 2, ...), the 10 P tiles on the second half, which owns whole stored P
+  // blocks. Both kinds are formed transposed (C = K_ct X_rt^T), so that a lane holds 4
+  // consecutive columns of one row of the wanted tile:
+  //   A tiles (rt >= ct): A_tj = beta_t e^{b_t - b_j} (k_t . k_j) for j < t, into LDS;
+  //   P^T tiles: C = K_ct Q_rt^T, whose C fragment IS half of the stored A fragment of
+  //   P = (Q K^T) o Gamma o lower-incl: block (rt, kb) holds tiles ct = 2 kb (slots 0-3) and
+  //   2 kb + 1 (slots 4-7; zeros where ct > rt), written as whole 16-byte fragments.
   // The products run first; waves 0 .. NV - 1 form their head's gate cumsum meanwhile. After
   // one barrier the first half writes the A tiles of all NV heads to LDS while the second half
   // writes the P blocks to the workspace.
   constexpr int HW = NWV / 2;                 // waves per half
-  constexpr int NJ = (10 + HW - 1) / HW;      // jobs per wave
+  constexpr int NJ = (10 + HW - 1) / HW;      // A tiles per wave
+  constexpr int NPB = NV == 2 ? 2 : 3;        // P blocks per wave
   const bool pw = wave >= HW;                 // P-tile wave
   const int wj = pw ? wave - HW : wave;       // index inside the half
   const char* sK = sKQ;
@@ -176,29 +161,53 @@ __global__ __launch_bounds__(256 * NV) void chunk_intra_kernel(IntraParams p) {
     r1 = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // row tile
     r2 = tt - r1 * (r1 + 1) / 2;                        // column tile (<= r1)
   };
-  f32x4 acc[NJ];
-#pragma unroll
-  for (int i = 0; i < NJ; ++i) {
-    const int tt = wj + HW * i;
-    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tt < 10) {
-      int r1, r2;
-      job_tiles(tt, r1, r2);
-      // Rows r2 of K against rows r1 of K (A^T tiles) or of Q (P^T tiles).
-      const int ra = 16 * r2 + idx;
-      const int rb = 16 * r1 + idx;
-      const char* bsrc = pw ? sQ : sK;
-      frag_t fa[KB], fb[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        fa[kb] = row_frag<Mode, ROWB>(sK, ra, kb, grp);
-        fb[kb] = row_frag<Mode, ROWB>(bsrc, rb, kb, grp);
-      }
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) c = mma32(fa[kb], fb[kb], c);
-      acc[i] = c;
+  // P block i of P wave wj (tri_block numbering), -1 for none: whole blocks split as evenly as
+  // they allow (NV = 2: 3, 3, 2, 2 tiles; NV = 1: 5 and 5 tiles)
+  auto pblock = [](int w, int i) -> int {
+    if constexpr (NV == 2) {
+      if (i == 0) return w == 0 ? 4 : w == 1 ? 5 : w == 2 ? 2 : 1;
+      return w == 0 ? 0 : w == 1 ? 3 : -1;
+    } else {
+      if (i == 0) return w == 0 ? 4 : 5;
+      if (i == 1) return w == 0 ? 0 : 2;
+      return w == 0 ? 3 : 1;
     }
+  };
+  auto block_rt = [](int bl) { return bl < 2 ? bl : 2 + (bl - 2) / 2; };
+  auto block_kb = [](int bl) { return bl < 2 ? 0 : (bl - 2) % 2; };
+  // C = K_{rows 16 ra_t} X_{rows 16 rb_t}^T over d_k
+  auto tile_product = [&](int ra_t, int rb_t, const char* bsrc) {
+    frag_t fa[KB], fb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      fa[kb] = row_frag<Mode, ROWB>(sK, 16 * ra_t + idx, kb, grp);
+      fb[kb] = row_frag<Mode, ROWB>(bsrc, 16 * rb_t + idx, kb, grp);
+    }
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) c = mma32(fa[kb], fb[kb], c);
+    return c;
+  };
+  // One product loop for both kinds: job j of an A wave is A tile wj + HW j; job j of a P wave
+  // is tile j % 2 of its P block j / 2.
+  constexpr int NJM = NJ > 2 * NPB ? NJ : 2 * NPB;
+  f32x4 acc[NJM];
+#pragma unroll
+  for (int i = 0; i < NJM; ++i) {
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int ra_t = 0, rb_t = 0;
+    bool ok;
+    if (!pw) {
+      const int tt = wj + HW * i;
+      ok = i < NJ && tt < 10;
+      if (ok) job_tiles(tt, rb_t, ra_t);  // rows ra_t = column tile of K, rb_t = row tile of K
+    } else {
+      const int bl = i / 2 < NPB ? pblock(wj, i / 2) : -1;
+      ra_t = bl >= 0 ? 2 * block_kb(bl) + (i & 1) : 0;  // K rows: column tile ct
+      rb_t = bl >= 0 ? block_rt(bl) : 0;                 // Q rows: row tile rt
+      ok = bl >= 0 && ra_t <= rb_t;
+    }
+    if (ok) acc[i] = tile_product(ra_t, rb_t, pw ? sQ : sK);
   }
   if (wave < NV) {
     const float cs = wave_inclusive_scan(gate_g, lane);
@@ -209,25 +218,19 @@ __global__ __launch_bounds__(256 * NV) void chunk_intra_kernel(IntraParams p) {
     reinterpret_cast<float*>(rec(wave) + kWsDOff)[lane] = __expf(cl - cs);
   }
   lds_barrier();  // sb, sbeta ready; every wave is done with the staged rows (sA may overwrite)
-  if (pw && wj < 2 * NV) {
-    const int v = wj >> 1, rt = (wj & 1) ? 2 : 0;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    store_half_global(Mode{}, rec(v) + kWsPOff + tri_block(rt, rt / 2) * kWsBlockBytes, lane, 1, z);
-  }
+  if (!pw) {
 #pragma unroll
-  for (int i = 0; i < NJ; ++i) {
-    const int tt = wj + HW * i;
-    if (tt >= 10) continue;
-    int r1, r2;
-    job_tiles(tt, r1, r2);
-    // lane: row t = 16 r1 + idx, columns j = 16 r2 + 4 grp + r (one 16-byte access)
-    const int t = 16 * r1 + idx;
+    for (int i = 0; i < NJ; ++i) {
+      const int tt = wj + HW * i;
+      if (tt >= 10) continue;
+      int r1, r2;
+      job_tiles(tt, r1, r2);
+      // lane: row t = 16 r1 + idx, columns j = 16 r2 + 4 grp + r (one 16-byte access)
+      const int t = 16 * r1 + idx;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const float bt = sb[v][t];
-      const f32x4 bj = *reinterpret_cast<const f32x4*>(&sb[v][16 * r2 + 4 * grp]);
-      if (!pw) {
-        const float bet = sbeta[v][t];
+      for (int v = 0; v < NV; ++v) {
+        const float bt = sb[v][t], bet = sbeta[v][t];
+        const f32x4 bj = *reinterpret_cast<const f32x4*>(&sb[v][16 * r2 + 4 * grp]);
         f32x4 av;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -235,15 +238,30 @@ __global__ __launch_bounds__(256 * NV) void chunk_intra_kernel(IntraParams p) {
           av[r] = jc < t ? bet * __expf(bt - bj[r]) * acc[i][r] : 0.f;
         }
         *reinterpret_cast<f32x4*>(sA(v) + t * kLd + 16 * r2 + 4 * grp) = av;
-      } else {
-        f32x4 pv;
+      }
+    }
+  } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jc = 16 * r2 + 4 * grp + r;
-          pv[r] = jc <= t ? __expf(bt - bj[r]) * acc[i][r] : 0.f;
+    for (int i = 0; i < NPB; ++i) {
+      const int bl = pblock(wj, i);
+      if (bl < 0) continue;
+      const int rt = block_rt(bl), kb = block_kb(bl);
+      const int t = 16 * rt + idx;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float bt = sb[v][t];
+        float x[8];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int ct = 2 * kb + hf;
+          const f32x4 bj = *reinterpret_cast<const f32x4*>(&sb[v][16 * ct + 4 * grp]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jc = 16 * ct + 4 * grp + r;
+            x[4 * hf + r] = jc <= t ? __expf(bt - bj[r]) * acc[2 * i + hf][r] : 0.f;
+          }
         }
-        store_half_global(Mode{}, rec(v) + kWsPOff + tri_block(r1, r2 >> 1) * kWsBlockBytes,
-                          lane, r2 & 1, pv);
+        Mode::store_block(rec(v) + kWsPOff + bl * kWsBlockBytes, lane, Mode::make(x));
       }
     }
   }
