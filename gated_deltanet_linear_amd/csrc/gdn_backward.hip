@@ -192,8 +192,8 @@ __device__ __forceinline__ bool slot_chunk(const BwdParams& p, int slot, int& n,
 }
 
 // ---- bwd_intra ------------------------------------------------------------------------------
-// One workgroup of 4 waves per (chunk slot, V head); the G workgroups of a (chunk slot, QK head)
-// run back to back on one XCD (their q/k rows come from its L2). The chunk's q/k rows are staged
+// One workgroup of 4 waves per (chunk slot, V head); the H_v workgroups of a chunk slot run back
+// to back on one XCD (the q/k rows of a QK head and the gate lines come from its L2). The chunk's q/k rows are staged
 // in LDS (rows past the end as zeros); the 20 lower 16x16 tiles of K K^T and Q K^T are formed
 // transposed (C = K_ct X_rt^T, so a lane holds 4 consecutive columns of one row and writes
 // them with one 16-byte store); then T = (I + diag(beta) At)^-1 in place of the staged rows.
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(BwdParams p) {
   float* const sM = reinterpret_cast<float*>(sKQ);
 
   const int G = p.hv / p.hqk;
-  const int j = blockIdx.x >> 3, unit = 8 * (j / G) + (blockIdx.x & 7);
-  const int slot = unit / p.hqk, m = unit % p.hqk, h = m * G + j % G;
+  const int j = blockIdx.x >> 3, per_slot = p.hqk * G;
+  const int slot = 8 * (j / per_slot) + (blockIdx.x & 7), h = j % per_slot, m = h / G;
   int n, t0, L;
   if (slot >= p.num_slots || !slot_chunk(p, slot, n, t0, L)) return;
   const int tid = threadIdx.x, lane = tid & 63, idx = lane & 15, grp = lane >> 4;
@@ -1198,10 +1198,9 @@ inline BwdLayout bwd_layout(const gdn_shape_t& s) {
 
 template <typename InT, typename OT, int D>
 hipError_t launch_bwd_t(const gdn_shape_t& s, BwdParams p, hipStream_t stream) {
-  // (chunk slot, QK head) units dealt to the 8 XCDs round robin, the G V heads of a unit back to
-  // back on one XCD
-  const unsigned intra_blocks =
-      (unsigned)(8 * (p.hv / p.hqk) * (((long long)p.num_slots * p.hqk + 7) / 8));
+  // chunk slots dealt to the 8 XCDs round robin, the H_v workgroups of a slot back to back on
+  // its XCD (a token's gates share a cache line; a QK head's G V heads share its q/k rows)
+  const unsigned intra_blocks = (unsigned)(8 * p.hv * (((long long)p.num_slots + 7) / 8));
   const unsigned slot_blocks_qk = (unsigned)(p.num_slots * p.hqk);
   const unsigned scan_blocks = (unsigned)(8 * (D / 16) * ((s.num_seqs * s.num_v_heads + 7) / 8));
   if (s.total_tokens > 0) {

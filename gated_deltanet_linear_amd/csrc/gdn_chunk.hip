@@ -86,12 +86,13 @@ void chunk_intra_kernel(IntraParams p) {
   __shared__ __attribute__((aligned(16))) float sbeta[NV][64];
   auto sA = [&](int v) { return reinterpret_cast<float*>(sKQ + v * TBYTES); };
 
-  // Work assignment: units (chunk slot, QK head) are dealt to the 8 XCDs round robin (the
-  // hardware deals workgroups b to XCD b % 8); the G / NV workgroups of a unit (its V-head
-  // groups, which read the same q/k rows) are dispatched back to back on one XCD and share its L2.
+  // Work assignment: chunk slots are dealt to the 8 XCDs round robin (the hardware deals
+  // workgroups b to XCD b % 8) and all H_qk * G / NV workgroups of a slot run back to back on its
+  // XCD: the gates of a token (all V heads in one cache line) and the q/k rows of a QK head (read
+  // by its G / NV workgroups) come from that XCD's L2.
   const int G = p.hv / p.hqk, NG = G / NV;
-  const int j = blockIdx.x >> 3, unit = 8 * (j / NG) + (blockIdx.x & 7);
-  const int slot = unit / p.hqk, m = unit % p.hqk, hb = m * G + (j % NG) * NV;
+  const int j = blockIdx.x >> 3, per_slot = p.hqk * NG, r_ = j % per_slot;
+  const int slot = 8 * (j / per_slot) + (blockIdx.x & 7), m = r_ / NG, hb = m * G + (r_ % NG) * NV;
   if (slot >= p.num_slots) return;  // padding workgroup (uniform)
   const int n = slot_to_seq(p.cu, p.num_seqs, slot);
   const int t0 = p.cu[n] + kChunk * (slot - slot_base(p.cu, n));
@@ -299,11 +300,12 @@ template <typename Mode, int D>
 hipError_t launch_intra_t(const gdn_shape_t& s, const IntraParams& p, hipStream_t stream) {
   const long long slots = chunk_slots(s);
   if (slots <= 0 || s.total_tokens == 0) return hipSuccess;
-  const long long units = slots * s.num_qk_heads, G = s.num_v_heads / s.num_qk_heads;
+  const long long G = s.num_v_heads / s.num_qk_heads;
   IntraParams q = p;
   q.num_slots = (int)slots;
   // one workgroup per (unit, pair of V heads) when G is even, else per (unit, V head)
-  const unsigned blocks = (unsigned)(8 * ((G % 2 == 0) ? G / 2 : G) * ((units + 7) / 8));
+  const unsigned blocks =
+      (unsigned)(8 * s.num_qk_heads * ((G % 2 == 0) ? G / 2 : G) * ((slots + 7) / 8));
   if (G % 2 == 0)
     hipLaunchKernelGGL((chunk_intra_kernel<Mode, D, 2>), dim3(blocks), dim3(512), 0, stream, q);
   else
