@@ -401,7 +401,8 @@ def run_decode_front(torch, gdn, si, steps, warmup):
                                               "gdn_decode_step_decode_front_256x1_bf16_state")),
                 gated=dict(ms_per_step=ms4, tokens_per_s=N / (ms4 / 1e3), kernels_ms=kms4,
                            roofline=_hbm("gdn_decode_step_gated", Bfused + N * hv * dv * e + dv * 4,
-                                         kms4["gdn_decode_step_gated"]),
+                                         kms4["gdn_decode_step_gated"],
+                                         "gdn_decode_step_gated_decode_front_256x1"),
                            unfused=dict(ms_per_step=ms5, tokens_per_s=N / (ms5 / 1e3),
                                         kernels_ms=kms5)),
                 two_call=dict(ms_per_step=ms2, tokens_per_s=N / (ms2 / 1e3), kernels_ms=kms2,
