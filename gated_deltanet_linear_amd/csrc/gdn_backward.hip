@@ -53,15 +53,6 @@ __device__ __forceinline__ const double* rec_b(const float* rec) {
   return reinterpret_cast<const double*>(rec + 3 * kC * kC);
 }
 
-__device__ __forceinline__ double wave_inclusive_scan_f64(double x, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const double y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
 struct BwdParams {
   const int32_t* cu;
   const void* q;

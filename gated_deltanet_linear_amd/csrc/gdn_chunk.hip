@@ -16,8 +16,9 @@
 // head). It forms K K^T and the masked decayed Q K^T on MFMA (the decay and beta applied on
 // the fly to the result fragments), inverts the unit-lower-triangular I + A (16x16 diagonal
 // blocks by substitution, off-diagonal blocks by two levels of 16x16 fp32 MFMA products) and
-// writes T diag(beta), P (as ready-made MFMA A fragments), e^{b_t} and e^{b_C - b_t} to the
-// workspace. The sequential half, chunk_scan, is in gdn_scan.hip.
+// writes T diag(beta), scale P (as ready-made MFMA A fragments; the output scale is applied
+// here, where the kernel waits on memory, and to the Q H term by the scan), e^{b_t} and
+// e^{b_C - b_t} to the workspace. The sequential half, chunk_scan, is in gdn_scan.hip.
 #include "gdn_device.hpp"
 #include "gdn_internal.h"
 
@@ -33,6 +34,7 @@ struct IntraParams {
   const float* beta;
   char* ws;
   int num_seqs, hqk, hv, num_slots;
+  float scale;  // the output scale, folded into P
 };
 
 template <typename Mode, int ROWB>
@@ -82,7 +84,9 @@ void chunk_intra_kernel(IntraParams p) {
   // Staged q/k rows; once the K K^T / Q K^T products are in registers the same bytes hold the
   // heads' A (then T) matrices.
   __shared__ __attribute__((aligned(1024))) char sKQ[SBYTES];
-  __shared__ __attribute__((aligned(16))) float sb[NV][64];
+  // In-chunk gate cumsums in fp64: model gates sum to hundreds over a chunk, where an fp32 b
+  // carries absolute errors of ~1e-4 into every decay e^{b_t - b_j} and e^{b_C - b_t}.
+  __shared__ __attribute__((aligned(16))) double sb[NV][64];
   __shared__ __attribute__((aligned(16))) float sbeta[NV][64];
   auto sA = [&](int v) { return reinterpret_cast<float*>(sKQ + v * TBYTES); };
 
@@ -211,12 +215,12 @@ void chunk_intra_kernel(IntraParams p) {
     if (ok) acc[i] = tile_product(ra_t, rb_t, pw ? sQ : sK);
   }
   if (wave < NV) {
-    const float cs = wave_inclusive_scan(gate_g, lane);
-    const float cl = __shfl(cs, kChunk - 1, kWave);  // b_C (identity steps keep it at b_{len-1})
+    const double cs = wave_inclusive_scan_f64(gate_g, lane);
+    const double cl = __shfl(cs, kChunk - 1, kWave);  // b_C (identity steps keep it at b_{len-1})
     sb[wave][lane] = cs;
     sbeta[wave][lane] = gate_b;
-    reinterpret_cast<float*>(rec(wave) + kWsGOff)[lane] = __expf(cs);
-    reinterpret_cast<float*>(rec(wave) + kWsDOff)[lane] = __expf(cl - cs);
+    reinterpret_cast<float*>(rec(wave) + kWsGOff)[lane] = __expf((float)cs);
+    reinterpret_cast<float*>(rec(wave) + kWsDOff)[lane] = __expf((float)(cl - cs));
   }
   lds_barrier();  // sb, sbeta ready; every wave is done with the staged rows (sA may overwrite)
   if (!pw) {
@@ -230,13 +234,14 @@ void chunk_intra_kernel(IntraParams p) {
       const int t = 16 * r1 + idx;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const float bt = sb[v][t], bet = sbeta[v][t];
-        const f32x4 bj = *reinterpret_cast<const f32x4*>(&sb[v][16 * r2 + 4 * grp]);
+        const double bt = sb[v][t];
+        const float bet = sbeta[v][t];
+        const f64x4 bj = ld_f64x4(&sb[v][16 * r2 + 4 * grp]);
         f32x4 av;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int jc = 16 * r2 + 4 * grp + r;
-          av[r] = jc < t ? bet * __expf(bt - bj[r]) * acc[i][r] : 0.f;
+          av[r] = jc < t ? bet * __expf((float)(bt - bj[r])) * acc[i][r] : 0.f;
         }
         *reinterpret_cast<f32x4*>(sA(v) + t * kLd + 16 * r2 + 4 * grp) = av;
       }
@@ -250,16 +255,17 @@ void chunk_intra_kernel(IntraParams p) {
       const int t = 16 * rt + idx;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const float bt = sb[v][t];
+        const double bt = sb[v][t];
         float x[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int ct = 2 * kb + hf;
-          const f32x4 bj = *reinterpret_cast<const f32x4*>(&sb[v][16 * ct + 4 * grp]);
+          const f64x4 bj = ld_f64x4(&sb[v][16 * ct + 4 * grp]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int jc = 16 * ct + 4 * grp + r;
-            x[4 * hf + r] = jc <= t ? __expf(bt - bj[r]) * acc[2 * i + hf][r] : 0.f;
+            x[4 * hf + r] =
+                jc <= t ? __expf((float)(bt - bj[r])) * (p.scale * acc[2 * i + hf][r]) : 0.f;
           }
         }
         Mode::store_block(rec(v) + kWsPOff + bl * kWsBlockBytes, lane, Mode::make(x));
@@ -329,7 +335,7 @@ hipError_t launch_chunk_intra(const gdn_shape_t& s, const int32_t* cu, const voi
                               const void* k, const float* g, const float* beta, void* ws,
                               hipStream_t stream) {
   IntraParams p{cu, q, k, g, beta, static_cast<char*>(ws), s.num_seqs, s.num_qk_heads,
-                s.num_v_heads, 0};
+                s.num_v_heads, 0, s.scale};
   if (s.qkv_dtype == GDN_DTYPE_BF16) return launch_intra_d<Bf16Mode>(s, p, stream);
   return launch_intra_d<F32Mode>(s, p, stream);
 }

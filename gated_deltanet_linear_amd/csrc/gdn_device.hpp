@@ -247,6 +247,24 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   }
   return x;
 }
+// 4 consecutive doubles (32 bytes, two 16-byte accesses)
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+struct f64x4 {
+  double v[4];
+  __device__ double operator[](int i) const { return v[i]; }
+};
+__device__ __forceinline__ f64x4 ld_f64x4(const double* p) {
+  const f64x2 a = *reinterpret_cast<const f64x2*>(p), b = *reinterpret_cast<const f64x2*>(p + 2);
+  return f64x4{{a[0], a[1], b[0], b[1]}};
+}
+__device__ __forceinline__ double wave_inclusive_scan_f64(double x, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
 
 // Workspace record of one (chunk slot, V head), written by the intra kernel and read by the
 // scan kernel. Both matrices are stored as the A operands of 64x64 @ 64x16 products: six

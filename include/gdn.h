@@ -157,7 +157,7 @@ gdn_status_t gdn_chunk_forward_noalloc(const gdn_shape_t* shape, const int32_t* 
  * unit-lower-triangular inverse (I + A)^-1 and the masked decayed Q K^T) into the workspace.
  * gdn_chunk_scan then runs the sequential cross-chunk recurrence (Steps 5-7) from it. The
  * workspace contents between the two calls are private to the library; scan must use the same
- * shape, cu_seqlens, q, k, g and beta as the intra call that filled it. Alignment as for
+ * shape (its scale included), cu_seqlens, q, k, g and beta as the intra call that filled it. Alignment as for
  * gdn_chunk_forward (q, k, v, o 16 bytes; workspace 256 bytes).
  */
 gdn_status_t gdn_chunk_intra(const gdn_shape_t* shape, const int32_t* cu_seqlens,

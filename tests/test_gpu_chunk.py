@@ -233,6 +233,32 @@ def test_scan_batch_invariance_across_layouts(dt, dd):
     assert_rms_close(h32, h_ref, TOL[dt], f"{dt} d={dd} final state")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_scale_across_layouts(dt):
+    """The output scale (folded into the workspace's masked Q K^T and into the Q H term) on both
+    scan layouts: three sequences alone (row-split layout) and followed by 70 fillers (one wave
+    per tile; for bf16 q/k/v the many-chain kernel) agree bit for bit at scale 0.37, and the
+    small run meets the oracle's scaled output; the final states do not depend on the scale."""
+    base = si.make_core_case([300, 64, 5], 2, 4, 128, 128, dtype=dt, gate="model", h0_std=0.02,
+                             seed=131)
+    T0 = int(base.cu_seqlens[-1])
+    runs = {}
+    for fill in (0, 70):
+        case = base if fill == 0 else _concat_cases(
+            base, si.make_core_case([64] * fill, 2, 4, 128, 128, dtype=dt, gate="model",
+                                    h0_std=0.02, seed=600 + fill))
+        d = to_dev(case)
+        print(f"scale case {dt} fillers={fill}", flush=True)
+        o, h = gdn.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                 initial_state=d["h0"], scale=0.37, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        runs[fill] = (o[:T0].cpu(), h[:3].cpu())
+    assert torch.equal(runs[0][0], runs[70][0]) and torch.equal(runs[0][1], runs[70][1]), dt
+    o_ref, h_ref = oracle_case(base)
+    assert_rms_close(runs[0][0], 0.37 * o_ref, TOL[dt], f"{dt} scale 0.37 o")
+    assert_rms_close(runs[0][1], h_ref, TOL[dt], f"{dt} scale 0.37 final state")
+
+
 def test_binding_output_buffers_follow_the_given_tensor():
     """A caller-provided o decides the output dtype when out_dtype is not given (fp32 q/k/v with
     a bf16 o writes bf16, the rounded fp32 result); an o, final state or workspace that does not
