@@ -480,10 +480,12 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
   // O^T = H^T Q^T diag(scale gamma) + V'^T (scale P)^T, computed transposed so that lane
   // (idx = token, grp) holds 4 consecutive columns of its token's output row and stores them
   // directly (the workspace holds P already multiplied by the scale).
-  OutT* Oh = static_cast<OutT*>(p.o) + (size_t)h * D + col0 + 4 * grp;
+  // this lane's output row (token idx of the chunk) advances by whole chunks and row tiles
+  const size_t orow = (size_t)p.hv * D;  // elements between token rows
+  OutT* Oh = static_cast<OutT*>(p.o) + (size_t)(start + idx) * orow + (size_t)h * D + col0 + 4 * grp;
   if (nchunks > 0) lds_barrier();  // B(0)
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0c = start + kChunk * c, len = min(kChunk, L - kChunk * c);
+  for (int c = 0; c < nchunks; ++c, Oh += kChunk * orow) {
+    const int len = min(kChunk, L - kChunk * c);
     f16x8 HB[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) HB[kb] = Half::load_block(HX + kb * 1024, lane);
@@ -518,8 +520,7 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
 #pragma unroll
       for (int kb = 0; kb <= (rt >> 1); ++kb)
         acc = M::mma_ss_t(acc, VB[kb], PB[tri_block(rt, kb)]);
-      if (16 * rt + idx < len)
-        store4<OutT>(Oh + (size_t)(t0c + 16 * rt + idx) * p.hv * D, acc);
+      if (16 * rt + idx < len) store4<OutT>(Oh + 16 * rt * orow, acc);
     }
     if (c + 1 < nchunks) lds_barrier();  // B(c + 1)
   }
