@@ -526,9 +526,9 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
 
     // (b) K H, Q H on this wave's row tiles; Y = V - gamma K H, scale gamma Q H.
     // The K / Q fragments of a row tile are read before its products (and, for bf16, those
-    // of the next row tile while these run), so LDS latency overlaps the MFMA chains. One
-    // accumulator per product, depth blocks in order: the many-chain kernel accumulates in the
-    // same order, so the two layouts give the same bits.
+    // of the next row tile while these run), so LDS latency overlaps the MFMA chains. Two
+    // accumulators per product (even / odd depth blocks) halve the dependent chains; the
+    // many-chain kernel accumulates in the same order, so the two layouts give the same bits.
     using frag_t = typename Mode::frag_t;
     // fp32 operands over four row tiles leave no registers for reading ahead.
     constexpr bool EARLY = !(std::is_same<Mode, F32Mode>::value && R > 1);
@@ -549,20 +549,21 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       if (EARLY && KQB == 1 && i > 0) load_kq(0, rt);
       const f32x4 v4 = VRows<in_t>::cfrag(sV + 16 * rt * C::VSTR, C::VSTR, lane);
       const f32x4 gam = gamma4(rt);
-      f32x4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
+      f32x4 kh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      f32x4 qh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const frag_t kf = EARLY ? ka[b][kb] : F::a(sK, 16 * rt + idx, kb, grp);
         const frag_t qf = EARLY ? qa[b][kb] : F::a(sQ, 16 * rt + idx, kb, grp);
-        kh = SO::mma(kh, kf, HB[kb]);
-        qh = SO::mma(qh, qf, HB[kb]);
+        kh[kb & 1] = SO::mma(kh[kb & 1], kf, HB[kb]);
+        qh[kb & 1] = SO::mma(qh[kb & 1], qf, HB[kb]);
       }
       if (KQB > 1 && i + 1 < R) load_kq(b ^ 1, rt + 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float vr = 16 * rt + 4 * grp + r < len ? v4[r] : 0.f;
-        Y[i][r] = vr - gam[r] * kh[r];
-        QH[i][r] = qh[r] * (gam[r] * p.scale);
+        Y[i][r] = vr - gam[r] * (kh[0][r] + kh[1][r]);
+        QH[i][r] = (qh[0][r] + qh[1][r]) * (gam[r] * p.scale);
       }
     }
 

@@ -381,9 +381,9 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
         f16x8 kf[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) kf[kb] = hfrag(sK, 16 * rt + idx, kb);
-        f32x4 kh = {0.f, 0.f, 0.f, 0.f};
+        f32x4 kh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kh = Half::mma(kf[kb], HB[kb], kh);
+        for (int kb = 0; kb < KB; ++kb) kh[kb & 1] = Half::mma(kf[kb], HB[kb], kh[kb & 1]);
         const int vg = lane >> 4, vs = lane & 15, va = vs & 3, ve = vs >> 2;
         const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(sV + (16 * rt + 4 * vg + ve) * C::VSTR + 8 * va));
@@ -393,7 +393,7 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
         // and columns of T diag(beta) past the end are zero (identity steps, beta = 0), so these
         // rows add exactly 0 to V' and V' is 0 there.
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Y[rt][r] = (float)vb[r] - gam[r] * kh[r];
+        for (int r = 0; r < 4; ++r) Y[rt][r] = (float)vb[r] - gam[r] * (kh[0][r] + kh[1][r]);
       }
       // Operands of the later phases are read into registers ahead of the barrier that precedes
       // their use, so that their LDS latency overlaps the wait (a read just before its MFMAs
@@ -495,10 +495,10 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
       f16x8 qf[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) qf[kb] = hfrag(sQ, 16 * rt + idx, kb);
-      f32x4 qh = {0.f, 0.f, 0.f, 0.f};
+      f32x4 qh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qh = Half::mma(HB[kb], qf[kb], qh);
-      QH[rt] = qh * (sgam[16 * rt + idx] * p.scale);
+      for (int kb = 0; kb < KB; ++kb) qh[kb & 1] = Half::mma(HB[kb], qf[kb], qh[kb & 1]);
+      QH[rt] = (qh[0] + qh[1]) * (sgam[16 * rt + idx] * p.scale);
     }
     lds_barrier();  // M(c)
     Op PB[6];  // staged before M(c); read ahead of X(c) so that the wait covers their latency
