@@ -465,7 +465,7 @@ def run_backward(torch, gdn, si, steps, warmup):
                                    "MFMA; priced against the bf16 dense peak"))
 
 
-def cpu_baseline(case, budget_s=20.0, min_s=3.0):
+def cpu_baseline(case, budget_s=30.0, min_s=10.0):
     """The float64 oracle as it stands on this host, on whole (sequence, V head) chains of a
     prefill workload: chains are taken in order (sequence-major, all V heads of a sequence with
     their QK heads) in groups of one per thread until about min_s of work (or the budget) is
