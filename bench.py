@@ -80,13 +80,13 @@ def prefill_bytes(lengths, hqk, hv, dk, dv, e, h0_given, state_out=True):
 
 def scan_bytes(lengths, hqk, hv, dk, dv, e, h0_given, state_out=True, eo=None):
     """Algorithmic HBM bytes of one scan launch: q and k (each unique byte once), v (e bytes an
-    element), the workspace records the intra kernel wrote (25088 bytes per chunk and V head),
+    element), the workspace records the intra kernel wrote (20992 bytes per chunk and V head),
     the initial states, o (eo bytes an element, e unless given) and the final states."""
     T = sum(lengths)
     n = len(lengths)
     chunks = sum((L + C - 1) // C for L in lengths)
     eo = e if eo is None else eo
-    b = T * (hqk * 2 * dk * e + hv * dv * (e + eo)) + chunks * hv * 25088
+    b = T * (hqk * 2 * dk * e + hv * dv * (e + eo)) + chunks * hv * 20992
     b += n * hv * dk * dv * 4 * ((1 if state_out else 0) + (1 if h0_given else 0))
     return b
 

@@ -268,7 +268,7 @@ void chunk_intra_kernel(IntraParams p) {
                 jc <= t ? __expf((float)(bt - bj[r])) * (p.scale * acc[2 * i + hf][r]) : 0.f;
           }
         }
-        Mode::store_block(rec(v) + kWsPOff + bl * kWsBlockBytes, lane, Mode::make(x));
+        ws_store<Mode>(rec(v) + kWsPOff, bl, lane, Mode::make(x));
       }
     }
   }
@@ -295,7 +295,7 @@ void chunk_intra_kernel(IntraParams p) {
       const int jc = 32 * kb + kslot(gr, s);
       x[s] = jc <= t ? (s < 4 ? ta[s] * be0[s] : tb[s - 4] * be1[s - 4]) : 0.f;
     }
-    Mode::store_block(rec(v) + kWsTOff + bi * kWsBlockBytes, ln, Mode::make(x));
+    ws_store<Mode>(rec(v) + kWsTOff, bi, ln, Mode::make(x));
   }
 }
 

@@ -127,6 +127,37 @@ struct Bf16Mode {
     *reinterpret_cast<bf16x8*>(blk + lane * 16) = o.hi;
     *reinterpret_cast<bf16x8*>(blk + 1024 + lane * 16) = o.lo;
   }
+  // Half block (slots 4-7 zero): [hi slots 0-3 of 64 lanes][lo slots 0-3 of 64 lanes] = 1 KiB.
+  __device__ __forceinline__ static Op load_half(const char* blk, int lane) {
+    const bf16x4 h = *reinterpret_cast<const bf16x4*>(blk + lane * 8);
+    const bf16x4 l = *reinterpret_cast<const bf16x4*>(blk + 512 + lane * 8);
+    const bf16 z = (bf16)0.f;
+    Op o;
+    o.hi = bf16x8{h[0], h[1], h[2], h[3], z, z, z, z};
+    o.lo = bf16x8{l[0], l[1], l[2], l[3], z, z, z, z};
+    return o;
+  }
+  __device__ __forceinline__ static void store_half(char* blk, int lane, const Op& o) {
+    *reinterpret_cast<bf16x4*>(blk + lane * 8) = bf16x4{o.hi[0], o.hi[1], o.hi[2], o.hi[3]};
+    *reinterpret_cast<bf16x4*>(blk + 512 + lane * 8) = bf16x4{o.lo[0], o.lo[1], o.lo[2], o.lo[3]};
+  }
+  // A full or a half block without a branch: the same four 8-byte loads either way (for a half
+  // block the second of each pair reads the next lane's slots, or for lane 63 the first bytes
+  // after the block, and is replaced by zeros).
+  __device__ __forceinline__ static Op load_sel(const char* blk, int lane, bool half) {
+    const int st = half ? 8 : 16, lo = half ? 512 : 1024;
+    const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(blk + lane * st);
+    const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(blk + lane * st + 8);
+    const bf16x4 l0 = *reinterpret_cast<const bf16x4*>(blk + lo + lane * st);
+    const bf16x4 l1 = *reinterpret_cast<const bf16x4*>(blk + lo + lane * st + 8);
+    const uint64_t keep = half ? 0ull : ~0ull;
+    const bf16x4 h1k = __builtin_bit_cast(bf16x4, __builtin_bit_cast(uint64_t, h1) & keep);
+    const bf16x4 l1k = __builtin_bit_cast(bf16x4, __builtin_bit_cast(uint64_t, l1) & keep);
+    Op o;
+    o.hi = bf16x8{h0[0], h0[1], h0[2], h0[3], h1k[0], h1k[1], h1k[2], h1k[3]};
+    o.lo = bf16x8{l0[0], l0[1], l0[2], l0[3], l1k[0], l1k[1], l1k[2], l1k[3]};
+    return o;
+  }
 };
 
 // fp16 operands of the scan's two products with the state when q / k / v are bf16: K H and Q H.
@@ -224,6 +255,26 @@ struct F32Mode {
   __device__ __forceinline__ static void store_block(char* blk, int lane, const Op& o) {
     *reinterpret_cast<f32x8*>(blk + lane * 32) = o.v;
   }
+  // Half block (slots 4-7 zero): slots 0-3 of 64 lanes = 1 KiB.
+  __device__ __forceinline__ static Op load_half(const char* blk, int lane) {
+    const f32x4 h = *reinterpret_cast<const f32x4*>(blk + lane * 16);
+    Op o;
+    o.v = f32x8{h[0], h[1], h[2], h[3], 0.f, 0.f, 0.f, 0.f};
+    return o;
+  }
+  __device__ __forceinline__ static void store_half(char* blk, int lane, const Op& o) {
+    *reinterpret_cast<f32x4*>(blk + lane * 16) = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
+  }
+  // A full or a half block without a branch (as Bf16Mode::load_sel: two 16-byte loads).
+  __device__ __forceinline__ static Op load_sel(const char* blk, int lane, bool half) {
+    const int st = half ? 16 : 32;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(blk + lane * st);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(blk + lane * st + 16);
+    Op o;
+    o.v = f32x8{a[0], a[1], a[2], a[3], half ? 0.f : b[0], half ? 0.f : b[1], half ? 0.f : b[2],
+                half ? 0.f : b[3]};
+    return o;
+  }
 };
 
 // 8 values of a 32-deep B fragment from two C fragments (rows 0-15 and 16-31 of the depth).
@@ -268,16 +319,45 @@ __device__ __forceinline__ double wave_inclusive_scan_f64(double x, int lane) {
 
 // Workspace record of one (chunk slot, V head), written by the intra kernel and read by the
 // scan kernel. Both matrices are stored as the A operands of 64x64 @ 64x16 products: six
-// 32-deep blocks (row tile rt, depth block kb) with kb <= rt/2, 2 KiB each.
+// 32-deep blocks (row tile rt, depth block kb) with kb <= rt/2, block b = tri_block(rt, kb),
+// 2 KiB each in the fragment layout of the mode. Blocks 0 (rows 0-15, columns 0-31) and 3
+// (rows 32-47, columns 32-63) hold zeros in slots 4-7 of every lane (the 16 columns past the
+// diagonal tile of a lower-triangular matrix): they are stored as half blocks, slots 0-3 only.
 constexpr int kWsBlockBytes = 2048;
-constexpr int kWsTOff = 0;                      // T*diag(beta): 6 blocks
-constexpr int kWsPOff = 6 * kWsBlockBytes;      // masked decayed Q K^T: 6 blocks
-constexpr int kWsGOff = 12 * kWsBlockBytes;     // gamma_t = e^{b_t}: 64 fp32
-constexpr int kWsDOff = kWsGOff + 256;          // delta_t = e^{b_C - b_t}: 64 fp32
-constexpr int kWsRecordBytes = kWsDOff + 256;   // 25088 bytes
-
 __host__ __device__ constexpr int tri_block(int rt, int kb) {
   return rt < 2 ? rt : 2 + 2 * (rt - 2) + kb;
+}
+__host__ __device__ constexpr bool ws_half_block(int b) { return b == 0 || b == 3; }
+__host__ __device__ constexpr int ws_block_off(int b) {  // 0, 1024, 3072, 5120, 6144, 8192
+  return b * kWsBlockBytes - (b > 0 ? kWsBlockBytes / 2 : 0) - (b > 3 ? kWsBlockBytes / 2 : 0);
+}
+constexpr int kWsMatBytes = ws_block_off(6);    // 10240 bytes per matrix
+constexpr int kWsTOff = 0;                      // T*diag(beta)
+constexpr int kWsPOff = kWsMatBytes;            // masked decayed Q K^T (times the output scale)
+constexpr int kWsGOff = 2 * kWsMatBytes;        // gamma_t = e^{b_t}: 64 fp32
+constexpr int kWsDOff = kWsGOff + 256;          // delta_t = e^{b_C - b_t}: 64 fp32
+constexpr int kWsRecordBytes = kWsDOff + 256;   // 20992 bytes
+static_assert(kWsMatBytes == 10240 && kWsRecordBytes == 20992, "record layout");
+
+// Block b of a record matrix starting at `mat` (global memory or a verbatim LDS copy).
+template <typename M>
+__device__ __forceinline__ void ws_store(char* mat, int b, int lane, const typename M::Op& o) {
+  if (ws_half_block(b))
+    M::store_half(mat + ws_block_off(b), lane, o);
+  else
+    M::store_block(mat + ws_block_off(b), lane, o);
+}
+template <typename M>
+__device__ __forceinline__ typename M::Op ws_load(const char* mat, int b, int lane) {
+  return ws_half_block(b) ? M::load_half(mat + ws_block_off(b), lane)
+                          : M::load_block(mat + ws_block_off(b), lane);
+}
+// The same for a block index known only at run time, without a branch (loads that must stay in
+// flight across code whose waits the compiler counts exactly). Reads up to 8 (bf16) or 16
+// (fp32) bytes past a half block: the next block of the same matrix.
+template <typename M>
+__device__ __forceinline__ typename M::Op ws_load_nb(const char* mat, int b, int lane) {
+  return M::load_sel(mat + ws_block_off(b), lane, ws_half_block(b));
 }
 
 // Chunk slot of chunk c of sequence n: n + floor(cu[n] / 64) + c. Injective over all

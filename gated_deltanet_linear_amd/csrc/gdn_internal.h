@@ -64,7 +64,7 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
 // Bytes of one workspace record (one chunk slot x one V head); the layout is private to
 // gdn_chunk.hip, which checks this value at compile time.
-constexpr long long kWorkspaceRecordBytes = 25088;
+constexpr long long kWorkspaceRecordBytes = 20992;
 
 // Number of chunk slots the workspace holds: num_seqs + total_tokens / 64.
 inline long long chunk_slots(const gdn_shape_t& s) {

@@ -470,8 +470,8 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
       const char* rec = p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f.TB[kb] = Mode::load_block(rec + kWsTOff + tri_block(rt, kb) * kWsBlockBytes, lane);
-        f.PB[kb] = Mode::load_block(rec + kWsPOff + tri_block(rt, kb) * kWsBlockBytes, lane);
+        f.TB[kb] = ws_load_nb<Mode>(rec + kWsTOff, tri_block(rt, kb), lane);
+        f.PB[kb] = ws_load_nb<Mode>(rec + kWsPOff, tri_block(rt, kb), lane);
       }
       f.gam = *reinterpret_cast<const f32x4*>(rec + kWsGOff + 4 * (16 * rt + 4 * grp));
       f.del = *reinterpret_cast<const f32x4*>(rec + kWsDOff + 4 * (16 * rt + 4 * grp));
@@ -495,11 +495,11 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     // Operand accessors: RREC waves use the fetched registers (rt is always their own).
     auto tblock = [&](int rt, int kb) -> Op {
       if constexpr (C::RREC) return cur.TB[kb];
-      return Mode::load_block(sR + kWsTOff + tri_block(rt, kb) * 2048, lane);
+      return ws_load<Mode>(sR + kWsTOff, tri_block(rt, kb), lane);
     };
     auto pblock = [&](int rt, int kb) -> Op {
       if constexpr (C::RREC) return cur.PB[kb];
-      return Mode::load_block(sR + kWsPOff + tri_block(rt, kb) * 2048, lane);
+      return ws_load<Mode>(sR + kWsPOff, tri_block(rt, kb), lane);
     };
     auto gamma4 = [&](int rt) -> f32x4 {
       if constexpr (C::RREC) return cur.gam;

@@ -81,7 +81,7 @@ struct TilesCfg {
   static constexpr int KU = KBYTES / 1024;             // ... in 1 KiB units
   static constexpr int NCH = ROWB / 16, RPU = 64 / NCH;  // 16-byte pieces per row, rows per unit
   static constexpr int KTBYTES = NST * 2 * 1024;       // K^T fragments: (state tile, 32 tokens)
-  static constexpr int TBYTES = 6 * kWsBlockBytes;     // T diag(beta) (or P) blocks of a record
+  static constexpr int TBYTES = kWsMatBytes;           // T diag(beta) (or P) blocks of a record
   static constexpr int TU = TBYTES / 1024;             // ... in 1 KiB units
   static constexpr int VROWB = 32;                     // one row of a 16-column bf16 tile
   static constexpr int VSTR = NT * VROWB + 16;         // padded stride: tile reads spread banks
@@ -101,12 +101,11 @@ struct TilesCfg {
   static constexpr int NP = 4;                         // producers: 16 rows of K and Q each
   static constexpr int KPER = KU / NP;                 // K (and Q) units per producer
   static constexpr int VPER = (VU + NP - 1) / NP;      // v units per producer (round robin)
-  static constexpr int TPER = (TU + NP - 1) / NP;      // T (and P) units per producer
+  static constexpr int TPER = (TU + NP - 1) / NP;      // T (and P) units per producer (at most)
   static constexpr int NW = 2 * NT + NP;               // chain waves, output waves, producers
   static constexpr int THREADS = 64 * NW;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(KU % NP == 0 && KPER * RPU == 16, "a producer stages 16 whole K rows");
-  static_assert(TU % NP == 0, "T / P units per producer");
   static_assert(NW <= 16, "waves per workgroup");
 };
 
@@ -184,6 +183,9 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
       const int rs = p.hqk * C::ROWB;          // bytes between token rows of q / k
       const int vrs = p.hv * D * 2;            // ... of v
       f32x4 rk[C::KPER], rq[C::KPER], rv[C::VPER], rt_[C::TPER], rp[C::TPER], rg;
+      // 1 KiB units of the T (and P) blocks this producer moves, dealt round robin (the index is a
+      // compile-time constant in the unrolled loops, so the bound check costs nothing)
+      auto tunit = [](int i) { return PW + C::NP * i; };
       auto rec_of = [&](int c) {
         return p.ws + ((size_t)(slot0 + c) * p.hv + h) * kWsRecordBytes;
       };
@@ -213,8 +215,8 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
         const char* rec = rec_of(c);
 #pragma unroll
         for (int i = 0; i < C::TPER; ++i)
-          rt_[i] = *reinterpret_cast<const f32x4*>(rec + kWsTOff + 1024 * (PW * C::TPER + i) +
-                                                   16 * lane);
+          if (tunit(i) < C::TU)
+            rt_[i] = *reinterpret_cast<const f32x4*>(rec + kWsTOff + 1024 * tunit(i) + 16 * lane);
         if (PW == 0)  // 512 bytes: lanes 32..63 re-read the last 16 bytes
           rg = *reinterpret_cast<const f32x4*>(rec + kWsGOff + 16 * min(lane, 31));
       };
@@ -222,8 +224,8 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
         const char* rec = rec_of(c);
 #pragma unroll
         for (int i = 0; i < C::TPER; ++i)
-          rp[i] = *reinterpret_cast<const f32x4*>(rec + kWsPOff + 1024 * (PW * C::TPER + i) +
-                                                  16 * lane);
+          if (tunit(i) < C::TU)
+            rp[i] = *reinterpret_cast<const f32x4*>(rec + kWsPOff + 1024 * tunit(i) + 16 * lane);
       };
       auto commit_rows = [&]() {  // K and Q rows staged as fp16 (operands of the state products)
 #pragma unroll
@@ -245,13 +247,15 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
       auto commit_t = [&]() {
 #pragma unroll
         for (int i = 0; i < C::TPER; ++i)
-          *reinterpret_cast<f32x4*>(smem + C::TOFF + 1024 * (PW * C::TPER + i) + 16 * lane) = rt_[i];
+          if (tunit(i) < C::TU)
+            *reinterpret_cast<f32x4*>(smem + C::TOFF + 1024 * tunit(i) + 16 * lane) = rt_[i];
         if (PW == 0 && lane < 32) *reinterpret_cast<f32x4*>(smem + C::GOFF + 16 * lane) = rg;
       };
       auto commit_p = [&]() {
 #pragma unroll
         for (int i = 0; i < C::TPER; ++i)
-          *reinterpret_cast<f32x4*>(smem + C::POFF + 1024 * (PW * C::TPER + i) + 16 * lane) = rp[i];
+          if (tunit(i) < C::TU)
+            *reinterpret_cast<f32x4*>(smem + C::POFF + 1024 * tunit(i) + 16 * lane) = rp[i];
       };
       // K^T fragments from this producer's own 16 staged K rows (tokens 16 PW .. 16 PW + 15, the
       // half hf = PW & 1 of token block kbp = PW >> 1). ds_read_b64_tr_b16 hands lane (g, 4a + b)
@@ -400,7 +404,7 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
       // would stall every pair of them).
       Op TB[6];
 #pragma unroll
-      for (int b = 0; b < 6; ++b) TB[b] = M::load_block(sT + b * kWsBlockBytes, lane);
+      for (int b = 0; b < 6; ++b) TB[b] = ws_load<M>(sT, b, lane);
       lds_barrier();  // M(c)
 
       Op YB[2];
@@ -503,7 +507,7 @@ __global__ __launch_bounds__((TilesCfg<D, NT>::THREADS)) void chunk_scan_tiles_k
     lds_barrier();  // M(c)
     Op PB[6];  // staged before M(c); read ahead of X(c) so that the wait covers their latency
 #pragma unroll
-    for (int b = 0; b < 6; ++b) PB[b] = M::load_block(sP + b * kWsBlockBytes, lane);
+    for (int b = 0; b < 6; ++b) PB[b] = ws_load<M>(sP, b, lane);
     lds_barrier();  // X(c): V' of chunk c from the chain wave
     Op VB[2];
 #pragma unroll

@@ -101,7 +101,7 @@ gdn_status_t gdn_prepare(const gdn_shape_t* shape, const int32_t* cu_seqlens,
 
 /* Bytes of device workspace gdn_chunk_forward needs for this shape (0 on a bad shape). The
  * bound uses total_tokens and num_seqs only: (num_seqs + total_tokens / 64) chunk slots times
- * H_v times 25088 bytes. */
+ * H_v times 20992 bytes. */
 size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
 
 /*
@@ -139,7 +139,7 @@ gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqle
  * the library's first use on that GPU until the process ends. It calls no hipMalloc, hipFree or
  * other allocating routine. A shape whose workspace (gdn_chunk_forward_workspace_size) exceeds the
  * array returns GDN_ERR_SCRATCH_LIMIT without launching anything: 64 MiB holds, for example, one
- * 4096-token sequence at 32 V heads ((1 + 64) x 32 records of 25088 bytes). All calls on one GPU
+ * 4096-token sequence at 32 V heads ((1 + 64) x 32 records of 20992 bytes). All calls on one GPU
  * share the array, so calls that overlap on one GPU (different streams or host threads) race and
  * must be serialised by the caller. Other errors as gdn_chunk_forward.
  */

@@ -52,7 +52,7 @@ def _shape(**kw):
 
 def test_workspace_size_formula(lib):
     s = _shape()
-    expect = (2 + 300 // 64) * 32 * 25088
+    expect = (2 + 300 // 64) * 32 * 20992
     assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(s)) == expect
     assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(_shape(num_v_heads=33))) == 0
     assert lib.gdn_chunk_forward_workspace_size(None) == 0
@@ -286,9 +286,9 @@ def test_chunk_forward_noalloc_validation(lib):
     assert call(None) == INVALID
     assert call(_shape(num_v_heads=33)) == INVALID
     assert call(_shape(head_dim_k=96, head_dim_v=96)) == UNSUPPORTED
-    # 64 MiB holds 2674 records of 25088 bytes: 1 x 4096 tokens at 32 V heads is 65 x 32 = 2080
+    # 64 MiB holds 3196 records of 20992 bytes: 1 x 4096 tokens at 32 V heads is 65 x 32 = 2080
     limit = 64 << 20
-    big = _shape(num_seqs=1, total_tokens=8192)  # 129 slots x 32 heads x 25088 > 64 MiB
+    big = _shape(num_seqs=1, total_tokens=8192)  # 129 slots x 32 heads x 20992 > 64 MiB
     assert lib.gdn_chunk_forward_workspace_size(ctypes.byref(big)) > limit
     assert call(big) == 5  # GDN_ERR_SCRATCH_LIMIT
     assert b"SCRATCH_LIMIT" in lib.gdn_status_string(5)
