@@ -247,13 +247,14 @@ def run_decode(torch, gdn, si, steps, warmup):
                               algorithmic_bytes_per_launch=B))
 
 
-def run_front(torch, gdn, si, steps, warmup):
+def run_front(torch, gdn, si, steps, warmup, split=True):
     """Workload 5 (8 packed sequences, 16 QK / 64 V heads, d = 128, bf16 projected inputs,
     initial states): gdn_prepare then the chunked core, exactly the call sequence the end-to-end
     parity test checks. q, k and v cross from the front end to the core in fp32: rounding them
     to bf16 there moves the result ~15% x RMS away from the float64 front end + core on this
     workload (its conv makes neighbouring keys nearly collinear), so the bf16 intermediates do
-    not meet the bf16 bar."""
+    not meet the bf16 bar. ``split``: the core takes them on the split-bf16 MFMA path
+    (split_f32); else on the fp32-MFMA path."""
     fc = si.workload_case(5)
     dev = "cuda"
     x, w, a, b = (t.to(dev) for t in (fc.mixed_qkv, fc.conv_weight, fc.a, fc.b))
@@ -275,11 +276,12 @@ def run_front(torch, gdn, si, steps, warmup):
 
     def intra():
         q, k, v, g, beta = qkv["t"]
-        gdn.chunk_intra(q, k, g, beta, cu, hv, ws)
+        gdn.chunk_intra(q, k, g, beta, cu, hv, ws, split_f32=split)
 
     def scan():
         q, k, v, g, beta = qkv["t"]
-        gdn.chunk_scan(q, k, v, g, beta, cu, ws, initial_state=h0, o=o, final_state=ht)
+        gdn.chunk_scan(q, k, v, g, beta, cu, ws, initial_state=h0, o=o, final_state=ht,
+                       split_f32=split)
 
     ev_ms, ms, kms = _measure(
         torch, [("gdn_prepare", prep), ("gdn_chunk_intra", intra), ("gdn_chunk_scan", scan)],
@@ -290,10 +292,11 @@ def run_front(torch, gdn, si, steps, warmup):
     Bprep = T * (conv_dim * 2 + 2 * hv * 2 + 8 * hv + conv_dim * eq)
     Fscan = scan_flops_per_token_head(dk, dv) * T * hv
     F = prefill_flops_per_token_head(hqk, hv, dk, dv) * T * hv
-    peak = PEAK_F32_TFLOPS if qkv_dtype == torch.float32 else PEAK_BF16_TFLOPS
+    peak = PEAK_F32_TFLOPS if qkv_dtype == torch.float32 and not split else PEAK_BF16_TFLOPS
     Bscan = scan_bytes(m["lengths"], hqk, hv, dk, dv, eq, True, eo=2)
     return dict(T=T, lengths=m["lengths"], ms_per_step=ms, step_ms_events=ev_ms,
                 tokens_per_s=T / (ms / 1e3), qkv_dtype=str(qkv_dtype).replace("torch.", ""),
+                core_products="split-bf16 MFMA" if split else "fp32 MFMA",
                 kernels_ms=kms, path_tflops=F / (ms / 1e3) / 1e12,
                 prepare=_hbm("gdn_prepare", Bprep, kms["gdn_prepare"],
                              "gdn_prepare_prefill_397b_packed_8xU512_8192_f32qkv"),
@@ -302,7 +305,8 @@ def run_front(torch, gdn, si, steps, warmup):
                               peak=peak, unit="TFLOP/s",
                               frac=round(Fscan / (kms["gdn_chunk_scan"] / 1e3) / 1e12 / peak, 5),
                               traffic=_traffic("gdn_chunk_scan_prefill_397b_packed_8xU512_8192"
-                                               + ("_f32qkv" if eq == 4 else "")),
+                                               + ("_f32qkv" if eq == 4 else "")
+                                               + ("_split" if split else "")),
                               algorithmic_flops_per_launch=Fscan,
                               algorithmic_bytes_per_launch=Bscan,
                               hbm_gbs=round(Bscan / (kms["gdn_chunk_scan"] / 1e3) / 1e9, 1)))
@@ -551,6 +555,9 @@ def main():
         out["decode"] = run_decode(torch, gdn, si, args.steps, args.warmup)
     if only in (None, "front"):
         out["front_end_packed_8_seqs"] = run_front(torch, gdn, si, max(3, args.steps // 5), 2)
+        f32 = run_front(torch, gdn, si, max(3, args.steps // 5), 2, split=False)
+        out["front_end_packed_8_seqs"]["fp32_mfma_core"] = {
+            k: f32[k] for k in ("ms_per_step", "kernels_ms", "roofline")}
     if only in (None, "gate"):
         out["output_gate_1x4096"] = run_gate(torch, gdn, si, args.steps, args.warmup)
     if only in (None, "backward"):

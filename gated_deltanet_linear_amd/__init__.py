@@ -31,8 +31,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgdn.so")
 CHUNK = 64
 
-ABI_VERSION = 2  # GDN_ABI_VERSION of include/gdn.h that GdnShape and the signatures follow
-GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+ABI_VERSION = 3  # GDN_ABI_VERSION of include/gdn.h that GdnShape and the signatures follow
+GDN_DTYPE_F32, GDN_DTYPE_BF16, GDN_DTYPE_F32_SPLIT = 0, 1, 2
 _DT = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
 
 
@@ -159,9 +159,14 @@ def _dtype_code(dt: torch.dtype, name: str) -> int:
 
 
 def _shape(num_seqs, total_tokens, hqk, hv, dk, dv, qkv_dtype, out_dtype, in_dtype=None,
-           scale=1.0, state_dtype=None) -> GdnShape:
+           scale=1.0, state_dtype=None, split_f32=False) -> GdnShape:
+    qc = _dtype_code(qkv_dtype, "q/k/v")
+    if split_f32:
+        if qc != GDN_DTYPE_F32:
+            raise GdnError("split_f32 takes float32 q/k/v")
+        qc = GDN_DTYPE_F32_SPLIT
     return GdnShape(int(num_seqs), int(total_tokens), int(hqk), int(hv), int(dk), int(dv),
-                    _dtype_code(qkv_dtype, "q/k/v"), _dtype_code(out_dtype, "o"),
+                    qc, _dtype_code(out_dtype, "o"),
                     _dtype_code(in_dtype or torch.bfloat16, "front-end input"), float(scale),
                     _dtype_code(state_dtype or torch.float32, "state"))
 
@@ -174,7 +179,8 @@ def _state_dtype(*states, default=None):
     return dts.pop() if dts else (default or torch.float32)
 
 
-def _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, state_dtype=None):
+def _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, state_dtype=None,
+                split_f32=False):
     _dev(q, "q")
     _dev(k, "k", q.dtype)
     _dev(g, "g", torch.float32)
@@ -189,7 +195,7 @@ def _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, out_dtype, state_dtype
         raise GdnError("cu_seqlens must be [N + 1]")
     n = cu_seqlens.numel() - 1
     return _shape(n, T, hqk, hv, dk, dv, q.dtype, out_dtype or q.dtype, scale=scale,
-                  state_dtype=state_dtype), n
+                  state_dtype=state_dtype, split_f32=split_f32), n
 
 
 def _v_shape(v, q):
@@ -222,17 +228,19 @@ def _workspace(s: GdnShape, device, workspace):
 
 def chunk_forward(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_state=True,
                   scale=1.0, out_dtype=None, workspace=None, final_state=None, o=None,
-                  state_dtype=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  state_dtype=None,
+                  split_f32=False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill. Returns (o [T, H_v, d_v], final_state [N, H_v, d_k, d_v] or None).
 
     ``final_state`` may be passed (and may be ``initial_state`` itself for an in-place update).
     States are fp32 or bf16 (one dtype for both: ``state_dtype``, else the given states' dtype,
-    else fp32).
+    else fp32). ``split_f32``: float32 q/k/v taken on the split-bf16 MFMA path
+    (GDN_DTYPE_F32_SPLIT) instead of the fp32 one.
     """
     hv, dv = _v_shape(v, q)
     sd = _state_dtype(initial_state, final_state, default=state_dtype)
     od = _out_dtype(out_dtype, o, q.dtype)
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd, split_f32)
     T, dk = s.total_tokens, s.head_dim_k
     if initial_state is not None:
         _dev(initial_state, "initial_state", sd)
@@ -251,14 +259,14 @@ def chunk_forward(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final
 
 def chunk_forward_noalloc(q, k, v, g, beta, cu_seqlens, initial_state=None,
                           output_final_state=True, scale=1.0, out_dtype=None, final_state=None,
-                          o=None, state_dtype=None):
+                          o=None, state_dtype=None, split_f32=False):
     """chunk_forward through gdn_chunk_forward_noalloc: the same result, with the workspace in the
     library's own device array (no device allocation by the library; this wrapper still creates
     o and final_state unless they are given)."""
     hv, dv = _v_shape(v, q)
     sd = _state_dtype(initial_state, final_state, default=state_dtype)
     od = _out_dtype(out_dtype, o, q.dtype)
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd, split_f32)
     T, dk = s.total_tokens, s.head_dim_k
     if initial_state is not None:
         _dev(initial_state, "initial_state", sd)
@@ -274,9 +282,10 @@ def chunk_forward_noalloc(q, k, v, g, beta, cu_seqlens, initial_state=None,
     return o, final_state
 
 
-def chunk_intra(q, k, g, beta, cu_seqlens, num_v_heads, workspace, scale=1.0):
+def chunk_intra(q, k, g, beta, cu_seqlens, num_v_heads, workspace, scale=1.0, split_f32=False):
     """Stage 1 of chunk_forward (state-independent in-chunk work) into ``workspace``."""
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, int(num_v_heads), q.shape[2], scale, None)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, int(num_v_heads), q.shape[2], scale, None,
+                       split_f32=split_f32)
     _dev(workspace, "workspace", torch.uint8)
     rc = _load().gdn_chunk_intra(ctypes.byref(s), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(g),
                                  _ptr(beta), _ptr(workspace), workspace.numel(), _stream())
@@ -284,12 +293,12 @@ def chunk_intra(q, k, g, beta, cu_seqlens, num_v_heads, workspace, scale=1.0):
 
 
 def chunk_scan(q, k, v, g, beta, cu_seqlens, workspace, initial_state=None, o=None,
-               final_state=None, scale=1.0, out_dtype=None):
+               final_state=None, scale=1.0, out_dtype=None, split_f32=False):
     """Stage 2 of chunk_forward (sequential cross-chunk recurrence) from ``workspace``."""
     hv, dv = _v_shape(v, q)
     sd = _state_dtype(initial_state, final_state)
     od = _out_dtype(out_dtype, o, q.dtype)
-    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd)
+    s, n = _core_shape(q, k, g, beta, cu_seqlens, hv, dv, scale, od, sd, split_f32)
     for t, name in ((initial_state, "initial_state"), (final_state, "final_state")):
         if t is not None:
             _dev(t, name, sd)

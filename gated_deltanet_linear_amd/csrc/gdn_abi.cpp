@@ -12,13 +12,15 @@ namespace {
 
 bool dtype_ok(int32_t d) { return d == GDN_DTYPE_F32 || d == GDN_DTYPE_BF16; }
 
-// Shape checks shared by all entry points.
-gdn_status_t check_shape(const gdn_shape_t* s) {
+// Shape checks shared by all entry points. `split_ok`: the call accepts GDN_DTYPE_F32_SPLIT as
+// its qkv_dtype (the front end and the chunked prefill).
+gdn_status_t check_shape(const gdn_shape_t* s, bool split_ok = false) {
   if (s == nullptr) return GDN_ERR_INVALID_ARGUMENT;
   if (s->num_seqs < 1 || s->total_tokens < 0 || s->num_qk_heads < 1 || s->num_v_heads < 1)
     return GDN_ERR_INVALID_ARGUMENT;
   if (s->num_v_heads % s->num_qk_heads != 0) return GDN_ERR_INVALID_ARGUMENT;
-  if (!dtype_ok(s->qkv_dtype) || !dtype_ok(s->out_dtype) || !dtype_ok(s->state_dtype))
+  const bool qkv_ok = dtype_ok(s->qkv_dtype) || (split_ok && s->qkv_dtype == GDN_DTYPE_F32_SPLIT);
+  if (!qkv_ok || !dtype_ok(s->out_dtype) || !dtype_ok(s->state_dtype))
     return GDN_ERR_INVALID_ARGUMENT;
   if (s->head_dim_k < 1 || s->head_dim_v < 1) return GDN_ERR_INVALID_ARGUMENT;
   if (!(s->scale == s->scale)) return GDN_ERR_INVALID_ARGUMENT;  // NaN
@@ -66,7 +68,7 @@ const char* gdn_status_string(gdn_status_t status) {
 }
 
 size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* s) {
-  if (check_shape(s) != GDN_OK) return 0;
+  if (check_shape(s, true) != GDN_OK) return 0;
   return (size_t)gdn::chunk_slots(*s) * (size_t)s->num_v_heads *
          (size_t)gdn::kWorkspaceRecordBytes;
 }
@@ -75,7 +77,7 @@ gdn_status_t gdn_prepare(const gdn_shape_t* s, const int32_t* cu, const void* x,
                          const void* bias, const void* a, const void* b, const float* A_log,
                          const float* dt_bias, float eps, void* q, void* k, void* v, float* g,
                          float* beta, void* stream) {
-  gdn_status_t st = check_shape(s);
+  gdn_status_t st = check_shape(s, true);
   if (st != GDN_OK) return st;
   if (!dtype_ok(s->in_dtype)) return GDN_ERR_INVALID_ARGUMENT;
   if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARGUMENT;
@@ -93,7 +95,7 @@ gdn_status_t gdn_prepare(const gdn_shape_t* s, const int32_t* cu, const void* x,
 
 static gdn_status_t check_chunk_common(const gdn_shape_t* s, const int32_t* cu, const void* q,
                                        const void* k, const void* ws, size_t ws_bytes) {
-  gdn_status_t st = check_shape(s);
+  gdn_status_t st = check_shape(s, true);
   if (st != GDN_OK) return st;
   if (!cu) return GDN_ERR_INVALID_ARGUMENT;
   if (s->total_tokens > 0 && (!q || !k || !ws)) return GDN_ERR_INVALID_ARGUMENT;
@@ -144,7 +146,7 @@ gdn_status_t gdn_chunk_forward_noalloc(const gdn_shape_t* s, const int32_t* cu, 
                                        void* stream) {
   // The same checks as gdn_chunk_forward (with the library's array standing in for the
   // workspace), and the size limit, before any HIP call.
-  gdn_status_t st = check_shape(s);
+  gdn_status_t st = check_shape(s, true);
   if (st != GDN_OK) return st;
   if (gdn_chunk_forward_workspace_size(s) > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
     return GDN_ERR_SCRATCH_LIMIT;

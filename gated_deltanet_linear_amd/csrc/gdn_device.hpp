@@ -277,6 +277,45 @@ struct F32Mode {
   }
 };
 
+// F32SplitMode: q / k / v stored as fp32 and every product taken on bf16 MFMA with both operands
+// as hi + lo bf16 pairs: the inputs are split when they are staged, and the workspace blocks
+// (written by the fp32 intra kernel, F32Mode's layout) when they are read. An operand then
+// keeps about 16 significant bits (x = hi + lo to ~2^-17 relative) instead of fp32's 24, and a
+// 32-deep block costs three bf16 MFMAs instead of eight fp32 ones. For fp32 q / k / v that
+// stand for bf16-derived values (a front end's output) where the fp32 bar is not the contract.
+struct F32SplitMode {
+  using in_t = float;
+  using Op = Bf16Mode::Op;
+  using frag_t = Op;
+  static constexpr bool kSplit = true;
+  __device__ __forceinline__ static Op make(const float (&x)[8]) { return Bf16Mode::make(x); }
+  __device__ __forceinline__ static Op split(const f32x8& v) {
+    float x[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[s] = v[s];
+    return Bf16Mode::make(x);
+  }
+  __device__ __forceinline__ static f32x4 mma_xs(f32x4 c, const frag_t& a, const Op& b) {
+    return Bf16Mode::mma_ss(c, a, b);
+  }
+  __device__ __forceinline__ static f32x4 mma_ss(f32x4 c, const Op& a, const Op& b) {
+    return Bf16Mode::mma_ss(c, a, b);
+  }
+  __device__ __forceinline__ static f32x4 mma_ss_t(f32x4 c, const Op& a, const Op& b) {
+    return Bf16Mode::mma_ss_t(c, a, b);
+  }
+  // Blocks in F32Mode's layout, split on the way in.
+  __device__ __forceinline__ static Op load_block(const char* blk, int lane) {
+    return split(F32Mode::load_block(blk, lane).v);
+  }
+  __device__ __forceinline__ static Op load_half(const char* blk, int lane) {
+    return split(F32Mode::load_half(blk, lane).v);
+  }
+  __device__ __forceinline__ static Op load_sel(const char* blk, int lane, bool half) {
+    return split(F32Mode::load_sel(blk, lane, half).v);
+  }
+};
+
 // 8 values of a 32-deep B fragment from two C fragments (rows 0-15 and 16-31 of the depth).
 __device__ __forceinline__ void pack_c_pair(const f32x4& c0, const f32x4& c1, float (&x)[8]) {
   x[0] = c0[0];

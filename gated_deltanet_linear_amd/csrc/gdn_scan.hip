@@ -115,6 +115,19 @@ struct Frags<F32Mode, ROWB> {
     return ktfrag_f32<ROWB>(b, it, kbp, lane);
   }
 };
+// F32SplitMode: the fp32 K (or Q) rows of a chunk are staged as two bf16 planes, the hi halves
+// of all 64 rows and then the lo halves, each laid out like bf16 rows (ROWB / 2 bytes, the same
+// swizzle), so both halves of an operand are read with the bf16 readers.
+template <int ROWB>
+struct Frags<F32SplitMode, ROWB> {
+  static constexpr int HROWB = ROWB / 2, PLANE = 64 * HROWB;
+  __device__ static Bf16Mode::Op a(const char* b, int row, int kb, int grp) {
+    return {afrag<HROWB>(b, row, kb, grp), afrag<HROWB>(b + PLANE, row, kb, grp)};
+  }
+  __device__ static Bf16Mode::Op kt(const char* b, int it, int kbp, int lane) {
+    return {ktfrag<HROWB>(b, it, kbp, lane), ktfrag<HROWB>(b + PLANE, it, kbp, lane)};
+  }
+};
 
 // Half of an operand block (slots 4*half .. 4*half+3 of every lane), split like Mode::make.
 __device__ __forceinline__ void store_half(Bf16Mode, char* blk, int lane, int half,
@@ -132,6 +145,10 @@ __device__ __forceinline__ void store_half(F32Mode, char* blk, int lane, int hal
                                            const f32x4& x) {
   *reinterpret_cast<f32x4*>(blk + lane * 32 + half * 16) = x;
 }
+__device__ __forceinline__ void store_half(F32SplitMode, char* blk, int lane, int half,
+                                           const f32x4& x) {
+  store_half(F32Mode{}, blk, lane, half, x);  // F32SplitMode::load_block reads this layout
+}
 
 // Operand of the two products with the state (K H, Q H): fp16 for bf16 q / k / v (K and Q rows
 // then staged as fp16, see Half), the mode's own operand for fp32. kt() turns a K^T fragment read
@@ -141,7 +158,7 @@ struct StateOp;
 template <>
 struct StateOp<Bf16Mode> {
   using op = f16x8;
-  static constexpr bool kHalfRows = true;
+  static constexpr bool kHalfRows = true, kSplitRows = false;
   __device__ static op make(const float (&x)[8]) { return Half::make(x); }
   __device__ static op load(const char* blk, int lane) { return Half::load_block(blk, lane); }
   __device__ static void store(char* blk, int lane, const op& o) { Half::store_block(blk, lane, o); }
@@ -155,12 +172,24 @@ struct StateOp<Bf16Mode> {
 template <>
 struct StateOp<F32Mode> {
   using op = F32Mode::Op;
-  static constexpr bool kHalfRows = false;
+  static constexpr bool kHalfRows = false, kSplitRows = false;
   __device__ static op make(const float (&x)[8]) { return F32Mode::make(x); }
   __device__ static op load(const char* blk, int lane) { return F32Mode::load_block(blk, lane); }
   __device__ static void store(char* blk, int lane, const op& o) { F32Mode::store_block(blk, lane, o); }
   __device__ static f32x4 mma(f32x4 c, const f32x8& a, const op& b) { return F32Mode::mma_xs(c, a, b); }
   __device__ static f32x8 kt(const f32x8& f) { return f; }
+};
+template <>
+struct StateOp<F32SplitMode> {
+  using op = Bf16Mode::Op;
+  static constexpr bool kHalfRows = false, kSplitRows = true;
+  __device__ static op make(const float (&x)[8]) { return Bf16Mode::make(x); }
+  __device__ static op load(const char* blk, int lane) { return Bf16Mode::load_block(blk, lane); }
+  __device__ static void store(char* blk, int lane, const op& o) { Bf16Mode::store_block(blk, lane, o); }
+  __device__ static f32x4 mma(f32x4 c, const Bf16Mode::Op& a, const op& b) {
+    return Bf16Mode::mma_ss(c, a, b);
+  }
+  __device__ static Bf16Mode::Op kt(const Bf16Mode::Op& f) { return f; }
 };
 
 constexpr int kRecUnits = kWsRecordBytes / 16;                   // 16-byte units per record
@@ -337,7 +366,9 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
               const int jj = j < C::KI ? j : j - C::KI;
               const int row = jj * C::RPU + lane / C::NCH;
               base = j < C::KI ? Kb : Qb;
-              off = min(row, lenc - 1) * rs + 16 * ((lane % C::NCH) ^ swz<C::ROWB>(row));
+              // (split rows take the swizzle of their bf16 planes when they are written)
+              off = min(row, lenc - 1) * rs +
+                    16 * ((lane % C::NCH) ^ (SO::kSplitRows ? 0 : swz<C::ROWB>(row)));
             } else if (j < C::KQ + C::RI) {
               base = rec;
               off = 16 * min(64 * (j - C::KQ) + lane, kRecUnits - 1);
@@ -355,7 +386,21 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
 #pragma unroll
         for (int u = 0; u < C::PER; ++u) {
           const int j = PW + C::NP * u;
-          if (j < C::TOTAL) {
+          if (j < C::TOTAL && SO::kSplitRows && j < C::KQ) {
+            // 4 fp32 values of one K (or Q) row -> 8 bytes in the hi plane and 8 in the lo plane
+            const int jj = j < C::KI ? j : j - C::KI;
+            const int row = jj * C::RPU + lane / C::NCH, cp = lane % C::NCH;
+            char* plane = buf + (j < C::KI ? 0 : C::QOFF);
+            const int off = swz_off<C::ROWB / 2, 2>(row, 4 * cp);
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hi[e] = (bf16)r[u][e];
+              lo[e] = (bf16)(r[u][e] - (float)hi[e]);
+            }
+            *reinterpret_cast<bf16x4*>(plane + off) = hi;
+            *reinterpret_cast<bf16x4*>(plane + 64 * (C::ROWB / 2) + off) = lo;
+          } else if (j < C::TOTAL) {
             int dst;
             if (j < C::KQ + C::RI) {
               dst = 1024 * j + 16 * lane;
@@ -768,10 +813,11 @@ hipError_t launch_scan_t(const gdn_shape_t& s, const ScanParams& p, hipStream_t 
   const int G = s.num_v_heads / s.num_qk_heads;
   constexpr int tiles = D / 16;
   // Few (sequence, head) chains: 4 waves per 16-column tile so that every SIMD gets work.
-  // Many chains, fp32 operands: 1 wave per tile, 4 (or 2) tiles per workgroup sharing the staged
-  // chunk. (Many chains with bf16 operands run chunk_scan_tiles_kernel, gdn_scan_tiles.hip.)
+  // Many chains, fp32 q / k / v (F32Mode or F32SplitMode): 1 wave per tile, 4 (or 2) tiles per
+  // workgroup sharing the staged chunk. (Many chains with bf16 operands run
+  // chunk_scan_tiles_kernel, gdn_scan_tiles.hip.)
   if (heads * tiles <= 512) return launch_scan_cfg<Mode, D, 1, 4, OutT>(p, heads, G, stream);
-  if constexpr (std::is_same<Mode, F32Mode>::value) {
+  if constexpr (!std::is_same<Mode, Bf16Mode>::value) {
     if constexpr (tiles % 4 == 0) return launch_scan_cfg<Mode, D, 4, 1, OutT>(p, heads, G, stream);
     else return launch_scan_cfg<Mode, D, 2, 1, OutT>(p, heads, G, stream);
   }
@@ -802,6 +848,9 @@ hipError_t launch_chunk_scan(const gdn_shape_t& s, const int32_t* cu, const void
   if (s.qkv_dtype == GDN_DTYPE_BF16)
     return out_bf ? launch_scan_d<Bf16Mode, bf16>(s, p, stream)
                   : launch_scan_d<Bf16Mode, float>(s, p, stream);
+  if (s.qkv_dtype == GDN_DTYPE_F32_SPLIT)
+    return out_bf ? launch_scan_d<F32SplitMode, bf16>(s, p, stream)
+                  : launch_scan_d<F32SplitMode, float>(s, p, stream);
   return out_bf ? launch_scan_d<F32Mode, bf16>(s, p, stream)
                 : launch_scan_d<F32Mode, float>(s, p, stream);
 }

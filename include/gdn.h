@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 #define GDN_CHUNK 64 /* chunk length of the chunked prefill ([MoE report] §3.7 Step 2) */
 
 typedef enum {
@@ -51,7 +51,14 @@ typedef enum {
                                library-owned array holds (GDN_NOALLOC_SCRATCH_BYTES) */
 } gdn_status_t;
 
-typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype_t;
+/* GDN_DTYPE_F32_SPLIT names fp32 storage read at a lower operand precision: accepted only as
+ * the qkv_dtype of gdn_prepare (which then writes fp32 q/k/v) and of the chunked-prefill calls
+ * (gdn_chunk_forward, its _noalloc variant, gdn_chunk_intra, gdn_chunk_scan and the workspace
+ * size), GDN_ERR_INVALID_ARGUMENT elsewhere. The prefill then takes its products on bf16 MFMA
+ * with fp32 q/k/v and every computed operand as hi + lo bf16 pairs (about 16 significant bits;
+ * T diag(beta) and P formed in fp32). It is meant for fp32 q/k/v derived from bf16 inputs (the
+ * front end's output), whose own bar is the bf16 one; the F32 path keeps every product fp32. */
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1, GDN_DTYPE_F32_SPLIT = 2 } gdn_dtype_t;
 
 typedef struct gdn_shape {
   int32_t num_seqs;     /* N >= 1                                                         */
@@ -61,7 +68,8 @@ typedef struct gdn_shape {
   int32_t head_dim_k;   /* d_k                                                            */
   int32_t head_dim_v;   /* d_v                                                            */
   int32_t qkv_dtype;    /* gdn_dtype_t of q, k, v (core inputs, front-end outputs). BF16   */
-                        /* runs the bf16-MFMA path, F32 the fp32-MFMA path.                */
+                        /* runs the bf16-MFMA path, F32 the fp32-MFMA path, F32_SPLIT      */
+                        /* (prefill only) fp32 storage on the split-bf16 MFMA path.        */
   int32_t out_dtype;    /* gdn_dtype_t of o. BF16 output is the round-to-nearest-even cast */
                         /* of the same fp32 result an F32 output would hold.               */
   int32_t in_dtype;     /* gdn_dtype_t of the front-end inputs (mixed_qkv, conv weight and */
@@ -124,6 +132,9 @@ size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
  * below that; L2-normalised vectors are in range) and the state rounded to fp16 once per chunk
  * for these products (so its magnitude must stay below 65504). The state update, T diag(beta) Y
  * and P V' take the computed operands as hi + lo bf16 pairs (about 16 significant bits).
+ * With qkv_dtype GDN_DTYPE_F32_SPLIT (fp32 q/k/v) T diag(beta) and P are formed on fp32 MFMA and
+ * every product of the cross-chunk scan on bf16 MFMA with both operands as hi + lo bf16 pairs,
+ * k and q included (about 16 significant bits each; the state itself stays fp32).
  */
 gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                                const void* q, const void* k, const void* v, const float* g,

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import gated_deltanet_linear_amd as gdn
 from gated_deltanet_linear_amd import GdnShape
@@ -104,6 +105,28 @@ def test_chunk_forward_rejects_bad_pointers_and_workspace(lib):
                               1 << 40, None) == INVALID  # v
     assert lib.gdn_chunk_scan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, mis, None, FAKE,
                               1 << 40, None) == INVALID  # o
+
+
+def test_split_qkv_dtype_only_on_the_prefill_calls(lib):
+    """GDN_DTYPE_F32_SPLIT (2) passes the chunked-prefill calls' validation (they get as far as
+    the workspace check) and the workspace size, and is refused by the decode step and the
+    backward."""
+    s = _shape(qkv_dtype=2)
+    need = lib.gdn_chunk_forward_workspace_size(ctypes.byref(s))
+    assert need == lib.gdn_chunk_forward_workspace_size(ctypes.byref(_shape())) > 0
+    assert _chunk(lib, s, ws_bytes=need - 1) == WS_SMALL
+    assert lib.gdn_chunk_intra(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                               None) == WS_SMALL
+    assert lib.gdn_chunk_scan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                              need - 1, None) == WS_SMALL
+    assert _chunk(lib, _shape(qkv_dtype=3), ws_bytes=need - 1) == INVALID
+    s2 = _shape(total_tokens=2, qkv_dtype=2)
+    assert lib.gdn_recurrent_step(ctypes.byref(s2), *([FAKE] * 7), None) == INVALID
+    assert lib.gdn_chunk_backward_workspace_size(ctypes.byref(s)) == 0
+    with pytest.raises(gdn.GdnError):  # the binding takes split_f32 for float32 q/k/v only
+        gdn._shape(1, 4, 1, 1, 32, 32, torch.bfloat16, torch.bfloat16, split_f32=True)
+    assert gdn._shape(1, 4, 1, 1, 32, 32, torch.float32, torch.float32,
+                      split_f32=True).qkv_dtype == 2
 
 
 def test_recurrent_step_validation(lib):

@@ -121,12 +121,12 @@ def test_front_end_workload_stagewise_and_end_to_end():
     Stage by stage: the front end against the oracle's front end, and the core on the front
     end's bf16 outputs against the oracle core on the same values (all 512 chains).
 
-    End to end, exactly the benchmark's call sequence: gdn_prepare with fp32 q / k / v, then
-    gdn_chunk_intra and gdn_chunk_scan with a bf16 output, against the float64 front end + float64
-    core (all chains): the fp32 output twin meets the bf16 bar and the bf16 output is its
-    round-to-nearest-even cast. The path with bf16 q / k / v between the two stages is measured
-    and printed but not held to the bar: that rounding alone moves the float64 result by ~13% x
-    RMS on this workload."""
+    End to end: gdn_prepare with fp32 q / k / v, then gdn_chunk_intra and gdn_chunk_scan with a
+    bf16 output, on the fp32-MFMA path and on the split-bf16 path (split_f32, the benchmark's call
+    sequence), against the float64 front end + float64 core (all chains): the fp32 output twin
+    meets the bf16 bar and the bf16 output is its round-to-nearest-even cast. The path with bf16
+    q / k / v between the two stages is measured and printed but not held to the bar: that
+    rounding alone moves the float64 result by ~13% x RMS on this workload."""
     fc = si.workload_case(5)
     print(f"[front] lengths={fc.meta['lengths']}", flush=True)
     dev = "cuda"
@@ -157,19 +157,25 @@ def test_front_end_workload_stagewise_and_end_to_end():
           f"final state {rel_err(f64(ht), e2e_href):.3e} x RMS (not held to the bar)", flush=True)
     del o, ht
 
-    # the benchmark's sequence: fp32 q/k/v, intra, scan; bf16 output and its fp32 twin
+    # fp32 q/k/v, intra, scan, on the fp32-MFMA path and on the split-bf16 one (the benchmark's
+    # sequence); bf16 output and its fp32 twin
     q32, k32, v32, g32, b32 = _prep_gpu(fc, qkv_dtype=torch.float32)
     T, n_seqs = q32.shape[0], len(fc.meta["lengths"])
     ws = torch.empty(gdn.workspace_size(T, n_seqs, 16, 64, 128), dtype=torch.uint8, device=dev)
-    outs = {}
-    for od in (torch.float32, torch.bfloat16):
-        gdn.chunk_intra(q32, k32, g32, b32, cu, 64, ws)
-        o_e, h_e = gdn.chunk_scan(q32, k32, v32, g32, b32, cu, ws, initial_state=h0,
-                                  final_state=torch.empty_like(h0), out_dtype=od)
-        torch.cuda.synchronize()
-        outs[od] = (o_e.cpu(), h_e.cpu())
-    eo, eh = outs[torch.float32]
-    assert_rms_close(eo, e2e_ref, TOL["bf16"], "front workload end-to-end o (all chains)")
-    assert_rms_close(eh, e2e_href, TOL["bf16"], "front workload end-to-end final state (all chains)")
-    assert torch.equal(outs[torch.bfloat16][0], outs[torch.float32][0].to(torch.bfloat16))
-    assert torch.equal(outs[torch.bfloat16][1], outs[torch.float32][1])
+    for split in (False, True):
+        path = "split-bf16" if split else "fp32"
+        outs = {}
+        for od in (torch.float32, torch.bfloat16):
+            gdn.chunk_intra(q32, k32, g32, b32, cu, 64, ws, split_f32=split)
+            o_e, h_e = gdn.chunk_scan(q32, k32, v32, g32, b32, cu, ws, initial_state=h0,
+                                      final_state=torch.empty_like(h0), out_dtype=od,
+                                      split_f32=split)
+            torch.cuda.synchronize()
+            outs[od] = (o_e.cpu(), h_e.cpu())
+        eo, eh = outs[torch.float32]
+        assert_rms_close(eo, e2e_ref, TOL["bf16"],
+                         f"front workload end-to-end o, {path} (all chains)")
+        assert_rms_close(eh, e2e_href, TOL["bf16"],
+                         f"front workload end-to-end final state, {path} (all chains)")
+        assert torch.equal(outs[torch.bfloat16][0], outs[torch.float32][0].to(torch.bfloat16))
+        assert torch.equal(outs[torch.bfloat16][1], outs[torch.float32][1])
