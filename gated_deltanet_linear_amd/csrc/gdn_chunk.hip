@@ -13,12 +13,15 @@
 // forming W = T diag(beta gamma) K: the same product, and W is never stored.
 //
 // This file holds the chunk-parallel half, chunk_intra: one workgroup per (chunk slot, V
-// head). It forms K K^T and the masked decayed Q K^T on MFMA (the decay and beta applied on
-// the fly to the result fragments), inverts the unit-lower-triangular I + A (16x16 diagonal
+// head). It forms K K^T and the masked decayed Q K^T on MFMA (bf16 rows; fp32 rows on fp32
+// MFMA, or as hi + lo bf16 pairs under F32SplitMode; the decay and beta applied on the fly to
+// the result fragments), inverts the unit-lower-triangular I + A (16x16 diagonal
 // blocks by substitution, off-diagonal blocks by two levels of 16x16 fp32 MFMA products) and
 // writes T diag(beta), scale P (as ready-made MFMA A fragments; the output scale is applied
 // here, where the kernel waits on memory, and to the Q H term by the scan), e^{b_t} and
 // e^{b_C - b_t} to the workspace. The sequential half, chunk_scan, is in gdn_scan.hip.
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_internal.h"
 
@@ -63,6 +66,22 @@ template <>
 __device__ __forceinline__ f32x8 row_frag<F32Mode, 512>(const char* b, int r, int kb, int g) {
   return afrag_f32<512>(b, r, kb, g);
 }
+// F32SplitMode: fp32 rows, each fragment split into hi + lo bf16 as it is read
+template <>
+__device__ __forceinline__ Bf16Mode::Op row_frag<F32SplitMode, 128>(const char* b, int r, int kb,
+                                                                    int g) {
+  return F32SplitMode::split(afrag_f32<128>(b, r, kb, g));
+}
+template <>
+__device__ __forceinline__ Bf16Mode::Op row_frag<F32SplitMode, 256>(const char* b, int r, int kb,
+                                                                    int g) {
+  return F32SplitMode::split(afrag_f32<256>(b, r, kb, g));
+}
+template <>
+__device__ __forceinline__ Bf16Mode::Op row_frag<F32SplitMode, 512>(const char* b, int r, int kb,
+                                                                    int g) {
+  return F32SplitMode::split(afrag_f32<512>(b, r, kb, g));
+}
 
 // One workgroup per (chunk slot, group of NV V heads of one QK head): NV = 2 when the heads per
 // QK head come in pairs, else 1. K K^T and Q K^T of the chunk's QK head are formed once and
@@ -75,6 +94,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Mode::in_t) == 4 && DK == 128
 void chunk_intra_kernel(IntraParams p) {
   using in_t = typename Mode::in_t;
   using frag_t = typename Mode::frag_t;
+  // record layout: F32SplitMode's records are F32Mode's (its scan splits them when it reads them)
+  using RecM = std::conditional_t<std::is_same<Mode, F32SplitMode>::value, F32Mode, Mode>;
   constexpr int NWV = 4 * NV;  // waves
   constexpr int KB = DK / 32;
   constexpr int ROWB = DK * (int)sizeof(in_t), KBYTES = 64 * ROWB;
@@ -190,7 +211,12 @@ void chunk_intra_kernel(IntraParams p) {
     }
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) c = mma32(fa[kb], fb[kb], c);
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (std::is_same<Mode, F32SplitMode>::value)
+        c = Mode::mma_ss(c, fa[kb], fb[kb]);
+      else
+        c = mma32(fa[kb], fb[kb], c);
+    }
     return c;
   };
   // One product loop for both kinds: job j of an A wave is A tile wj + HW j; job j of a P wave
@@ -268,7 +294,7 @@ void chunk_intra_kernel(IntraParams p) {
                 jc <= t ? __expf((float)(bt - bj[r])) * (p.scale * acc[2 * i + hf][r]) : 0.f;
           }
         }
-        ws_store<Mode>(rec(v) + kWsPOff, bl, lane, Mode::make(x));
+        ws_store<RecM>(rec(v) + kWsPOff, bl, lane, RecM::make(x));
       }
     }
   }
@@ -295,7 +321,7 @@ void chunk_intra_kernel(IntraParams p) {
       const int jc = 32 * kb + kslot(gr, s);
       x[s] = jc <= t ? (s < 4 ? ta[s] * be0[s] : tb[s - 4] * be1[s - 4]) : 0.f;
     }
-    ws_store<Mode>(rec(v) + kWsTOff, bi, ln, Mode::make(x));
+    ws_store<RecM>(rec(v) + kWsTOff, bi, ln, RecM::make(x));
   }
 }
 
@@ -337,6 +363,7 @@ hipError_t launch_chunk_intra(const gdn_shape_t& s, const int32_t* cu, const voi
   IntraParams p{cu, q, k, g, beta, static_cast<char*>(ws), s.num_seqs, s.num_qk_heads,
                 s.num_v_heads, 0, s.scale};
   if (s.qkv_dtype == GDN_DTYPE_BF16) return launch_intra_d<Bf16Mode>(s, p, stream);
+  if (s.qkv_dtype == GDN_DTYPE_F32_SPLIT) return launch_intra_d<F32SplitMode>(s, p, stream);
   return launch_intra_d<F32Mode>(s, p, stream);
 }
 

@@ -67,6 +67,7 @@ __device__ __forceinline__ f32x4 mma32(const f32x8& a, const f32x8& b, f32x4 c) 
 //     relative), and a product of two such operands takes hi*hi + hi*lo + lo*hi, all on
 //     bf16 MFMA with fp32 accumulation.
 //   F32Mode: inputs and operands are fp32 on fp32 MFMA.
+//   F32SplitMode (below): fp32 inputs, every operand a hi + lo pair on bf16 MFMA.
 struct Bf16Mode {
   using in_t = bf16;
   using frag_t = bf16x8;
@@ -278,8 +279,8 @@ struct F32Mode {
 };
 
 // F32SplitMode: q / k / v stored as fp32 and every product taken on bf16 MFMA with both operands
-// as hi + lo bf16 pairs: the inputs are split when they are staged, and the workspace blocks
-// (written by the fp32 intra kernel, F32Mode's layout) when they are read. An operand then
+// as hi + lo bf16 pairs: the inputs are split when they are staged or read, and the workspace
+// blocks (stored in F32Mode's layout) when they are read. An operand then
 // keeps about 16 significant bits (x = hi + lo to ~2^-17 relative) instead of fp32's 24, and a
 // 32-deep block costs three bf16 MFMAs instead of eight fp32 ones. For fp32 q / k / v that
 // stand for bf16-derived values (a front end's output) where the fp32 bar is not the contract.

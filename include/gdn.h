@@ -56,8 +56,9 @@ typedef enum {
  * (gdn_chunk_forward, its _noalloc variant, gdn_chunk_intra, gdn_chunk_scan and the workspace
  * size), GDN_ERR_INVALID_ARGUMENT elsewhere. The prefill then takes its products on bf16 MFMA
  * with fp32 q/k/v and every computed operand as hi + lo bf16 pairs (about 16 significant bits;
- * T diag(beta) and P formed in fp32). It is meant for fp32 q/k/v derived from bf16 inputs (the
- * front end's output), whose own bar is the bf16 one; the F32 path keeps every product fp32. */
+ * the inverse (I + A)^-1 stays on fp32 MFMA). It is meant for fp32 q/k/v derived from bf16
+ * inputs (the front end's output), whose own bar is the bf16 one; the F32 path keeps every
+ * product fp32. */
 typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1, GDN_DTYPE_F32_SPLIT = 2 } gdn_dtype_t;
 
 typedef struct gdn_shape {
@@ -132,9 +133,9 @@ size_t gdn_chunk_forward_workspace_size(const gdn_shape_t* shape);
  * below that; L2-normalised vectors are in range) and the state rounded to fp16 once per chunk
  * for these products (so its magnitude must stay below 65504). The state update, T diag(beta) Y
  * and P V' take the computed operands as hi + lo bf16 pairs (about 16 significant bits).
- * With qkv_dtype GDN_DTYPE_F32_SPLIT (fp32 q/k/v) T diag(beta) and P are formed on fp32 MFMA and
- * every product of the cross-chunk scan on bf16 MFMA with both operands as hi + lo bf16 pairs,
- * k and q included (about 16 significant bits each; the state itself stays fp32).
+ * With qkv_dtype GDN_DTYPE_F32_SPLIT (fp32 q/k/v) every product but the inverse (fp32 MFMA)
+ * runs on bf16 MFMA with both operands as hi + lo bf16 pairs, k and q included (about 16
+ * significant bits each; the state itself stays fp32).
  */
 gdn_status_t gdn_chunk_forward(const gdn_shape_t* shape, const int32_t* cu_seqlens,
                                const void* q, const void* k, const void* v, const float* g,

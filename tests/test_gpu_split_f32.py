@@ -1,6 +1,6 @@
 """GPU parity of the chunked prefill on fp32 q/k/v taken on the split-bf16 MFMA path
-(qkv_dtype GDN_DTYPE_F32_SPLIT: every product of the scan on bf16 MFMA with both operands as
-hi + lo bf16 pairs, T diag(beta) and P formed by the fp32 intra kernel).
+(qkv_dtype GDN_DTYPE_F32_SPLIT: every product but the intra kernel's inverse on bf16 MFMA with
+both operands as hi + lo bf16 pairs).
 
 Such q/k/v stand for values derived from bf16 inputs (the front end's fp32 output), so the bar
 is the bf16 one, 2e-2 x RMS, against the float64 oracle on the same fp32 values. Both scan
