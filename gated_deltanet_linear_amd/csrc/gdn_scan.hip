@@ -192,6 +192,26 @@ struct StateOp<F32SplitMode> {
   __device__ static Bf16Mode::Op kt(const Bf16Mode::Op& f) { return f; }
 };
 
+// Layout of the record blocks as staged in LDS: F32SplitMode's producers split the fp32 blocks
+// into Bf16Mode's hi / lo layout once per chunk, so the compute waves read them as bf16 pairs.
+template <typename Mode>
+struct RecLds {
+  using type = Mode;
+};
+template <>
+struct RecLds<F32SplitMode> {
+  using type = Bf16Mode;
+};
+
+// Block of 1 KiB unit um of a record matrix (units 0 .. kWsMatBytes / 1024 - 1; every block
+// boundary is a multiple of 1 KiB).
+__host__ __device__ constexpr int ws_unit_block(int um) {
+  return um == 0 ? 0 : um <= 2 ? 1 : um <= 4 ? 2 : um == 5 ? 3 : um <= 7 ? 4 : 5;
+}
+static_assert(ws_block_off(ws_unit_block(9)) == 8192 && ws_unit_block(5) == 3 &&
+                  ws_block_off(3) == 5120 && kWsMatBytes / 1024 == 10,
+              "unit -> block map of the record matrices");
+
 constexpr int kRecUnits = kWsRecordBytes / 16;                   // 16-byte units per record
 constexpr int kRecStage = (kWsRecordBytes + 1023) / 1024 * 1024;  // staged record bytes
 constexpr int kLdsBytes = 160 * 1024;                             // LDS per workgroup
@@ -400,6 +420,31 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
             }
             *reinterpret_cast<bf16x4*>(plane + off) = hi;
             *reinterpret_cast<bf16x4*>(plane + 64 * (C::ROWB / 2) + off) = lo;
+          } else if (j < C::TOTAL && SO::kSplitRows && j >= C::KQ &&
+                     j < C::KQ + 2 * (kWsMatBytes / 1024)) {
+            // a 1 KiB unit of T diag(beta) or P in F32Mode's layout -> hi / lo halves in
+            // Bf16Mode's layout (the same block offsets; within a block, lane l' of the full
+            // layout holds 8 floats at 32 l', of the half layout 4 at 16 l')
+            constexpr int MU = kWsMatBytes / 1024;
+            const int um = (j - C::KQ) % MU;
+            const int b = ws_unit_block(um), ob = ws_block_off(b);
+            int hoff, lsep;
+            if (ws_half_block(b)) {
+              hoff = ob + 8 * lane;
+              lsep = 512;
+            } else {
+              hoff = ob + 16 * (32 * (um - ob / 1024) + (lane >> 1)) + 8 * (lane & 1);
+              lsep = 1024;
+            }
+            char* mat = buf + C::ROFF + ((j - C::KQ) / MU) * kWsMatBytes;
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hi[e] = (bf16)r[u][e];
+              lo[e] = (bf16)(r[u][e] - (float)hi[e]);
+            }
+            *reinterpret_cast<bf16x4*>(mat + hoff) = hi;
+            *reinterpret_cast<bf16x4*>(mat + hoff + lsep) = lo;
           } else if (j < C::TOTAL) {
             int dst;
             if (j < C::KQ + C::RI) {
@@ -538,13 +583,14 @@ __global__ __launch_bounds__((ScanCfg<Mode, D, NT, RW, OutT>::THREADS)) void chu
     const float* sdel = reinterpret_cast<const float*>(sR + kWsDOff);
     char* const Wc = Wo + (c & 1) * C::OBYTES + tile * C::OROWB;
     // Operand accessors: RREC waves use the fetched registers (rt is always their own).
+    using RM = typename RecLds<Mode>::type;  // layout of the staged record blocks
     auto tblock = [&](int rt, int kb) -> Op {
       if constexpr (C::RREC) return cur.TB[kb];
-      return ws_load<Mode>(sR + kWsTOff, tri_block(rt, kb), lane);
+      return ws_load<RM>(sR + kWsTOff, tri_block(rt, kb), lane);
     };
     auto pblock = [&](int rt, int kb) -> Op {
       if constexpr (C::RREC) return cur.PB[kb];
-      return ws_load<Mode>(sR + kWsPOff, tri_block(rt, kb), lane);
+      return ws_load<RM>(sR + kWsPOff, tri_block(rt, kb), lane);
     };
     auto gamma4 = [&](int rt) -> f32x4 {
       if constexpr (C::RREC) return cur.gam;
