@@ -10,8 +10,8 @@
 // Columns of H evolve independently, so a workgroup owns NT tiles of 16 d_v columns of one
 // (sequence, V head) and walks its chunks in order. Each tile is computed by RW waves:
 //   RW = 1: one wave owns all 64 rows of the chunk and its [d_k x 16] fp32 state slice stays
-//           in that wave's registers for the whole sequence (fp32 operands with many chains;
-//           bf16 operands with many chains run gdn_scan_tiles.hip).
+//           in that wave's registers for the whole sequence (fp32 q / k / v with many chains;
+//           bf16 q / k / v with many chains run gdn_scan_tiles.hip).
 //   RW = 4: wave r owns row tile r (16 tokens) and 32 rows of the state; Y, V' and the new
 //           state cross waves through LDS (4x the waves for shapes with few sequences x heads).
 // Separate producer waves move the data: while chunk c is computed they write chunk c+1 (held
@@ -19,7 +19,10 @@
 // rows of chunk c-1; the compute waves' only global memory instructions in the chunk loop are
 // the row-split layout's loads of their own workspace-record blocks, one chunk ahead. q/k rows
 // are staged row-major with a 16-byte XOR swizzle; K^T operand fragments are read from the same
-// rows with ds_read_b64_tr_b16. In the row-split layout the waves of a tile exchange Y and V'
+// rows with ds_read_b64_tr_b16. Precision modes: bf16 q / k / v (Bf16Mode, K and Q staged as
+// fp16 for the products with the state), fp32 on fp32 MFMA (F32Mode), and fp32 on split-bf16
+// MFMA (F32SplitMode: each fp32 K / Q row staged as a hi and a lo bf16 plane, and the record
+// blocks split into the bf16 hi / lo layout, by the producers, once per chunk). In the row-split layout the waves of a tile exchange Y and V'
 // at two s_barriers per chunk that the producers also pass.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
 #include <type_traits>
@@ -278,7 +281,8 @@ struct ScanCfg {
   static constexpr int BUFB = VOFF + 64 * VSTR;
   static constexpr int NC = NT * RW;
   // producers hold <= 32 units each in registers; with bf16 q / k / v they also convert the K and
-  // Q rows to fp16 on the way, and four of them share that work
+  // Q rows to fp16 on the way (F32SplitMode: split them and the record blocks), and four of
+  // them share that work
   static constexpr int NP = std::is_same<Mode, Bf16Mode>::value ? 4 : (TOTAL + 31) / 32;
   static constexpr int PER = (TOTAL + NP - 1) / NP;
   static constexpr int THREADS = 64 * (NC + NP);
