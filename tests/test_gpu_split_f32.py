@@ -7,12 +7,15 @@ is the bf16 one, 2e-2 x RMS, against the float64 oracle on the same fp32 values.
 layouts are covered: few chains (four waves per 16-column tile) and many chains (one wave per
 tile)."""
 
+import dataclasses
+
 import pytest
 import torch
 
 import gated_deltanet_linear_amd as gdn
 import synthetic_inputs as si
-from gdn_testutil import TOL, assert_rms_close, oracle_case, rel_err
+from gdn_testutil import (TOL, assert_rms_close, assert_rms_close_rounded_out, oracle_case,
+                          rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +95,25 @@ def test_split_f32_rejects_bf16_inputs():
     case = si.make_core_case([10], 1, 1, 32, 32, dtype="bf16", seed=933)
     with pytest.raises(gdn.GdnError):
         _run(case, split=True)
+
+
+@pytest.mark.parametrize("layout", ["few", "many"])
+def test_split_f32_scale_and_bf16_state(layout):
+    """Output scale 0.37 (folded into P by the intra kernel and into the Q H term by the scan) and
+    bf16 initial / final states, against the oracle on the same bf16 initial state."""
+    c = CASES[(layout, 128)]
+    case = si.make_core_case(c["lengths"], c["hqk"], c["hv"], 128, 128, dtype="f32",
+                             gate="model", h0_std=0.02, seed=934)
+    case = dataclasses.replace(case, h0=case.h0.to(torch.bfloat16).float())  # bf16 values
+    dev = "cuda"
+    d = {k: getattr(case, k).to(dev) for k in ("q", "k", "v", "g", "beta", "cu_seqlens")}
+    h0 = case.h0.to(torch.bfloat16).to(dev)
+    o, ht = gdn.chunk_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                              initial_state=h0, scale=0.37, out_dtype=torch.float32,
+                              split_f32=True)
+    torch.cuda.synchronize()
+    assert ht.dtype == torch.bfloat16
+    ref_o, ref_h = oracle_case(case)
+    assert_rms_close(o.cpu(), 0.37 * ref_o, TOL["bf16"], "split o, scale 0.37")
+    # the final state is stored as bf16: one bf16 rounding of the reference allowed
+    assert_rms_close_rounded_out(ht.cpu(), ref_h, TOL["bf16"], "split bf16 final state")
