@@ -66,21 +66,27 @@ template <>
 __device__ __forceinline__ f32x8 row_frag<F32Mode, 512>(const char* b, int r, int kb, int g) {
   return afrag_f32<512>(b, r, kb, g);
 }
-// F32SplitMode: fp32 rows, each fragment split into hi + lo bf16 as it is read
+// F32SplitMode: the fp32 rows of a matrix (ROWB bytes each) are staged as two bf16 planes, the
+// hi halves of all 64 rows and then the lo halves, each laid out like bf16 rows of ROWB / 2
+// bytes (the same swizzle), so a fragment is two conflict-free 16-byte reads.
+template <int ROWB>
+__device__ __forceinline__ Bf16Mode::Op split_row_frag(const char* b, int r, int kb, int g) {
+  return {afrag<ROWB / 2>(b, r, kb, g), afrag<ROWB / 2>(b + 64 * (ROWB / 2), r, kb, g)};
+}
 template <>
 __device__ __forceinline__ Bf16Mode::Op row_frag<F32SplitMode, 128>(const char* b, int r, int kb,
                                                                     int g) {
-  return F32SplitMode::split(afrag_f32<128>(b, r, kb, g));
+  return split_row_frag<128>(b, r, kb, g);
 }
 template <>
 __device__ __forceinline__ Bf16Mode::Op row_frag<F32SplitMode, 256>(const char* b, int r, int kb,
                                                                     int g) {
-  return F32SplitMode::split(afrag_f32<256>(b, r, kb, g));
+  return split_row_frag<256>(b, r, kb, g);
 }
 template <>
 __device__ __forceinline__ Bf16Mode::Op row_frag<F32SplitMode, 512>(const char* b, int r, int kb,
                                                                     int g) {
-  return F32SplitMode::split(afrag_f32<512>(b, r, kb, g));
+  return split_row_frag<512>(b, r, kb, g);
 }
 
 // One workgroup per (chunk slot, group of NV V heads of one QK head): NV = 2 when the heads per
@@ -133,8 +139,10 @@ void chunk_intra_kernel(IntraParams p) {
 
   // ---- all memory reads at once: q/k rows into registers (16-byte loads, 1 KiB per wave
   // instruction) and the gates; then the rows go to LDS, row-major with the 16-byte XOR
-  // swizzle. Rows past len are written as zeros (identity steps).
+  // swizzle (F32SplitMode: as hi and lo bf16 planes, the swizzle of bf16 rows). Rows past len
+  // are written as zeros (identity steps).
   {
+    constexpr bool SPLIT = std::is_same<Mode, F32SplitMode>::value;
     constexpr int NCH = ROWB / 16, RPU = 64 / NCH, KI = KBYTES / 1024;
     constexpr int PER = (2 * KI + NWV - 1) / NWV;  // units per wave (the last ones may idle)
     const in_t* Kg = static_cast<const in_t*>(p.k);
@@ -147,7 +155,8 @@ void chunk_intra_kernel(IntraParams p) {
     for (int u = 0; u < PER; ++u) {
       const int j2 = wave + NWV * u, jj = j2 < KI ? j2 : j2 - KI;
       const int row = jj * RPU + lane / NCH;
-      const unsigned off = min(row, len - 1) * rs + 16 * ((lane % NCH) ^ swz<ROWB>(row));
+      const unsigned off =
+          min(row, len - 1) * rs + 16 * ((lane % NCH) ^ (SPLIT ? 0 : swz<ROWB>(row)));
       if (j2 < 2 * KI) r[u] = *reinterpret_cast<const f32x4*>((j2 < KI ? Kb : Qb) + off);
     }
     if (wave < NV && lane < len) {
@@ -159,8 +168,24 @@ void chunk_intra_kernel(IntraParams p) {
       const int j2 = wave + NWV * u, jj = j2 < KI ? j2 : j2 - KI;
       const int row = jj * RPU + lane / NCH;
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      if (j2 < 2 * KI)
-        *reinterpret_cast<f32x4*>(sKQ + 1024 * j2 + 16 * lane) = row < len ? r[u] : z;
+      if (j2 < 2 * KI) {
+        if constexpr (SPLIT) {
+          // 4 fp32 values of a row -> 8 bytes in the hi plane and 8 in the lo plane
+          const f32x4 x = row < len ? r[u] : z;
+          char* plane = sKQ + (j2 < KI ? 0 : KBYTES);
+          const int o2 = swz_off<ROWB / 2, 2>(row, 4 * (lane % NCH));
+          bf16x4 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = (bf16)x[e];
+            lo[e] = (bf16)(x[e] - (float)hi[e]);
+          }
+          *reinterpret_cast<bf16x4*>(plane + o2) = hi;
+          *reinterpret_cast<bf16x4*>(plane + 64 * (ROWB / 2) + o2) = lo;
+        } else {
+          *reinterpret_cast<f32x4*>(sKQ + 1024 * j2 + 16 * lane) = row < len ? r[u] : z;
+        }
+      }
     }
   }
   lds_barrier();
