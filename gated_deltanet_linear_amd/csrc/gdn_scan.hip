@@ -22,8 +22,9 @@
 // rows with ds_read_b64_tr_b16. Precision modes: bf16 q / k / v (Bf16Mode, K and Q staged as
 // fp16 for the products with the state), fp32 on fp32 MFMA (F32Mode), and fp32 on split-bf16
 // MFMA (F32SplitMode: each fp32 K / Q row staged as a hi and a lo bf16 plane, and the record
-// blocks split into the bf16 hi / lo layout, by the producers, once per chunk). In the row-split layout the waves of a tile exchange Y and V'
-// at two s_barriers per chunk that the producers also pass.
+// blocks split into the bf16 hi / lo layout, by the producers, once per chunk). In the row-split
+// layout the waves of a tile exchange Y and V' at two s_barriers per chunk that the producers
+// also pass.
 // Every product runs on MFMA in the fragment convention of gdn_device.hpp.
 #include <type_traits>
 
